@@ -1,0 +1,480 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Nothing here re-types the oracle's own formula: each check is a closed form, an invariant,
+brute force on a tiny input, or a special case that reduces to a LAPACK routine.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from activation_aware_rank_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _spd(n, seed, cond=None):
+    r = np.random.default_rng(seed)
+    Q, _ = np.linalg.qr(r.standard_normal((n, n)))
+    if cond is None:
+        d = r.uniform(0.5, 10.0, n)
+    else:
+        d = np.geomspace(1.0, 1.0 / cond, n)
+    return (Q * d) @ Q.T, d
+
+
+# ---------------------------------------------------------------------------------------------
+# input widening
+# ---------------------------------------------------------------------------------------------
+
+def test_widen_bf16_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F], dtype=np.uint16)
+    v = oracle.widen(bits, "bf16")
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 1.0 + 2.0 ** -7 and v[3] == 0.0
+    assert v[4] == 0.0 and np.signbit(v[4])
+    assert v[5] == (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def test_generator_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(3).standard_normal(100000).astype(np.float32) * 7.0
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0]  # ties: to even
+    ours = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# O1 covariance
+# ---------------------------------------------------------------------------------------------
+
+def test_cov_closed_form_diagonal():
+    s = np.array([0.5, 3.0, -2.0, 7.25])
+    X = np.vstack([np.diag(s), np.zeros((3, 4))])
+    C = oracle.covariance(X, "f64")
+    assert np.array_equal(C, np.diag(s * s))
+
+
+def test_cov_bruteforce_tiny():
+    r = np.random.default_rng(1)
+    X = r.standard_normal((5, 3))
+    W = r.standard_normal((3, 4))
+    C = oracle.covariance(X, "f64", W, "f64")
+    ref = np.zeros((4, 4))
+    for i, j in itertools.product(range(4), range(4)):
+        s = 0.0
+        for t in range(5):
+            yi = sum(X[t, a] * W[a, i] for a in range(3))
+            yj = sum(X[t, a] * W[a, j] for a in range(3))
+            s += yi * yj
+        ref[i, j] = s
+    assert np.allclose(C, ref, rtol=1e-14, atol=1e-14)
+
+
+def test_cov_additivity_scaling_trace_chunks():
+    d = inputs.single_layer(n_tok=300, d_in=24, d_out=20)
+    X, W = d["X"], d["W"]
+    C = oracle.covariance(X, "f32", W, "f32")
+    C2 = oracle.covariance(np.vstack([X, X]), "f32", W, "f32")
+    assert np.allclose(C2, 2 * C, rtol=1e-14, atol=0)
+    Cs = oracle.covariance(X * np.float32(2.0), "f32", W, "f32")
+    assert np.array_equal(Cs, 4 * C)
+    Y = oracle.widen(X, "f32") @ oracle.widen(W, "f32")
+    assert np.isclose(np.trace(C), np.sum(Y * Y), rtol=1e-13)
+    Cc = oracle.covariance(X, "f32", W, "f32", chunk_rows=7)
+    assert np.allclose(Cc, C, rtol=1e-13, atol=1e-13 * np.abs(C).max())
+    assert np.array_equal(C, C.T)
+
+
+def test_cov_identity_weight_is_gram_of_x():
+    X = np.random.default_rng(2).standard_normal((40, 6))
+    assert np.allclose(oracle.covariance(X, "f64"), X.T @ X, rtol=1e-14, atol=1e-14)
+
+
+def test_cov_per_head_blocks_are_diagonal_blocks():
+    d = inputs.per_head(n_tok=256, d_model=64, head_dim=16)
+    X, W = d["X"], d["W"]
+    full = oracle.covariance(X, "bf16", W, "bf16")
+    blocks = oracle.covariance(X, "bf16", W, "bf16", n_blocks=4)
+    for h in range(4):
+        assert np.allclose(blocks[h], full[16 * h:16 * h + 16, 16 * h:16 * h + 16], rtol=1e-13, atol=1e-13)
+
+
+def test_cov_entries_match_full():
+    d = inputs.single_layer(n_tok=200, d_in=16, d_out=12)
+    C = oracle.covariance(d["X"], "f32", d["W"], "f32")
+    rows, cols = np.array([0, 3, 11, 5]), np.array([0, 7, 11, 2])
+    e = oracle.covariance_entries(d["X"], "f32", d["W"], "f32", rows, cols, chunk_rows=64)
+    assert np.allclose(e, C[rows, cols], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------------
+# O2 eigendecomposition (cyclic Jacobi)
+# ---------------------------------------------------------------------------------------------
+
+def test_eig_2x2_closed_form():
+    a, b, c = 3.0, -1.25, 0.5
+    lam, V = oracle.eigh(np.array([[a, b], [b, c]]))
+    m, r = (a + c) / 2, np.hypot((a - c) / 2, b)
+    assert np.allclose(lam, [m + r, m - r], rtol=1e-15)
+    # eigenvector of the larger eigenvalue is proportional to (b, lam1 - a)
+    v = np.array([b, lam[0] - a])
+    v /= np.linalg.norm(v)
+    assert abs(abs(v @ V[:, 0]) - 1) < 1e-15
+
+
+def test_eig_diagonal_exact_and_sorted():
+    dvals = np.array([2.0, -1.0, 5.0, 5.0, 0.0, 3.5])
+    lam, V = oracle.eigh(np.diag(dvals))
+    assert np.array_equal(lam, np.array([5.0, 5.0, 3.5, 2.0, 0.0, -1.0]))
+    # stable order of the tie: original positions 2 then 3
+    assert V[2, 0] == 1.0 and V[3, 1] == 1.0
+    assert np.array_equal(np.abs(V).sum(0), np.ones(6))
+
+
+@pytest.mark.parametrize("n,seed", [(3, 0), (17, 1), (64, 2), (129, 3), (200, 4)])
+def test_eig_matches_lapack(n, seed):
+    C, d = _spd(n, seed)
+    lam, V = oracle.eigh(C)
+    ref_l, ref_V = np.linalg.eigh(C)
+    ref_l, ref_V = ref_l[::-1], ref_V[:, ::-1]
+    assert np.allclose(lam, ref_l, rtol=1e-12, atol=1e-12 * ref_l[0])
+    # eigenvectors agree up to sign for a separated spectrum
+    gaps = np.min(np.abs(np.diff(ref_l)))
+    assert gaps > 1e-6
+    assert np.max(np.abs(np.abs(np.sum(V * ref_V, 0)) - 1)) < 1e-10
+    assert np.max(np.abs(V.T @ V - np.eye(n))) < 1e-13
+    assert np.linalg.norm(C @ V - V * lam) <= 1e-13 * np.linalg.norm(C)
+    assert np.isclose(lam.sum(), np.trace(C), rtol=1e-13)
+
+
+def test_eig_sign_convention():
+    C, _ = _spd(31, 7)
+    _, V = oracle.eigh(C)
+    idx = np.argmax(np.abs(V), axis=0)
+    assert np.all(V[idx, np.arange(31)] > 0)
+
+
+def test_eig_repeated_and_rank_deficient():
+    r = np.random.default_rng(5)
+    Q, _ = np.linalg.qr(r.standard_normal((9, 9)))
+    d = np.array([4, 4, 4, 1, 1, 0, 0, 0, 0], dtype=float)
+    C = (Q * d) @ Q.T
+    lam, V = oracle.eigh(C)
+    assert np.allclose(lam, d, atol=1e-14 * 4)
+    P_ref = Q[:, :3] @ Q[:, :3].T
+    assert np.allclose(V[:, :3] @ V[:, :3].T, P_ref, atol=1e-13)
+
+
+def test_eig_rank_r_weight_gives_zero_tail():
+    r = np.random.default_rng(6)
+    X = r.standard_normal((300, 40))
+    W = r.standard_normal((40, 5)) @ r.standard_normal((5, 30))  # rank 5
+    C = oracle.covariance(X, "f64", W, "f64")
+    lam, _ = oracle.eigh(C)
+    assert np.all(np.abs(lam[5:]) <= 1e-13 * lam[0])
+    assert lam[4] > 1e-3 * lam[0]
+
+
+def test_eig_identity_weight_is_pca_of_x():
+    X = inputs.single_layer(n_tok=120, d_in=18, d_out=18)["X"]
+    C = oracle.covariance(X, "f32")
+    lam, V = oracle.eigh(C)
+    s = np.linalg.svd(oracle.widen(X, "f32"), compute_uv=False)
+    assert np.allclose(lam, s * s, rtol=1e-11, atol=1e-12 * lam[0])
+
+
+def test_eig_identity_input_gives_weight_spectrum():
+    W = inputs.single_layer(n_tok=24, d_in=24, d_out=24)["W"]
+    C = oracle.covariance(np.eye(24), "f64", W, "f32")
+    lam, V = oracle.eigh(C)
+    s = np.linalg.svd(oracle.widen(W, "f32"), compute_uv=False)
+    assert np.allclose(lam, s * s, rtol=1e-11, atol=1e-13 * lam[0])
+
+
+def test_eig_nonconvergence_is_reported():
+    C, _ = _spd(40, 8)
+    with pytest.raises(oracle.OracleError):
+        oracle.eigh(C, max_sweeps=1)
+
+
+def test_eig_upper_triangle_reader():
+    C, _ = _spd(12, 9)
+    U = np.triu(C) + np.tril(np.full((12, 12), 1e9), -1)  # garbage below the diagonal
+    l1, V1 = oracle.eigh_upper(U)
+    l2, V2 = oracle.eigh(C)
+    assert np.allclose(l1, l2, rtol=1e-14) and np.allclose(V1, V2, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# O3-O5 truncation and its error (Swift-SVD page, section 2-ga and the results' numerical
+# stability claim in section 4: the reconstruction error equals the theoretical minimum)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("which", ["single", "heads"])
+def test_closed_form_identity(which):
+    if which == "single":
+        d = inputs.single_layer(n_tok=512, d_in=48, d_out=40)
+        X, W, dt = d["X"], d["W"], "f32"
+    else:
+        d = inputs.per_head(n_tok=512, d_model=48, head_dim=48)
+        X, W, dt = d["X"], d["W"], "bf16"
+    C = oracle.covariance(X, dt, W, dt)
+    lam, V = oracle.eigh(C)
+    eps = oracle.error_curve(lam)
+    W64 = oracle.widen(W, dt)
+    for k in range(0, W64.shape[1] + 1):
+        A, B = oracle.truncate(W64, V, k)
+        e = oracle.direct_error(X, dt, W64, A @ B)
+        assert abs(e - eps[k]) <= 1e-10 * eps[0], (k, e, eps[k])
+
+
+def test_eckart_young_bruteforce_tiny():
+    r = np.random.default_rng(11)
+    X = r.standard_normal((40, 10)) * r.uniform(0.1, 3, 10)
+    W = r.standard_normal((10, 8))
+    C = oracle.covariance(X, "f64", W, "f64")
+    lam, V = oracle.eigh(C)
+    eps = oracle.error_curve(lam)
+    Y = X @ W
+    s = np.linalg.svd(Y, compute_uv=False)
+    assert np.allclose(lam, s * s, rtol=1e-12, atol=1e-12 * lam[0])
+    for k in (1, 3, 5):
+        # random rank-k W' = P Q never beats eps_k
+        P = r.standard_normal((2000, 10, k))
+        Qm = r.standard_normal((2000, k, 8))
+        R = Y[None] - X[None] @ (P @ Qm)
+        errs = np.sum(R * R, axis=(1, 2))
+        assert np.all(errs >= eps[k] * (1 - 1e-12))
+        # random rank-k W' = W V' V'^T with V' near span(V_k) never beats it either
+        for _ in range(200):
+            Vp, _ = np.linalg.qr(V[:, :k] + 1e-3 * r.standard_normal((8, k)))
+            Wp = W @ Vp @ Vp.T
+            e = np.sum((Y - X @ Wp) ** 2)
+            assert e >= eps[k] * (1 - 1e-12)
+
+
+def test_identity_input_truncation_is_truncated_svd():
+    r = np.random.default_rng(12)
+    W = r.standard_normal((16, 12))
+    C = oracle.covariance(np.eye(16), "f64", W, "f64")
+    lam, V = oracle.eigh(C)
+    U, s, Vt = np.linalg.svd(W)
+    for k in (1, 4, 11):
+        A, B = oracle.truncate(W, V, k)
+        ref = (U[:, :k] * s[:k]) @ Vt[:k]
+        assert np.allclose(A @ B, ref, atol=1e-12 * s[0])
+
+
+def test_error_curve_properties():
+    lam = np.array([5.0, 2.0, 2.0, 0.25, 0.0, -1e-17])
+    eps = oracle.error_curve(lam)
+    assert eps[-1] == 0.0 and eps.shape == (7,)
+    assert np.allclose(np.diff(eps), -lam, rtol=0, atol=1e-15)
+    assert np.isclose(eps[0], lam.sum())
+    assert eps[4] == 0.0 + (-1e-17) + 0.0  # summed from the smallest
+    batch = oracle.error_curve(np.stack([lam, lam * 2]))
+    assert np.array_equal(batch[1], 2 * batch[0])
+
+
+# ---------------------------------------------------------------------------------------------
+# O6 Fisher importance (FLRC page, method 1)
+# ---------------------------------------------------------------------------------------------
+
+def test_fisher_constant_inputs():
+    g = inputs.f32_to_bf16_bits(np.full(1000, 0.375, np.float32))
+    w = inputs.f32_to_bf16_bits(np.full(1000, -1.5, np.float32))
+    assert oracle.fisher(g, w) == 1000 * (0.375 * -1.5) ** 2
+
+
+def test_fisher_scaling_and_bruteforce():
+    G = inputs.gradient(7, 9, 1e-4, 4, 0, 0)
+    W = inputs.weight(7, 9, "bf16", 4, 0, 0)
+    a = oracle.fisher(G, W)
+    G2 = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(G) * 2)
+    assert oracle.fisher(G2, W) == 4 * a
+    gs, ws = inputs.bf16_bits_to_f32(G).ravel(), inputs.bf16_bits_to_f32(W).ravel()
+    ref = 0.0
+    for x, y in zip(gs.tolist(), ws.tolist()):
+        ref += (x * y) ** 2
+    assert np.isclose(a, ref, rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------------
+# O7 greedy allocation (LASER page, method 2; FLRC page, method 1; Swift-SVD page, 2-na)
+# ---------------------------------------------------------------------------------------------
+
+def _alloc_args(ex):
+    ms = ex["matrices"]
+    return ([m["alpha"] for m in ms], [np.array(m["lam"]) for m in ms], [m["eps0"] for m in ms],
+            [m["cost"] for m in ms])
+
+
+def test_alloc_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "alloc_worked_example.json")))
+    alpha, lams, eps0, cost = _alloc_args(ex)
+    for case in ex["cases"]:
+        k, info = oracle.allocate_ranks(alpha, lams, eps0, cost, case["budget"], case["k_min"])
+        assert info == case["info"], case
+        assert list(k) == case["k"], case
+
+
+def _greedy_by_definition(alpha, lams, eps0, cost, budget, k_min):
+    """Repeatedly take the best remaining component (highest priority; ties: lower m, lower k)
+    while it fits; stop at the first that does not.  Priorities compared as exact rationals
+    of the same fp64 values."""
+    M = len(lams)
+    k = list(k_min)
+    rem = budget - sum(k_min[m] * cost[m] for m in range(M))
+    if rem < 0:
+        return k, 4
+    taken = set()
+    cand = []
+    for m in range(M):
+        w = np.float64(alpha[m]) / (np.float64(eps0[m]) * np.float64(cost[m])) if eps0[m] else 0.0
+        for kk in range(k_min[m] + 1, len(lams[m]) + 1):
+            cand.append((float(np.float64(w) * max(np.float64(lams[m][kk - 1]), 0.0)), m, kk))
+    while True:
+        best = None
+        for c in cand:
+            if c in taken:
+                continue
+            if best is None or (c[0] > best[0]) or (c[0] == best[0] and (c[1], c[2]) < (best[1], best[2])):
+                best = c
+        if best is None or cost[best[1]] > rem:
+            return k, 0
+        taken.add(best)
+        rem -= cost[best[1]]
+        k[best[1]] += 1
+
+
+def test_alloc_equals_greedy_definition_random():
+    r = np.random.default_rng(13)
+    for trial in range(60):
+        M = r.integers(1, 5)
+        lams = [np.sort(r.choice([0.0, 0.5, 1.0, 2.0, 3.0, -0.5], size=r.integers(1, 6)))[::-1]
+                for _ in range(M)]
+        alpha = list(r.choice([0.0, 1.0, 2.0, 3.0], size=M))
+        eps0 = [float(max(np.sum(l), 0.0)) for l in lams]
+        cost = list(r.integers(1, 5, size=M))
+        k_min = [int(r.integers(0, len(l) + 1)) if r.random() < 0.3 else 0 for l in lams]
+        total = sum(len(l) * c for l, c in zip(lams, cost))
+        for budget in (0, 1, 3, total // 2, total, total + 3):
+            k, info = oracle.allocate_ranks(alpha, lams, eps0, cost, budget, k_min)
+            k2, info2 = _greedy_by_definition(alpha, lams, eps0, cost, budget, k_min)
+            assert info == info2 and list(k) == list(k2), (trial, budget)
+
+
+def test_alloc_invariants_and_monotone_budget():
+    r = np.random.default_rng(14)
+    M = 6
+    lams = [np.sort(r.exponential(1.0, 40))[::-1] for _ in range(M)]
+    alpha = r.exponential(1.0, M)
+    eps0 = [l.sum() for l in lams]
+    cost = r.integers(3, 9, M)
+    prev = np.zeros(M, dtype=int)
+    p, mm, kk = oracle.allocation_priorities(alpha, lams, eps0, cost, np.zeros(M, int))
+    order = np.lexsort((kk, mm, -p))
+    for budget in range(0, int(np.sum(cost * 40)) + 10, 37):
+        k, info = oracle.allocate_ranks(alpha, lams, eps0, cost, budget)
+        assert info == 0
+        used = int(np.sum(k * cost))
+        assert used <= budget
+        assert np.all(k >= prev) and np.all(k <= 40)
+        n_taken = int(np.sum(k))
+        if n_taken < len(order):
+            assert used + cost[mm[order[n_taken]]] > budget
+        prev = k
+
+
+def test_alloc_identical_matrices_equal_ranks():
+    lam = np.sort(np.random.default_rng(15).exponential(1.0, 30))[::-1]
+    k, info = oracle.allocate_ranks([2.0, 2.0], [lam, lam.copy()], [lam.sum()] * 2, [5, 5], 5 * 31)
+    assert info == 0 and abs(int(k[0]) - int(k[1])) <= 1 and k.sum() == 31
+
+
+def test_alloc_bad_score_info5():
+    k, info = oracle.allocate_ranks([1.0, np.nan], [np.ones(3), np.ones(3)], [3.0, 3.0], [1, 1], 10)
+    assert info == 5
+    k, info = oracle.allocate_ranks([1.0, -1.0], [np.ones(3), np.ones(3)], [3.0, 3.0], [1, 1], 10)
+    assert info == 5
+
+
+# ---------------------------------------------------------------------------------------------
+# O8 curvature-weighted variant (LASER page, method 1)
+# ---------------------------------------------------------------------------------------------
+
+def test_cholesky_matches_lapack_and_reconstructs():
+    S, _ = _spd(50, 21, cond=1e6)
+    L = oracle.cholesky(S)
+    assert np.allclose(L, np.linalg.cholesky(S), rtol=1e-9, atol=1e-12)
+    assert np.linalg.norm(L @ L.T - S) <= 1e-14 * np.linalg.norm(S)
+    assert np.array_equal(L, np.tril(L))
+
+
+def test_cholesky_not_positive_definite():
+    S = np.diag([1.0, 2.0, -1.0, 3.0])
+    with pytest.raises(oracle.OracleError):
+        oracle.cholesky(S)
+
+
+def test_triangular_solves():
+    L = np.tril(np.random.default_rng(22).standard_normal((9, 9))) + 5 * np.eye(9)
+    B = np.random.default_rng(23).standard_normal((9, 4))
+    assert np.allclose(L @ oracle.solve_lower(L, B), B, atol=1e-13)
+    assert np.allclose(L.T @ oracle.solve_lower_t(L, B), B, atol=1e-13)
+
+
+def _kfac_problem(seed, din=14, dout=20, n=400):
+    r = np.random.default_rng(seed)
+    Aact = r.standard_normal((n, din)) * np.exp(r.standard_normal(din))
+    Gam = r.standard_normal((n, dout)) * 1e-3
+    Sx = Aact.T @ Aact / n
+    Sg = Gam.T @ Gam / n
+    W = r.standard_normal((din, dout)) * 0.02
+    return Sx, Sg, W
+
+
+def test_kfac_closed_form_error_and_b_forms():
+    Sx, Sg, W = _kfac_problem(31)
+    k = 5
+    out = oracle.kfac_compress(Sx, Sg, W, k)
+    Lx, Lg, A, B = out["Lx"], out["Lg"], out["A"], out["B"]
+    R = Lx.T @ (W - A @ B) @ Lg
+    tail = np.sum(np.maximum(out["lam"][k:], 0))
+    assert abs(np.sum(R * R) - tail) <= 1e-10 * np.sum(out["lam"])
+    # curvature form of the same loss: vec(dW)^T (Sg (x) Sx) vec(dW) = tr(dW^T Sx dW Sg)
+    D = W - A @ B
+    assert np.isclose(np.trace(D.T @ Sx @ D @ Sg), tail, rtol=1e-9)
+    # B = V_k^T Lg^{-1} with V_k the right singular vectors of W~
+    U, s, Vt = np.linalg.svd(out["Wt"])
+    B2 = oracle.solve_lower_t(Lg, Vt[:k].T).T  # (Lg^{-T} V_k)^T = V_k^T Lg^{-1}
+    sgn = np.sign(np.sum(B2 * B, axis=1))
+    assert np.allclose(B2 * sgn[:, None], B, rtol=1e-8, atol=1e-10 * np.abs(B).max())
+
+
+def test_kfac_independent_of_factorisation():
+    Sx, Sg, W = _kfac_problem(32)
+    k = 4
+    out = oracle.kfac_compress(Sx, Sg, W, k)
+    # symmetric square roots instead of Cholesky factors give the same optimum W_k
+    def sqrtm(S):
+        l, V = np.linalg.eigh(S)
+        return (V * np.sqrt(l)) @ V.T
+    Rx, Rg = sqrtm(Sx), sqrtm(Sg)
+    Wt = Rx @ W @ Rg
+    U, s, Vt = np.linalg.svd(Wt)
+    Wk = np.linalg.solve(Rx, (U[:, :k] * s[:k]) @ Vt[:k]) @ np.linalg.inv(Rg)
+    assert np.allclose(out["A"] @ out["B"], Wk, rtol=1e-7, atol=1e-9 * np.abs(Wk).max())
+    assert np.allclose(np.sqrt(np.maximum(out["lam"][:len(s)], 0)), s, rtol=1e-9)
+
+
+def test_kfac_identity_curvature_is_truncated_svd():
+    W = np.random.default_rng(33).standard_normal((10, 13))
+    k = 3
+    out = oracle.kfac_compress(np.eye(10), np.eye(13), W, k)
+    U, s, Vt = np.linalg.svd(W)
+    assert np.allclose(out["A"] @ out["B"], (U[:, :k] * s[:k]) @ Vt[:k], atol=1e-12)
