@@ -1,0 +1,210 @@
+// C-ABI entry points of liblrc: argument validation, then dispatch to the per-op launchers.
+// Nothing is launched when validation fails.
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "lrc_internal.h"
+
+namespace lrc {
+
+static thread_local std::string g_last_error;
+
+lrc_status fail(lrc_status s, const std::string &msg) {
+    g_last_error = msg;
+    return s;
+}
+
+lrc_status hip_fail(hipError_t e, const char *what) {
+    char buf[512];
+    snprintf(buf, sizeof(buf), "%s failed: %s (%d)", what, hipGetErrorString(e), int(e));
+    g_last_error = buf;
+    return LRC_ERR_HIP;
+}
+
+static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace lrc
+
+using namespace lrc;
+
+#define REQUIRE(cond, code, msg) \
+    do {                         \
+        if (!(cond)) return fail(code, msg); \
+    } while (0)
+
+extern "C" {
+
+int lrc_abi_version(void) { return LRC_ABI_VERSION; }
+
+const char *lrc_status_string(lrc_status s) {
+    switch (s) {
+        case LRC_OK: return "ok";
+        case LRC_ERR_ARG: return "invalid argument";
+        case LRC_ERR_DTYPE: return "unsupported dtype";
+        case LRC_ERR_WORKSPACE: return "workspace missing or too small";
+        case LRC_ERR_HIP: return "HIP runtime error";
+        case LRC_ERR_UNIMPLEMENTED: return "not implemented";
+    }
+    return "unknown status";
+}
+
+const char *lrc_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------------------------
+size_t lrc_cov_accumulate_workspace(lrc_dtype x_t, int64_t n_tok, int64_t d_in, int has_w, int64_t d_out,
+                                    int32_t n_blocks) {
+    if (n_tok <= 0 || d_in <= 0 || d_out <= 0 || n_blocks <= 0) return 0;
+    return cov_workspace(x_t, n_tok, d_in, has_w, d_out, n_blocks);
+}
+
+lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64_t d_in, int64_t ldx,
+                              const void *W, lrc_dtype w_t, int64_t d_out, int64_t ldw, int32_t n_blocks,
+                              float *C, int64_t ldc, void *ws, size_t ws_bytes, int32_t *info, void *stream) {
+    REQUIRE(X && C && info, LRC_ERR_ARG, "X, C and info must be non-NULL");
+    REQUIRE(n_tok > 0 && d_in > 0 && d_out > 0, LRC_ERR_ARG, "n_tok, d_in, d_out must be positive");
+    REQUIRE(ldx >= d_in, LRC_ERR_ARG, "ldx < d_in");
+    REQUIRE(n_blocks >= 1 && d_out % n_blocks == 0, LRC_ERR_ARG, "n_blocks must divide d_out");
+    REQUIRE(x_t == LRC_BF16 || x_t == LRC_F32, LRC_ERR_DTYPE, "x_t must be LRC_BF16 or LRC_F32");
+    if (W) {
+        REQUIRE(w_t == x_t, LRC_ERR_DTYPE, "w_t must equal x_t");
+        REQUIRE(ldw >= d_out, LRC_ERR_ARG, "ldw < d_out");
+    } else {
+        REQUIRE(d_out == d_in, LRC_ERR_ARG, "W == NULL (identity) needs d_out == d_in");
+    }
+    const int64_t hd = d_out / n_blocks;
+    REQUIRE(ldc >= hd && (n_blocks > 1 || ldc >= d_out), LRC_ERR_ARG, "ldc too small");
+    size_t need = cov_workspace(x_t, n_tok, d_in, W != nullptr, d_out, n_blocks);
+    REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned(ws, 256))), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_cov_accumulate_workspace() or not 256-byte aligned");
+    CovArgs a{X, x_t, n_tok, d_in, ldx, W, d_out, ldw, n_blocks, C, ldc, info};
+    return cov_run(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+size_t lrc_eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype prec) {
+    if (n <= 0 || batch <= 0 || n_vec < 0 || n_vec > n) return 0;
+    return eigh_workspace(n, batch, n_vec, prec);
+}
+
+lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64_t stride_c, lrc_dtype prec,
+                    double *lambda, float *V, int64_t ldv, int64_t n_vec, int64_t stride_v, void *ws,
+                    size_t ws_bytes, int32_t *info, void *stream) {
+    REQUIRE(C && lambda && info, LRC_ERR_ARG, "C, lambda and info must be non-NULL");
+    REQUIRE(n > 0 && batch > 0, LRC_ERR_ARG, "n and batch must be positive");
+    REQUIRE(n <= (int64_t(1) << 20), LRC_ERR_ARG, "n too large");
+    REQUIRE(ldc >= n, LRC_ERR_ARG, "ldc < n");
+    REQUIRE(batch == 1 || stride_c >= n * ldc - (ldc - n), LRC_ERR_ARG, "stride_c overlaps matrices");
+    REQUIRE(n_vec >= 0 && n_vec <= n, LRC_ERR_ARG, "n_vec must be in [0, n]");
+    REQUIRE(n_vec == 0 || (V && ldv >= n_vec), LRC_ERR_ARG, "V NULL or ldv < n_vec");
+    REQUIRE(n_vec == 0 || batch == 1 || stride_v >= n * ldv - (ldv - n_vec), LRC_ERR_ARG,
+            "stride_v overlaps matrices");
+    REQUIRE(prec == LRC_F32 || prec == LRC_F64, LRC_ERR_DTYPE, "prec must be LRC_F32 or LRC_F64");
+    size_t need = eigh_workspace(n, batch, n_vec, prec);
+    REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned(ws, 256))), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_eigh_workspace() or not 256-byte aligned");
+    EighArgs a{C, n, ldc, batch, stride_c, prec, lambda, V, ldv, n_vec, stride_v, info};
+    return eigh_run(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+lrc_status lrc_error_curve(const double *lambda, int64_t n, int64_t batch, double *eps, void *stream) {
+    REQUIRE(lambda && eps, LRC_ERR_ARG, "lambda and eps must be non-NULL");
+    REQUIRE(n > 0 && batch > 0, LRC_ERR_ARG, "n and batch must be positive");
+    return error_curve_run(lambda, n, batch, eps, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+lrc_status lrc_factorize(const void *W, lrc_dtype w_t, int32_t trans_w, int64_t d_in, int64_t d_out, int64_t ldw,
+                         const float *V, int64_t ldv, int64_t k, int64_t batch, int64_t stride_w,
+                         int64_t stride_v, float *A, int64_t lda, int64_t stride_a, float *B, int64_t ldb,
+                         int64_t stride_b, void *stream) {
+    REQUIRE(W && V && A, LRC_ERR_ARG, "W, V and A must be non-NULL");
+    REQUIRE(trans_w == 0 || trans_w == 1, LRC_ERR_ARG, "trans_w must be 0 or 1");
+    REQUIRE(d_in > 0 && d_out > 0 && k > 0 && batch > 0, LRC_ERR_ARG, "sizes must be positive");
+    REQUIRE(ldw >= d_out, LRC_ERR_ARG, "ldw < d_out");
+    REQUIRE(ldv >= k && lda >= k, LRC_ERR_ARG, "ldv or lda < k");
+    const int64_t vrows = trans_w ? d_in : d_out;
+    REQUIRE(k <= vrows, LRC_ERR_ARG, "k larger than the rows of V");
+    REQUIRE(!B || ldb >= vrows, LRC_ERR_ARG, "ldb < rows of V");
+    REQUIRE(batch == 1 || (stride_w >= 0 && stride_v >= 0 && stride_a > 0 && (!B || stride_b > 0)),
+            LRC_ERR_ARG, "bad batch strides");
+    REQUIRE(w_t == LRC_BF16 || w_t == LRC_F32 || w_t == LRC_F64, LRC_ERR_DTYPE, "w_t must be bf16, f32 or f64");
+    FactorizeArgs a{W, w_t, trans_w, d_in, d_out, ldw, V, ldv, k, batch, stride_w, stride_v,
+                    A, lda, stride_a, B, ldb, stride_b};
+    return factorize_run(a, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+size_t lrc_fisher_scores_workspace(int32_t n_mats, const int64_t *numel) {
+    if (n_mats <= 0 || !numel) return 0;
+    for (int i = 0; i < n_mats; ++i)
+        if (numel[i] < 0) return 0;
+    return fisher_workspace(n_mats, numel);
+}
+
+lrc_status lrc_fisher_scores(int32_t n_mats, const void *const *G, const void *const *W, const int64_t *numel,
+                             lrc_dtype t, double *alpha, void *ws, size_t ws_bytes, int32_t *info, void *stream) {
+    REQUIRE(n_mats > 0 && G && W && numel && alpha && info, LRC_ERR_ARG, "null argument or n_mats <= 0");
+    REQUIRE(t == LRC_BF16 || t == LRC_F32, LRC_ERR_DTYPE, "t must be LRC_BF16 or LRC_F32");
+    for (int i = 0; i < n_mats; ++i) {
+        REQUIRE(numel[i] >= 0, LRC_ERR_ARG, "negative numel");
+        REQUIRE(numel[i] == 0 || (G[i] && W[i]), LRC_ERR_ARG, "null G[m] or W[m]");
+    }
+    size_t need = fisher_workspace(n_mats, numel);
+    REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned(ws, 256))), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_fisher_scores_workspace() or not 256-byte aligned");
+    return fisher_run(n_mats, G, W, numel, t, alpha, ws, ws_bytes, info, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+size_t lrc_allocate_ranks_workspace(int32_t n_mats, int64_t n_items) {
+    if (n_mats <= 0 || n_items < 0) return 0;
+    return alloc_workspace(n_mats, n_items);
+}
+
+lrc_status lrc_allocate_ranks(int32_t n_mats, const double *alpha, const double *lambda_packed,
+                              const int64_t *offsets, int64_t n_items, const double *eps0, const int64_t *cost,
+                              const int32_t *k_min, int64_t budget_params, int32_t *k_out, void *ws,
+                              size_t ws_bytes, int32_t *info, void *stream) {
+    REQUIRE(n_mats > 0 && alpha && offsets && eps0 && cost && k_out && info, LRC_ERR_ARG,
+            "null argument or n_mats <= 0");
+    REQUIRE(n_items >= 0 && (n_items == 0 || lambda_packed), LRC_ERR_ARG, "bad n_items or lambda_packed");
+    REQUIRE(n_items < (int64_t(1) << 31), LRC_ERR_ARG, "n_items too large");
+    REQUIRE(budget_params >= 0, LRC_ERR_ARG, "negative budget");
+    size_t need = alloc_workspace(n_mats, n_items);
+    REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned(ws, 256))), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_allocate_ranks_workspace() or not 256-byte aligned");
+    AllocArgs a{n_mats, alpha, lambda_packed, offsets, n_items, eps0, cost, k_min, budget_params, k_out, info};
+    return alloc_run(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
+size_t lrc_cholesky_workspace(int64_t n) { return n > 0 ? cholesky_workspace(n) : 0; }
+
+lrc_status lrc_cholesky(double *A, int64_t n, int64_t lda, void *ws, size_t ws_bytes, int32_t *info, void *stream) {
+    REQUIRE(A && info, LRC_ERR_ARG, "A and info must be non-NULL");
+    REQUIRE(n > 0 && lda >= n, LRC_ERR_ARG, "bad n or lda");
+    size_t need = cholesky_workspace(n);
+    REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned(ws, 256))), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_cholesky_workspace() or not 256-byte aligned");
+    return cholesky_run(A, n, lda, ws, ws_bytes, info, static_cast<hipStream_t>(stream));
+}
+
+lrc_status lrc_trmm(int32_t side, int32_t trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B,
+                    int64_t ldb, void *stream) {
+    REQUIRE(L && B, LRC_ERR_ARG, "L and B must be non-NULL");
+    REQUIRE((side == 0 || side == 1) && (trans == 0 || trans == 1), LRC_ERR_ARG, "side/trans must be 0 or 1");
+    REQUIRE(m > 0 && n > 0 && ldb >= n && ldl >= (side ? n : m), LRC_ERR_ARG, "bad sizes or leading dims");
+    return trmm_run(side, trans, m, n, L, ldl, B, ldb, static_cast<hipStream_t>(stream));
+}
+
+lrc_status lrc_trsm(int32_t side, int32_t trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B,
+                    int64_t ldb, void *stream) {
+    REQUIRE(L && B, LRC_ERR_ARG, "L and B must be non-NULL");
+    REQUIRE((side == 0 || side == 1) && (trans == 0 || trans == 1), LRC_ERR_ARG, "side/trans must be 0 or 1");
+    REQUIRE(m > 0 && n > 0 && ldb >= n && ldl >= (side ? n : m), LRC_ERR_ARG, "bad sizes or leading dims");
+    return trsm_run(side, trans, m, n, L, ldl, B, ldb, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

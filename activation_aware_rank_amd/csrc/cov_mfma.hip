@@ -1,0 +1,401 @@
+// bf16 MFMA path of the covariance accumulation.
+//
+// Per chunk of tokens (Swift-SVD page, section 2-ga: C is aggregated over the calibration
+// tokens, one chunk at a time):
+//   1. GEMM  Y^T[i][t] = sum_k W^T[i][k] X[t][k]        (bf16 MFMA, fp32 accumulation)
+//      epilogue: hi = bf16(y), lo = bf16(y - hi), stored token-contiguous.
+//   2. SYRK  C[I,J] += Yhi_I Yhi_J^T + Yhi_I Ylo_J^T + Ylo_I Yhi_J^T   for tiles I <= J
+//      (bf16 MFMA, fp32 accumulation).  The lo*lo term is below fp32 rounding of C.
+// With W == NULL (C += X^T X) the chunk is transposed exactly and one product suffices.
+//
+// Both phases are one "NT" kernel: D = A B^T with A and B row-major along the contraction
+// axis, which is exactly the layout the 32x32x16 bf16 MFMA operands want (each lane holds 8
+// contiguous k-values of one row).  Block tile BM x BM with 4 waves (2 x 2), k step 32,
+// double-buffered LDS with an XOR swizzle of the 16-byte chunks (no padding, no bank
+// conflicts on 16-byte reads), one barrier per k step.
+//
+// Load balance of the SYRK: the upper triangle may have fewer tiles than the GPU has CUs, so
+// the token range of a chunk is split S ways; split s > 0 accumulates into its own fp32
+// buffer and the buffers are added to C in split order at the end of the call (fixed order,
+// deterministic).
+#include <cmath>
+
+#include "cov_mfma.h"
+
+namespace lrc {
+
+constexpr int MK = 32;                   // k step, bf16 elements (4 chunks of 16 bytes)
+constexpr int64_t MFMA_CHUNK = 32768;    // tokens per internal chunk
+constexpr int MFMA_THREADS = 256;
+
+__device__ __forceinline__ int swz(int r, int c) { return r * MK + ((c ^ ((r >> 1) & 3)) << 3); }
+
+template <int BM, int NOPS>
+struct MfmaTile {
+    static constexpr int TM = BM / 64;                  // 32x32 MFMA tiles per wave per dim
+    static constexpr int WM = BM / 2;                   // wave tile
+    static constexpr int U = BM * (MK / 8) / MFMA_THREADS;  // 16-byte chunks per thread per operand
+};
+
+// acc[tm][tn] += sum over k in [0, klen) of A[row][k] B[col][k]; ops: {A(,Alo), B(,Blo)}
+template <int BM, int NOPS, int NPROD>
+__device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const int64_t *ld, const int *rows,
+                                              int64_t klen, f32x16_t (&acc)[BM / 64][BM / 64], bf16_t *lds) {
+    using T = MfmaTile<BM, NOPS>;
+    constexpr int TM = T::TM, U = T::U;
+    constexpr int OPSZ = BM * MK;  // elements of one operand tile
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = int((klen + MK - 1) / MK);
+    u32x4_t regs[NOPS][U];
+
+    auto gload = [&](int kt) {
+        const int64_t k0 = int64_t(kt) * MK;
+#pragma unroll
+        for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = tid + MFMA_THREADS * u;
+                const int r = q >> 2, c = q & 3;
+                const int64_t k = k0 + c * 8;
+                if (r < rows[o] && k < klen)
+                    regs[o][u] = *reinterpret_cast<const u32x4_t *>(base[o] + int64_t(r) * ld[o] + k);
+                else
+                    regs[o][u] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int q = tid + MFMA_THREADS * u;
+                const int r = q >> 2, c = q & 3;
+                *reinterpret_cast<u32x4_t *>(lds + (buf * NOPS + o) * OPSZ + swz(r, c)) = regs[o][u];
+            }
+    };
+
+    if (nk <= 0) return;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    constexpr int NA = (NPROD == 3) ? 2 : 1;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        const bf16_t *sb = lds + cur * NOPS * OPSZ;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c = ks * 2 + (lane >> 5);
+            bf16x8_t af[NA][TM], bfr[NA][TM];
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int t = 0; t < TM; ++t) {
+                    const int ra = wm * T::WM + t * 32 + (lane & 31);
+                    const int rb = wn * T::WM + t * 32 + (lane & 31);
+                    af[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + a * OPSZ + swz(ra, c));
+                    bfr[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + (NA + a) * OPSZ + swz(rb, c));
+                }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TM; ++tn) {
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[0][tn], acc[tm][tn], 0, 0, 0);
+                    if (NPROD == 3) {
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[1][tn], acc[tm][tn], 0, 0, 0);
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[0][tn], acc[tm][tn], 0, 0, 0);
+                    }
+                }
+        }
+        if (kt + 1 < nk) sstore(cur ^ 1);
+        __syncthreads();
+    }
+}
+
+// Output position of accumulator element r of lane `lane` in a 32x32 MFMA tile.
+__device__ __forceinline__ int acc_row(int lane, int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
+
+// Y^T[ib + row][t] for the 16 values of one lane: hi = bf16(y), lo = bf16(y - hi)
+__device__ __forceinline__ void store_split_tile(const f32x16_t a, int64_t ib, int64_t t, int lane, int64_t d_out,
+                                                 bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo, int64_t ldy) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t i = ib + acc_row(lane, r);
+        if (i < d_out) {
+            const float y = a[r];
+            const bf16_t hi = f32_to_bf16(y);
+            Yhi[i * ldy + t] = hi;
+            Ylo[i * ldy + t] = f32_to_bf16(y - bf16_to_f32(hi));
+        }
+    }
+}
+
+// dst[rb + row][cc] += value for the upper triangle (row <= col) inside the hd x hd block
+__device__ __forceinline__ void add_upper_tile(const f32x16_t a, int64_t rb, int64_t cc, int lane, int64_t hd,
+                                               float *__restrict__ dst, int64_t ldd) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t rr = rb + acc_row(lane, r);
+        if (rr < hd && cc < hd && rr <= cc) dst[rr * ldd + cc] += a[r];
+    }
+}
+
+// Phase 1: Y^T tile (rows = output features i, cols = tokens t), split into hi/lo.
+template <int BM>
+__global__ void __launch_bounds__(MFMA_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const bf16_t *__restrict__ X, int64_t ldx,
+             int64_t tc, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo, int64_t ldy) {
+    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * BM * MK];
+    constexpr int TM = BM / 64;
+    const int64_t i0 = int64_t(blockIdx.x) * BM, t0 = int64_t(blockIdx.y) * BM;
+    const bf16_t *base[2] = {Wt + i0 * d_in, X + t0 * ldx};
+    const int64_t ld[2] = {d_in, ldx};
+    const int rows[2] = {int(std::min<int64_t>(BM, d_out - i0)), int(std::max<int64_t>(0, std::min<int64_t>(BM, tc - t0)))};
+    f32x16_t acc[TM][TM];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = f32x16_t{};
+    mfma_mainloop<BM, 2, 1>(base, ld, rows, d_in, acc, lds);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TM; ++tn) {
+            const int64_t ib = i0 + wm * (BM / 2) + tm * 32;
+            const int64_t t = t0 + wn * (BM / 2) + tn * 32 + acc_col(lane);
+            store_split_tile(acc[tm][tn], ib, t, lane, d_out, Yhi, Ylo, ldy);
+        }
+}
+
+// Phase 2: upper tiles of each head block, split s of the token range.
+template <int BM, int NPROD>
+__global__ void __launch_bounds__(MFMA_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64_t ldy, int64_t ktot, int64_t kchunk,
+           int64_t hd, float *__restrict__ C, int64_t ldc, float *__restrict__ P, int32_t n_blocks) {
+    constexpr int NOPS = (NPROD == 3) ? 4 : 2;
+    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * NOPS * BM * MK];
+    constexpr int TM = BM / 64;
+    const int u = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    int J = int((sqrtf(8.f * float(u) + 1.f) - 1.f) * 0.5f);
+    while (J * (J + 1) / 2 > u) --J;
+    while ((J + 1) * (J + 2) / 2 <= u) ++J;
+    const int I = u - J * (J + 1) / 2;
+    const int64_t kb = int64_t(s) * kchunk;
+    const int64_t klen = std::min(kchunk, ktot - kb);
+    if (klen <= 0) return;
+    const int64_t r0 = int64_t(h) * hd + int64_t(I) * BM, c0 = int64_t(h) * hd + int64_t(J) * BM;
+    const int rowsI = int(std::min<int64_t>(BM, hd - int64_t(I) * BM));
+    const int rowsJ = int(std::min<int64_t>(BM, hd - int64_t(J) * BM));
+    const bf16_t *base[4];
+    int64_t ld[4];
+    int rows[4];
+    if (NPROD == 3) {
+        base[0] = Yhi + r0 * ldy + kb; base[1] = Ylo + r0 * ldy + kb;
+        base[2] = Yhi + c0 * ldy + kb; base[3] = Ylo + c0 * ldy + kb;
+        rows[0] = rows[1] = rowsI; rows[2] = rows[3] = rowsJ;
+    } else {
+        base[0] = Yhi + r0 * ldy + kb; base[1] = Yhi + c0 * ldy + kb;
+        rows[0] = rowsI; rows[1] = rowsJ;
+    }
+    for (int o = 0; o < 4; ++o) ld[o] = ldy;
+    f32x16_t acc[TM][TM];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = f32x16_t{};
+    mfma_mainloop<BM, NOPS, NPROD>(base, ld, rows, klen, acc, lds);
+    float *dst;
+    int64_t ldd;
+    if (s == 0) {
+        dst = C + int64_t(h) * hd * ldc;
+        ldd = ldc;
+    } else {
+        dst = P + (int64_t(s - 1) * n_blocks + h) * hd * hd;
+        ldd = hd;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TM; ++tn) {
+            const int64_t rb = int64_t(I) * BM + wm * (BM / 2) + tm * 32;
+            const int64_t cc = int64_t(J) * BM + wn * (BM / 2) + tn * 32 + acc_col(lane);
+            add_upper_tile(acc[tm][tn], rb, cc, lane, hd, dst, ldd);
+        }
+}
+
+// W^T (d_out x d_in) from W (d_in x d_out, ldw)
+__global__ void __launch_bounds__(256) k_transpose_bf16(const bf16_t *__restrict__ W, int64_t ldw, int64_t rows,
+                                                        int64_t cols, bf16_t *__restrict__ Wt, int64_t ldt) {
+    __shared__ bf16_t tile[64][65];
+    const int64_t r0 = int64_t(blockIdx.y) * 64, c0 = int64_t(blockIdx.x) * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int rr = e / 64, cc = e % 64;
+        if (r0 + rr < rows && c0 + cc < cols) tile[rr][cc] = W[(r0 + rr) * ldw + c0 + cc];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int cc = e / 64, rr = e % 64;
+        if (r0 + rr < rows && c0 + cc < cols) Wt[(c0 + cc) * ldt + r0 + rr] = tile[rr][cc];
+    }
+}
+
+// Y^T = X^T for a chunk of tc tokens; columns tc .. ldy-1 are zero.
+__global__ void __launch_bounds__(256) k_chunk_transpose(const bf16_t *__restrict__ X, int64_t ldx, int64_t tc,
+                                                         int64_t d, bf16_t *__restrict__ Yt, int64_t ldy) {
+    __shared__ bf16_t tile[64][65];
+    const int64_t t0 = int64_t(blockIdx.y) * 64, c0 = int64_t(blockIdx.x) * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int rr = e / 64, cc = e % 64;
+        tile[rr][cc] = (t0 + rr < tc && c0 + cc < d) ? X[(t0 + rr) * ldx + c0 + cc] : bf16_t(0);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int cc = e / 64, rr = e % 64;
+        if (c0 + cc < d && t0 + rr < ldy) Yt[(c0 + cc) * ldy + t0 + rr] = tile[rr][cc];
+    }
+}
+
+__global__ void k_fill_f32(float *__restrict__ p, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = 0.f;
+}
+
+// C[upper] += P_1 + ... + P_{S-1} in split order
+__global__ void k_add_partials(float *__restrict__ C, int64_t ldc, const float *__restrict__ P, int nsplit,
+                               int64_t hd, int32_t n_blocks) {
+    const int64_t per = hd * hd;
+    const int64_t total = per * n_blocks;
+    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total; e += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t h = e / per, rr = (e % per) / hd, cc = e % hd;
+        if (rr > cc) continue;
+        float acc = C[h * hd * ldc + rr * ldc + cc];
+        for (int s = 0; s < nsplit - 1; ++s) acc += P[int64_t(s) * total + e];
+        C[h * hd * ldc + rr * ldc + cc] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------------------------
+struct MfmaPlan {
+    int bm;         // SYRK block tile
+    int64_t tcmax;  // tokens per chunk
+    int64_t ldy;    // leading dim of Y^T (multiple of 256)
+    int nsplit;     // token splits of the SYRK
+    int64_t n_upper;
+};
+
+static MfmaPlan plan(int64_t n_tok, int64_t d_out, int32_t n_blocks) {
+    MfmaPlan p;
+    const int64_t hd = d_out / n_blocks;
+    p.bm = hd >= 256 ? 256 : 128;
+    p.tcmax = std::min<int64_t>(MFMA_CHUNK, n_tok);
+    p.ldy = (p.tcmax + 255) / 256 * 256;
+    const int64_t th = (hd + p.bm - 1) / p.bm;
+    p.n_upper = th * (th + 1) / 2;
+    const int64_t tiles = p.n_upper * n_blocks;
+    // smallest split count that fills >= 90% of the last wave of 256 single-block CUs, while
+    // keeping at least 8 k-steps per split
+    const int64_t ksteps = p.ldy / MK;
+    p.nsplit = 1;
+    for (int s = 1; s <= 16; ++s) {
+        if (s > 1 && ksteps / s < 8) break;
+        const int64_t blocks = tiles * s;
+        const int64_t waves = (blocks + 255) / 256;
+        p.nsplit = s;
+        if (double(blocks) / double(waves * 256) >= 0.9) break;
+    }
+    return p;
+}
+
+bool cov_mfma_shape_ok(int64_t d_in, int64_t d_out, int32_t n_blocks) {
+    return d_in % 8 == 0 && d_out > 0 && n_blocks > 0;
+}
+
+bool cov_mfma_supported(lrc_dtype x_t, const void *X, int64_t ldx, const void *W, int64_t ldw, int64_t d_in,
+                        int64_t d_out, int32_t n_blocks) {
+    (void)W;
+    (void)ldw;
+    return x_t == LRC_BF16 && cov_mfma_shape_ok(d_in, d_out, n_blocks) && ldx % 8 == 0 &&
+           (reinterpret_cast<uintptr_t>(X) % 16) == 0;
+}
+
+size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks) {
+    const MfmaPlan p = plan(n_tok, d_out, n_blocks);
+    const int64_t hd = d_out / n_blocks;
+    Counter c;
+    if (has_w) c.carve<bf16_t>(size_t(d_out) * size_t(d_in));
+    c.carve<bf16_t>(size_t(d_out) * size_t(p.ldy));
+    if (has_w) c.carve<bf16_t>(size_t(d_out) * size_t(p.ldy));
+    c.carve<float>(size_t(p.nsplit - 1) * size_t(n_blocks) * size_t(hd) * size_t(hd) + 1);
+    // the generic path's buffer, used when the call's pointers are not aligned
+    c.carve<float>(size_t(d_out) * size_t(std::min<int64_t>(4096, n_tok)));
+    return c.off;
+}
+
+lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
+    const MfmaPlan p = plan(a.n_tok, a.d_out, a.n_blocks);
+    const int64_t hd = a.d_out / a.n_blocks;
+    const bool has_w = a.W != nullptr;
+    Carver cv(ws, ws_bytes);
+    bf16_t *Wt = has_w ? cv.carve<bf16_t>(size_t(a.d_out) * size_t(a.d_in)) : nullptr;
+    bf16_t *Yhi = cv.carve<bf16_t>(size_t(a.d_out) * size_t(p.ldy));
+    bf16_t *Ylo = has_w ? cv.carve<bf16_t>(size_t(a.d_out) * size_t(p.ldy)) : nullptr;
+    const size_t pn = size_t(p.nsplit - 1) * size_t(a.n_blocks) * size_t(hd) * size_t(hd);
+    float *P = cv.carve<float>(pn + 1);
+    if (!P || !Yhi || (has_w && (!Wt || !Ylo))) return fail(LRC_ERR_WORKSPACE, "covariance workspace too small");
+    const bf16_t *X = static_cast<const bf16_t *>(a.X);
+    if (has_w) {
+        dim3 g(cdiv(a.d_out, 64), cdiv(a.d_in, 64));
+        hipLaunchKernelGGL(k_transpose_bf16, g, dim3(256), 0, s, static_cast<const bf16_t *>(a.W), a.ldw, a.d_in,
+                           a.d_out, Wt, a.d_in);
+        LRC_LAUNCH_CHECK("k_transpose_bf16");
+    }
+    if (pn) {
+        hipLaunchKernelGGL(k_fill_f32, dim3(1024), dim3(256), 0, s, P, int64_t(pn));
+        LRC_LAUNCH_CHECK("k_fill_f32");
+    }
+    for (int64_t t0 = 0; t0 < a.n_tok; t0 += p.tcmax) {
+        const int64_t tc = std::min(p.tcmax, a.n_tok - t0);
+        const int64_t ktot = (tc + MK - 1) / MK * MK;
+        if (has_w) {
+            dim3 g(cdiv(a.d_out, 256), cdiv(ktot, 256));
+            hipLaunchKernelGGL(k_cov_gemm_y<256>, g, dim3(MFMA_THREADS), 0, s, Wt, a.d_in, a.d_out, X + t0 * a.ldx,
+                               a.ldx, tc, Yhi, Ylo, p.ldy);
+            LRC_LAUNCH_CHECK("k_cov_gemm_y");
+        } else {
+            dim3 g(cdiv(a.d_out, 64), cdiv(ktot, 64));
+            hipLaunchKernelGGL(k_chunk_transpose, g, dim3(256), 0, s, X + t0 * a.ldx, a.ldx, tc, a.d_out, Yhi, p.ldy);
+            LRC_LAUNCH_CHECK("k_chunk_transpose");
+        }
+        const int64_t kchunk = ((ktot + p.nsplit - 1) / p.nsplit + MK - 1) / MK * MK;
+        dim3 g(unsigned(p.n_upper), unsigned(a.n_blocks), unsigned(p.nsplit));
+        if (p.bm == 256) {
+            if (has_w)
+                hipLaunchKernelGGL((k_cov_syrk<256, 3>), g, dim3(MFMA_THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk, hd,
+                                   a.C, a.ldc, P, a.n_blocks);
+            else
+                hipLaunchKernelGGL((k_cov_syrk<256, 1>), g, dim3(MFMA_THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk, hd,
+                                   a.C, a.ldc, P, a.n_blocks);
+        } else {
+            if (has_w)
+                hipLaunchKernelGGL((k_cov_syrk<128, 3>), g, dim3(MFMA_THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk, hd,
+                                   a.C, a.ldc, P, a.n_blocks);
+            else
+                hipLaunchKernelGGL((k_cov_syrk<128, 1>), g, dim3(MFMA_THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk, hd,
+                                   a.C, a.ldc, P, a.n_blocks);
+        }
+        LRC_LAUNCH_CHECK("k_cov_syrk");
+    }
+    if (p.nsplit > 1) {
+        hipLaunchKernelGGL(k_add_partials, dim3(2048), dim3(256), 0, s, a.C, a.ldc, P, p.nsplit, hd, a.n_blocks);
+        LRC_LAUNCH_CHECK("k_add_partials");
+    }
+    return LRC_OK;
+}
+
+}  // namespace lrc

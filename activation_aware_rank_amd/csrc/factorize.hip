@@ -1,0 +1,124 @@
+// Factor projection of the closed-form truncation (Swift-SVD page, section 2-ga:
+// W_k = (W V_k) V_k^T): A = W V[:, :k] (or W^T V[:, :k]) and B = V[:, :k]^T.
+// Products and sums in fp64 (inputs widened exactly), A rounded once to fp32.
+#include "lrc_internal.h"
+
+namespace lrc {
+
+constexpr int FT = 64;  // output tile
+constexpr int FK = 16;  // contraction step
+
+template <class WT>
+__device__ __forceinline__ double wload(const WT *p, int64_t i);
+template <>
+__device__ __forceinline__ double wload<bf16_t>(const bf16_t *p, int64_t i) { return double(bf16_to_f32(p[i])); }
+template <>
+__device__ __forceinline__ double wload<float>(const float *p, int64_t i) { return double(p[i]); }
+template <>
+__device__ __forceinline__ double wload<double>(const double *p, int64_t i) { return p[i]; }
+
+// A[i][j] = sum_r Wop[i][r] V[r][j]; Wop = W (TRANS 0: i < d_in, r < d_out) or W^T (TRANS 1)
+template <class WT, int TRANS>
+__global__ void __launch_bounds__(256) k_factor_gemm(const WT *__restrict__ W, int64_t ldw, int64_t d_in, int64_t d_out,
+                                                     const float *__restrict__ V, int64_t ldv, int64_t k,
+                                                     float *__restrict__ A, int64_t lda, int64_t stride_w,
+                                                     int64_t stride_v, int64_t stride_a) {
+    __shared__ double Ws[FK][FT + 1];
+    __shared__ double Vs[FK][FT + 1];
+    const int64_t b = blockIdx.z;
+    W += b * stride_w;
+    V += b * stride_v;
+    A += b * stride_a;
+    const int64_t M = TRANS ? d_out : d_in;  // rows of A
+    const int64_t R = TRANS ? d_in : d_out;  // contraction length
+    const int64_t i0 = int64_t(blockIdx.y) * FT, j0 = int64_t(blockIdx.x) * FT;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    double acc[4][4] = {};
+    for (int64_t r0 = 0; r0 < R; r0 += FK) {
+        for (int e = threadIdx.x; e < FK * FT; e += 256) {
+            int rr, ii;
+            if (TRANS) { rr = e / FT; ii = e % FT; }   // W[r][i] contiguous in i
+            else { ii = e / FK; rr = e % FK; }         // W[i][r] contiguous in r
+            const int64_t r = r0 + rr, i = i0 + ii;
+            double wv = 0.0;
+            if (r < R && i < M) wv = TRANS ? wload(W, r * ldw + i) : wload(W, i * ldw + r);
+            Ws[rr][ii] = wv;
+            const int vr = e / FT, vj = e % FT;
+            const int64_t rv = r0 + vr, jj = j0 + vj;
+            Vs[vr][vj] = (rv < R && jj < k) ? double(V[rv * ldv + jj]) : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rr = 0; rr < FK; ++rr) {
+            double a[4], v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a[u] = Ws[rr][ty * 4 + u];
+                v[u] = Vs[rr][tx * 4 + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc[u][w] = fma(a[u], v[w], acc[u][w]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int64_t i = i0 + ty * 4 + u, j = j0 + tx * 4 + w;
+            if (i < M && j < k) A[i * lda + j] = float(acc[u][w]);
+        }
+}
+
+// B[q][r] = V[r][q], q < k, r < rows
+__global__ void __launch_bounds__(256) k_factor_bt(const float *__restrict__ V, int64_t ldv, int64_t rows, int64_t k,
+                                                   float *__restrict__ B, int64_t ldb, int64_t stride_v, int64_t stride_b) {
+    __shared__ float tile[64][65];
+    const int64_t b = blockIdx.z;
+    V += b * stride_v;
+    B += b * stride_b;
+    const int64_t r0 = int64_t(blockIdx.y) * 64, q0 = int64_t(blockIdx.x) * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int rr = e / 64, qq = e % 64;
+        if (r0 + rr < rows && q0 + qq < k) tile[rr][qq] = V[(r0 + rr) * ldv + q0 + qq];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int qq = e / 64, rr = e % 64;
+        if (r0 + rr < rows && q0 + qq < k) B[(q0 + qq) * ldb + r0 + rr] = tile[rr][qq];
+    }
+}
+
+template <class WT>
+static void launch_gemm(const FactorizeArgs &a, hipStream_t s) {
+    const int64_t M = a.trans_w ? a.d_out : a.d_in;
+    dim3 g(cdiv(a.k, FT), cdiv(M, FT), unsigned(a.batch));
+    const WT *W = static_cast<const WT *>(a.W);
+    if (a.trans_w)
+        hipLaunchKernelGGL((k_factor_gemm<WT, 1>), g, dim3(256), 0, s, W, a.ldw, a.d_in, a.d_out, a.V, a.ldv, a.k, a.A,
+                           a.lda, a.stride_w, a.stride_v, a.stride_a);
+    else
+        hipLaunchKernelGGL((k_factor_gemm<WT, 0>), g, dim3(256), 0, s, W, a.ldw, a.d_in, a.d_out, a.V, a.ldv, a.k, a.A,
+                           a.lda, a.stride_w, a.stride_v, a.stride_a);
+}
+
+lrc_status factorize_run(const FactorizeArgs &a, hipStream_t s) {
+    if (a.batch > 65535) return fail(LRC_ERR_ARG, "batch too large");
+    switch (a.w_t) {
+        case LRC_BF16: launch_gemm<bf16_t>(a, s); break;
+        case LRC_F32: launch_gemm<float>(a, s); break;
+        case LRC_F64: launch_gemm<double>(a, s); break;
+    }
+    LRC_LAUNCH_CHECK("k_factor_gemm");
+    if (a.B) {
+        const int64_t rows = a.trans_w ? a.d_in : a.d_out;
+        dim3 g(cdiv(a.k, 64), cdiv(rows, 64), unsigned(a.batch));
+        hipLaunchKernelGGL(k_factor_bt, g, dim3(256), 0, s, a.V, a.ldv, rows, a.k, a.B, a.ldb, a.stride_v, a.stride_b);
+        LRC_LAUNCH_CHECK("k_factor_bt");
+    }
+    return LRC_OK;
+}
+
+}  // namespace lrc

@@ -1,0 +1,307 @@
+"""Thin ctypes binding of liblrc (include/lrc.h), with the same entry-point names.
+
+Only argument marshalling happens here: tensors are checked for device, dtype and layout, their
+data pointers, leading dimensions and torch's current stream are passed to the C ABI, and
+workspace is allocated as a torch uint8 tensor.  Every computation runs in the HIP kernels of
+liblrc.so.  Importing this module fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblrc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("liblrc.so is not built; run `python -m activation_aware_rank_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+LRC_BF16, LRC_F32, LRC_F64 = 0, 1, 2
+STATUS = {0: "LRC_OK", 1: "LRC_ERR_ARG", 2: "LRC_ERR_DTYPE", 3: "LRC_ERR_WORKSPACE", 4: "LRC_ERR_HIP",
+          5: "LRC_ERR_UNIMPLEMENTED"}
+INFO = {0: "ok", 1: "non-finite input", 2: "no convergence", 3: "not positive definite",
+        4: "mandatory ranks exceed the budget", 5: "negative or NaN score"}
+
+_vp, _i64, _i32, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_int
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_abi = _sig("lrc_abi_version", _int)
+_status_string = _sig("lrc_status_string", ctypes.c_char_p, _int)
+_last_error = _sig("lrc_last_error", ctypes.c_char_p)
+_cov_ws = _sig("lrc_cov_accumulate_workspace", _sz, _int, _i64, _i64, _int, _i64, _i32)
+_cov = _sig("lrc_cov_accumulate", _int, _vp, _int, _i64, _i64, _i64, _vp, _int, _i64, _i64, _i32, _vp, _i64, _vp, _sz,
+            _vp, _vp)
+_eigh_ws = _sig("lrc_eigh_workspace", _sz, _i64, _i64, _i64, _int)
+_eigh = _sig("lrc_eigh", _int, _vp, _i64, _i64, _i64, _i64, _int, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp, _vp)
+_err = _sig("lrc_error_curve", _int, _vp, _i64, _i64, _vp, _vp)
+_fac = _sig("lrc_factorize", _int, _vp, _int, _i32, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64,
+            _i64, _vp, _i64, _i64, _vp)
+_fsh_ws = _sig("lrc_fisher_scores_workspace", _sz, _i32, _vp)
+_fsh = _sig("lrc_fisher_scores", _int, _i32, _vp, _vp, _vp, _int, _vp, _vp, _sz, _vp, _vp)
+_alc_ws = _sig("lrc_allocate_ranks_workspace", _sz, _i32, _i64)
+_alc = _sig("lrc_allocate_ranks", _int, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp, _vp)
+_chol_ws = _sig("lrc_cholesky_workspace", _sz, _i64)
+_chol = _sig("lrc_cholesky", _int, _vp, _i64, _i64, _vp, _sz, _vp, _vp)
+_trmm = _sig("lrc_trmm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp)
+_trsm = _sig("lrc_trsm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp)
+
+EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_accumulate_workspace",
+            "lrc_cov_accumulate", "lrc_eigh_workspace", "lrc_eigh", "lrc_error_curve", "lrc_factorize",
+            "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_allocate_ranks_workspace",
+            "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm", "lrc_trsm")
+
+
+class LrcError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s: %s" % (STATUS.get(code, str(code)), msg))
+        self.code = code
+
+
+def _check(code: int):
+    if code != 0:
+        raise LrcError(code, (_last_error() or b"").decode())
+
+
+def lrc_abi_version() -> int:
+    return _abi()
+
+
+def lrc_status_string(code: int) -> str:
+    return _status_string(code).decode()
+
+
+def lrc_last_error() -> str:
+    return (_last_error() or b"").decode()
+
+
+# ----------------------------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------------------------
+_DT = {torch.bfloat16: LRC_BF16, torch.float32: LRC_F32, torch.float64: LRC_F64}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return _DT[t.dtype]
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a matrix (or batch of matrices) with a contiguous last axis."""
+    _dev(t, name)
+    if t.dim() < 2 or t.stride(-1) != 1:
+        raise ValueError("%s must be a matrix with a contiguous last dimension" % name)
+    return t.stride(-2)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(nbytes: int, device, ws=None):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() >= nbytes:
+        return ws, ws.numel()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _info(info, n, device):
+    if info is None:
+        info = torch.empty(n, dtype=torch.int32, device=device)
+    if info.dtype != torch.int32 or info.numel() < n:
+        raise ValueError("info must be int32 with at least %d entries" % n)
+    return info
+
+
+# ----------------------------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------------------------
+def lrc_cov_accumulate_workspace(x_dtype: int, n_tok: int, d_in: int, has_w: bool, d_out: int, n_blocks: int = 1) -> int:
+    return _cov_ws(x_dtype, n_tok, d_in, int(bool(has_w)), d_out, n_blocks)
+
+
+def lrc_cov_accumulate(X: torch.Tensor, W: torch.Tensor | None, C: torch.Tensor, n_blocks: int = 1, info=None,
+                       ws=None, stream=None) -> torch.Tensor:
+    """C[upper] += (X W)^T (X W).  X (n_tok, d_in); W (d_in, d_out) or None; C (d_out, d_out) fp32,
+    or (n_blocks, hd, hd) for the per-head diagonal blocks.  Returns the int32 info tensor."""
+    ldx = _rows(X, "X")
+    n_tok, d_in = X.shape
+    if W is not None:
+        ldw = _rows(W, "W")
+        d_out = W.shape[1]
+        wt = _dt(W)
+    else:
+        ldw, d_out, wt = 0, d_in, _dt(X)
+    ldc = _rows(C, "C")
+    if C.dtype != torch.float32:
+        raise TypeError("C must be float32")
+    nbytes = lrc_cov_accumulate_workspace(_dt(X), n_tok, d_in, W is not None, d_out, n_blocks)
+    w, wn = _workspace(nbytes, X.device, ws)
+    info = _info(info, 1, X.device)
+    _check(_cov(_ptr(X), _dt(X), n_tok, d_in, ldx, _ptr(W), wt, d_out, ldw, n_blocks, _ptr(C), ldc, _ptr(w), wn,
+                _ptr(info), _stream(stream)))
+    return info
+
+
+def lrc_eigh_workspace(n: int, batch: int, n_vec: int, prec: int = LRC_F32) -> int:
+    return _eigh_ws(n, batch, n_vec, prec)
+
+
+def lrc_eigh(C: torch.Tensor, n_vec: int, prec: int = LRC_F32, lam=None, V=None, info=None, ws=None, stream=None):
+    """Eigenpairs of the symmetric fp32 matrix (or batch) C, upper triangle read.
+    Returns (lambda fp64 (batch, n) descending, V fp32 (batch, n, n_vec), info int32 (batch,))."""
+    ldc = _rows(C, "C")
+    squeeze = C.dim() == 2
+    Cb = C.unsqueeze(0) if squeeze else C
+    batch, n = Cb.shape[0], Cb.shape[1]
+    stride_c = Cb.stride(0)
+    dev = C.device
+    if lam is None:
+        lam = torch.empty(batch, n, dtype=torch.float64, device=dev)
+    if V is None and n_vec > 0:
+        V = torch.empty(batch, n, n_vec, dtype=torch.float32, device=dev)
+    ldv = _rows(V, "V") if V is not None else max(n_vec, 1)
+    stride_v = (V.stride(0) if V.dim() == 3 else 0) if V is not None else 0
+    nbytes = lrc_eigh_workspace(n, batch, n_vec, prec)
+    w, wn = _workspace(nbytes, dev, ws)
+    info = _info(info, batch, dev)
+    _check(_eigh(_ptr(C), n, ldc, batch, stride_c, prec, _ptr(lam), _ptr(V), ldv, n_vec, stride_v, _ptr(w), wn,
+                 _ptr(info), _stream(stream)))
+    if squeeze:
+        return lam[0], (V[0] if V is not None else None), info
+    return lam, V, info
+
+
+def lrc_error_curve(lam: torch.Tensor, eps=None, stream=None) -> torch.Tensor:
+    """eps[b][k] = sum of lam[b][i] for i >= k, k = 0..n (fp64)."""
+    _dev(lam, "lambda")
+    if lam.dtype != torch.float64 or not lam.is_contiguous():
+        raise ValueError("lambda must be contiguous float64")
+    n = lam.shape[-1]
+    batch = lam.numel() // n
+    if eps is None:
+        eps = torch.empty(lam.shape[:-1] + (n + 1,), dtype=torch.float64, device=lam.device)
+    _check(_err(_ptr(lam), n, batch, _ptr(eps), _stream(stream)))
+    return eps
+
+
+def lrc_factorize(W: torch.Tensor, V: torch.Tensor, k: int, A: torch.Tensor, B: torch.Tensor | None = None,
+                  trans_w: int = 0, d_in: int | None = None, d_out: int | None = None, batch: int = 1,
+                  stride_w: int = 0, stride_v: int = 0, stride_a: int = 0, stride_b: int = 0, stream=None):
+    """A = W V[:, :k] (trans_w 0) or W^T V[:, :k] (trans_w 1); B = V[:, :k]^T when given.
+    Batched matrices are addressed by element strides (a per-head W_h is a column slice)."""
+    ldw, ldv, lda = _rows(W, "W"), _rows(V, "V"), _rows(A, "A")
+    ldb = _rows(B, "B") if B is not None else 0
+    d_in = W.shape[-2] if d_in is None else d_in
+    d_out = W.shape[-1] if d_out is None else d_out
+    if V.dtype != torch.float32 or A.dtype != torch.float32 or (B is not None and B.dtype != torch.float32):
+        raise TypeError("V, A and B must be float32")
+    _check(_fac(_ptr(W), _dt(W), trans_w, d_in, d_out, ldw, _ptr(V), ldv, k, batch, stride_w, stride_v, _ptr(A), lda,
+                stride_a, _ptr(B), ldb, stride_b, _stream(stream)))
+    return A, B
+
+
+def lrc_fisher_scores(Gs, Ws, alpha=None, info=None, ws=None, stream=None):
+    """alpha[m] = sum (G_m * W_m)^2 in fp64 for lists of same-dtype contiguous GPU tensors."""
+    n = len(Gs)
+    if n != len(Ws) or n == 0:
+        raise ValueError("G and W lists must have the same non-zero length")
+    for g, w in zip(Gs, Ws):
+        _dev(g, "G")
+        _dev(w, "W")
+        if g.numel() != w.numel() or not g.is_contiguous() or not w.is_contiguous() or g.dtype != w.dtype:
+            raise ValueError("G[m] and W[m] must be contiguous, same size and dtype")
+    dev = Gs[0].device
+    gp = (ctypes.c_void_p * n)(*[g.data_ptr() for g in Gs])
+    wp = (ctypes.c_void_p * n)(*[w.data_ptr() for w in Ws])
+    ne = (ctypes.c_int64 * n)(*[g.numel() for g in Gs])
+    nbytes = _fsh_ws(n, ne)
+    w, wn = _workspace(nbytes, dev, ws)
+    if alpha is None:
+        alpha = torch.empty(n, dtype=torch.float64, device=dev)
+    info = _info(info, n, dev)
+    _check(_fsh(n, gp, wp, ne, _dt(Gs[0]), _ptr(alpha), _ptr(w), wn, _ptr(info), _stream(stream)))
+    return alpha, info
+
+
+def lrc_fisher_scores_workspace(numel) -> int:
+    ne = (ctypes.c_int64 * len(numel))(*[int(x) for x in numel])
+    return _fsh_ws(len(numel), ne)
+
+
+def lrc_allocate_ranks_workspace(n_mats: int, n_items: int) -> int:
+    return _alc_ws(n_mats, n_items)
+
+
+def lrc_cholesky_workspace(n: int) -> int:
+    return _chol_ws(n)
+
+
+def lrc_allocate_ranks(alpha, lambda_packed, offsets, eps0, cost, budget: int, k_min=None, k_out=None, info=None,
+                       ws=None, stream=None):
+    """Greedy rank allocation; all arrays device tensors (alpha, lambda_packed, eps0 fp64; offsets,
+    cost int64; k_min int32 or None).  Returns (k int32 per matrix, info int32 (1,))."""
+    n = alpha.numel()
+    for t, nm in ((alpha, "alpha"), (eps0, "eps0"), (lambda_packed, "lambda")):
+        _dev(t, nm)
+        if t.dtype != torch.float64 or not t.is_contiguous():
+            raise ValueError("%s must be contiguous float64" % nm)
+    for t, nm in ((offsets, "offsets"), (cost, "cost")):
+        _dev(t, nm)
+        if t.dtype != torch.int64 or not t.is_contiguous():
+            raise ValueError("%s must be contiguous int64" % nm)
+    if k_min is not None and (k_min.dtype != torch.int32 or not k_min.is_cuda):
+        raise ValueError("k_min must be a GPU int32 tensor")
+    n_items = lambda_packed.numel()
+    dev = alpha.device
+    nbytes = _alc_ws(n, n_items)
+    w, wn = _workspace(nbytes, dev, ws)
+    if k_out is None:
+        k_out = torch.empty(n, dtype=torch.int32, device=dev)
+    info = _info(info, 1, dev)
+    _check(_alc(n, _ptr(alpha), _ptr(lambda_packed), _ptr(offsets), n_items, _ptr(eps0), _ptr(cost), _ptr(k_min),
+                int(budget), _ptr(k_out), _ptr(w), wn, _ptr(info), _stream(stream)))
+    return k_out, info
+
+
+def lrc_cholesky(A: torch.Tensor, info=None, ws=None, stream=None):
+    lda = _rows(A, "A")
+    n = A.shape[0]
+    w, wn = _workspace(_chol_ws(n), A.device, ws)
+    info = _info(info, 1, A.device)
+    _check(_chol(_ptr(A), n, lda, _ptr(w), wn, _ptr(info), _stream(stream)))
+    return A, info
+
+
+def lrc_trmm(side: int, trans: int, L: torch.Tensor, B: torch.Tensor, stream=None):
+    _check(_trmm(side, trans, B.shape[0], B.shape[1], _ptr(L), _rows(L, "L"), _ptr(B), _rows(B, "B"), _stream(stream)))
+    return B
+
+
+def lrc_trsm(side: int, trans: int, L: torch.Tensor, B: torch.Tensor, stream=None):
+    _check(_trsm(side, trans, B.shape[0], B.shape[1], _ptr(L), _rows(L, "L"), _ptr(B), _rows(B, "B"), _stream(stream)))
+    return B

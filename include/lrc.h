@@ -1,0 +1,218 @@
+/*
+ * lrc.h -- C ABI of liblrc, activation-aware low-rank compression on MI355X (gfx950).
+ *
+ * The method (Swift-SVD page, "Swift-SVD: Theoretical Optimality Meets Practical
+ * Efficiency in Low-Rank LLM Compression", section 2-ga): calibration activations X
+ * stream through Y = X W; the output covariance C = sum_t y_t^T y_t is accumulated; one
+ * symmetric eigendecomposition C = V diag(lambda) V^T gives the right singular vectors
+ * and squared singular values of Y; the closed-form optimum of rank k is
+ * W_k = (W V_k) V_k^T and its error eps_k = sum_{i>k} lambda_i.  Ranks are spread over
+ * many matrices by a greedy allocation under a parameter budget (LASER page, "LASER:
+ * Loss-Aware Singular-value Decomposition and Rank Allocation", method 2) weighted by the
+ * Fisher importance alpha = sum (G (.) W)^2 (FLRC page, "FLRC: Fine-grained Low-Rank
+ * Compressor for Efficient LLM Inference", method 1).
+ *
+ * Orientation: Y = X W with X n_tok x d_in (tokens x input features), W d_in x d_out,
+ * C d_out x d_out.  A PyTorch nn.Linear weight is the transpose of this W.
+ *
+ * Conventions shared by every entry point:
+ *  - All matrices are row-major with an explicit leading dimension (elements).
+ *  - All array pointers are DEVICE pointers unless marked (host).  Buffers are owned by
+ *    the caller; the library keeps no state between calls except per-device kernel
+ *    modules.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  A call only enqueues work
+ *    on that stream and returns; buffers must stay alive until the stream reaches it.
+ *  - Argument errors are reported synchronously as an lrc_status and then nothing is
+ *    launched.  lrc_last_error() gives a thread-local message for the last failure.
+ *  - Numerical outcomes found on the device are written to a caller-provided int32
+ *    `info` array in device memory (one entry per matrix unless stated), readable after
+ *    the stream has been synchronised:  0 ok, 1 non-finite input, 2 no convergence,
+ *    3 not positive definite, 4 mandatory ranks exceed the budget, 5 negative or NaN
+ *    score.  Entry points that write info set it on every call (0 when all is well).
+ *  - Workspace (`ws`, `ws_bytes`) is caller-allocated device memory of at least the size
+ *    returned by the matching *_workspace() query, 256-byte aligned; it may be NULL when
+ *    that size is 0.  Its contents are scratch and need no initialisation.
+ *  - Results are deterministic: identical inputs and launch give bit-identical outputs
+ *    (fixed-order reductions, no floating-point atomics).
+ */
+#ifndef LRC_H
+#define LRC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LRC_ABI_VERSION 1
+
+typedef enum {
+    LRC_OK = 0,
+    LRC_ERR_ARG = 1,           /* bad size, stride, pointer or flag */
+    LRC_ERR_DTYPE = 2,         /* dtype not supported by this entry point */
+    LRC_ERR_WORKSPACE = 3,     /* ws NULL or smaller than the query says */
+    LRC_ERR_HIP = 4,           /* a HIP runtime call failed (message in lrc_last_error) */
+    LRC_ERR_UNIMPLEMENTED = 5  /* valid request this build does not implement */
+} lrc_status;
+
+typedef enum { LRC_BF16 = 0, LRC_F32 = 1, LRC_F64 = 2 } lrc_dtype;
+
+enum {
+    LRC_INFO_OK = 0,
+    LRC_INFO_NONFINITE = 1,
+    LRC_INFO_NO_CONVERGENCE = 2,
+    LRC_INFO_NOT_PD = 3,
+    LRC_INFO_BUDGET = 4,
+    LRC_INFO_BAD_SCORE = 5
+};
+
+/* LRC_ABI_VERSION of the built library. */
+int lrc_abi_version(void);
+/* Static text for a status code. */
+const char *lrc_status_string(lrc_status s);
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char *lrc_last_error(void);
+
+/* ------------------------------------------------------------------------------------
+ * Covariance accumulation (Swift-SVD page, section 2-ga: the covariance of Y = XW is
+ * aggregated incrementally over calibration tokens).
+ *
+ *   C[upper] += (X W)^T (X W)   over the n_tok rows of X.
+ *
+ * X: n_tok x d_in, leading dim ldx >= d_in, dtype x_t (LRC_BF16 or LRC_F32).
+ * W: d_in x d_out, leading dim ldw >= d_out, dtype w_t (must equal x_t); W == NULL means
+ *    the identity (then d_out must equal d_in and C += X^T X).
+ * n_blocks == 1: C is d_out x d_out fp32 (ldc >= d_out); the upper triangle including the
+ *    diagonal is accumulated, the strict lower triangle is never read or written.
+ * n_blocks > 1 (per-head, WSVD page "WSVD: Weighted Low-Rank Approximation for Fast and
+ *    Efficient Execution of Low-Precision Vision-Language Models", methodology 1): only
+ *    the n_blocks diagonal blocks of width hd = d_out / n_blocks are formed; block h is
+ *    Y[:, h hd:(h+1) hd]^T Y[:, h hd:(h+1) hd], stored at C + h*hd*ldc as an hd x hd
+ *    matrix with leading dim ldc >= hd (upper triangle accumulated).
+ * Accumulates: the caller zeroes C before the first chunk.  Any chunking of the tokens
+ *    gives the same C up to fp32 rounding of the running sum.
+ * Arithmetic: bf16 inputs use bf16 MFMA with fp32 accumulation for Y; Y is then split
+ *    into bf16 hi + lo parts and C += hi^T hi + hi^T lo + lo^T hi (fp32 accumulation).
+ *    fp32 inputs use fp32 arithmetic throughout.
+ * info: one int32; set to 1 when the updated C has a non-finite diagonal entry.
+ * Errors: LRC_ERR_ARG for non-positive sizes, small leading dims, d_out % n_blocks != 0,
+ *    NULL X or C; LRC_ERR_DTYPE for other dtypes or x_t != w_t; LRC_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_cov_accumulate_workspace(lrc_dtype x_t, int64_t n_tok, int64_t d_in, int has_w,
+                                    int64_t d_out, int32_t n_blocks);
+lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64_t d_in, int64_t ldx,
+                              const void *W, lrc_dtype w_t, int64_t d_out, int64_t ldw, int32_t n_blocks,
+                              float *C, int64_t ldc, void *ws, size_t ws_bytes, int32_t *info,
+                              void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Symmetric eigendecomposition (Swift-SVD page, section 2-ga: one eigendecomposition of
+ * Y^T Y gives V and Sigma^2 of Y).
+ *
+ * C: batch matrices n x n fp32, matrix b at C + b*stride_c, leading dim ldc >= n; only the
+ *    upper triangle (incl. diagonal) is read.  Not modified.
+ * lambda: batch x n fp64 (matrix b at lambda + b*n), all eigenvalues, descending.
+ * V: batch x n x n_vec fp32 (matrix b at V + b*stride_v, leading dim ldv >= n_vec): column
+ *    j is the unit eigenvector of lambda[j], j < n_vec, with its entry of largest
+ *    magnitude positive (first index on ties).  V may be NULL when n_vec == 0.
+ * prec: working precision, LRC_F32 or LRC_F64.
+ *    n <= 128: one-sided Jacobi, one matrix per workgroup held in LDS, in prec.
+ *    n > 128: Householder tridiagonalisation and back-transformation in prec; the
+ *    tridiagonal eigenproblem (bisection, inverse iteration) always in fp64.
+ * info: batch int32: 2 when the Jacobi sweeps did not converge, 1 for non-finite input.
+ * Errors: LRC_ERR_ARG (sizes, strides, n_vec > n), LRC_ERR_DTYPE (prec), LRC_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype prec);
+lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64_t stride_c,
+                    lrc_dtype prec, double *lambda, float *V, int64_t ldv, int64_t n_vec,
+                    int64_t stride_v, void *ws, size_t ws_bytes, int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Error curve (Swift-SVD page, section 2-ga: the closed-form minimal error eps*_k).
+ *
+ *   eps[b][k] = sum_{i >= k} lambda[b][i]  (0-based lambda; = sum of the eigenvalues
+ *   beyond the first k), k = 0..n, eps[b][n] = 0, summed from the smallest term.
+ * lambda: batch x n fp64; eps: batch x (n+1) fp64.
+ * ------------------------------------------------------------------------------------ */
+lrc_status lrc_error_curve(const double *lambda, int64_t n, int64_t batch, double *eps, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Factor projection (Swift-SVD page, section 2-ga: W_k = (W V_k) V_k^T).
+ *
+ * trans_w == 0:  A = W V[:, :k]   (A: d_in x k),  W d_in x d_out, V d_out x (>= k).
+ * trans_w == 1:  A = W^T V[:, :k] (A: d_out x k), W d_in x d_out, V d_in x (>= k).
+ * B = V[:, :k]^T (k x rows(V)) when B != NULL.
+ * W: dtype w_t (LRC_BF16, LRC_F32 or LRC_F64), leading dim ldw >= d_out; V fp32 with
+ *    leading dim ldv >= k; A fp32 (lda >= k); B fp32 (ldb >= rows of V).
+ * Batched: matrix b uses W + b*stride_w, V + b*stride_v, A + b*stride_a, B + b*stride_b
+ *    (element offsets; a per-head W_h is a column slice: stride_w = head width).
+ * Arithmetic: products and sums in fp64 (fp64 MFMA), A rounded once to fp32.
+ * ------------------------------------------------------------------------------------ */
+lrc_status lrc_factorize(const void *W, lrc_dtype w_t, int32_t trans_w, int64_t d_in, int64_t d_out,
+                         int64_t ldw, const float *V, int64_t ldv, int64_t k, int64_t batch,
+                         int64_t stride_w, int64_t stride_v, float *A, int64_t lda, int64_t stride_a,
+                         float *B, int64_t ldb, int64_t stride_b, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Fisher importance (FLRC page, method 1: alpha_{l,p} = sum_i (G_{l,p}[i] W_{l,p}[i])^2).
+ *
+ * G, W, numel: (host) arrays of n_mats device pointers / element counts; G[m] and W[m]
+ *    hold numel[m] contiguous elements of dtype t (LRC_BF16 or LRC_F32).
+ * alpha: n_mats fp64 (device).  Products are exact in fp32 for bf16 inputs; squares and
+ *    sums in fp64 with a fixed-order reduction.
+ * info: n_mats int32, 1 when alpha[m] is not finite.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_fisher_scores_workspace(int32_t n_mats, const int64_t *numel /* host */);
+lrc_status lrc_fisher_scores(int32_t n_mats, const void *const *G /* host */, const void *const *W /* host */,
+                             const int64_t *numel /* host */, lrc_dtype t, double *alpha, void *ws,
+                             size_t ws_bytes, int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Greedy global rank allocation under a parameter budget (LASER page, method 2: take the
+ * singular components of highest importance per parameter cost until the budget is
+ * reached; FLRC page, method 1: Fisher importance per projection; Swift-SVD page, section
+ * 2-na: a guaranteed minimum rank per layer).
+ *
+ * For matrix m (0 <= m < n_mats), candidates are ranks k = k_min[m]+1 .. K_m with
+ * K_m = offsets[m+1] - offsets[m]; candidate k has cost cost[m] parameters (d_in + d_out)
+ * and priority p = w_m * max(lambda_m[k-1], 0), w_m = alpha[m] / (eps0[m] * cost[m])
+ * (w_m = 0 when eps0[m] == 0), each step one IEEE fp64 multiply or divide.  Candidates are
+ * ordered by p descending, then m ascending, then k ascending; the mandatory
+ * sum_m k_min[m] cost[m] is charged first; candidates are taken in order while they fit
+ * in the budget, stopping at the first that does not.  k_out[m] = k_min[m] + number taken.
+ *
+ * alpha, eps0: n_mats fp64; lambda_packed: fp64, matrix m's lambda at offsets[m];
+ * offsets: n_mats+1 int64 (device); cost: n_mats int64 (> 0); k_min: n_mats int32 or NULL
+ * (all 0); n_items = offsets[n_mats] (host copy, for launch sizing); k_out: n_mats int32.
+ * info: one int32: 4 mandatory ranks exceed the budget, 5 an alpha/eps0 negative or NaN.
+ * Bit-exact: the result depends only on the fp64 priorities, computed as stated.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_allocate_ranks_workspace(int32_t n_mats, int64_t n_items);
+lrc_status lrc_allocate_ranks(int32_t n_mats, const double *alpha, const double *lambda_packed,
+                              const int64_t *offsets, int64_t n_items, const double *eps0,
+                              const int64_t *cost, const int32_t *k_min, int64_t budget_params,
+                              int32_t *k_out, void *ws, size_t ws_bytes, int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Curvature-weighted variant (LASER page, method 1: W~ = S_x W S_g with S_x, S_g Cholesky
+ * factors of the activation and gradient covariances; SVD of W~; factors mapped back).
+ *
+ * lrc_cholesky: in-place lower Cholesky factor of the n x n fp64 SPD matrix A (lower
+ *   triangle read; strict upper triangle set to 0).  info: 3 when a pivot is not positive.
+ * lrc_trmm: B <- op(L) B (side 0, B m x n, L m x m) or B <- B op(L) (side 1, L n x n),
+ *   op(L) = L (trans 0) or L^T (trans 1), L lower triangular fp64.
+ * lrc_trsm: B <- op(L)^{-1} B (side 0) or B <- B op(L)^{-1} (side 1), same conventions.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_cholesky_workspace(int64_t n);
+lrc_status lrc_cholesky(double *A, int64_t n, int64_t lda, void *ws, size_t ws_bytes, int32_t *info,
+                        void *stream);
+lrc_status lrc_trmm(int32_t side, int32_t trans, int64_t m, int64_t n, const double *L, int64_t ldl,
+                    double *B, int64_t ldb, void *stream);
+lrc_status lrc_trsm(int32_t side, int32_t trans, int64_t m, int64_t n, const double *L, int64_t ldl,
+                    double *B, int64_t ldb, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LRC_H */

@@ -265,13 +265,21 @@ def allocate_ranks(alpha, lams, eps0, cost, budget: int, k_min=None) -> tuple[np
     Sort the candidates by (p desc, m asc, k asc), subtract the mandatory sum k_min_m cost_m
     from the budget, take items in order while they fit and stop at the first that does not.
     Returns (k per matrix, info) with info 4 when the mandatory ranks exceed the budget and
-    5 when a score is negative or NaN.
+    5 when an alpha or eps0 is negative or NaN, a weight is not finite, a cost is not positive,
+    an eigenvalue is NaN or a minimum rank is outside [0, K_m].
     """
     M = len(lams)
     k_min = np.zeros(M, dtype=np.int64) if k_min is None else np.asarray(k_min, dtype=np.int64)
     cost = np.asarray(cost, dtype=np.int64)
     alpha = np.asarray(alpha, dtype=np.float64)
-    if np.any(~(alpha >= 0)):
+    eps0 = np.asarray(eps0, dtype=np.float64)
+    # a score that is not a non-negative number makes the order undefined: info 5
+    with np.errstate(all="ignore"):
+        w = np.where(eps0 != 0, alpha / (eps0 * cost.astype(np.float64)), 0.0)
+    bad = (np.any(~(alpha >= 0)) or np.any(~(eps0 >= 0)) or np.any(cost <= 0) or np.any(~np.isfinite(w))
+           or any(np.any(np.isnan(np.asarray(l, dtype=np.float64))) for l in lams)
+           or np.any(k_min < 0) or any(int(k_min[m]) > len(lams[m]) for m in range(M)))
+    if bad:
         return k_min.copy(), 5
     mandatory = int(np.sum(k_min * cost))
     if mandatory > budget:

@@ -1,0 +1,45 @@
+"""Helpers shared by the GPU parity tests (comparison metrics and host<->device moves only)."""
+import numpy as np
+import torch
+
+
+def dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """Stored host array ('bf16' uint16 bits, 'f32', 'f64', ints) -> GPU tensor with the same bytes."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def sin_theta_max(V_hat: np.ndarray, V: np.ndarray, k: int) -> float:
+    """sin of the largest principal angle between span(V_hat[:, :k]) and span(V[:, :k]) (fp64)."""
+    Vh = np.asarray(V_hat[:, :k], dtype=np.float64)
+    Vk = np.asarray(V[:, :k], dtype=np.float64)
+    R = Vh - Vk @ (Vk.T @ Vh)
+    return float(np.linalg.norm(R, 2))
+
+
+def check_lambda(lam_hat, lam, tol=1e-5):
+    err = np.max(np.abs(np.asarray(lam_hat) - np.asarray(lam))) / abs(lam[0])
+    assert err <= tol, "eigenvalue error %.3e lambda_max (limit %.1e)" % (err, tol)
+    return err
+
+
+def check_eps(eps_hat, eps, rel=1e-4, floor=1e-8):
+    """eps_k within rel relative where eps_k >= rel * eps_0; elsewhere within floor * eps_0."""
+    eps_hat = np.asarray(eps_hat, dtype=np.float64)
+    eps = np.asarray(eps, dtype=np.float64)
+    big = eps >= rel * eps[0]
+    e_big = np.max(np.abs(eps_hat[big] - eps[big]) / eps[big]) if big.any() else 0.0
+    e_small = np.max(np.abs(eps_hat[~big] - eps[~big])) / eps[0] if (~big).any() else 0.0
+    assert e_big <= rel, "eps relative error %.3e (limit %.1e)" % (e_big, rel)
+    assert e_small <= floor, "eps tail error %.3e eps_0 (limit %.1e)" % (e_small, floor)
+    return e_big, e_small
+
+
+def gap(lam, k):
+    return (lam[k - 1] - lam[k]) / lam[0]

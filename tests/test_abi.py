@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every entry point include/lrc.h declares, and rejects bad
+arguments synchronously (no kernel is launched on these paths, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrc.h")
+LIB = os.path.join(ROOT, "activation_aware_rank_amd", "liblrc.so")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lrc_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("liblrc.so not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_north_star_entry_points():
+    d = declared()
+    for name in ("lrc_cov_accumulate", "lrc_eigh", "lrc_factorize", "lrc_error_curve", "lrc_fisher_scores",
+                 "lrc_allocate_ranks"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    from activation_aware_rank_amd import lrc
+    assert sorted(lrc.EXPORTED) == declared()
+    for n in declared():
+        assert callable(getattr(lrc, n))
+
+
+def test_abi_version_and_status_strings(lib):
+    from activation_aware_rank_amd import lrc
+    assert lrc.lrc_abi_version() == 1
+    assert lrc.lrc_status_string(0) == "ok"
+    assert lrc.lrc_status_string(3).startswith("workspace")
+
+
+def test_argument_errors_are_synchronous():
+    from activation_aware_rank_amd import lrc
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    # NULL X
+    rc = lrc._cov(None, 0, 10, 8, 8, fake, 0, 8, 8, 1, fake, 8, None, 0, fake, None)
+    assert rc == 1 and "non-NULL" in lrc.lrc_last_error()
+    # ldx < d_in
+    rc = lrc._cov(fake, 0, 10, 8, 4, fake, 0, 8, 8, 1, fake, 8, None, 0, fake, None)
+    assert rc == 1 and "ldx" in lrc.lrc_last_error()
+    # n_blocks does not divide d_out
+    rc = lrc._cov(fake, 0, 10, 8, 8, fake, 0, 12, 12, 5, fake, 12, None, 0, fake, None)
+    assert rc == 1
+    # dtype mismatch
+    rc = lrc._cov(fake, 0, 10, 8, 8, fake, 1, 8, 8, 1, fake, 8, None, 0, fake, None)
+    assert rc == 2
+    # identity W with d_out != d_in
+    rc = lrc._cov(fake, 0, 10, 8, 8, None, 0, 16, 0, 1, fake, 16, None, 0, fake, None)
+    assert rc == 1
+    # workspace too small
+    need = lrc.lrc_cov_accumulate_workspace(0, 1000, 64, True, 64, 1)
+    assert need > 0
+    rc = lrc._cov(fake, 0, 1000, 64, 64, fake, 0, 64, 64, 1, fake, 64, fake, need - 1, fake, None)
+    assert rc == 3
+    # eigh: n_vec > n, bad prec
+    rc = lrc._eigh(fake, 10, 10, 1, 0, 1, fake, fake, 11, 11, 0, None, 0, fake, None)
+    assert rc == 1
+    rc = lrc._eigh(fake, 10, 10, 1, 0, 0, fake, fake, 4, 4, 0, None, 0, fake, None)
+    assert rc == 2
+    # factorize: k larger than V's rows
+    rc = lrc._fac(fake, 0, 0, 8, 4, 4, fake, 8, 5, 1, 0, 0, fake, 8, 0, None, 0, 0, None)
+    assert rc == 1
+    # error curve: n <= 0
+    assert lrc._err(fake, 0, 1, fake, None) == 1
+    # fisher: negative numel
+    ne = (ctypes.c_int64 * 1)(-1)
+    ptrs = (ctypes.c_void_p * 1)(256)
+    assert lrc._fsh(1, ptrs, ptrs, ne, 0, fake, None, 0, fake, None) == 1
+    # allocate: negative budget
+    assert lrc._alc(1, fake, fake, fake, 3, fake, fake, None, -1, fake, None, 0, fake, None) == 1
+    # triangular: bad side flag
+    assert lrc._trsm(2, 0, 4, 4, fake, 4, fake, 4, None) == 1
+
+
+def test_workspace_queries_are_consistent():
+    from activation_aware_rank_amd import lrc
+    a = lrc.lrc_cov_accumulate_workspace(0, 100000, 4096, True, 4096, 1)
+    b = lrc.lrc_cov_accumulate_workspace(0, 100000, 4096, True, 11008, 1)
+    assert 0 < a < b
+    assert lrc.lrc_eigh_workspace(4096, 1, 1228, 1) > lrc.lrc_eigh_workspace(4096, 1, 0, 1)
+    assert lrc.lrc_eigh_workspace(128, 32, 32, 2) == 0  # Jacobi keeps everything in LDS
+    assert lrc.lrc_allocate_ranks_workspace(224, 548704) > 548704 * 8

@@ -1,0 +1,426 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs,
+at sizes the oracle finishes in seconds that still span several tiles and have ragged tails.
+
+Tolerances (the contract): eigenvalues within 1e-5 lambda_max; eps_k within 1e-4 relative where
+eps_k >= 1e-4 eps_0 and within 1e-8 eps_0 below that; largest principal angle of the retained
+subspace below 1e-3 rad; allocation bit-exact on identical inputs; error curve bit-exact on
+identical eigenvalues (same summation order).  Diagnostics: covariance entries within 1e-5
+lambda_max, Fisher scores within 1e-12 relative, factors within 1e-6 relative (Frobenius).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_aware_rank_amd import inputs
+from parity_utils import check_eps, check_lambda, dev, gap, host, sin_theta_max
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def lrc():
+    from activation_aware_rank_amd import lrc as m
+    return m
+
+
+def _say(msg):
+    print("\n[case] " + msg, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# covariance
+# ---------------------------------------------------------------------------------------------
+
+def _cov_gpu(lrc, X, xdt, W, n_blocks=1, C=None):
+    Xd = dev(X, xdt)
+    Wd = dev(W, xdt) if W is not None else None
+    d_out = X.shape[1] if W is None else W.shape[1]
+    hd = d_out // n_blocks
+    if C is None:
+        C = torch.zeros((n_blocks, hd, hd) if n_blocks > 1 else (d_out, d_out), dtype=torch.float32, device="cuda")
+    info = lrc.lrc_cov_accumulate(Xd, Wd, C, n_blocks=n_blocks)
+    assert int(host(info)[0]) == 0
+    return C
+
+
+def _upper_err(C_hat, C_ref):
+    U = np.triu(np.ones(C_ref.shape[-2:], dtype=bool))
+    return np.max(np.abs(np.where(U, C_hat - C_ref, 0.0)))
+
+
+def test_cov_single_layer_fp32(lrc):
+    _say("cov fp32 2048x256 -> 256 (full single-layer size)")
+    d = inputs.single_layer()
+    C = host(_cov_gpu(lrc, d["X"], "f32", d["W"]))
+    Cr = oracle.covariance(d["X"], "f32", d["W"], "f32")
+    lam1 = np.linalg.eigvalsh(Cr)[-1]
+    assert _upper_err(C, Cr) <= 1e-5 * lam1
+    assert np.all(np.tril(C, -1) == 0)  # lower triangle never written
+
+
+@pytest.mark.parametrize("n_tok,d_in,d_out", [(5000, 512, 1376), (40000, 256, 600), (777, 136, 200)])
+def test_cov_bf16_mfma_ragged(lrc, n_tok, d_in, d_out):
+    _say("cov bf16 %dx%d -> %d" % (n_tok, d_in, d_out))
+    X = inputs.block_activations(d_in, n_tok)
+    W = inputs.weight(d_in, d_out, "bf16", inputs.CFG_BLOCK, 0, 1)
+    C = host(_cov_gpu(lrc, X, "bf16", W))
+    Cr = oracle.covariance(X, "bf16", W, "bf16")
+    lam1 = np.linalg.eigvalsh(Cr)[-1]
+    err = _upper_err(C, Cr) / lam1
+    print("max |dC| / lambda_max = %.3e" % err)
+    assert err <= 1e-5
+    assert np.all(np.tril(C, -1) == 0)
+
+
+def test_cov_identity_weight(lrc):
+    _say("cov bf16 W = I, 3000 x 264")
+    X = inputs.block_activations(264, 3000)
+    C = host(_cov_gpu(lrc, X, "bf16", None))
+    Cr = oracle.covariance(X, "bf16")
+    lam1 = np.linalg.eigvalsh(Cr)[-1]
+    assert _upper_err(C, Cr) <= 2e-6 * lam1
+
+
+def test_cov_per_head_blocks(lrc):
+    _say("cov per-head bf16 4096 x 512, 4 heads of 128")
+    d = inputs.per_head(n_tok=4096, d_model=512, head_dim=128)
+    C = host(_cov_gpu(lrc, d["X"], "bf16", d["W"], n_blocks=4))
+    Cr = oracle.covariance(d["X"], "bf16", d["W"], "bf16", n_blocks=4)
+    for h in range(4):
+        lam1 = np.linalg.eigvalsh(Cr[h])[-1]
+        assert _upper_err(C[h], Cr[h]) <= 1e-5 * lam1, h
+
+
+def test_cov_accumulates_and_is_deterministic(lrc):
+    _say("cov chunked calls and repeatability")
+    X = inputs.block_activations(256, 6000)
+    W = inputs.weight(256, 384, "bf16", inputs.CFG_BLOCK, 0, 2)
+    C1 = host(_cov_gpu(lrc, X, "bf16", W))
+    C1b = host(_cov_gpu(lrc, X, "bf16", W))
+    assert np.array_equal(C1, C1b)  # bitwise repeatable
+    C = torch.zeros(384, 384, dtype=torch.float32, device="cuda")
+    _cov_gpu(lrc, X[:2500], "bf16", W, C=C)
+    _cov_gpu(lrc, X[2500:], "bf16", W, C=C)
+    C2 = host(C)
+    lam1 = np.linalg.eigvalsh(np.triu(C1) + np.triu(C1, 1).T)[-1]
+    assert np.max(np.abs(C2 - C1)) <= 1e-6 * lam1
+
+
+def test_cov_nonfinite_input_sets_info(lrc):
+    _say("cov with a NaN input")
+    X = inputs.single_layer(n_tok=64, d_in=16, d_out=16)["X"].copy()
+    X[3, 5] = np.nan
+    Xd, Wd = dev(X, "f32"), dev(np.eye(16, dtype=np.float32), "f32")
+    C = torch.zeros(16, 16, dtype=torch.float32, device="cuda")
+    info = lrc.lrc_cov_accumulate(Xd, Wd, C)
+    assert int(host(info)[0]) == 1
+
+
+def test_cov_rejects_empty(lrc):
+    X = torch.zeros(0, 8, dtype=torch.float32, device="cuda")
+    C = torch.zeros(8, 8, dtype=torch.float32, device="cuda")
+    with pytest.raises(lrc.LrcError):
+        lrc.lrc_cov_accumulate(X, None, C)
+
+
+# ---------------------------------------------------------------------------------------------
+# eigendecomposition
+# ---------------------------------------------------------------------------------------------
+
+def _oracle_cov32(X, xdt, W, n_blocks=1):
+    """Oracle covariance rounded to fp32 (the GPU eig's input) and the same values in fp64."""
+    C = oracle.covariance(X, xdt, W, xdt, n_blocks=n_blocks)
+    C32 = C.astype(np.float32)
+    return C32, C32.astype(np.float64)
+
+
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("case", ["single256", "block300", "gate_like"])
+def test_eigh_large_vs_oracle(lrc, case, prec):
+    _say("eigh large %s prec %d" % (case, prec))
+    if case == "single256":
+        d = inputs.single_layer()
+        C32, C64 = _oracle_cov32(d["X"], "f32", d["W"])
+        k = 64
+    elif case == "block300":
+        X = inputs.block_activations(320, 4096)
+        W = inputs.weight(320, 300, "bf16", inputs.CFG_BLOCK, 0, 3)
+        C32, C64 = _oracle_cov32(X, "bf16", W)
+        k = inputs.rank_at_ratio(320, 300, 0.6)
+    else:  # 160 -> 430: rank-deficient covariance, like gate/up
+        X = inputs.block_activations(160, 4096)
+        W = inputs.weight(160, 430, "bf16", inputs.CFG_BLOCK, 0, 4)
+        C32, C64 = _oracle_cov32(X, "bf16", W)
+        k = inputs.rank_at_ratio(160, 430, 0.6)
+    n = C32.shape[0]
+    lam_r, V_r = oracle.eigh(C64)
+    Cu = np.triu(C32) + np.tril(np.full((n, n), np.nan, np.float32), -1)  # lower triangle must not be read
+    lam, V, info = lrc.lrc_eigh(dev(Cu, "f32"), n_vec=n, prec=prec)
+    lam, V = host(lam), host(V)
+    assert int(host(info)[0]) == 0
+    e = check_lambda(lam, lam_r)
+    s = sin_theta_max(V, V_r, k)
+    print("lambda err %.2e, sin theta(k=%d) %.2e, gap %.2e" % (e, k, s, gap(lam_r, k)))
+    assert s <= 1e-3
+    V64 = V.astype(np.float64)
+    assert np.max(np.abs(V64.T @ V64 - np.eye(n))) <= 1e-5
+    assert np.linalg.norm(C64 @ V64 - V64 * lam) <= 1e-5 * np.linalg.norm(C64)
+    idx = np.argmax(np.abs(V), axis=0)
+    assert np.all(V[idx, np.arange(n)] > 0)
+    assert np.all(np.diff(lam) <= 0)
+
+
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("n,batch", [(128, 4), (17, 3), (64, 2)])
+def test_eigh_jacobi_vs_oracle(lrc, n, batch, prec):
+    _say("eigh jacobi n=%d batch=%d prec %d" % (n, batch, prec))
+    d = inputs.per_head(n_tok=4096, d_model=n * batch, head_dim=n)
+    C = oracle.covariance(d["X"], "bf16", d["W"], "bf16", n_blocks=batch) if batch > 1 else None
+    C32 = C.astype(np.float32)
+    lam, V, info = lrc.lrc_eigh(dev(C32, "f32"), n_vec=n, prec=prec)
+    lam, V, info = host(lam), host(V), host(info)
+    k = max(1, n // 4)
+    for b in range(batch):
+        assert info[b] == 0
+        lam_r, V_r = oracle.eigh(C32[b].astype(np.float64))
+        check_lambda(lam[b], lam_r)
+        s = sin_theta_max(V[b], V_r, k)
+        lim = 1e-3 if prec == 2 else 1e-2
+        assert s <= lim, (b, s, gap(lam_r, k))
+
+
+def test_eigh_nonfinite_sets_info(lrc):
+    C = np.eye(200, dtype=np.float32)
+    C[3, 7] = np.inf
+    lam, V, info = lrc.lrc_eigh(dev(C, "f32"), n_vec=4)
+    assert int(host(info)[0]) == 1
+    Cj = np.eye(32, dtype=np.float32)[None].repeat(2, 0)
+    Cj[1, 0, 5] = np.nan
+    lam, V, info = lrc.lrc_eigh(dev(Cj, "f32"), n_vec=4, prec=2)
+    assert list(host(info)) == [0, 1]
+
+
+def test_eigh_diagonal_and_repeated(lrc):
+    _say("eigh diagonal with repeated eigenvalues")
+    dvals = np.array([5.0] * 40 + [2.0] * 100 + [1.0] * 60, dtype=np.float32)
+    perm = np.random.default_rng(0).permutation(200)
+    C = np.diag(dvals[perm]).astype(np.float32)
+    lam, V, info = lrc.lrc_eigh(dev(C, "f32"), n_vec=200)
+    lam, V = host(lam), host(V).astype(np.float64)
+    assert np.allclose(lam, np.sort(dvals)[::-1], atol=1e-5 * 5)
+    assert np.max(np.abs(V.T @ V - np.eye(200))) <= 1e-5
+    P = V[:, :40] @ V[:, :40].T  # projector onto the lambda = 5 eigenspace
+    assert np.allclose(P, np.diag((dvals[perm] == 5).astype(float)), atol=1e-5)
+
+
+# ---------------------------------------------------------------------------------------------
+# error curve, factors, Fisher, allocation
+# ---------------------------------------------------------------------------------------------
+
+def test_error_curve_bitexact(lrc):
+    _say("error curve")
+    r = np.random.default_rng(1)
+    lam = np.sort(r.exponential(1.0, (5, 777)), axis=1)[:, ::-1].copy()
+    lam[:, -3:] = [1e-18, 0.0, -1e-17]
+    eps = host(lrc.lrc_error_curve(dev(lam, "f64")))
+    assert np.array_equal(eps, oracle.error_curve(lam))
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_factorize_matches_fp64_product(lrc, wdt):
+    _say("factorize %s" % wdt)
+    W = inputs.weight(520, 1376, wdt, inputs.CFG_BLOCK, 0, 5)
+    Q, _ = np.linalg.qr(np.random.default_rng(2).standard_normal((1376, 300)))
+    V = Q.astype(np.float32)
+    k = 237
+    A = torch.empty(520, k, dtype=torch.float32, device="cuda")
+    B = torch.empty(k, 1376, dtype=torch.float32, device="cuda")
+    lrc.lrc_factorize(dev(W, wdt), dev(V, "f32"), k, A, B)
+    W64 = oracle.widen(W, wdt)
+    ref = W64 @ V[:, :k].astype(np.float64)
+    Ah = host(A).astype(np.float64)
+    assert np.linalg.norm(Ah - ref) <= 1e-6 * np.linalg.norm(ref)
+    assert np.array_equal(host(B), V[:, :k].T)
+    # transposed weight (maps factors back through W^T): A = W^T V with V d_in x k
+    V2 = np.linalg.qr(np.random.default_rng(3).standard_normal((520, 90)))[0].astype(np.float32)
+    A2 = torch.empty(1376, 90, dtype=torch.float32, device="cuda")
+    lrc.lrc_factorize(dev(W, wdt), dev(V2, "f32"), 90, A2, None, trans_w=1)
+    ref2 = W64.T @ V2.astype(np.float64)
+    assert np.linalg.norm(host(A2) - ref2) <= 1e-6 * np.linalg.norm(ref2)
+
+
+def test_factorize_per_head_batch(lrc):
+    _say("factorize per-head batch")
+    W = inputs.weight(512, 512, "bf16", inputs.CFG_HEADS, 0, 0)
+    Vh = np.stack([np.linalg.qr(np.random.default_rng(10 + h).standard_normal((128, 128)))[0]
+                   for h in range(4)]).astype(np.float32)
+    k = 32
+    A = torch.empty(4, 512, k, dtype=torch.float32, device="cuda")
+    B = torch.empty(4, k, 128, dtype=torch.float32, device="cuda")
+    Wd = dev(W, "bf16")
+    lrc.lrc_factorize(Wd, dev(Vh, "f32"), k, A, B, d_in=512, d_out=128, batch=4, stride_w=128,
+                      stride_v=128 * 128, stride_a=512 * k, stride_b=k * 128)
+    W64 = oracle.widen(W, "bf16")
+    Ah = host(A)
+    for h in range(4):
+        ref = W64[:, 128 * h:128 * h + 128] @ Vh[h][:, :k].astype(np.float64)
+        assert np.linalg.norm(Ah[h] - ref) <= 1e-6 * np.linalg.norm(ref)
+        assert np.array_equal(host(B)[h], Vh[h][:, :k].T)
+
+
+def test_fisher_scores(lrc):
+    _say("fisher")
+    shapes = [(37, 41), (256, 128), (1000, 333), (1, 1), (2048, 4096)]
+    Gs, Ws = [], []
+    for i, (a, b) in enumerate(shapes):
+        Gs.append(inputs.gradient(a, b, 1e-4, inputs.CFG_STACK, 0, i))
+        Ws.append(inputs.weight(a, b, "bf16", inputs.CFG_STACK, 0, i))
+    alpha, info = lrc.lrc_fisher_scores([dev(g, "bf16") for g in Gs], [dev(w, "bf16") for w in Ws])
+    alpha, info = host(alpha), host(info)
+    for i in range(len(shapes)):
+        ref = oracle.fisher(Gs[i], Ws[i])
+        assert abs(alpha[i] - ref) <= 1e-12 * ref, i
+        assert info[i] == 0
+    # unaligned view (offset by one element) goes through the scalar path
+    G0 = dev(Gs[4], "bf16").reshape(-1)[1:]
+    W0 = dev(Ws[4], "bf16").reshape(-1)[1:]
+    a1, _ = lrc.lrc_fisher_scores([G0], [W0])
+    ref = oracle.fisher(Gs[4].reshape(-1)[1:], Ws[4].reshape(-1)[1:])
+    assert abs(host(a1)[0] - ref) <= 1e-12 * ref
+    # fp32 inputs
+    g32 = np.random.default_rng(4).standard_normal(5000).astype(np.float32)
+    w32 = np.random.default_rng(5).standard_normal(5000).astype(np.float32)
+    a2, _ = lrc.lrc_fisher_scores([dev(g32, "f32")], [dev(w32, "f32")])
+    ref = float(np.sum((g32.astype(np.float64) * w32.astype(np.float64)) ** 2))
+    assert abs(host(a2)[0] - ref) <= 1e-12 * ref
+
+
+def test_fisher_nonfinite(lrc):
+    g = inputs.f32_to_bf16_bits(np.array([1.0, np.inf, 2.0], np.float32))
+    w = inputs.f32_to_bf16_bits(np.array([1.0, 1.0, 2.0], np.float32))
+    _, info = lrc.lrc_fisher_scores([dev(g, "bf16")], [dev(w, "bf16")])
+    assert int(host(info)[0]) == 1
+
+
+def _alloc_gpu(lrc, alpha, lams, eps0, cost, budget, k_min=None):
+    offs = np.concatenate([[0], np.cumsum([len(l) for l in lams])]).astype(np.int64)
+    lp = np.concatenate([np.asarray(l, dtype=np.float64) for l in lams]) if offs[-1] else np.zeros(0)
+    km = None if k_min is None else dev(np.asarray(k_min, dtype=np.int32), "i32")
+    k, info = lrc.lrc_allocate_ranks(dev(np.asarray(alpha, np.float64), "f64"), dev(lp, "f64"),
+                                     dev(offs, "i64"), dev(np.asarray(eps0, np.float64), "f64"),
+                                     dev(np.asarray(cost, np.int64), "i64"), budget, k_min=km)
+    return host(k), int(host(info)[0])
+
+
+def test_allocate_worked_example(lrc):
+    ex = json.load(open(os.path.join(GOLDEN, "alloc_worked_example.json")))
+    ms = ex["matrices"]
+    args = ([m["alpha"] for m in ms], [m["lam"] for m in ms], [m["eps0"] for m in ms], [m["cost"] for m in ms])
+    for case in ex["cases"]:
+        k, info = _alloc_gpu(lrc, *args, case["budget"], case["k_min"])
+        assert info == case["info"] and list(k) == case["k"], case
+
+
+def test_allocate_bitexact_random_with_ties(lrc):
+    _say("allocation random")
+    r = np.random.default_rng(7)
+    for trial in range(40):
+        M = int(r.integers(1, 12))
+        lams = []
+        for m in range(M):
+            K = int(r.integers(0, 60))
+            if trial % 3 == 0:  # many exact ties
+                l = np.sort(r.choice([0.0, 0.5, 1.0, 2.0, -1e-9], K))[::-1]
+            else:
+                l = np.sort(r.exponential(1.0, K))[::-1]
+            lams.append(l)
+        alpha = r.choice([0.0, 1.0, 3.0], M) if trial % 3 == 0 else r.exponential(1.0, M)
+        eps0 = [float(np.sum(np.maximum(l, 0))) for l in lams]
+        cost = r.integers(1, 9, M)
+        k_min = [int(r.integers(0, len(l) + 1)) if r.random() < 0.3 else 0 for l in lams]
+        total = int(sum(len(l) * c for l, c in zip(lams, cost)))
+        for budget in (0, total // 3, total // 2 + 1, total, total + 5):
+            kg, ig = _alloc_gpu(lrc, alpha, lams, eps0, cost, budget, k_min)
+            ko, io = oracle.allocate_ranks(alpha, lams, eps0, cost, budget, k_min)
+            assert ig == io and list(kg) == list(ko), (trial, budget)
+
+
+def test_allocate_bad_scores(lrc):
+    k, info = _alloc_gpu(lrc, [1.0, np.nan], [[1.0, 0.5], [2.0]], [1.5, 2.0], [3, 3], 100)
+    assert info == 5
+    k, info = _alloc_gpu(lrc, [1.0, 1.0], [[1.0, 0.5], [2.0]], [1.5, -2.0], [3, 3], 100)
+    assert info == 5
+
+
+# ---------------------------------------------------------------------------------------------
+# the whole path, end to end
+# ---------------------------------------------------------------------------------------------
+
+def _pipeline(lrc, X, xdt, W, k, n_blocks=1, prec=1):
+    """cov -> eigh -> error curve -> factorize on the GPU; returns host arrays."""
+    C = _cov_gpu(lrc, X, xdt, W, n_blocks=n_blocks)
+    d_out = W.shape[1]
+    hd = d_out // n_blocks
+    if n_blocks == 1:
+        lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=prec)
+        lam, V = lam[None], V[None]
+    else:
+        lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=2)
+    assert np.all(host(info) == 0)
+    eps = lrc.lrc_error_curve(lam)
+    A = torch.empty(n_blocks, W.shape[0], k, dtype=torch.float32, device="cuda")
+    B = torch.empty(n_blocks, k, hd, dtype=torch.float32, device="cuda")
+    lrc.lrc_factorize(dev(W, xdt), V, k, A, B, d_in=W.shape[0], d_out=hd, batch=n_blocks, stride_w=hd,
+                      stride_v=hd * k, stride_a=W.shape[0] * k, stride_b=k * hd)
+    return host(lam), host(V), host(eps), host(A), host(B)
+
+
+def _check_pipeline(X, xdt, W, k, lam, V, eps, A, B, n_blocks=1):
+    C = oracle.covariance(X, xdt, W, xdt, n_blocks=n_blocks)
+    C = C[None] if n_blocks == 1 else C
+    W64 = oracle.widen(W, xdt)
+    X64 = oracle.widen(X, xdt)
+    hd = W.shape[1] // n_blocks
+    for h in range(n_blocks):
+        lam_r, V_r = oracle.eigh(C[h])
+        eps_r = oracle.error_curve(lam_r)
+        el = check_lambda(lam[h], lam_r)
+        ee = check_eps(eps[h], eps_r)
+        s = sin_theta_max(V[h], V_r, k)
+        Wh = W64[:, h * hd:(h + 1) * hd]
+        # the GPU factors reach the closed-form error: ||X W - X A B||^2 = eps_k (test-side fp64)
+        R = X64 @ (Wh - A[h].astype(np.float64) @ B[h].astype(np.float64))
+        direct = float(np.sum(R * R))
+        print("head %d: lambda %.2e, eps %.2e/%.2e, sin theta %.2e (gap %.2e), direct/eps_k - 1 = %.2e"
+              % (h, el, ee[0], ee[1], s, gap(lam_r, k), direct / eps_r[k] - 1))
+        assert s <= 1e-3
+        assert abs(direct - eps_r[k]) <= 1e-4 * eps_r[k] + 1e-6 * eps_r[0]
+
+
+def test_pipeline_single_layer(lrc):
+    _say("pipeline single layer 2048 x 256 -> 256, k = 64")
+    d = inputs.single_layer()
+    out = _pipeline(lrc, d["X"], "f32", d["W"], 64)
+    _check_pipeline(d["X"], "f32", d["W"], 64, *out)
+
+
+def test_pipeline_block_scaled(lrc):
+    _say("pipeline scaled block 16384 x 512 -> 640")
+    X = inputs.block_activations(512, 16384)
+    W = inputs.weight(512, 640, "bf16", inputs.CFG_BLOCK, 0, 0)
+    k = inputs.rank_at_ratio(512, 640, 0.6)
+    out = _pipeline(lrc, X, "bf16", W, k)
+    _check_pipeline(X, "bf16", W, k, *out)
+
+
+def test_pipeline_per_head_scaled(lrc):
+    _say("pipeline per-head 8192 x 512, 4 heads of 128, k = 32")
+    d = inputs.per_head(n_tok=8192, d_model=512, head_dim=128)
+    out = _pipeline(lrc, d["X"], "bf16", d["W"], 32, n_blocks=4)
+    _check_pipeline(d["X"], "bf16", d["W"], 32, *out, n_blocks=4)
