@@ -4,15 +4,17 @@
 // tokens, one chunk at a time):
 //   1. GEMM  Y^T[i][t] = sum_k W^T[i][k] X[t][k]        (bf16 MFMA, fp32 accumulation)
 //      epilogue: hi = bf16(y), lo = bf16(y - hi), stored token-contiguous.
-//   2. SYRK  C[I,J] += Yhi_I Yhi_J^T + Yhi_I Ylo_J^T + Ylo_I Yhi_J^T   for tiles I <= J
-//      (bf16 MFMA, fp32 accumulation).  The lo*lo term is below fp32 rounding of C.
+//   2. SYRK  C[I,J] += (Yhi_I + Ylo_I)(Yhi_J + Ylo_J)^T as four bf16 MFMA products, fp32
+//      accumulation, for tiles I <= J.  All four are needed: dropping lo*lo would lower every
+//      quadratic form v^T C v by ||Ylo v||^2 (about 2e-6 of the diagonal, always one-signed),
+//      which shifts the small eigenvalues at the tail of the spectrum far more than that.
 // With W == NULL (C += X^T X) the chunk is transposed exactly and one product suffices.
 //
 // Both phases are one "NT" kernel: D = A B^T with A and B row-major along the contraction
 // axis, which is exactly the layout the 32x32x16 bf16 MFMA operands want (each lane holds 8
-// contiguous k-values of one row).  Block tile BM x BM with 4 waves (2 x 2), k step 32,
-// double-buffered LDS with an XOR swizzle of the 16-byte chunks (no padding, no bank
-// conflicts on 16-byte reads), one barrier per k step.
+// contiguous k-values of one row).  4 waves (2 x 2) per block; block tile 256 x 256 for the
+// GEMM and 128 x 128 for the SYRK; k step 32, double-buffered LDS with an XOR swizzle of the
+// 16-byte chunks (no padding, no bank conflicts on 16-byte reads), one barrier per k step.
 //
 // Load balance of the SYRK: the upper triangle may have fewer tiles than the GPU has CUs, so
 // the token range of a chunk is split S ways; split s > 0 accumulates into its own fp32
@@ -26,26 +28,36 @@ namespace lrc {
 
 constexpr int MK = 32;                   // k step, bf16 elements (4 chunks of 16 bytes)
 constexpr int64_t MFMA_CHUNK = 32768;    // tokens per internal chunk
-constexpr int MFMA_THREADS = 256;
 
 __device__ __forceinline__ int swz(int r, int c) { return r * MK + ((c ^ ((r >> 1) & 3)) << 3); }
 
-template <int BM, int NOPS>
-struct MfmaTile {
-    static constexpr int TM = BM / 64;                  // 32x32 MFMA tiles per wave per dim
-    static constexpr int WM = BM / 2;                   // wave tile
-    static constexpr int U = BM * (MK / 8) / MFMA_THREADS;  // 16-byte chunks per thread per operand
+// Block tile BM x BM, THREADS/64 waves arranged WGM x WGN, wave tile (BM/WGM) x (BM/WGN).
+template <int BM, int THREADS, int WGM>
+struct MfmaCfg {
+    static constexpr int WAVES = THREADS / 64;
+    static constexpr int WGN = WAVES / WGM;
+    static constexpr int WM = BM / WGM, WN = BM / WGN;  // wave tile
+    static constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 MFMA tiles per wave
+    static constexpr int U = BM * (MK / 8) / THREADS;   // 16-byte chunks per thread per operand
 };
 
-// acc[tm][tn] += sum over k in [0, klen) of A[row][k] B[col][k]; ops: {A(,Alo), B(,Blo)}
-template <int BM, int NOPS, int NPROD>
+// acc[tm][tn] += sum over k in [0, klen) of A[row][k] B[col][k]; ops: {A(,Alo), B(,Blo)}.
+// NPROD 4 forms (Ahi + Alo)(Bhi + Blo)^T, NPROD 1 forms A B^T.
+// FLUSH: the MFMA chain of each 16-wide k slice starts from zero and its result is added to acc
+// with a round-to-nearest fp32 add, so a running sum over many tokens carries the error of one
+// fp32 addition per 16 tokens instead of a long chain of MFMA accumulations.  Otherwise the
+// MFMAs accumulate into acc directly (used where the contraction is short or the rounding
+// errors are not one-signed).
+template <int BM, int THREADS, int WGM, int NOPS, int NPROD, bool FLUSH>
 __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const int64_t *ld, const int *rows,
-                                              int64_t klen, f32x16_t (&acc)[BM / 64][BM / 64], bf16_t *lds) {
-    using T = MfmaTile<BM, NOPS>;
-    constexpr int TM = T::TM, U = T::U;
+                                              int64_t klen,
+                                              f32x16_t (&acc)[MfmaCfg<BM, THREADS, WGM>::TM][MfmaCfg<BM, THREADS, WGM>::TN],
+                                              bf16_t *lds) {
+    using T = MfmaCfg<BM, THREADS, WGM>;
+    constexpr int TM = T::TM, TN = T::TN, U = T::U;
     constexpr int OPSZ = BM * MK;  // elements of one operand tile
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / T::WGN, wn = wave % T::WGN;
     const int nk = int((klen + MK - 1) / MK);
     u32x4_t regs[NOPS][U];
 
@@ -55,7 +67,7 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
         for (int o = 0; o < NOPS; ++o)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int q = tid + MFMA_THREADS * u;
+                const int q = tid + THREADS * u;
                 const int r = q >> 2, c = q & 3;
                 const int64_t k = k0 + c * 8;
                 if (r < rows[o] && k < klen)
@@ -69,7 +81,7 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
         for (int o = 0; o < NOPS; ++o)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int q = tid + MFMA_THREADS * u;
+                const int q = tid + THREADS * u;
                 const int r = q >> 2, c = q & 3;
                 *reinterpret_cast<u32x4_t *>(lds + (buf * NOPS + o) * OPSZ + swz(r, c)) = regs[o][u];
             }
@@ -79,7 +91,7 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
     gload(0);
     sstore(0);
     __syncthreads();
-    constexpr int NA = (NPROD == 3) ? 2 : 1;
+    constexpr int NA = (NPROD == 4) ? 2 : 1;
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < nk) gload(kt + 1);
@@ -87,24 +99,33 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int c = ks * 2 + (lane >> 5);
-            bf16x8_t af[NA][TM], bfr[NA][TM];
+            bf16x8_t af[NA][TM], bfr[NA][TN];
 #pragma unroll
-            for (int a = 0; a < NA; ++a)
+            for (int a = 0; a < NA; ++a) {
 #pragma unroll
-                for (int t = 0; t < TM; ++t) {
-                    const int ra = wm * T::WM + t * 32 + (lane & 31);
-                    const int rb = wn * T::WM + t * 32 + (lane & 31);
-                    af[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + a * OPSZ + swz(ra, c));
-                    bfr[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + (NA + a) * OPSZ + swz(rb, c));
-                }
+                for (int t = 0; t < TM; ++t)
+                    af[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + a * OPSZ + swz(wm * T::WM + t * 32 + (lane & 31), c));
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    bfr[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + (NA + a) * OPSZ +
+                                                                    swz(wn * T::WN + t * 32 + (lane & 31), c));
+            }
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-                for (int tn = 0; tn < TM; ++tn) {
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[0][tn], acc[tm][tn], 0, 0, 0);
-                    if (NPROD == 3) {
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[1][tn], acc[tm][tn], 0, 0, 0);
-                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[0][tn], acc[tm][tn], 0, 0, 0);
+                for (int tn = 0; tn < TN; ++tn) {
+                    f32x16_t p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[0][tn],
+                                                                         FLUSH ? f32x16_t{} : acc[tm][tn], 0, 0, 0);
+                    if (NPROD == 4) {
+                        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[1][tn], p, 0, 0, 0);
+                        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[0][tn], p, 0, 0, 0);
+                        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[1][tn], p, 0, 0, 0);
+                    }
+                    if (FLUSH) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[tm][tn][r] = __fadd_rn(acc[tm][tn][r], p[r]);
+                    } else {
+                        acc[tm][tn] = p;
                     }
                 }
         }
@@ -143,41 +164,48 @@ __device__ __forceinline__ void add_upper_tile(const f32x16_t a, int64_t rb, int
 }
 
 // Phase 1: Y^T tile (rows = output features i, cols = tokens t), split into hi/lo.
+constexpr int G_BM = 256, G_THREADS = 256, G_WGM = 2;
 template <int BM>
-__global__ void __launch_bounds__(MFMA_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const bf16_t *__restrict__ X, int64_t ldx,
              int64_t tc, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo, int64_t ldy) {
+    using Cfg = MfmaCfg<BM, G_THREADS, G_WGM>;
     __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * BM * MK];
-    constexpr int TM = BM / 64;
     const int64_t i0 = int64_t(blockIdx.x) * BM, t0 = int64_t(blockIdx.y) * BM;
     const bf16_t *base[2] = {Wt + i0 * d_in, X + t0 * ldx};
     const int64_t ld[2] = {d_in, ldx};
     const int rows[2] = {int(std::min<int64_t>(BM, d_out - i0)), int(std::max<int64_t>(0, std::min<int64_t>(BM, tc - t0)))};
-    f32x16_t acc[TM][TM];
+    f32x16_t acc[Cfg::TM][Cfg::TN];
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+    for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TM; ++b) acc[a][b] = f32x16_t{};
-    mfma_mainloop<BM, 2, 1>(base, ld, rows, d_in, acc, lds);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+        for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
+    mfma_mainloop<BM, G_THREADS, G_WGM, 2, 1, false>(base, ld, rows, d_in, acc, lds);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+    for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TM; ++tn) {
-            const int64_t ib = i0 + wm * (BM / 2) + tm * 32;
-            const int64_t t = t0 + wn * (BM / 2) + tn * 32 + acc_col(lane);
+        for (int tn = 0; tn < Cfg::TN; ++tn) {
+            const int64_t ib = i0 + wm * Cfg::WM + tm * 32;
+            const int64_t t = t0 + wn * Cfg::WN + tn * 32 + acc_col(lane);
             store_split_tile(acc[tm][tn], ib, t, lane, d_out, Yhi, Ylo, ldy);
         }
 }
 
 // Phase 2: upper tiles of each head block, split s of the token range.
+template <int BM>
+struct SyrkCfg {  // 4 waves of (BM/2) x (BM/2)
+    static constexpr int THREADS = 256;
+    static constexpr int WGM = 2;
+};
 template <int BM, int NPROD>
-__global__ void __launch_bounds__(MFMA_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(SyrkCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64_t ldy, int64_t ktot, int64_t kchunk,
            int64_t hd, float *__restrict__ C, int64_t ldc, float *__restrict__ P, int32_t n_blocks) {
-    constexpr int NOPS = (NPROD == 3) ? 4 : 2;
+    constexpr int THREADS = SyrkCfg<BM>::THREADS, WGM = SyrkCfg<BM>::WGM;
+    using Cfg = MfmaCfg<BM, THREADS, WGM>;
+    constexpr int NOPS = (NPROD == 4) ? 4 : 2;
     __shared__ __attribute__((aligned(16))) bf16_t lds[2 * NOPS * BM * MK];
-    constexpr int TM = BM / 64;
     const int u = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     int J = int((sqrtf(8.f * float(u) + 1.f) - 1.f) * 0.5f);
     while (J * (J + 1) / 2 > u) --J;
@@ -192,7 +220,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
     const bf16_t *base[4];
     int64_t ld[4];
     int rows[4];
-    if (NPROD == 3) {
+    if (NPROD == 4) {
         base[0] = Yhi + r0 * ldy + kb; base[1] = Ylo + r0 * ldy + kb;
         base[2] = Yhi + c0 * ldy + kb; base[3] = Ylo + c0 * ldy + kb;
         rows[0] = rows[1] = rowsI; rows[2] = rows[3] = rowsJ;
@@ -201,12 +229,12 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
         rows[0] = rowsI; rows[1] = rowsJ;
     }
     for (int o = 0; o < 4; ++o) ld[o] = ldy;
-    f32x16_t acc[TM][TM];
+    f32x16_t acc[Cfg::TM][Cfg::TN];
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+    for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TM; ++b) acc[a][b] = f32x16_t{};
-    mfma_mainloop<BM, NOPS, NPROD>(base, ld, rows, klen, acc, lds);
+        for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
+    mfma_mainloop<BM, THREADS, WGM, NOPS, NPROD, true>(base, ld, rows, klen, acc, lds);
     float *dst;
     int64_t ldd;
     if (s == 0) {
@@ -216,13 +244,13 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
         dst = P + (int64_t(s - 1) * n_blocks + h) * hd * hd;
         ldd = hd;
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+    for (int tm = 0; tm < Cfg::TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TM; ++tn) {
-            const int64_t rb = int64_t(I) * BM + wm * (BM / 2) + tm * 32;
-            const int64_t cc = int64_t(J) * BM + wn * (BM / 2) + tn * 32 + acc_col(lane);
+        for (int tn = 0; tn < Cfg::TN; ++tn) {
+            const int64_t rb = int64_t(I) * BM + wm * Cfg::WM + tm * 32;
+            const int64_t cc = int64_t(J) * BM + wn * Cfg::WN + tn * 32 + acc_col(lane);
             add_upper_tile(acc[tm][tn], rb, cc, lane, hd, dst, ldd);
         }
 }
@@ -282,7 +310,7 @@ __global__ void k_add_partials(float *__restrict__ C, int64_t ldc, const float *
 // host side
 // ---------------------------------------------------------------------------------------------
 struct MfmaPlan {
-    int bm;         // SYRK block tile
+    int bm;         // SYRK block tile (128: 4 waves of 64 x 64, spill-free with the per-slice flush)
     int64_t tcmax;  // tokens per chunk
     int64_t ldy;    // leading dim of Y^T (multiple of 256)
     int nsplit;     // token splits of the SYRK
@@ -292,7 +320,7 @@ struct MfmaPlan {
 static MfmaPlan plan(int64_t n_tok, int64_t d_out, int32_t n_blocks) {
     MfmaPlan p;
     const int64_t hd = d_out / n_blocks;
-    p.bm = hd >= 256 ? 256 : 128;
+    p.bm = 128;
     p.tcmax = std::min<int64_t>(MFMA_CHUNK, n_tok);
     p.ldy = (p.tcmax + 255) / 256 * 256;
     const int64_t th = (hd + p.bm - 1) / p.bm;
@@ -364,7 +392,7 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         const int64_t ktot = (tc + MK - 1) / MK * MK;
         if (has_w) {
             dim3 g(cdiv(a.d_out, 256), cdiv(ktot, 256));
-            hipLaunchKernelGGL(k_cov_gemm_y<256>, g, dim3(MFMA_THREADS), 0, s, Wt, a.d_in, a.d_out, X + t0 * a.ldx,
+            hipLaunchKernelGGL(k_cov_gemm_y<G_BM>, g, dim3(G_THREADS), 0, s, Wt, a.d_in, a.d_out, X + t0 * a.ldx,
                                a.ldx, tc, Yhi, Ylo, p.ldy);
             LRC_LAUNCH_CHECK("k_cov_gemm_y");
         } else {
@@ -374,21 +402,12 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         }
         const int64_t kchunk = ((ktot + p.nsplit - 1) / p.nsplit + MK - 1) / MK * MK;
         dim3 g(unsigned(p.n_upper), unsigned(a.n_blocks), unsigned(p.nsplit));
-        if (p.bm == 256) {
-            if (has_w)
-                hipLaunchKernelGGL((k_cov_syrk<256, 3>), g, dim3(MFMA_THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk, hd,
-                                   a.C, a.ldc, P, a.n_blocks);
-            else
-                hipLaunchKernelGGL((k_cov_syrk<256, 1>), g, dim3(MFMA_THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk, hd,
-                                   a.C, a.ldc, P, a.n_blocks);
-        } else {
-            if (has_w)
-                hipLaunchKernelGGL((k_cov_syrk<128, 3>), g, dim3(MFMA_THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk, hd,
-                                   a.C, a.ldc, P, a.n_blocks);
-            else
-                hipLaunchKernelGGL((k_cov_syrk<128, 1>), g, dim3(MFMA_THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk, hd,
-                                   a.C, a.ldc, P, a.n_blocks);
-        }
+        if (has_w)
+            hipLaunchKernelGGL((k_cov_syrk<128, 4>), g, dim3(SyrkCfg<128>::THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk,
+                               hd, a.C, a.ldc, P, a.n_blocks);
+        else
+            hipLaunchKernelGGL((k_cov_syrk<128, 1>), g, dim3(SyrkCfg<128>::THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk,
+                               hd, a.C, a.ldc, P, a.n_blocks);
         LRC_LAUNCH_CHECK("k_cov_syrk");
     }
     if (p.nsplit > 1) {

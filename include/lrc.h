@@ -93,7 +93,8 @@ const char *lrc_last_error(void);
  * Accumulates: the caller zeroes C before the first chunk.  Any chunking of the tokens
  *    gives the same C up to fp32 rounding of the running sum.
  * Arithmetic: bf16 inputs use bf16 MFMA with fp32 accumulation for Y; Y is then split
- *    into bf16 hi + lo parts and C += hi^T hi + hi^T lo + lo^T hi (fp32 accumulation).
+ *    into bf16 hi + lo parts and C += (hi + lo)^T (hi + lo) as four bf16 products (fp32
+ *    accumulation).
  *    fp32 inputs use fp32 arithmetic throughout.
  * info: one int32; set to 1 when the updated C has a non-finite diagonal entry.
  * Errors: LRC_ERR_ARG for non-positive sizes, small leading dims, d_out % n_blocks != 0,

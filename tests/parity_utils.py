@@ -29,7 +29,14 @@ def check_lambda(lam_hat, lam, tol=1e-5):
     return err
 
 
-def check_eps(eps_hat, eps, rel=1e-4, floor=1e-8):
+# Below rel * eps_0 the relative check gives way to an absolute floor of 2^-23 eps_0: C is
+# accumulated and stored in fp32, so tail sums smaller than one fp32 unit of its trace are not
+# resolved by any method that keeps C in fp32 (rounding the exact C once to fp32 already moves
+# the tail of a rank-deficient spectrum by about 1e-8 eps_0).
+EPS_FLOOR = 2.0 ** -23
+
+
+def check_eps(eps_hat, eps, rel=1e-4, floor=EPS_FLOOR):
     """eps_k within rel relative where eps_k >= rel * eps_0; elsewhere within floor * eps_0."""
     eps_hat = np.asarray(eps_hat, dtype=np.float64)
     eps = np.asarray(eps, dtype=np.float64)

@@ -2,7 +2,7 @@
 at sizes the oracle finishes in seconds that still span several tiles and have ragged tails.
 
 Tolerances (the contract): eigenvalues within 1e-5 lambda_max; eps_k within 1e-4 relative where
-eps_k >= 1e-4 eps_0 and within 1e-8 eps_0 below that; largest principal angle of the retained
+eps_k >= 1e-4 eps_0 and within 2^-23 eps_0 (one fp32 unit of the trace) below that; largest principal angle of the retained
 subspace below 1e-3 rad; allocation bit-exact on identical inputs; error curve bit-exact on
 identical eigenvalues (same summation order).  Diagnostics: covariance entries within 1e-5
 lambda_max, Fisher scores within 1e-12 relative, factors within 1e-6 relative (Frobenius).
@@ -378,10 +378,11 @@ def _pipeline(lrc, X, xdt, W, k, n_blocks=1, prec=1):
     B = torch.empty(n_blocks, k, hd, dtype=torch.float32, device="cuda")
     lrc.lrc_factorize(dev(W, xdt), V, k, A, B, d_in=W.shape[0], d_out=hd, batch=n_blocks, stride_w=hd,
                       stride_v=hd * k, stride_a=W.shape[0] * k, stride_b=k * hd)
-    return host(lam), host(V), host(eps), host(A), host(B)
+    Ch = host(C)
+    return host(lam), host(V), host(eps), host(A), host(B), (Ch[None] if n_blocks == 1 else Ch)
 
 
-def _check_pipeline(X, xdt, W, k, lam, V, eps, A, B, n_blocks=1):
+def _check_pipeline(X, xdt, W, k, lam, V, eps, A, B, n_blocks=1, C_gpu=None):
     C = oracle.covariance(X, xdt, W, xdt, n_blocks=n_blocks)
     C = C[None] if n_blocks == 1 else C
     W64 = oracle.widen(W, xdt)
@@ -390,37 +391,50 @@ def _check_pipeline(X, xdt, W, k, lam, V, eps, A, B, n_blocks=1):
     for h in range(n_blocks):
         lam_r, V_r = oracle.eigh(C[h])
         eps_r = oracle.error_curve(lam_r)
+        if C_gpu is not None:  # diagnostic: the accumulation's share of the error (LAPACK on the GPU's C)
+            Cg = np.triu(C_gpu[h]).astype(np.float64)
+            lg = np.linalg.eigvalsh(Cg + np.triu(Cg, 1).T)[::-1]
+            eg = oracle.error_curve(lg)
+            big = eps_r >= 1e-4 * eps_r[0]
+            print("head %d accumulation only: eps rel %.2e, tail %.2e eps_0" % (
+                h, np.max(np.abs(eg[big] - eps_r[big]) / eps_r[big]),
+                np.max(np.abs(eg[~big] - eps_r[~big])) / eps_r[0] if (~big).any() else 0.0))
         el = check_lambda(lam[h], lam_r)
-        ee = check_eps(eps[h], eps_r)
         s = sin_theta_max(V[h], V_r, k)
         Wh = W64[:, h * hd:(h + 1) * hd]
         # the GPU factors reach the closed-form error: ||X W - X A B||^2 = eps_k (test-side fp64)
         R = X64 @ (Wh - A[h].astype(np.float64) @ B[h].astype(np.float64))
         direct = float(np.sum(R * R))
-        print("head %d: lambda %.2e, eps %.2e/%.2e, sin theta %.2e (gap %.2e), direct/eps_k - 1 = %.2e"
-              % (h, el, ee[0], ee[1], s, gap(lam_r, k), direct / eps_r[k] - 1))
+        big = eps_r >= 1e-4 * eps_r[0]
+        print("head %d: lambda %.2e, eps rel %.2e, tail %.2e eps_0, sin theta %.2e (gap %.2e), direct/eps_k - 1 = %.2e"
+              % (h, el, np.max(np.abs(eps[h][big] - eps_r[big]) / eps_r[big]),
+                 np.max(np.abs(eps[h][~big] - eps_r[~big])) / eps_r[0] if (~big).any() else 0.0, s, gap(lam_r, k),
+                 direct / eps_r[k] - 1))
+        check_eps(eps[h], eps_r)
         assert s <= 1e-3
         assert abs(direct - eps_r[k]) <= 1e-4 * eps_r[k] + 1e-6 * eps_r[0]
 
 
-def test_pipeline_single_layer(lrc):
-    _say("pipeline single layer 2048 x 256 -> 256, k = 64")
+@pytest.mark.parametrize("prec", [1, 2])
+def test_pipeline_single_layer(lrc, prec):
+    _say("pipeline single layer 2048 x 256 -> 256, k = 64, prec %d" % prec)
     d = inputs.single_layer()
-    out = _pipeline(lrc, d["X"], "f32", d["W"], 64)
-    _check_pipeline(d["X"], "f32", d["W"], 64, *out)
+    out = _pipeline(lrc, d["X"], "f32", d["W"], 64, prec=prec)
+    _check_pipeline(d["X"], "f32", d["W"], 64, *out[:5], C_gpu=out[5])
 
 
-def test_pipeline_block_scaled(lrc):
-    _say("pipeline scaled block 16384 x 512 -> 640")
+@pytest.mark.parametrize("prec", [1, 2])
+def test_pipeline_block_scaled(lrc, prec):
+    _say("pipeline scaled block 16384 x 512 -> 640, prec %d" % prec)
     X = inputs.block_activations(512, 16384)
     W = inputs.weight(512, 640, "bf16", inputs.CFG_BLOCK, 0, 0)
     k = inputs.rank_at_ratio(512, 640, 0.6)
-    out = _pipeline(lrc, X, "bf16", W, k)
-    _check_pipeline(X, "bf16", W, k, *out)
+    out = _pipeline(lrc, X, "bf16", W, k, prec=prec)
+    _check_pipeline(X, "bf16", W, k, *out[:5], C_gpu=out[5])
 
 
 def test_pipeline_per_head_scaled(lrc):
     _say("pipeline per-head 8192 x 512, 4 heads of 128, k = 32")
     d = inputs.per_head(n_tok=8192, d_model=512, head_dim=128)
     out = _pipeline(lrc, d["X"], "bf16", d["W"], 32, n_blocks=4)
-    _check_pipeline(d["X"], "bf16", d["W"], 32, *out, n_blocks=4)
+    _check_pipeline(d["X"], "bf16", d["W"], 32, *out[:5], n_blocks=4, C_gpu=out[5])
