@@ -1,0 +1,250 @@
+"""Benchmark: activation-aware truncated SVD of one LLaMA-7B-shaped block on one MI355X.
+
+Workload (one "step" = the whole path over one batch of synthetic calibration data):
+  * block: q/k/v/o 4096x4096, gate/up 4096x11008, down 11008x4096 (Y = X W orientation), bf16
+    weights ~ N(0, 0.02^2); calibration 256 sequences x 2048 tokens = 524288 tokens, X = N(0,1)
+    times a per-channel lognormal(0,1) scale, bf16 (the down projection gets its own X of width
+    11008 drawn the same way); rank for 60% of each matrix's parameters (1228 / 1791).
+  * per matrix: covariance C = sum Y^T Y (lrc_cov_accumulate), eigendecomposition (lrc_eigh),
+    error curve (lrc_error_curve), factors A = W V_k, B = V_k^T (lrc_factorize);
+  * over the block: Fisher scores of synthetic gradients ~ N(0, 1e-4^2) (lrc_fisher_scores) and
+    the greedy allocation of the same 60% parameter budget from the error curves
+    (lrc_allocate_ranks; its ranks are reported, the factors use the per-matrix 60% ranks).
+Inputs are generated on the GPU (torch's seeded generator) and are resident in HBM before the
+timed region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+MATS = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+
+
+def shapes(d_model, d_ff):
+    return {"q_proj": (d_model, d_model), "k_proj": (d_model, d_model), "v_proj": (d_model, d_model),
+            "o_proj": (d_model, d_model), "gate_proj": (d_model, d_ff), "up_proj": (d_model, d_ff),
+            "down_proj": (d_ff, d_model)}
+
+
+def cov_flops(n_tok, d_in, d_out):
+    """Algorithmic flops of C += (XW)^T(XW): the GEMM plus the upper triangle of the SYRK."""
+    return n_tok * (2 * d_in * d_out + d_out * (d_out + 1))
+
+
+def gen_inputs(torch, n_tok, d_model, d_ff, seed, dev):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+
+    def act(width):
+        scale = torch.exp(torch.randn(width, generator=g, device=dev, dtype=torch.float32))
+        X = torch.empty(n_tok, width, dtype=torch.bfloat16, device=dev)
+        for r0 in range(0, n_tok, 65536):
+            r1 = min(n_tok, r0 + 65536)
+            X[r0:r1] = (torch.randn(r1 - r0, width, generator=g, device=dev, dtype=torch.float32) * scale).to(
+                torch.bfloat16)
+        return X
+
+    X = act(d_model)
+    Xd = act(d_ff)
+    W, G = {}, {}
+    for m, (di, do) in shapes(d_model, d_ff).items():
+        W[m] = (torch.randn(di, do, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        G[m] = (torch.randn(di, do, generator=g, device=dev) * 1e-4).to(torch.bfloat16)
+    return X, Xd, W, G
+
+
+def cpu_baseline(d_model, d_ff, sample_tok):
+    """The fp64 oracle's covariance throughput on a bounded token sample of the same block."""
+    import numpy as np
+
+    import oracle
+    from activation_aware_rank_amd import inputs
+    X = inputs.block_activations(d_model, sample_tok)
+    Xd = inputs.block_activations(d_ff, sample_tok, feeds_down=True)
+    Ws = {m: inputs.block_weight(m, d_model, d_ff) for m in MATS}
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    for m in MATS:
+        oracle.covariance(Xd if m == "down_proj" else X, "bf16", Ws[m], "bf16")
+    dt = time.perf_counter() - t0
+    return {"value": sample_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 direct covariance (Y = XW, C = Y^T Y) of all 7 block matrices over %d tokens "
+                      "(%.1f s); eigendecomposition, error curve and factors excluded, so this is an upper "
+                      "bound on the oracle's whole-step throughput" % (sample_tok, dt),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--tokens", type=int, default=524288)
+    ap.add_argument("--d-model", type=int, default=4096)
+    ap.add_argument("--d-ff", type=int, default=11008)
+    ap.add_argument("--ratio", type=float, default=0.6)
+    ap.add_argument("--prec", choices=("f32", "f64"), default="f32", help="eigensolver working precision")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--seed", type=int, default=20261203)
+    ap.add_argument("--breakdown", action="store_true", help="print per-call timings to stderr")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py runs on exactly one GPU; --gpus %d is not supported (the path would shard matrices "
+              "or token ranges across GPUs, see DESIGN.md)" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from activation_aware_rank_amd import lrc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    prec = lrc.LRC_F32 if a.prec == "f32" else lrc.LRC_F64
+    sh = shapes(a.d_model, a.d_ff)
+    ks = {m: int(np.floor(a.ratio * di * do / (di + do))) for m, (di, do) in sh.items()}
+    X, Xd, W, G = gen_inputs(torch, a.tokens, a.d_model, a.d_ff, a.seed, dev)
+    # outputs and workspaces allocated once, outside the timed region
+    C = {m: torch.empty(do, do, dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
+    lam = {m: torch.empty(do, dtype=torch.float64, device=dev) for m, (di, do) in sh.items()}
+    V = {m: torch.empty(do, ks[m], dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
+    eps = {m: torch.empty(do + 1, dtype=torch.float64, device=dev) for m, (di, do) in sh.items()}
+    A = {m: torch.empty(di, ks[m], dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
+    B = {m: torch.empty(ks[m], do, dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
+    info = torch.zeros(8, dtype=torch.int32, device=dev)
+    ws_cov = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, di, True, do, 1)
+                             for di, do in sh.values()), dtype=torch.uint8, device=dev)
+    ws_eig = torch.empty(max(lrc.lrc_eigh_workspace(do, 1, ks[m], prec) for m, (di, do) in sh.items()),
+                         dtype=torch.uint8, device=dev)
+    kcap = {m: (di * do) // (di + do) for m, (di, do) in sh.items()}
+    offs_h = [0] + list(np.cumsum([kcap[m] for m in MATS]))
+    offs = torch.tensor(offs_h, dtype=torch.int64, device=dev)
+    lam_packed = torch.empty(int(offs_h[-1]), dtype=torch.float64, device=dev)
+    eps0 = torch.empty(len(MATS), dtype=torch.float64, device=dev)
+    cost = torch.tensor([sum(sh[m]) for m in MATS], dtype=torch.int64, device=dev)
+    budget = int(np.floor(a.ratio * sum(di * do for di, do in sh.values())))
+    ws_alc = torch.empty(lrc.lrc_allocate_ranks_workspace(len(MATS), lam_packed.numel()), dtype=torch.uint8,
+                         device=dev)
+    ws_fsh = torch.empty(lrc.lrc_fisher_scores_workspace([G[m].numel() for m in MATS]), dtype=torch.uint8,
+                         device=dev)
+    alpha = torch.empty(len(MATS), dtype=torch.float64, device=dev)
+    k_out = torch.empty(len(MATS), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(times):
+        for i, m in enumerate(MATS):
+            xin = Xd if m == "down_proj" else X
+            C[m].zero_()
+            e0 = ev()
+            lrc.lrc_cov_accumulate(xin, W[m], C[m], info=info[i:i + 1], ws=ws_cov)
+            e1 = ev()
+            lrc.lrc_eigh(C[m], ks[m], prec=prec, lam=lam[m][None], V=V[m][None], info=info[7:8], ws=ws_eig)
+            e2 = ev()
+            lrc.lrc_error_curve(lam[m], eps=eps[m])
+            e3 = ev()
+            lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m])
+            e4 = ev()
+            times.append((m, e0, e1, e2, e3, e4))
+        e5 = ev()
+        lrc.lrc_fisher_scores([G[m] for m in MATS], [W[m] for m in MATS], alpha=alpha, ws=ws_fsh)
+        for i, m in enumerate(MATS):  # gather lambda_m[:K_m] and eps_{m,0} (device copies)
+            lam_packed[offs_h[i]:offs_h[i] + kcap[m]].copy_(lam[m][:kcap[m]])
+            eps0[i:i + 1].copy_(eps[m][0:1])
+        e6 = ev()
+        lrc.lrc_allocate_ranks(alpha, lam_packed, offs, eps0, cost, budget, k_out=k_out, ws=ws_alc)
+        e7 = ev()
+        times.append(("fisher", e5, e6, None, None, None))
+        times.append(("alloc", e6, e7, None, None, None))
+
+    for _ in range(a.warmup):
+        step([])
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        r = []
+        step(r)
+        recs.append(r)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
+
+    # per-call times from the events (ms), averaged over steps
+    def el(x, y):
+        return x.elapsed_time(y)
+
+    per = {}
+    for r in recs:
+        for m, e0, e1, e2, e3, e4 in r:
+            if m in ("fisher", "alloc"):
+                per.setdefault(m, []).append(el(e0, e1))
+            else:
+                per.setdefault(m + ".cov", []).append(el(e0, e1))
+                per.setdefault(m + ".eigh", []).append(el(e1, e2))
+                per.setdefault(m + ".err", []).append(el(e2, e3))
+                per.setdefault(m + ".fac", []).append(el(e3, e4))
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    step_ms = wall * 1000.0 / a.steps
+    cov_ms = sum(avg[m + ".cov"] for m in MATS)
+    eig_ms = sum(avg[m + ".eigh"] for m in MATS)
+    cov_flops_total = sum(cov_flops(a.tokens, di, do) for di, do in sh.values())
+    cov_tflops = cov_flops_total / (cov_ms / 1000.0) / 1e12
+    layer_s = (avg["q_proj.cov"] + avg["q_proj.eigh"] + avg["q_proj.err"] + avg["q_proj.fac"]) / 1000.0
+    if a.breakdown:
+        for k in sorted(avg):
+            print("%-20s %10.3f ms" % (k, avg[k]), file=sys.stderr)
+    # dominant op of the step by time, with its roofline
+    dominant = "cov" if cov_ms >= eig_ms else "eigh"
+    if dominant == "cov":
+        roof = {"kernel": "lrc_cov_accumulate (k_cov_gemm_y + k_cov_syrk per 32768-token chunk)",
+                "bound": "mfma", "achieved": cov_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": cov_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                "per_launch": "N (2 d_in d_out + d_out (d_out+1)) algorithmic flops per call, N = %d" % a.tokens}
+    else:
+        n = a.d_ff
+        tri_bytes = sum((n - c - 1) ** 2 / 2 for c in range(0, n - 1)) * (4 if prec == lrc.LRC_F32 else 8)
+        ms = avg["gate_proj.eigh"]
+        roof = {"kernel": "lrc_eigh n=%d (tridiagonalisation symv-bound)" % n, "bound": "hbm",
+                "achieved": tri_bytes / (ms / 1000.0) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": tri_bytes / (ms / 1000.0) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                "per_launch": "sum over columns of the trailing lower triangle, %d-byte elements"
+                              % (4 if prec == lrc.LRC_F32 else 8)}
+    out = {
+        "metric": "calibration tokens/s into Y^T Y; sec per 4096x4096 layer compressed (eig incl.)",
+        "value": a.tokens / (step_ms / 1000.0),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": step_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded, generated on the GPU)",
+        "config": {"workload": "LLaMA-7B-shaped block: q/k/v/o 4096x4096, gate/up 4096x11008, down 11008x4096, "
+                               "%d calibration tokens, 60%% params per matrix, eig prec %s" % (a.tokens, a.prec),
+                   "tokens": a.tokens, "d_model": a.d_model, "d_ff": a.d_ff, "ranks": ks,
+                   "allocated_ranks": dict(zip(MATS, k_out.cpu().tolist()))},
+        "sec_per_4096_layer": layer_s,
+        "cov_tokens_per_s": a.tokens / (cov_ms / 1000.0),
+        "cov_ms": cov_ms, "eigh_ms": eig_ms,
+        "breakdown_ms": {k: round(v, 3) for k, v in avg.items()},
+        "roofline": roof,
+    }
+    if a.cpu_sample > 0:
+        out["cpu_baseline"] = cpu_baseline(a.d_model, a.d_ff, a.cpu_sample)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
