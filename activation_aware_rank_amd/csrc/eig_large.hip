@@ -5,10 +5,10 @@
 //  1. Householder tridiagonalisation Q^T C Q = T, blocked (panel of NB columns, then a rank-2NB
 //     update of the trailing matrix), working precision T_ (fp32 or fp64).  The matrix is kept
 //     in full (both triangles) so the symmetric matrix-vector product of each column is a plain
-//     row-wise product with coalesced rows.
-//  2. All n eigenvalues of T by bisection on Sturm counts, fp64, one thread per eigenvalue.
+//     row-wise product with coalesced rows; three launches per column.
+//  2. All n eigenvalues of T by multisection on Sturm counts, fp64, 16 lanes per eigenvalue.
 //  3. Eigenvectors of T for the n_vec largest eigenvalues by inverse iteration, fp64, one thread
-//     per vector (LU with partial pivoting of T - lambda I, recomputed each iteration); vectors of
+//     per vector (LU with partial pivoting of T - lambda I once, then three solves); vectors of
 //     eigenvalues closer than a cluster tolerance are re-orthogonalised by modified Gram-Schmidt.
 //  4. Back-transformation V = Q Z with the reflectors grouped in blocks of NBT,
 //     Q_b = I - V_b T_b V_b^T (compact WY), applied from the last block to the first, in fp64.
@@ -24,7 +24,7 @@ namespace lrc {
 constexpr int NB = 32;    // tridiagonalisation panel width
 constexpr int NBT = 32;   // back-transformation block of reflectors
 constexpr int RCH = 512;  // rows per partial in the back-transformation reductions
-constexpr int SYMV_ROWS = 16;  // rows per block in the symmetric product
+constexpr int SYMV_BLOCKS = 128;  // blocks of 16 waves in the symmetric product (rows strided over them)
 
 // ---------------------------------------------------------------------------------------------
 // 1. tridiagonalisation
@@ -60,163 +60,208 @@ __device__ __forceinline__ T block_sum(T v, T *sh) {
     return r;  // every thread
 }
 
-// A[r][c] -= sum_{q<j} V[r][q] W[c][q] + W[r][q] V[c][q] for r in [c, n); partial sum of squares of
-// rows r >= c+2 (the part of the column below the reflector's leading entry)
+// Each column of a panel takes three launches; each global reduction is done by the next launch,
+// redundantly in every block that needs it and always in the same fixed order, so all blocks see
+// bit-identical values (no atomics, no device-wide fences):
+//   k_trd_col : finish W[:, j-1] (reduces the previous column's w1.v partials), update column c,
+//               partials of ||x||^2
+//   k_trd_symv: reflector of column c (reduces the ||x||^2 partials; block 0 stores d[c], e[c],
+//               tau[c]); v into V[:, j] and Rt[c]; w_raw = A v over the trailing rows; partials of
+//               W^T v and V^T v
+//   k_trd_w1  : w1 = tau (w_raw - V q1 - W q2) (reduces the q partials); partials of w1.v
+// W[:, j] = w1 - (tau/2)(w1.v) v is formed by the next k_trd_col (or k_trd_wlast at panel end).
+
+// fixed-order sum of p[0..np) by one block: strided per-thread sums, then a tree (every thread)
 template <class T>
-__global__ void __launch_bounds__(256) k_col_update(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
-                                                    const T *__restrict__ Vp, const T *__restrict__ Wp,
-                                                    T *__restrict__ part) {
+__device__ __forceinline__ T block_sum_array(const T *__restrict__ p, int np, T *red) {
+    T acc = T(0);
+    for (int i = threadIdx.x; i < np; i += blockDim.x) acc += p[i];
+    return block_sum(acc, red);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) k_trd_col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
+                                                 T *__restrict__ Vp, T *__restrict__ Wp, const T *__restrict__ w1buf,
+                                                 T *__restrict__ colbuf, T *__restrict__ part, const T *__restrict__ dpart,
+                                                 int ndp, const T *__restrict__ tau, double *__restrict__ d) {
     __shared__ T sh[4];
     __shared__ T vc[NB], wc[NB];
-    if (threadIdx.x < j) {
-        vc[threadIdx.x] = Vp[c * NB + threadIdx.x];
-        wc[threadIdx.x] = Wp[c * NB + threadIdx.x];
+    T half = T(0);
+    if (j > 0) half = T(0.5) * tau[c - 1] * block_sum_array(dpart, ndp, sh);
+    if (threadIdx.x < NB) {
+        const int q = threadIdx.x;
+        vc[q] = q < j ? Vp[c * NB + q] : T(0);
+        T wv = q < j ? Wp[c * NB + q] : T(0);
+        if (q == j - 1) wv = w1buf[c] - half * Vp[c * NB + q];  // row c of the column being finished
+        wc[q] = wv;
     }
     __syncthreads();
     const int64_t r = c + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     T ss = T(0);
     if (r < n) {
+        T wl = T(0);
+        if (j > 0) {  // finish W[r][j-1] for this row
+            wl = w1buf[r] - half * Vp[r * NB + j - 1];
+            Wp[r * NB + j - 1] = wl;
+        }
         T a = A[r * lda + c];
-        for (int q = 0; q < j; ++q) a -= Vp[r * NB + q] * wc[q] + Wp[r * NB + q] * vc[q];
+        for (int q = 0; q < j; ++q) {
+            const T wr = (q == j - 1) ? wl : Wp[r * NB + q];
+            a -= Vp[r * NB + q] * wc[q] + wr * vc[q];
+        }
         A[r * lda + c] = a;
+        colbuf[r] = a;
         if (r >= c + 2) ss = a * a;
+        if (r == c) d[c] = double(a);
     }
     ss = block_sum(ss, sh);
     if (threadIdx.x == 0) part[blockIdx.x] = ss;
 }
 
-// One block: the reflector of column c from the updated column, and its vector v (v[c+1] = 1).
+// w_raw[r] = sum_{k > c} A[r][k] v[k] for rows r in [c+1, n), one row per wave at a time (rows
+// strided over the grid), read with 16-byte loads from the aligned column kb <= c+1 (v[k] = 0 for
+// k <= c).  Also stores v in V[:, j] and Rt[c], and the block partials of W^T v and V^T v.
+constexpr int SYMV_WAVES = 16;
 template <class T>
-__global__ void __launch_bounds__(1024) k_householder(T *__restrict__ A, int64_t lda, int64_t n, int64_t c,
-                                                      const T *__restrict__ part, int npart, T *__restrict__ vbuf,
-                                                      T *__restrict__ Rt, int64_t ldr, T *__restrict__ tau,
-                                                      double *__restrict__ d, double *__restrict__ e, T *__restrict__ scal) {
-    __shared__ T sh[16];
-    __shared__ T s_scale;
-    T acc = T(0);
-    if (threadIdx.x == 0)
-        for (int i = 0; i < npart; ++i) acc += part[i];  // fixed order
-    if (threadIdx.x == 0) {
-        const T sigma2 = acc;
-        const T alpha = A[(c + 1) * lda + c];
-        T beta, tv, scale;
-        if (sigma2 == T(0)) {
-            tv = T(0);
-            beta = alpha;
-            scale = T(0);
-        } else {
-            const T nrm = sqrt(alpha * alpha + sigma2);
-            beta = alpha >= T(0) ? -nrm : nrm;
-            tv = (beta - alpha) / beta;
-            scale = T(1) / (alpha - beta);
-        }
-        d[c] = double(A[c * lda + c]);
+__global__ void __launch_bounds__(SYMV_WAVES * 64) k_trd_symv(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c,
+                                                              int j, const T *__restrict__ colbuf,
+                                                              const T *__restrict__ part, int npart,
+                                                              T *__restrict__ Vp, const T *__restrict__ Wp,
+                                                              T *__restrict__ Rt, T *__restrict__ wbuf,
+                                                              T *__restrict__ qpart, T *__restrict__ tau,
+                                                              double *__restrict__ e) {
+    constexpr int VEC = 16 / sizeof(T);
+    constexpr int NW = SYMV_WAVES;
+    typedef T vec_t __attribute__((ext_vector_type(VEC)));
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    T *vs = reinterpret_cast<T *>(smem_raw);  // v[kb .. n)
+    __shared__ T sh[NW];
+    // the reflector of column c: alpha = x[0], sigma2 = ||x[1:]||^2; tau = (beta - alpha)/beta,
+    // v = [1, x[1:] / (alpha - beta)], beta = -sign(alpha) ||x||; tau = 0 when x[1:] = 0
+    const T sigma2 = block_sum_array(part, npart, sh);
+    const T alpha = colbuf[c + 1];
+    T beta, tv, scale;
+    if (sigma2 == T(0)) {
+        tv = T(0);
+        beta = alpha;
+        scale = T(0);
+    } else {
+        const T nrm = sqrt(alpha * alpha + sigma2);
+        beta = alpha >= T(0) ? -nrm : nrm;
+        tv = (beta - alpha) / beta;
+        scale = T(1) / (alpha - beta);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         e[c] = double(beta);
         tau[c] = tv;
-        scal[0] = tv;
-        s_scale = scale;
     }
-    __syncthreads();
-    const T scale = s_scale;
-    for (int64_t r = threadIdx.x; r < n; r += blockDim.x) {
-        T v;
-        if (r <= c) v = T(0);
-        else if (r == c + 1) v = T(1);
-        else v = A[r * lda + c] * scale;
-        if (r > c) vbuf[r] = v;
-        Rt[c * ldr + r] = v;
+    const int64_t kb = (c + 1) / VEC * VEC;
+    const int64_t m = n - kb;
+    const int64_t mv = m / VEC;
+    for (int64_t k = threadIdx.x; k < m; k += blockDim.x) {
+        const int64_t kk = kb + k;
+        vs[k] = kk <= c ? T(0) : (kk == c + 1 ? T(1) : colbuf[kk] * scale);
     }
-}
-
-// w_raw[r] = sum_{k > c} A[r][k] v[k] for rows r in [c+1, n), SYMV_ROWS rows per block (one wave
-// per row at a time); block partials of q1 = W^T v and q2 = V^T v over the block's rows.
-template <class T>
-__global__ void __launch_bounds__(256) k_symv(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c,
-                                              const T *__restrict__ vbuf, T *__restrict__ wbuf, const T *__restrict__ Vp,
-                                              const T *__restrict__ Wp, int j, T *__restrict__ qpart) {
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    T *vs = reinterpret_cast<T *>(smem_raw);  // v[c+1 .. n)
-    const int64_t m = n - c - 1;
-    for (int64_t k = threadIdx.x; k < m; k += blockDim.x) vs[k] = vbuf[c + 1 + k];
+    if (blockIdx.x == 0)  // the reflector's zeros above row c+1
+        for (int64_t k = threadIdx.x; k <= c; k += blockDim.x) Rt[c * n + k] = T(0);
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t rbase = c + 1 + int64_t(blockIdx.x) * SYMV_ROWS;
-    for (int rr = wave; rr < SYMV_ROWS; rr += 4) {
-        const int64_t r = rbase + rr;
-        if (r >= n) break;
-        const T *row = A + r * lda + c + 1;
-        T acc = T(0);
-        for (int64_t k = lane; k < m; k += 64) acc += row[k] * vs[k];
-        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-        if (lane == 0) wbuf[r] = acc;
-    }
-    // q partials: thread q (< 2j) sums over the block's rows
-    const int t = threadIdx.x;
-    if (t < 2 * j) {
-        const int q = t % j;
-        const T *src = t < j ? Wp : Vp;
-        T acc = T(0);
-        for (int rr = 0; rr < SYMV_ROWS; ++rr) {
-            const int64_t r = rbase + rr;
-            if (r >= n) break;
-            acc += src[r * NB + q] * vs[r - c - 1];
+    const int64_t nrows = n - c - 1;
+    const int64_t wstride = int64_t(gridDim.x) * NW;
+    T qw = T(0), qv = T(0);
+    const vec_t *vs4 = reinterpret_cast<const vec_t *>(vs);
+    for (int64_t rr = int64_t(blockIdx.x) * NW + wave; rr < nrows; rr += wstride) {
+        const int64_t r = c + 1 + rr;
+        const T *row = A + r * lda + kb;
+        const vec_t *row4 = reinterpret_cast<const vec_t *>(row);
+        T acc0 = T(0), acc1 = T(0), acc2 = T(0), acc3 = T(0);
+        int64_t kv = lane;
+        for (; kv + 192 < mv; kv += 256) {
+            const vec_t a0 = __builtin_nontemporal_load(row4 + kv), a1 = __builtin_nontemporal_load(row4 + kv + 64);
+            const vec_t a2 = __builtin_nontemporal_load(row4 + kv + 128), a3 = __builtin_nontemporal_load(row4 + kv + 192);
+            const vec_t b0 = vs4[kv], b1 = vs4[kv + 64], b2 = vs4[kv + 128], b3 = vs4[kv + 192];
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) {
+                acc0 += a0[q] * b0[q];
+                acc1 += a1[q] * b1[q];
+                acc2 += a2[q] * b2[q];
+                acc3 += a3[q] * b3[q];
+            }
         }
-        qpart[int64_t(blockIdx.x) * 2 * NB + t] = acc;
+        for (; kv < mv; kv += 64) {
+            const vec_t a0 = row4[kv], b0 = vs4[kv];
+#pragma unroll
+            for (int q = 0; q < VEC; ++q) acc0 += a0[q] * b0[q];
+        }
+        for (int64_t k = mv * VEC + lane; k < m; k += 64) acc0 += row[k] * vs[k];
+        T acc = (acc0 + acc1) + (acc2 + acc3);
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        const T vr = vs[r - kb];
+        if (lane == 0) {
+            wbuf[r] = acc;
+            Rt[c * n + r] = vr;
+            Vp[r * NB + j] = vr;
+        }
+        if (lane < j) {
+            qw += Wp[r * NB + lane] * vr;
+            qv += Vp[r * NB + lane] * vr;
+        }
+    }
+    __shared__ T qs[NW][2 * NB];
+    if (lane < NB) {
+        qs[wave][lane] = lane < j ? qw : T(0);
+        qs[wave][NB + lane] = lane < j ? qv : T(0);
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < 2 * NB) {
+        T sum = T(0);
+        for (int w = 0; w < NW; ++w) sum += qs[w][t];
+        qpart[int64_t(blockIdx.x) * 2 * NB + t] = sum;
     }
 }
 
-// q[t] = sum over blocks of qpart (fixed order); one block
+// w1[r] = tau (w_raw[r] - V[r][:j] q1 - W[r][:j] q2) for r in [c+1, n); partials of w1.v
 template <class T>
-__global__ void k_qreduce(const T *__restrict__ qpart, int nblk, int j, T *__restrict__ q) {
-    const int t = threadIdx.x;
-    if (t >= 2 * j) return;
-    T acc = T(0);
-    for (int b = 0; b < nblk; ++b) acc += qpart[int64_t(b) * 2 * NB + t];
-    q[t] = acc;
-}
-
-// w[r] = tau (w_raw[r] - V[r] q1 - W[r] q2); partial dots w.v
-template <class T>
-__global__ void __launch_bounds__(256) k_wfinal1(int64_t n, int64_t c, const T *__restrict__ vbuf, T *__restrict__ wbuf,
-                                                 const T *__restrict__ Vp, const T *__restrict__ Wp, int j,
-                                                 const T *__restrict__ q, const T *__restrict__ scal, T *__restrict__ dpart) {
+__global__ void __launch_bounds__(256) k_trd_w1(int64_t n, int64_t c, int j, const T *__restrict__ Vp,
+                                                const T *__restrict__ Wp, const T *__restrict__ wbuf,
+                                                const T *__restrict__ qpart, int nqp, const T *__restrict__ tau,
+                                                T *__restrict__ w1buf, T *__restrict__ dpart) {
     __shared__ T sh[4];
+    __shared__ T red[4][2 * NB];
     __shared__ T qs[2 * NB];
-    if (threadIdx.x < 2 * j) qs[threadIdx.x] = q[threadIdx.x];
-    __syncthreads();
-    const T tv = scal[0];
+    {  // q[v] = sum over the symv blocks, fixed order: 4 strided sums per value, then in order
+        const int v = threadIdx.x % (2 * NB), sidx = threadIdx.x / (2 * NB);
+        T acc = T(0);
+        for (int b = sidx; b < nqp; b += 4) acc += qpart[int64_t(b) * 2 * NB + v];
+        red[sidx][v] = acc;
+        __syncthreads();
+        if (sidx == 0) qs[v] = (red[0][v] + red[1][v]) + (red[2][v] + red[3][v]);
+        __syncthreads();
+    }
+    const T tv = tau[c];
     const int64_t r = c + 1 + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     T dot = T(0);
     if (r < n) {
         T w = wbuf[r];
-        for (int k = 0; k < j; ++k) w -= Vp[r * NB + k] * qs[k] + Wp[r * NB + k] * qs[j + k];
+        for (int k = 0; k < j; ++k) w -= Vp[r * NB + k] * qs[k] + Wp[r * NB + k] * qs[NB + k];
         w *= tv;
-        wbuf[r] = w;
-        dot = w * vbuf[r];
+        w1buf[r] = w;
+        dot = w * Vp[r * NB + j];
     }
     dot = block_sum(dot, sh);
     if (threadIdx.x == 0) dpart[blockIdx.x] = dot;
 }
 
-// w -= (tau/2)(w.v) v; store V[:, j] = v, W[:, j] = w for rows r > c
+// W[r][j] = w1[r] - (tau/2)(w1.v) v[r] for the panel's last column (rows r > c)
 template <class T>
-__global__ void __launch_bounds__(256) k_wfinal2(int64_t n, int64_t c, const T *__restrict__ vbuf, const T *__restrict__ wbuf,
-                                                 T *__restrict__ Vp, T *__restrict__ Wp, int j, const T *__restrict__ scal,
-                                                 const T *__restrict__ dpart, int ndp) {
-    __shared__ T s_g;
-    if (threadIdx.x == 0) {
-        T g = T(0);
-        for (int i = 0; i < ndp; ++i) g += dpart[i];
-        s_g = g;
-    }
-    __syncthreads();
-    const T half = T(0.5) * scal[0] * s_g;
+__global__ void __launch_bounds__(256) k_trd_wlast(int64_t n, int64_t c, int j, const T *__restrict__ Vp,
+                                                   T *__restrict__ Wp, const T *__restrict__ w1buf,
+                                                   const T *__restrict__ dpart, int ndp, const T *__restrict__ tau) {
+    __shared__ T sh[4];
+    const T half = T(0.5) * tau[c] * block_sum_array(dpart, ndp, sh);
     const int64_t r = c + 1 + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (r < n) {
-        const T v = vbuf[r];
-        Vp[r * NB + j] = v;
-        Wp[r * NB + j] = wbuf[r] - half * v;
-    }
+    if (r < n) Wp[r * NB + j] = w1buf[r] - half * Vp[r * NB + j];
 }
 
 // A[r][s] -= sum_q V[r][q] W[s][q] + W[r][q] V[s][q]   for r, s in [p, n)   (64 x 64 tiles)
@@ -257,11 +302,6 @@ __global__ void __launch_bounds__(256) k_trailing(T *__restrict__ A, int64_t lda
             const int64_t r = r0 + ty * 4 + u, s = s0 + tx * 4 + w;
             if (r < n && s < n) A[r * lda + s] -= acc[u][w];
         }
-}
-
-template <class T>
-__global__ void k_last_diag(const T *__restrict__ A, int64_t lda, int64_t n, double *__restrict__ d) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) d[n - 1] = double(A[(n - 1) * lda + (n - 1)]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -315,21 +355,34 @@ __global__ void k_tri_prep(const double *__restrict__ d, const double *__restric
     }
 }
 
-// lam_asc[i] = i-th smallest eigenvalue of T
-__global__ void __launch_bounds__(64) k_bisect(const double *__restrict__ d, const double *__restrict__ e2, int64_t n,
-                                               const double *__restrict__ bounds, double *__restrict__ lam_asc) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= n) return;
+// lam_asc[i] = i-th smallest eigenvalue of T, by 16-way multisection: a group of 16 lanes owns one
+// eigenvalue; each pass the lanes count at 15 interior points of [lo, hi] and the group keeps the
+// sixteenth that holds eigenvalue i (about 14 passes to full fp64 accuracy).
+constexpr int MSEC = 16;
+__global__ void __launch_bounds__(256) k_bisect(const double *__restrict__ d, const double *__restrict__ e2, int64_t n,
+                                                const double *__restrict__ bounds, double *__restrict__ lam_asc) {
+    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t i = gid / MSEC;
+    const int sub = int(gid % MSEC);
+    if (i >= n) return;  // whole groups leave together (n * MSEC threads rounded to blocks)
     double lo = bounds[0], hi = bounds[1];
     const double pivmin = bounds[2];
     const double atol = DBL_EPSILON * bounds[3];  // absolute accuracy eps ||T||
-    for (int it = 0; it < 128; ++it) {
-        const double mid = 0.5 * (lo + hi);
-        if (mid <= lo || mid >= hi) break;
+    for (int it = 0; it < 24; ++it) {
         if (hi - lo <= 2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi)) + atol) break;
-        if (sturm_count(d, e2, n, mid, pivmin) > i) hi = mid; else lo = mid;
+        const double x = sub < MSEC - 1 ? lo + (hi - lo) * double(sub + 1) / double(MSEC) : hi;
+        const bool at_or_below = sub < MSEC - 1 && x > lo && x < hi && sturm_count(d, e2, n, x, pivmin) <= i;
+        const bool above = sub < MSEC - 1 && x > lo && x < hi && !at_or_below;
+        double nlo = at_or_below ? x : lo, nhi = above ? x : hi;
+        for (int o = MSEC / 2; o > 0; o >>= 1) {
+            nlo = fmax(nlo, __shfl_xor(nlo, o));
+            nhi = fmin(nhi, __shfl_xor(nhi, o));
+        }
+        if (nlo == lo && nhi == hi) break;  // no representable point strictly inside
+        lo = nlo;
+        hi = nhi;
     }
-    lam_asc[i] = 0.5 * (lo + hi);
+    if (sub == 0) lam_asc[i] = 0.5 * (lo + hi);
 }
 
 // lambda (descending) from lam_asc
@@ -354,44 +407,66 @@ __device__ __forceinline__ double hash_unit(uint64_t x) {
 __global__ void __launch_bounds__(64) k_invit(const double *__restrict__ d, const double *__restrict__ e, int64_t n,
                                               const double *__restrict__ lam_asc, const double *__restrict__ bounds,
                                               int64_t nv, double *__restrict__ Z, double *__restrict__ U0,
-                                              double *__restrict__ U1, double *__restrict__ U2) {
+                                              double *__restrict__ U1, double *__restrict__ U2, double *__restrict__ ML,
+                                              uint8_t *__restrict__ SW) {
     const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (j >= nv) return;
     const double lam = lam_asc[n - 1 - j];
     const double tnorm = bounds[3];
     const double tiny = DBL_EPSILON * fmax(tnorm, DBL_MIN);
-    // start vector
-    for (int64_t r = 0; r < n; ++r) Z[r * nv + j] = hash_unit(uint64_t(r) * 0x9E3779B97F4A7C15ULL + uint64_t(j) + 1);
-    for (int iter = 0; iter < 4; ++iter) {
-        // forward elimination with partial pivoting on T - lam I, applied to b = Z[:, j]
-        double u0 = d[0] - lam, u1 = n > 1 ? e[0] : 0.0, u2 = 0.0;  // current pivot-row candidates
-        double bcur = Z[j];
-        for (int64_t k = 0; k < n - 1; ++k) {
-            const double l = e[k], dd = d[k + 1] - lam, ee = k + 1 < n - 1 ? e[k + 1] : 0.0;
-            const double bnext = Z[(k + 1) * nv + j];
-            double p0, p1, p2, bp, n1, n2, bn;
-            if (fabs(l) > fabs(u0)) {  // swap rows k, k+1
-                const double mlt = u0 / l;
-                p0 = l; p1 = dd; p2 = ee; bp = bnext;
-                n1 = u1 - mlt * dd; n2 = u2 - mlt * ee; bn = bcur - mlt * bnext;
-            } else {
-                if (u0 == 0.0) u0 = tiny;
-                const double mlt = l / u0;
-                p0 = u0; p1 = u1; p2 = u2; bp = bcur;
-                n1 = dd - mlt * u1; n2 = ee - mlt * u2; bn = bnext - mlt * bcur;
-            }
-            U0[k * nv + j] = p0;
-            U1[k * nv + j] = p1;
-            U2[k * nv + j] = p2;
-            Z[k * nv + j] = bp;
-            u0 = n1; u1 = n2; u2 = 0.0; bcur = bn;
+    // LU with partial pivoting of T - lam I, once: rows k of U in (U0 = 1/pivot, U1, U2), the
+    // multiplier of step k in ML and whether rows k, k+1 were swapped in SW; the start vector is
+    // eliminated on the way
+    double u0 = d[0] - lam, u1 = n > 1 ? e[0] : 0.0, u2 = 0.0;
+    double bcur = hash_unit(uint64_t(j) + 1);
+    for (int64_t k = 0; k < n - 1; ++k) {
+        const double l = e[k], dd = d[k + 1] - lam, ee = k + 1 < n - 1 ? e[k + 1] : 0.0;
+        const double bnext = hash_unit(uint64_t(k + 1) * 0x9E3779B97F4A7C15ULL + uint64_t(j) + 1);
+        double p0, p1, p2, bp, mlt;
+        uint8_t sw;
+        if (fabs(l) > fabs(u0)) {
+            mlt = u0 / l;
+            sw = 1;
+            p0 = l; p1 = dd; p2 = ee; bp = bnext;
+            u0 = u1 - mlt * dd; u1 = u2 - mlt * ee; bcur = bcur - mlt * bnext;
+        } else {
+            if (u0 == 0.0) u0 = tiny;
+            mlt = l / u0;
+            sw = 0;
+            p0 = u0; p1 = u1; p2 = u2; bp = bcur;
+            u0 = dd - mlt * u1; u1 = ee - mlt * u2; bcur = bnext - mlt * bcur;
         }
-        if (u0 == 0.0) u0 = tiny;
-        // back substitution
-        double y2 = 0.0, y1 = bcur / u0, ymax = fabs(y1);
+        u2 = 0.0;
+        U0[k * nv + j] = 1.0 / p0;
+        U1[k * nv + j] = p1;
+        U2[k * nv + j] = p2;
+        ML[k * nv + j] = mlt;
+        SW[k * nv + j] = sw;
+        Z[k * nv + j] = bp;
+    }
+    if (u0 == 0.0) u0 = tiny;
+    U0[(n - 1) * nv + j] = 1.0 / u0;
+    Z[(n - 1) * nv + j] = bcur;
+    for (int iter = 0; iter < 3; ++iter) {
+        if (iter > 0) {  // apply the stored elimination to the new right-hand side
+            double bc = Z[j];
+            for (int64_t k = 0; k < n - 1; ++k) {
+                const double bn = Z[(k + 1) * nv + j], mlt = ML[k * nv + j];
+                if (SW[k * nv + j]) {
+                    Z[k * nv + j] = bn;
+                    bc = bc - mlt * bn;
+                } else {
+                    Z[k * nv + j] = bc;
+                    bc = bn - mlt * bc;
+                }
+            }
+            Z[(n - 1) * nv + j] = bc;
+        }
+        // back substitution with U, then scale by the largest entry
+        double y2 = 0.0, y1 = Z[(n - 1) * nv + j] * U0[(n - 1) * nv + j], ymax = fabs(y1);
         Z[(n - 1) * nv + j] = y1;
         for (int64_t k = n - 2; k >= 0; --k) {
-            const double y = (Z[k * nv + j] - U1[k * nv + j] * y1 - U2[k * nv + j] * y2) / U0[k * nv + j];
+            const double y = (Z[k * nv + j] - U1[k * nv + j] * y1 - U2[k * nv + j] * y2) * U0[k * nv + j];
             Z[k * nv + j] = y;
             ymax = fmax(ymax, fabs(y));
             y2 = y1;
@@ -400,9 +475,9 @@ __global__ void __launch_bounds__(64) k_invit(const double *__restrict__ d, cons
         const double inv = ymax > 0.0 ? 1.0 / ymax : 1.0;
         for (int64_t r = 0; r < n; ++r) Z[r * nv + j] *= inv;
     }
-    double s = 0.0;
-    for (int64_t r = 0; r < n; ++r) s += Z[r * nv + j] * Z[r * nv + j];
-    const double inv = s > 0.0 ? 1.0 / sqrt(s) : 0.0;
+    double s2 = 0.0;
+    for (int64_t r = 0; r < n; ++r) s2 += Z[r * nv + j] * Z[r * nv + j];
+    const double inv = s2 > 0.0 ? 1.0 / sqrt(s2) : 0.0;
     for (int64_t r = 0; r < n; ++r) Z[r * nv + j] *= inv;
 }
 
@@ -531,28 +606,25 @@ __global__ void __launch_bounds__(256) k_bt_g(const T *__restrict__ Rt, int64_t 
         for (int u = 0; u < NBT / 4; ++u) Gp[(int64_t(blockIdx.y) * NBT + ty + 4 * u) * nv + col] = acc[u];
 }
 
-// G = T (sum of partials)
+// G = T (sum of partials): thread (q, col) adds the partials of G[q][col] in chunk order, then
+// thread (a, col) forms sum_q T[a][q] G[q][col] from LDS.  Blocks of 8 columns x NBT.
+constexpr int GR_COLS = 256 / NBT;
 __global__ void __launch_bounds__(256) k_bt_greduce(const double *__restrict__ Gp, int nchunk, int64_t nv,
                                                     const double *__restrict__ Tf, double *__restrict__ G) {
-    __shared__ double Tm[NBT][NBT];
+    __shared__ double Tm[NBT][NBT + 1];
+    __shared__ double g[NBT][GR_COLS];
     for (int e = threadIdx.x; e < NBT * NBT; e += 256) Tm[e / NBT][e % NBT] = Tf[e];
+    const int q = threadIdx.x / GR_COLS, cl = threadIdx.x % GR_COLS;
+    const int64_t col = int64_t(blockIdx.x) * GR_COLS + cl;
+    double acc = 0.0;
+    if (col < nv)
+        for (int k = 0; k < nchunk; ++k) acc += Gp[(int64_t(k) * NBT + q) * nv + col];
+    g[q][cl] = acc;
     __syncthreads();
-    const int64_t col = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (col >= nv) return;
-    double g[NBT];
-#pragma unroll
-    for (int q = 0; q < NBT; ++q) {
-        double s = 0.0;
-        for (int k = 0; k < nchunk; ++k) s += Gp[(int64_t(k) * NBT + q) * nv + col];
-        g[q] = s;
-    }
-#pragma unroll
-    for (int a = 0; a < NBT; ++a) {
-        double s = 0.0;
-#pragma unroll
-        for (int q = 0; q < NBT; ++q) s += Tm[a][q] * g[q];
-        G[int64_t(a) * nv + col] = s;
-    }
+    double r = 0.0;
+#pragma unroll 8
+    for (int qq = 0; qq < NBT; ++qq) r += Tm[q][qq] * g[qq][cl];
+    if (col < nv) G[int64_t(q) * nv + col] = r;
 }
 
 // Z[r][col] -= sum_q Rt[c0+q][r] G[q][col] for r > c0
@@ -635,32 +707,32 @@ __global__ void k_set_info(int32_t *info, const int *bad) {
 // ---------------------------------------------------------------------------------------------
 template <class T>
 struct LargeWs {
-    T *A, *Rt, *Vp, *Wp, *tau, *vbuf, *wbuf, *part, *qpart, *q, *dpart, *scal;
-    double *d, *e, *e2, *bounds, *lam, *Z, *U0, *U1, *U2, *Sp, *Tf, *Gp, *G;
+    T *A, *Rt, *Vp, *Wp, *tau, *colbuf, *wbuf, *w1buf, *part, *qpart, *dpart;
+    double *d, *e, *e2, *bounds, *lam, *Z, *U0, *U1, *U2, *ML, *Sp, *Tf, *Gp, *G;
+    uint8_t *SW;
     int *bad;
     int64_t lda;
 };
 
-static int64_t nsymv_blocks(int64_t n) { return (n + SYMV_ROWS - 1) / SYMV_ROWS; }
+static int64_t nsymv_blocks(int64_t) { return SYMV_BLOCKS; }
 
 template <class C_, class T>
 static void layout(C_ &cv, LargeWs<T> &w, int64_t n, int64_t nv, bool count_only) {
     (void)count_only;
-    w.lda = n;
+    w.lda = (n + 63) / 64 * 64;
     const int64_t nv1 = nv > 0 ? nv : 1;
     const int64_t nch = (n + RCH - 1) / RCH;
-    w.A = cv.template carve<T>(size_t(n) * size_t(n));
+    w.A = cv.template carve<T>(size_t(n) * size_t(w.lda));
     w.Rt = cv.template carve<T>(size_t(n) * size_t(n));
     w.Vp = cv.template carve<T>(size_t(n) * NB);
     w.Wp = cv.template carve<T>(size_t(n) * NB);
     w.tau = cv.template carve<T>(size_t(n));
-    w.vbuf = cv.template carve<T>(size_t(n));
+    w.colbuf = cv.template carve<T>(size_t(n));
+    w.w1buf = cv.template carve<T>(size_t(n));
     w.wbuf = cv.template carve<T>(size_t(n));
     w.part = cv.template carve<T>(size_t((n + 255) / 256 + 1));
     w.qpart = cv.template carve<T>(size_t(nsymv_blocks(n)) * 2 * NB);
-    w.q = cv.template carve<T>(2 * NB);
     w.dpart = cv.template carve<T>(size_t((n + 255) / 256 + 1));
-    w.scal = cv.template carve<T>(4);
     w.d = cv.template carve<double>(size_t(n));
     w.e = cv.template carve<double>(size_t(n));
     w.e2 = cv.template carve<double>(size_t(n));
@@ -670,6 +742,8 @@ static void layout(C_ &cv, LargeWs<T> &w, int64_t n, int64_t nv, bool count_only
     w.U0 = cv.template carve<double>(size_t(n) * size_t(nv1));
     w.U1 = cv.template carve<double>(size_t(n) * size_t(nv1));
     w.U2 = cv.template carve<double>(size_t(n) * size_t(nv1));
+    w.ML = cv.template carve<double>(size_t(n) * size_t(nv1));
+    w.SW = cv.template carve<uint8_t>(size_t(n) * size_t(nv1));
     w.Sp = cv.template carve<double>(size_t(nch) * NBT * NBT);
     w.Tf = cv.template carve<double>(NBT * NBT);
     w.Gp = cv.template carve<double>(size_t(nch) * NBT * size_t(nv1));
@@ -702,52 +776,52 @@ static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *
     hipLaunchKernelGGL(k_fill_full<T>, dim3(2048), dim3(256), 0, s, C, ldc, n, w.A, lda, w.bad);
     LRC_LAUNCH_CHECK("k_fill_full");
     const size_t symv_smem = size_t(n) * sizeof(T);
-    LRC_HIP(hipFuncSetAttribute(reinterpret_cast<const void *>(k_symv<T>), hipFuncAttributeMaxDynamicSharedMemorySize,
+    LRC_HIP(hipFuncSetAttribute(reinterpret_cast<const void *>(k_trd_symv<T>), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 int(symv_smem)));
-    // 1. tridiagonalisation, panels over reflector columns 0 .. n-2
+    // 1. tridiagonalisation, panels over reflector columns 0 .. n-2 (three launches per column)
+    int ndp = 0;  // number of w1.v partials of the previous column
     for (int64_t p0 = 0; p0 < n - 1; p0 += NB) {
         const int64_t p1 = std::min<int64_t>(p0 + NB, n - 1);
-        hipLaunchKernelGGL(k_fill_zero<T>, dim3(64), dim3(256), 0, s, w.Vp, int64_t(n) * NB);
-        hipLaunchKernelGGL(k_fill_zero<T>, dim3(64), dim3(256), 0, s, w.Wp, int64_t(n) * NB);
+        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w.Vp, int64_t(n) * NB);
+        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w.Wp, int64_t(n) * NB);
         for (int64_t c = p0; c < p1; ++c) {
             const int j = int(c - p0);
             const int nbu = cdiv(n - c, 256);
-            hipLaunchKernelGGL(k_col_update<T>, dim3(nbu), dim3(256), 0, s, w.A, lda, n, c, j, w.Vp, w.Wp, w.part);
-            hipLaunchKernelGGL(k_householder<T>, dim3(1), dim3(1024), 0, s, w.A, lda, n, c, w.part, nbu, w.vbuf, w.Rt, n,
-                               w.tau, w.d, w.e, w.scal);
+            hipLaunchKernelGGL(k_trd_col<T>, dim3(nbu), dim3(256), 0, s, w.A, lda, n, c, j, w.Vp, w.Wp, w.w1buf,
+                               w.colbuf, w.part, w.dpart, ndp, w.tau, w.d);
             const int64_t m = n - c - 1;
-            const int nsb = cdiv(m, SYMV_ROWS);
-            hipLaunchKernelGGL(k_symv<T>, dim3(nsb), dim3(256), size_t(m) * sizeof(T), s, w.A, lda, n, c, w.vbuf, w.wbuf,
-                               w.Vp, w.Wp, j, w.qpart);
-            hipLaunchKernelGGL(k_qreduce<T>, dim3(1), dim3(64), 0, s, w.qpart, nsb, j, w.q);
-            const int nwb = cdiv(m, 256);
-            hipLaunchKernelGGL(k_wfinal1<T>, dim3(nwb), dim3(256), 0, s, n, c, w.vbuf, w.wbuf, w.Vp, w.Wp, j, w.q, w.scal,
-                               w.dpart);
-            hipLaunchKernelGGL(k_wfinal2<T>, dim3(nwb), dim3(256), 0, s, n, c, w.vbuf, w.wbuf, w.Vp, w.Wp, j, w.scal,
-                               w.dpart, nwb);
+            const int nsb = int(std::min<int64_t>(SYMV_BLOCKS, (m + SYMV_WAVES - 1) / SYMV_WAVES));
+            const int64_t kb = (c + 1) / (16 / int(sizeof(T))) * (16 / int(sizeof(T)));
+            hipLaunchKernelGGL(k_trd_symv<T>, dim3(nsb), dim3(SYMV_WAVES * 64), size_t(n - kb) * sizeof(T), s, w.A, lda,
+                               n, c, j, w.colbuf, w.part, nbu, w.Vp, w.Wp, w.Rt, w.wbuf, w.qpart, w.tau, w.e);
+            ndp = cdiv(m, 256);
+            hipLaunchKernelGGL(k_trd_w1<T>, dim3(ndp), dim3(256), 0, s, n, c, j, w.Vp, w.Wp, w.wbuf, w.qpart, nsb, w.tau,
+                               w.w1buf, w.dpart);
         }
         LRC_LAUNCH_CHECK("tridiagonal panel");
         const int jn = int(p1 - p0);
         if (p1 < n - 1) {
+            hipLaunchKernelGGL(k_trd_wlast<T>, dim3(cdiv(n - p1, 256)), dim3(256), 0, s, n, p1 - 1, jn - 1, w.Vp, w.Wp,
+                               w.w1buf, w.dpart, ndp, w.tau);
             const int64_t m = n - p1;
             dim3 g(cdiv(m, 64), cdiv(m, 64));
             hipLaunchKernelGGL(k_trailing<T>, g, dim3(256), 0, s, w.A, lda, n, p1, jn, w.Vp, w.Wp);
             LRC_LAUNCH_CHECK("k_trailing");
-        } else {
-            hipLaunchKernelGGL(k_col_update<T>, dim3(1), dim3(256), 0, s, w.A, lda, n, n - 1, jn, w.Vp, w.Wp, w.part);
-            LRC_LAUNCH_CHECK("k_col_update");
+        } else {  // last column: finish W[:, jn-1], update it, d[n-1]
+            hipLaunchKernelGGL(k_trd_col<T>, dim3(1), dim3(256), 0, s, w.A, lda, n, n - 1, jn, w.Vp, w.Wp, w.w1buf,
+                               w.colbuf, w.part, w.dpart, ndp, w.tau, w.d);
+            LRC_LAUNCH_CHECK("k_trd_col");
         }
     }
-    hipLaunchKernelGGL(k_last_diag<T>, dim3(1), dim3(64), 0, s, w.A, lda, n, w.d);
     // 2. eigenvalues
     hipLaunchKernelGGL(k_tri_prep, dim3(1), dim3(256), 0, s, w.d, w.e, n, w.e2, w.bounds);
-    hipLaunchKernelGGL(k_bisect, dim3(cdiv(n, 64)), dim3(64), 0, s, w.d, w.e2, n, w.bounds, w.lam);
+    hipLaunchKernelGGL(k_bisect, dim3(cdiv(n * MSEC, 256)), dim3(256), 0, s, w.d, w.e2, n, w.bounds, w.lam);
     hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(n, 256)), dim3(256), 0, s, w.lam, n, lambda, w.bad);
     LRC_LAUNCH_CHECK("bisection");
     if (nv > 0) {
         // 3. eigenvectors of T
         hipLaunchKernelGGL(k_invit, dim3(cdiv(nv, 64)), dim3(64), 0, s, w.d, w.e, n, w.lam, w.bounds, nv, w.Z, w.U0, w.U1,
-                           w.U2);
+                           w.U2, w.ML, w.SW);
         hipLaunchKernelGGL(k_cluster_mgs, dim3(unsigned(nv)), dim3(256), 0, s, w.lam, n, nv, w.bounds, w.Z);
         LRC_LAUNCH_CHECK("inverse iteration");
         // 4. back-transformation, last block of reflectors first
@@ -758,7 +832,7 @@ static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *
             hipLaunchKernelGGL(k_bt_gram<T>, dim3(nch), dim3(256), 0, s, w.Rt, n, n, c0, nb, w.Sp);
             hipLaunchKernelGGL(k_bt_tfactor<T>, dim3(1), dim3(256), 0, s, w.Sp, nch, w.tau, c0, nb, w.Tf);
             hipLaunchKernelGGL(k_bt_g<T>, dim3(cdiv(nv, 64), nch), dim3(256), 0, s, w.Rt, n, n, c0, nb, w.Z, nv, w.Gp);
-            hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, 256)), dim3(256), 0, s, w.Gp, nch, nv, w.Tf, w.G);
+            hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, GR_COLS)), dim3(256), 0, s, w.Gp, nch, nv, w.Tf, w.G);
             const int64_t mrows = n - c0 - 1;
             hipLaunchKernelGGL(k_bt_update<T>, dim3(cdiv(nv, 64), cdiv(mrows, 64)), dim3(256), 0, s, w.Rt, n, n, c0, nb,
                                w.G, w.Z, nv);
