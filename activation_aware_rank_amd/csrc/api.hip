@@ -2,7 +2,9 @@
 // Nothing is launched when validation fails.
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "lrc_internal.h"
 
@@ -23,6 +25,42 @@ lrc_status hip_fail(hipError_t e, const char *what) {
 }
 
 static bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------------------------------------
+// kernel timing records
+// ---------------------------------------------------------------------------------------------
+struct TimingRec {
+    std::string kernel;
+    hipEvent_t start, stop;
+    double flops;
+};
+static std::mutex g_tmu;
+static bool g_timing = false;
+static std::vector<TimingRec> g_recs;
+
+int timing_begin(const char *kernel, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (!g_timing) return -1;
+    TimingRec r;
+    r.kernel = kernel;
+    r.flops = 0.0;
+    if (hipEventCreate(&r.start) != hipSuccess) return -1;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+        (void)hipEventDestroy(r.start);
+        return -1;
+    }
+    (void)hipEventRecord(r.start, s);
+    g_recs.push_back(r);
+    return int(g_recs.size()) - 1;
+}
+
+void timing_end(int token, hipStream_t s, double flops) {
+    if (token < 0) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (token >= int(g_recs.size())) return;
+    (void)hipEventRecord(g_recs[token].stop, s);
+    g_recs[token].flops = flops;
+}
 
 }  // namespace lrc
 
@@ -50,6 +88,42 @@ const char *lrc_status_string(lrc_status s) {
 }
 
 const char *lrc_last_error(void) { return g_last_error.c_str(); }
+
+lrc_status lrc_timing_enable(int enable) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing = enable != 0;
+    return LRC_OK;
+}
+
+lrc_status lrc_timing_read(const char *kernel, int64_t *launches, double *total_ms, double *total_flops, int reset) {
+    REQUIRE(kernel && launches && total_ms && total_flops, LRC_ERR_ARG, "null argument");
+    std::lock_guard<std::mutex> lk(g_tmu);
+    int64_t n = 0;
+    double ms = 0.0, fl = 0.0;
+    for (auto &r : g_recs) {
+        if (r.kernel != kernel) continue;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float t = 0.f;
+        e = hipEventElapsedTime(&t, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        ms += double(t);
+        fl += r.flops;
+        ++n;
+    }
+    *launches = n;
+    *total_ms = ms;
+    *total_flops = fl;
+    if (reset) {
+        for (auto &r : g_recs) {
+            (void)hipEventSynchronize(r.stop);
+            (void)hipEventDestroy(r.start);
+            (void)hipEventDestroy(r.stop);
+        }
+        g_recs.clear();
+    }
+    return LRC_OK;
+}
 
 // ---------------------------------------------------------------------------------------------
 size_t lrc_cov_accumulate_workspace(lrc_dtype x_t, int64_t n_tok, int64_t d_in, int has_w, int64_t d_out,

@@ -57,6 +57,11 @@ struct Counter {
 
 inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
+// Kernel timing hooks (api.hip).  timing_begin returns a token (or -1 when timing is off) that
+// the caller passes to timing_end after launching the kernel on the same stream.
+int timing_begin(const char *kernel, hipStream_t s);
+void timing_end(int token, hipStream_t s, double flops);
+
 // ---------------------------------------------------------------------------------------------
 // device helpers
 // ---------------------------------------------------------------------------------------------

@@ -56,11 +56,15 @@ _chol_ws = _sig("lrc_cholesky_workspace", _sz, _i64)
 _chol = _sig("lrc_cholesky", _int, _vp, _i64, _i64, _vp, _sz, _vp, _vp)
 _trmm = _sig("lrc_trmm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp)
 _trsm = _sig("lrc_trsm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp)
+_tim_en = _sig("lrc_timing_enable", _int, _int)
+_tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
+               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _int)
 
 EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_accumulate_workspace",
             "lrc_cov_accumulate", "lrc_eigh_workspace", "lrc_eigh", "lrc_error_curve", "lrc_factorize",
             "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_allocate_ranks_workspace",
-            "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm", "lrc_trsm")
+            "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm", "lrc_trsm",
+            "lrc_timing_enable", "lrc_timing_read")
 
 
 class LrcError(RuntimeError):
@@ -295,6 +299,19 @@ def lrc_cholesky(A: torch.Tensor, info=None, ws=None, stream=None):
     info = _info(info, 1, A.device)
     _check(_chol(_ptr(A), n, lda, _ptr(w), wn, _ptr(info), _stream(stream)))
     return A, info
+
+
+def lrc_timing_enable(enable: bool = True):
+    _check(_tim_en(1 if enable else 0))
+
+
+def lrc_timing_read(kernel: str, reset: bool = True):
+    """(launches, total_ms, total_algorithmic_flops) recorded for one kernel name."""
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    fl = ctypes.c_double(0.0)
+    _check(_tim_rd(kernel.encode(), ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl), 1 if reset else 0))
+    return n.value, ms.value, fl.value
 
 
 def lrc_trmm(side: int, trans: int, L: torch.Tensor, B: torch.Tensor, stream=None):

@@ -97,6 +97,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--seed", type=int, default=20261203)
     ap.add_argument("--breakdown", action="store_true", help="print per-call timings to stderr")
+    ap.add_argument("--calib-copy-mb", type=int, default=1024, help="size of the byte-counter reference copy")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported (the path would shard matrices "
@@ -171,9 +172,17 @@ def main():
         times.append(("fisher", e5, e6, None, None, None))
         times.append(("alloc", e6, e7, None, None, None))
 
+    # a plain copy of known size, outside the timed region: the reference that scales HBM byte
+    # counters (FETCH_SIZE / WRITE_SIZE) of a profiled run into bytes
+    calib_src = torch.empty(a.calib_copy_mb << 20, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    del calib_src, calib_dst
     for _ in range(a.warmup):
         step([])
     torch.cuda.synchronize()
+    lrc.lrc_timing_read("k_cov_syrk", reset=True)
+    lrc.lrc_timing_enable(True)
     recs = []
     t0 = time.perf_counter()
     for _ in range(a.steps):
@@ -182,6 +191,9 @@ def main():
         recs.append(r)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    lrc.lrc_timing_enable(False)
+    syrk_n, syrk_ms, syrk_fl = lrc.lrc_timing_read("k_cov_syrk", reset=False)
+    gemm_n, gemm_ms, gemm_fl = lrc.lrc_timing_read("k_cov_gemm_y", reset=True)
     assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
 
     # per-call times from the events (ms), averaged over steps
@@ -208,22 +220,20 @@ def main():
     if a.breakdown:
         for k in sorted(avg):
             print("%-20s %10.3f ms" % (k, avg[k]), file=sys.stderr)
-    # dominant op of the step by time, with its roofline
-    dominant = "cov" if cov_ms >= eig_ms else "eigh"
-    if dominant == "cov":
-        roof = {"kernel": "lrc_cov_accumulate (k_cov_gemm_y + k_cov_syrk per 32768-token chunk)",
-                "bound": "mfma", "achieved": cov_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": cov_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                "per_launch": "N (2 d_in d_out + d_out (d_out+1)) algorithmic flops per call, N = %d" % a.tokens}
-    else:
-        n = a.d_ff
-        tri_bytes = sum((n - c - 1) ** 2 / 2 for c in range(0, n - 1)) * (4 if prec == lrc.LRC_F32 else 8)
-        ms = avg["gate_proj.eigh"]
-        roof = {"kernel": "lrc_eigh n=%d (tridiagonalisation symv-bound)" % n, "bound": "hbm",
-                "achieved": tri_bytes / (ms / 1000.0) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": tri_bytes / (ms / 1000.0) / 1e9 / PEAK_HBM_GBS, "traffic": None,
-                "per_launch": "sum over columns of the trailing lower triangle, %d-byte elements"
-                              % (4 if prec == lrc.LRC_F32 else 8)}
+    # roofline of the dominant single kernel (the covariance SYRK), from HIP events recorded by the
+    # library around each of its launches on the launch stream during the timed steps
+    syrk_tf = syrk_fl / (syrk_ms / 1000.0) / 1e12
+    roof = {"kernel": "k_cov_syrk", "bound": "mfma", "achieved": syrk_tf, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": syrk_tf / PEAK_BF16_TFLOPS, "traffic": None,
+            "launches": syrk_n, "avg_launch_ms": syrk_ms / max(syrk_n, 1),
+            "per_launch": "algorithmic flops = tokens in the chunk x d_out (d_out + 1) (upper triangle incl. "
+                          "diagonal); the kernel executes 4 bf16 MFMA products per flop pair (hi/lo split), "
+                          "so executed MFMA utilisation is 4x frac"}
+    gemm_tf = gemm_fl / (gemm_ms / 1000.0) / 1e12 if gemm_ms > 0 else 0.0
+    roof_gemm = {"kernel": "k_cov_gemm_y", "bound": "mfma", "achieved": gemm_tf, "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": gemm_tf / PEAK_BF16_TFLOPS, "launches": gemm_n,
+                 "avg_launch_ms": gemm_ms / max(gemm_n, 1),
+                 "per_launch": "algorithmic flops = 2 x tokens in the chunk x d_in x d_out"}
     out = {
         "metric": "calibration tokens/s into Y^T Y; sec per 4096x4096 layer compressed (eig incl.)",
         "value": a.tokens / (step_ms / 1000.0),
@@ -240,6 +250,7 @@ def main():
         "cov_ms": cov_ms, "eigh_ms": eig_ms,
         "breakdown_ms": {k: round(v, 3) for k, v in avg.items()},
         "roofline": roof,
+        "roofline_gemm_y": roof_gemm,
     }
     if a.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(a.d_model, a.d_ff, a.cpu_sample)

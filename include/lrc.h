@@ -67,6 +67,20 @@ enum {
     LRC_INFO_BAD_SCORE = 5
 };
 
+/* ------------------------------------------------------------------------------------
+ * Kernel timing (instrumentation, not part of the method).  While enabled, the library
+ * records a HIP event pair on the launch stream around every launch of the named kernels
+ * ("k_cov_syrk", "k_cov_gemm_y") and remembers each launch's algorithmic flop count.
+ * lrc_timing_read synchronises on the recorded events and returns, for one kernel name,
+ * the number of launches, their summed duration in milliseconds and summed algorithmic
+ * flops since the last reset; reset != 0 then discards the records.  Enabling adds two
+ * event records per instrumented launch and nothing else.  Not thread-safe with respect
+ * to concurrent lrc_timing_read calls.
+ * ------------------------------------------------------------------------------------ */
+lrc_status lrc_timing_enable(int enable);
+lrc_status lrc_timing_read(const char *kernel, int64_t *launches, double *total_ms, double *total_flops,
+                           int reset);
+
 /* LRC_ABI_VERSION of the built library. */
 int lrc_abi_version(void);
 /* Static text for a status code. */
