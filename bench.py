@@ -63,6 +63,21 @@ def gen_inputs(torch, n_tok, d_model, d_ff, seed, dev):
     return X, Xd, W, G
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter record, if the kernel's source is
+    unchanged since the counters were taken (else None)."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "%s_traffic.json" % kernel)
+    try:
+        rec = json.load(open(rec_path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def cpu_baseline(d_model, d_ff, sample_tok):
     """The fp64 oracle's covariance throughput on a bounded token sample of the same block."""
     import numpy as np
@@ -224,7 +239,7 @@ def main():
     # library around each of its launches on the launch stream during the timed steps
     syrk_tf = syrk_fl / (syrk_ms / 1000.0) / 1e12
     roof = {"kernel": "k_cov_syrk", "bound": "mfma", "achieved": syrk_tf, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": syrk_tf / PEAK_BF16_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": syrk_tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("k_cov_syrk"),
             "launches": syrk_n, "avg_launch_ms": syrk_ms / max(syrk_n, 1),
             "per_launch": "algorithmic flops = tokens in the chunk x d_out (d_out + 1) (upper triangle incl. "
                           "diagonal); the kernel executes 4 bf16 MFMA products per flop pair (hi/lo split), "
