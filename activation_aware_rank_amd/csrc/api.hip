@@ -265,20 +265,53 @@ lrc_status lrc_cholesky(double *A, int64_t n, int64_t lda, void *ws, size_t ws_b
     return cholesky_run(A, n, lda, ws, ws_bytes, info, static_cast<hipStream_t>(stream));
 }
 
+size_t lrc_trmm_workspace(int64_t m, int64_t n) { return (m > 0 && n > 0) ? trmm_workspace(m, n) : 0; }
+
 lrc_status lrc_trmm(int32_t side, int32_t trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B,
-                    int64_t ldb, void *stream) {
+                    int64_t ldb, void *ws, size_t ws_bytes, void *stream) {
     REQUIRE(L && B, LRC_ERR_ARG, "L and B must be non-NULL");
     REQUIRE((side == 0 || side == 1) && (trans == 0 || trans == 1), LRC_ERR_ARG, "side/trans must be 0 or 1");
     REQUIRE(m > 0 && n > 0 && ldb >= n && ldl >= (side ? n : m), LRC_ERR_ARG, "bad sizes or leading dims");
-    return trmm_run(side, trans, m, n, L, ldl, B, ldb, static_cast<hipStream_t>(stream));
+    size_t need = trmm_workspace(m, n);
+    REQUIRE(ws_bytes >= need && ws && aligned(ws, 256), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_trmm_workspace() or not 256-byte aligned");
+    return trmm_run(side, trans, m, n, L, ldl, B, ldb, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t lrc_trsm_workspace(int32_t side, int64_t m, int64_t n) {
+    return (m > 0 && n > 0 && (side == 0 || side == 1)) ? trsm_workspace(side, m, n) : 0;
 }
 
 lrc_status lrc_trsm(int32_t side, int32_t trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B,
-                    int64_t ldb, void *stream) {
+                    int64_t ldb, void *ws, size_t ws_bytes, void *stream) {
     REQUIRE(L && B, LRC_ERR_ARG, "L and B must be non-NULL");
     REQUIRE((side == 0 || side == 1) && (trans == 0 || trans == 1), LRC_ERR_ARG, "side/trans must be 0 or 1");
     REQUIRE(m > 0 && n > 0 && ldb >= n && ldl >= (side ? n : m), LRC_ERR_ARG, "bad sizes or leading dims");
-    return trsm_run(side, trans, m, n, L, ldl, B, ldb, static_cast<hipStream_t>(stream));
+    size_t need = trsm_workspace(side, m, n);
+    REQUIRE(ws_bytes >= need && ws && aligned(ws, 256), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_trsm_workspace() or not 256-byte aligned");
+    return trsm_run(side, trans, m, n, L, ldl, B, ldb, ws, static_cast<hipStream_t>(stream));
+}
+
+lrc_status lrc_sym_to_f64(const float *C, int64_t n, int64_t ldc, double scale, double *A, int64_t lda,
+                          void *stream) {
+    REQUIRE(C && A, LRC_ERR_ARG, "C and A must be non-NULL");
+    REQUIRE(n > 0 && ldc >= n && lda >= n, LRC_ERR_ARG, "bad n or leading dims");
+    return sym_to_f64_run(C, n, ldc, scale, A, lda, static_cast<hipStream_t>(stream));
+}
+
+lrc_status lrc_to_f64(const void *X, lrc_dtype t, int64_t rows, int64_t cols, int64_t ldx, double scale, double *Y,
+                      int64_t ldy, void *stream) {
+    REQUIRE(X && Y, LRC_ERR_ARG, "X and Y must be non-NULL");
+    REQUIRE(t == LRC_BF16 || t == LRC_F32 || t == LRC_F64, LRC_ERR_DTYPE, "X must be bf16, fp32 or fp64");
+    REQUIRE(rows > 0 && cols > 0 && ldx >= cols && ldy >= cols, LRC_ERR_ARG, "bad sizes or leading dims");
+    return to_f64_run(X, t, rows, cols, ldx, scale, Y, ldy, static_cast<hipStream_t>(stream));
+}
+
+lrc_status lrc_gram_f64(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg, void *stream) {
+    REQUIRE(B && G, LRC_ERR_ARG, "B and G must be non-NULL");
+    REQUIRE(m > 0 && n > 0 && ldb >= n && ldg >= m, LRC_ERR_ARG, "bad sizes or leading dims");
+    return gram_f64_run(B, m, n, ldb, G, ldg, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -1,21 +1,502 @@
-// Curvature-weighted variant (LASER page, method 1): Cholesky factor and triangular products /
-// solves with it.  Filled in by a later change; until then these report LRC_ERR_UNIMPLEMENTED.
+// Curvature-weighted variant (LASER page, "LASER: Loss-Aware Singular-value Decomposition and
+// Rank Allocation", method 1): the weight is moved into the metric of the Kronecker-factored
+// curvature by Cholesky factors of the activation and gradient covariances, truncated there, and
+// mapped back.  This file holds the fp64 dense pieces of that chain:
+//
+//  * k_dgemm: one tiled fp64 MFMA contraction C = alpha op(A) op(B) + beta C with optional
+//    triangular masks on either operand (the mask also bounds the k range a tile visits) and a
+//    lower- or upper-tile output selector.  It serves the Cholesky panel and trailing updates,
+//    TRMM, the blocked TRSM updates and the Gram matrix B B^T.
+//  * k_potrf_diag: one 64x64 diagonal block factored in LDS (right-looking, column by column)
+//    and inverted by forward substitution; the panel below is then A21 Linv^T (a k_dgemm).
+//  * k_trinv: batched inverses of the 64x64 diagonal blocks of a lower-triangular matrix, so
+//    that a triangular solve becomes a sequence of small in-place products and rank-64 updates.
+//
+// The inverse-based block solve is the usual GPU formulation of a blocked triangular solve;
+// its error is bounded by the condition number of each 64x64 diagonal block (not of the whole
+// factor) times the fp64 unit roundoff.
 #include "lrc_internal.h"
 
+#include <algorithm>
+
 namespace lrc {
+namespace {
 
-size_t cholesky_workspace(int64_t) { return 0; }
+constexpr int GT = 64;        // output tile edge of k_dgemm (rows and cols)
+constexpr int GK = 16;        // k-tile of k_dgemm
+constexpr int GLD = GT + 16;  // padded LDS row (doubles): k rows 1 apart land in other banks
+constexpr int NBC = 64;       // block size of the Cholesky and of the triangular solves
+constexpr int GRID_Y_MAX = 65535;
 
-lrc_status cholesky_run(double *, int64_t, int64_t, void *, size_t, int32_t *, hipStream_t) {
-    return fail(LRC_ERR_UNIMPLEMENTED, "lrc_cholesky is not implemented in this build");
+struct GemmArgs {
+    int64_t M, N, K;
+    const double *A;
+    int64_t lda;
+    const double *B;
+    int64_t ldb;
+    double *C;   // fp64 output (OUTF == 0)
+    float *Cf;   // fp32 upper output (OUTF == 1)
+    int64_t ldc;
+    double alpha, beta;
+    int tiles;   // 0 every tile; 1 tiles with ti >= tj, writing row >= col; 2 ti <= tj, row <= col
+};
+
+// op(A)[i][k] is A[i*lda + k] (TA 0) or A[k*lda + i] (TA 1); op(B)[k][j] is B[k*ldb + j] (TB 0)
+// or B[j*ldb + k] (TB 1).  Masks: MA 1 keeps op(A)[i][k] only for k <= i, MA 2 only for k >= i;
+// MB 1 keeps op(B)[k][j] only for k <= j, MB 2 only for k >= j.  Masked entries are never read.
+// OUTF 0: C = alpha acc + beta C (C not read when beta == 0); OUTF 1: Cf = (float)(alpha acc).
+template <int TA, int TB, int MA, int MB, int OUTF>
+__global__ __launch_bounds__(256) void k_dgemm(GemmArgs g) {
+    const int ti = blockIdx.y, tj = blockIdx.x;
+    if (g.tiles == 1 && ti < tj) return;
+    if (g.tiles == 2 && ti > tj) return;
+    const int64_t m0 = int64_t(ti) * GT, n0 = int64_t(tj) * GT;
+    int64_t kb = 0, ke = g.K;
+    if (MA == 1) ke = min(ke, m0 + GT);
+    if (MA == 2) kb = max(kb, m0);
+    if (MB == 1) ke = min(ke, n0 + GT);
+    if (MB == 2) kb = max(kb, n0);
+
+    __shared__ double sA[GK][GLD];
+    __shared__ double sB[GK][GLD];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+
+    // each thread stages 4 entries of each operand per k-tile
+    double ra[4], rb[4];
+    auto gload = [&](int64_t k0) {
+        if (TA == 0) {
+            const int i = t >> 2, kq = (t & 3) * 4;
+            const int64_t row = m0 + i;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t k = k0 + kq + u;
+                bool ok = row < g.M && k < ke;
+                if (MA == 1) ok = ok && k <= row;
+                if (MA == 2) ok = ok && k >= row;
+                ra[u] = ok ? g.A[row * g.lda + k] : 0.0;
+            }
+        } else {
+            const int kk = t >> 4, iq = (t & 15) * 4;
+            const int64_t k = k0 + kk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t row = m0 + iq + u;
+                bool ok = row < g.M && k < ke;
+                if (MA == 1) ok = ok && k <= row;
+                if (MA == 2) ok = ok && k >= row;
+                ra[u] = ok ? g.A[k * g.lda + row] : 0.0;
+            }
+        }
+        if (TB == 0) {
+            const int kk = t >> 4, jq = (t & 15) * 4;
+            const int64_t k = k0 + kk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t col = n0 + jq + u;
+                bool ok = col < g.N && k < ke;
+                if (MB == 1) ok = ok && k <= col;
+                if (MB == 2) ok = ok && k >= col;
+                rb[u] = ok ? g.B[k * g.ldb + col] : 0.0;
+            }
+        } else {
+            const int j = t >> 2, kq = (t & 3) * 4;
+            const int64_t col = n0 + j;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t k = k0 + kq + u;
+                bool ok = col < g.N && k < ke;
+                if (MB == 1) ok = ok && k <= col;
+                if (MB == 2) ok = ok && k >= col;
+                rb[u] = ok ? g.B[col * g.ldb + k] : 0.0;
+            }
+        }
+    };
+    auto sstore = [&]() {
+        if (TA == 0) {
+            const int i = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sA[kq + u][i] = ra[u];
+        } else {
+            const int kk = t >> 4, iq = (t & 15) * 4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sA[kk][iq + u] = ra[u];
+        }
+        if (TB == 0) {
+            const int kk = t >> 4, jq = (t & 15) * 4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sB[kk][jq + u] = rb[u];
+        } else {
+            const int j = t >> 2, kq = (t & 3) * 4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sB[kq + u][j] = rb[u];
+        }
+    };
+
+    f64x4_t acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+
+    if (kb < ke) {
+        gload(kb);
+        for (int64_t k0 = kb; k0 < ke; k0 += GK) {
+            sstore();
+            __syncthreads();
+            if (k0 + GK < ke) gload(k0 + GK);
+#pragma unroll
+            for (int ks = 0; ks < GK / 4; ++ks) {
+                const int kk = ks * 4 + (lane >> 4);
+                const double a0 = sA[kk][wr + (lane & 15)];
+                const double a1 = sA[kk][wr + 16 + (lane & 15)];
+                const double b0 = sB[kk][wc + (lane & 15)];
+                const double b1 = sB[kk][wc + 16 + (lane & 15)];
+                acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+                acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+                acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+                acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+            }
+            __syncthreads();
+        }
+    }
+
+    // 16x16 f64 MFMA result: accumulator r of a lane holds row 4 r + lane/16, column lane%16
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wr + a * 16 + r * 4 + (lane >> 4);
+                const int64_t col = n0 + wc + b * 16 + (lane & 15);
+                if (row >= g.M || col >= g.N) continue;
+                if (g.tiles == 1 && row < col) continue;
+                if (g.tiles == 2 && row > col) continue;
+                const double v = g.alpha * acc[a][b][r];
+                if (OUTF == 1) {
+                    g.Cf[row * g.ldc + col] = float(v);
+                } else {
+                    double* p = g.C + row * g.ldc + col;
+                    *p = g.beta != 0.0 ? v + g.beta * *p : v;
+                }
+            }
 }
 
-lrc_status trmm_run(int, int, int64_t, int64_t, const double *, int64_t, double *, int64_t, hipStream_t) {
-    return fail(LRC_ERR_UNIMPLEMENTED, "lrc_trmm is not implemented in this build");
+template <int TA, int TB, int MA, int MB, int OUTF>
+lrc_status launch_gemm(const GemmArgs &g, hipStream_t s) {
+    if (g.M <= 0 || g.N <= 0) return LRC_OK;
+    const int gy = cdiv(g.M, GT), gx = cdiv(g.N, GT);
+    if (gy > GRID_Y_MAX) return fail(LRC_ERR_ARG, "matrix too tall for the fp64 product kernel");
+    const int tok = timing_begin("k_dgemm", s);
+    hipLaunchKernelGGL((k_dgemm<TA, TB, MA, MB, OUTF>), dim3(gx, gy), dim3(256), 0, s, g);
+    timing_end(tok, s, 2.0 * double(g.M) * double(g.N) * double(g.K));
+    LRC_LAUNCH_CHECK("k_dgemm");
+    return LRC_OK;
 }
 
-lrc_status trsm_run(int, int, int64_t, int64_t, const double *, int64_t, double *, int64_t, hipStream_t) {
-    return fail(LRC_ERR_UNIMPLEMENTED, "lrc_trsm is not implemented in this build");
+GemmArgs gemm(int64_t M, int64_t N, int64_t K, const double *A, int64_t lda, const double *B, int64_t ldb,
+              double *C, int64_t ldc, double alpha, double beta, int tiles = 0) {
+    GemmArgs g;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.A = A;
+    g.lda = lda;
+    g.B = B;
+    g.ldb = ldb;
+    g.C = C;
+    g.Cf = nullptr;
+    g.ldc = ldc;
+    g.alpha = alpha;
+    g.beta = beta;
+    g.tiles = tiles;
+    return g;
+}
+
+// Inverse of the lower-triangular 64x64 matrix in s (rows past the valid size padded with the
+// identity) into inv, column c by thread c: row i of L^{-1} e_c from rows < i.  A thread reads
+// and writes only its own column of inv, so the loop needs no barrier.
+__device__ __forceinline__ void lower_inverse_64(const double (*s)[NBC + 1], double (*inv)[NBC + 1]) {
+    const int c = threadIdx.x;
+    if (c >= NBC) return;
+    for (int i = 0; i < NBC; ++i) {
+        double x = (i == c) ? 1.0 : 0.0;
+        for (int p = c; p < i; ++p) x -= s[i][p] * inv[p][c];
+        inv[i][c] = (i >= c) ? x / s[i][i] : 0.0;
+    }
+}
+
+// Factor the diagonal block A[j0:j0+nb, j0:j0+nb] (lower triangle read) in place, zero its strict
+// upper triangle, and write the inverse of the factor (64x64, zero-padded) to Linv.
+// info: 1 when a pivot is not finite, 3 when a pivot is <= 0 (first failure kept).
+__global__ __launch_bounds__(256) void k_potrf_diag(double *__restrict__ A, int64_t lda, int64_t n, int64_t j0,
+                                                    double *__restrict__ Linv, int32_t *__restrict__ info) {
+    __shared__ double s[NBC][NBC + 1];
+    __shared__ double inv[NBC][NBC + 1];
+    const int t = threadIdx.x;
+    const int nb = int(min<int64_t>(NBC, n - j0));
+    for (int e = t; e < NBC * NBC; e += 256) {
+        const int i = e >> 6, j = e & 63;
+        double v = (i == j) ? 1.0 : 0.0;
+        if (i < nb && j <= i) v = A[(j0 + i) * lda + j0 + j];
+        s[i][j] = (j <= i) ? v : 0.0;
+    }
+    __syncthreads();
+    bool bad = false;
+    for (int c = 0; c < nb; ++c) {
+        const double p = s[c][c];
+        const double d = sqrt(p);
+        if (t == 0 && !bad && !(p > 0.0 && p <= 1.7976931348623157e308)) {
+            bad = true;
+            if (*info == 0) *info = (p != p || p > 1.7976931348623157e308) ? LRC_INFO_NONFINITE : LRC_INFO_NOT_PD;
+        }
+        if (t > c && t < NBC) s[t][c] = s[t][c] / d;
+        __syncthreads();
+        if (t == 0) s[c][c] = d;
+        for (int e = (c + 1) * NBC + t; e < NBC * NBC; e += 256) {
+            const int i = e >> 6, j = e & 63;
+            if (j > c && j <= i) s[i][j] -= s[i][c] * s[j][c];
+        }
+        __syncthreads();
+    }
+    lower_inverse_64(s, inv);
+    __syncthreads();
+    for (int e = t; e < NBC * NBC; e += 256) {
+        const int i = e >> 6, j = e & 63;
+        if (i < nb && j < nb) A[(j0 + i) * lda + j0 + j] = (j <= i) ? s[i][j] : 0.0;
+        Linv[e] = inv[i][j];
+    }
+}
+
+// Inverses of the diagonal 64x64 blocks of the lower-triangular L (dim x dim), block b to
+// Linv + 4096 b.  The strict upper triangle of L is not read.
+__global__ __launch_bounds__(256) void k_trinv(const double *__restrict__ L, int64_t ldl, int64_t dim,
+                                               double *__restrict__ Linv) {
+    __shared__ double s[NBC][NBC + 1];
+    __shared__ double inv[NBC][NBC + 1];
+    const int t = threadIdx.x;
+    const int64_t j0 = int64_t(blockIdx.x) * NBC;
+    const int nb = int(min<int64_t>(NBC, dim - j0));
+    for (int e = t; e < NBC * NBC; e += 256) {
+        const int i = e >> 6, j = e & 63;
+        double v = (i == j) ? 1.0 : 0.0;
+        if (i < nb && j <= i) v = L[(j0 + i) * ldl + j0 + j];
+        s[i][j] = (j <= i) ? v : 0.0;
+    }
+    __syncthreads();
+    lower_inverse_64(s, inv);
+    __syncthreads();
+    double *out = Linv + int64_t(blockIdx.x) * NBC * NBC;
+    for (int e = t; e < NBC * NBC; e += 256) out[e] = inv[e >> 6][e & 63];
+}
+
+__global__ void k_info_zero(int32_t *info) {
+    if (threadIdx.x == 0) *info = 0;
+}
+
+// Zero the strict upper triangle of an n x n matrix (row r: columns r+1 .. n-1).
+__global__ void k_zero_upper(double *__restrict__ A, int64_t lda, int64_t n) {
+    for (int64_t r = blockIdx.y; r < n; r += gridDim.y)
+        for (int64_t c = r + 1 + int64_t(blockIdx.x) * blockDim.x + threadIdx.x; c < n;
+             c += int64_t(gridDim.x) * blockDim.x)
+            A[r * lda + c] = 0.0;
+}
+
+__global__ void k_copy2d(const double *__restrict__ X, int64_t ldx, int64_t rows, int64_t cols, double *__restrict__ Y,
+                         int64_t ldy) {
+    const int64_t n = rows * cols;
+    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t r = e / cols, c = e - r * cols;
+        Y[r * ldy + c] = X[r * ldx + c];
+    }
+}
+
+template <class T>
+__device__ __forceinline__ double widen(const T *p, int64_t i);
+template <>
+__device__ __forceinline__ double widen<bf16_t>(const bf16_t *p, int64_t i) {
+    return double(bf16_to_f32(p[i]));
+}
+template <>
+__device__ __forceinline__ double widen<float>(const float *p, int64_t i) {
+    return double(p[i]);
+}
+template <>
+__device__ __forceinline__ double widen<double>(const double *p, int64_t i) {
+    return p[i];
+}
+
+template <class T>
+__global__ void k_to_f64(const T *__restrict__ X, int64_t ldx, int64_t rows, int64_t cols, double scale,
+                         double *__restrict__ Y, int64_t ldy) {
+    const int64_t n = rows * cols;
+    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t r = e / cols, c = e - r * cols;
+        Y[r * ldy + c] = scale * widen<T>(X, r * ldx + c);
+    }
+}
+
+// A = scale * sym(C) from the upper triangle of C: tile pair (ti <= tj) staged through LDS so
+// that both the tile and its mirror image are written with coalesced rows.
+__global__ __launch_bounds__(256) void k_sym_to_f64(const float *__restrict__ C, int64_t ldc, int64_t n,
+                                                    double scale, double *__restrict__ A, int64_t lda) {
+    const int ti = blockIdx.y, tj = blockIdx.x;
+    if (ti > tj) return;
+    __shared__ float s[64][65];
+    const int t = threadIdx.x;
+    const int64_t r0 = int64_t(ti) * 64, c0 = int64_t(tj) * 64;
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int i = e >> 6, j = e & 63;
+        const int64_t r = r0 + i, c = c0 + j;
+        float v = 0.0f;
+        if (r < n && c < n && r <= c) v = C[r * ldc + c];
+        s[i][j] = v;
+    }
+    __syncthreads();
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int i = e >> 6, j = e & 63;
+        const int64_t r = r0 + i, c = c0 + j;
+        if (r < n && c < n) {
+            const float v = (ti == tj && i > j) ? s[j][i] : s[i][j];
+            A[r * lda + c] = scale * double(v);
+        }
+        // mirror: A[c0 + i][r0 + j] = C[r0 + j][c0 + i]
+        const int64_t mr = c0 + i, mc = r0 + j;
+        if (ti != tj && mr < n && mc < n) A[mr * lda + mc] = scale * double(s[j][i]);
+    }
+}
+
+int grid1d(int64_t n) { return int(std::min<int64_t>(std::max<int64_t>(cdiv(n, 256), 1), 8192)); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+size_t cholesky_workspace(int64_t) { return align256(size_t(NBC) * NBC * sizeof(double)); }
+
+lrc_status cholesky_run(double *A, int64_t n, int64_t lda, void *ws, size_t, int32_t *info, hipStream_t s) {
+    double *Linv = static_cast<double *>(ws);
+    hipLaunchKernelGGL(k_info_zero, dim3(1), dim3(64), 0, s, info);
+    LRC_LAUNCH_CHECK("k_info_zero");
+    for (int64_t j0 = 0; j0 < n; j0 += NBC) {
+        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, s, A, lda, n, j0, Linv, info);
+        LRC_LAUNCH_CHECK("k_potrf_diag");
+        const int64_t j1 = j0 + NBC;
+        if (j1 >= n) break;
+        double *A21 = A + j1 * lda + j0;
+        // L21 = A21 L11^{-T}, in place: one output column tile, so each workgroup reads its rows
+        // of A21 completely before it writes them
+        lrc_status st = launch_gemm<0, 1, 0, 1, 0>(gemm(n - j1, NBC, NBC, A21, lda, Linv, NBC, A21, lda, 1.0, 0.0), s);
+        if (st != LRC_OK) return st;
+        // A22 -= L21 L21^T on the lower triangle
+        st = launch_gemm<0, 1, 0, 0, 0>(
+            gemm(n - j1, n - j1, NBC, A21, lda, A21, lda, A + j1 * lda + j1, lda, -1.0, 1.0, 1), s);
+        if (st != LRC_OK) return st;
+    }
+    if (n > 1) {
+        hipLaunchKernelGGL(k_zero_upper, dim3(std::max(1, std::min(cdiv(n, 256), 64)), unsigned(std::min<int64_t>(n, GRID_Y_MAX))),
+                           dim3(256), 0, s, A, lda, n);
+        LRC_LAUNCH_CHECK("k_zero_upper");
+    }
+    return LRC_OK;
+}
+
+size_t trmm_workspace(int64_t m, int64_t n) { return align256(size_t(m) * size_t(n) * sizeof(double)); }
+
+lrc_status trmm_run(int side, int trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B, int64_t ldb,
+                    void *ws, hipStream_t s) {
+    double *T = static_cast<double *>(ws);
+    lrc_status st;
+    if (side == 0) {
+        const GemmArgs g = gemm(m, n, m, L, ldl, B, ldb, T, n, 1.0, 0.0);
+        st = trans ? launch_gemm<1, 0, 2, 0, 0>(g, s) : launch_gemm<0, 0, 1, 0, 0>(g, s);
+    } else {
+        const GemmArgs g = gemm(m, n, n, B, ldb, L, ldl, T, n, 1.0, 0.0);
+        st = trans ? launch_gemm<0, 1, 0, 1, 0>(g, s) : launch_gemm<0, 0, 0, 2, 0>(g, s);
+    }
+    if (st != LRC_OK) return st;
+    hipLaunchKernelGGL(k_copy2d, dim3(grid1d(m * n)), dim3(256), 0, s, T, n, m, n, B, ldb);
+    LRC_LAUNCH_CHECK("k_copy2d");
+    return LRC_OK;
+}
+
+size_t trsm_workspace(int side, int64_t m, int64_t n) {
+    const int64_t dim = side ? n : m;
+    return align256(size_t(cdiv(dim, NBC)) * NBC * NBC * sizeof(double));
+}
+
+lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B, int64_t ldb,
+                    void *ws, hipStream_t s) {
+    double *Linv = static_cast<double *>(ws);
+    const int64_t dim = side ? n : m;
+    const int nblk = cdiv(dim, NBC);
+    hipLaunchKernelGGL(k_trinv, dim3(nblk), dim3(256), 0, s, L, ldl, dim, Linv);
+    LRC_LAUNCH_CHECK("k_trinv");
+    lrc_status st = LRC_OK;
+    for (int step = 0; step < nblk && st == LRC_OK; ++step) {
+        // forward order for L^{-1} B and B L^{-T}; backward for L^{-T} B and B L^{-1}
+        const bool fwd = (side == 0) == (trans == 0);
+        const int b = fwd ? step : nblk - 1 - step;
+        const int64_t b0 = int64_t(b) * NBC, b1 = std::min<int64_t>(b0 + NBC, dim), nb = b1 - b0;
+        const double *Li = Linv + int64_t(b) * NBC * NBC;
+        if (side == 0) {
+            double *Bb = B + b0 * ldb;
+            // X_b = op(Linv_b) B_b in place (K = nb <= one tile of rows)
+            const GemmArgs g = gemm(nb, n, nb, Li, NBC, Bb, ldb, Bb, ldb, 1.0, 0.0);
+            st = trans ? launch_gemm<1, 0, 2, 0, 0>(g, s) : launch_gemm<0, 0, 1, 0, 0>(g, s);
+            if (st != LRC_OK) break;
+            if (!trans && b1 < m) {  // B[b1:] -= L[b1:, b0:b1] X_b
+                st = launch_gemm<0, 0, 0, 0, 0>(
+                    gemm(m - b1, n, nb, L + b1 * ldl + b0, ldl, Bb, ldb, B + b1 * ldb, ldb, -1.0, 1.0), s);
+            } else if (trans && b0 > 0) {  // B[:b0] -= L[b0:b1, :b0]^T X_b
+                st = launch_gemm<1, 0, 0, 0, 0>(gemm(b0, n, nb, L + b0 * ldl, ldl, Bb, ldb, B, ldb, -1.0, 1.0), s);
+            }
+        } else {
+            double *Bb = B + b0;
+            // X_b = B_b op(Linv_b) in place (K = nb <= one tile of columns)
+            const GemmArgs g = gemm(m, nb, nb, Bb, ldb, Li, NBC, Bb, ldb, 1.0, 0.0);
+            st = trans ? launch_gemm<0, 1, 0, 1, 0>(g, s) : launch_gemm<0, 0, 0, 2, 0>(g, s);
+            if (st != LRC_OK) break;
+            if (!trans && b0 > 0) {  // B[:, :b0] -= X_b L[b0:b1, :b0]
+                st = launch_gemm<0, 0, 0, 0, 0>(gemm(m, b0, nb, Bb, ldb, L + b0 * ldl, ldl, B, ldb, -1.0, 1.0), s);
+            } else if (trans && b1 < n) {  // B[:, b1:] -= X_b L[b1:, b0:b1]^T
+                st = launch_gemm<0, 1, 0, 0, 0>(
+                    gemm(m, n - b1, nb, Bb, ldb, L + b1 * ldl + b0, ldl, B + b1, ldb, -1.0, 1.0), s);
+            }
+        }
+    }
+    return st;
+}
+
+lrc_status sym_to_f64_run(const float *C, int64_t n, int64_t ldc, double scale, double *A, int64_t lda,
+                          hipStream_t s) {
+    const int nt = cdiv(n, 64);
+    if (nt > GRID_Y_MAX) return fail(LRC_ERR_ARG, "n too large");
+    hipLaunchKernelGGL(k_sym_to_f64, dim3(nt, nt), dim3(256), 0, s, C, ldc, n, scale, A, lda);
+    LRC_LAUNCH_CHECK("k_sym_to_f64");
+    return LRC_OK;
+}
+
+lrc_status to_f64_run(const void *X, lrc_dtype t, int64_t rows, int64_t cols, int64_t ldx, double scale, double *Y,
+                      int64_t ldy, hipStream_t s) {
+    const int grid = grid1d(rows * cols);
+    if (t == LRC_BF16)
+        hipLaunchKernelGGL(k_to_f64<bf16_t>, dim3(grid), dim3(256), 0, s, static_cast<const bf16_t *>(X), ldx, rows,
+                           cols, scale, Y, ldy);
+    else if (t == LRC_F32)
+        hipLaunchKernelGGL(k_to_f64<float>, dim3(grid), dim3(256), 0, s, static_cast<const float *>(X), ldx, rows,
+                           cols, scale, Y, ldy);
+    else
+        hipLaunchKernelGGL(k_to_f64<double>, dim3(grid), dim3(256), 0, s, static_cast<const double *>(X), ldx, rows,
+                           cols, scale, Y, ldy);
+    LRC_LAUNCH_CHECK("k_to_f64");
+    return LRC_OK;
+}
+
+lrc_status gram_f64_run(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg, hipStream_t s) {
+    GemmArgs g = gemm(m, m, n, B, ldb, B, ldb, nullptr, ldg, 1.0, 0.0, 2);
+    g.Cf = G;
+    return launch_gemm<0, 1, 0, 0, 1>(g, s);
 }
 
 }  // namespace lrc

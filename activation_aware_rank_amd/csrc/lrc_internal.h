@@ -153,9 +153,17 @@ lrc_status alloc_run(const AllocArgs &a, void *ws, size_t ws_bytes, hipStream_t 
 size_t cholesky_workspace(int64_t n);
 lrc_status cholesky_run(double *A, int64_t n, int64_t lda, void *ws, size_t ws_bytes, int32_t *info,
                         hipStream_t s);
+size_t trmm_workspace(int64_t m, int64_t n);
 lrc_status trmm_run(int side, int trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B,
-                    int64_t ldb, hipStream_t s);
+                    int64_t ldb, void *ws, hipStream_t s);
+size_t trsm_workspace(int side, int64_t m, int64_t n);
 lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B,
-                    int64_t ldb, hipStream_t s);
+                    int64_t ldb, void *ws, hipStream_t s);
+lrc_status sym_to_f64_run(const float *C, int64_t n, int64_t ldc, double scale, double *A, int64_t lda,
+                          hipStream_t s);
+lrc_status to_f64_run(const void *X, lrc_dtype t, int64_t rows, int64_t cols, int64_t ldx, double scale,
+                      double *Y, int64_t ldy, hipStream_t s);
+lrc_status gram_f64_run(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg,
+                        hipStream_t s);
 
 }  // namespace lrc

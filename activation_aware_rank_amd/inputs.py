@@ -204,3 +204,16 @@ def block_activations(width: int, n_tok: int, feeds_down: bool = False, cfg: int
 def rank_at_ratio(d_in: int, d_out: int, ratio: float) -> int:
     """Rank whose factor parameters k (d_in + d_out) keep the given fraction of d_in d_out."""
     return int(np.floor(ratio * d_in * d_out / (d_in + d_out)))
+
+
+def curvature_layer(n_tok: int = 131072, d_in: int = 5120, d_out: int = 13824) -> dict:
+    """Curvature-weighted case of one FFN matrix (13B shape at full size): activations N(0,1)
+    with lognormal channel scales, output gradients N(0, 1e-3^2), weight N(0, 0.02^2); all bf16."""
+    s = channel_scales_lognormal(d_in, CFG_KFAC, 0, 0)
+    return {
+        "X": activations_scaled(n_tok, d_in, s, "bf16", CFG_KFAC, 0, 0),
+        "G": gaussian(n_tok, d_out, 1e-3, "bf16", CFG_KFAC, 0, 1, S_GRAD),
+        "W": weight(d_in, d_out, "bf16", CFG_KFAC, 0, 2),
+        "dtype": "bf16",
+    }
+

@@ -54,8 +54,13 @@ _alc_ws = _sig("lrc_allocate_ranks_workspace", _sz, _i32, _i64)
 _alc = _sig("lrc_allocate_ranks", _int, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp, _vp)
 _chol_ws = _sig("lrc_cholesky_workspace", _sz, _i64)
 _chol = _sig("lrc_cholesky", _int, _vp, _i64, _i64, _vp, _sz, _vp, _vp)
-_trmm = _sig("lrc_trmm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp)
-_trsm = _sig("lrc_trsm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp)
+_trmm_ws = _sig("lrc_trmm_workspace", _sz, _i64, _i64)
+_trmm = _sig("lrc_trmm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp)
+_trsm_ws = _sig("lrc_trsm_workspace", _sz, _i32, _i64, _i64)
+_trsm = _sig("lrc_trsm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp)
+_sym64 = _sig("lrc_sym_to_f64", _int, _vp, _i64, _i64, ctypes.c_double, _vp, _i64, _vp)
+_to64 = _sig("lrc_to_f64", _int, _vp, _int, _i64, _i64, _i64, ctypes.c_double, _vp, _i64, _vp)
+_gram64 = _sig("lrc_gram_f64", _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp)
 _tim_en = _sig("lrc_timing_enable", _int, _int)
 _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _int)
@@ -63,7 +68,8 @@ _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c
 EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_accumulate_workspace",
             "lrc_cov_accumulate", "lrc_eigh_workspace", "lrc_eigh", "lrc_error_curve", "lrc_factorize",
             "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_allocate_ranks_workspace",
-            "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm", "lrc_trsm",
+            "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm_workspace", "lrc_trmm",
+            "lrc_trsm_workspace", "lrc_trsm", "lrc_sym_to_f64", "lrc_to_f64", "lrc_gram_f64",
             "lrc_timing_enable", "lrc_timing_read")
 
 
@@ -314,11 +320,69 @@ def lrc_timing_read(kernel: str, reset: bool = True):
     return n.value, ms.value, fl.value
 
 
-def lrc_trmm(side: int, trans: int, L: torch.Tensor, B: torch.Tensor, stream=None):
-    _check(_trmm(side, trans, B.shape[0], B.shape[1], _ptr(L), _rows(L, "L"), _ptr(B), _rows(B, "B"), _stream(stream)))
+def _f64_matrix(t: torch.Tensor, name: str) -> int:
+    if t.dtype != torch.float64:
+        raise ValueError("%s must be float64" % name)
+    return _rows(t, name)
+
+
+def lrc_trmm_workspace(m: int, n: int) -> int:
+    return _trmm_ws(m, n)
+
+
+def lrc_trsm_workspace(side: int, m: int, n: int) -> int:
+    return _trsm_ws(side, m, n)
+
+
+def lrc_trmm(side: int, trans: int, L: torch.Tensor, B: torch.Tensor, ws=None, stream=None):
+    """B <- op(L) B (side 0) or B op(L) (side 1), op(L) = L or L^T; L lower, fp64, in place."""
+    ldl, ldb = _f64_matrix(L, "L"), _f64_matrix(B, "B")
+    m, n = B.shape
+    w, wn = _workspace(_trmm_ws(m, n), B.device, ws)
+    _check(_trmm(side, trans, m, n, _ptr(L), ldl, _ptr(B), ldb, _ptr(w), wn, _stream(stream)))
     return B
 
 
-def lrc_trsm(side: int, trans: int, L: torch.Tensor, B: torch.Tensor, stream=None):
-    _check(_trsm(side, trans, B.shape[0], B.shape[1], _ptr(L), _rows(L, "L"), _ptr(B), _rows(B, "B"), _stream(stream)))
+def lrc_trsm(side: int, trans: int, L: torch.Tensor, B: torch.Tensor, ws=None, stream=None):
+    """B <- op(L)^{-1} B (side 0) or B op(L)^{-1} (side 1); L lower, fp64, in place."""
+    ldl, ldb = _f64_matrix(L, "L"), _f64_matrix(B, "B")
+    m, n = B.shape
+    w, wn = _workspace(_trsm_ws(side, m, n), B.device, ws)
+    _check(_trsm(side, trans, m, n, _ptr(L), ldl, _ptr(B), ldb, _ptr(w), wn, _stream(stream)))
     return B
+
+
+def lrc_sym_to_f64(C: torch.Tensor, scale: float = 1.0, A=None, stream=None):
+    """fp64 symmetric A = scale * C from the upper triangle of the fp32 matrix C."""
+    if C.dtype != torch.float32:
+        raise ValueError("C must be float32")
+    ldc = _rows(C, "C")
+    n = C.shape[-1]
+    if A is None:
+        A = torch.empty(n, n, dtype=torch.float64, device=C.device)
+    lda = _f64_matrix(A, "A")
+    _check(_sym64(_ptr(C), n, ldc, float(scale), _ptr(A), lda, _stream(stream)))
+    return A
+
+
+def lrc_to_f64(X: torch.Tensor, scale: float = 1.0, Y=None, stream=None):
+    """fp64 Y = scale * X for a bf16, fp32 or fp64 matrix X."""
+    ldx = _rows(X, "X")
+    rows, cols = X.shape
+    if Y is None:
+        Y = torch.empty(rows, cols, dtype=torch.float64, device=X.device)
+    ldy = _f64_matrix(Y, "Y")
+    _check(_to64(_ptr(X), _dt(X), rows, cols, ldx, float(scale), _ptr(Y), ldy, _stream(stream)))
+    return Y
+
+
+def lrc_gram_f64(B: torch.Tensor, G=None, stream=None):
+    """Upper triangle of the fp32 matrix G = B B^T, summed in fp64 from the fp64 matrix B."""
+    ldb = _f64_matrix(B, "B")
+    m, n = B.shape
+    if G is None:
+        G = torch.zeros(m, m, dtype=torch.float32, device=B.device)
+    if G.dtype != torch.float32:
+        raise ValueError("G must be float32")
+    _check(_gram64(_ptr(B), m, n, ldb, _ptr(G), _rows(G, "G"), _stream(stream)))
+    return G

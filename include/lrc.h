@@ -210,22 +210,44 @@ lrc_status lrc_allocate_ranks(int32_t n_mats, const double *alpha, const double 
                               int32_t *k_out, void *ws, size_t ws_bytes, int32_t *info, void *stream);
 
 /* ------------------------------------------------------------------------------------
- * Curvature-weighted variant (LASER page, method 1: W~ = S_x W S_g with S_x, S_g Cholesky
- * factors of the activation and gradient covariances; SVD of W~; factors mapped back).
+ * Curvature-weighted variant (LASER page, method 1: the loss increase of a perturbation dW
+ * is approximated by 1/2 vec(dW)^T (G (x) X) vec(dW) with X, G the activation and gradient
+ * covariances; W is moved to W~ = S_x W S_g with Cholesky factors S_x, S_g, truncated there
+ * by SVD, and the factors are mapped back).  With lower factors Sigma = L L^T the transform
+ * is W~ = L_x^T W L_g, so ||L_x^T dW L_g||_F^2 = vec(dW)^T (Sigma_g (x) Sigma_x) vec(dW) for
+ * Y = X W.  All matrices fp64, row-major, in place where stated.
  *
- * lrc_cholesky: in-place lower Cholesky factor of the n x n fp64 SPD matrix A (lower
- *   triangle read; strict upper triangle set to 0).  info: 3 when a pivot is not positive.
- * lrc_trmm: B <- op(L) B (side 0, B m x n, L m x m) or B <- B op(L) (side 1, L n x n),
- *   op(L) = L (trans 0) or L^T (trans 1), L lower triangular fp64.
- * lrc_trsm: B <- op(L)^{-1} B (side 0) or B <- B op(L)^{-1} (side 1), same conventions.
+ * lrc_cholesky: A <- L, the lower Cholesky factor of the n x n SPD matrix A (lower triangle
+ *   read; strict upper triangle set to 0).  info (one entry): 3 when a pivot is <= 0, 1 when
+ *   a pivot is not finite (the first failure is kept; the factor is then not usable).
+ * lrc_trmm: B <- op(L) B (side 0; B m x n, L m x m) or B <- B op(L) (side 1; L n x n), with
+ *   op(L) = L (trans 0) or L^T (trans 1), L lower triangular (upper part not read).  Needs
+ *   workspace of lrc_trmm_workspace(m, n) bytes (the product is formed out of place).
+ * lrc_trsm: B <- op(L)^{-1} B (side 0) or B <- B op(L)^{-1} (side 1), same conventions, in
+ *   place; workspace of lrc_trsm_workspace(side, m, n) bytes holds the inverted 64x64
+ *   diagonal blocks of L.  A zero or non-finite diagonal of L gives non-finite results.
+ * lrc_sym_to_f64: A (n x n, both triangles) = scale * C, C fp32 with its upper triangle read
+ *   (the layout lrc_cov_accumulate writes).
+ * lrc_to_f64: Y (rows x cols) = scale * X, X of dtype t (LRC_BF16, LRC_F32 or LRC_F64).
+ * lrc_gram_f64: G[upper] = B B^T for B m x n fp64, fp64 sums, G m x m fp32 (upper triangle
+ *   incl. diagonal written, strict lower never touched) -- the Gram matrix of W~ whose
+ *   eigendecomposition gives its left singular vectors and squared singular values.
  * ------------------------------------------------------------------------------------ */
 size_t lrc_cholesky_workspace(int64_t n);
 lrc_status lrc_cholesky(double *A, int64_t n, int64_t lda, void *ws, size_t ws_bytes, int32_t *info,
                         void *stream);
+size_t lrc_trmm_workspace(int64_t m, int64_t n);
 lrc_status lrc_trmm(int32_t side, int32_t trans, int64_t m, int64_t n, const double *L, int64_t ldl,
-                    double *B, int64_t ldb, void *stream);
+                    double *B, int64_t ldb, void *ws, size_t ws_bytes, void *stream);
+size_t lrc_trsm_workspace(int32_t side, int64_t m, int64_t n);
 lrc_status lrc_trsm(int32_t side, int32_t trans, int64_t m, int64_t n, const double *L, int64_t ldl,
-                    double *B, int64_t ldb, void *stream);
+                    double *B, int64_t ldb, void *ws, size_t ws_bytes, void *stream);
+lrc_status lrc_sym_to_f64(const float *C, int64_t n, int64_t ldc, double scale, double *A, int64_t lda,
+                          void *stream);
+lrc_status lrc_to_f64(const void *X, lrc_dtype t, int64_t rows, int64_t cols, int64_t ldx, double scale,
+                      double *Y, int64_t ldy, void *stream);
+lrc_status lrc_gram_f64(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg,
+                        void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,8 @@ O7 ``allocate_ranks`` greedy global allocation by importance per parameter (LASE
                       method 2, "global optimisation"), with per-matrix Fisher weights.
 O8 ``kfac_*``         LASER page, method 1: covariances of activations and gradients,
                       Cholesky factors, whitened W~ = L_x^T W L_g, its SVD from the eig of
-                      W~ W~^T, factors mapped back.
+                      W~ W~^T, factors mapped back; ``cholesky``, ``tri_product`` and
+                      ``tri_solve`` are its dense steps on their own.
 
 Readings of points the pages leave open (each one stated where it is used):
 * C is unnormalised (a sum over tokens), so eps_k = ||XW - XW_k||_F^2 exactly.
@@ -330,6 +331,25 @@ def solve_lower_t(L: np.ndarray, B: np.ndarray) -> np.ndarray:
             X[i] -= L[i + 1:, i] @ X[i + 1:]
         X[i] /= L[i, i]
     return X
+
+
+def tri_product(side: int, trans: int, L: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """op(L) B (side 0) or B op(L) (side 1), op(L) = L or L^T with L's lower triangle only
+    (the products of the curvature transform W~ = L_x^T W L_g, LASER page, method 1)."""
+    Lt = np.tril(np.asarray(L, dtype=np.float64))
+    op = Lt.T if trans else Lt
+    B = np.asarray(B, dtype=np.float64)
+    return op @ B if side == 0 else B @ op
+
+
+def tri_solve(side: int, trans: int, L: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """op(L)^{-1} B (side 0) or B op(L)^{-1} (side 1) by substitution with L's lower triangle
+    (the map back A = L_x^{-T} U_k of LASER page, method 1).  Side 1 goes through the
+    transpose: B L^{-1} = (L^{-T} B^T)^T and B L^{-T} = (L^{-1} B^T)^T."""
+    B = np.asarray(B, dtype=np.float64)
+    if side == 0:
+        return solve_lower_t(L, B) if trans else solve_lower(L, B)
+    return (solve_lower(L, B.T) if trans else solve_lower_t(L, B.T)).T
 
 
 def kfac_compress(Sx: np.ndarray, Sg: np.ndarray, W64: np.ndarray, k: int) -> dict:

@@ -90,7 +90,19 @@ def test_argument_errors_are_synchronous():
     # allocate: negative budget
     assert lrc._alc(1, fake, fake, fake, 3, fake, fake, None, -1, fake, None, 0, fake, None) == 1
     # triangular: bad side flag
-    assert lrc._trsm(2, 0, 4, 4, fake, 4, fake, 4, None) == 1
+    assert lrc._trsm(2, 0, 4, 4, fake, 4, fake, 4, fake, 1 << 20, None) == 1
+    # triangular: workspace too small, leading dimension too small
+    need = lrc.lrc_trsm_workspace(0, 100, 8)
+    assert need >= 2 * 64 * 64 * 8
+    assert lrc._trsm(0, 0, 100, 8, fake, 100, fake, 8, fake, need - 1, None) == 3
+    assert lrc._trmm(0, 1, 100, 8, fake, 99, fake, 8, fake, 1 << 20, None) == 1
+    assert lrc._trmm(1, 0, 8, 100, fake, 100, fake, 100, fake, lrc.lrc_trmm_workspace(8, 100) - 1, None) == 3
+    # cholesky: lda < n; conversions: bad dtype, ldx < cols; gram: ldg < m
+    assert lrc._chol(fake, 10, 9, fake, 1 << 20, fake, None) == 1
+    assert lrc._to64(fake, 7, 4, 4, 4, 1.0, fake, 4, None) == 2
+    assert lrc._to64(fake, 0, 4, 4, 3, 1.0, fake, 4, None) == 1
+    assert lrc._sym64(fake, 8, 7, 1.0, fake, 8, None) == 1
+    assert lrc._gram64(fake, 8, 4, 4, fake, 7, None) == 1
 
 
 def test_workspace_queries_are_consistent():

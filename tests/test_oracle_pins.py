@@ -478,3 +478,29 @@ def test_kfac_identity_curvature_is_truncated_svd():
     out = oracle.kfac_compress(np.eye(10), np.eye(13), W, k)
     U, s, Vt = np.linalg.svd(W)
     assert np.allclose(out["A"] @ out["B"], (U[:, :k] * s[:k]) @ Vt[:k], atol=1e-12)
+
+
+def test_tri_product_hand_example():
+    # L = [[2, 0], [3, 4]] with a stray upper entry that must be ignored
+    L = np.array([[2.0, 99.0], [3.0, 4.0]])
+    B = np.array([[1.0, -1.0], [2.0, 5.0]])
+    assert np.array_equal(oracle.tri_product(0, 0, L, B), [[2.0, -2.0], [11.0, 17.0]])
+    assert np.array_equal(oracle.tri_product(0, 1, L, B), [[8.0, 13.0], [8.0, 20.0]])
+    assert np.array_equal(oracle.tri_product(1, 0, L, B), [[-1.0, -4.0], [19.0, 20.0]])
+    assert np.array_equal(oracle.tri_product(1, 1, L, B), [[2.0, -1.0], [4.0, 26.0]])
+
+
+@pytest.mark.parametrize("side,trans", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_tri_solve_against_dense_solve(side, trans):
+    r = np.random.default_rng(40 + 2 * side + trans)
+    L = np.tril(r.standard_normal((11, 11))) + 4 * np.eye(11)
+    L[np.triu_indices(11, 1)] = np.nan  # never read
+    Lt = np.tril(np.nan_to_num(L, nan=0.0))
+    op = Lt.T if trans else Lt
+    B = r.standard_normal((11, 6)) if side == 0 else r.standard_normal((6, 11))
+    X = oracle.tri_solve(side, trans, L, B)
+    ref = np.linalg.solve(op, B) if side == 0 else np.linalg.solve(op.T, B.T).T
+    assert np.allclose(X, ref, rtol=1e-12, atol=1e-12)
+    # and the product undoes the solve
+    assert np.allclose(oracle.tri_product(side, trans, Lt, X), B, atol=1e-12)
+
