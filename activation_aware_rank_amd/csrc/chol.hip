@@ -188,9 +188,14 @@ lrc_status launch_gemm(const GemmArgs &g, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return LRC_OK;
     const int gy = cdiv(g.M, GT), gx = cdiv(g.N, GT);
     if (gy > GRID_Y_MAX) return fail(LRC_ERR_ARG, "matrix too tall for the fp64 product kernel");
+    // algorithmic flops: a triangular output (square M = N) counts its triangle incl. the diagonal,
+    // a triangular operand of order K its nonzero half
+    double flops = 2.0 * double(g.M) * double(g.N) * double(g.K);
+    if (g.tiles != 0) flops = double(g.M) * double(g.M + 1) * double(g.K);
+    if (MA != 0 || MB != 0) flops = double(g.M) * double(g.N) * double(g.K + 1);
     const int tok = timing_begin("k_dgemm", s);
     hipLaunchKernelGGL((k_dgemm<TA, TB, MA, MB, OUTF>), dim3(gx, gy), dim3(256), 0, s, g);
-    timing_end(tok, s, 2.0 * double(g.M) * double(g.N) * double(g.K));
+    timing_end(tok, s, flops);
     LRC_LAUNCH_CHECK("k_dgemm");
     return LRC_OK;
 }

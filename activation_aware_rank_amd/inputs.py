@@ -217,3 +217,20 @@ def curvature_layer(n_tok: int = 131072, d_in: int = 5120, d_out: int = 13824) -
         "dtype": "bf16",
     }
 
+
+def curvature_layer_gpu(n_tok: int, d_in: int, d_out: int, seed: int, device) -> dict:
+    """The curvature_layer recipe drawn on the GPU by torch's seeded generator (other numbers than
+    the host draw; used at full size, where results are checked through properties)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    scale = torch.exp(torch.randn(d_in, generator=g, device=device, dtype=torch.float32))
+    X = torch.empty(n_tok, d_in, dtype=torch.bfloat16, device=device)
+    G = torch.empty(n_tok, d_out, dtype=torch.bfloat16, device=device)
+    for r0 in range(0, n_tok, 16384):
+        r1 = min(n_tok, r0 + 16384)
+        X[r0:r1] = (torch.randn(r1 - r0, d_in, generator=g, device=device) * scale).to(torch.bfloat16)
+        G[r0:r1] = (torch.randn(r1 - r0, d_out, generator=g, device=device) * 1e-3).to(torch.bfloat16)
+    W = (torch.randn(d_in, d_out, generator=g, device=device) * 0.02).to(torch.bfloat16)
+    return {"X": X, "G": G, "W": W}
+

@@ -99,6 +99,44 @@ def cpu_baseline(d_model, d_ff, sample_tok):
             "seconds": dt}
 
 
+PEAK_F64_TFLOPS = 78.6  # MI355X dense fp64 (MFMA and vector)
+
+
+def curvature_leg(torch, lrc, n_tok, seed, prec, dev, d_in=5120, d_out=13824, k=1024):
+    """The curvature-weighted chain (LASER page, method 1) on a 13B-shaped FFN matrix: one warm-up
+    run, then one timed run with per-stage events and the fp64 product kernel's own timings."""
+    from activation_aware_rank_amd import inputs
+    from activation_aware_rank_amd.curvature import curvature_truncation
+    d = inputs.curvature_layer_gpu(n_tok, d_in, d_out, seed + 5, dev)
+    curvature_truncation(d["X"], d["G"], d["W"], k, prec)
+    torch.cuda.synchronize()
+    for kern in ("k_dgemm", "k_cov_syrk", "k_cov_gemm_y"):
+        lrc.lrc_timing_read(kern, reset=True)
+    lrc.lrc_timing_enable(True)
+    marks = []
+    t0 = time.perf_counter()
+    out = curvature_truncation(d["X"], d["G"], d["W"], k, prec, marks=marks)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lrc.lrc_timing_enable(False)
+    dg_n, dg_ms, dg_fl = lrc.lrc_timing_read("k_dgemm", reset=False)
+    sy_n, sy_ms, sy_fl = lrc.lrc_timing_read("k_cov_syrk", reset=True)  # a reset drops every record
+    assert int(out["info"].sum().item()) == 0, "curvature chain info flags: %s" % out["info"].tolist()
+    stages = {marks[i][0]: round(marks[i - 1][1].elapsed_time(marks[i][1]), 3) for i in range(1, len(marks))}
+    dg_tf = dg_fl / (dg_ms / 1000.0) / 1e12 if dg_ms > 0 else 0.0
+    return {
+        "workload": "13B-shaped FFN matrix W %dx%d bf16, %d calibration tokens (activations and output "
+                    "gradients), k = %d, eig prec %s" % (d_in, d_out, n_tok, k, "f64" if prec == 2 else "f32"),
+        "seconds_per_layer": wall,
+        "stage_ms": stages,
+        "roofline_dgemm": {"kernel": "k_dgemm", "bound": "mfma", "achieved": dg_tf, "peak": PEAK_F64_TFLOPS,
+                           "unit": "TFLOP/s", "frac": dg_tf / PEAK_F64_TFLOPS, "launches": dg_n, "total_ms": dg_ms,
+                           "per_launch": "algorithmic flops = 2 M N K of the launch; a triangular output "
+                                         "counts M (M + 1) K, a triangular operand M N (K + 1)"},
+        "syrk_ms": sy_ms, "syrk_tflops": (sy_fl / (sy_ms / 1000.0) / 1e12) if sy_ms > 0 else 0.0,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +151,9 @@ def main():
     ap.add_argument("--seed", type=int, default=20261203)
     ap.add_argument("--breakdown", action="store_true", help="print per-call timings to stderr")
     ap.add_argument("--calib-copy-mb", type=int, default=1024, help="size of the byte-counter reference copy")
+    ap.add_argument("--curvature-tokens", type=int, default=131072,
+                    help="tokens of the curvature-weighted 13B FFN leg, timed after the block (0: skip)")
+    ap.add_argument("--curvature-prec", choices=("f32", "f64"), default="f64")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported (the path would shard matrices "
@@ -267,6 +308,11 @@ def main():
         "roofline": roof,
         "roofline_gemm_y": roof_gemm,
     }
+    if a.curvature_tokens > 0:
+        del X, Xd, W, G, C, V, A, B, ws_cov, ws_eig
+        torch.cuda.empty_cache()
+        out["curvature_layer"] = curvature_leg(torch, lrc, a.curvature_tokens, a.seed,
+                                               lrc.LRC_F32 if a.curvature_prec == "f32" else lrc.LRC_F64, dev)
     if a.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(a.d_model, a.d_ff, a.cpu_sample)
     print(json.dumps(out))

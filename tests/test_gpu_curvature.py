@@ -226,3 +226,59 @@ def test_curvature_chain_parity(lrc, prec):
     R = Lx.T @ (W64 - Wk) @ Lg
     tail = np.sum(np.maximum(lam[k:], 0.0))
     assert abs(np.sum(R * R) - tail) <= 1e-4 * tail
+
+
+def test_curvature_chain_full_size_properties(lrc):
+    """13B-shaped FFN matrix at full size (131072 tokens, 5120 x 13824, k = 1024), inputs drawn on
+    the GPU; checked through properties that hold at any size (fp64 torch products as the checker):
+    Cholesky backward error on sampled rows, the whitening products on sampled columns, eigen-
+    residual and orthogonality of U_k, L_x^T A = U_k, and the closed-form weighted error."""
+    from activation_aware_rank_amd.curvature import curvature_truncation
+    n_tok, d_in, d_out, k = 131072, 5120, 13824, 1024
+    _say("curvature chain full size N=%d %dx%d k=%d prec=2" % (n_tok, d_in, d_out, k))
+    d = inputs.curvature_layer_gpu(n_tok, d_in, d_out, 20261203, torch.device("cuda"))
+    out = curvature_truncation(d["X"], d["G"], d["W"], k, prec=2)
+    assert np.all(host(out["info"]) == 0), host(out["info"])
+    f64 = torch.float64
+    gen = torch.Generator().manual_seed(5)
+
+    # Cholesky: |L L^T - Sigma|_ij <= 2 (n + 1) 2^-53 sqrt(Sigma_ii Sigma_jj), Sigma recomputed by
+    # the same deterministic entry points
+    for name, X, n in (("Lx", d["X"], d_in), ("Lg", d["G"], d_out)):
+        C = torch.zeros(n, n, dtype=torch.float32, device="cuda")
+        lrc.lrc_cov_accumulate(X, None, C)
+        S = lrc.lrc_sym_to_f64(C, 1.0 / n_tok)
+        del C
+        L = out[name]
+        rows = torch.randint(0, n, (48,), generator=gen).cuda()
+        R = L[rows] @ L.T
+        dS = torch.sqrt(torch.diagonal(S))
+        bound = 2 * (n + 1) * 2.0 ** -53 * dS[rows][:, None] * dS[None, :]
+        excess = float(((R - S[rows]).abs() - bound).max())
+        assert excess <= 0.0, "%s backward error exceeds the bound by %.3e" % (name, excess)
+        del S, R
+    Lx, Lg = out["Lx"], out["Lg"]
+    W64 = d["W"].to(f64)
+    # whitening: W~[:, cols] = L_x^T (W L_g[:, cols])
+    cols = torch.randint(0, d_out, (32,), generator=gen).cuda()
+    ref = Lx.T @ (W64 @ Lg[:, cols])
+    e = float((out["Wt"][:, cols] - ref).abs().max() / ref.abs().max())
+    assert e <= 1e-12, "whitening error %.3e" % e
+    # eigenpairs of M = W~ W~^T (fp32 storage): residual and orthogonality of U_k
+    lam = out["lam"]
+    U = out["U"].to(f64)
+    Wt = out["Wt"]
+    MU = Wt @ (Wt.T @ U)
+    res = float(torch.linalg.vector_norm(MU - U * lam[:k], dim=0).max() / lam[0])
+    orth = float((U.T @ U - torch.eye(k, dtype=f64, device="cuda")).abs().max())
+    assert res <= 1e-5 and orth <= 1e-5, "eig residual %.3e, orthogonality %.3e" % (res, orth)
+    # A solves L_x^T A = U_k
+    e = float((Lx.T @ out["A"] - U).abs().max())
+    assert e <= 1e-10, "triangular solve residual %.3e" % e
+    # closed form: ||L_x^T (W - A B) L_g||_F^2 = sum of the discarded eigenvalues
+    D = W64 - out["A"] @ out["Bt"].to(f64).T
+    R = (Lx.T @ D) @ Lg
+    tail = float(lam[k:].clamp(min=0).sum())
+    got = float((R * R).sum())
+    print("closed form: %.6e vs tail %.6e, eig residual %.2e, orth %.2e" % (got, tail, res, orth))
+    assert abs(got - tail) <= 1e-4 * tail
