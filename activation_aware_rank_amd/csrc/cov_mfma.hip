@@ -21,6 +21,7 @@
 // buffer and the buffers are added to C in split order at the end of the call (fixed order,
 // deterministic).
 #include <cmath>
+#include <type_traits>
 
 #include "cov_mfma.h"
 
@@ -28,8 +29,19 @@ namespace lrc {
 
 constexpr int MK = 32;                   // k step, bf16 elements (4 chunks of 16 bytes)
 constexpr int64_t MFMA_CHUNK = 32768;    // tokens per internal chunk
+#ifndef SYRK_FE
+#define SYRK_FE 2
+#endif
+#ifndef SYRK_WPE
+#define SYRK_WPE 1  // SYRK waves per SIMD (resident blocks per CU)
+#endif
+#ifndef SYRK_DEPTH
+#define SYRK_DEPTH 2
+#endif
 
-__device__ __forceinline__ int swz(int r, int c) { return r * MK + ((c ^ ((r >> 1) & 3)) << 3); }
+// 16-byte chunk c of row r: XOR with bits 1..3 of r so that 16 consecutive rows reading one chunk
+// column hit 16 distinct 16-byte bank groups (and 8 consecutive rows 8 distinct groups)
+__device__ __forceinline__ int swz(int r, int c) { return r * MK + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 3); }
 
 // Block tile BM x BM, THREADS/64 waves arranged WGM x WGN, wave tile (BM/WGM) x (BM/WGN).
 template <int BM, int THREADS, int WGM>
@@ -48,7 +60,9 @@ struct MfmaCfg {
 // fp32 addition per 16 tokens instead of a long chain of MFMA accumulations.  Otherwise the
 // MFMAs accumulate into acc directly (used where the contraction is short or the rounding
 // errors are not one-signed).
-template <int BM, int THREADS, int WGM, int NOPS, int NPROD, bool FLUSH>
+// DEPTH: k steps of global loads in flight (1: the next step; 2: the next two, in two register
+// sets used alternately -- the k loop is unrolled by two so that every index is static).
+template <int BM, int THREADS, int WGM, int NOPS, int NPROD, bool FLUSH, int FE = 1, bool KCHECK = true, int DEPTH = 1>
 __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const int64_t *ld, const int *rows,
                                               int64_t klen,
                                               f32x16_t (&acc)[MfmaCfg<BM, THREADS, WGM>::TM][MfmaCfg<BM, THREADS, WGM>::TN],
@@ -59,42 +73,72 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / T::WGN, wn = wave % T::WGN;
     const int nk = int((klen + MK - 1) / MK);
-    u32x4_t regs[NOPS][U];
+    u32x4_t regs[DEPTH][NOPS][U];
+    // One buffer resource per operand covering its rows[o] rows: a load past them returns zero
+    // without a branch.  Offsets are 32-bit byte offsets from the operand's first row (the host
+    // keeps rows * ld * 2 below 2^31).
+    __amdgpu_buffer_rsrc_t rs[NOPS];
+#pragma unroll
+    for (int o = 0; o < NOPS; ++o)
+        rs[o] = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base[o]), short(0),
+                                                  int(int64_t(rows[o]) * ld[o] * 2), 0x00020000);
 
-    auto gload = [&](int kt) {
-        const int64_t k0 = int64_t(kt) * MK;
+    auto gload = [&](int kt, auto set) {
+        constexpr int S = decltype(set)::value;
+        const int k0 = kt * MK;
 #pragma unroll
         for (int o = 0; o < NOPS; ++o)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int q = tid + THREADS * u;
                 const int r = q >> 2, c = q & 3;
-                const int64_t k = k0 + c * 8;
-                if (r < rows[o] && k < klen)
-                    regs[o][u] = *reinterpret_cast<const u32x4_t *>(base[o] + int64_t(r) * ld[o] + k);
-                else
-                    regs[o][u] = u32x4_t{0u, 0u, 0u, 0u};
+                const int k = k0 + c * 8;
+                u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs[o], (r * int(ld[o]) + k) * 2, 0, 0);
+                if (KCHECK && k >= klen) v = u32x4_t{0u, 0u, 0u, 0u};
+                regs[S][o][u] = v;
             }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int buf, auto set) {
+        constexpr int S = decltype(set)::value;
 #pragma unroll
         for (int o = 0; o < NOPS; ++o)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int q = tid + THREADS * u;
                 const int r = q >> 2, c = q & 3;
-                *reinterpret_cast<u32x4_t *>(lds + (buf * NOPS + o) * OPSZ + swz(r, c)) = regs[o][u];
+                *reinterpret_cast<u32x4_t *>(lds + (buf * NOPS + o) * OPSZ + swz(r, c)) = regs[S][o][u];
             }
     };
 
     if (nk <= 0) return;
-    gload(0);
-    sstore(0);
+    // FLUSH: p holds the MFMA chain of the last FE 16-wide k slices (FE = 1 or 2)
+    f32x16_t p[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) p[tm][tn] = f32x16_t{};
+    auto flush = [&]() {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[tm][tn][r] = __fadd_rn(acc[tm][tn][r], p[tm][tn][r]);
+            }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    gload(0, I0{});
+    sstore(0, I0{});
+    if constexpr (DEPTH == 2) {
+        if (nk > 1) gload(1, I1{});
+    }
     __syncthreads();
     constexpr int NA = (NPROD == 4) ? 2 : 1;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+    // one k step from LDS buffer cur; loads of step kt + DEPTH go to register set lset, and step
+    // kt + 1 is stored from register set sset
+    auto step = [&](int kt, int cur, auto lset, auto sset) {
+        if (kt + DEPTH < nk) gload(kt + DEPTH, lset);
         const bf16_t *sb = lds + cur * NOPS * OPSZ;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -114,23 +158,33 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
-                    f32x16_t p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[0][tn],
-                                                                         FLUSH ? f32x16_t{} : acc[tm][tn], 0, 0, 0);
+                    // a flush group's first slice starts the chain from a literal zero
+                    const bool fresh = FLUSH && (FE == 1 || (FE == 2 && ks == 0));
+                    f32x16_t q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[0][tm], bfr[0][tn], fresh ? f32x16_t{} : (FLUSH ? p[tm][tn] : acc[tm][tn]), 0, 0, 0);
                     if (NPROD == 4) {
-                        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[1][tn], p, 0, 0, 0);
-                        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[0][tn], p, 0, 0, 0);
-                        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[1][tn], p, 0, 0, 0);
+                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[1][tn], q, 0, 0, 0);
+                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[0][tn], q, 0, 0, 0);
+                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[1][tn], q, 0, 0, 0);
                     }
-                    if (FLUSH) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[tm][tn][r] = __fadd_rn(acc[tm][tn][r], p[r]);
-                    } else {
-                        acc[tm][tn] = p;
-                    }
+                    if (FLUSH)
+                        p[tm][tn] = q;
+                    else
+                        acc[tm][tn] = q;
                 }
+            if (FLUSH && FE == 1) flush();
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
+        if (FLUSH && FE == 2) flush();
+        if (kt + 1 < nk) sstore(cur ^ 1, sset);
         __syncthreads();
+    };
+    if constexpr (DEPTH == 1) {
+        for (int kt = 0; kt < nk; ++kt) step(kt, kt & 1, I0{}, I0{});
+    } else {
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, 0, I0{}, I1{});
+            if (kt + 1 < nk) step(kt + 1, 1, I1{}, I0{});
+        }
     }
 }
 
@@ -165,7 +219,7 @@ __device__ __forceinline__ void add_upper_tile(const f32x16_t a, int64_t rb, int
 
 // Phase 1: Y^T tile (rows = output features i, cols = tokens t), split into hi/lo.
 constexpr int G_BM = 256, G_THREADS = 256, G_WGM = 2;
-template <int BM>
+template <int BM, bool KCHECK>
 __global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const bf16_t *__restrict__ X, int64_t ldx,
              int64_t tc, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo, int64_t ldy) {
@@ -180,7 +234,7 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
     for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
-    mfma_mainloop<BM, G_THREADS, G_WGM, 2, 1, false>(base, ld, rows, d_in, acc, lds);
+    mfma_mainloop<BM, G_THREADS, G_WGM, 2, 1, false, 1, KCHECK>(base, ld, rows, d_in, acc, lds);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm)
@@ -199,7 +253,7 @@ struct SyrkCfg {  // 4 waves of (BM/2) x (BM/2)
     static constexpr int WGM = 2;
 };
 template <int BM, int NPROD>
-__global__ void __launch_bounds__(SyrkCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(SyrkCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(SYRK_WPE, SYRK_WPE)))
 k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64_t ldy, int64_t ktot, int64_t kchunk,
            int64_t hd, float *__restrict__ C, int64_t ldc, float *__restrict__ P, int32_t n_blocks) {
     constexpr int THREADS = SyrkCfg<BM>::THREADS, WGM = SyrkCfg<BM>::WGM;
@@ -234,7 +288,8 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
     for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
-    mfma_mainloop<BM, THREADS, WGM, NOPS, NPROD, true>(base, ld, rows, klen, acc, lds);
+    // klen is a multiple of MK here, so no k check is needed
+    mfma_mainloop<BM, THREADS, WGM, NOPS, NPROD, true, SYRK_FE, false, SYRK_DEPTH>(base, ld, rows, klen, acc, lds);
     float *dst;
     int64_t ldd;
     if (s == 0) {
@@ -326,16 +381,17 @@ static MfmaPlan plan(int64_t n_tok, int64_t d_out, int32_t n_blocks) {
     const int64_t th = (hd + p.bm - 1) / p.bm;
     p.n_upper = th * (th + 1) / 2;
     const int64_t tiles = p.n_upper * n_blocks;
-    // smallest split count that fills >= 90% of the last wave of 256 single-block CUs, while
-    // keeping at least 8 k-steps per split
+    // smallest split count that fills >= 90% of the last wave of 256 CUs x SYRK_WPE resident
+    // blocks, while keeping at least 8 k-steps per split
     const int64_t ksteps = p.ldy / MK;
+    const int64_t slots = 256 * SYRK_WPE;
     p.nsplit = 1;
     for (int s = 1; s <= 16; ++s) {
         if (s > 1 && ksteps / s < 8) break;
         const int64_t blocks = tiles * s;
-        const int64_t waves = (blocks + 255) / 256;
+        const int64_t waves = (blocks + slots - 1) / slots;
         p.nsplit = s;
-        if (double(blocks) / double(waves * 256) >= 0.9) break;
+        if (double(blocks) / double(waves * slots) >= 0.9) break;
     }
     return p;
 }
@@ -348,8 +404,9 @@ bool cov_mfma_supported(lrc_dtype x_t, const void *X, int64_t ldx, const void *W
                         int64_t d_out, int32_t n_blocks) {
     (void)W;
     (void)ldw;
+    // buffer-load byte offsets are 32-bit: a 256-row operand tile must stay below 2^31 bytes
     return x_t == LRC_BF16 && cov_mfma_shape_ok(d_in, d_out, n_blocks) && ldx % 8 == 0 &&
-           (reinterpret_cast<uintptr_t>(X) % 16) == 0;
+           (reinterpret_cast<uintptr_t>(X) % 16) == 0 && ldx < (int64_t(1) << 21) && d_in < (int64_t(1) << 21);
 }
 
 size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks) {
@@ -393,8 +450,13 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         if (has_w) {
             dim3 g(cdiv(a.d_out, 256), cdiv(ktot, 256));
             const int tk = timing_begin("k_cov_gemm_y", s);
-            hipLaunchKernelGGL(k_cov_gemm_y<G_BM>, g, dim3(G_THREADS), 0, s, Wt, a.d_in, a.d_out, X + t0 * a.ldx,
-                               a.ldx, tc, Yhi, Ylo, p.ldy);
+            // d_in a multiple of the k step: no partial last step, no k check in the loads
+            if (a.d_in % MK == 0)
+                hipLaunchKernelGGL((k_cov_gemm_y<G_BM, false>), g, dim3(G_THREADS), 0, s, Wt, a.d_in, a.d_out,
+                                   X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo, p.ldy);
+            else
+                hipLaunchKernelGGL((k_cov_gemm_y<G_BM, true>), g, dim3(G_THREADS), 0, s, Wt, a.d_in, a.d_out,
+                                   X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo, p.ldy);
             timing_end(tk, s, 2.0 * double(tc) * double(a.d_in) * double(a.d_out));
             LRC_LAUNCH_CHECK("k_cov_gemm_y");
         } else {

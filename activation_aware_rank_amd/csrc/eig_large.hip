@@ -24,20 +24,28 @@ namespace lrc {
 constexpr int NB = 32;    // tridiagonalisation panel width
 constexpr int NBT = 32;   // back-transformation block of reflectors
 constexpr int RCH = 512;  // rows per partial in the back-transformation reductions
-constexpr int SYMV_BLOCKS = 128;  // blocks of 16 waves in the symmetric product (rows strided over them)
 
 // ---------------------------------------------------------------------------------------------
 // 1. tridiagonalisation
 // ---------------------------------------------------------------------------------------------
+// Storage: A is n x lda (lda a multiple of 64), row-major; only the upper triangle (r <= s) is kept
+// current, and the padding columns [n, lda) hold zeros.  Column c below the diagonal is read as
+// row c right of it, so every access to it is contiguous.  The panel factors V and W (NB columns
+// of length n) are column-major, V[q][r] at Vp[q * n + r], so that per-row loops over a panel
+// column read consecutive addresses.
 template <class T>
 __global__ void k_fill_full(const float *__restrict__ C, int64_t ldc, int64_t n, T *__restrict__ A, int64_t lda,
                             int *__restrict__ bad) {
-    const int64_t total = n * n;
+    const int64_t total = n * lda;
     for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total; e += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t i = e / n, j = e % n;
+        const int64_t i = e / lda, j = e % lda;
+        if (j >= n) {
+            A[e] = T(0);
+            continue;
+        }
         const float v = i <= j ? C[i * ldc + j] : C[j * ldc + i];
         if (!isfinite(v)) atomicOr(bad, 1);
-        A[i * lda + j] = T(v);
+        A[e] = T(v);
     }
 }
 
@@ -63,12 +71,12 @@ __device__ __forceinline__ T block_sum(T v, T *sh) {
 // Each column of a panel takes three launches; each global reduction is done by the next launch,
 // redundantly in every block that needs it and always in the same fixed order, so all blocks see
 // bit-identical values (no atomics, no device-wide fences):
-//   k_trd_col : finish W[:, j-1] (reduces the previous column's w1.v partials), update column c,
-//               partials of ||x||^2
-//   k_trd_symv: reflector of column c (reduces the ||x||^2 partials; block 0 stores d[c], e[c],
-//               tau[c]); v into V[:, j] and Rt[c]; w_raw = A v over the trailing rows; partials of
-//               W^T v and V^T v
-//   k_trd_w1  : w1 = tau (w_raw - V q1 - W q2) (reduces the q partials); partials of w1.v
+//   k_trd_col : finish W[:, j-1] (reduces the previous column's w1.v partials), update row c (the
+//               column below the diagonal), partials of ||x||^2
+//   k_trd_symv: reflector of column c (reduces the ||x||^2 partials; block 0 stores e[c], tau[c]);
+//               y = A v over the upper tiles of the trailing matrix as fixed-order partials; v
+//               into V[:, j] and Rt[c]; partials of W^T v and V^T v
+//   k_trd_w1  : y from its partials; w1 = tau (y - V q1 - W q2); partials of w1.v
 // W[:, j] = w1 - (tau/2)(w1.v) v is formed by the next k_trd_col (or k_trd_wlast at panel end).
 
 // fixed-order sum of p[0..np) by one block: strided per-thread sums, then a tree (every thread)
@@ -79,63 +87,134 @@ __device__ __forceinline__ T block_sum_array(const T *__restrict__ p, int np, T 
     return block_sum(acc, red);
 }
 
+// Sum over the 64 lanes of each of 64 per-lane values, by a butterfly that halves the values each
+// lane keeps at every step (63 exchanges): afterwards lane l holds the sum of value l.
+template <int ST, class T>
+__device__ __forceinline__ void transpose_sum_stage(T (&p)[64], int lane) {
+    const bool up = (lane & ST) != 0;
+#pragma unroll
+    for (int k = 0; k < ST; ++k) {  // constant trip count: the array stays in registers
+        const T send = up ? p[k] : p[k + ST];
+        const T keep = up ? p[k + ST] : p[k];
+        p[k] = keep + __shfl_xor(send, ST);
+    }
+}
 template <class T>
-__global__ void __launch_bounds__(256) k_trd_col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
-                                                 T *__restrict__ Vp, T *__restrict__ Wp, const T *__restrict__ w1buf,
-                                                 T *__restrict__ colbuf, T *__restrict__ part, const T *__restrict__ dpart,
-                                                 int ndp, const T *__restrict__ tau, double *__restrict__ d) {
+__device__ __forceinline__ T wave_transpose_sum64(T (&p)[64]) {
+    const int lane = threadIdx.x & 63;
+    transpose_sum_stage<32>(p, lane);
+    transpose_sum_stage<16>(p, lane);
+    transpose_sum_stage<8>(p, lane);
+    transpose_sum_stage<4>(p, lane);
+    transpose_sum_stage<2>(p, lane);
+    transpose_sum_stage<1>(p, lane);
+    return p[0];
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) k_trd_col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
+                                                 const T *__restrict__ Vp, T *__restrict__ Wp,
+                                                 const T *__restrict__ w1buf, T *__restrict__ colbuf,
+                                                 T *__restrict__ part, T *__restrict__ qcol,
+                                                 const T *__restrict__ dpart, int ndp, const T *__restrict__ tau,
+                                                 double *__restrict__ d) {
     __shared__ T sh[4];
     __shared__ T vc[NB], wc[NB];
+    __shared__ T qred[4][2 * NB];
     T half = T(0);
     if (j > 0) half = T(0.5) * tau[c - 1] * block_sum_array(dpart, ndp, sh);
     if (threadIdx.x < NB) {
         const int q = threadIdx.x;
-        vc[q] = q < j ? Vp[c * NB + q] : T(0);
-        T wv = q < j ? Wp[c * NB + q] : T(0);
-        if (q == j - 1) wv = w1buf[c] - half * Vp[c * NB + q];  // row c of the column being finished
+        vc[q] = q < j ? Vp[q * n + c] : T(0);
+        T wv = q < j ? Wp[q * n + c] : T(0);
+        if (q == j - 1) wv = w1buf[c] - half * Vp[q * n + c];  // row c of the column being finished
         wc[q] = wv;
     }
     __syncthreads();
     const int64_t r = c + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     T ss = T(0);
+    T pq[64];  // W[q][r] x[r] (q < NB) and V[q][r] x[r] for the W^T x, V^T x partials
+#pragma unroll
+    for (int q = 0; q < 64; ++q) pq[q] = T(0);
     if (r < n) {
-        T wl = T(0);
+        T wrow[NB], vrow[NB];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            vrow[q] = q < j ? Vp[q * n + r] : T(0);
+            wrow[q] = q < j - 1 ? Wp[q * n + r] : T(0);
+        }
         if (j > 0) {  // finish W[r][j-1] for this row
-            wl = w1buf[r] - half * Vp[r * NB + j - 1];
-            Wp[r * NB + j - 1] = wl;
+            const T wl = w1buf[r] - half * Vp[(j - 1) * n + r];
+            Wp[(j - 1) * n + r] = wl;
+#pragma unroll
+            for (int q = 0; q < NB; ++q)
+                if (q == j - 1) wrow[q] = wl;
         }
-        T a = A[r * lda + c];
-        for (int q = 0; q < j; ++q) {
-            const T wr = (q == j - 1) ? wl : Wp[r * NB + q];
-            a -= Vp[r * NB + q] * wc[q] + wr * vc[q];
-        }
-        A[r * lda + c] = a;
+        T a = A[c * lda + r];  // = A[r][c] (upper storage)
+#pragma unroll
+        for (int q = 0; q < NB; ++q) a -= vrow[q] * wc[q] + wrow[q] * vc[q];
+        A[c * lda + r] = a;
         colbuf[r] = a;
-        if (r >= c + 2) ss = a * a;
+        if (r >= c + 2) {
+            ss = a * a;
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                pq[q] = wrow[q] * a;
+                pq[NB + q] = vrow[q] * a;
+            }
+        }
         if (r == c) d[c] = double(a);
     }
     ss = block_sum(ss, sh);
     if (threadIdx.x == 0) part[blockIdx.x] = ss;
+    const T qsum = wave_transpose_sum64(pq);
+    qred[threadIdx.x >> 6][threadIdx.x & 63] = qsum;
+    __syncthreads();
+    if (threadIdx.x < 2 * NB)
+        qcol[int64_t(blockIdx.x) * 2 * NB + threadIdx.x] =
+            (qred[0][threadIdx.x] + qred[1][threadIdx.x]) + (qred[2][threadIdx.x] + qred[3][threadIdx.x]);
 }
 
-// w_raw[r] = sum_{k > c} A[r][k] v[k] for rows r in [c+1, n), one row per wave at a time (rows
-// strided over the grid), read with 16-byte loads from the aligned column kb <= c+1 (v[k] = 0 for
-// k <= c).  Also stores v in V[:, j] and Rt[c], and the block partials of W^T v and V^T v.
-constexpr int SYMV_WAVES = 16;
+// Symmetric product y = A v over the upper tiles of the trailing matrix.  Tiles are TS x TS,
+// aligned to multiples of TS (TS = 64 for fp32, 32 for fp64: 256-byte tile rows of 16 chunks of
+// 16 bytes).  Work item (block row i, chunk ch) covers tiles J = i + ch*CH ... of that block row;
+// the items are numbered by L = NT - i (the number of upper tiles in block row i), L = 1 first.
+// Each wave takes one tile at a time: it stages the tile in LDS with the 16-byte chunks of row r
+// XOR-permuted by (r mod 16), then lane rr forms the row part sum_k A[rr][k] v_J[k] (reading
+// 16-byte chunks along its row) and lane cc the column part sum_r A[r][cc] v_I[r] (scalar reads
+// down its column); both patterns are free of bank conflicts.  Row parts accumulate over the
+// chunk's tiles and are written once per item; column parts go to colpart[i][J] (J > i) or, for
+// the diagonal tile, into the row part (strict upper entries only; the lower half of a diagonal
+// tile is never read).
 template <class T>
-__global__ void __launch_bounds__(SYMV_WAVES * 64) k_trd_symv(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c,
-                                                              int j, const T *__restrict__ colbuf,
-                                                              const T *__restrict__ part, int npart,
-                                                              T *__restrict__ Vp, const T *__restrict__ Wp,
-                                                              T *__restrict__ Rt, T *__restrict__ wbuf,
-                                                              T *__restrict__ qpart, T *__restrict__ tau,
-                                                              double *__restrict__ e) {
-    constexpr int VEC = 16 / sizeof(T);
-    constexpr int NW = SYMV_WAVES;
-    typedef T vec_t __attribute__((ext_vector_type(VEC)));
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    T *vs = reinterpret_cast<T *>(smem_raw);  // v[kb .. n)
-    __shared__ T sh[NW];
+struct SymvTile {
+    static constexpr int TS = sizeof(T) == 4 ? 64 : 32;
+    static constexpr int EPC = 16 / int(sizeof(T));  // elements per 16-byte chunk
+    static constexpr int H = 64 / TS;                 // lanes per tile row
+};
+
+// number of work items of block rows with L = 1 .. m tiles, chunks of ch tiles
+__host__ __device__ __forceinline__ int64_t symv_items(int64_t m, int64_t ch) {
+    const int64_t q = m / ch, r = m % ch;
+    return ch * q * (q + 1) / 2 + r * (q + 1);
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) k_trd_symv(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
+                                                  const T *__restrict__ colbuf, const T *__restrict__ part,
+                                                  int npart, T *__restrict__ Vp, const T *__restrict__ Wp,
+                                                  T *__restrict__ Rt, T *__restrict__ rowpart,
+                                                  T *__restrict__ colpart, const T *__restrict__ qcol,
+                                                  T *__restrict__ qvec, T *__restrict__ tau, double *__restrict__ e,
+                                                  int NT, int CHK) {
+    constexpr int TS = SymvTile<T>::TS, EPC = SymvTile<T>::EPC, H = SymvTile<T>::H;
+    static_assert(16 * EPC == TS, "tile geometry");
+    typedef T vec_t __attribute__((ext_vector_type(EPC)));
+    __shared__ __attribute__((aligned(16))) T tile[4][TS * TS];
+    __shared__ __attribute__((aligned(16))) T vI[TS];
+    __shared__ __attribute__((aligned(16))) T vJ[8 * TS];
+    __shared__ T rowacc[4][TS];
+    __shared__ T sh[4];
     // the reflector of column c: alpha = x[0], sigma2 = ||x[1:]||^2; tau = (beta - alpha)/beta,
     // v = [1, x[1:] / (alpha - beta)], beta = -sign(alpha) ||x||; tau = 0 when x[1:] = 0
     const T sigma2 = block_sum_array(part, npart, sh);
@@ -155,99 +234,135 @@ __global__ void __launch_bounds__(SYMV_WAVES * 64) k_trd_symv(const T *__restric
         e[c] = double(beta);
         tau[c] = tv;
     }
-    const int64_t kb = (c + 1) / VEC * VEC;
-    const int64_t m = n - kb;
-    const int64_t mv = m / VEC;
-    for (int64_t k = threadIdx.x; k < m; k += blockDim.x) {
-        const int64_t kk = kb + k;
-        vs[k] = kk <= c ? T(0) : (kk == c + 1 ? T(1) : colbuf[kk] * scale);
+    // work item: L with items(L - 1) <= g < items(L)
+    const int64_t g = blockIdx.x;
+    const int T0 = int((c + 1) / TS);
+    int lo = 1, hi = NT - T0;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (symv_items(mid, CHK) > g) hi = mid; else lo = mid + 1;
     }
-    if (blockIdx.x == 0)  // the reflector's zeros above row c+1
-        for (int64_t k = threadIdx.x; k <= c; k += blockDim.x) Rt[c * n + k] = T(0);
+    const int L = lo;
+    const int i = NT - L;
+    const int ch = int(g - symv_items(L - 1, CHK));
+    const int J0 = i + ch * CHK, J1 = min(J0 + CHK, NT);
+    auto vval = [&](int64_t x) -> T {
+        return (x <= c || x >= n) ? T(0) : (x == c + 1 ? T(1) : colbuf[x] * scale);
+    };
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    if (t < TS) vI[t] = vval(int64_t(i) * TS + t);
+    for (int x = t; x < (J1 - J0) * TS; x += 256) vJ[x] = vval(int64_t(J0) * TS + x);
     __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t nrows = n - c - 1;
-    const int64_t wstride = int64_t(gridDim.x) * NW;
-    T qw = T(0), qv = T(0);
-    const vec_t *vs4 = reinterpret_cast<const vec_t *>(vs);
-    for (int64_t rr = int64_t(blockIdx.x) * NW + wave; rr < nrows; rr += wstride) {
-        const int64_t r = c + 1 + rr;
-        const T *row = A + r * lda + kb;
-        const vec_t *row4 = reinterpret_cast<const vec_t *>(row);
-        T acc0 = T(0), acc1 = T(0), acc2 = T(0), acc3 = T(0);
-        int64_t kv = lane;
-        for (; kv + 192 < mv; kv += 256) {
-            const vec_t a0 = __builtin_nontemporal_load(row4 + kv), a1 = __builtin_nontemporal_load(row4 + kv + 64);
-            const vec_t a2 = __builtin_nontemporal_load(row4 + kv + 128), a3 = __builtin_nontemporal_load(row4 + kv + 192);
-            const vec_t b0 = vs4[kv], b1 = vs4[kv + 64], b2 = vs4[kv + 128], b3 = vs4[kv + 192];
+
+    const int rows_i = int(min<int64_t>(TS, n - int64_t(i) * TS));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(A + int64_t(i) * TS * lda), short(0), int(int64_t(rows_i) * lda * int64_t(sizeof(T))),
+        0x00020000);
+    const int rr = lane % TS, hh = lane / TS;  // row (and column) of this lane, half of the tile
+    T *tl = tile[wave];
+    T yrow = T(0);
+    for (int J = J0 + wave; J < J1; J += 4) {
 #pragma unroll
-            for (int q = 0; q < VEC; ++q) {
-                acc0 += a0[q] * b0[q];
-                acc1 += a1[q] * b1[q];
-                acc2 += a2[q] * b2[q];
-                acc3 += a3[q] * b3[q];
+        for (int u = 0; u < TS / 4; ++u) {  // TS rows x 16 chunks, 64 lanes
+            const int idx = lane + 64 * u;
+            const int r = idx >> 4, q = idx & 15;
+            const u32x4_t raw = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, int((int64_t(r) * lda + int64_t(J) * TS) * int64_t(sizeof(T))) + q * 16, 0, 0);
+            *reinterpret_cast<u32x4_t *>(tl + (r * 16 + (q ^ (r & 15))) * EPC) = raw;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const bool diag = (J == i);
+        const T *vj = vJ + (J - J0) * TS;
+        // row part: lane (rr, hh) sums chunks hh*16/H .. of row rr
+#pragma unroll
+        for (int q0 = 0; q0 < 16 / H; ++q0) {
+            const int q = hh * (16 / H) + q0;
+            const vec_t a = *reinterpret_cast<const vec_t *>(tl + (rr * 16 + (q ^ (rr & 15))) * EPC);
+            const vec_t b = *reinterpret_cast<const vec_t *>(vj + q * EPC);
+#pragma unroll
+            for (int x = 0; x < EPC; ++x) {
+                const int k = q * EPC + x;
+                const T av = (diag && k < rr) ? T(0) : a[x];
+                yrow += av * b[x];
             }
         }
-        for (; kv < mv; kv += 64) {
-            const vec_t a0 = row4[kv], b0 = vs4[kv];
-#pragma unroll
-            for (int q = 0; q < VEC; ++q) acc0 += a0[q] * b0[q];
+        // column part: lane (cc = rr, hh) sums rows hh*TS/H .. of column cc
+        T ycol = T(0);
+        const int cq = rr / EPC, cx = rr % EPC;
+#pragma unroll 8
+        for (int r0 = 0; r0 < TS / H; ++r0) {
+            const int r = hh * (TS / H) + r0;
+            const T av = tl[(r * 16 + (cq ^ (r & 15))) * EPC + cx];
+            ycol += ((diag && r >= rr) ? T(0) : av) * vI[r];
         }
-        for (int64_t k = mv * VEC + lane; k < m; k += 64) acc0 += row[k] * vs[k];
-        T acc = (acc0 + acc1) + (acc2 + acc3);
-        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-        const T vr = vs[r - kb];
-        if (lane == 0) {
-            wbuf[r] = acc;
-            Rt[c * n + r] = vr;
-            Vp[r * NB + j] = vr;
+        if (H == 2) ycol += __shfl_xor(ycol, 32);
+        if (diag) {
+            if (hh == 0) yrow += ycol;
+        } else if (hh == 0) {
+            colpart[(int64_t(i) * NT + J) * TS + rr] = ycol;
         }
-        if (lane < j) {
-            qw += Wp[r * NB + lane] * vr;
-            qv += Vp[r * NB + lane] * vr;
-        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
-    __shared__ T qs[NW][2 * NB];
-    if (lane < NB) {
-        qs[wave][lane] = lane < j ? qw : T(0);
-        qs[wave][NB + lane] = lane < j ? qv : T(0);
-    }
+    if (H == 2) yrow += __shfl_xor(yrow, 32);
+    if (hh == 0) rowacc[wave][rr] = yrow;
     __syncthreads();
-    const int t = threadIdx.x;
-    if (t < 2 * NB) {
-        T sum = T(0);
-        for (int w = 0; w < NW; ++w) sum += qs[w][t];
-        qpart[int64_t(blockIdx.x) * 2 * NB + t] = sum;
+    if (t < TS) rowpart[(int64_t(i) * NT + ch) * TS + t] = (rowacc[0][t] + rowacc[1][t]) + (rowacc[2][t] + rowacc[3][t]);
+    if (blockIdx.x == 0)  // the reflector's zeros before the first block row
+        for (int64_t r = t; r < int64_t(T0) * TS; r += 256) Rt[c * n + r] = T(0);
+    if (ch == 0 && t < TS) {  // v into Rt[c] and V[:, j] for block row i
+        const int64_t r = int64_t(i) * TS + t;
+        if (r < n) {
+            Rt[c * n + r] = vI[t];
+            if (r > c) Vp[int64_t(j) * n + r] = vI[t];
+        }
+    }
+    if (blockIdx.x == 0 && t < 2 * NB) {
+        // q = (W^T v, V^T v) over the panel's first j columns from the column kernel's partials of
+        // W^T x, V^T x over rows c+2 .. n-1 (fixed order): v = scale x there and v[c+1] = 1
+        const int q = t % NB;
+        T acc = T(0);
+        for (int b = 0; b < npart; ++b) acc += qcol[int64_t(b) * 2 * NB + t];
+        T qv = T(0);
+        if (q < j) qv = scale * acc + (t < NB ? Wp[int64_t(q) * n + c + 1] : Vp[int64_t(q) * n + c + 1]);
+        qvec[t] = qv;
     }
 }
 
-// w1[r] = tau (w_raw[r] - V[r][:j] q1 - W[r][:j] q2) for r in [c+1, n); partials of w1.v
+// y[r] from the symv partials, then w1[r] = tau (y[r] - V[r][:j] q1 - W[r][:j] q2) for r in
+// [c+1, n); partials of w1.v.  64 rows per block, 4 threads per row summing every fourth
+// partial; the four sums are added in a fixed order.
 template <class T>
 __global__ void __launch_bounds__(256) k_trd_w1(int64_t n, int64_t c, int j, const T *__restrict__ Vp,
-                                                const T *__restrict__ Wp, const T *__restrict__ wbuf,
-                                                const T *__restrict__ qpart, int nqp, const T *__restrict__ tau,
-                                                T *__restrict__ w1buf, T *__restrict__ dpart) {
+                                                const T *__restrict__ Wp, const T *__restrict__ rowpart,
+                                                const T *__restrict__ colpart, const T *__restrict__ qvec, int NT,
+                                                int CHK, const T *__restrict__ tau, T *__restrict__ w1buf,
+                                                T *__restrict__ dpart) {
+    constexpr int TS = SymvTile<T>::TS;
     __shared__ T sh[4];
-    __shared__ T red[4][2 * NB];
     __shared__ T qs[2 * NB];
-    {  // q[v] = sum over the symv blocks, fixed order: 4 strided sums per value, then in order
-        const int v = threadIdx.x % (2 * NB), sidx = threadIdx.x / (2 * NB);
-        T acc = T(0);
-        for (int b = sidx; b < nqp; b += 4) acc += qpart[int64_t(b) * 2 * NB + v];
-        red[sidx][v] = acc;
-        __syncthreads();
-        if (sidx == 0) qs[v] = (red[0][v] + red[1][v]) + (red[2][v] + red[3][v]);
-        __syncthreads();
-    }
-    const T tv = tau[c];
-    const int64_t r = c + 1 + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    T dot = T(0);
+    __shared__ T ys[4][64];
+    const int T0 = int((c + 1) / TS);
+    if (threadIdx.x < 2 * NB) qs[threadIdx.x] = qvec[threadIdx.x];
+    const int rl = threadIdx.x & 63, sub = threadIdx.x >> 6;
+    const int64_t r = c + 1 + int64_t(blockIdx.x) * 64 + rl;
+    T y = T(0);
     if (r < n) {
-        T w = wbuf[r];
-        for (int k = 0; k < j; ++k) w -= Vp[r * NB + k] * qs[k] + Wp[r * NB + k] * qs[NB + k];
-        w *= tv;
+        const int I = int(r / TS), o = int(r % TS);
+        const int nch = int((NT - I + CHK - 1) / CHK);
+        for (int ch = sub; ch < nch; ch += 4) y += rowpart[(int64_t(I) * NT + ch) * TS + o];
+        for (int ib = T0 + sub; ib < I; ib += 4) y += colpart[(int64_t(ib) * NT + I) * TS + o];
+    }
+    ys[sub][rl] = y;
+    __syncthreads();
+    T dot = T(0);
+    if (sub == 0 && r < n) {
+        T w = (ys[0][rl] + ys[1][rl]) + (ys[2][rl] + ys[3][rl]);
+        for (int k = 0; k < j; ++k) w -= Vp[int64_t(k) * n + r] * qs[k] + Wp[int64_t(k) * n + r] * qs[NB + k];
+        w *= tau[c];
         w1buf[r] = w;
-        dot = w * Vp[r * NB + j];
+        dot = w * Vp[int64_t(j) * n + r];
     }
     dot = block_sum(dot, sh);
     if (threadIdx.x == 0) dpart[blockIdx.x] = dot;
@@ -261,22 +376,24 @@ __global__ void __launch_bounds__(256) k_trd_wlast(int64_t n, int64_t c, int j, 
     __shared__ T sh[4];
     const T half = T(0.5) * tau[c] * block_sum_array(dpart, ndp, sh);
     const int64_t r = c + 1 + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (r < n) Wp[r * NB + j] = w1buf[r] - half * Vp[r * NB + j];
+    if (r < n) Wp[int64_t(j) * n + r] = w1buf[r] - half * Vp[int64_t(j) * n + r];
 }
 
-// A[r][s] -= sum_q V[r][q] W[s][q] + W[r][q] V[s][q]   for r, s in [p, n)   (64 x 64 tiles)
+// A[r][s] -= sum_q V[r][q] W[s][q] + W[r][q] V[s][q] for p <= r, s < n on the upper 64 x 64 tiles
+// (tiles below the diagonal exit at once)
 template <class T>
 __global__ void __launch_bounds__(256) k_trailing(T *__restrict__ A, int64_t lda, int64_t n, int64_t p, int jn,
                                                   const T *__restrict__ Vp, const T *__restrict__ Wp) {
+    if (blockIdx.y > blockIdx.x) return;
     __shared__ T vr[64][NB + 1], wr[64][NB + 1], vs_[64][NB + 1], ws_[64][NB + 1];
     const int64_t r0 = p + int64_t(blockIdx.y) * 64, s0 = p + int64_t(blockIdx.x) * 64;
     for (int e = threadIdx.x; e < 64 * NB; e += 256) {
-        const int rr = e / NB, q = e % NB;
+        const int q = e / 64, rr = e % 64;
         const bool okr = r0 + rr < n && q < jn, oks = s0 + rr < n && q < jn;
-        vr[rr][q] = okr ? Vp[(r0 + rr) * NB + q] : T(0);
-        wr[rr][q] = okr ? Wp[(r0 + rr) * NB + q] : T(0);
-        vs_[rr][q] = oks ? Vp[(s0 + rr) * NB + q] : T(0);
-        ws_[rr][q] = oks ? Wp[(s0 + rr) * NB + q] : T(0);
+        vr[rr][q] = okr ? Vp[int64_t(q) * n + r0 + rr] : T(0);
+        wr[rr][q] = okr ? Wp[int64_t(q) * n + r0 + rr] : T(0);
+        vs_[rr][q] = oks ? Vp[int64_t(q) * n + s0 + rr] : T(0);
+        ws_[rr][q] = oks ? Wp[int64_t(q) * n + s0 + rr] : T(0);
     }
     __syncthreads();
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -707,14 +824,15 @@ __global__ void k_set_info(int32_t *info, const int *bad) {
 // ---------------------------------------------------------------------------------------------
 template <class T>
 struct LargeWs {
-    T *A, *Rt, *Vp, *Wp, *tau, *colbuf, *wbuf, *w1buf, *part, *qpart, *dpart;
+    T *A, *Rt, *Vp, *Wp, *tau, *colbuf, *w1buf, *part, *qcol, *qvec, *dpart, *rowpart, *colpart;
     double *d, *e, *e2, *bounds, *lam, *Z, *U0, *U1, *U2, *ML, *Sp, *Tf, *Gp, *G;
     uint8_t *SW;
     int *bad;
     int64_t lda;
 };
 
-static int64_t nsymv_blocks(int64_t) { return SYMV_BLOCKS; }
+template <class T>
+static int64_t symv_tiles(int64_t n) { return (n + SymvTile<T>::TS - 1) / SymvTile<T>::TS; }
 
 template <class C_, class T>
 static void layout(C_ &cv, LargeWs<T> &w, int64_t n, int64_t nv, bool count_only) {
@@ -729,10 +847,13 @@ static void layout(C_ &cv, LargeWs<T> &w, int64_t n, int64_t nv, bool count_only
     w.tau = cv.template carve<T>(size_t(n));
     w.colbuf = cv.template carve<T>(size_t(n));
     w.w1buf = cv.template carve<T>(size_t(n));
-    w.wbuf = cv.template carve<T>(size_t(n));
+    const int64_t nt = symv_tiles<T>(n);
     w.part = cv.template carve<T>(size_t((n + 255) / 256 + 1));
-    w.qpart = cv.template carve<T>(size_t(nsymv_blocks(n)) * 2 * NB);
-    w.dpart = cv.template carve<T>(size_t((n + 255) / 256 + 1));
+    w.qcol = cv.template carve<T>(size_t((n + 255) / 256 + 1) * 2 * NB);
+    w.qvec = cv.template carve<T>(2 * NB);
+    w.dpart = cv.template carve<T>(size_t((n + 63) / 64 + 1));
+    w.rowpart = cv.template carve<T>(size_t(nt) * size_t(nt) * SymvTile<T>::TS);
+    w.colpart = cv.template carve<T>(size_t(nt) * size_t(nt) * SymvTile<T>::TS);
     w.d = cv.template carve<double>(size_t(n));
     w.e = cv.template carve<double>(size_t(n));
     w.e2 = cv.template carve<double>(size_t(n));
@@ -775,9 +896,7 @@ static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *
     hipLaunchKernelGGL(k_fill_zero<int>, dim3(1), dim3(64), 0, s, w.bad, int64_t(1));
     hipLaunchKernelGGL(k_fill_full<T>, dim3(2048), dim3(256), 0, s, C, ldc, n, w.A, lda, w.bad);
     LRC_LAUNCH_CHECK("k_fill_full");
-    const size_t symv_smem = size_t(n) * sizeof(T);
-    LRC_HIP(hipFuncSetAttribute(reinterpret_cast<const void *>(k_trd_symv<T>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                int(symv_smem)));
+    const int NT = int(symv_tiles<T>(n));
     // 1. tridiagonalisation, panels over reflector columns 0 .. n-2 (three launches per column)
     int ndp = 0;  // number of w1.v partials of the previous column
     for (int64_t p0 = 0; p0 < n - 1; p0 += NB) {
@@ -788,15 +907,18 @@ static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *
             const int j = int(c - p0);
             const int nbu = cdiv(n - c, 256);
             hipLaunchKernelGGL(k_trd_col<T>, dim3(nbu), dim3(256), 0, s, w.A, lda, n, c, j, w.Vp, w.Wp, w.w1buf,
-                               w.colbuf, w.part, w.dpart, ndp, w.tau, w.d);
+                               w.colbuf, w.part, w.qcol, w.dpart, ndp, w.tau, w.d);
             const int64_t m = n - c - 1;
-            const int nsb = int(std::min<int64_t>(SYMV_BLOCKS, (m + SYMV_WAVES - 1) / SYMV_WAVES));
-            const int64_t kb = (c + 1) / (16 / int(sizeof(T))) * (16 / int(sizeof(T)));
-            hipLaunchKernelGGL(k_trd_symv<T>, dim3(nsb), dim3(SYMV_WAVES * 64), size_t(n - kb) * sizeof(T), s, w.A, lda,
-                               n, c, j, w.colbuf, w.part, nbu, w.Vp, w.Wp, w.Rt, w.wbuf, w.qpart, w.tau, w.e);
-            ndp = cdiv(m, 256);
-            hipLaunchKernelGGL(k_trd_w1<T>, dim3(ndp), dim3(256), 0, s, n, c, j, w.Vp, w.Wp, w.wbuf, w.qpart, nsb, w.tau,
-                               w.w1buf, w.dpart);
+            // tiles per symv work item: the largest of 8, 4, 2 that still gives >= 512 items
+            const int mt = NT - int((c + 1) / SymvTile<T>::TS);
+            int chk = 8;
+            while (chk > 1 && symv_items(mt, chk) < 512) chk >>= 1;
+            const int nitems = int(symv_items(mt, chk));
+            hipLaunchKernelGGL(k_trd_symv<T>, dim3(nitems), dim3(256), 0, s, w.A, lda, n, c, j, w.colbuf, w.part, nbu,
+                               w.Vp, w.Wp, w.Rt, w.rowpart, w.colpart, w.qcol, w.qvec, w.tau, w.e, NT, chk);
+            ndp = cdiv(m, 64);
+            hipLaunchKernelGGL(k_trd_w1<T>, dim3(ndp), dim3(256), 0, s, n, c, j, w.Vp, w.Wp, w.rowpart, w.colpart,
+                               w.qvec, NT, chk, w.tau, w.w1buf, w.dpart);
         }
         LRC_LAUNCH_CHECK("tridiagonal panel");
         const int jn = int(p1 - p0);
@@ -809,7 +931,7 @@ static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *
             LRC_LAUNCH_CHECK("k_trailing");
         } else {  // last column: finish W[:, jn-1], update it, d[n-1]
             hipLaunchKernelGGL(k_trd_col<T>, dim3(1), dim3(256), 0, s, w.A, lda, n, n - 1, jn, w.Vp, w.Wp, w.w1buf,
-                               w.colbuf, w.part, w.dpart, ndp, w.tau, w.d);
+                               w.colbuf, w.part, w.qcol, w.dpart, ndp, w.tau, w.d);
             LRC_LAUNCH_CHECK("k_trd_col");
         }
     }
