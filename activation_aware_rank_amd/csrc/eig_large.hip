@@ -71,13 +71,13 @@ __device__ __forceinline__ T block_sum(T v, T *sh) {
 // Each column of a panel takes three launches; each global reduction is done by the next launch,
 // redundantly in every block that needs it and always in the same fixed order, so all blocks see
 // bit-identical values (no atomics, no device-wide fences):
-//   k_trd_col : finish W[:, j-1] (reduces the previous column's w1.v partials), update row c (the
-//               column below the diagonal), partials of ||x||^2
-//   k_trd_symv: reflector of column c (reduces the ||x||^2 partials; block 0 stores e[c], tau[c]);
-//               y = A v over the upper tiles of the trailing matrix as fixed-order partials; v
-//               into V[:, j] and Rt[c]; partials of W^T v and V^T v
-//   k_trd_w1  : y from its partials; w1 = tau (y - V q1 - W q2); partials of w1.v
-// W[:, j] = w1 - (tau/2)(w1.v) v is formed by the next k_trd_col (or k_trd_wlast at panel end).
+//   k_trd_symv : reflector of column c (reduces the ||x||^2 partials; block 0 also reduces the
+//                W^T x, V^T x partials into q and stores e[c], tau[c]); y = A v over the upper
+//                tiles of the trailing matrix as fixed-order partials, with scalar partials of
+//                v^T y; v into V[:, j] and Rt[c]
+//   k_trd_w1col: W[:, j] from y, q and v^T y; then row c+1 with the panel's corrections (the
+//                next column), its ||x||^2 and W^T x, V^T x partials
+// The first column of a panel takes k_trd_col0 instead of a previous k_trd_w1col.
 
 // fixed-order sum of p[0..np) by one block: strided per-thread sums, then a tree (every thread)
 template <class T>
@@ -111,68 +111,23 @@ __device__ __forceinline__ T wave_transpose_sum64(T (&p)[64]) {
     return p[0];
 }
 
+// First column c of a panel (no panel corrections yet): x = row c right of the diagonal,
+// d[c], partials of ||x[2:]||^2 over 256-row blocks.
 template <class T>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) k_trd_col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
-                                                 const T *__restrict__ Vp, T *__restrict__ Wp,
-                                                 const T *__restrict__ w1buf, T *__restrict__ colbuf,
-                                                 T *__restrict__ part, T *__restrict__ qcol,
-                                                 const T *__restrict__ dpart, int ndp, const T *__restrict__ tau,
-                                                 double *__restrict__ d) {
+__global__ void __launch_bounds__(256) k_trd_col0(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c,
+                                                  T *__restrict__ colbuf, T *__restrict__ part,
+                                                  double *__restrict__ d) {
     __shared__ T sh[4];
-    __shared__ T vc[NB], wc[NB];
-    __shared__ T qred[4][2 * NB];
-    T half = T(0);
-    if (j > 0) half = T(0.5) * tau[c - 1] * block_sum_array(dpart, ndp, sh);
-    if (threadIdx.x < NB) {
-        const int q = threadIdx.x;
-        vc[q] = q < j ? Vp[q * n + c] : T(0);
-        T wv = q < j ? Wp[q * n + c] : T(0);
-        if (q == j - 1) wv = w1buf[c] - half * Vp[q * n + c];  // row c of the column being finished
-        wc[q] = wv;
-    }
-    __syncthreads();
     const int64_t r = c + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     T ss = T(0);
-    T pq[64];  // W[q][r] x[r] (q < NB) and V[q][r] x[r] for the W^T x, V^T x partials
-#pragma unroll
-    for (int q = 0; q < 64; ++q) pq[q] = T(0);
     if (r < n) {
-        T wrow[NB], vrow[NB];
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            vrow[q] = q < j ? Vp[q * n + r] : T(0);
-            wrow[q] = q < j - 1 ? Wp[q * n + r] : T(0);
-        }
-        if (j > 0) {  // finish W[r][j-1] for this row
-            const T wl = w1buf[r] - half * Vp[(j - 1) * n + r];
-            Wp[(j - 1) * n + r] = wl;
-#pragma unroll
-            for (int q = 0; q < NB; ++q)
-                if (q == j - 1) wrow[q] = wl;
-        }
-        T a = A[c * lda + r];  // = A[r][c] (upper storage)
-#pragma unroll
-        for (int q = 0; q < NB; ++q) a -= vrow[q] * wc[q] + wrow[q] * vc[q];
-        A[c * lda + r] = a;
+        const T a = A[c * lda + r];  // = A[r][c] (upper storage)
         colbuf[r] = a;
-        if (r >= c + 2) {
-            ss = a * a;
-#pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                pq[q] = wrow[q] * a;
-                pq[NB + q] = vrow[q] * a;
-            }
-        }
+        if (r >= c + 2) ss = a * a;
         if (r == c) d[c] = double(a);
     }
     ss = block_sum(ss, sh);
     if (threadIdx.x == 0) part[blockIdx.x] = ss;
-    const T qsum = wave_transpose_sum64(pq);
-    qred[threadIdx.x >> 6][threadIdx.x & 63] = qsum;
-    __syncthreads();
-    if (threadIdx.x < 2 * NB)
-        qcol[int64_t(blockIdx.x) * 2 * NB + threadIdx.x] =
-            (qred[0][threadIdx.x] + qred[1][threadIdx.x]) + (qred[2][threadIdx.x] + qred[3][threadIdx.x]);
 }
 
 // Symmetric product y = A v over the upper tiles of the trailing matrix.  Tiles are TS x TS,
@@ -200,13 +155,13 @@ __host__ __device__ __forceinline__ int64_t symv_items(int64_t m, int64_t ch) {
 }
 
 template <class T>
-__global__ void __launch_bounds__(256) k_trd_symv(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_trd_symv(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
                                                   const T *__restrict__ colbuf, const T *__restrict__ part,
                                                   int npart, T *__restrict__ Vp, const T *__restrict__ Wp,
                                                   T *__restrict__ Rt, T *__restrict__ rowpart,
                                                   T *__restrict__ colpart, const T *__restrict__ qcol,
-                                                  T *__restrict__ qvec, T *__restrict__ tau, double *__restrict__ e,
-                                                  int NT, int CHK) {
+                                                  T *__restrict__ qvec, T *__restrict__ spart, T *__restrict__ tau,
+                                                  double *__restrict__ e, int NT, int CHK) {
     constexpr int TS = SymvTile<T>::TS, EPC = SymvTile<T>::EPC, H = SymvTile<T>::H;
     static_assert(16 * EPC == TS, "tile geometry");
     typedef T vec_t __attribute__((ext_vector_type(EPC)));
@@ -215,25 +170,7 @@ __global__ void __launch_bounds__(256) k_trd_symv(const T *__restrict__ A, int64
     __shared__ __attribute__((aligned(16))) T vJ[8 * TS];
     __shared__ T rowacc[4][TS];
     __shared__ T sh[4];
-    // the reflector of column c: alpha = x[0], sigma2 = ||x[1:]||^2; tau = (beta - alpha)/beta,
-    // v = [1, x[1:] / (alpha - beta)], beta = -sign(alpha) ||x||; tau = 0 when x[1:] = 0
-    const T sigma2 = block_sum_array(part, npart, sh);
-    const T alpha = colbuf[c + 1];
-    T beta, tv, scale;
-    if (sigma2 == T(0)) {
-        tv = T(0);
-        beta = alpha;
-        scale = T(0);
-    } else {
-        const T nrm = sqrt(alpha * alpha + sigma2);
-        beta = alpha >= T(0) ? -nrm : nrm;
-        tv = (beta - alpha) / beta;
-        scale = T(1) / (alpha - beta);
-    }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        e[c] = double(beta);
-        tau[c] = tv;
-    }
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     // work item: L with items(L - 1) <= g < items(L)
     const int64_t g = blockIdx.x;
     const int T0 = int((c + 1) / TS);
@@ -246,36 +183,83 @@ __global__ void __launch_bounds__(256) k_trd_symv(const T *__restrict__ A, int64
     const int i = NT - L;
     const int ch = int(g - symv_items(L - 1, CHK));
     const int J0 = i + ch * CHK, J1 = min(J0 + CHK, NT);
-    auto vval = [&](int64_t x) -> T {
-        return (x <= c || x >= n) ? T(0) : (x == c + 1 ? T(1) : colbuf[x] * scale);
-    };
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    if (t < TS) vI[t] = vval(int64_t(i) * TS + t);
-    for (int x = t; x < (J1 - J0) * TS; x += 256) vJ[x] = vval(int64_t(J0) * TS + x);
-    __syncthreads();
-
     const int rows_i = int(min<int64_t>(TS, n - int64_t(i) * TS));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T *>(A + int64_t(i) * TS * lda), short(0), int(int64_t(rows_i) * lda * int64_t(sizeof(T))),
         0x00020000);
-    const int rr = lane % TS, hh = lane / TS;  // row (and column) of this lane, half of the tile
-    T *tl = tile[wave];
-    T yrow = T(0);
-    for (int J = J0 + wave; J < J1; J += 4) {
+    // Every load that does not depend on the reflector is issued first: this wave's first tile,
+    // the raw column values behind v, the ||x||^2 partials, and (block 0) the W^T x, V^T x partials.
+    u32x4_t pre[TS / 4];
+    auto tile_load = [&](int J) {
 #pragma unroll
         for (int u = 0; u < TS / 4; ++u) {  // TS rows x 16 chunks, 64 lanes
             const int idx = lane + 64 * u;
             const int r = idx >> 4, q = idx & 15;
-            const u32x4_t raw = __builtin_amdgcn_raw_buffer_load_b128(
+            pre[u] = __builtin_amdgcn_raw_buffer_load_b128(
                 rs, int((int64_t(r) * lda + int64_t(J) * TS) * int64_t(sizeof(T))) + q * 16, 0, 0);
-            *reinterpret_cast<u32x4_t *>(tl + (r * 16 + (q ^ (r & 15))) * EPC) = raw;
+        }
+    };
+    const int Jf = J0 + wave;
+    if (Jf < J1) tile_load(Jf);
+    auto xraw = [&](int64_t x) -> T { return (x <= c + 1 || x >= n) ? T(0) : colbuf[x]; };
+    const T xI = t < TS ? xraw(int64_t(i) * TS + t) : T(0);
+    T xJ[8 * TS / 256];
+#pragma unroll
+    for (int u = 0; u < 8 * TS / 256; ++u) {
+        const int x = t + 256 * u;
+        xJ[u] = x < (J1 - J0) * TS ? xraw(int64_t(J0) * TS + x) : T(0);
+    }
+    T sacc = T(0);
+    for (int b2 = t; b2 < npart; b2 += 256) sacc += part[b2];
+    const T alpha = colbuf[c + 1];
+    T qacc = T(0);  // block 0: W^T x, V^T x, value t % 64, every fourth partial from t / 64
+    if (blockIdx.x == 0)
+        for (int b2 = t >> 6; b2 < npart; b2 += 4) qacc += qcol[int64_t(b2) * 2 * NB + (t & 63)];
+    // the reflector of column c: alpha = x[0], sigma2 = ||x[1:]||^2; tau = (beta - alpha)/beta,
+    // v = [1, x[1:] / (alpha - beta)], beta = -sign(alpha) ||x||; tau = 0 when x[1:] = 0
+    const T sigma2 = block_sum(sacc, sh);
+    T beta, tv, scale;
+    if (sigma2 == T(0)) {
+        tv = T(0);
+        beta = alpha;
+        scale = T(0);
+    } else {
+        const T nrm = sqrt(alpha * alpha + sigma2);
+        beta = alpha >= T(0) ? -nrm : nrm;
+        tv = (beta - alpha) / beta;
+        scale = T(1) / (alpha - beta);
+    }
+    if (blockIdx.x == 0 && t == 0) {
+        e[c] = double(beta);
+        tau[c] = tv;
+    }
+    auto vof = [&](int64_t x, T raw) -> T { return x == c + 1 ? T(1) : raw * scale; };
+    if (t < TS) vI[t] = vof(int64_t(i) * TS + t, xI);
+#pragma unroll
+    for (int u = 0; u < 8 * TS / 256; ++u) {
+        const int x = t + 256 * u;
+        if (x < (J1 - J0) * TS) vJ[x] = vof(int64_t(J0) * TS + x, xJ[u]);
+    }
+    __syncthreads();
+
+    const int rr = lane % TS, hh = lane / TS;  // row (and column) of this lane, half of the tile
+    T *tl = tile[wave];
+    T yrow = T(0);
+    T sdot = T(0);  // this lane's share of v^T y from the column parts
+    for (int J = Jf; J < J1; J += 4) {
+        if (J != Jf) tile_load(J);
+#pragma unroll
+        for (int u = 0; u < TS / 4; ++u) {
+            const int idx = lane + 64 * u;
+            const int r = idx >> 4, q = idx & 15;
+            *reinterpret_cast<u32x4_t *>(tl + (r * 16 + (q ^ (r & 15))) * EPC) = pre[u];
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
         const bool diag = (J == i);
         const T *vj = vJ + (J - J0) * TS;
         // row part: lane (rr, hh) sums chunks hh*16/H .. of row rr
-#pragma unroll
+#pragma unroll 4
         for (int q0 = 0; q0 < 16 / H; ++q0) {
             const int q = hh * (16 / H) + q0;
             const vec_t a = *reinterpret_cast<const vec_t *>(tl + (rr * 16 + (q ^ (rr & 15))) * EPC);
@@ -301,6 +285,7 @@ __global__ void __launch_bounds__(256) k_trd_symv(const T *__restrict__ A, int64
             if (hh == 0) yrow += ycol;
         } else if (hh == 0) {
             colpart[(int64_t(i) * NT + J) * TS + rr] = ycol;
+            sdot += ycol * vj[rr];
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -308,7 +293,13 @@ __global__ void __launch_bounds__(256) k_trd_symv(const T *__restrict__ A, int64
     if (H == 2) yrow += __shfl_xor(yrow, 32);
     if (hh == 0) rowacc[wave][rr] = yrow;
     __syncthreads();
-    if (t < TS) rowpart[(int64_t(i) * NT + ch) * TS + t] = (rowacc[0][t] + rowacc[1][t]) + (rowacc[2][t] + rowacc[3][t]);
+    if (t < TS) {
+        const T yr = (rowacc[0][t] + rowacc[1][t]) + (rowacc[2][t] + rowacc[3][t]);
+        rowpart[(int64_t(i) * NT + ch) * TS + t] = yr;
+        sdot += yr * vI[t];
+    }
+    sdot = block_sum(sdot, sh);
+    if (t == 0) spart[g] = sdot;
     if (blockIdx.x == 0)  // the reflector's zeros before the first block row
         for (int64_t r = t; r < int64_t(T0) * TS; r += 256) Rt[c * n + r] = T(0);
     if (ch == 0 && t < TS) {  // v into Rt[c] and V[:, j] for block row i
@@ -318,65 +309,153 @@ __global__ void __launch_bounds__(256) k_trd_symv(const T *__restrict__ A, int64
             if (r > c) Vp[int64_t(j) * n + r] = vI[t];
         }
     }
-    if (blockIdx.x == 0 && t < 2 * NB) {
+    if (blockIdx.x == 0) {
         // q = (W^T v, V^T v) over the panel's first j columns from the column kernel's partials of
         // W^T x, V^T x over rows c+2 .. n-1 (fixed order): v = scale x there and v[c+1] = 1
-        const int q = t % NB;
-        T acc = T(0);
-        for (int b = 0; b < npart; ++b) acc += qcol[int64_t(b) * 2 * NB + t];
-        T qv = T(0);
-        if (q < j) qv = scale * acc + (t < NB ? Wp[int64_t(q) * n + c + 1] : Vp[int64_t(q) * n + c + 1]);
-        qvec[t] = qv;
+        T *qr = &tile[0][0];  // reused: [4][2 NB]
+        __syncthreads();
+        qr[t] = qacc;
+        __syncthreads();
+        if (t < 2 * NB) {
+            const int q = t % NB;
+            const T acc = (qr[t] + qr[64 + t]) + (qr[128 + t] + qr[192 + t]);
+            T qv = T(0);
+            if (q < j) qv = scale * acc + (t < NB ? Wp[int64_t(q) * n + c + 1] : Vp[int64_t(q) * n + c + 1]);
+            qvec[t] = qv;
+        }
     }
 }
 
-// y[r] from the symv partials, then w1[r] = tau (y[r] - V[r][:j] q1 - W[r][:j] q2) for r in
-// [c+1, n); partials of w1.v.  64 rows per block, 4 threads per row summing every fourth
-// partial; the four sums are added in a fixed order.
+// Second launch of column c (rows r in [c+1, n), 64 per block, 4 threads per row reducing the symv
+// partials of y = A v):
+//   w1[r]   = tau (y[r] - V[r][:j] q1 - W[r][:j] q2)       (q1 = W^T v, q2 = V^T v)
+//   W[r][j] = w1[r] - (tau/2)(w1.v) v[r],  w1.v = tau (v^T y - 2 q1.q2)  (v^T y from the symv's
+//             scalar partials, so no further reduction is needed)
+// and, unless the panel ends here, the first launch of column c+1 for the same rows: row c+1 of the
+// current matrix (the column below the diagonal) with the panel's corrections, ||x||^2 partials and
+// the W^T x, V^T x partials.  Each block forms W[c+1][j] itself from a redundant reduction of y[c+1].
 template <class T>
-__global__ void __launch_bounds__(256) k_trd_w1(int64_t n, int64_t c, int j, const T *__restrict__ Vp,
-                                                const T *__restrict__ Wp, const T *__restrict__ rowpart,
-                                                const T *__restrict__ colpart, const T *__restrict__ qvec, int NT,
-                                                int CHK, const T *__restrict__ tau, T *__restrict__ w1buf,
-                                                T *__restrict__ dpart) {
+__device__ __forceinline__ T symv_y(int64_t r, const T *__restrict__ rowpart, const T *__restrict__ colpart, int NT,
+                                    int CHK, int T0, int sub, int nsub) {
     constexpr int TS = SymvTile<T>::TS;
-    __shared__ T sh[4];
+    const int I = int(r / TS), o = int(r % TS);
+    const int nch = int((NT - I + CHK - 1) / CHK);
+    T y = T(0);
+    for (int ch = sub; ch < nch; ch += nsub) y += rowpart[(int64_t(I) * NT + ch) * TS + o];
+    for (int ib = T0 + sub; ib < I; ib += nsub) y += colpart[(int64_t(ib) * NT + I) * TS + o];
+    return y;
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int next, T *__restrict__ Vp,
+            T *__restrict__ Wp, const T *__restrict__ rowpart, const T *__restrict__ colpart,
+            const T *__restrict__ qvec, const T *__restrict__ spart, int nsp, int NT, int CHK,
+            const T *__restrict__ tau, T *__restrict__ colbuf, T *__restrict__ part, T *__restrict__ qcol,
+            double *__restrict__ d) {
+    __shared__ T sh[8];
     __shared__ T qs[2 * NB];
     __shared__ T ys[4][64];
-    const int T0 = int((c + 1) / TS);
-    if (threadIdx.x < 2 * NB) qs[threadIdx.x] = qvec[threadIdx.x];
-    const int rl = threadIdx.x & 63, sub = threadIdx.x >> 6;
+    __shared__ T vc[NB], wc[NB];
+    const int T0 = int((c + 1) / SymvTile<T>::TS);
+    const int t = threadIdx.x;
+    const int rl = t & 63, sub = t >> 6;
     const int64_t r = c + 1 + int64_t(blockIdx.x) * 64 + rl;
-    T y = T(0);
-    if (r < n) {
-        const int I = int(r / TS), o = int(r % TS);
-        const int nch = int((NT - I + CHK - 1) / CHK);
-        for (int ch = sub; ch < nch; ch += 4) y += rowpart[(int64_t(I) * NT + ch) * TS + o];
-        for (int ib = T0 + sub; ib < I; ib += 4) y += colpart[(int64_t(ib) * NT + I) * TS + o];
+    // every independent load first: q, row c+1 of V and W, the v^T y partials, the partials of
+    // y[c+1] and y[r], and (one thread per row) the row's panel values and A[c+1][r]
+    const T qv = t < 2 * NB ? qvec[t] : T(0);
+    T w1row = T(0), v1row = T(0);
+    if (t < NB) {
+        w1row = Wp[int64_t(t) * n + c + 1];
+        v1row = Vp[int64_t(t) * n + c + 1];
     }
-    ys[sub][rl] = y;
+    T sp = T(0);
+    for (int b2 = t; b2 < nsp; b2 += 256) sp += spart[b2];
+    const T ycp = next ? symv_y(c + 1, rowpart, colpart, NT, CHK, T0, t, 256) : T(0);
+    const T yr = r < n ? symv_y(r, rowpart, colpart, NT, CHK, T0, sub, 4) : T(0);
+    T vrow[NB], wrow[NB];
+    T aold = T(0);
+    const bool mine = sub == 0 && r < n;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+        vrow[q] = (mine && q <= j) ? Vp[int64_t(q) * n + r] : T(0);
+        wrow[q] = (mine && q < j) ? Wp[int64_t(q) * n + r] : T(0);
+    }
+    if (mine && next) aold = A[(c + 1) * lda + r];
+    const T tv = tau[c];
+    if (t < 2 * NB) qs[t] = qv;
+    ys[sub][rl] = yr;
+    // v^T y and y[c+1] in one block reduction
+    T vty = sp, yc = ycp;
+    for (int o = 32; o > 0; o >>= 1) {
+        vty += __shfl_xor(vty, o);
+        yc += __shfl_xor(yc, o);
+    }
     __syncthreads();
-    T dot = T(0);
-    if (sub == 0 && r < n) {
-        T w = (ys[0][rl] + ys[1][rl]) + (ys[2][rl] + ys[3][rl]);
-        for (int k = 0; k < j; ++k) w -= Vp[int64_t(k) * n + r] * qs[k] + Wp[int64_t(k) * n + r] * qs[NB + k];
-        w *= tau[c];
-        w1buf[r] = w;
-        dot = w * Vp[int64_t(j) * n + r];
+    if (rl == 0) {
+        sh[sub] = vty;
+        sh[4 + sub] = yc;
     }
-    dot = block_sum(dot, sh);
-    if (threadIdx.x == 0) dpart[blockIdx.x] = dot;
-}
-
-// W[r][j] = w1[r] - (tau/2)(w1.v) v[r] for the panel's last column (rows r > c)
-template <class T>
-__global__ void __launch_bounds__(256) k_trd_wlast(int64_t n, int64_t c, int j, const T *__restrict__ Vp,
-                                                   T *__restrict__ Wp, const T *__restrict__ w1buf,
-                                                   const T *__restrict__ dpart, int ndp, const T *__restrict__ tau) {
-    __shared__ T sh[4];
-    const T half = T(0.5) * tau[c] * block_sum_array(dpart, ndp, sh);
-    const int64_t r = c + 1 + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (r < n) Wp[int64_t(j) * n + r] = w1buf[r] - half * Vp[int64_t(j) * n + r];
+    __syncthreads();
+    vty = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+    yc = (sh[4] + sh[5]) + (sh[6] + sh[7]);
+    T q12 = T(0);
+    for (int k = 0; k < j; ++k) q12 += qs[k] * qs[NB + k];
+    const T half = T(0.5) * tv * (tv * (vty - T(2) * q12));
+    if (next && t < NB) {  // row c+1 of the panel, with W[c+1][j] from y[c+1]
+        const int q = t;
+        T wv = q < j ? w1row : T(0);
+        if (q == j) {
+            T w = yc;
+            for (int k = 0; k < j; ++k)
+                w -= Vp[int64_t(k) * n + c + 1] * qs[k] + Wp[int64_t(k) * n + c + 1] * qs[NB + k];
+            wv = tv * w - half * v1row;
+        }
+        wc[q] = wv;
+        vc[q] = q <= j ? v1row : T(0);
+    }
+    __syncthreads();
+    T ss = T(0);
+    T pq[64];
+#pragma unroll
+    for (int q = 0; q < 64; ++q) pq[q] = T(0);
+    if (mine) {
+        T w = (ys[0][rl] + ys[1][rl]) + (ys[2][rl] + ys[3][rl]);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) w -= vrow[q] * qs[q] + wrow[q] * qs[NB + q];
+        T vj = T(0);
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+            if (q == j) vj = vrow[q];
+        const T wj = tv * w - half * vj;
+        Wp[int64_t(j) * n + r] = wj;
+        if (next) {  // row c+1 of the current matrix, corrected by the panel's first j+1 columns
+#pragma unroll
+            for (int q = 0; q < NB; ++q)
+                if (q == j) wrow[q] = wj;
+            T a = aold;
+#pragma unroll
+            for (int q = 0; q < NB; ++q) a -= vrow[q] * wc[q] + wrow[q] * vc[q];
+            A[(c + 1) * lda + r] = a;
+            colbuf[r] = a;
+            if (r == c + 1) d[c + 1] = double(a);
+            if (r >= c + 3) {
+                ss = a * a;
+#pragma unroll
+                for (int q = 0; q < NB; ++q) {
+                    pq[q] = wrow[q] * a;
+                    pq[NB + q] = vrow[q] * a;
+                }
+            }
+        }
+    }
+    if (!next) return;
+    ss = block_sum(ss, sh);
+    if (t == 0) part[blockIdx.x] = ss;
+    if (sub == 0) {
+        const T qsum = wave_transpose_sum64(pq);
+        qcol[int64_t(blockIdx.x) * 2 * NB + rl] = qsum;
+    }
 }
 
 // A[r][s] -= sum_q V[r][q] W[s][q] + W[r][q] V[s][q] for p <= r, s < n on the upper 64 x 64 tiles
@@ -824,7 +903,7 @@ __global__ void k_set_info(int32_t *info, const int *bad) {
 // ---------------------------------------------------------------------------------------------
 template <class T>
 struct LargeWs {
-    T *A, *Rt, *Vp, *Wp, *tau, *colbuf, *w1buf, *part, *qcol, *qvec, *dpart, *rowpart, *colpart;
+    T *A, *Rt, *Vp, *Wp, *tau, *colbuf, *part, *qcol, *qvec, *spart, *rowpart, *colpart;
     double *d, *e, *e2, *bounds, *lam, *Z, *U0, *U1, *U2, *ML, *Sp, *Tf, *Gp, *G;
     uint8_t *SW;
     int *bad;
@@ -846,12 +925,11 @@ static void layout(C_ &cv, LargeWs<T> &w, int64_t n, int64_t nv, bool count_only
     w.Wp = cv.template carve<T>(size_t(n) * NB);
     w.tau = cv.template carve<T>(size_t(n));
     w.colbuf = cv.template carve<T>(size_t(n));
-    w.w1buf = cv.template carve<T>(size_t(n));
     const int64_t nt = symv_tiles<T>(n);
-    w.part = cv.template carve<T>(size_t((n + 255) / 256 + 1));
-    w.qcol = cv.template carve<T>(size_t((n + 255) / 256 + 1) * 2 * NB);
+    w.part = cv.template carve<T>(size_t((n + 63) / 64 + 1));
+    w.qcol = cv.template carve<T>(size_t((n + 63) / 64 + 1) * 2 * NB);
     w.qvec = cv.template carve<T>(2 * NB);
-    w.dpart = cv.template carve<T>(size_t((n + 63) / 64 + 1));
+    w.spart = cv.template carve<T>(size_t(symv_items(nt, 1)));
     w.rowpart = cv.template carve<T>(size_t(nt) * size_t(nt) * SymvTile<T>::TS);
     w.colpart = cv.template carve<T>(size_t(nt) * size_t(nt) * SymvTile<T>::TS);
     w.d = cv.template carve<double>(size_t(n));
@@ -897,42 +975,39 @@ static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *
     hipLaunchKernelGGL(k_fill_full<T>, dim3(2048), dim3(256), 0, s, C, ldc, n, w.A, lda, w.bad);
     LRC_LAUNCH_CHECK("k_fill_full");
     const int NT = int(symv_tiles<T>(n));
-    // 1. tridiagonalisation, panels over reflector columns 0 .. n-2 (three launches per column)
-    int ndp = 0;  // number of w1.v partials of the previous column
+    // 1. tridiagonalisation, panels over reflector columns 0 .. n-2 (two launches per column)
     for (int64_t p0 = 0; p0 < n - 1; p0 += NB) {
         const int64_t p1 = std::min<int64_t>(p0 + NB, n - 1);
         hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w.Vp, int64_t(n) * NB);
         hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w.Wp, int64_t(n) * NB);
+        int npart = cdiv(n - p0, 256);
+        hipLaunchKernelGGL(k_trd_col0<T>, dim3(npart), dim3(256), 0, s, w.A, lda, n, p0, w.colbuf, w.part, w.d);
         for (int64_t c = p0; c < p1; ++c) {
             const int j = int(c - p0);
-            const int nbu = cdiv(n - c, 256);
-            hipLaunchKernelGGL(k_trd_col<T>, dim3(nbu), dim3(256), 0, s, w.A, lda, n, c, j, w.Vp, w.Wp, w.w1buf,
-                               w.colbuf, w.part, w.qcol, w.dpart, ndp, w.tau, w.d);
-            const int64_t m = n - c - 1;
             // tiles per symv work item: the largest of 8, 4, 2 that still gives >= 512 items
             const int mt = NT - int((c + 1) / SymvTile<T>::TS);
             int chk = 8;
             while (chk > 1 && symv_items(mt, chk) < 512) chk >>= 1;
             const int nitems = int(symv_items(mt, chk));
-            hipLaunchKernelGGL(k_trd_symv<T>, dim3(nitems), dim3(256), 0, s, w.A, lda, n, c, j, w.colbuf, w.part, nbu,
-                               w.Vp, w.Wp, w.Rt, w.rowpart, w.colpart, w.qcol, w.qvec, w.tau, w.e, NT, chk);
-            ndp = cdiv(m, 64);
-            hipLaunchKernelGGL(k_trd_w1<T>, dim3(ndp), dim3(256), 0, s, n, c, j, w.Vp, w.Wp, w.rowpart, w.colpart,
-                               w.qvec, NT, chk, w.tau, w.w1buf, w.dpart);
+            hipLaunchKernelGGL(k_trd_symv<T>, dim3(nitems), dim3(256), 0, s, w.A, lda, n, c, j, w.colbuf, w.part,
+                               npart, w.Vp, w.Wp, w.Rt, w.rowpart, w.colpart, w.qcol, w.qvec, w.spart, w.tau, w.e,
+                               NT, chk);
+            // the next column is handled here unless a trailing update comes first (the last
+            // column n-1 has no reflector, only d[n-1])
+            const int next = (c + 1 < p1 || p1 == n - 1) ? 1 : 0;
+            const int nw = cdiv(n - c - 1, 64);
+            hipLaunchKernelGGL(k_trd_w1col<T>, dim3(nw), dim3(256), 0, s, w.A, lda, n, c, j, next, w.Vp, w.Wp,
+                               w.rowpart, w.colpart, w.qvec, w.spart, nitems, NT, chk, w.tau, w.colbuf, w.part,
+                               w.qcol, w.d);
+            npart = nw;
         }
         LRC_LAUNCH_CHECK("tridiagonal panel");
         const int jn = int(p1 - p0);
         if (p1 < n - 1) {
-            hipLaunchKernelGGL(k_trd_wlast<T>, dim3(cdiv(n - p1, 256)), dim3(256), 0, s, n, p1 - 1, jn - 1, w.Vp, w.Wp,
-                               w.w1buf, w.dpart, ndp, w.tau);
             const int64_t m = n - p1;
             dim3 g(cdiv(m, 64), cdiv(m, 64));
             hipLaunchKernelGGL(k_trailing<T>, g, dim3(256), 0, s, w.A, lda, n, p1, jn, w.Vp, w.Wp);
             LRC_LAUNCH_CHECK("k_trailing");
-        } else {  // last column: finish W[:, jn-1], update it, d[n-1]
-            hipLaunchKernelGGL(k_trd_col<T>, dim3(1), dim3(256), 0, s, w.A, lda, n, n - 1, jn, w.Vp, w.Wp, w.w1buf,
-                               w.colbuf, w.part, w.qcol, w.dpart, ndp, w.tau, w.d);
-            LRC_LAUNCH_CHECK("k_trd_col");
         }
     }
     // 2. eigenvalues
