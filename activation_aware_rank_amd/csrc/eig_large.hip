@@ -510,7 +510,23 @@ __device__ __forceinline__ int sturm_count(const double *__restrict__ d, const d
     double q = d[0] - x;
     if (fabs(q) < pivmin) q = -pivmin;
     if (q < 0.0) ++cnt;
-    for (int64_t i = 1; i < n; ++i) {
+    int64_t i = 1;
+    // 8 steps at a time with their loads issued first (they do not depend on the recurrence)
+    for (; i + 8 <= n; i += 8) {
+        double dd[8], ee[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            dd[u] = d[i + u];
+            ee[u] = e2[i + u - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            q = dd[u] - x - ee[u] / q;
+            if (fabs(q) < pivmin) q = -pivmin;
+            if (q < 0.0) ++cnt;
+        }
+    }
+    for (; i < n; ++i) {
         q = d[i] - x - e2[i - 1] / q;
         if (fabs(q) < pivmin) q = -pivmin;
         if (q < 0.0) ++cnt;
@@ -563,9 +579,11 @@ __global__ void __launch_bounds__(256) k_bisect(const double *__restrict__ d, co
     if (i >= n) return;  // whole groups leave together (n * MSEC threads rounded to blocks)
     double lo = bounds[0], hi = bounds[1];
     const double pivmin = bounds[2];
-    const double atol = DBL_EPSILON * bounds[3];  // absolute accuracy eps ||T||
+    // stop at a width of 1e-13 relative plus 1e-13 ||T|| absolute: about 11 passes from the
+    // Gershgorin interval, far below the working precision of the matrix the eigenvalues come from
+    const double atol = 1e-13 * bounds[3];
     for (int it = 0; it < 24; ++it) {
-        if (hi - lo <= 2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi)) + atol) break;
+        if (hi - lo <= 1e-13 * fmax(fabs(lo), fabs(hi)) + atol) break;
         const double x = sub < MSEC - 1 ? lo + (hi - lo) * double(sub + 1) / double(MSEC) : hi;
         const bool at_or_below = sub < MSEC - 1 && x > lo && x < hi && sturm_count(d, e2, n, x, pivmin) <= i;
         const bool above = sub < MSEC - 1 && x > lo && x < hi && !at_or_below;
@@ -643,11 +661,35 @@ __global__ void __launch_bounds__(64) k_invit(const double *__restrict__ d, cons
     if (u0 == 0.0) u0 = tiny;
     U0[(n - 1) * nv + j] = 1.0 / u0;
     Z[(n - 1) * nv + j] = bcur;
+    // three steps of inverse iteration; each back substitution's result is scaled by 1/max when
+    // it is read by the next sweep (the elimination of the next step, or the final normalisation)
+    double scl = 1.0;
     for (int iter = 0; iter < 3; ++iter) {
         if (iter > 0) {  // apply the stored elimination to the new right-hand side
-            double bc = Z[j];
-            for (int64_t k = 0; k < n - 1; ++k) {
-                const double bn = Z[(k + 1) * nv + j], mlt = ML[k * nv + j];
+            double bc = Z[j] * scl;
+            int64_t k = 0;
+            for (; k + 8 <= n - 1; k += 8) {
+                double bn[8], ml[8];
+                uint8_t sw[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    bn[u] = Z[(k + u + 1) * nv + j] * scl;
+                    ml[u] = ML[(k + u) * nv + j];
+                    sw[u] = SW[(k + u) * nv + j];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (sw[u]) {
+                        Z[(k + u) * nv + j] = bn[u];
+                        bc = bc - ml[u] * bn[u];
+                    } else {
+                        Z[(k + u) * nv + j] = bc;
+                        bc = bn[u] - ml[u] * bc;
+                    }
+                }
+            }
+            for (; k < n - 1; ++k) {
+                const double bn = Z[(k + 1) * nv + j] * scl, mlt = ML[k * nv + j];
                 if (SW[k * nv + j]) {
                     Z[k * nv + j] = bn;
                     bc = bc - mlt * bn;
@@ -658,22 +700,44 @@ __global__ void __launch_bounds__(64) k_invit(const double *__restrict__ d, cons
             }
             Z[(n - 1) * nv + j] = bc;
         }
-        // back substitution with U, then scale by the largest entry
+        // back substitution with U; the largest entry sets the next scale
         double y2 = 0.0, y1 = Z[(n - 1) * nv + j] * U0[(n - 1) * nv + j], ymax = fabs(y1);
         Z[(n - 1) * nv + j] = y1;
-        for (int64_t k = n - 2; k >= 0; --k) {
+        int64_t k = n - 2;
+        for (; k - 7 >= 0; k -= 8) {
+            double zz[8], a0[8], a1[8], a2[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t kk = k - u;
+                zz[u] = Z[kk * nv + j];
+                a0[u] = U0[kk * nv + j];
+                a1[u] = U1[kk * nv + j];
+                a2[u] = U2[kk * nv + j];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const double y = (zz[u] - a1[u] * y1 - a2[u] * y2) * a0[u];
+                Z[(k - u) * nv + j] = y;
+                ymax = fmax(ymax, fabs(y));
+                y2 = y1;
+                y1 = y;
+            }
+        }
+        for (; k >= 0; --k) {
             const double y = (Z[k * nv + j] - U1[k * nv + j] * y1 - U2[k * nv + j] * y2) * U0[k * nv + j];
             Z[k * nv + j] = y;
             ymax = fmax(ymax, fabs(y));
             y2 = y1;
             y1 = y;
         }
-        const double inv = ymax > 0.0 ? 1.0 / ymax : 1.0;
-        for (int64_t r = 0; r < n; ++r) Z[r * nv + j] *= inv;
+        scl = ymax > 0.0 ? 1.0 / ymax : 1.0;
     }
     double s2 = 0.0;
-    for (int64_t r = 0; r < n; ++r) s2 += Z[r * nv + j] * Z[r * nv + j];
-    const double inv = s2 > 0.0 ? 1.0 / sqrt(s2) : 0.0;
+    for (int64_t r = 0; r < n; ++r) {
+        const double z = Z[r * nv + j] * scl;
+        s2 += z * z;
+    }
+    const double inv = s2 > 0.0 ? scl / sqrt(s2) : 0.0;
     for (int64_t r = 0; r < n; ++r) Z[r * nv + j] *= inv;
 }
 
