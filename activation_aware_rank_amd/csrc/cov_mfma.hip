@@ -30,7 +30,7 @@ namespace lrc {
 constexpr int MK = 32;                   // k step, bf16 elements (4 chunks of 16 bytes)
 constexpr int64_t MFMA_CHUNK = 32768;    // tokens per internal chunk
 #ifndef SYRK_FE
-#define SYRK_FE 2
+#define SYRK_FE 4  // 16-token k slices per flush of the SYRK's MFMA chains
 #endif
 #ifndef SYRK_WPE
 #define SYRK_WPE 1  // SYRK waves per SIMD (resident blocks per CU)
@@ -111,7 +111,7 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
     };
 
     if (nk <= 0) return;
-    // FLUSH: p holds the MFMA chain of the last FE 16-wide k slices (FE = 1 or 2)
+    // FLUSH: p holds the MFMA chain of the last FE 16-wide k slices (FE = 1, 2 or 4)
     f32x16_t p[TM][TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -137,7 +137,9 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
     constexpr int NA = (NPROD == 4) ? 2 : 1;
     // one k step from LDS buffer cur; loads of step kt + DEPTH go to register set lset, and step
     // kt + 1 is stored from register set sset
-    auto step = [&](int kt, int cur, auto lset, auto sset) {
+    // par: the step's position in the unrolled pair (static); with FE 4 a flush group is the pair
+    auto step = [&](int kt, int cur, auto lset, auto sset, auto par) {
+        constexpr int PAR = decltype(par)::value;
         if (kt + DEPTH < nk) gload(kt + DEPTH, lset);
         const bf16_t *sb = lds + cur * NOPS * OPSZ;
 #pragma unroll
@@ -159,7 +161,7 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
                     // a flush group's first slice starts the chain from a literal zero
-                    const bool fresh = FLUSH && (FE == 1 || (FE == 2 && ks == 0));
+                    const bool fresh = FLUSH && (FE == 1 || (FE == 2 && ks == 0) || (FE == 4 && PAR == 0 && ks == 0));
                     f32x16_t q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         af[0][tm], bfr[0][tn], fresh ? f32x16_t{} : (FLUSH ? p[tm][tn] : acc[tm][tn]), 0, 0, 0);
                     if (NPROD == 4) {
@@ -174,17 +176,19 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
                 }
             if (FLUSH && FE == 1) flush();
         }
-        if (FLUSH && FE == 2) flush();
+        if (FLUSH && (FE == 2 || (FE == 4 && PAR == 1))) flush();
         if (kt + 1 < nk) sstore(cur ^ 1, sset);
         __syncthreads();
     };
+    static_assert(FE != 4 || DEPTH == 2, "a 64-token flush group needs the unrolled pair");
     if constexpr (DEPTH == 1) {
-        for (int kt = 0; kt < nk; ++kt) step(kt, kt & 1, I0{}, I0{});
+        for (int kt = 0; kt < nk; ++kt) step(kt, kt & 1, I0{}, I0{}, I0{});
     } else {
         for (int kt = 0; kt < nk; kt += 2) {
-            step(kt, 0, I0{}, I1{});
-            if (kt + 1 < nk) step(kt + 1, 1, I1{}, I0{});
+            step(kt, 0, I0{}, I1{}, I0{});
+            if (kt + 1 < nk) step(kt + 1, 1, I1{}, I0{}, I1{});
         }
+        if (FLUSH && FE == 4 && (nk & 1)) flush();  // the last group had only its first step
     }
 }
 

@@ -189,18 +189,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         0x00020000);
     // Every load that does not depend on the reflector is issued first: this wave's first tile,
     // the raw column values behind v, the ||x||^2 partials, and (block 0) the W^T x, V^T x partials.
-    u32x4_t pre[TS / 4];
-    auto tile_load = [&](int J) {
+    // A work item has at most 8 tiles, so a wave has at most two (J0 + wave and J0 + wave + 4):
+    // both are loaded here, into two register sets.
+    u32x4_t pre[2][TS / 4];
+    auto tile_load = [&](int J, u32x4_t (&dst)[TS / 4]) {
 #pragma unroll
         for (int u = 0; u < TS / 4; ++u) {  // TS rows x 16 chunks, 64 lanes
             const int idx = lane + 64 * u;
             const int r = idx >> 4, q = idx & 15;
-            pre[u] = __builtin_amdgcn_raw_buffer_load_b128(
+            dst[u] = __builtin_amdgcn_raw_buffer_load_b128(
                 rs, int((int64_t(r) * lda + int64_t(J) * TS) * int64_t(sizeof(T))) + q * 16, 0, 0);
         }
     };
     const int Jf = J0 + wave;
-    if (Jf < J1) tile_load(Jf);
+    if (Jf < J1) tile_load(Jf, pre[0]);
+    if (Jf + 4 < J1) tile_load(Jf + 4, pre[1]);
     auto xraw = [&](int64_t x) -> T { return (x <= c + 1 || x >= n) ? T(0) : colbuf[x]; };
     const T xI = t < TS ? xraw(int64_t(i) * TS + t) : T(0);
     T xJ[8 * TS / 256];
@@ -246,13 +249,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     T *tl = tile[wave];
     T yrow = T(0);
     T sdot = T(0);  // this lane's share of v^T y from the column parts
-    for (int J = Jf; J < J1; J += 4) {
-        if (J != Jf) tile_load(J);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int J = Jf + 4 * tt;
+        if (J >= J1) break;
 #pragma unroll
         for (int u = 0; u < TS / 4; ++u) {
             const int idx = lane + 64 * u;
             const int r = idx >> 4, q = idx & 15;
-            *reinterpret_cast<u32x4_t *>(tl + (r * 16 + (q ^ (r & 15))) * EPC) = pre[u];
+            *reinterpret_cast<u32x4_t *>(tl + (r * 16 + (q ^ (r & 15))) * EPC) = pre[tt][u];
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
