@@ -3,6 +3,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <unordered_map>
 #include <string>
 #include <vector>
 
@@ -36,30 +37,39 @@ struct TimingRec {
 };
 static std::mutex g_tmu;
 static bool g_timing = false;
+static int g_stride = 1;                                    // record every g_stride-th launch
+static std::unordered_map<std::string, int64_t> g_counts;  // launches seen per kernel
+static std::unordered_map<std::string, int> g_kstride;     // per-kernel strides (override g_stride)
 static std::vector<TimingRec> g_recs;
+static std::vector<hipEvent_t> g_free;  // events of discarded records, reused (creation is slow)
 
-int timing_begin(const char *kernel, hipStream_t s) {
-    std::lock_guard<std::mutex> lk(g_tmu);
-    if (!g_timing) return -1;
-    TimingRec r;
-    r.kernel = kernel;
-    r.flops = 0.0;
-    if (hipEventCreate(&r.start) != hipSuccess) return -1;
-    if (hipEventCreate(&r.stop) != hipSuccess) {
-        (void)hipEventDestroy(r.start);
-        return -1;
+static bool take_event(hipEvent_t *e) {
+    if (!g_free.empty()) {
+        *e = g_free.back();
+        g_free.pop_back();
+        return true;
     }
-    (void)hipEventRecord(r.start, s);
-    g_recs.push_back(r);
-    return int(g_recs.size()) - 1;
+    return hipEventCreate(e) == hipSuccess;
 }
 
-void timing_end(int token, hipStream_t s, double flops) {
-    if (token < 0) return;
+bool timing_sample(const char *kernel, double work, hipEvent_t *start, hipEvent_t *stop) {
     std::lock_guard<std::mutex> lk(g_tmu);
-    if (token >= int(g_recs.size())) return;
-    (void)hipEventRecord(g_recs[token].stop, s);
-    g_recs[token].flops = flops;
+    if (!g_timing) return false;
+    const auto ks = g_kstride.find(kernel);
+    const int stride = ks == g_kstride.end() ? g_stride : ks->second;
+    if (g_counts[kernel]++ % stride != 0) return false;
+    TimingRec r;
+    r.kernel = kernel;
+    r.flops = work;
+    if (!take_event(&r.start)) return false;
+    if (!take_event(&r.stop)) {
+        g_free.push_back(r.start);
+        return false;
+    }
+    g_recs.push_back(r);
+    *start = r.start;
+    *stop = r.stop;
+    return true;
 }
 
 }  // namespace lrc
@@ -89,14 +99,24 @@ const char *lrc_status_string(lrc_status s) {
 
 const char *lrc_last_error(void) { return g_last_error.c_str(); }
 
-lrc_status lrc_timing_enable(int enable) {
+lrc_status lrc_timing_enable(int stride) {
+    REQUIRE(stride >= 0, LRC_ERR_ARG, "stride must be >= 0");
     std::lock_guard<std::mutex> lk(g_tmu);
-    g_timing = enable != 0;
+    g_timing = stride != 0;
+    if (stride > 0) g_stride = stride;
+    g_counts.clear();
     return LRC_OK;
 }
 
-lrc_status lrc_timing_read(const char *kernel, int64_t *launches, double *total_ms, double *total_flops, int reset) {
-    REQUIRE(kernel && launches && total_ms && total_flops, LRC_ERR_ARG, "null argument");
+lrc_status lrc_timing_set_stride(const char *kernel, int stride) {
+    REQUIRE(kernel && stride >= 1, LRC_ERR_ARG, "kernel must be non-NULL and stride >= 1");
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_kstride[kernel] = stride;
+    return LRC_OK;
+}
+
+lrc_status lrc_timing_read(const char *kernel, int64_t *launches, double *total_ms, double *total_work, int reset) {
+    REQUIRE(kernel && launches && total_ms && total_work, LRC_ERR_ARG, "null argument");
     std::lock_guard<std::mutex> lk(g_tmu);
     int64_t n = 0;
     double ms = 0.0, fl = 0.0;
@@ -113,12 +133,12 @@ lrc_status lrc_timing_read(const char *kernel, int64_t *launches, double *total_
     }
     *launches = n;
     *total_ms = ms;
-    *total_flops = fl;
+    *total_work = fl;
     if (reset) {
         for (auto &r : g_recs) {
             (void)hipEventSynchronize(r.stop);
-            (void)hipEventDestroy(r.start);
-            (void)hipEventDestroy(r.stop);
+            g_free.push_back(r.start);
+            g_free.push_back(r.stop);
         }
         g_recs.clear();
     }

@@ -193,9 +193,7 @@ lrc_status launch_gemm(const GemmArgs &g, hipStream_t s) {
     double flops = 2.0 * double(g.M) * double(g.N) * double(g.K);
     if (g.tiles != 0) flops = double(g.M) * double(g.M + 1) * double(g.K);
     if (MA != 0 || MB != 0) flops = double(g.M) * double(g.N) * double(g.K + 1);
-    const int tok = timing_begin("k_dgemm", s);
-    hipLaunchKernelGGL((k_dgemm<TA, TB, MA, MB, OUTF>), dim3(gx, gy), dim3(256), 0, s, g);
-    timing_end(tok, s, flops);
+    LRC_TIMED_LAUNCH("k_dgemm", flops, (k_dgemm<TA, TB, MA, MB, OUTF>), dim3(gx, gy), dim3(256), 0, s, g);
     LRC_LAUNCH_CHECK("k_dgemm");
     return LRC_OK;
 }

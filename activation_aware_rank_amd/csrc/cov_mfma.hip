@@ -453,15 +453,14 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         const int64_t ktot = (tc + MK - 1) / MK * MK;
         if (has_w) {
             dim3 g(cdiv(a.d_out, 256), cdiv(ktot, 256));
-            const int tk = timing_begin("k_cov_gemm_y", s);
+            const double fl = 2.0 * double(tc) * double(a.d_in) * double(a.d_out);
             // d_in a multiple of the k step: no partial last step, no k check in the loads
             if (a.d_in % MK == 0)
-                hipLaunchKernelGGL((k_cov_gemm_y<G_BM, false>), g, dim3(G_THREADS), 0, s, Wt, a.d_in, a.d_out,
-                                   X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo, p.ldy);
+                LRC_TIMED_LAUNCH("k_cov_gemm_y", fl, (k_cov_gemm_y<G_BM, false>), g, dim3(G_THREADS), 0, s, Wt,
+                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo, p.ldy);
             else
-                hipLaunchKernelGGL((k_cov_gemm_y<G_BM, true>), g, dim3(G_THREADS), 0, s, Wt, a.d_in, a.d_out,
-                                   X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo, p.ldy);
-            timing_end(tk, s, 2.0 * double(tc) * double(a.d_in) * double(a.d_out));
+                LRC_TIMED_LAUNCH("k_cov_gemm_y", fl, (k_cov_gemm_y<G_BM, true>), g, dim3(G_THREADS), 0, s, Wt,
+                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo, p.ldy);
             LRC_LAUNCH_CHECK("k_cov_gemm_y");
         } else {
             dim3 g(cdiv(a.d_out, 64), cdiv(ktot, 64));
@@ -470,15 +469,14 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         }
         const int64_t kchunk = ((ktot + p.nsplit - 1) / p.nsplit + MK - 1) / MK * MK;
         dim3 g(unsigned(p.n_upper), unsigned(a.n_blocks), unsigned(p.nsplit));
-        const int tk = timing_begin("k_cov_syrk", s);
-        if (has_w)
-            hipLaunchKernelGGL((k_cov_syrk<128, 4>), g, dim3(SyrkCfg<128>::THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk,
-                               hd, a.C, a.ldc, P, a.n_blocks);
-        else
-            hipLaunchKernelGGL((k_cov_syrk<128, 1>), g, dim3(SyrkCfg<128>::THREADS), 0, s, Yhi, Ylo, p.ldy, ktot, kchunk,
-                               hd, a.C, a.ldc, P, a.n_blocks);
         // algorithmic flops of the launch: the upper triangle (incl. diagonal) of each head block
-        timing_end(tk, s, double(tc) * double(hd) * double(hd + 1) * double(a.n_blocks));
+        const double fl = double(tc) * double(hd) * double(hd + 1) * double(a.n_blocks);
+        if (has_w)
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 4>), g, dim3(SyrkCfg<128>::THREADS), 0, s, Yhi, Ylo,
+                             p.ldy, ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+        else
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 1>), g, dim3(SyrkCfg<128>::THREADS), 0, s, Yhi, Ylo,
+                             p.ldy, ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         LRC_LAUNCH_CHECK("k_cov_syrk");
     }
     if (p.nsplit > 1) {

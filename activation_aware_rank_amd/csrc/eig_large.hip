@@ -1058,9 +1058,11 @@ static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *
             int chk = 8;
             while (chk > 1 && symv_items(mt, chk) < 512) chk >>= 1;
             const int nitems = int(symv_items(mt, chk));
-            hipLaunchKernelGGL(k_trd_symv<T>, dim3(nitems), dim3(256), 0, s, w.A, lda, n, c, j, w.colbuf, w.part,
-                               npart, w.Vp, w.Wp, w.Rt, w.rowpart, w.colpart, w.qcol, w.qvec, w.spart, w.tau, w.e,
-                               NT, chk);
+            // algorithmic bytes: the upper triangle of the trailing matrix, read once
+            const double m1 = double(n - c - 1);
+            LRC_TIMED_LAUNCH("k_trd_symv", m1 * (m1 + 1.0) * 0.5 * double(sizeof(T)), k_trd_symv<T>, dim3(nitems),
+                             dim3(256), 0, s, w.A, lda, n, c, j, w.colbuf, w.part, npart, w.Vp, w.Wp, w.Rt, w.rowpart,
+                             w.colpart, w.qcol, w.qvec, w.spart, w.tau, w.e, NT, chk);
             // the next column is handled here unless a trailing update comes first (the last
             // column n-1 has no reflector, only d[n-1])
             const int next = (c + 1 < p1 || p1 == n - 1) ? 1 : 0;

@@ -1,6 +1,7 @@
 // Internal declarations of liblrc (not installed, not part of the C ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -57,10 +58,19 @@ struct Counter {
 
 inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
-// Kernel timing hooks (api.hip).  timing_begin returns a token (or -1 when timing is off) that
-// the caller passes to timing_end after launching the kernel on the same stream.
-int timing_begin(const char *kernel, hipStream_t s);
-void timing_end(int token, hipStream_t s, double flops);
+// Kernel timing (api.hip).  timing_sample returns true when this launch of `kernel` is one of the
+// sampled ones; the caller then launches with hipExtLaunchKernelGGL and the two events, which the
+// dispatch itself records at the kernel's start and end (so the duration excludes queueing).
+bool timing_sample(const char *kernel, double work, hipEvent_t *start, hipEvent_t *stop);
+
+#define LRC_TIMED_LAUNCH(name, work, kern, grid, block, shmem, stream, ...)                          \
+    do {                                                                                            \
+        hipEvent_t ts_, te_;                                                                        \
+        if (::lrc::timing_sample(name, work, &ts_, &te_))                                           \
+            hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, ts_, te_, 0, __VA_ARGS__);      \
+        else                                                                                        \
+            hipLaunchKernelGGL(kern, grid, block, shmem, stream, __VA_ARGS__);                      \
+    } while (0)
 
 // ---------------------------------------------------------------------------------------------
 // device helpers

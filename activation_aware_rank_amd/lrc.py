@@ -62,6 +62,7 @@ _sym64 = _sig("lrc_sym_to_f64", _int, _vp, _i64, _i64, ctypes.c_double, _vp, _i6
 _to64 = _sig("lrc_to_f64", _int, _vp, _int, _i64, _i64, _i64, ctypes.c_double, _vp, _i64, _vp)
 _gram64 = _sig("lrc_gram_f64", _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp)
 _tim_en = _sig("lrc_timing_enable", _int, _int)
+_tim_st = _sig("lrc_timing_set_stride", _int, ctypes.c_char_p, _int)
 _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _int)
 
@@ -70,7 +71,7 @@ EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_a
             "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_allocate_ranks_workspace",
             "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm_workspace", "lrc_trmm",
             "lrc_trsm_workspace", "lrc_trsm", "lrc_sym_to_f64", "lrc_to_f64", "lrc_gram_f64",
-            "lrc_timing_enable", "lrc_timing_read")
+            "lrc_timing_enable", "lrc_timing_set_stride", "lrc_timing_read")
 
 
 class LrcError(RuntimeError):
@@ -307,8 +308,16 @@ def lrc_cholesky(A: torch.Tensor, info=None, ws=None, stream=None):
     return A, info
 
 
-def lrc_timing_enable(enable: bool = True):
-    _check(_tim_en(1 if enable else 0))
+def lrc_timing_enable(enable=True):
+    """True (or 1): record every launch of the instrumented kernels; an int s > 1: every s-th
+    launch of each kernel; False / 0: off."""
+    stride = int(enable) if not isinstance(enable, bool) else (1 if enable else 0)
+    _check(_tim_en(stride))
+
+
+def lrc_timing_set_stride(kernel: str, stride: int):
+    """Record every stride-th launch of one kernel (overrides the stride given to lrc_timing_enable)."""
+    _check(_tim_st(kernel.encode(), int(stride)))
 
 
 def lrc_timing_read(kernel: str, reset: bool = True):

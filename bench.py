@@ -112,7 +112,8 @@ def curvature_leg(torch, lrc, n_tok, seed, prec, dev, d_in=5120, d_out=13824, k=
     torch.cuda.synchronize()
     for kern in ("k_dgemm", "k_cov_syrk", "k_cov_gemm_y"):
         lrc.lrc_timing_read(kern, reset=True)
-    lrc.lrc_timing_enable(True)
+    lrc.lrc_timing_enable(1)
+    lrc.lrc_timing_set_stride("k_trd_symv", 16)
     marks = []
     t0 = time.perf_counter()
     out = curvature_truncation(d["X"], d["G"], d["W"], k, prec, marks=marks)
@@ -154,6 +155,8 @@ def main():
     ap.add_argument("--curvature-tokens", type=int, default=131072,
                     help="tokens of the curvature-weighted 13B FFN leg, timed after the block (0: skip)")
     ap.add_argument("--curvature-prec", choices=("f32", "f64"), default="f64")
+    ap.add_argument("--timing-stride", type=int, default=16,
+                    help="time every s-th launch of the per-column symmetric product in the timed steps")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported (the path would shard matrices "
@@ -198,35 +201,36 @@ def main():
     k_out = torch.empty(len(MATS), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def ev():
+    def ev(st):
         e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
+        e.record(st)
         return e
 
     def step(times):
         for i, m in enumerate(MATS):
             xin = Xd if m == "down_proj" else X
             C[m].zero_()
-            e0 = ev()
+            e0 = ev(stream)
             lrc.lrc_cov_accumulate(xin, W[m], C[m], info=info[i:i + 1], ws=ws_cov)
-            e1 = ev()
+            e1 = ev(stream)
             lrc.lrc_eigh(C[m], ks[m], prec=prec, lam=lam[m][None], V=V[m][None], info=info[7:8], ws=ws_eig)
-            e2 = ev()
+            e2 = ev(stream)
             lrc.lrc_error_curve(lam[m], eps=eps[m])
-            e3 = ev()
+            e3 = ev(stream)
             lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m])
-            e4 = ev()
-            times.append((m, e0, e1, e2, e3, e4))
-        e5 = ev()
+            e4 = ev(stream)
+            times.append((m, e0, e1, e1, e2, e3, e4))
+        e5 = ev(stream)
         lrc.lrc_fisher_scores([G[m] for m in MATS], [W[m] for m in MATS], alpha=alpha, ws=ws_fsh)
+        e6 = ev(stream)
         for i, m in enumerate(MATS):  # gather lambda_m[:K_m] and eps_{m,0} (device copies)
             lam_packed[offs_h[i]:offs_h[i] + kcap[m]].copy_(lam[m][:kcap[m]])
             eps0[i:i + 1].copy_(eps[m][0:1])
-        e6 = ev()
+        e7 = ev(stream)
         lrc.lrc_allocate_ranks(alpha, lam_packed, offs, eps0, cost, budget, k_out=k_out, ws=ws_alc)
-        e7 = ev()
-        times.append(("fisher", e5, e6, None, None, None))
-        times.append(("alloc", e6, e7, None, None, None))
+        e8 = ev(stream)
+        times.append(("fisher", e5, e6, None, None, None, None))
+        times.append(("alloc", e7, e8, None, None, None, None))
 
     # a plain copy of known size, outside the timed region: the reference that scales HBM byte
     # counters (FETCH_SIZE / WRITE_SIZE) of a profiled run into bytes
@@ -237,8 +241,9 @@ def main():
     for _ in range(a.warmup):
         step([])
     torch.cuda.synchronize()
-    lrc.lrc_timing_read("k_cov_syrk", reset=True)
-    lrc.lrc_timing_enable(True)
+    lrc.lrc_timing_read("k_cov_syrk", reset=True)  # a reset drops the records of every kernel
+    lrc.lrc_timing_enable(1)  # every launch of the long kernels
+    lrc.lrc_timing_set_stride("k_trd_symv", a.timing_stride)  # one launch per column: a sample
     recs = []
     t0 = time.perf_counter()
     for _ in range(a.steps):
@@ -249,7 +254,8 @@ def main():
     wall = time.perf_counter() - t0
     lrc.lrc_timing_enable(False)
     syrk_n, syrk_ms, syrk_fl = lrc.lrc_timing_read("k_cov_syrk", reset=False)
-    gemm_n, gemm_ms, gemm_fl = lrc.lrc_timing_read("k_cov_gemm_y", reset=True)
+    gemm_n, gemm_ms, gemm_fl = lrc.lrc_timing_read("k_cov_gemm_y", reset=False)
+    symv_n, symv_ms, symv_by = lrc.lrc_timing_read("k_trd_symv", reset=True)
     assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
 
     # per-call times from the events (ms), averaged over steps
@@ -258,12 +264,12 @@ def main():
 
     per = {}
     for r in recs:
-        for m, e0, e1, e2, e3, e4 in r:
+        for m, e0, e1, e1b, e2, e3, e4 in r:
             if m in ("fisher", "alloc"):
                 per.setdefault(m, []).append(el(e0, e1))
             else:
                 per.setdefault(m + ".cov", []).append(el(e0, e1))
-                per.setdefault(m + ".eigh", []).append(el(e1, e2))
+                per.setdefault(m + ".eigh", []).append(el(e1b, e2))
                 per.setdefault(m + ".err", []).append(el(e2, e3))
                 per.setdefault(m + ".fac", []).append(el(e3, e4))
     avg = {k: float(np.mean(v)) for k, v in per.items()}
@@ -276,20 +282,35 @@ def main():
     if a.breakdown:
         for k in sorted(avg):
             print("%-20s %10.3f ms" % (k, avg[k]), file=sys.stderr)
-    # roofline of the dominant single kernel (the covariance SYRK), from HIP events recorded by the
-    # library around each of its launches on the launch stream during the timed steps
+    # rooflines from HIP events the library records around each launch on its launch stream during
+    # the timed steps; "roofline" is the kernel with the largest summed time
     syrk_tf = syrk_fl / (syrk_ms / 1000.0) / 1e12
-    roof = {"kernel": "k_cov_syrk", "bound": "mfma", "achieved": syrk_tf, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": syrk_tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("k_cov_syrk"),
-            "launches": syrk_n, "avg_launch_ms": syrk_ms / max(syrk_n, 1),
-            "per_launch": "algorithmic flops = tokens in the chunk x d_out (d_out + 1) (upper triangle incl. "
-                          "diagonal); the kernel executes 4 bf16 MFMA products per flop pair (hi/lo split), "
-                          "so executed MFMA utilisation is 4x frac"}
+    roof_syrk = {"kernel": "k_cov_syrk", "bound": "mfma", "achieved": syrk_tf, "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": syrk_tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("k_cov_syrk"),
+                 "launches": syrk_n, "avg_launch_ms": syrk_ms / max(syrk_n, 1),
+                 "total_ms_per_step": syrk_ms / a.steps,
+                 "per_launch": "algorithmic flops = tokens in the chunk x d_out (d_out + 1) (upper triangle incl. "
+                               "diagonal); the kernel executes 4 bf16 MFMA products per flop pair (hi/lo split), "
+                               "so executed MFMA utilisation is 4x frac"}
     gemm_tf = gemm_fl / (gemm_ms / 1000.0) / 1e12 if gemm_ms > 0 else 0.0
     roof_gemm = {"kernel": "k_cov_gemm_y", "bound": "mfma", "achieved": gemm_tf, "peak": PEAK_BF16_TFLOPS,
                  "unit": "TFLOP/s", "frac": gemm_tf / PEAK_BF16_TFLOPS, "launches": gemm_n,
                  "avg_launch_ms": gemm_ms / max(gemm_n, 1),
+                 "total_ms_per_step": gemm_ms / a.steps,
                  "per_launch": "algorithmic flops = 2 x tokens in the chunk x d_in x d_out"}
+    symv_gbs = symv_by / (symv_ms / 1000.0) / 1e9 if symv_ms > 0 else 0.0
+    roof_symv = {"kernel": "k_trd_symv", "bound": "hbm", "achieved": symv_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": symv_gbs / PEAK_HBM_GBS, "traffic": measured_traffic("k_trd_symv"), "launches": symv_n,
+                 "avg_launch_ms": symv_ms / max(symv_n, 1),
+                 "total_ms_per_step": symv_ms * a.timing_stride / a.steps,
+                 "avg_bytes_per_launch": symv_by / max(symv_n, 1),
+                 "per_launch": "algorithmic bytes = upper triangle of the trailing matrix read once, "
+                               "(n-c-1)(n-c)/2 x 4 bytes for column c (one launch per column)"}
+    for r in (roof_syrk, roof_gemm):
+        r["sampled"] = "every launch in the timed steps (start/stop events recorded by the dispatch)"
+    roof_symv["sampled"] = ("every %d-th launch in the timed steps (start/stop events recorded by the dispatch)"
+                            % a.timing_stride)
+    roof = max((roof_syrk, roof_symv), key=lambda r: r["total_ms_per_step"])
     out = {
         "metric": "calibration tokens/s into Y^T Y; sec per 4096x4096 layer compressed (eig incl.)",
         "value": a.tokens / (step_ms / 1000.0),
@@ -306,7 +327,7 @@ def main():
         "cov_ms": cov_ms, "eigh_ms": eig_ms,
         "breakdown_ms": {k: round(v, 3) for k, v in avg.items()},
         "roofline": roof,
-        "roofline_gemm_y": roof_gemm,
+        "rooflines": {"k_cov_syrk": roof_syrk, "k_trd_symv": roof_symv, "k_cov_gemm_y": roof_gemm},
     }
     if a.curvature_tokens > 0:
         del X, Xd, W, G, C, V, A, B, ws_cov, ws_eig

@@ -68,17 +68,23 @@ enum {
 };
 
 /* ------------------------------------------------------------------------------------
- * Kernel timing (instrumentation, not part of the method).  While enabled, the library
- * records a HIP event pair on the launch stream around every launch of the named kernels
- * ("k_cov_syrk", "k_cov_gemm_y") and remembers each launch's algorithmic flop count.
- * lrc_timing_read synchronises on the recorded events and returns, for one kernel name,
- * the number of launches, their summed duration in milliseconds and summed algorithmic
- * flops since the last reset; reset != 0 then discards the records.  Enabling adds two
- * event records per instrumented launch and nothing else.  Not thread-safe with respect
- * to concurrent lrc_timing_read calls.
+ * Kernel timing (instrumentation, not part of the method).  lrc_timing_enable(stride) with
+ * stride >= 1 makes the library record a HIP event pair on the launch stream around every
+ * stride-th launch of each of the named kernels ("k_cov_syrk", "k_cov_gemm_y", "k_trd_symv",
+ * "k_dgemm"; a uniform sample, counted per kernel from the enable call) and remember each
+ * recorded launch's algorithmic work: flops for the contractions, bytes for k_trd_symv (the
+ * upper triangle of the trailing matrix, read once).  stride 0 disables.  lrc_timing_read
+ * synchronises on the recorded events and returns, for one kernel name, the number of recorded
+ * launches, their summed duration in milliseconds and their summed algorithmic work since the
+ * last reset; reset != 0 then discards the records of every kernel.  lrc_timing_set_stride
+ * gives one kernel its own stride (>= 1), overriding the one of lrc_timing_enable.  Sampled
+ * launches go through hipExtLaunchKernel with a start and a stop event that the dispatch itself
+ * records, so the durations are the kernels' own, without queueing.  Not thread-safe with
+ * respect to concurrent lrc_timing_read calls.
  * ------------------------------------------------------------------------------------ */
-lrc_status lrc_timing_enable(int enable);
-lrc_status lrc_timing_read(const char *kernel, int64_t *launches, double *total_ms, double *total_flops,
+lrc_status lrc_timing_enable(int stride);
+lrc_status lrc_timing_set_stride(const char *kernel, int stride);
+lrc_status lrc_timing_read(const char *kernel, int64_t *launches, double *total_ms, double *total_work,
                            int reset);
 
 /* LRC_ABI_VERSION of the built library. */
