@@ -234,3 +234,51 @@ def curvature_layer_gpu(n_tok: int, d_in: int, d_out: int, seed: int, device) ->
     W = (torch.randn(d_in, d_out, generator=g, device=device) * 0.02).to(torch.bfloat16)
     return {"X": X, "G": G, "W": W}
 
+
+def block_gpu(n_tok: int, d_model: int, d_ff: int, seed: int, device) -> dict:
+    """The block recipe drawn on the GPU by torch's seeded generator: X (n_tok x d_model) and X_d
+    (n_tok x d_ff) N(0,1) times per-channel exp(N(0,1)) scales, weights N(0, 0.02^2) and gradients
+    N(0, 1e-4^2) of every block matrix, all bf16.  Other numbers than the host draw; used where
+    the sizes are the full ones."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def act(width):
+        scale = torch.exp(torch.randn(width, generator=g, device=device, dtype=torch.float32))
+        X = torch.empty(n_tok, width, dtype=torch.bfloat16, device=device)
+        for r0 in range(0, n_tok, 65536):
+            r1 = min(n_tok, r0 + 65536)
+            X[r0:r1] = (torch.randn(r1 - r0, width, generator=g, device=device, dtype=torch.float32) * scale).to(
+                torch.bfloat16)
+        return X
+
+    X = act(d_model)
+    Xd = act(d_ff)
+    W, G = {}, {}
+    for m, (di, do) in block_shapes(d_model, d_ff).items():
+        W[m] = (torch.randn(di, do, generator=g, device=device) * 0.02).to(torch.bfloat16)
+        G[m] = (torch.randn(di, do, generator=g, device=device) * 1e-4).to(torch.bfloat16)
+    return {"X": X, "Xd": Xd, "W": W, "G": G}
+
+
+def stack_spectra(n_layers: int = 32, d_model: int = 4096, d_ff: int = 11008, cfg: int = CFG_STACK) -> dict:
+    """Synthetic inputs of the cross-layer allocation over a stack of blocks: for every matrix a
+    decaying spectrum lambda_i = c (i + 1)^-p of its first K = floor(d_in d_out / (d_in + d_out))
+    values (c lognormal, p uniform in [0.5, 1.5]), eps_0 = the spectrum's sum times (1 + u), u
+    uniform in [0, 0.2) (the part beyond K), and an importance alpha lognormal; all fp64."""
+    shapes = block_shapes(d_model, d_ff)
+    lams, eps0, alpha, cost = [], [], [], []
+    for layer in range(n_layers):
+        for mi, name in enumerate(BLOCK_MATRICES):
+            di, do = shapes[name]
+            k = (di * do) // (di + do)
+            r = rng(cfg, layer, mi, S_SCALE, 1)
+            c, p = np.exp(r.standard_normal()), r.uniform(0.5, 1.5)
+            lam = c * (np.arange(k, dtype=np.float64) + 1.0) ** (-p)
+            lams.append(lam)
+            eps0.append(float(lam.sum()) * (1.0 + r.uniform(0.0, 0.2)))
+            alpha.append(float(np.exp(r.standard_normal())))
+            cost.append(di + do)
+    return {"lams": lams, "eps0": np.array(eps0), "alpha": np.array(alpha), "cost": np.array(cost, dtype=np.int64)}
+

@@ -41,28 +41,6 @@ def cov_flops(n_tok, d_in, d_out):
     return n_tok * (2 * d_in * d_out + d_out * (d_out + 1))
 
 
-def gen_inputs(torch, n_tok, d_model, d_ff, seed, dev):
-    g = torch.Generator(device=dev)
-    g.manual_seed(seed)
-
-    def act(width):
-        scale = torch.exp(torch.randn(width, generator=g, device=dev, dtype=torch.float32))
-        X = torch.empty(n_tok, width, dtype=torch.bfloat16, device=dev)
-        for r0 in range(0, n_tok, 65536):
-            r1 = min(n_tok, r0 + 65536)
-            X[r0:r1] = (torch.randn(r1 - r0, width, generator=g, device=dev, dtype=torch.float32) * scale).to(
-                torch.bfloat16)
-        return X
-
-    X = act(d_model)
-    Xd = act(d_ff)
-    W, G = {}, {}
-    for m, (di, do) in shapes(d_model, d_ff).items():
-        W[m] = (torch.randn(di, do, generator=g, device=dev) * 0.02).to(torch.bfloat16)
-        G[m] = (torch.randn(di, do, generator=g, device=dev) * 1e-4).to(torch.bfloat16)
-    return X, Xd, W, G
-
-
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter record, if the kernel's source is
     unchanged since the counters were taken (else None)."""
@@ -173,7 +151,10 @@ def main():
     prec = lrc.LRC_F32 if a.prec == "f32" else lrc.LRC_F64
     sh = shapes(a.d_model, a.d_ff)
     ks = {m: int(np.floor(a.ratio * di * do / (di + do))) for m, (di, do) in sh.items()}
-    X, Xd, W, G = gen_inputs(torch, a.tokens, a.d_model, a.d_ff, a.seed, dev)
+    from activation_aware_rank_amd import inputs
+    blk = inputs.block_gpu(a.tokens, a.d_model, a.d_ff, a.seed, dev)
+    X, Xd, W, G = blk["X"], blk["Xd"], blk["W"], blk["G"]
+    del blk
     # outputs and workspaces allocated once, outside the timed region
     C = {m: torch.empty(do, do, dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
     lam = {m: torch.empty(do, dtype=torch.float64, device=dev) for m, (di, do) in sh.items()}

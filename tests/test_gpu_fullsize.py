@@ -1,0 +1,183 @@
+"""Parity at the full sizes of the workloads, in the launch configuration bench.py times.
+
+The oracle cannot redo these whole (a 524288-token covariance of an 11008-wide block is 3e15 fp64
+flops), so every case checks outputs the oracle computes one by one, plus properties that hold at
+any size:
+* per-head keys (32768 tokens x 4096, 32 heads of 128, k = 32): three heads in full against the
+  oracle (covariance, eigenvalues, retained subspace, error curve, the direct error of the GPU
+  factors); all 32 heads by eigen-residual and orthogonality;
+* LLaMA-7B block at 524288 tokens (q_proj 4096 -> 4096, k = 1228; gate_proj 4096 -> 11008,
+  k = 1791), inputs drawn on the GPU as bench.py draws them: sampled covariance entries against the
+  oracle's sums over all tokens; residual and orthogonality of the retained eigenpairs; the closed
+  form eps_k = trace(C) - sum_{i<=k} v_i^T C v_i; A = W V_k on sampled rows;
+* 32-layer stack (224 matrices, 6,476,005,376 parameters): Fisher scores of every matrix on the GPU,
+  three checked against the oracle; the greedy allocation of an 80 % budget over all 548,704
+  candidate ranks, bit-exact against the oracle on identical (synthetic) spectra and scores.
+Tolerances are those of the reduced-size parity tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_aware_rank_amd import inputs
+from parity_utils import check_eps, check_lambda, dev, gap, host, sin_theta_max
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lrc():
+    from activation_aware_rank_amd import lrc as m
+    return m
+
+
+def _say(msg):
+    print("\n[case] " + msg, flush=True)
+
+
+def test_per_head_full_size(lrc):
+    _say("per-head keys at full size: 32768 x 4096, 32 heads of 128, k = 32")
+    d = inputs.per_head()
+    X, W = d["X"], d["W"]
+    nh, hd, k = 32, 128, 32
+    Xd, Wd = dev(X, "bf16"), dev(W, "bf16")
+    C = torch.zeros(nh, hd, hd, dtype=torch.float32, device="cuda")
+    info = lrc.lrc_cov_accumulate(Xd, Wd, C, n_blocks=nh)
+    assert int(host(info)[0]) == 0
+    lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=2)
+    assert np.all(host(info) == 0)
+    eps = lrc.lrc_error_curve(lam)
+    A = torch.empty(nh, 4096, k, dtype=torch.float32, device="cuda")
+    B = torch.empty(nh, k, hd, dtype=torch.float32, device="cuda")
+    lrc.lrc_factorize(Wd, V, k, A, B, d_in=4096, d_out=hd, batch=nh, stride_w=hd, stride_v=hd * k,
+                      stride_a=4096 * k, stride_b=k * hd)
+    Ch, lam_h, V_h, eps_h, A_h, B_h = host(C), host(lam), host(V), host(eps), host(A), host(B)
+    # every head: residual and orthogonality of the retained eigenpairs (GPU quantities, fp64)
+    for h in range(nh):
+        Cs = np.triu(Ch[h]).astype(np.float64)
+        Cs = Cs + np.triu(Cs, 1).T
+        Vk = V_h[h].astype(np.float64)
+        res = np.max(np.linalg.norm(Cs @ Vk - Vk * lam_h[h][:k], axis=0)) / lam_h[h][0]
+        orth = np.max(np.abs(Vk.T @ Vk - np.eye(k)))
+        assert res <= 1e-5 and orth <= 1e-5, "head %d: residual %.2e orthogonality %.2e" % (h, res, orth)
+    X64 = oracle.widen(X, "bf16")
+    W64 = oracle.widen(W, "bf16")
+    for h in (0, 13, 31):
+        Wh = W[:, h * hd:(h + 1) * hd]
+        Cr = oracle.covariance(X, "bf16", Wh, "bf16")
+        lam_r, V_r = oracle.eigh(Cr)
+        eps_r = oracle.error_curve(lam_r)
+        U = np.triu(np.ones((hd, hd), dtype=bool))
+        ec = np.max(np.abs(np.where(U, Ch[h] - Cr, 0.0))) / lam_r[0]
+        assert ec <= 1e-5, "head %d covariance %.2e lambda_max" % (h, ec)
+        check_lambda(lam_h[h], lam_r)
+        check_eps(eps_h[h], eps_r)
+        s = sin_theta_max(V_h[h], V_r, k)
+        R = X64 @ (W64[:, h * hd:(h + 1) * hd] - A_h[h].astype(np.float64) @ B_h[h].astype(np.float64))
+        direct = float(np.sum(R * R))
+        print("head %d: cov %.2e, sin theta %.2e (gap %.2e), direct/eps_k - 1 = %.2e"
+              % (h, ec, s, gap(lam_r, k), direct / eps_r[k] - 1))
+        assert s <= 1e-3
+        assert abs(direct - eps_r[k]) <= 1e-4 * eps_r[k] + 1e-6 * eps_r[0]
+
+
+@pytest.fixture(scope="module")
+def block_inputs():
+    return inputs.block_gpu(524288, 4096, 11008, 20261203, torch.device("cuda"))
+
+
+@pytest.mark.parametrize("name,k", [("q_proj", 1228), ("gate_proj", 1791)])
+def test_block_matrix_full_size(lrc, block_inputs, name, k):
+    _say("block %s at 524288 tokens, k = %d (bench configuration, eig prec fp32)" % (name, k))
+    X, W = block_inputs["X"], block_inputs["W"][name]
+    d_in, d_out = W.shape
+    C = torch.zeros(d_out, d_out, dtype=torch.float32, device="cuda")
+    info = lrc.lrc_cov_accumulate(X, W, C)
+    assert int(host(info)[0]) == 0
+    lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=1)
+    assert int(host(info)[0]) == 0
+    eps = lrc.lrc_error_curve(lam)
+    A = torch.empty(d_in, k, dtype=torch.float32, device="cuda")
+    B = torch.empty(k, d_out, dtype=torch.float32, device="cuda")
+    lrc.lrc_factorize(W, V, k, A, B)
+    f64 = torch.float64
+    Cs = torch.triu(C).to(f64)
+    Cs = Cs + torch.triu(Cs, 1).T
+    lam_d = lam.to(f64)
+    Vk = V.to(f64)
+    # retained eigenpairs: residual and orthogonality
+    res = float(torch.linalg.vector_norm(Cs @ Vk - Vk * lam_d[:k], dim=0).max() / lam_d[0])
+    orth = float((Vk.T @ Vk - torch.eye(k, dtype=f64, device="cuda")).abs().max())
+    # closed form: eps_k = trace(C) - sum_{i<=k} v_i^T C v_i
+    tr = float(torch.diagonal(Cs).sum())
+    kept = float((Vk * (Cs @ Vk)).sum())
+    eps_h = host(eps)
+    cf = abs((tr - kept) - eps_h[k]) / eps_h[k]
+    # factors: A = W V_k on sampled rows
+    rows = torch.randint(0, d_in, (64,), generator=torch.Generator().manual_seed(3)).cuda()
+    Ar = W[rows].to(f64) @ Vk
+    fa = float((A[rows].to(f64) - Ar).abs().max() / Ar.abs().max())
+    print("%s: residual %.2e, orthogonality %.2e, closed form %.2e, factor %.2e, eps_k/eps_0 %.3e"
+          % (name, res, orth, cf, fa, eps_h[k] / eps_h[0]))
+    assert res <= 1e-5 and orth <= 1e-5
+    assert cf <= 1e-4
+    assert fa <= 1e-6
+    assert abs(eps_h[0] - tr) <= 1e-6 * tr
+    # sampled covariance entries against the oracle's fp64 sums over all 524288 tokens
+    r = np.random.default_rng(17)
+    ii = np.concatenate([r.integers(0, d_out, 12), np.arange(4)])
+    jj = np.concatenate([r.integers(0, d_out, 12), np.arange(4)])
+    ii, jj = np.minimum(ii, jj), np.maximum(ii, jj)
+    Xh = host(X.view(torch.int16)).view(np.uint16)
+    Wh = host(W.view(torch.int16)).view(np.uint16)
+    ref = oracle.covariance_entries(Xh, "bf16", Wh, "bf16", ii, jj)
+    got = host(C)[ii, jj].astype(np.float64)
+    diag = host(torch.diagonal(C)).astype(np.float64)
+    dref = np.sqrt(diag[ii] * diag[jj])
+    err = np.max(np.abs(got - ref) / dref)
+    print("%s: sampled covariance entries, max error %.2e of sqrt(C_ii C_jj)" % (name, err))
+    assert err <= 1e-5
+
+
+def test_stack_fisher_full_size(lrc):
+    _say("Fisher scores of the 32-layer stack: 224 matrices, 6,476,005,376 parameters")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261204)
+    shapes = inputs.block_shapes()
+    Gs, Ws, names = [], [], []
+    for layer in range(32):
+        for name in inputs.BLOCK_MATRICES:
+            di, do = shapes[name]
+            Ws.append((torch.randn(di, do, generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+            Gs.append((torch.randn(di, do, generator=g, device="cuda") * 1e-4).to(torch.bfloat16))
+            names.append((layer, name))
+    assert sum(w.numel() for w in Ws) == 6476005376
+    alpha, info = lrc.lrc_fisher_scores(Gs, Ws)
+    assert np.all(host(info) == 0)
+    a = host(alpha)
+    for m in (0, 117, 223):
+        Gh = host(Gs[m].view(torch.int16)).view(np.uint16)
+        Wh = host(Ws[m].view(torch.int16)).view(np.uint16)
+        ref = oracle.fisher(Gh, Wh, "bf16")
+        print("matrix %d %s: alpha %.6e, relative error %.2e" % (m, names[m], a[m], abs(a[m] - ref) / ref))
+        assert abs(a[m] - ref) <= 1e-12 * ref
+
+
+def test_stack_allocation_full_size_bitexact(lrc):
+    _say("greedy allocation over 224 matrices, 548704 candidates, 80 % budget")
+    st = inputs.stack_spectra()
+    lams, eps0, alpha, cost = st["lams"], st["eps0"], st["alpha"], st["cost"]
+    n_items = sum(len(x) for x in lams)
+    assert len(lams) == 224 and n_items == 548704
+    budget = int(np.floor(0.8 * 6476005376))
+    k_ref, info_ref = oracle.allocate_ranks(alpha, lams, eps0, cost, budget)
+    offs = np.concatenate([[0], np.cumsum([len(x) for x in lams])]).astype(np.int64)
+    k_gpu, info = lrc.lrc_allocate_ranks(dev(alpha, "f64"), dev(np.concatenate(lams), "f64"), dev(offs, "i64"),
+                                         dev(eps0, "f64"), dev(cost, "i64"), budget)
+    assert int(host(info)[0]) == info_ref == 0
+    k_gpu = host(k_gpu)
+    assert np.array_equal(k_gpu, np.asarray(k_ref))
+    used = int(np.sum(k_gpu.astype(np.int64) * cost))
+    print("allocated %d of %d parameters; ranks %d .. %d" % (used, budget, k_gpu.min(), k_gpu.max()))
+    assert used <= budget
