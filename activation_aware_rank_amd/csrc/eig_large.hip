@@ -778,61 +778,55 @@ __global__ void __launch_bounds__(256) k_cluster_mgs(const double *__restrict__ 
 // ---------------------------------------------------------------------------------------------
 // 4. back-transformation
 // ---------------------------------------------------------------------------------------------
-// partial Gram S[a][b] = sum_{r in chunk} Rt[c0+a][r] Rt[c0+b][r]
+// T factor of every block of NBT reflectors in one launch (block b = blockIdx.x, reflectors
+// c0 = b NBT ...): S = V_b^T V_b over the block's rows (fixed order: per-thread strided sums, then a
+// fixed tree), then T forward, column by column: T[0:i, i] = -tau_i T[0:i, 0:i] S[0:i, i], T[i][i] =
+// tau_i.  V_b is rows c0 .. c0+nb-1 of Rt, nonzero from column c0+1 on.
 template <class T>
-__global__ void __launch_bounds__(256) k_bt_gram(const T *__restrict__ Rt, int64_t ldr, int64_t n, int64_t c0, int nb,
-                                                 double *__restrict__ Sp) {
-    __shared__ double vs[NBT][RCH / 8 + 1];
-    const int64_t r0 = int64_t(blockIdx.x) * RCH;
-    double acc[4] = {0, 0, 0, 0};
-    const int ab = threadIdx.x;  // pairs ab + 256 u, u < 4: a = pair / NBT, b = pair % NBT
-    for (int64_t rs = 0; rs < RCH; rs += RCH / 8) {
-        for (int e = threadIdx.x; e < NBT * (RCH / 8); e += 256) {
-            const int q = e / (RCH / 8), rr = e % (RCH / 8);
-            const int64_t r = r0 + rs + rr;
+__global__ void __launch_bounds__(256) k_bt_tall(const T *__restrict__ Rt, int64_t ldr, int64_t n, int64_t nrefl,
+                                                 const T *__restrict__ tau, double *__restrict__ Tall) {
+    __shared__ double vs[NBT][65];
+    __shared__ double S[NBT][NBT + 1], Tm[NBT][NBT + 1];
+    const int64_t c0 = int64_t(blockIdx.x) * NBT;
+    const int nb = int(min<int64_t>(NBT, nrefl - c0));
+    const int t = threadIdx.x;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};  // pairs t + 256 u: a = pair / NBT, b = pair % NBT
+    for (int64_t r0 = c0 + 1; r0 < n; r0 += 64) {
+        for (int e = t; e < NBT * 64; e += 256) {
+            const int q = e / 64, rr = e % 64;
+            const int64_t r = r0 + rr;
             vs[q][rr] = (q < nb && r < n) ? double(Rt[(c0 + q) * ldr + r]) : 0.0;
         }
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int pidx = ab + 256 * u;
+            const int pidx = t + 256 * u;
             const int pa = pidx / NBT, pb = pidx % NBT;
-            double s = 0.0;
-            for (int rr = 0; rr < RCH / 8; ++rr) s += vs[pa][rr] * vs[pb][rr];
-            acc[u] += s;
+            double sacc = 0.0;
+            for (int rr = 0; rr < 64; ++rr) sacc += vs[pa][rr] * vs[pb][rr];
+            acc[u] += sacc;
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) Sp[int64_t(blockIdx.x) * NBT * NBT + ab + 256 * u] = acc[u];
-}
-
-// one block: S = sum of partials; T factor of the block (forward, columnwise)
-template <class T>
-__global__ void __launch_bounds__(256) k_bt_tfactor(const double *__restrict__ Sp, int nchunk, const T *__restrict__ tau,
-                                                    int64_t c0, int nb, double *__restrict__ Tf) {
-    __shared__ double S[NBT][NBT], Tm[NBT][NBT];
-    for (int e = threadIdx.x; e < NBT * NBT; e += 256) {
-        double s = 0.0;
-        for (int k = 0; k < nchunk; ++k) s += Sp[int64_t(k) * NBT * NBT + e];
-        S[e / NBT][e % NBT] = s;
-        Tm[e / NBT][e % NBT] = 0.0;
+    for (int u = 0; u < 4; ++u) {
+        const int pidx = t + 256 * u;
+        S[pidx / NBT][pidx % NBT] = acc[u];
+        Tm[pidx / NBT][pidx % NBT] = 0.0;
     }
     __syncthreads();
     for (int i = 0; i < nb; ++i) {
         const double ti = double(tau[c0 + i]);
-        // T[0:i, i] = -tau_i T[0:i, 0:i] S[0:i, i]
         double v = 0.0;
-        const int a = threadIdx.x;
-        if (a < i) {
-            for (int k = a; k < i; ++k) v += Tm[a][k] * S[k][i];
-        }
+        if (t < i)
+            for (int k = t; k < i; ++k) v += Tm[t][k] * S[k][i];
         __syncthreads();
-        if (a < i) Tm[a][i] = -ti * v;
-        if (a == 0) Tm[i][i] = ti;
+        if (t < i) Tm[t][i] = -ti * v;
+        if (t == 0) Tm[i][i] = ti;
         __syncthreads();
     }
-    for (int e = threadIdx.x; e < NBT * NBT; e += 256) Tf[e] = Tm[e / NBT][e % NBT];
+    double *out = Tall + int64_t(blockIdx.x) * NBT * NBT;
+    for (int e = t; e < NBT * NBT; e += 256) out[e] = Tm[e / NBT][e % NBT];
 }
 
 // partial G[q][col] = sum_{r in chunk} Rt[c0+q][r] Z[r][col]; grid (col tiles of 64, row chunks)
@@ -973,7 +967,7 @@ __global__ void k_set_info(int32_t *info, const int *bad) {
 template <class T>
 struct LargeWs {
     T *A, *Rt, *Vp, *Wp, *tau, *colbuf, *part, *qcol, *qvec, *spart, *rowpart, *colpart;
-    double *d, *e, *e2, *bounds, *lam, *Z, *U0, *U1, *U2, *ML, *Sp, *Tf, *Gp, *G;
+    double *d, *e, *e2, *bounds, *lam, *Z, *U0, *U1, *U2, *ML, *Tf, *Gp, *G;
     uint8_t *SW;
     int *bad;
     int64_t lda;
@@ -1012,8 +1006,7 @@ static void layout(C_ &cv, LargeWs<T> &w, int64_t n, int64_t nv, bool count_only
     w.U2 = cv.template carve<double>(size_t(n) * size_t(nv1));
     w.ML = cv.template carve<double>(size_t(n) * size_t(nv1));
     w.SW = cv.template carve<uint8_t>(size_t(n) * size_t(nv1));
-    w.Sp = cv.template carve<double>(size_t(nch) * NBT * NBT);
-    w.Tf = cv.template carve<double>(NBT * NBT);
+    w.Tf = cv.template carve<double>(size_t((n + NBT - 1) / NBT) * NBT * NBT);
     w.Gp = cv.template carve<double>(size_t(nch) * NBT * size_t(nv1));
     w.G = cv.template carve<double>(NBT * size_t(nv1));
     w.bad = cv.template carve<int>(1);
@@ -1092,15 +1085,15 @@ static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *
                            w.U2, w.ML, w.SW);
         hipLaunchKernelGGL(k_cluster_mgs, dim3(unsigned(nv)), dim3(256), 0, s, w.lam, n, nv, w.bounds, w.Z);
         LRC_LAUNCH_CHECK("inverse iteration");
-        // 4. back-transformation, last block of reflectors first
+        // 4. back-transformation, last block of reflectors first; all T factors first, in one launch
         const int64_t nrefl = n - 1;
         const int nch = cdiv(n, RCH);
+        hipLaunchKernelGGL(k_bt_tall<T>, dim3(cdiv(nrefl, NBT)), dim3(256), 0, s, w.Rt, n, n, nrefl, w.tau, w.Tf);
         for (int64_t c0 = ((nrefl - 1) / NBT) * NBT; c0 >= 0; c0 -= NBT) {
             const int nb = int(std::min<int64_t>(NBT, nrefl - c0));
-            hipLaunchKernelGGL(k_bt_gram<T>, dim3(nch), dim3(256), 0, s, w.Rt, n, n, c0, nb, w.Sp);
-            hipLaunchKernelGGL(k_bt_tfactor<T>, dim3(1), dim3(256), 0, s, w.Sp, nch, w.tau, c0, nb, w.Tf);
             hipLaunchKernelGGL(k_bt_g<T>, dim3(cdiv(nv, 64), nch), dim3(256), 0, s, w.Rt, n, n, c0, nb, w.Z, nv, w.Gp);
-            hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, GR_COLS)), dim3(256), 0, s, w.Gp, nch, nv, w.Tf, w.G);
+            hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, GR_COLS)), dim3(256), 0, s, w.Gp, nch, nv,
+                               w.Tf + (c0 / NBT) * NBT * NBT, w.G);
             const int64_t mrows = n - c0 - 1;
             hipLaunchKernelGGL(k_bt_update<T>, dim3(cdiv(nv, 64), cdiv(mrows, 64)), dim3(256), 0, s, w.Rt, n, n, c0, nb,
                                w.G, w.Z, nv);
