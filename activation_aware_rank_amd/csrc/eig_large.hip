@@ -22,7 +22,7 @@
 namespace lrc {
 
 constexpr int NB = 32;    // tridiagonalisation panel width
-constexpr int NBT = 32;   // back-transformation block of reflectors
+constexpr int NBT = 64;   // back-transformation block of reflectors
 constexpr int RCH = 512;  // rows per partial in the back-transformation reductions
 
 // ---------------------------------------------------------------------------------------------
@@ -790,7 +790,10 @@ __global__ void __launch_bounds__(256) k_bt_tall(const T *__restrict__ Rt, int64
     const int64_t c0 = int64_t(blockIdx.x) * NBT;
     const int nb = int(min<int64_t>(NBT, nrefl - c0));
     const int t = threadIdx.x;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};  // pairs t + 256 u: a = pair / NBT, b = pair % NBT
+    constexpr int PU = NBT * NBT / 256;  // pairs per thread
+    double acc[PU];                      // pairs t + 256 u: a = pair / NBT, b = pair % NBT
+#pragma unroll
+    for (int u = 0; u < PU; ++u) acc[u] = 0.0;
     for (int64_t r0 = c0 + 1; r0 < n; r0 += 64) {
         for (int e = t; e < NBT * 64; e += 256) {
             const int q = e / 64, rr = e % 64;
@@ -799,7 +802,7 @@ __global__ void __launch_bounds__(256) k_bt_tall(const T *__restrict__ Rt, int64
         }
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < PU; ++u) {
             const int pidx = t + 256 * u;
             const int pa = pidx / NBT, pb = pidx % NBT;
             double sacc = 0.0;
@@ -809,7 +812,7 @@ __global__ void __launch_bounds__(256) k_bt_tall(const T *__restrict__ Rt, int64
         __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < PU; ++u) {
         const int pidx = t + 256 * u;
         S[pidx / NBT][pidx % NBT] = acc[u];
         Tm[pidx / NBT][pidx % NBT] = 0.0;
@@ -866,7 +869,7 @@ __global__ void __launch_bounds__(256) k_bt_g(const T *__restrict__ Rt, int64_t 
 }
 
 // G = T (sum of partials): thread (q, col) adds the partials of G[q][col] in chunk order, then
-// thread (a, col) forms sum_q T[a][q] G[q][col] from LDS.  Blocks of 8 columns x NBT.
+// thread (a, col) forms sum_q T[a][q] G[q][col] from LDS.  Blocks of 256 / NBT columns x NBT.
 constexpr int GR_COLS = 256 / NBT;
 __global__ void __launch_bounds__(256) k_bt_greduce(const double *__restrict__ Gp, int nchunk, int64_t nv,
                                                     const double *__restrict__ Tf, double *__restrict__ G) {
