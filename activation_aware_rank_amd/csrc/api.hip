@@ -181,9 +181,9 @@ size_t lrc_eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype pre
     return eigh_workspace(n, batch, n_vec, prec);
 }
 
-lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64_t stride_c, lrc_dtype prec,
-                    double *lambda, float *V, int64_t ldv, int64_t n_vec, int64_t stride_v, void *ws,
-                    size_t ws_bytes, int32_t *info, void *stream) {
+static lrc_status check_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64_t stride_c,
+                             const double *lambda, const float *V, int64_t ldv, int64_t n_vec, int64_t stride_v,
+                             const int32_t *info) {
     REQUIRE(C && lambda && info, LRC_ERR_ARG, "C, lambda and info must be non-NULL");
     REQUIRE(n > 0 && batch > 0, LRC_ERR_ARG, "n and batch must be positive");
     REQUIRE(n <= (int64_t(1) << 20), LRC_ERR_ARG, "n too large");
@@ -193,12 +193,54 @@ lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64
     REQUIRE(n_vec == 0 || (V && ldv >= n_vec), LRC_ERR_ARG, "V NULL or ldv < n_vec");
     REQUIRE(n_vec == 0 || batch == 1 || stride_v >= n * ldv - (ldv - n_vec), LRC_ERR_ARG,
             "stride_v overlaps matrices");
+    return LRC_OK;
+}
+
+lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64_t stride_c, lrc_dtype prec,
+                    double *lambda, float *V, int64_t ldv, int64_t n_vec, int64_t stride_v, void *ws,
+                    size_t ws_bytes, int32_t *info, void *stream) {
+    lrc_status st = check_eigh(C, n, ldc, batch, stride_c, lambda, V, ldv, n_vec, stride_v, info);
+    if (st != LRC_OK) return st;
     REQUIRE(prec == LRC_F32 || prec == LRC_F64, LRC_ERR_DTYPE, "prec must be LRC_F32 or LRC_F64");
     size_t need = eigh_workspace(n, batch, n_vec, prec);
     REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned(ws, 256))), LRC_ERR_WORKSPACE,
             "workspace smaller than lrc_eigh_workspace() or not 256-byte aligned");
     EighArgs a{C, n, ldc, batch, stride_c, prec, lambda, V, ldv, n_vec, stride_v, info};
     return eigh_run(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+static std::vector<EighArgs> eigh_groups(const lrc_eigh_group *g, int32_t count, lrc_dtype prec) {
+    std::vector<EighArgs> v;
+    v.reserve(size_t(count));
+    for (int32_t i = 0; i < count; ++i)
+        v.push_back(EighArgs{g[i].C, g[i].n, g[i].ldc, g[i].batch, g[i].stride_c, prec, g[i].lambda, g[i].V,
+                             g[i].ldv, g[i].n_vec, g[i].stride_v, g[i].info});
+    return v;
+}
+
+size_t lrc_eigh_multi_workspace(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec) {
+    if (!groups || count <= 0) return 0;
+    for (int32_t i = 0; i < count; ++i)
+        if (groups[i].n <= 0 || groups[i].batch <= 0 || groups[i].n_vec < 0 || groups[i].n_vec > groups[i].n) return 0;
+    std::vector<EighArgs> v = eigh_groups(groups, count, prec);
+    return eigh_multi_workspace(v.data(), count, prec);
+}
+
+lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec, void *ws, size_t ws_bytes,
+                          void *stream) {
+    REQUIRE(groups && count > 0, LRC_ERR_ARG, "groups must be non-NULL and count positive");
+    for (int32_t i = 0; i < count; ++i) {
+        const lrc_eigh_group &g = groups[i];
+        lrc_status st = check_eigh(g.C, g.n, g.ldc, g.batch, g.stride_c, g.lambda, g.V, g.ldv, g.n_vec, g.stride_v,
+                                   g.info);
+        if (st != LRC_OK) return st;
+    }
+    REQUIRE(prec == LRC_F32 || prec == LRC_F64, LRC_ERR_DTYPE, "prec must be LRC_F32 or LRC_F64");
+    std::vector<EighArgs> v = eigh_groups(groups, count, prec);
+    size_t need = eigh_multi_workspace(v.data(), count, prec);
+    REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned(ws, 256))), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_eigh_multi_workspace() or not 256-byte aligned");
+    return eigh_multi_run(v.data(), count, prec, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -14,8 +14,12 @@
 //     Q_b = I - V_b T_b V_b^T (compact WY), applied from the last block to the first, in fp64.
 //  5. Each column's entry of largest magnitude made positive.
 // Reflector c is H_c = I - tau_c v_c v_c^T with v_c[c+1] = 1 and v_c[r] = 0 for r <= c.
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <vector>
 
 #include "lrc_internal.h"
 
@@ -1032,110 +1036,310 @@ static size_t large_ws(int64_t n, int64_t nv) {
     return cc.c.off;
 }
 
+// One matrix's decomposition as a resumable sequence of launches: advance() enqueues the next
+// few columns of the tridiagonalisation (or the next blocks of the back-transformation) on the
+// job's stream and returns, so that the host can feed several matrices' streams in turn instead
+// of blocking on one stream's full queue while the others sit idle.
 template <class T>
-static lrc_status large_run_one(const float *C, int64_t ldc, int64_t n, double *lambda, float *V, int64_t ldv,
-                                int64_t nv, int32_t *info, LargeWs<T> &w, hipStream_t s) {
-    const int64_t lda = w.lda;
-    hipLaunchKernelGGL(k_fill_zero<int>, dim3(1), dim3(64), 0, s, w.bad, int64_t(1));
-    hipLaunchKernelGGL(k_fill_full<T>, dim3(2048), dim3(256), 0, s, C, ldc, n, w.A, lda, w.bad);
-    LRC_LAUNCH_CHECK("k_fill_full");
-    const int NT = int(symv_tiles<T>(n));
-    // 1. tridiagonalisation, panels over reflector columns 0 .. n-2 (two launches per column)
-    for (int64_t p0 = 0; p0 < n - 1; p0 += NB) {
-        const int64_t p1 = std::min<int64_t>(p0 + NB, n - 1);
-        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w.Vp, int64_t(n) * NB);
-        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w.Wp, int64_t(n) * NB);
-        int npart = cdiv(n - p0, 256);
-        hipLaunchKernelGGL(k_trd_col0<T>, dim3(npart), dim3(256), 0, s, w.A, lda, n, p0, w.colbuf, w.part, w.d);
-        for (int64_t c = p0; c < p1; ++c) {
-            const int j = int(c - p0);
-            // tiles per symv work item: the largest of 8, 4, 2 that still gives >= 512 items
-            const int mt = NT - int((c + 1) / SymvTile<T>::TS);
-            int chk = 8;
-            while (chk > 1 && symv_items(mt, chk) < 512) chk >>= 1;
-            const int nitems = int(symv_items(mt, chk));
-            // algorithmic bytes: the upper triangle of the trailing matrix, read once
-            const double m1 = double(n - c - 1);
-            LRC_TIMED_LAUNCH("k_trd_symv", m1 * (m1 + 1.0) * 0.5 * double(sizeof(T)), k_trd_symv<T>, dim3(nitems),
-                             dim3(256), 0, s, w.A, lda, n, c, j, w.colbuf, w.part, npart, w.Vp, w.Wp, w.Rt, w.rowpart,
-                             w.colpart, w.qcol, w.qvec, w.spart, w.tau, w.e, NT, chk);
-            // the next column is handled here unless a trailing update comes first (the last
-            // column n-1 has no reflector, only d[n-1])
-            const int next = (c + 1 < p1 || p1 == n - 1) ? 1 : 0;
-            const int nw = cdiv(n - c - 1, 64);
-            hipLaunchKernelGGL(k_trd_w1col<T>, dim3(nw), dim3(256), 0, s, w.A, lda, n, c, j, next, w.Vp, w.Wp,
-                               w.rowpart, w.colpart, w.qvec, w.spart, nitems, NT, chk, w.tau, w.colbuf, w.part,
-                               w.qcol, w.d);
-            npart = nw;
-        }
-        LRC_LAUNCH_CHECK("tridiagonal panel");
-        const int jn = int(p1 - p0);
-        if (p1 < n - 1) {
-            const int64_t m = n - p1;
-            dim3 g(cdiv(m, 64), cdiv(m, 64));
-            hipLaunchKernelGGL(k_trailing<T>, g, dim3(256), 0, s, w.A, lda, n, p1, jn, w.Vp, w.Wp);
-            LRC_LAUNCH_CHECK("k_trailing");
-        }
+struct EigJob {
+    const float *C = nullptr;
+    int64_t ldc = 0, n = 0, ldv = 0, nv = 0;
+    double *lambda = nullptr;
+    float *V = nullptr;
+    int32_t *info = nullptr;
+    LargeWs<T> *w = nullptr;
+    hipStream_t s = nullptr;
+    int stage = 0;  // 0 start, 1 tridiagonalisation, 2 eigenvalues and vectors of T, 3 back-transformation, 4 done
+    int NT = 0, npart = 0;
+    int64_t p0 = 0, p1 = 0, c = 0, c0 = 0;
+
+    void start_panel() {
+        p1 = std::min<int64_t>(p0 + NB, n - 1);
+        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w->Vp, int64_t(n) * NB);
+        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w->Wp, int64_t(n) * NB);
+        npart = cdiv(n - p0, 256);
+        hipLaunchKernelGGL(k_trd_col0<T>, dim3(npart), dim3(256), 0, s, w->A, w->lda, n, p0, w->colbuf, w->part, w->d);
+        c = p0;
     }
-    // 2. eigenvalues
-    hipLaunchKernelGGL(k_tri_prep, dim3(1), dim3(256), 0, s, w.d, w.e, n, w.e2, w.bounds);
-    hipLaunchKernelGGL(k_bisect, dim3(cdiv(n * MSEC, 256)), dim3(256), 0, s, w.d, w.e2, n, w.bounds, w.lam);
-    hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(n, 256)), dim3(256), 0, s, w.lam, n, lambda, w.bad);
-    LRC_LAUNCH_CHECK("bisection");
-    if (nv > 0) {
-        // 3. eigenvectors of T
-        hipLaunchKernelGGL(k_invit, dim3(cdiv(nv, 64)), dim3(64), 0, s, w.d, w.e, n, w.lam, w.bounds, nv, w.Z, w.U0, w.U1,
-                           w.U2, w.ML, w.SW);
-        hipLaunchKernelGGL(k_cluster_mgs, dim3(unsigned(nv)), dim3(256), 0, s, w.lam, n, nv, w.bounds, w.Z);
-        LRC_LAUNCH_CHECK("inverse iteration");
-        // 4. back-transformation, last block of reflectors first; all T factors first, in one launch
-        const int64_t nrefl = n - 1;
-        const int nch = cdiv(n, RCH);
-        hipLaunchKernelGGL(k_bt_tall<T>, dim3(cdiv(nrefl, NBT)), dim3(256), 0, s, w.Rt, n, n, nrefl, w.tau, w.Tf);
-        for (int64_t c0 = ((nrefl - 1) / NBT) * NBT; c0 >= 0; c0 -= NBT) {
-            const int nb = int(std::min<int64_t>(NBT, nrefl - c0));
-            hipLaunchKernelGGL(k_bt_g<T>, dim3(cdiv(nv, 64), nch), dim3(256), 0, s, w.Rt, n, n, c0, nb, w.Z, nv, w.Gp);
-            hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, GR_COLS)), dim3(256), 0, s, w.Gp, nch, nv,
-                               w.Tf + (c0 / NBT) * NBT * NBT, w.G);
-            const int64_t mrows = n - c0 - 1;
-            hipLaunchKernelGGL(k_bt_update<T>, dim3(cdiv(nv, 64), cdiv(mrows, 64)), dim3(256), 0, s, w.Rt, n, n, c0, nb,
-                               w.G, w.Z, nv);
-        }
-        LRC_LAUNCH_CHECK("back-transformation");
-        hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, w.Z, n, nv, V, ldv, w.bad);
-        LRC_LAUNCH_CHECK("k_sign_out");
+
+    void column() {
+        const int64_t lda = w->lda;
+        const int j = int(c - p0);
+        // tiles per symv work item: the largest of 8, 4, 2 that still gives >= 512 items
+        const int mt = NT - int((c + 1) / SymvTile<T>::TS);
+        int chk = 8;
+        while (chk > 1 && symv_items(mt, chk) < 512) chk >>= 1;
+        const int nitems = int(symv_items(mt, chk));
+        // algorithmic bytes: the upper triangle of the trailing matrix, read once
+        const double m1 = double(n - c - 1);
+        LRC_TIMED_LAUNCH("k_trd_symv", m1 * (m1 + 1.0) * 0.5 * double(sizeof(T)), k_trd_symv<T>, dim3(nitems),
+                         dim3(256), 0, s, w->A, lda, n, c, j, w->colbuf, w->part, npart, w->Vp, w->Wp, w->Rt,
+                         w->rowpart, w->colpart, w->qcol, w->qvec, w->spart, w->tau, w->e, NT, chk);
+        // the next column is handled here unless a trailing update comes first (the last column
+        // n-1 has no reflector, only d[n-1])
+        const int next = (c + 1 < p1 || p1 == n - 1) ? 1 : 0;
+        const int nw = cdiv(n - c - 1, 64);
+        hipLaunchKernelGGL(k_trd_w1col<T>, dim3(nw), dim3(256), 0, s, w->A, lda, n, c, j, next, w->Vp, w->Wp,
+                           w->rowpart, w->colpart, w->qvec, w->spart, nitems, NT, chk, w->tau, w->colbuf, w->part,
+                           w->qcol, w->d);
+        npart = nw;
     }
-    hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, s, info, w.bad);
-    LRC_LAUNCH_CHECK("k_set_info");
+
+    // Enqueues about `cols` columns' worth of launches; returns LRC_OK or a launch error.
+    lrc_status advance(int cols) {
+        if (stage == 0) {
+            hipLaunchKernelGGL(k_fill_zero<int>, dim3(1), dim3(64), 0, s, w->bad, int64_t(1));
+            hipLaunchKernelGGL(k_fill_full<T>, dim3(2048), dim3(256), 0, s, C, ldc, n, w->A, w->lda, w->bad);
+            LRC_LAUNCH_CHECK("k_fill_full");
+            NT = int(symv_tiles<T>(n));
+            p0 = 0;
+            start_panel();
+            stage = 1;
+            return LRC_OK;
+        }
+        if (stage == 1) {  // 1. tridiagonalisation, panels over reflector columns 0 .. n-2
+            for (int q = 0; q < cols; ++q) {
+                column();
+                if (++c < p1) continue;
+                LRC_LAUNCH_CHECK("tridiagonal panel");
+                if (p1 < n - 1) {
+                    const int64_t m = n - p1;
+                    dim3 g(cdiv(m, 64), cdiv(m, 64));
+                    hipLaunchKernelGGL(k_trailing<T>, g, dim3(256), 0, s, w->A, w->lda, n, p1, int(p1 - p0), w->Vp,
+                                       w->Wp);
+                    LRC_LAUNCH_CHECK("k_trailing");
+                }
+                p0 += NB;
+                if (p0 >= n - 1) {
+                    stage = 2;
+                    return LRC_OK;
+                }
+                start_panel();
+            }
+            return LRC_OK;
+        }
+        if (stage == 2) {
+            // 2. eigenvalues
+            hipLaunchKernelGGL(k_tri_prep, dim3(1), dim3(256), 0, s, w->d, w->e, n, w->e2, w->bounds);
+            hipLaunchKernelGGL(k_bisect, dim3(cdiv(n * MSEC, 256)), dim3(256), 0, s, w->d, w->e2, n, w->bounds, w->lam);
+            hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(n, 256)), dim3(256), 0, s, w->lam, n, lambda, w->bad);
+            LRC_LAUNCH_CHECK("bisection");
+            if (nv > 0) {
+                // 3. eigenvectors of T
+                hipLaunchKernelGGL(k_invit, dim3(cdiv(nv, 64)), dim3(64), 0, s, w->d, w->e, n, w->lam, w->bounds, nv,
+                                   w->Z, w->U0, w->U1, w->U2, w->ML, w->SW);
+                hipLaunchKernelGGL(k_cluster_mgs, dim3(unsigned(nv)), dim3(256), 0, s, w->lam, n, nv, w->bounds, w->Z);
+                LRC_LAUNCH_CHECK("inverse iteration");
+                // all T factors of the back-transformation first, in one launch
+                hipLaunchKernelGGL(k_bt_tall<T>, dim3(cdiv(n - 1, NBT)), dim3(256), 0, s, w->Rt, n, n, n - 1, w->tau,
+                                   w->Tf);
+                c0 = ((n - 2) / NBT) * NBT;
+                stage = 3;
+                return LRC_OK;
+            }
+            stage = 4;
+        }
+        if (stage == 3) {  // 4. back-transformation, last block of reflectors first
+            const int64_t nrefl = n - 1;
+            const int nch = cdiv(n, RCH);
+            for (int q = 0; q < cols && c0 >= 0; ++q, c0 -= NBT) {
+                const int nb = int(std::min<int64_t>(NBT, nrefl - c0));
+                hipLaunchKernelGGL(k_bt_g<T>, dim3(cdiv(nv, 64), nch), dim3(256), 0, s, w->Rt, n, n, c0, nb, w->Z, nv,
+                                   w->Gp);
+                hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, GR_COLS)), dim3(256), 0, s, w->Gp, nch, nv,
+                                   w->Tf + (c0 / NBT) * NBT * NBT, w->G);
+                const int64_t mrows = n - c0 - 1;
+                hipLaunchKernelGGL(k_bt_update<T>, dim3(cdiv(nv, 64), cdiv(mrows, 64)), dim3(256), 0, s, w->Rt, n, n,
+                                   c0, nb, w->G, w->Z, nv);
+            }
+            LRC_LAUNCH_CHECK("back-transformation");
+            if (c0 >= 0) return LRC_OK;
+            hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, w->Z, n, nv, V, ldv, w->bad);
+            LRC_LAUNCH_CHECK("k_sign_out");
+            stage = 4;
+        }
+        hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, s, info, w->bad);
+        LRC_LAUNCH_CHECK("k_set_info");
+        stage = 5;
+        return LRC_OK;
+    }
+    bool done() const { return stage == 5; }
+};
+
+// Batch members are independent: up to EIG_LANES of them run at once, each on a helper stream
+// of its own with its own workspace, so the per-column launch chains of several matrices
+// overlap (one chain alone leaves most of the GPU idle once the trailing matrix is small).  The
+// helper streams (default priority) and their events are created per device on first use and
+// kept; the caller's stream waits for all of them, so a call stays asynchronous.
+constexpr int EIG_LANES = 4;
+
+struct EigLanes {
+    hipStream_t st[EIG_LANES];
+    hipEvent_t start, done[EIG_LANES];
+    std::mutex busy;  // held while one call enqueues, so the shared events are not re-recorded under it
+    bool ok = false;
+};
+
+static lrc_status eig_lanes(EigLanes **out) {
+    static std::mutex mu;
+    static std::map<int, EigLanes> lanes;
+    int devid = 0;
+    LRC_HIP(hipGetDevice(&devid));
+    std::lock_guard<std::mutex> lk(mu);
+    EigLanes &L = lanes[devid];
+    if (!L.ok) {
+        for (int i = 0; i < EIG_LANES; ++i) {
+            LRC_HIP(hipStreamCreateWithFlags(&L.st[i], hipStreamNonBlocking));
+            LRC_HIP(hipEventCreateWithFlags(&L.done[i], hipEventDisableTiming));
+        }
+        LRC_HIP(hipEventCreateWithFlags(&L.start, hipEventDisableTiming));
+        L.ok = true;
+    }
+    *out = &L;
     return LRC_OK;
+}
+
+// Workspace of a multi-group call: one region for the Jacobi groups (run one after another on the
+// caller's stream) followed by one region per lane, each sized for the largest n and n_vec among
+// the n > 128 groups (every field of the layout grows with n and n_vec).
+struct MultiPlan {
+    size_t jac = 0, per = 0;
+    int lanes = 0;
+    int64_t maxn = 0, maxnv = 0, members = 0;
+};
+
+static MultiPlan multi_plan(const EighArgs *g, int count, lrc_dtype prec) {
+    MultiPlan p;
+    for (int i = 0; i < count; ++i) {
+        if (g[i].n <= 128) {
+            p.jac = std::max(p.jac, jacobi_workspace(g[i].n, g[i].batch, prec));
+        } else {
+            p.maxn = std::max(p.maxn, g[i].n);
+            p.maxnv = std::max(p.maxnv, g[i].n_vec);
+            p.members += g[i].batch;
+        }
+    }
+    p.jac = align256(p.jac);
+    if (p.members > 0) {
+        p.lanes = int(std::min<int64_t>(p.members, EIG_LANES));
+        p.per = prec == LRC_F64 ? large_ws<double>(p.maxn, p.maxnv) : large_ws<float>(p.maxn, p.maxnv);
+    }
+    return p;
+}
+
+size_t eigh_multi_workspace(const EighArgs *g, int count, lrc_dtype prec) {
+    const MultiPlan p = multi_plan(g, count, prec);
+    return p.jac + size_t(p.lanes) * p.per;
 }
 
 size_t eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype prec) {
-    (void)batch;
-    if (n <= 128) return jacobi_workspace(n, batch, prec);
-    return prec == LRC_F64 ? large_ws<double>(n, n_vec) : large_ws<float>(n, n_vec);
+    EighArgs a{nullptr, n, n, batch, 0, prec, nullptr, nullptr, n_vec, n_vec, 0, nullptr};
+    return eigh_multi_workspace(&a, 1, prec);
 }
 
+struct EigMember {
+    const float *C;
+    int64_t ldc, n;
+    double *lambda;
+    float *V;
+    int64_t ldv, nv;
+    int32_t *info;
+};
+
+// All members with n > 128 over up to EIG_LANES helper streams, largest n first; a lane whose
+// member is done takes the next one (its stream runs in order, so the lane's workspace is free by
+// then).  The host feeds the lanes in turn, a few columns at a time.
 template <class T>
-static lrc_status large_run(const EighArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
-    Carver cv(ws, ws_bytes);
-    LargeWs<T> w;
-    layout(cv, w, a.n, a.n_vec, false);
-    if (!w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
-    for (int64_t b = 0; b < a.batch; ++b) {
-        lrc_status st = large_run_one<T>(a.C + b * a.stride_c, a.ldc, a.n, a.lambda + b * a.n,
-                                         a.V ? a.V + b * a.stride_v : nullptr, a.ldv, a.n_vec, a.info + b, w, s);
+static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, char *ws, hipStream_t s) {
+    std::stable_sort(mem.begin(), mem.end(), [](const EigMember &x, const EigMember &y) { return x.n > y.n; });
+    const int lanes = p.lanes;
+    LargeWs<T> w[EIG_LANES];
+    EigJob<T> job[EIG_LANES];
+    EigLanes *L = nullptr;
+    std::unique_lock<std::mutex> hold;
+    if (lanes > 1) {
+        lrc_status st = eig_lanes(&L);
         if (st != LRC_OK) return st;
+        hold = std::unique_lock<std::mutex>(L->busy);
+        LRC_HIP(hipEventRecord(L->start, s));
+        for (int l = 0; l < lanes; ++l) LRC_HIP(hipStreamWaitEvent(L->st[l], L->start, 0));
+    }
+    size_t next = 0;
+    auto begin = [&](int l) -> bool {
+        const EigMember &m = mem[next++];
+        Carver cv(ws + p.per * size_t(l), p.per);
+        w[l] = LargeWs<T>();
+        layout(cv, w[l], m.n, m.nv, false);
+        if (!w[l].bad) return false;
+        EigJob<T> &j = job[l];
+        j = EigJob<T>();
+        j.C = m.C;
+        j.ldc = m.ldc;
+        j.n = m.n;
+        j.lambda = m.lambda;
+        j.V = m.V;
+        j.ldv = m.ldv;
+        j.nv = m.nv;
+        j.info = m.info;
+        j.w = &w[l];
+        j.s = lanes > 1 ? L->st[l] : s;
+        return true;
+    };
+    for (int l = 0; l < lanes; ++l)
+        if (!begin(l)) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
+    for (int active = lanes; active > 0;) {
+        active = 0;
+        for (int l = 0; l < lanes; ++l) {
+            if (job[l].done()) {
+                if (next >= mem.size()) continue;
+                if (!begin(l)) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
+            }
+            lrc_status st = job[l].advance(8);
+            if (st != LRC_OK) return st;
+            ++active;
+        }
+    }
+    if (lanes > 1) {
+        for (int l = 0; l < lanes; ++l) {
+            LRC_HIP(hipEventRecord(L->done[l], L->st[l]));
+            LRC_HIP(hipStreamWaitEvent(s, L->done[l], 0));
+        }
     }
     return LRC_OK;
 }
 
+lrc_status eigh_multi_run(const EighArgs *g, int count, lrc_dtype prec, void *ws, size_t ws_bytes, hipStream_t s) {
+    for (int i = 0; i < count; ++i) {
+        if (g[i].n <= 128) continue;
+        if (g[i].n * int64_t(sizeof(double)) > 160 * 1024 && prec == LRC_F64)
+            return fail(LRC_ERR_UNIMPLEMENTED, "fp64 working precision supports n <= 20480");
+        if (g[i].n * int64_t(sizeof(float)) > 160 * 1024) return fail(LRC_ERR_UNIMPLEMENTED, "n > 40960");
+    }
+    const MultiPlan p = multi_plan(g, count, prec);
+    if (ws_bytes < p.jac + size_t(p.lanes) * p.per) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
+    for (int i = 0; i < count; ++i) {
+        if (g[i].n > 128) continue;
+        EighArgs a = g[i];
+        a.prec = prec;
+        lrc_status st = jacobi_run(a, ws, p.jac, s);
+        if (st != LRC_OK) return st;
+    }
+    if (p.members == 0) return LRC_OK;
+    std::vector<EigMember> mem;
+    mem.reserve(size_t(p.members));
+    for (int i = 0; i < count; ++i) {
+        const EighArgs &a = g[i];
+        if (a.n <= 128) continue;
+        for (int64_t b = 0; b < a.batch; ++b)
+            mem.push_back(EigMember{a.C + b * a.stride_c, a.ldc, a.n, a.lambda + b * a.n,
+                                    a.V ? a.V + b * a.stride_v : nullptr, a.ldv, a.n_vec, a.info + b});
+    }
+    char *lw = static_cast<char *>(ws) + p.jac;
+    return prec == LRC_F64 ? large_sched<double>(mem, p, lw, s) : large_sched<float>(mem, p, lw, s);
+}
+
 lrc_status eigh_run(const EighArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
-    if (a.n <= 128) return jacobi_run(a, ws, ws_bytes, s);
-    if (int64_t(a.n) * int64_t(sizeof(double)) > 160 * 1024 && a.prec == LRC_F64)
-        return fail(LRC_ERR_UNIMPLEMENTED, "fp64 working precision supports n <= 20480");
-    if (int64_t(a.n) * int64_t(sizeof(float)) > 160 * 1024) return fail(LRC_ERR_UNIMPLEMENTED, "n > 40960");
-    return a.prec == LRC_F64 ? large_run<double>(a, ws, ws_bytes, s) : large_run<float>(a, ws, ws_bytes, s);
+    return eigh_multi_run(&a, 1, a.prec, ws, ws_bytes, s);
 }
 
 }  // namespace lrc

@@ -121,6 +121,9 @@ struct EighArgs {
 };
 size_t eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype prec);
 lrc_status eigh_run(const EighArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
+// several groups in one call (prec overrides each group's own)
+size_t eigh_multi_workspace(const EighArgs *g, int count, lrc_dtype prec);
+lrc_status eigh_multi_run(const EighArgs *g, int count, lrc_dtype prec, void *ws, size_t ws_bytes, hipStream_t s);
 // small-n batched Jacobi (n <= 128)
 size_t jacobi_workspace(int64_t n, int64_t batch, lrc_dtype prec);
 lrc_status jacobi_run(const EighArgs &a, void *ws, size_t ws_bytes, hipStream_t s);

@@ -67,7 +67,8 @@ _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c
                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), _int)
 
 EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_accumulate_workspace",
-            "lrc_cov_accumulate", "lrc_eigh_workspace", "lrc_eigh", "lrc_error_curve", "lrc_factorize",
+            "lrc_cov_accumulate", "lrc_eigh_workspace", "lrc_eigh", "lrc_eigh_multi_workspace", "lrc_eigh_multi",
+            "lrc_error_curve", "lrc_factorize",
             "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_allocate_ranks_workspace",
             "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm_workspace", "lrc_trmm",
             "lrc_trsm_workspace", "lrc_trsm", "lrc_sym_to_f64", "lrc_to_f64", "lrc_gram_f64",
@@ -182,14 +183,22 @@ def lrc_eigh_workspace(n: int, batch: int, n_vec: int, prec: int = LRC_F32) -> i
     return _eigh_ws(n, batch, n_vec, prec)
 
 
-def lrc_eigh(C: torch.Tensor, n_vec: int, prec: int = LRC_F32, lam=None, V=None, info=None, ws=None, stream=None):
-    """Eigenpairs of the symmetric fp32 matrix (or batch) C, upper triangle read.
-    Returns (lambda fp64 (batch, n) descending, V fp32 (batch, n, n_vec), info int32 (batch,))."""
+class _EighGroup(ctypes.Structure):
+    """struct lrc_eigh_group of include/lrc.h."""
+    _fields_ = [("C", _vp), ("n", _i64), ("ldc", _i64), ("batch", _i64), ("stride_c", _i64), ("lambda_", _vp),
+                ("V", _vp), ("ldv", _i64), ("n_vec", _i64), ("stride_v", _i64), ("info", _vp)]
+
+
+_eigh_mws = _sig("lrc_eigh_multi_workspace", _sz, ctypes.POINTER(_EighGroup), _i32, _int)
+_eigh_m = _sig("lrc_eigh_multi", _int, ctypes.POINTER(_EighGroup), _i32, _int, _vp, _sz, _vp)
+
+
+def _eigh_args(C, n_vec, lam, V, info):
+    """Marshals one lrc_eigh call: (struct, squeeze flag, lam, V, info)."""
     ldc = _rows(C, "C")
     squeeze = C.dim() == 2
     Cb = C.unsqueeze(0) if squeeze else C
     batch, n = Cb.shape[0], Cb.shape[1]
-    stride_c = Cb.stride(0)
     dev = C.device
     if lam is None:
         lam = torch.empty(batch, n, dtype=torch.float64, device=dev)
@@ -197,14 +206,50 @@ def lrc_eigh(C: torch.Tensor, n_vec: int, prec: int = LRC_F32, lam=None, V=None,
         V = torch.empty(batch, n, n_vec, dtype=torch.float32, device=dev)
     ldv = _rows(V, "V") if V is not None else max(n_vec, 1)
     stride_v = (V.stride(0) if V.dim() == 3 else 0) if V is not None else 0
-    nbytes = lrc_eigh_workspace(n, batch, n_vec, prec)
-    w, wn = _workspace(nbytes, dev, ws)
     info = _info(info, batch, dev)
-    _check(_eigh(_ptr(C), n, ldc, batch, stride_c, prec, _ptr(lam), _ptr(V), ldv, n_vec, stride_v, _ptr(w), wn,
-                 _ptr(info), _stream(stream)))
+    g = _EighGroup(_ptr(C), n, ldc, batch, Cb.stride(0), _ptr(lam), _ptr(V), ldv, n_vec, stride_v, _ptr(info))
+    return g, squeeze, lam, V, info
+
+
+def _eigh_out(squeeze, lam, V, info):
     if squeeze:
         return lam[0], (V[0] if V is not None else None), info
     return lam, V, info
+
+
+def lrc_eigh(C: torch.Tensor, n_vec: int, prec: int = LRC_F32, lam=None, V=None, info=None, ws=None, stream=None):
+    """Eigenpairs of the symmetric fp32 matrix (or batch) C, upper triangle read.
+    Returns (lambda fp64 (batch, n) descending, V fp32 (batch, n, n_vec), info int32 (batch,))."""
+    g, squeeze, lam, V, info = _eigh_args(C, n_vec, lam, V, info)
+    nbytes = lrc_eigh_workspace(g.n, g.batch, n_vec, prec)
+    w, wn = _workspace(nbytes, C.device, ws)
+    _check(_eigh(g.C, g.n, g.ldc, g.batch, g.stride_c, prec, g.lambda_, g.V, g.ldv, n_vec, g.stride_v, _ptr(w), wn,
+                 g.info, _stream(stream)))
+    return _eigh_out(squeeze, lam, V, info)
+
+
+def lrc_eigh_multi_workspace(groups, prec: int = LRC_F32) -> int:
+    """groups: sequence of (n, batch, n_vec)."""
+    arr = (_EighGroup * len(groups))(*[_EighGroup(None, n, n, b, 0, None, None, nv, nv, 0, None)
+                                      for n, b, nv in groups])
+    return _eigh_mws(arr, len(groups), prec)
+
+
+def lrc_eigh_multi(groups, prec: int = LRC_F32, ws=None, stream=None):
+    """Several lrc_eigh calls in one.  groups: sequence of (C, n_vec) or (C, n_vec, lam, V, info)
+    with the meaning of lrc_eigh's arguments.  Returns a list of (lambda, V, info) per group."""
+    parts = []
+    for grp in groups:
+        C, n_vec = grp[0], grp[1]
+        lam, V, info = (tuple(grp[2:5]) + (None, None, None))[:3]
+        parts.append(_eigh_args(C, n_vec, lam, V, info))
+    if not parts:
+        raise ValueError("lrc_eigh_multi needs at least one group")
+    arr = (_EighGroup * len(parts))(*[p[0] for p in parts])
+    nbytes = _eigh_mws(arr, len(parts), prec)
+    w, wn = _workspace(nbytes, groups[0][0].device, ws)
+    _check(_eigh_m(arr, len(parts), prec, _ptr(w), wn, _stream(stream)))
+    return [_eigh_out(*p[1:]) for p in parts]
 
 
 def lrc_error_curve(lam: torch.Tensor, eps=None, stream=None) -> torch.Tensor:

@@ -141,6 +141,11 @@ lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64
  *    n <= 128: one-sided Jacobi, one matrix per workgroup held in LDS, in prec.
  *    n > 128: Householder tridiagonalisation and back-transformation in prec; the
  *    tridiagonal eigenproblem (bisection, inverse iteration) always in fp64.
+ * Batches with n > 128: up to four members are decomposed at once, each on a helper
+ *    stream of the library's (default priority, created per device on first use and kept
+ *    until the process ends) with a workspace of its own; the call returns at once and
+ *    the caller's stream waits for every member, so results are ordered on `stream` as
+ *    for any other call.  Each member's result does not depend on the batch it is in.
  * info: batch int32: 2 when the Jacobi sweeps did not converge, 1 for non-finite input.
  * Errors: LRC_ERR_ARG (sizes, strides, n_vec > n), LRC_ERR_DTYPE (prec), LRC_ERR_WORKSPACE.
  * ------------------------------------------------------------------------------------ */
@@ -148,6 +153,36 @@ size_t lrc_eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype pre
 lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64_t stride_c,
                     lrc_dtype prec, double *lambda, float *V, int64_t ldv, int64_t n_vec,
                     int64_t stride_v, void *ws, size_t ws_bytes, int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Several eigendecompositions in one call (the operation of lrc_eigh, on each group).
+ *
+ * A block of a network has matrices of several widths (4096 and 11008 wide covariances in
+ * a LLaMA-7B block); one call over all of them lets the library run the matrices of
+ * different widths at the same time, which separate calls cannot (each call returns only
+ * after it has handed all of its launches to the GPU).
+ * groups[i]: the arguments of one lrc_eigh call (same meaning, layout and checks); all
+ *    groups use the working precision prec.  Groups must not overlap in lambda, V, info.
+ * Groups with n <= 128 run first, one Jacobi launch each, on `stream`; every member of
+ *    the groups with n > 128 is then decomposed on the helper streams described under
+ *    lrc_eigh, up to four at once, largest n first.  `stream` waits for all of them.
+ *    Each member's result equals that of lrc_eigh on the member alone, bit for bit.
+ * ws: lrc_eigh_multi_workspace(groups, count, prec) bytes, 256-byte aligned (one region
+ *    per concurrent member, each sized for the largest n and n_vec among the groups).
+ * Errors: those of lrc_eigh, for the first group that fails a check; LRC_ERR_ARG for a
+ *    NULL groups or count <= 0.  The workspace query returns 0 for invalid sizes.
+ * ------------------------------------------------------------------------------------ */
+typedef struct lrc_eigh_group {
+    const float *C;
+    int64_t n, ldc, batch, stride_c;
+    double *lambda;
+    float *V;
+    int64_t ldv, n_vec, stride_v;
+    int32_t *info;
+} lrc_eigh_group;
+size_t lrc_eigh_multi_workspace(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec);
+lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec, void *ws,
+                          size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------------
  * Error curve (Swift-SVD page, section 2-ga: the closed-form minimal error eps*_k).

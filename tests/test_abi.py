@@ -24,7 +24,7 @@ def lib():
     return ctypes.CDLL(LIB)
 
 
-def test_header_declares_the_north_star_entry_points():
+def test_header_declares_the_six_path_entry_points():
     d = declared()
     for name in ("lrc_cov_accumulate", "lrc_eigh", "lrc_factorize", "lrc_error_curve", "lrc_fisher_scores",
                  "lrc_allocate_ranks"):
@@ -103,6 +103,17 @@ def test_argument_errors_are_synchronous():
     assert lrc._to64(fake, 0, 4, 4, 3, 1.0, fake, 4, None) == 1
     assert lrc._sym64(fake, 8, 7, 1.0, fake, 8, None) == 1
     assert lrc._gram64(fake, 8, 4, 4, fake, 7, None) == 1
+    # eigh_multi: NULL groups, count 0, a group with n_vec > n, bad prec, small workspace
+    G = lrc._EighGroup
+    assert lrc._eigh_m(None, 1, 1, None, 0, None) == 1
+    ok = G(256, 300, 300, 2, 90000, 256, 256, 8, 8, 2400, 256)
+    bad = G(256, 300, 300, 1, 0, 256, 256, 8, 301, 0, 256)
+    arr = (G * 2)(ok, bad)
+    assert lrc._eigh_m(arr, 0, 1, None, 0, None) == 1
+    assert lrc._eigh_m(arr, 2, 1, fake, 1 << 40, None) == 1 and "n_vec" in lrc.lrc_last_error()
+    assert lrc._eigh_m(arr, 1, 7, fake, 1 << 40, None) == 2
+    need = lrc._eigh_mws(arr, 1, 1)
+    assert lrc._eigh_m(arr, 1, 1, fake, need - 1, None) == 3
 
 
 def test_workspace_queries_are_consistent():
@@ -112,4 +123,16 @@ def test_workspace_queries_are_consistent():
     assert 0 < a < b
     assert lrc.lrc_eigh_workspace(4096, 1, 1228, 1) > lrc.lrc_eigh_workspace(4096, 1, 0, 1)
     assert lrc.lrc_eigh_workspace(128, 32, 32, 2) == 0  # Jacobi keeps everything in LDS
+    # batched members run up to four at a time, each with a region of its own
+    one = lrc.lrc_eigh_workspace(4096, 1, 1228, 1)
+    assert lrc.lrc_eigh_workspace(4096, 3, 1228, 1) == 3 * one
+    assert lrc.lrc_eigh_workspace(4096, 9, 1228, 1) == 4 * one
+    # several groups: as many regions as concurrent members, each sized for the largest group
+    assert lrc.lrc_eigh_multi_workspace([(4096, 3, 1228)], 1) == 3 * one
+    big = lrc.lrc_eigh_workspace(11008, 1, 1791, 1)
+    assert lrc.lrc_eigh_multi_workspace([(4096, 5, 1228), (11008, 2, 1791), (128, 32, 32)], 1) == 4 * big
+    # the largest n and the largest n_vec may come from different groups
+    assert lrc.lrc_eigh_multi_workspace([(4096, 1, 1791), (11008, 1, 1228)], 1) == 2 * big
+    assert lrc.lrc_eigh_multi_workspace([(64, 4, 8)], 2) == 0
+    assert lrc.lrc_eigh_multi_workspace([(64, 4, 65)], 2) == 0
     assert lrc.lrc_allocate_ranks_workspace(224, 548704) > 548704 * 8

@@ -195,6 +195,64 @@ def test_eigh_jacobi_vs_oracle(lrc, n, batch, prec):
         assert s <= lim, (b, s, gap(lam_r, k))
 
 
+@pytest.mark.parametrize("prec", [1, 2])
+def test_eigh_large_batch_matches_single_calls(lrc, prec):
+    """Members of a batch (n > 128) run concurrently on helper streams, several at a time, each
+    with a workspace of its own; every member must equal the same matrix decomposed alone, bit for
+    bit, and a non-finite member flags only itself."""
+    _say("eigh large batch of 6 (n = 300, more members than helper streams) prec %d" % prec)
+    n, batch, nv = 300, 6, 40
+    X = inputs.block_activations(320, 4096)
+    Cs = []
+    for b in range(batch):
+        W = inputs.weight(320, n, "bf16", inputs.CFG_BLOCK, 0, 10 + b)
+        Cs.append(oracle.covariance(X, "bf16", W, "bf16").astype(np.float32))
+    Cs[4][2, 9] = np.nan
+    Cb = dev(np.stack(Cs), "f32")
+    lam, V, info = lrc.lrc_eigh(Cb, n_vec=nv, prec=prec)
+    lam, V, info = host(lam), host(V), host(info)
+    assert list(info) == [0, 0, 0, 0, 1, 0]
+    for b in (0, 1, 2, 3, 5):
+        l1, V1, i1 = lrc.lrc_eigh(dev(Cs[b], "f32"), n_vec=nv, prec=prec)
+        assert int(host(i1)[0]) == 0
+        assert np.array_equal(lam[b], host(l1)), b
+        assert np.array_equal(V[b], host(V1)), b
+    lam_r, V_r = oracle.eigh(Cs[5].astype(np.float64))
+    check_lambda(lam[5], lam_r)
+    assert sin_theta_max(V[5], V_r, 20) <= 1e-3
+
+
+@pytest.mark.parametrize("prec", [1, 2])
+def test_eigh_multi_matches_single_calls(lrc, prec):
+    """Groups of different n in one call: the n > 128 members share the helper streams (here more
+    members than streams, so a stream goes on from a larger matrix to a smaller one in the same
+    workspace region) and the Jacobi group runs on the caller's stream; every member must equal
+    lrc_eigh on that member alone, bit for bit."""
+    _say("eigh multi: 1 x 513, 2 x 300, 3 x 200 and a Jacobi group 2 x 64, prec %d" % prec)
+    X = inputs.block_activations(320, 4096)
+    spec = [(300, 2, 40), (200, 3, 64), (64, 2, 16), (513, 1, 10)]
+    groups, mats = [], []
+    for gi, (n, b, nv) in enumerate(spec):
+        Cs = []
+        for m in range(b):
+            W = inputs.weight(320, n, "bf16", inputs.CFG_BLOCK, 0, 20 + 4 * gi + m)
+            Cs.append(oracle.covariance(X, "bf16", W, "bf16").astype(np.float32))
+        mats.append(Cs)
+        groups.append((dev(np.stack(Cs), "f32"), nv))
+    out = lrc.lrc_eigh_multi(groups, prec=prec)
+    for (n, b, nv), Cs, (lam, V, info) in zip(spec, mats, out):
+        lam, V, info = host(lam), host(V), host(info)
+        assert np.all(info == 0)
+        for m in range(b):
+            l1, V1, i1 = lrc.lrc_eigh(dev(Cs[m], "f32"), n_vec=nv, prec=prec)
+            assert int(host(i1)[0]) == 0
+            assert np.array_equal(lam[m], host(l1)), (n, m)
+            assert np.array_equal(V[m], host(V1)), (n, m)
+    lam_r, V_r = oracle.eigh(mats[3][0].astype(np.float64))
+    check_lambda(host(out[3][0])[0], lam_r)
+    assert sin_theta_max(host(out[3][1])[0], V_r, 10) <= 1e-3
+
+
 def test_eigh_nonfinite_sets_info(lrc):
     C = np.eye(200, dtype=np.float32)
     C[3, 7] = np.inf
