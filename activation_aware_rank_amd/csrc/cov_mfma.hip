@@ -62,7 +62,13 @@ struct MfmaCfg {
 // errors are not one-signed).
 // DEPTH: k steps of global loads in flight (1: the next step; 2: the next two, in two register
 // sets used alternately -- the k loop is unrolled by two so that every index is static).
-template <int BM, int THREADS, int WGM, int NOPS, int NPROD, bool FLUSH, int FE = 1, bool KCHECK = true, int DEPTH = 1>
+// NOBRANCH: the loads of step kt + DEPTH and the LDS store of step kt + 1 are issued in every
+// step, also past the last one (those loads read zeros or unused values and those stores go to
+// the buffer no wave reads any more).  With no branch around them the compiler counts the loads
+// in flight exactly and waits only for the older register set before storing it; behind a
+// branch it also waits for the loads just issued, which leaves one step of latency hiding.
+template <int BM, int THREADS, int WGM, int NOPS, int NPROD, bool FLUSH, int FE = 1, bool KCHECK = true, int DEPTH = 1,
+          bool NOBRANCH = false>
 __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const int64_t *ld, const int *rows,
                                               int64_t klen,
                                               f32x16_t (&acc)[MfmaCfg<BM, THREADS, WGM>::TM][MfmaCfg<BM, THREADS, WGM>::TN],
@@ -74,14 +80,16 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
     const int wm = wave / T::WGN, wn = wave % T::WGN;
     const int nk = int((klen + MK - 1) / MK);
     u32x4_t regs[DEPTH][NOPS][U];
-    // One buffer resource per operand covering its rows[o] rows: a load past them returns zero
-    // without a branch.  Offsets are 32-bit byte offsets from the operand's first row (the host
-    // keeps rows * ld * 2 below 2^31).
+    // One buffer resource per operand, ending at element klen - 1 of its last row: a load past
+    // that returns zero without a branch (and never touches memory after the operand).  Offsets
+    // are 32-bit byte offsets from the operand's first row (the host keeps rows * ld * 2 below
+    // 2^31).
     __amdgpu_buffer_rsrc_t rs[NOPS];
 #pragma unroll
     for (int o = 0; o < NOPS; ++o)
-        rs[o] = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base[o]), short(0),
-                                                  int(int64_t(rows[o]) * ld[o] * 2), 0x00020000);
+        rs[o] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t *>(base[o]), short(0),
+            int(rows[o] > 0 ? ((int64_t(rows[o]) - 1) * ld[o] + klen) * 2 : int64_t(0)), 0x00020000);
 
     auto gload = [&](int kt, auto set) {
         constexpr int S = decltype(set)::value;
@@ -131,7 +139,7 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
     gload(0, I0{});
     sstore(0, I0{});
     if constexpr (DEPTH == 2) {
-        if (nk > 1) gload(1, I1{});
+        if (NOBRANCH || nk > 1) gload(1, I1{});
     }
     __syncthreads();
     constexpr int NA = (NPROD == 4) ? 2 : 1;
@@ -140,7 +148,9 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
     // par: the step's position in the unrolled pair (static); with FE 4 a flush group is the pair
     auto step = [&](int kt, int cur, auto lset, auto sset, auto par) {
         constexpr int PAR = decltype(par)::value;
-        if (kt + DEPTH < nk) gload(kt + DEPTH, lset);
+        if (NOBRANCH || kt + DEPTH < nk) gload(kt + DEPTH, lset);
+        // keep the loads at the top of the step, ahead of this step's MFMAs
+        if constexpr (NOBRANCH) __builtin_amdgcn_sched_barrier(0);
         const bf16_t *sb = lds + cur * NOPS * OPSZ;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -177,18 +187,24 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
             if (FLUSH && FE == 1) flush();
         }
         if (FLUSH && (FE == 2 || (FE == 4 && PAR == 1))) flush();
-        if (kt + 1 < nk) sstore(cur ^ 1, sset);
+        if (NOBRANCH || kt + 1 < nk) sstore(cur ^ 1, sset);
         __syncthreads();
     };
     static_assert(FE != 4 || DEPTH == 2, "a 64-token flush group needs the unrolled pair");
     if constexpr (DEPTH == 1) {
         for (int kt = 0; kt < nk; ++kt) step(kt, kt & 1, I0{}, I0{}, I0{});
     } else {
-        for (int kt = 0; kt < nk; kt += 2) {
+        // pairs of steps, then a lone last step when nk is odd (outside the loop, so that no path
+        // through the loop body skips a step and the compiler's count of loads in flight stays exact)
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
             step(kt, 0, I0{}, I1{}, I0{});
-            if (kt + 1 < nk) step(kt + 1, 1, I1{}, I0{}, I1{});
+            step(kt + 1, 1, I1{}, I0{}, I1{});
         }
-        if (FLUSH && FE == 4 && (nk & 1)) flush();  // the last group had only its first step
+        if (kt < nk) {
+            step(kt, 0, I0{}, I1{}, I0{});
+            if (FLUSH && FE == 4) flush();  // the last group had only its first step
+        }
     }
 }
 
@@ -293,7 +309,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
     // klen is a multiple of MK here, so no k check is needed
-    mfma_mainloop<BM, THREADS, WGM, NOPS, NPROD, true, SYRK_FE, false, SYRK_DEPTH>(base, ld, rows, klen, acc, lds);
+    mfma_mainloop<BM, THREADS, WGM, NOPS, NPROD, true, SYRK_FE, false, SYRK_DEPTH, true>(base, ld, rows, klen, acc, lds);
     float *dst;
     int64_t ldd;
     if (s == 0) {
