@@ -3,7 +3,9 @@
 // Per chunk of tokens (Swift-SVD page, section 2-ga: C is aggregated over the calibration
 // tokens, one chunk at a time):
 //   1. GEMM  Y^T[i][t] = sum_k W^T[i][k] X[t][k]        (bf16 MFMA, fp32 accumulation)
-//      epilogue: hi = bf16(y), lo = bf16(y - hi), stored token-contiguous.
+//      epilogue: hi = bf16(y), lo = bf16(y - hi), stored in blocks of MK tokens:
+//      Y^T[i][t] at ((t / MK) * D + i) * MK + t % MK (D = d_out), so that the MK-token slice of
+//      consecutive rows that one k step of the SYRK reads is one contiguous run.
 //   2. SYRK  C[I,J] += (Yhi_I + Ylo_I)(Yhi_J + Ylo_J)^T as four bf16 MFMA products, fp32
 //      accumulation, for tiles I <= J.  All four are needed: dropping lo*lo would lower every
 //      quadratic form v^T C v by ||Ylo v||^2 (about 2e-6 of the diagonal, always one-signed),
@@ -43,14 +45,17 @@ constexpr int64_t MFMA_CHUNK = 32768;    // tokens per internal chunk
 // column hit 16 distinct 16-byte bank groups (and 8 consecutive rows 8 distinct groups)
 __device__ __forceinline__ int swz(int r, int c) { return r * MK + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 3); }
 
-// Block tile BM x BM, THREADS/64 waves arranged WGM x WGN, wave tile (BM/WGM) x (BM/WGN).
-template <int BM, int THREADS, int WGM>
+// Block tile BM x BN (BM rows of the A operands, BN rows of the B operands), THREADS/64 waves
+// arranged WGM x WGN, wave tile (BM/WGM) x (BN/WGN).
+template <int BM, int BN, int THREADS, int WGM>
 struct MfmaCfg {
     static constexpr int WAVES = THREADS / 64;
     static constexpr int WGN = WAVES / WGM;
-    static constexpr int WM = BM / WGM, WN = BM / WGN;  // wave tile
+    static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
     static constexpr int TM = WM / 32, TN = WN / 32;    // 32x32 MFMA tiles per wave
-    static constexpr int U = BM * (MK / 8) / THREADS;   // 16-byte chunks per thread per operand
+    static constexpr int UA = BM * (MK / 8) / THREADS;  // 16-byte chunks per thread of an A operand
+    static constexpr int UB = BN * (MK / 8) / THREADS;  // ... of a B operand
+    static_assert(UA * THREADS == BM * (MK / 8) && UB * THREADS == BN * (MK / 8), "operand tile / threads");
 };
 
 // acc[tm][tn] += sum over k in [0, klen) of A[row][k] B[col][k]; ops: {A(,Alo), B(,Blo)}.
@@ -62,20 +67,32 @@ struct MfmaCfg {
 // errors are not one-signed).
 // DEPTH: k steps of global loads in flight (1: the next step; 2: the next two, in two register
 // sets used alternately -- the k loop is unrolled by two so that every index is static).
+// TILED: the operands are in the MK-token block layout of Y^T (ld = rows per token block, D):
+// row r of step kt is at (kt * D + r) * MK; operand o's buffer resource covers nrec[o] < 2^31
+// bytes from its base.  Rows past rows[o] (those of the next head block) read zero: their byte
+// offsets start at 2^31, past every resource, so the mask costs no wait on the loaded data.  In
+// the row-major layout a k step reads 64 bytes of each of 16 rows per wave instruction; in the
+// block layout it reads 1 KB in one run, which halves the cache lines the loads touch.
 // NOBRANCH: the loads of step kt + DEPTH and the LDS store of step kt + 1 are issued in every
 // step, also past the last one (those loads read zeros or unused values and those stores go to
 // the buffer no wave reads any more).  With no branch around them the compiler counts the loads
 // in flight exactly and waits only for the older register set before storing it; behind a
 // branch it also waits for the loads just issued, which leaves one step of latency hiding.
-template <int BM, int THREADS, int WGM, int NOPS, int NPROD, bool FLUSH, int FE = 1, bool KCHECK = true, int DEPTH = 1,
-          bool NOBRANCH = false>
-__device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const int64_t *ld, const int *rows,
-                                              int64_t klen,
-                                              f32x16_t (&acc)[MfmaCfg<BM, THREADS, WGM>::TM][MfmaCfg<BM, THREADS, WGM>::TN],
-                                              bf16_t *lds) {
-    using T = MfmaCfg<BM, THREADS, WGM>;
-    constexpr int TM = T::TM, TN = T::TN, U = T::U;
-    constexpr int OPSZ = BM * MK;  // elements of one operand tile
+// Operands 0 .. NOPS/2-1 are A operands (BM rows), the rest B operands (BN rows); LDS holds two
+// buffers of NOPS/2 * (BM + BN) rows of MK elements.
+template <int BM, int BN, int THREADS, int WGM, int NOPS, int NPROD, bool FLUSH, int FE = 1, bool KCHECK = true,
+          int DEPTH = 1, bool NOBRANCH = false, bool TILED = false>
+__device__ __forceinline__ void mfma_mainloop(
+    const bf16_t *const *base, const int64_t *ld, const int *rows, int64_t klen, const int64_t *nrec,
+    f32x16_t (&acc)[MfmaCfg<BM, BN, THREADS, WGM>::TM][MfmaCfg<BM, BN, THREADS, WGM>::TN], bf16_t *lds) {
+    using T = MfmaCfg<BM, BN, THREADS, WGM>;
+    constexpr int TM = T::TM, TN = T::TN, UA = T::UA, UB = T::UB;
+    constexpr int U = UA > UB ? UA : UB;
+    constexpr int NSIDE = NOPS / 2;
+    static_assert(NSIDE * 2 == NOPS, "as many A as B operands");
+    // element offset of operand o inside one LDS buffer, and the buffer size
+    auto opoff = [](int o) { return o < NSIDE ? o * BM * MK : NSIDE * BM * MK + (o - NSIDE) * BN * MK; };
+    constexpr int BUFSZ = NSIDE * (BM + BN) * MK;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / T::WGN, wn = wave % T::WGN;
     const int nk = int((klen + MK - 1) / MK);
@@ -89,19 +106,37 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
     for (int o = 0; o < NOPS; ++o)
         rs[o] = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<bf16_t *>(base[o]), short(0),
-            int(rows[o] > 0 ? ((int64_t(rows[o]) - 1) * ld[o] + klen) * 2 : int64_t(0)), 0x00020000);
+            int(TILED ? nrec[o] : rows[o] > 0 ? ((int64_t(rows[o]) - 1) * ld[o] + klen) * 2 : int64_t(0)), 0x00020000);
 
+    // TILED: per operand and chunk, the byte offset of its row at step 0 (2^31 for masked rows)
+    uint32_t roff[NOPS][U];
+    if constexpr (TILED) {
+#pragma unroll
+        for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+            for (int u = 0; u < (o < NSIDE ? UA : UB); ++u) {
+                const int q = tid + THREADS * u;
+                const int r = q >> 2, c = q & 3;
+                roff[o][u] = r < rows[o] ? uint32_t((r * MK + c * 8) * 2) : 0x80000000u;
+            }
+    }
     auto gload = [&](int kt, auto set) {
         constexpr int S = decltype(set)::value;
         const int k0 = kt * MK;
 #pragma unroll
         for (int o = 0; o < NOPS; ++o)
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < (o < NSIDE ? UA : UB); ++u) {
                 const int q = tid + THREADS * u;
                 const int r = q >> 2, c = q & 3;
                 const int k = k0 + c * 8;
-                u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs[o], (r * int(ld[o]) + k) * 2, 0, 0);
+                u32x4_t v;
+                if constexpr (TILED) {
+                    const uint32_t off = roff[o][u] + uint32_t(kt) * uint32_t(ld[o] * MK * 2);
+                    v = __builtin_amdgcn_raw_buffer_load_b128(rs[o], int(off), 0, 0);
+                } else {
+                    v = __builtin_amdgcn_raw_buffer_load_b128(rs[o], (r * int(ld[o]) + k) * 2, 0, 0);
+                }
                 if (KCHECK && k >= klen) v = u32x4_t{0u, 0u, 0u, 0u};
                 regs[S][o][u] = v;
             }
@@ -111,10 +146,10 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
 #pragma unroll
         for (int o = 0; o < NOPS; ++o)
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < (o < NSIDE ? UA : UB); ++u) {
                 const int q = tid + THREADS * u;
                 const int r = q >> 2, c = q & 3;
-                *reinterpret_cast<u32x4_t *>(lds + (buf * NOPS + o) * OPSZ + swz(r, c)) = regs[S][o][u];
+                *reinterpret_cast<u32x4_t *>(lds + buf * BUFSZ + opoff(o) + swz(r, c)) = regs[S][o][u];
             }
     };
 
@@ -151,7 +186,7 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
         if (NOBRANCH || kt + DEPTH < nk) gload(kt + DEPTH, lset);
         // keep the loads at the top of the step, ahead of this step's MFMAs
         if constexpr (NOBRANCH) __builtin_amdgcn_sched_barrier(0);
-        const bf16_t *sb = lds + cur * NOPS * OPSZ;
+        const bf16_t *sb = lds + cur * BUFSZ;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int c = ks * 2 + (lane >> 5);
@@ -160,10 +195,11 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
             for (int a = 0; a < NA; ++a) {
 #pragma unroll
                 for (int t = 0; t < TM; ++t)
-                    af[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + a * OPSZ + swz(wm * T::WM + t * 32 + (lane & 31), c));
+                    af[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + opoff(a) +
+                                                                   swz(wm * T::WM + t * 32 + (lane & 31), c));
 #pragma unroll
                 for (int t = 0; t < TN; ++t)
-                    bfr[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + (NA + a) * OPSZ +
+                    bfr[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + opoff(NSIDE + a) +
                                                                     swz(wn * T::WN + t * 32 + (lane & 31), c));
             }
 #pragma unroll
@@ -212,17 +248,19 @@ __device__ __forceinline__ void mfma_mainloop(const bf16_t *const *base, const i
 __device__ __forceinline__ int acc_row(int lane, int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
-// Y^T[ib + row][t] for the 16 values of one lane: hi = bf16(y), lo = bf16(y - hi)
+// Y^T[ib + row][t] for the 16 values of one lane, in the MK-token block layout: hi = bf16(y),
+// lo = bf16(y - hi)
 __device__ __forceinline__ void store_split_tile(const f32x16_t a, int64_t ib, int64_t t, int lane, int64_t d_out,
-                                                 bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo, int64_t ldy) {
+                                                 bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo) {
+    const int64_t tb = (t / MK) * d_out * MK + t % MK;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int64_t i = ib + acc_row(lane, r);
         if (i < d_out) {
             const float y = a[r];
             const bf16_t hi = f32_to_bf16(y);
-            Yhi[i * ldy + t] = hi;
-            Ylo[i * ldy + t] = f32_to_bf16(y - bf16_to_f32(hi));
+            Yhi[tb + i * MK] = hi;
+            Ylo[tb + i * MK] = f32_to_bf16(y - bf16_to_f32(hi));
         }
     }
 }
@@ -242,8 +280,8 @@ constexpr int G_BM = 256, G_THREADS = 256, G_WGM = 2;
 template <int BM, bool KCHECK>
 __global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const bf16_t *__restrict__ X, int64_t ldx,
-             int64_t tc, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo, int64_t ldy) {
-    using Cfg = MfmaCfg<BM, G_THREADS, G_WGM>;
+             int64_t tc, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo) {
+    using Cfg = MfmaCfg<BM, BM, G_THREADS, G_WGM>;
     __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * BM * MK];
     const int64_t i0 = int64_t(blockIdx.x) * BM, t0 = int64_t(blockIdx.y) * BM;
     const bf16_t *base[2] = {Wt + i0 * d_in, X + t0 * ldx};
@@ -254,7 +292,7 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
     for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
-    mfma_mainloop<BM, G_THREADS, G_WGM, 2, 1, false, 1, KCHECK>(base, ld, rows, d_in, acc, lds);
+    mfma_mainloop<BM, BM, G_THREADS, G_WGM, 2, 1, false, 1, KCHECK>(base, ld, rows, d_in, nullptr, acc, lds);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm)
@@ -262,54 +300,91 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
         for (int tn = 0; tn < Cfg::TN; ++tn) {
             const int64_t ib = i0 + wm * Cfg::WM + tm * 32;
             const int64_t t = t0 + wn * Cfg::WN + tn * 32 + acc_col(lane);
-            store_split_tile(acc[tm][tn], ib, t, lane, d_out, Yhi, Ylo, ldy);
+            store_split_tile(acc[tm][tn], ib, t, lane, d_out, Yhi, Ylo);
         }
 }
 
-// Phase 2: upper tiles of each head block, split s of the token range.
-template <int BM>
-struct SyrkCfg {  // 4 waves of (BM/2) x (BM/2)
+// Phase 2: block tiles of each head block that meet its upper triangle, split s of the token
+// range.  A tile is BM rows (block row I) by BN columns (block column J); it meets the upper
+// triangle when its last column is at or right of its first row.  Tiles are numbered column
+// by column: column J holds syrk_col_tiles(J) tiles, I = 0, 1, ...
+template <int BM, int BN>
+__host__ __device__ __forceinline__ int syrk_col_tiles(int J, int nI) {
+    return min(nI, (BN * J + BN - 1) / BM + 1);
+}
+template <int BM, int BN>
+__host__ __device__ __forceinline__ int syrk_tiles(int hd) {
+    const int nI = (hd + BM - 1) / BM, nJ = (hd + BN - 1) / BN;
+    int n = 0;
+    for (int J = 0; J < nJ; ++J) n += syrk_col_tiles<BM, BN>(J, nI);
+    return n;
+}
+template <int BM, int BN>
+struct SyrkCfg {  // 4 waves of (BM/2) x (BN/2)
     static constexpr int THREADS = 256;
     static constexpr int WGM = 2;
 };
-template <int BM, int NPROD>
-__global__ void __launch_bounds__(SyrkCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(SYRK_WPE, SYRK_WPE)))
+template <int BM, int BN, int NPROD>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SYRK_WPE, SYRK_WPE)))
 k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64_t ldy, int64_t ktot, int64_t kchunk,
            int64_t hd, float *__restrict__ C, int64_t ldc, float *__restrict__ P, int32_t n_blocks) {
-    constexpr int THREADS = SyrkCfg<BM>::THREADS, WGM = SyrkCfg<BM>::WGM;
-    using Cfg = MfmaCfg<BM, THREADS, WGM>;
+    constexpr int THREADS = SyrkCfg<BM, BN>::THREADS, WGM = SyrkCfg<BM, BN>::WGM;
+    static_assert(THREADS == 256, "launch bounds");
+    using Cfg = MfmaCfg<BM, BN, THREADS, WGM>;
     constexpr int NOPS = (NPROD == 4) ? 4 : 2;
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * NOPS * BM * MK];
+    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (NOPS / 2) * (BM + BN) * MK];
     const int u = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-    int J = int((sqrtf(8.f * float(u) + 1.f) - 1.f) * 0.5f);
-    while (J * (J + 1) / 2 > u) --J;
-    while ((J + 1) * (J + 2) / 2 <= u) ++J;
-    const int I = u - J * (J + 1) / 2;
+    int I, J;
+    if constexpr (BM == BN) {  // column J holds J + 1 tiles: closed form
+        J = int((sqrtf(8.f * float(u) + 1.f) - 1.f) * 0.5f);
+        while (J * (J + 1) / 2 > u) --J;
+        while ((J + 1) * (J + 2) / 2 <= u) ++J;
+        I = u - J * (J + 1) / 2;
+    } else {
+        const int nI = int((hd + BM - 1) / BM);
+        int rem = u;
+        J = 0;
+        while (rem >= syrk_col_tiles<BM, BN>(J, nI)) rem -= syrk_col_tiles<BM, BN>(J++, nI);
+        I = rem;
+    }
     const int64_t kb = int64_t(s) * kchunk;
     const int64_t klen = std::min(kchunk, ktot - kb);
     if (klen <= 0) return;
-    const int64_t r0 = int64_t(h) * hd + int64_t(I) * BM, c0 = int64_t(h) * hd + int64_t(J) * BM;
+    const int64_t r0 = int64_t(h) * hd + int64_t(I) * BM, c0 = int64_t(h) * hd + int64_t(J) * BN;
     const int rowsI = int(std::min<int64_t>(BM, hd - int64_t(I) * BM));
-    const int rowsJ = int(std::min<int64_t>(BM, hd - int64_t(J) * BM));
+    const int rowsJ = int(std::min<int64_t>(BN, hd - int64_t(J) * BN));
+    // operands in the MK-token block layout (D rows per block); each buffer resource runs from
+    // the operand's first element to the end of the chunk (D * ldy elements)
+    const int64_t D = hd * n_blocks;
+    const int64_t offI = (kb / MK) * D * MK + r0 * MK, offJ = (kb / MK) * D * MK + c0 * MK;
     const bf16_t *base[4];
     int64_t ld[4];
     int rows[4];
     if (NPROD == 4) {
-        base[0] = Yhi + r0 * ldy + kb; base[1] = Ylo + r0 * ldy + kb;
-        base[2] = Yhi + c0 * ldy + kb; base[3] = Ylo + c0 * ldy + kb;
+        base[0] = Yhi + offI; base[1] = Ylo + offI;
+        base[2] = Yhi + offJ; base[3] = Ylo + offJ;
         rows[0] = rows[1] = rowsI; rows[2] = rows[3] = rowsJ;
     } else {
-        base[0] = Yhi + r0 * ldy + kb; base[1] = Yhi + c0 * ldy + kb;
+        base[0] = Yhi + offI; base[1] = Yhi + offJ;
         rows[0] = rowsI; rows[1] = rowsJ;
     }
-    for (int o = 0; o < 4; ++o) ld[o] = ldy;
+    int64_t nrec[4];  // bytes from each operand's base to the end of its buffer
+    for (int o = 0; o < 4; ++o) ld[o] = D;
+    if (NPROD == 4) {
+        nrec[0] = nrec[1] = (D * ldy - offI) * 2;
+        nrec[2] = nrec[3] = (D * ldy - offJ) * 2;
+    } else {
+        nrec[0] = (D * ldy - offI) * 2;
+        nrec[1] = (D * ldy - offJ) * 2;
+    }
     f32x16_t acc[Cfg::TM][Cfg::TN];
 #pragma unroll
     for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
     // klen is a multiple of MK here, so no k check is needed
-    mfma_mainloop<BM, THREADS, WGM, NOPS, NPROD, true, SYRK_FE, false, SYRK_DEPTH, true>(base, ld, rows, klen, acc, lds);
+    mfma_mainloop<BM, BN, THREADS, WGM, NOPS, NPROD, true, SYRK_FE, false, SYRK_DEPTH, true, true>(base, ld, rows, klen,
+                                                                                                 nrec, acc, lds);
     float *dst;
     int64_t ldd;
     if (s == 0) {
@@ -325,7 +400,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
 #pragma unroll
         for (int tn = 0; tn < Cfg::TN; ++tn) {
             const int64_t rb = int64_t(I) * BM + wm * Cfg::WM + tm * 32;
-            const int64_t cc = int64_t(J) * BM + wn * Cfg::WN + tn * 32 + acc_col(lane);
+            const int64_t cc = int64_t(J) * BN + wn * Cfg::WN + tn * 32 + acc_col(lane);
             add_upper_tile(acc[tm][tn], rb, cc, lane, hd, dst, ldd);
         }
 }
@@ -346,7 +421,7 @@ __global__ void __launch_bounds__(256) k_transpose_bf16(const bf16_t *__restrict
     }
 }
 
-// Y^T = X^T for a chunk of tc tokens; columns tc .. ldy-1 are zero.
+// Y^T = X^T for a chunk of tc tokens, in the MK-token block layout; tokens tc .. ldy-1 are zero.
 __global__ void __launch_bounds__(256) k_chunk_transpose(const bf16_t *__restrict__ X, int64_t ldx, int64_t tc,
                                                          int64_t d, bf16_t *__restrict__ Yt, int64_t ldy) {
     __shared__ bf16_t tile[64][65];
@@ -358,7 +433,8 @@ __global__ void __launch_bounds__(256) k_chunk_transpose(const bf16_t *__restric
     __syncthreads();
     for (int e = threadIdx.x; e < 64 * 64; e += 256) {
         const int cc = e / 64, rr = e % 64;
-        if (c0 + cc < d && t0 + rr < ldy) Yt[(c0 + cc) * ldy + t0 + rr] = tile[rr][cc];
+        const int64_t t = t0 + rr;
+        if (c0 + cc < d && t < ldy) Yt[((t / MK) * d + c0 + cc) * MK + t % MK] = tile[rr][cc];
     }
 }
 
@@ -385,21 +461,22 @@ __global__ void k_add_partials(float *__restrict__ C, int64_t ldc, const float *
 // host side
 // ---------------------------------------------------------------------------------------------
 struct MfmaPlan {
-    int bm;         // SYRK block tile (128: 4 waves of 64 x 64, spill-free with the per-slice flush)
+    bool wide;      // SYRK block tile 256 x 128 (4 waves of 128 x 64); else 128 x 128 (64 x 64)
     int64_t tcmax;  // tokens per chunk
     int64_t ldy;    // leading dim of Y^T (multiple of 256)
     int nsplit;     // token splits of the SYRK
-    int64_t n_upper;
+    int64_t n_upper;  // SYRK tiles per head block
 };
 
 static MfmaPlan plan(int64_t n_tok, int64_t d_out, int32_t n_blocks) {
     MfmaPlan p;
     const int64_t hd = d_out / n_blocks;
-    p.bm = 128;
+    // the wide tile moves a quarter less LDS and L2 data per MFMA; below 256 rows it would be
+    // half empty
+    p.wide = hd >= 256;
     p.tcmax = std::min<int64_t>(MFMA_CHUNK, n_tok);
     p.ldy = (p.tcmax + 255) / 256 * 256;
-    const int64_t th = (hd + p.bm - 1) / p.bm;
-    p.n_upper = th * (th + 1) / 2;
+    p.n_upper = p.wide ? syrk_tiles<256, 128>(int(hd)) : syrk_tiles<128, 128>(int(hd));
     const int64_t tiles = p.n_upper * n_blocks;
     // smallest split count that fills >= 90% of the last wave of 256 CUs x SYRK_WPE resident
     // blocks, while keeping at least 8 k-steps per split
@@ -424,9 +501,12 @@ bool cov_mfma_supported(lrc_dtype x_t, const void *X, int64_t ldx, const void *W
                         int64_t d_out, int32_t n_blocks) {
     (void)W;
     (void)ldw;
-    // buffer-load byte offsets are 32-bit: a 256-row operand tile must stay below 2^31 bytes
+    // buffer-load byte offsets are 32-bit: a 256-row operand tile of X and W, and the Y^T chunk
+    // (d_out x MFMA_CHUNK bf16 read through one resource, plus the two k steps loaded past its
+    // end), must stay below 2^31 bytes
     return x_t == LRC_BF16 && cov_mfma_shape_ok(d_in, d_out, n_blocks) && ldx % 8 == 0 &&
-           (reinterpret_cast<uintptr_t>(X) % 16) == 0 && ldx < (int64_t(1) << 21) && d_in < (int64_t(1) << 21);
+           (reinterpret_cast<uintptr_t>(X) % 16) == 0 && ldx < (int64_t(1) << 21) && d_in < (int64_t(1) << 21) &&
+           (d_out + 1) * (MFMA_CHUNK + 4 * MK) * 2 < (int64_t(1) << 31);
 }
 
 size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks) {
@@ -473,10 +553,10 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
             // d_in a multiple of the k step: no partial last step, no k check in the loads
             if (a.d_in % MK == 0)
                 LRC_TIMED_LAUNCH("k_cov_gemm_y", fl, (k_cov_gemm_y<G_BM, false>), g, dim3(G_THREADS), 0, s, Wt,
-                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo, p.ldy);
+                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo);
             else
                 LRC_TIMED_LAUNCH("k_cov_gemm_y", fl, (k_cov_gemm_y<G_BM, true>), g, dim3(G_THREADS), 0, s, Wt,
-                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo, p.ldy);
+                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo);
             LRC_LAUNCH_CHECK("k_cov_gemm_y");
         } else {
             dim3 g(cdiv(a.d_out, 64), cdiv(ktot, 64));
@@ -487,12 +567,18 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         dim3 g(unsigned(p.n_upper), unsigned(a.n_blocks), unsigned(p.nsplit));
         // algorithmic flops of the launch: the upper triangle (incl. diagonal) of each head block
         const double fl = double(tc) * double(hd) * double(hd + 1) * double(a.n_blocks);
-        if (has_w)
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 4>), g, dim3(SyrkCfg<128>::THREADS), 0, s, Yhi, Ylo,
-                             p.ldy, ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+        if (has_w && p.wide)
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, 4>), g, dim3(256), 0, s, Yhi, Ylo, p.ldy, ktot,
+                             kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+        else if (has_w)
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, 4>), g, dim3(256), 0, s, Yhi, Ylo, p.ldy, ktot,
+                             kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+        else if (p.wide)
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, 1>), g, dim3(256), 0, s, Yhi, Ylo, p.ldy, ktot,
+                             kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         else
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 1>), g, dim3(SyrkCfg<128>::THREADS), 0, s, Yhi, Ylo,
-                             p.ldy, ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, 1>), g, dim3(256), 0, s, Yhi, Ylo, p.ldy, ktot,
+                             kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         LRC_LAUNCH_CHECK("k_cov_syrk");
     }
     if (p.nsplit > 1) {
