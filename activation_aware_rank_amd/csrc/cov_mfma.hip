@@ -244,6 +244,143 @@ __device__ __forceinline__ void mfma_mainloop(
     }
 }
 
+// SYRK main loop with the operands loaded straight into LDS (16-byte buffer loads with an LDS
+// destination) from the MK-token block layout of Y^T.  Three LDS stages, each its own array: the
+// loads of step kt + 2 are issued right after the barrier of step kt, into the stage that step
+// kt - 1 read.  Before the barrier of step kt each wave waits only for its own loads of step kt
+// (those of step kt + 1 stay in flight); the barrier is a plain s_barrier, since the compiler
+// would otherwise wait for every load into LDS before each barrier.  No registers stage the
+// operands and no LDS stores are issued.
+// A wave's 16-byte load of row r lands at lds + r * 64 + 16 * (lane & 3) (linear in the lane), so
+// the XOR swizzle of swz() is applied to the global side: that lane loads chunk (lane & 3) ^ f(r).
+// Rows past rows[o] read zero through an offset of 2^31, past every operand's resource.
+// FE 4: the MFMA chains restart every 64 tokens (two steps) and are added to acc with one
+// round-to-nearest fp32 add, as in mfma_mainloop.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// s_waitcnt with vmcnt = n (0..63) and no wait on the other counters (gfx9 encoding)
+#define LRC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+template <int BM, int BN, int NOPS, int NPROD>
+__device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, const int64_t D, const int *rows,
+                                                  int64_t klen, const int64_t *nrec,
+                                                  f32x16_t (&acc)[MfmaCfg<BM, BN, 256, 2>::TM][MfmaCfg<BM, BN, 256, 2>::TN],
+                                                  bf16_t *lds0, bf16_t *lds1, bf16_t *lds2) {
+    using T = MfmaCfg<BM, BN, 256, 2>;
+    constexpr int THREADS = 256;
+    constexpr int TM = T::TM, TN = T::TN, UA = T::UA, UB = T::UB;
+    constexpr int U = UA > UB ? UA : UB;
+    constexpr int NSIDE = NOPS / 2;
+    constexpr int NA = (NPROD == 4) ? 2 : 1;
+    static_assert(NSIDE == NA, "hi/lo operands per side");
+    constexpr int LPS = NSIDE * (UA + UB);  // loads per thread per step
+    auto opoff = [](int o) { return o < NSIDE ? o * BM * MK : NSIDE * BM * MK + (o - NSIDE) * BN * MK; };
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / T::WGN, wn = wave % T::WGN;
+    const int nk = int(klen / MK);
+    if (nk <= 0) return;
+    __amdgpu_buffer_rsrc_t rs[NOPS];
+    uint32_t roff[NOPS][U];
+#pragma unroll
+    for (int o = 0; o < NOPS; ++o) {
+        rs[o] = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base[o]), short(0), int(nrec[o]), 0x00020000);
+#pragma unroll
+        for (int u = 0; u < (o < NSIDE ? UA : UB); ++u) {
+            const int r = 16 * wave + (lane >> 2) + 64 * u;  // row of this lane's 16 bytes
+            const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+            roff[o][u] = r < rows[o] ? uint32_t((r * MK + c * 8) * 2) : 0x80000000u;
+        }
+    }
+    const uint32_t kstride = uint32_t(D * MK * 2);
+    // loads of step kt into a stage: for operand o and chunk u, wave w fills rows 16 w + 64 u ..
+    auto issue = [&](int kt, bf16_t *st) {
+#pragma unroll
+        for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+            for (int u = 0; u < (o < NSIDE ? UA : UB); ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs[o], (lds_void_t *)(st + opoff(o) + (16 * wave + 64 * u) * MK), 16,
+                    int(roff[o][u] + uint32_t(kt) * kstride), 0, 0, 0);
+    };
+    f32x16_t p[TM][TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) p[tm][tn] = f32x16_t{};
+    auto flush = [&]() {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[tm][tn][r] = __fadd_rn(acc[tm][tn][r], p[tm][tn][r]);
+    };
+    // one step: publish stage `cur` (this wave's loads of step kt done, then the barrier), issue the
+    // loads of step kt + 2 into `nxt`, then the MFMAs from `cur`; PAR: position in the flush group
+    auto step = [&](int kt, const bf16_t *cur, bf16_t *nxt, auto par) {
+        constexpr int PAR = decltype(par)::value;
+        LRC_WAIT_VMCNT(LPS);
+        lds_barrier();
+        issue(kt + 2, nxt);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c = ks * 2 + (lane >> 5);
+            bf16x8_t af[NA][TM], bfr[NA][TN];
+#pragma unroll
+            for (int a = 0; a < NA; ++a) {
+#pragma unroll
+                for (int t = 0; t < TM; ++t)
+                    af[a][t] = *reinterpret_cast<const bf16x8_t *>(cur + opoff(a) +
+                                                                   swz(wm * T::WM + t * 32 + (lane & 31), c));
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    bfr[a][t] = *reinterpret_cast<const bf16x8_t *>(cur + opoff(NSIDE + a) +
+                                                                    swz(wn * T::WN + t * 32 + (lane & 31), c));
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    // a flush group's first slice starts the chain from a literal zero
+                    const bool fresh = PAR == 0 && ks == 0;
+                    f32x16_t q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[0][tn],
+                                                                         fresh ? f32x16_t{} : p[tm][tn], 0, 0, 0);
+                    if (NPROD == 4) {
+                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[1][tn], q, 0, 0, 0);
+                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[0][tn], q, 0, 0, 0);
+                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[1][tn], q, 0, 0, 0);
+                    }
+                    p[tm][tn] = q;
+                }
+        }
+        if (PAR == 1) flush();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    issue(0, lds0);
+    issue(1, lds1);
+    // six steps per iteration: stages 0 1 2 0 1 2, flush-group positions 0 1 0 1 0 1
+    int kt = 0;
+    for (; kt + 5 < nk; kt += 6) {
+        step(kt, lds0, lds2, I0{});
+        step(kt + 1, lds1, lds0, I1{});
+        step(kt + 2, lds2, lds1, I0{});
+        step(kt + 3, lds0, lds2, I1{});
+        step(kt + 4, lds1, lds0, I0{});
+        step(kt + 5, lds2, lds1, I1{});
+    }
+    const int r = nk - kt;
+    if (r > 0) step(kt, lds0, lds2, I0{});
+    if (r > 1) step(kt + 1, lds1, lds0, I1{});
+    if (r > 2) step(kt + 2, lds2, lds1, I0{});
+    if (r > 3) step(kt + 3, lds0, lds2, I1{});
+    if (r > 4) step(kt + 4, lds1, lds0, I0{});
+    if (r & 1) flush();  // the last flush group had only its first step
+    // the loads issued past the last step still write LDS: let them land before the epilogue
+    LRC_WAIT_VMCNT(0);
+    lds_barrier();
+}
+
 // Output position of accumulator element r of lane `lane` in a 32x32 MFMA tile.
 __device__ __forceinline__ int acc_row(int lane, int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
@@ -332,7 +469,10 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
     static_assert(THREADS == 256, "launch bounds");
     using Cfg = MfmaCfg<BM, BN, THREADS, WGM>;
     constexpr int NOPS = (NPROD == 4) ? 4 : 2;
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (NOPS / 2) * (BM + BN) * MK];
+    constexpr int STAGE = (NOPS / 2) * (BM + BN) * MK;  // elements of one LDS stage
+    __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE];
+    __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
+    __shared__ __attribute__((aligned(16))) bf16_t lds2[STAGE];
     const int u = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     int I, J;
     if constexpr (BM == BN) {  // column J holds J + 1 tiles: closed form
@@ -383,8 +523,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
     // klen is a multiple of MK here, so no k check is needed
-    mfma_mainloop<BM, BN, THREADS, WGM, NOPS, NPROD, true, SYRK_FE, false, SYRK_DEPTH, true, true>(base, ld, rows, klen,
-                                                                                                 nrec, acc, lds);
+    syrk_dma_mainloop<BM, BN, NOPS, NPROD>(base, D, rows, klen, nrec, acc, lds0, lds1, lds2);
     float *dst;
     int64_t ldd;
     if (s == 0) {
