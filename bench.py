@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--curvature-tokens", type=int, default=131072,
                     help="tokens of the curvature-weighted 13B FFN leg, timed after the block (0: skip)")
     ap.add_argument("--curvature-prec", choices=("f32", "f64"), default="f64")
+    ap.add_argument("--layer-runs", type=int, default=2,
+                    help="runs of one 4096x4096 layer on its own after the timed steps (0: skip)")
     ap.add_argument("--timing-stride", type=int, default=16,
                     help="time every s-th launch of the per-column symmetric product in the timed steps")
     a = ap.parse_args()
@@ -266,7 +268,7 @@ def main():
         assert int(gi.sum().item()) == 0, "eigh info flags set (n = %d): %s" % (n, gi.tolist())
 
     # one 4096x4096 layer on its own, after the timed steps: covariance, eigendecomposition (alone,
-    # not batched), error curve, factors; mean of two runs
+    # not batched), error curve, factors; mean of --layer-runs runs
     def one_layer(m="q_proj"):
         C[m].zero_()
         e0 = ev(stream)
@@ -277,9 +279,9 @@ def main():
         e1 = ev(stream)
         return e0, e1
 
-    layer_runs = [one_layer() for _ in range(2)]
+    layer_runs = [one_layer() for _ in range(a.layer_runs)]
     torch.cuda.synchronize()
-    layer_alone_s = float(np.mean([x.elapsed_time(y) for x, y in layer_runs])) / 1000.0
+    layer_alone_s = float(np.mean([x.elapsed_time(y) for x, y in layer_runs])) / 1000.0 if layer_runs else None
     assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
 
     # per-call times from the events (ms), averaged over steps
@@ -332,7 +334,13 @@ def main():
         r["sampled"] = "every launch in the timed steps (start/stop events recorded by the dispatch)"
     roof_symv["sampled"] = ("every %d-th launch in the timed steps (start/stop events recorded by the dispatch)"
                             % a.timing_stride)
-    roof = max((roof_syrk, roof_symv), key=lambda r: r["total_ms_per_step"])
+    roof_symv["overlap"] = ("launches on up to four helper streams overlap (several eigendecompositions at once): "
+                            "a launch's event-timed duration includes time its workgroups wait for CUs held by the "
+                            "other streams' kernels, and summed durations exceed the eigendecomposition stage's "
+                            "wall time")
+    # the roofline entry is the covariance SYRK: the kernel with the largest time among those that
+    # run alone (the covariance stage is serial), so its event-timed duration is its execution time
+    roof = roof_syrk
     out = {
         "metric": "calibration tokens/s into Y^T Y; sec per 4096x4096 layer compressed (eig incl.)",
         "value": a.tokens / (step_ms / 1000.0),
