@@ -158,20 +158,18 @@ def main():
     X, Xd, W, G = blk["X"], blk["Xd"], blk["W"], blk["G"]
     del blk
     # outputs and workspaces allocated once, outside the timed region.  The matrices are grouped
-    # by output width (q/k/v/o/down: 4096, gate/up: 11008); each group's covariances sit in one
-    # stack and go through one batched eigendecomposition, whose members the library runs
-    # concurrently.  A group computes the largest rank of its members; the factors use each
-    # matrix's own leading k columns.
+    # by output width and rank (q/k/v/o: 4096 and 1228, down: 4096 and 1791, gate/up: 11008 and
+    # 1791); each group's covariances sit in one stack, and all groups go through one call that
+    # decomposes up to four matrices at once.
     groups = {}
     for m in MATS:
-        groups.setdefault(sh[m][1], []).append(m)
-    gC = {n: torch.empty(len(ms), n, n, dtype=torch.float32, device=dev) for n, ms in groups.items()}
-    gnv = {n: max(ks[m] for m in ms) for n, ms in groups.items()}
-    glam = {n: torch.empty(len(ms), n, dtype=torch.float64, device=dev) for n, ms in groups.items()}
-    gV = {n: torch.empty(len(ms), n, gnv[n], dtype=torch.float32, device=dev) for n, ms in groups.items()}
-    geps = {n: torch.empty(len(ms), n + 1, dtype=torch.float64, device=dev) for n, ms in groups.items()}
-    ginfo = {n: torch.zeros(len(ms), dtype=torch.int32, device=dev) for n, ms in groups.items()}
-    where = {m: (n, ms.index(m)) for n, ms in groups.items() for m in ms}
+        groups.setdefault((sh[m][1], ks[m]), []).append(m)
+    gC = {g: torch.empty(len(ms), g[0], g[0], dtype=torch.float32, device=dev) for g, ms in groups.items()}
+    glam = {g: torch.empty(len(ms), g[0], dtype=torch.float64, device=dev) for g, ms in groups.items()}
+    gV = {g: torch.empty(len(ms), g[0], g[1], dtype=torch.float32, device=dev) for g, ms in groups.items()}
+    geps = {g: torch.empty(len(ms), g[0] + 1, dtype=torch.float64, device=dev) for g, ms in groups.items()}
+    ginfo = {g: torch.zeros(len(ms), dtype=torch.int32, device=dev) for g, ms in groups.items()}
+    where = {m: (g, ms.index(m)) for g, ms in groups.items() for m in ms}
     C = {m: gC[where[m][0]][where[m][1]] for m in MATS}
     lam = {m: glam[where[m][0]][where[m][1]] for m in MATS}
     V = {m: gV[where[m][0]][where[m][1]] for m in MATS}
@@ -181,10 +179,10 @@ def main():
     info = torch.zeros(8, dtype=torch.int32, device=dev)
     ws_cov = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, di, True, do, 1)
                              for di, do in sh.values()), dtype=torch.uint8, device=dev)
-    ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace([(n, len(ms), gnv[n]) for n, ms in groups.items()], prec),
+    ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace([(g[0], len(ms), g[1]) for g, ms in groups.items()], prec),
                          dtype=torch.uint8, device=dev)
-    eig_groups = [(gC[n], gnv[n], glam[n], gV[n], ginfo[n]) for n in groups]
-    gkey = "+".join("%dx%d" % (len(ms), n) for n, ms in groups.items())
+    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g]) for g in groups]
+    gkey = "+".join("%dx%d_k%d" % (len(ms), g[0], g[1]) for g, ms in groups.items())
     kcap = {m: (di * do) // (di + do) for m, (di, do) in sh.items()}
     offs_h = [0] + list(np.cumsum([kcap[m] for m in MATS]))
     offs = torch.tensor(offs_h, dtype=torch.int64, device=dev)
@@ -217,8 +215,8 @@ def main():
         e0 = ev(stream)
         lrc.lrc_eigh_multi(eig_groups, prec=prec, ws=ws_eig)
         e1 = ev(stream)
-        for n in groups:
-            lrc.lrc_error_curve(glam[n], eps=geps[n])
+        for g in groups:
+            lrc.lrc_error_curve(glam[g], eps=geps[g])
         e2 = ev(stream)
         times.append(("eigh." + gkey, e0, e1))
         times.append(("err." + gkey, e1, e2))
@@ -264,8 +262,8 @@ def main():
     gemm_n, gemm_ms, gemm_fl = lrc.lrc_timing_read("k_cov_gemm_y", reset=False)
     symv_n, symv_ms, symv_by = lrc.lrc_timing_read("k_trd_symv", reset=True)
     assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
-    for n, gi in ginfo.items():
-        assert int(gi.sum().item()) == 0, "eigh info flags set (n = %d): %s" % (n, gi.tolist())
+    for g, gi in ginfo.items():
+        assert int(gi.sum().item()) == 0, "eigh info flags set (n = %d): %s" % (g[0], gi.tolist())
 
     # one 4096x4096 layer on its own, after the timed steps: covariance, eigendecomposition (alone,
     # not batched), error curve, factors; mean of --layer-runs runs
