@@ -103,6 +103,19 @@ __device__ __forceinline__ void transpose_sum_stage(T (&p)[64], int lane) {
         p[k] = keep + __shfl_xor(send, ST);
     }
 }
+// One reduce-scatter step over lane bit MBIT: lanes with the bit set keep values HALF .. 2 HALF - 1
+// (moved to 0 .. HALF - 1), the others 0 .. HALF - 1, each summed with the partner's copy.
+template <int HALF, int MBIT, int N, class T>
+__device__ __forceinline__ void rs_step(T (&p)[N], int lane) {
+    static_assert(2 * HALF <= N, "reduce-scatter step");
+    const bool up = (lane & MBIT) != 0;
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) {
+        const T send = up ? p[k] : p[k + HALF];
+        const T keep = up ? p[k + HALF] : p[k];
+        p[k] = keep + __shfl_xor(send, MBIT);
+    }
+}
 template <class T>
 __device__ __forceinline__ T wave_transpose_sum64(T (&p)[64]) {
     const int lane = threadIdx.x & 63;
@@ -169,10 +182,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int TS = SymvTile<T>::TS, EPC = SymvTile<T>::EPC, H = SymvTile<T>::H;
     static_assert(16 * EPC == TS, "tile geometry");
     typedef T vec_t __attribute__((ext_vector_type(EPC)));
-    __shared__ __attribute__((aligned(16))) T tile[4][TS * TS];
     __shared__ __attribute__((aligned(16))) T vI[TS];
     __shared__ __attribute__((aligned(16))) T vJ[8 * TS];
     __shared__ T rowacc[4][TS];
+    __shared__ T dcol[4][TS];
+    __shared__ T qr[256];
     __shared__ T sh[4];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     // work item: L with items(L - 1) <= g < items(L)
@@ -249,58 +263,85 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     __syncthreads();
 
-    const int rr = lane % TS, hh = lane / TS;  // row (and column) of this lane, half of the tile
-    T *tl = tile[wave];
-    T yrow = T(0);
+    // Each lane holds, of every tile it loaded, rows gq + 4u (u < RPL) and the EPC columns of
+    // chunk q.  Both parts are formed from these registers: the row part accumulates over the
+    // wave's tiles and is reduced once across the 16 lanes that share rows (each lane keeps one
+    // row); the column part of each tile is reduced across the 4 lanes that share columns (each
+    // keeps one column).  No LDS copy of the tile: staging it and reading it back (a scalar read
+    // per column element) took 40 % of the kernel's time at the largest trailing sizes.
+    constexpr int RPL = TS / 4;  // rows per lane (16 fp32, 8 fp64)
+    const int gq = lane >> 4, q = lane & 15;
+    const int xsel = EPC == 4 ? ((lane >> 4) & 3) : ((lane >> 5) & 1);  // column kept after the reduction
+    const int csel = q * EPC + xsel;
+    const int rsel = gq + 4 * (RPL == 16 ? (lane & 15) : ((lane & 14) >> 1));  // row kept after the reduction
+    const bool cwriter = EPC == 4 || (lane & 16) == 0;  // one lane per column (fp64: two hold it)
+    T vIr[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) vIr[u] = vI[gq + 4 * u];
+    T rp[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) rp[u] = T(0);
     T sdot = T(0);  // this lane's share of v^T y from the column parts
+    T dcs = T(0);   // diagonal tile: this lane's column sum, added to the row of the same index
+    bool had_diag = false;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         const int J = Jf + 4 * tt;
         if (J >= J1) break;
-#pragma unroll
-        for (int u = 0; u < TS / 4; ++u) {
-            const int idx = lane + 64 * u;
-            const int r = idx >> 4, q = idx & 15;
-            *reinterpret_cast<u32x4_t *>(tl + (r * 16 + (q ^ (r & 15))) * EPC) = pre[tt][u];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
         const bool diag = (J == i);
-        const T *vj = vJ + (J - J0) * TS;
-        // row part: lane (rr, hh) sums chunks hh*16/H .. of row rr
-#pragma unroll 4
-        for (int q0 = 0; q0 < 16 / H; ++q0) {
-            const int q = hh * (16 / H) + q0;
-            const vec_t a = *reinterpret_cast<const vec_t *>(tl + (rr * 16 + (q ^ (rr & 15))) * EPC);
-            const vec_t b = *reinterpret_cast<const vec_t *>(vj + q * EPC);
+        const vec_t bj = *reinterpret_cast<const vec_t *>(vJ + (J - J0) * TS + q * EPC);
+        T cp[EPC];
+#pragma unroll
+        for (int x = 0; x < EPC; ++x) cp[x] = T(0);
+#pragma unroll
+        for (int u = 0; u < RPL; ++u) {
+            const vec_t a = __builtin_bit_cast(vec_t, pre[tt][u]);
+            const int r = gq + 4 * u;
 #pragma unroll
             for (int x = 0; x < EPC; ++x) {
-                const int k = q * EPC + x;
-                const T av = (diag && k < rr) ? T(0) : a[x];
-                yrow += av * b[x];
+                const int cc = q * EPC + x;
+                // the diagonal tile holds the upper triangle only: the row part takes cc >= r and
+                // the column part r < cc
+                const T ar = (diag && cc < r) ? T(0) : a[x];
+                const T ac = (diag && r >= cc) ? T(0) : a[x];
+                rp[u] += ar * bj[x];
+                cp[x] += ac * vIr[u];
             }
         }
-        // column part: lane (cc = rr, hh) sums rows hh*TS/H .. of column cc
-        T ycol = T(0);
-        const int cq = rr / EPC, cx = rr % EPC;
-#pragma unroll 8
-        for (int r0 = 0; r0 < TS / H; ++r0) {
-            const int r = hh * (TS / H) + r0;
-            const T av = tl[(r * 16 + (cq ^ (r & 15))) * EPC + cx];
-            ycol += ((diag && r >= rr) ? T(0) : av) * vI[r];
+        if constexpr (EPC == 4) {
+            rs_step<2, 32>(cp, lane);
+            rs_step<1, 16>(cp, lane);
+        } else {
+            rs_step<1, 32>(cp, lane);
+            cp[0] += __shfl_xor(cp[0], 16);
         }
-        if (H == 2) ycol += __shfl_xor(ycol, 32);
         if (diag) {
-            if (hh == 0) yrow += ycol;
-        } else if (hh == 0) {
-            colpart[(int64_t(i) * NT + J) * TS + rr] = ycol;
-            sdot += ycol * vj[rr];
+            had_diag = true;
+            dcs = cp[0];
+        } else if (cwriter) {
+            colpart[(int64_t(i) * NT + J) * TS + csel] = cp[0];
+            sdot += cp[0] * bj[xsel];
         }
+    }
+    if constexpr (RPL == 16) {
+        rs_step<8, 8>(rp, lane);
+        rs_step<4, 4>(rp, lane);
+        rs_step<2, 2>(rp, lane);
+        rs_step<1, 1>(rp, lane);
+    } else {
+        rs_step<4, 8>(rp, lane);
+        rs_step<2, 4>(rp, lane);
+        rs_step<1, 2>(rp, lane);
+        rp[0] += __shfl_xor(rp[0], 1);
+    }
+    T yrow = rp[0];
+    if (had_diag) {  // wave-uniform
+        dcol[wave][csel] = dcs;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        yrow += dcol[wave][rsel];
     }
-    if (H == 2) yrow += __shfl_xor(yrow, 32);
-    if (hh == 0) rowacc[wave][rr] = yrow;
+    rowacc[wave][rsel] = yrow;
     __syncthreads();
     if (t < TS) {
         const T yr = (rowacc[0][t] + rowacc[1][t]) + (rowacc[2][t] + rowacc[3][t]);
@@ -321,7 +362,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (blockIdx.x == 0) {
         // q = (W^T v, V^T v) over the panel's first j columns from the column kernel's partials of
         // W^T x, V^T x over rows c+2 .. n-1 (fixed order): v = scale x there and v[c+1] = 1
-        T *qr = &tile[0][0];  // reused: [4][2 NB]
         __syncthreads();
         qr[t] = qacc;
         __syncthreads();
