@@ -406,6 +406,7 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
     __shared__ T qs[2 * NB];
     __shared__ T ys[4][64];
     __shared__ T vc[NB], wc[NB];
+    __shared__ T v1s[NB], w1s[NB];
     const int T0 = int((c + 1) / SymvTile<T>::TS);
     const int t = threadIdx.x;
     const int rl = t & 63, sub = t >> 6;
@@ -433,6 +434,10 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
     if (mine && next) aold = A[(c + 1) * lda + r];
     const T tv = tau[c];
     if (t < 2 * NB) qs[t] = qv;
+    if (t < NB) {  // row c+1 of the panel, for the thread that forms W[c+1][j]
+        w1s[t] = w1row;
+        v1s[t] = v1row;
+    }
     ys[sub][rl] = yr;
     // v^T y and y[c+1] in one block reduction
     T vty = sp, yc = ycp;
@@ -456,8 +461,7 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
         T wv = q < j ? w1row : T(0);
         if (q == j) {
             T w = yc;
-            for (int k = 0; k < j; ++k)
-                w -= Vp[int64_t(k) * n + c + 1] * qs[k] + Wp[int64_t(k) * n + c + 1] * qs[NB + k];
+            for (int k = 0; k < j; ++k) w -= v1s[k] * qs[k] + w1s[k] * qs[NB + k];
             wv = tv * w - half * v1row;
         }
         wc[q] = wv;
