@@ -72,6 +72,25 @@ __device__ __forceinline__ T block_sum(T v, T *sh) {
     return r;  // every thread
 }
 
+// Sum of at(i) for i = i0, i0 + step, ... < i1 with eight loads in flight (eight running sums,
+// combined in a fixed order); a loop of dependent load-add steps would wait for every load.
+template <class T, class F>
+__device__ __forceinline__ T sum_strided8(F at, int i0, int i1, int step) {
+    T a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = T(0);
+    int i = i0;
+    for (; i + 7 * step < i1; i += 8 * step) {
+        T v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = at(i + u * step);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += v[u];
+    }
+    for (; i < i1; i += step) a[0] += at(i);
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
 // Each column of a panel takes three launches; each global reduction is done by the next launch,
 // redundantly in every block that needs it and always in the same fixed order, so all blocks see
 // bit-identical values (no atomics, no device-wide fences):
@@ -391,7 +410,8 @@ __device__ __forceinline__ T symv_y(int64_t r, const T *__restrict__ rowpart, co
     const int nch = int((NT - I + CHK - 1) / CHK);
     T y = T(0);
     for (int ch = sub; ch < nch; ch += nsub) y += rowpart[(int64_t(I) * NT + ch) * TS + o];
-    for (int ib = T0 + sub; ib < I; ib += nsub) y += colpart[(int64_t(ib) * NT + I) * TS + o];
+    // the column parts of the tiles above: up to NT of them for the last block rows
+    y += sum_strided8<T>([&](int ib) { return colpart[(int64_t(ib) * NT + I) * TS + o]; }, T0 + sub, I, nsub);
     return y;
 }
 
