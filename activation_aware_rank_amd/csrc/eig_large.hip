@@ -27,7 +27,7 @@ namespace lrc {
 
 constexpr int NB = 32;    // tridiagonalisation panel width
 constexpr int NBT = 64;   // back-transformation block of reflectors
-constexpr int RCH = 512;  // rows per partial in the back-transformation reductions
+constexpr int RCH = 256;  // rows per partial in the back-transformation reductions
 
 // ---------------------------------------------------------------------------------------------
 // 1. tridiagonalisation
@@ -900,98 +900,144 @@ __global__ void __launch_bounds__(256) k_bt_tall(const T *__restrict__ Rt, int64
     for (int e = t; e < NBT * NBT; e += 256) out[e] = Tm[e / NBT][e % NBT];
 }
 
-// partial G[q][col] = sum_{r in chunk} Rt[c0+q][r] Z[r][col]; grid (col tiles of 64, row chunks)
-template <class T>
-__global__ void __launch_bounds__(256) k_bt_g(const T *__restrict__ Rt, int64_t ldr, int64_t n, int64_t c0, int nb,
-                                              const double *__restrict__ Z, int64_t nv, double *__restrict__ Gp) {
-    __shared__ double vs[NBT][65];
-    __shared__ double zs[64][65];
-    const int64_t col0 = int64_t(blockIdx.x) * 64, r0 = int64_t(blockIdx.y) * RCH;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 4 rows of q per thread group
-    double acc[NBT / 4];
+// fp64 MFMA tiles of the back-transformation: a workgroup of 4 waves forms a 64 x 64 tile, wave wv
+// the 32 x 32 quarter (wr, wc), as 2 x 2 products of 16x16x4 fp64 MFMA.
+constexpr int BK = 16;         // contraction step staged in LDS
+constexpr int BLD = 64 + 16;   // padded LDS row (doubles)
+
+// acc += sum_{k0 <= k < k1} A(i, k) B(k, j) over the tile.  la(i, k) and lb(k, j) return an operand
+// value (0 outside the operand); each thread reads 4 consecutive values of each operand per step,
+// along k for A when AK = 1 (A contiguous in k), else along i, and along j for B.  Both operands are
+// staged k-major in LDS, and the next step's values are loaded while the current one is multiplied.
+template <int AK, class LA, class LB>
+__device__ __forceinline__ void bt_mfma(const LA &la, const LB &lb, int64_t k0, int64_t k1, f64x4_t (&acc)[2][2],
+                                        double (&As)[BK][BLD], double (&Bs)[BK][BLD]) {
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int wr = (wv >> 1) * 32, wc = (wv & 1) * 32;
+    double ra[4], rb[4];
+    auto gload = [&](int64_t kb) {
 #pragma unroll
-    for (int u = 0; u < NBT / 4; ++u) acc[u] = 0.0;
-    for (int64_t rs = 0; rs < RCH; rs += 64) {
-        for (int e = threadIdx.x; e < NBT * 64; e += 256) {
-            const int q = e / 64, rr = e % 64;
-            const int64_t r = r0 + rs + rr;
-            vs[q][rr] = (q < nb && r < n) ? double(Rt[(c0 + q) * ldr + r]) : 0.0;
+        for (int u = 0; u < 4; ++u) {
+            if (AK) ra[u] = la(t >> 2, kb + (t & 3) * 4 + u);
+            else ra[u] = la((t & 15) * 4 + u, kb + (t >> 4));
+            rb[u] = lb(kb + (t >> 4), (t & 15) * 4 + u);
         }
-        for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-            const int rr = e / 64, cc = e % 64;
-            const int64_t r = r0 + rs + rr, col = col0 + cc;
-            zs[rr][cc] = (r < n && col < nv) ? Z[r * nv + col] : 0.0;
+    };
+    gload(k0);
+    for (int64_t kb = k0; kb < k1; kb += BK) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (AK) As[(t & 3) * 4 + u][t >> 2] = ra[u];
+            else As[t >> 4][(t & 15) * 4 + u] = ra[u];
+            Bs[t >> 4][(t & 15) * 4 + u] = rb[u];
         }
         __syncthreads();
-        for (int rr = 0; rr < 64; ++rr) {
-            const double z = zs[rr][tx];
+        if (kb + BK < k1) gload(kb + BK);
 #pragma unroll
-            for (int u = 0; u < NBT / 4; ++u) acc[u] += vs[ty + 4 * u][rr] * z;
+        for (int ks = 0; ks < BK / 4; ++ks) {
+            // operands: lane i + 16 kq holds row (or column) i of k-slice kq
+            const int kk = ks * 4 + (lane >> 4);
+            const double a0 = As[kk][wr + (lane & 15)], a1 = As[kk][wr + 16 + (lane & 15)];
+            const double b0 = Bs[kk][wc + (lane & 15)], b1 = Bs[kk][wc + 16 + (lane & 15)];
+            acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
         }
         __syncthreads();
     }
-    const int64_t col = col0 + tx;
-    if (col < nv)
-#pragma unroll
-        for (int u = 0; u < NBT / 4; ++u) Gp[(int64_t(blockIdx.y) * NBT + ty + 4 * u) * nv + col] = acc[u];
 }
 
-// G = T (sum of partials): thread (q, col) adds the partials of G[q][col] in chunk order, then
-// thread (a, col) forms sum_q T[a][q] G[q][col] from LDS.  Blocks of 256 / NBT columns x NBT.
-constexpr int GR_COLS = 256 / NBT;
+// accumulator r of a lane holds row 4 r + lane / 16, column lane % 16 of its 16 x 16 product
+__device__ __forceinline__ int bt_row(int x, int r) { return ((threadIdx.x >> 7) * 32) + x * 16 + r * 4 + ((threadIdx.x & 63) >> 4); }
+__device__ __forceinline__ int bt_col(int y) { return (((threadIdx.x >> 6) & 1) * 32) + y * 16 + (threadIdx.x & 15); }
+
+// partial G[q][col] = sum of Rt[c0+q][r] Z[r][col] over rows r of chunk y, rows c0+1 + y rch ..
+// (the block's reflectors vanish on rows <= c0); grid (column tiles of 64, chunks)
+template <class T>
+__global__ void __launch_bounds__(256) k_bt_g(const T *__restrict__ Rt, int64_t ldr, int64_t n, int64_t c0, int nb,
+                                              const double *__restrict__ Z, int64_t nv, double *__restrict__ Gp,
+                                              int rch) {
+    __shared__ double As[BK][BLD], Bs[BK][BLD];
+    const int64_t j0 = int64_t(blockIdx.x) * 64;
+    const int64_t r0 = c0 + 1 + int64_t(blockIdx.y) * rch, r1 = min(r0 + rch, n);
+    const T *V = Rt + c0 * ldr;
+    f64x4_t acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    bt_mfma<1>([&](int q, int64_t r) { return (q < nb && r < r1) ? double(V[q * ldr + r]) : 0.0; },
+               [&](int64_t r, int j) { return (r < r1 && j0 + j < nv) ? Z[r * nv + j0 + j] : 0.0; }, r0, r1, acc, As,
+               Bs);
+    double *out = Gp + int64_t(blockIdx.y) * NBT * nv;
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+        const int64_t col = j0 + bt_col(y);
+        if (col < nv)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[int64_t(bt_row(x, r)) * nv + col] = acc[x][y][r];
+    }
+}
+
+// G = T (sum of the partials): thread (column cl, rows 4 qg .. 4 qg + 3) adds the nchunk partials of
+// its 4 values in chunk order, then forms its 4 rows of T G from LDS (T is upper triangular).
+// Blocks of 16 columns.
+constexpr int GR_COLS = 16;
 __global__ void __launch_bounds__(256) k_bt_greduce(const double *__restrict__ Gp, int nchunk, int64_t nv,
                                                     const double *__restrict__ Tf, double *__restrict__ G) {
     __shared__ double Tm[NBT][NBT + 1];
-    __shared__ double g[NBT][GR_COLS];
-    for (int e = threadIdx.x; e < NBT * NBT; e += 256) Tm[e / NBT][e % NBT] = Tf[e];
-    const int q = threadIdx.x / GR_COLS, cl = threadIdx.x % GR_COLS;
+    __shared__ double g[NBT][GR_COLS + 1];
+    const int t = threadIdx.x, cl = t % GR_COLS, qg = t / GR_COLS;
+    for (int e = t; e < NBT * NBT; e += 256) Tm[e / NBT][e % NBT] = Tf[e];
     const int64_t col = int64_t(blockIdx.x) * GR_COLS + cl;
-    double acc = 0.0;
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
     if (col < nv)
-        for (int k = 0; k < nchunk; ++k) acc += Gp[(int64_t(k) * NBT + q) * nv + col];
-    g[q][cl] = acc;
+        for (int k = 0; k < nchunk; ++k)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) a[u] += Gp[(int64_t(k) * NBT + 4 * qg + u) * nv + col];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) g[4 * qg + u][cl] = a[u];
     __syncthreads();
-    double r = 0.0;
-#pragma unroll 8
-    for (int qq = 0; qq < NBT; ++qq) r += Tm[q][qq] * g[qq][cl];
-    if (col < nv) G[int64_t(q) * nv + col] = r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int q = 4 * qg + u;
+        double r = 0.0;
+        for (int qq = q; qq < NBT; ++qq) r += Tm[q][qq] * g[qq][cl];
+        if (col < nv) G[int64_t(q) * nv + col] = r;
+    }
 }
 
-// Z[r][col] -= sum_q Rt[c0+q][r] G[q][col] for r > c0
+// Z[r][col] -= sum_q Rt[c0+q][r] G[q][col] for rows r > c0: 64 x 64 tiles of Z, the contraction over
+// the block's nb reflectors on MFMA; grid (column tiles, row tiles from row c0 + 1)
 template <class T>
 __global__ void __launch_bounds__(256) k_bt_update(const T *__restrict__ Rt, int64_t ldr, int64_t n, int64_t c0, int nb,
                                                    const double *__restrict__ G, double *__restrict__ Z, int64_t nv) {
-    __shared__ double vs[64][NBT + 1];
-    __shared__ double gs[NBT][65];
-    const int64_t col0 = int64_t(blockIdx.x) * 64, r0 = c0 + 1 + int64_t(blockIdx.y) * 64;
-    for (int e = threadIdx.x; e < NBT * 64; e += 256) {
-        const int q = e / 64, rr = e % 64;
-        const int64_t r = r0 + rr, col = col0 + rr;
-        vs[rr][q] = (q < nb && r < n) ? double(Rt[(c0 + q) * ldr + r]) : 0.0;
-        gs[q][rr] = (q < nb && col < nv) ? G[int64_t(q) * nv + col] : 0.0;
+    __shared__ double As[BK][BLD], Bs[BK][BLD];
+    const int64_t j0 = int64_t(blockIdx.x) * 64, i0 = c0 + 1 + int64_t(blockIdx.y) * 64;
+    const T *V = Rt + c0 * ldr + i0;
+    f64x4_t acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    bt_mfma<0>([&](int i, int64_t q) { return (q < nb && i0 + i < n) ? double(V[q * ldr + i]) : 0.0; },
+               [&](int64_t q, int j) { return (q < nb && j0 + j < nv) ? G[q * nv + j0 + j] : 0.0; }, 0, nb, acc, As,
+               Bs);
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+        const int64_t col = j0 + bt_col(y);
+        if (col < nv)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = i0 + bt_row(x, r);
+                    if (row < n) Z[row * nv + col] -= acc[x][y][r];
+                }
     }
-    __syncthreads();
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    double acc[4][4] = {};
-    for (int q = 0; q < nb; ++q) {
-        double a[4], b[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = vs[ty * 4 + u][q];
-            b[u] = gs[q][tx * 4 + u];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) acc[u][w] += a[u] * b[w];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int64_t r = r0 + ty * 4 + u, col = col0 + tx * 4 + w;
-            if (r < n && col < nv) Z[r * nv + col] -= acc[u][w];
-        }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1205,14 +1251,14 @@ struct EigJob {
         }
         if (stage == 3) {  // 4. back-transformation, last block of reflectors first
             const int64_t nrefl = n - 1;
-            const int nch = cdiv(n, RCH);
             for (int q = 0; q < cols && c0 >= 0; ++q, c0 -= NBT) {
                 const int nb = int(std::min<int64_t>(NBT, nrefl - c0));
+                const int64_t mrows = n - c0 - 1;  // rows the block's reflectors touch
+                const int nch = cdiv(mrows, RCH);
                 hipLaunchKernelGGL(k_bt_g<T>, dim3(cdiv(nv, 64), nch), dim3(256), 0, s, w->Rt, n, n, c0, nb, w->Z, nv,
-                                   w->Gp);
+                                   w->Gp, RCH);
                 hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, GR_COLS)), dim3(256), 0, s, w->Gp, nch, nv,
                                    w->Tf + (c0 / NBT) * NBT * NBT, w->G);
-                const int64_t mrows = n - c0 - 1;
                 hipLaunchKernelGGL(k_bt_update<T>, dim3(cdiv(nv, 64), cdiv(mrows, 64)), dim3(256), 0, s, w->Rt, n, n,
                                    c0, nb, w->G, w->Z, nv);
             }
