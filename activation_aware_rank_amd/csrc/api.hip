@@ -1,5 +1,6 @@
 // C-ABI entry points of liblrc: argument validation, then dispatch to the per-op launchers.
 // Nothing is launched when validation fails.
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -36,7 +37,7 @@ struct TimingRec {
     double flops;
 };
 static std::mutex g_tmu;
-static bool g_timing = false;
+static std::atomic<bool> g_timing{false};  // read without the lock on every launch
 static int g_stride = 1;                                    // record every g_stride-th launch
 static std::unordered_map<std::string, int64_t> g_counts;  // launches seen per kernel
 static std::unordered_map<std::string, int> g_kstride;     // per-kernel strides (override g_stride)
@@ -53,6 +54,7 @@ static bool take_event(hipEvent_t *e) {
 }
 
 bool timing_sample(const char *kernel, double work, hipEvent_t *start, hipEvent_t *stop) {
+    if (!g_timing.load(std::memory_order_relaxed)) return false;
     std::lock_guard<std::mutex> lk(g_tmu);
     if (!g_timing) return false;
     const auto ks = g_kstride.find(kernel);

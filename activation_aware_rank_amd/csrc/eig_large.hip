@@ -15,10 +15,13 @@
 //  5. Each column's entry of largest magnitude made positive.
 // Reflector c is H_c = I - tau_c v_c v_c^T with v_c[c+1] = 1 and v_c[r] = 0 for r <= c.
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 #include <cmath>
 #include <map>
 #include <mutex>
+#include <string>
+#include <thread>
 #include <vector>
 
 #include "lrc_internal.h"
@@ -1278,9 +1281,12 @@ struct EigJob {
 
 // Batch members are independent: up to EIG_LANES of them run at once, each on a helper stream
 // of its own with its own workspace, so the per-column launch chains of several matrices
-// overlap (one chain alone leaves most of the GPU idle once the trailing matrix is small).  The
-// helper streams (default priority) and their events are created per device on first use and
-// kept; the caller's stream waits for all of them, so a call stays asynchronous.
+// overlap (one chain alone leaves most of the GPU idle once the trailing matrix is small).  Each
+// lane is fed by a host thread of its own: a chain is two or three small launches per column, and
+// one thread enqueueing for all lanes would both cap the launch rate and stall every lane while
+// one lane's queue is full.  The helper streams (default priority) and their events are created
+// per device on first use and kept; the caller's stream waits for all of them, so a call stays
+// asynchronous (it returns once every launch is enqueued).
 constexpr int EIG_LANES = 4;
 
 struct EigLanes {
@@ -1356,65 +1362,88 @@ struct EigMember {
     int32_t *info;
 };
 
-// All members with n > 128 over up to EIG_LANES helper streams, largest n first; a lane whose
-// member is done takes the next one (its stream runs in order, so the lane's workspace is free by
-// then).  The host feeds the lanes in turn, a few columns at a time.
+// All members with n > 128 over up to EIG_LANES helper streams, largest n first: each lane's
+// thread takes the next member once its own is enqueued (its stream runs in order, so the lane's
+// workspace is free by then).  Which lane runs a member does not change its results: the
+// computation depends only on the member, and every lane's workspace has the same layout.
+template <class T>
+static lrc_status run_member(const EigMember &m, const MultiPlan &p, char *lws, hipStream_t s, LargeWs<T> &w) {
+    Carver cv(lws, p.per);
+    w = LargeWs<T>();
+    layout(cv, w, m.n, m.nv, false);
+    if (!w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
+    EigJob<T> j;
+    j.C = m.C;
+    j.ldc = m.ldc;
+    j.n = m.n;
+    j.lambda = m.lambda;
+    j.V = m.V;
+    j.ldv = m.ldv;
+    j.nv = m.nv;
+    j.info = m.info;
+    j.w = &w;
+    j.s = s;
+    while (!j.done()) {
+        const lrc_status st = j.advance(64);
+        if (st != LRC_OK) return st;
+    }
+    return LRC_OK;
+}
+
 template <class T>
 static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, char *ws, hipStream_t s) {
     std::stable_sort(mem.begin(), mem.end(), [](const EigMember &x, const EigMember &y) { return x.n > y.n; });
     const int lanes = p.lanes;
     LargeWs<T> w[EIG_LANES];
-    EigJob<T> job[EIG_LANES];
-    EigLanes *L = nullptr;
-    std::unique_lock<std::mutex> hold;
-    if (lanes > 1) {
-        lrc_status st = eig_lanes(&L);
-        if (st != LRC_OK) return st;
-        hold = std::unique_lock<std::mutex>(L->busy);
-        LRC_HIP(hipEventRecord(L->start, s));
-        for (int l = 0; l < lanes; ++l) LRC_HIP(hipStreamWaitEvent(L->st[l], L->start, 0));
-    }
-    size_t next = 0;
-    auto begin = [&](int l) -> bool {
-        const EigMember &m = mem[next++];
-        Carver cv(ws + p.per * size_t(l), p.per);
-        w[l] = LargeWs<T>();
-        layout(cv, w[l], m.n, m.nv, false);
-        if (!w[l].bad) return false;
-        EigJob<T> &j = job[l];
-        j = EigJob<T>();
-        j.C = m.C;
-        j.ldc = m.ldc;
-        j.n = m.n;
-        j.lambda = m.lambda;
-        j.V = m.V;
-        j.ldv = m.ldv;
-        j.nv = m.nv;
-        j.info = m.info;
-        j.w = &w[l];
-        j.s = lanes > 1 ? L->st[l] : s;
-        return true;
-    };
-    for (int l = 0; l < lanes; ++l)
-        if (!begin(l)) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
-    for (int active = lanes; active > 0;) {
-        active = 0;
-        for (int l = 0; l < lanes; ++l) {
-            if (job[l].done()) {
-                if (next >= mem.size()) continue;
-                if (!begin(l)) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
-            }
-            lrc_status st = job[l].advance(8);
+    if (lanes <= 1) {
+        for (const EigMember &m : mem) {
+            const lrc_status st = run_member<T>(m, p, ws, s, w[0]);
             if (st != LRC_OK) return st;
-            ++active;
         }
+        return LRC_OK;
     }
-    if (lanes > 1) {
-        for (int l = 0; l < lanes; ++l) {
-            LRC_HIP(hipEventRecord(L->done[l], L->st[l]));
-            LRC_HIP(hipStreamWaitEvent(s, L->done[l], 0));
+    EigLanes *L = nullptr;
+    lrc_status st0 = eig_lanes(&L);
+    if (st0 != LRC_OK) return st0;
+    std::lock_guard<std::mutex> hold(L->busy);
+    int dev = 0;
+    LRC_HIP(hipGetDevice(&dev));
+    LRC_HIP(hipEventRecord(L->start, s));
+    for (int l = 0; l < lanes; ++l) LRC_HIP(hipStreamWaitEvent(L->st[l], L->start, 0));
+    std::atomic<size_t> next{0};
+    std::atomic<bool> stop{false};
+    lrc_status st[EIG_LANES];
+    std::string msg[EIG_LANES];
+    auto lane = [&](int l) {
+        st[l] = LRC_OK;
+        const hipError_t e = hipSetDevice(dev);  // the current device is per thread
+        if (e != hipSuccess) st[l] = hip_fail(e, "hipSetDevice");
+        while (st[l] == LRC_OK && !stop.load()) {
+            const size_t i = next.fetch_add(1);
+            if (i >= mem.size()) break;
+            st[l] = run_member<T>(mem[i], p, ws + p.per * size_t(l), L->st[l], w[l]);
         }
+        if (st[l] != LRC_OK) {
+            msg[l] = lrc_last_error();
+            stop.store(true);
+        }
+    };
+    std::vector<std::thread> th;
+    try {
+        for (int l = 1; l < lanes; ++l) th.emplace_back(lane, l);
+    } catch (...) {
+        stop.store(true);
+        for (auto &t : th) t.join();
+        return fail(LRC_ERR_HIP, "could not start the eigh lane threads");
     }
+    lane(0);
+    for (auto &t : th) t.join();
+    for (int l = 0; l < lanes; ++l) {
+        LRC_HIP(hipEventRecord(L->done[l], L->st[l]));
+        LRC_HIP(hipStreamWaitEvent(s, L->done[l], 0));
+    }
+    for (int l = 0; l < lanes; ++l)
+        if (st[l] != LRC_OK) return fail(st[l], msg[l]);
     return LRC_OK;
 }
 
