@@ -75,8 +75,15 @@ __device__ __forceinline__ T block_sum(T v, T *sh) {
     return r;  // every thread
 }
 
+// Kernel arguments are read from memory by scalar loads, which the compiler issues where each
+// value is first needed, every group followed by a wait for it; in a short kernel these round
+// trips line up one after another before the first global load can start.  Naming all the
+// arguments in one empty asm statement at entry makes it load them in one batch.
+#define LRC_ARGS_AT_ENTRY(...) asm volatile("" ::__VA_ARGS__)
+
 // Sum of at(i) for i = i0, i0 + step, ... < i1 with eight loads in flight (eight running sums,
-// combined in a fixed order); a loop of dependent load-add steps would wait for every load.
+// combined in a fixed order); a loop of dependent load-add steps would wait for every load.  The
+// last (partial) group of eight is loaded under a mask, also in one batch.
 template <class T, class F>
 __device__ __forceinline__ T sum_strided8(F at, int i0, int i1, int step) {
     T a[8];
@@ -90,9 +97,43 @@ __device__ __forceinline__ T sum_strided8(F at, int i0, int i1, int step) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) a[u] += v[u];
     }
-    for (; i < i1; i += step) a[0] += at(i);
+    if (i < i1) {
+        T v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = i + u * step < i1 ? at(i + u * step) : T(0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += v[u];
+    }
     return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
 }
+
+// The same sum in two steps, so that the loads of several sums are in flight together: first()
+// loads the first eight terms under a mask in straight-line code, rest() adds them and any
+// further terms (eight loads at a time).  Terms are summed in the order sum_strided8 uses.
+template <class T>
+struct StridedSum {
+    T v[8];
+    int i0, i1, step;
+    template <class F>
+    __device__ __forceinline__ void first(F at, int a0, int a1, int st) {
+        i0 = a0;
+        i1 = a1;
+        step = st;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = i0 + u * step < i1 ? at(i0 + u * step) : T(0);
+    }
+    template <class F>
+    __device__ __forceinline__ T rest(F at) {
+        for (int i = i0 + 8 * step; i < i1; i += 8 * step) {
+            T w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = i + u * step < i1 ? at(i + u * step) : T(0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] += w[u];
+        }
+        return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    }
+};
 
 // Each column of a panel takes three launches; each global reduction is done by the next launch,
 // redundantly in every block that needs it and always in the same fixed order, so all blocks see
@@ -106,25 +147,6 @@ __device__ __forceinline__ T sum_strided8(F at, int i0, int i1, int step) {
 // The first column of a panel takes k_trd_col0 instead of a previous k_trd_w1col.
 
 // fixed-order sum of p[0..np) by one block: strided per-thread sums, then a tree (every thread)
-template <class T>
-__device__ __forceinline__ T block_sum_array(const T *__restrict__ p, int np, T *red) {
-    T acc = T(0);
-    for (int i = threadIdx.x; i < np; i += blockDim.x) acc += p[i];
-    return block_sum(acc, red);
-}
-
-// Sum over the 64 lanes of each of 64 per-lane values, by a butterfly that halves the values each
-// lane keeps at every step (63 exchanges): afterwards lane l holds the sum of value l.
-template <int ST, class T>
-__device__ __forceinline__ void transpose_sum_stage(T (&p)[64], int lane) {
-    const bool up = (lane & ST) != 0;
-#pragma unroll
-    for (int k = 0; k < ST; ++k) {  // constant trip count: the array stays in registers
-        const T send = up ? p[k] : p[k + ST];
-        const T keep = up ? p[k + ST] : p[k];
-        p[k] = keep + __shfl_xor(send, ST);
-    }
-}
 // One reduce-scatter step over lane bit MBIT: lanes with the bit set keep values HALF .. 2 HALF - 1
 // (moved to 0 .. HALF - 1), the others 0 .. HALF - 1, each summed with the partner's copy.
 template <int HALF, int MBIT, int N, class T>
@@ -137,17 +159,6 @@ __device__ __forceinline__ void rs_step(T (&p)[N], int lane) {
         const T keep = up ? p[k + HALF] : p[k];
         p[k] = keep + __shfl_xor(send, MBIT);
     }
-}
-template <class T>
-__device__ __forceinline__ T wave_transpose_sum64(T (&p)[64]) {
-    const int lane = threadIdx.x & 63;
-    transpose_sum_stage<32>(p, lane);
-    transpose_sum_stage<16>(p, lane);
-    transpose_sum_stage<8>(p, lane);
-    transpose_sum_stage<4>(p, lane);
-    transpose_sum_stage<2>(p, lane);
-    transpose_sum_stage<1>(p, lane);
-    return p[0];
 }
 
 // First column c of a panel (no panel corrections yet): x = row c right of the diagonal,
@@ -201,6 +212,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
                                                   T *__restrict__ colpart, const T *__restrict__ qcol,
                                                   T *__restrict__ qvec, T *__restrict__ spart, T *__restrict__ tau,
                                                   double *__restrict__ e, int NT, int CHK) {
+    LRC_ARGS_AT_ENTRY("s"(A), "s"(lda), "s"(n), "s"(c), "s"(j), "s"(colbuf), "s"(part), "s"(npart), "s"(Vp), "s"(Wp),
+                      "s"(Rt), "s"(rowpart), "s"(colpart), "s"(qcol), "s"(qvec), "s"(spart), "s"(tau), "s"(e),
+                      "s"(NT), "s"(CHK));
     constexpr int TS = SymvTile<T>::TS, EPC = SymvTile<T>::EPC, H = SymvTile<T>::H;
     static_assert(16 * EPC == TS, "tile geometry");
     typedef T vec_t __attribute__((ext_vector_type(EPC)));
@@ -252,12 +266,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int x = t + 256 * u;
         xJ[u] = x < (J1 - J0) * TS ? xraw(int64_t(J0) * TS + x) : T(0);
     }
-    T sacc = T(0);
-    for (int b2 = t; b2 < npart; b2 += 256) sacc += part[b2];
+    const T sacc = sum_strided8<T>([&](int b2) { return part[b2]; }, t, npart, 256);
     const T alpha = colbuf[c + 1];
     T qacc = T(0);  // block 0: W^T x, V^T x, value t % 64, every fourth partial from t / 64
     if (blockIdx.x == 0)
-        for (int b2 = t >> 6; b2 < npart; b2 += 4) qacc += qcol[int64_t(b2) * 2 * NB + (t & 63)];
+        qacc = sum_strided8<T>([&](int b2) { return qcol[int64_t(b2) * 2 * NB + (t & 63)]; }, t >> 6, npart, 4);
     // the reflector of column c: alpha = x[0], sigma2 = ||x[1:]||^2; tau = (beta - alpha)/beta,
     // v = [1, x[1:] / (alpha - beta)], beta = -sign(alpha) ||x||; tau = 0 when x[1:] = 0
     const T sigma2 = block_sum(sacc, sh);
@@ -397,27 +410,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-// Second launch of column c (rows r in [c+1, n), 64 per block, 4 threads per row reducing the symv
-// partials of y = A v):
+// Second launch of column c (rows r in [c+1, n), 64 per block; the block's four waves share every
+// row: wave sub reduces a quarter of the symv partials of y[r] and holds panel columns
+// q = 8 sub .. 8 sub + 7 of the row):
 //   w1[r]   = tau (y[r] - V[r][:j] q1 - W[r][:j] q2)       (q1 = W^T v, q2 = V^T v)
 //   W[r][j] = w1[r] - (tau/2)(w1.v) v[r],  w1.v = tau (v^T y - 2 q1.q2)  (v^T y from the symv's
 //             scalar partials, so no further reduction is needed)
 // and, unless the panel ends here, the first launch of column c+1 for the same rows: row c+1 of the
 // current matrix (the column below the diagonal) with the panel's corrections, ||x||^2 partials and
 // the W^T x, V^T x partials.  Each block forms W[c+1][j] itself from a redundant reduction of y[c+1].
-template <class T>
-__device__ __forceinline__ T symv_y(int64_t r, const T *__restrict__ rowpart, const T *__restrict__ colpart, int NT,
-                                    int CHK, int T0, int sub, int nsub) {
-    constexpr int TS = SymvTile<T>::TS;
-    const int I = int(r / TS), o = int(r % TS);
-    const int nch = int((NT - I + CHK - 1) / CHK);
-    T y = T(0);
-    for (int ch = sub; ch < nch; ch += nsub) y += rowpart[(int64_t(I) * NT + ch) * TS + o];
-    // the column parts of the tiles above: up to NT of them for the last block rows
-    y += sum_strided8<T>([&](int ib) { return colpart[(int64_t(ib) * NT + I) * TS + o]; }, T0 + sub, I, nsub);
-    return y;
-}
-
+// Sums over q are formed per wave and added in wave order; every load of the kernel is issued
+// before the first wait (a wave has at most about 50 in flight).
 template <class T>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int next, T *__restrict__ Vp,
@@ -425,37 +428,53 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
             const T *__restrict__ qvec, const T *__restrict__ spart, int nsp, int NT, int CHK,
             const T *__restrict__ tau, T *__restrict__ colbuf, T *__restrict__ part, T *__restrict__ qcol,
             double *__restrict__ d) {
+    constexpr int QW = NB / 4;  // panel columns per wave
     __shared__ T sh[8];
     __shared__ T qs[2 * NB];
-    __shared__ T ys[4][64];
+    __shared__ T ys[4][64], pw[4][64], pa[4][64];
     __shared__ T vc[NB], wc[NB];
     __shared__ T v1s[NB], w1s[NB];
+    LRC_ARGS_AT_ENTRY("s"(A), "s"(lda), "s"(n), "s"(c), "s"(j), "s"(next), "s"(Vp), "s"(Wp), "s"(rowpart),
+                      "s"(colpart), "s"(qvec), "s"(spart), "s"(nsp), "s"(NT), "s"(CHK), "s"(tau), "s"(colbuf),
+                      "s"(part), "s"(qcol), "s"(d));
     const int T0 = int((c + 1) / SymvTile<T>::TS);
     const int t = threadIdx.x;
     const int rl = t & 63, sub = t >> 6;
     const int64_t r = c + 1 + int64_t(blockIdx.x) * 64 + rl;
+    const bool live = r < n;
     // every independent load first: q, row c+1 of V and W, the v^T y partials, the partials of
-    // y[c+1] and y[r], and (one thread per row) the row's panel values and A[c+1][r]
+    // y[c+1] and y[r], the row's panel values in this wave's columns, V[r][j] and A[c+1][r]
     const T qv = t < 2 * NB ? qvec[t] : T(0);
     T w1row = T(0), v1row = T(0);
     if (t < NB) {
         w1row = Wp[int64_t(t) * n + c + 1];
         v1row = Vp[int64_t(t) * n + c + 1];
     }
-    T sp = T(0);
-    for (int b2 = t; b2 < nsp; b2 += 256) sp += spart[b2];
-    const T ycp = next ? symv_y(c + 1, rowpart, colpart, NT, CHK, T0, t, 256) : T(0);
-    const T yr = r < n ? symv_y(r, rowpart, colpart, NT, CHK, T0, sub, 4) : T(0);
-    T vrow[NB], wrow[NB];
-    T aold = T(0);
-    const bool mine = sub == 0 && r < n;
+    // y[x] = sum of the row parts of block row I = x / TS (chunks ch) and the column parts of the
+    // tiles above it (block rows T0 .. I-1), each sum split over the threads given to it
+    constexpr int TS = SymvTile<T>::TS;
+    auto rowp = [&](int64_t x) { return [=](int ch) { return rowpart[(x / TS * NT + ch) * TS + x % TS]; }; };
+    auto colp = [&](int64_t x) { return [=](int ib) { return colpart[(int64_t(ib) * NT + x / TS) * TS + x % TS]; }; };
+    auto nchunks = [&](int64_t x) { return int((NT - x / TS + CHK - 1) / CHK); };
+    StridedSum<T> s_sp, s_cr, s_rr, s_rc;
+    s_sp.first([&](int b2) { return spart[b2]; }, t, nsp, 256);
+    s_cr.first(rowp(c + 1), t, next ? nchunks(c + 1) : 0, 256);  // y[c+1]: no tiles above (I = T0)
+    const int Ir = int(r / TS);
+    s_rr.first(rowp(r), sub, live ? nchunks(r) : 0, 4);
+    s_rc.first(colp(r), T0 + sub, live ? Ir : 0, 4);
+    T vr[QW], wr[QW];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-        vrow[q] = (mine && q <= j) ? Vp[int64_t(q) * n + r] : T(0);
-        wrow[q] = (mine && q < j) ? Wp[int64_t(q) * n + r] : T(0);
+    for (int u = 0; u < QW; ++u) {
+        const int q = QW * sub + u;
+        vr[u] = (live && q <= j) ? Vp[int64_t(q) * n + r] : T(0);
+        wr[u] = (live && q < j) ? Wp[int64_t(q) * n + r] : T(0);
     }
-    if (mine && next) aold = A[(c + 1) * lda + r];
+    const T vj = live ? Vp[int64_t(j) * n + r] : T(0);
+    const T aold = (live && next) ? A[(c + 1) * lda + r] : T(0);
     const T tv = tau[c];
+    const T sp = s_sp.rest([&](int b2) { return spart[b2]; });
+    const T ycp = s_cr.rest(rowp(c + 1));
+    const T yr = s_rr.rest(rowp(r)) + s_rc.rest(colp(r));
     if (t < 2 * NB) qs[t] = qv;
     if (t < NB) {  // row c+1 of the panel, for the thread that forms W[c+1][j]
         w1s[t] = w1row;
@@ -473,6 +492,11 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
         sh[sub] = vty;
         sh[4 + sub] = yc;
     }
+    // this wave's share of V[r][:j] q1 + W[r][:j] q2
+    T pwv = T(0);
+#pragma unroll
+    for (int u = 0; u < QW; ++u) pwv += vr[u] * qs[QW * sub + u] + wr[u] * qs[NB + QW * sub + u];
+    pw[sub][rl] = pwv;
     __syncthreads();
     vty = (sh[0] + sh[1]) + (sh[2] + sh[3]);
     yc = (sh[4] + sh[5]) + (sh[6] + sh[7]);
@@ -490,47 +514,52 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
         wc[q] = wv;
         vc[q] = q <= j ? v1row : T(0);
     }
-    __syncthreads();
-    T ss = T(0);
-    T pq[64];
-#pragma unroll
-    for (int q = 0; q < 64; ++q) pq[q] = T(0);
-    if (mine) {
-        T w = (ys[0][rl] + ys[1][rl]) + (ys[2][rl] + ys[3][rl]);
-#pragma unroll
-        for (int q = 0; q < NB; ++q) w -= vrow[q] * qs[q] + wrow[q] * qs[NB + q];
-        T vj = T(0);
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-            if (q == j) vj = vrow[q];
-        const T wj = tv * w - half * vj;
-        Wp[int64_t(j) * n + r] = wj;
-        if (next) {  // row c+1 of the current matrix, corrected by the panel's first j+1 columns
-#pragma unroll
-            for (int q = 0; q < NB; ++q)
-                if (q == j) wrow[q] = wj;
-            T a = aold;
-#pragma unroll
-            for (int q = 0; q < NB; ++q) a -= vrow[q] * wc[q] + wrow[q] * vc[q];
-            A[(c + 1) * lda + r] = a;
-            colbuf[r] = a;
-            if (r == c + 1) d[c + 1] = double(a);
-            if (r >= c + 3) {
-                ss = a * a;
-#pragma unroll
-                for (int q = 0; q < NB; ++q) {
-                    pq[q] = wrow[q] * a;
-                    pq[NB + q] = vrow[q] * a;
-                }
-            }
-        }
-    }
+    const T w = ((ys[0][rl] + ys[1][rl]) + (ys[2][rl] + ys[3][rl])) -
+                ((pw[0][rl] + pw[1][rl]) + (pw[2][rl] + pw[3][rl]));
+    const T wj = tv * w - half * vj;
+    if (sub == 0 && live) Wp[int64_t(j) * n + r] = wj;
     if (!next) return;
+    __syncthreads();
+    // row c+1 of the current matrix, corrected by the panel's first j+1 columns (W[r][j] = wj)
+#pragma unroll
+    for (int u = 0; u < QW; ++u)
+        if (QW * sub + u == j) wr[u] = wj;
+    T pav = T(0);
+#pragma unroll
+    for (int u = 0; u < QW; ++u) pav += vr[u] * wc[QW * sub + u] + wr[u] * vc[QW * sub + u];
+    pa[sub][rl] = pav;
+    __syncthreads();
+    const T a = aold - ((pa[0][rl] + pa[1][rl]) + (pa[2][rl] + pa[3][rl]));
+    if (sub == 0 && live) {
+        A[(c + 1) * lda + r] = a;
+        colbuf[r] = a;
+        if (r == c + 1) d[c + 1] = double(a);
+    }
+    const bool tailrow = live && r >= c + 3;  // rows of x[2:]
+    T ss = (sub == 0 && tailrow) ? a * a : T(0);
+    // W^T x and V^T x over the block's rows: this wave's 2 QW values summed over its 64 lanes by a
+    // reduce-scatter over lane bits 5 .. 2 and a sum over bits 1, 0; lane l ends with value
+    // (l >> 2) & 15: W part for values 0 .. QW-1, V part for QW .. 2 QW - 1
+    static_assert(QW == 8, "reduce-scatter layout");
+    T pq[2 * QW];
+#pragma unroll
+    for (int u = 0; u < QW; ++u) {
+        pq[u] = tailrow ? wr[u] * a : T(0);
+        pq[QW + u] = tailrow ? vr[u] * a : T(0);
+    }
+    rs_step<8, 32>(pq, rl);
+    rs_step<4, 16>(pq, rl);
+    rs_step<2, 8>(pq, rl);
+    rs_step<1, 4>(pq, rl);
+    T qsum = pq[0];
+    qsum += __shfl_xor(qsum, 2);
+    qsum += __shfl_xor(qsum, 1);
     ss = block_sum(ss, sh);
     if (t == 0) part[blockIdx.x] = ss;
-    if (sub == 0) {
-        const T qsum = wave_transpose_sum64(pq);
-        qcol[int64_t(blockIdx.x) * 2 * NB + rl] = qsum;
+    if ((rl & 3) == 0) {
+        const int v = (rl >> 2) & 15;
+        const int idx = v < QW ? QW * sub + v : NB + QW * sub + (v - QW);
+        qcol[int64_t(blockIdx.x) * 2 * NB + idx] = qsum;
     }
 }
 
@@ -1178,10 +1207,11 @@ struct EigJob {
     void column() {
         const int64_t lda = w->lda;
         const int j = int(c - p0);
-        // tiles per symv work item: the largest of 8, 4, 2 that still gives >= 512 items
+        // tiles per symv work item: the largest of 8, 4, 2 that still gives >= 256 items (more,
+        // smaller items only add dispatch time: workgroups start at about 100 per microsecond)
         const int mt = NT - int((c + 1) / SymvTile<T>::TS);
         int chk = 8;
-        while (chk > 1 && symv_items(mt, chk) < 512) chk >>= 1;
+        while (chk > 1 && symv_items(mt, chk) < 256) chk >>= 1;
         const int nitems = int(symv_items(mt, chk));
         // algorithmic bytes: the upper triangle of the trailing matrix, read once
         const double m1 = double(n - c - 1);
