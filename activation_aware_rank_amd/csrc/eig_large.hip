@@ -563,45 +563,123 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
     }
 }
 
-// A[r][s] -= sum_q V[r][q] W[s][q] + W[r][q] V[s][q] for p <= r, s < n on the upper 64 x 64 tiles
-// (tiles below the diagonal exit at once)
+// Rank-2 jn update of the trailing matrix, A[r][s] -= sum_q V[r][q] W[s][q] + W[r][q] V[s][q] for
+// p <= r, s < n, over the 64 x 64 tiles (I, J) with I <= J (block u: column J, row I, numbered
+// column by column).  A tile is the product [V_I W_I] [W_J V_J]^T, a contraction of length 2 NB
+// (panel columns q >= jn are zero), staged k-major in LDS and formed on MFMA by 4 waves of
+// 32 x 32: fp32 32x32x2 (one product per lane and k slice), fp64 16x16x4 (2 x 2 products).
+// The lower half of a diagonal tile is updated too and never read; the padding columns [n, lda)
+// are left alone.
+template <class T>
+struct TrailMfma;
+template <>
+struct TrailMfma<float> {
+    typedef f32x16_t acc_t[1][1];
+    static __device__ __forceinline__ void zero(acc_t &c) { c[0][0] = f32x16_t{}; }
+    template <int LD>
+    static __device__ __forceinline__ void run(const float (*ar)[LD], const float (*bs)[LD], int wr, int wc, int lane,
+                                               acc_t &c) {
+#pragma unroll 8
+        for (int k = 0; k < 2 * NB; k += 2) {
+            const float a = ar[k + (lane >> 5)][wr + (lane & 31)];
+            const float b = bs[k + (lane >> 5)][wc + (lane & 31)];
+            c[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c[0][0], 0, 0, 0);
+        }
+    }
+    // element r of the lane: row and column within the wave's 32 x 32 tile
+    static __device__ __forceinline__ int row(int x, int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
+    static __device__ __forceinline__ int col(int y, int lane) { return lane & 31; }
+    static __device__ __forceinline__ float get(const acc_t &c, int x, int y, int r) { return c[0][0][r]; }
+    static constexpr int NX = 1, NR = 16;
+};
+template <>
+struct TrailMfma<double> {
+    typedef f64x4_t acc_t[2][2];
+    static __device__ __forceinline__ void zero(acc_t &c) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) c[x][y] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    }
+    template <int LD>
+    static __device__ __forceinline__ void run(const double (*ar)[LD], const double (*bs)[LD], int wr, int wc, int lane,
+                                               acc_t &c) {
+#pragma unroll 4
+        for (int k = 0; k < 2 * NB; k += 4) {
+            const int kk = k + (lane >> 4);
+            const double a0 = ar[kk][wr + (lane & 15)], a1 = ar[kk][wr + 16 + (lane & 15)];
+            const double b0 = bs[kk][wc + (lane & 15)], b1 = bs[kk][wc + 16 + (lane & 15)];
+            c[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, c[0][0], 0, 0, 0);
+            c[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, c[0][1], 0, 0, 0);
+            c[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, c[1][0], 0, 0, 0);
+            c[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, c[1][1], 0, 0, 0);
+        }
+    }
+    static __device__ __forceinline__ int row(int x, int r, int lane) { return x * 16 + r * 4 + (lane >> 4); }
+    static __device__ __forceinline__ int col(int y, int lane) { return y * 16 + (lane & 15); }
+    static __device__ __forceinline__ double get(const acc_t &c, int x, int y, int r) { return c[x][y][r]; }
+    static constexpr int NX = 2, NR = 4;
+};
+
 template <class T>
 __global__ void __launch_bounds__(256) k_trailing(T *__restrict__ A, int64_t lda, int64_t n, int64_t p, int jn,
                                                   const T *__restrict__ Vp, const T *__restrict__ Wp) {
-    if (blockIdx.y > blockIdx.x) return;
-    __shared__ T vr[64][NB + 1], wr[64][NB + 1], vs_[64][NB + 1], ws_[64][NB + 1];
-    const int64_t r0 = p + int64_t(blockIdx.y) * 64, s0 = p + int64_t(blockIdx.x) * 64;
-    for (int e = threadIdx.x; e < 64 * NB; e += 256) {
-        const int q = e / 64, rr = e % 64;
-        const bool okr = r0 + rr < n && q < jn, oks = s0 + rr < n && q < jn;
-        vr[rr][q] = okr ? Vp[int64_t(q) * n + r0 + rr] : T(0);
-        wr[rr][q] = okr ? Wp[int64_t(q) * n + r0 + rr] : T(0);
-        vs_[rr][q] = oks ? Vp[int64_t(q) * n + s0 + rr] : T(0);
-        ws_[rr][q] = oks ? Wp[int64_t(q) * n + s0 + rr] : T(0);
-    }
-    __syncthreads();
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    T acc[4][4] = {};
-    for (int q = 0; q < jn; ++q) {
-        T a1[4], a2[4], b1[4], b2[4];
+    using M = TrailMfma<T>;
+    constexpr int LD = 64 + 4;
+    __shared__ T ar[2 * NB][LD], bs[2 * NB][LD];
+    const int u = blockIdx.x;
+    int J = int((sqrtf(8.f * float(u) + 1.f) - 1.f) * 0.5f);
+    while (J * (J + 1) / 2 > u) --J;
+    while ((J + 1) * (J + 2) / 2 <= u) ++J;
+    const int I = u - J * (J + 1) / 2;
+    const int64_t r0 = p + int64_t(I) * 64, s0 = p + int64_t(J) * 64;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wr = (wv >> 1) * 32, wc = (wv & 1) * 32;
+    // every load first (one round trip): the operands, k-major (ar[k][i] = V[r0+i][k] for k < NB,
+    // W[r0+i][k-NB] above; bs[k][j] = W[s0+j][k], V[s0+j][k-NB]), and this lane's entries of A
+    constexpr int PER = 2 * NB * 64 / 256;
+    T va[PER], vb[PER];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a1[u] = vr[ty * 4 + u][q];
-            a2[u] = wr[ty * 4 + u][q];
-            b1[u] = ws_[tx * 4 + u][q];
-            b2[u] = vs_[tx * 4 + u][q];
+    for (int u = 0; u < PER; ++u) {
+        const int e = threadIdx.x + 256 * u;
+        const int k = e >> 6, i = e & 63, q = k % NB;
+        const bool hiq = k >= NB;
+        const bool okr = r0 + i < n && q < jn, oks = s0 + i < n && q < jn;
+        va[u] = okr ? (hiq ? Wp : Vp)[int64_t(q) * n + r0 + i] : T(0);
+        vb[u] = oks ? (hiq ? Vp : Wp)[int64_t(q) * n + s0 + i] : T(0);
+    }
+    T aold[M::NX][M::NX][M::NR];
+#pragma unroll
+    for (int x = 0; x < M::NX; ++x)
+#pragma unroll
+        for (int y = 0; y < M::NX; ++y) {
+            const int64_t sc = s0 + wc + M::col(y, lane);
+#pragma unroll
+            for (int r = 0; r < M::NR; ++r) {
+                const int64_t rr = r0 + wr + M::row(x, r, lane);
+                aold[x][y][r] = (rr < n && sc < n) ? A[rr * lda + sc] : T(0);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) acc[u][w] += a1[u] * b1[w] + a2[u] * b2[w];
+    for (int u = 0; u < PER; ++u) {
+        const int e = threadIdx.x + 256 * u;
+        ar[e >> 6][e & 63] = va[u];
+        bs[e >> 6][e & 63] = vb[u];
     }
+    __syncthreads();
+    typename M::acc_t acc;
+    M::zero(acc);
+    M::template run<LD>(ar, bs, wr, wc, lane, acc);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int x = 0; x < M::NX; ++x)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int64_t r = r0 + ty * 4 + u, s = s0 + tx * 4 + w;
-            if (r < n && s < n) A[r * lda + s] -= acc[u][w];
+        for (int y = 0; y < M::NX; ++y) {
+            const int64_t sc = s0 + wc + M::col(y, lane);
+#pragma unroll
+            for (int r = 0; r < M::NR; ++r) {
+                const int64_t rr = r0 + wr + M::row(x, r, lane);
+                if (rr < n && sc < n) A[rr * lda + sc] = aold[x][y][r] - M::get(acc, x, y, r);
+            }
         }
 }
 
@@ -1246,10 +1324,9 @@ struct EigJob {
                 if (++c < p1) continue;
                 LRC_LAUNCH_CHECK("tridiagonal panel");
                 if (p1 < n - 1) {
-                    const int64_t m = n - p1;
-                    dim3 g(cdiv(m, 64), cdiv(m, 64));
-                    hipLaunchKernelGGL(k_trailing<T>, g, dim3(256), 0, s, w->A, w->lda, n, p1, int(p1 - p0), w->Vp,
-                                       w->Wp);
+                    const int64_t nt = cdiv(n - p1, 64);  // tile rows of the trailing matrix
+                    hipLaunchKernelGGL(k_trailing<T>, dim3(unsigned(nt * (nt + 1) / 2)), dim3(256), 0, s, w->A, w->lda,
+                                       n, p1, int(p1 - p0), w->Vp, w->Wp);
                     LRC_LAUNCH_CHECK("k_trailing");
                 }
                 p0 += NB;
