@@ -204,8 +204,22 @@ __host__ __device__ __forceinline__ int64_t symv_items(int64_t m, int64_t ch) {
     return ch * q * (q + 1) / 2 + r * (q + 1);
 }
 
+// Tiles per wave of a symmetric-product work item (1 or 2), and waves per SIMD.  One tile per wave
+// keeps a wave under 128 registers, so four workgroups share a CU: while one forms its products
+// from registers the others' loads are in flight (two tiles per wave, two workgroups per CU
+// keep the memory system busy for a smaller share of the time).
+#ifndef SYMV_TPW
+#define SYMV_TPW 1
+#endif
+#ifndef SYMV_WPE
+#define SYMV_WPE (SYMV_TPW == 1 ? 4 : 2)
+#endif
+#ifndef SYMV_MIN_ITEMS
+#define SYMV_MIN_ITEMS 256
+#endif
+
 template <class T>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) k_trd_symv(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SYMV_WPE, SYMV_WPE))) k_trd_symv(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j,
                                                   const T *__restrict__ colbuf, const T *__restrict__ part,
                                                   int npart, T *__restrict__ Vp, const T *__restrict__ Wp,
                                                   T *__restrict__ Rt, T *__restrict__ rowpart,
@@ -219,7 +233,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     static_assert(16 * EPC == TS, "tile geometry");
     typedef T vec_t __attribute__((ext_vector_type(EPC)));
     __shared__ __attribute__((aligned(16))) T vI[TS];
-    __shared__ __attribute__((aligned(16))) T vJ[8 * TS];
+    constexpr int NVJ = 4 * SYMV_TPW * TS;            // v values of an item's column tiles
+    constexpr int XJ = NVJ >= 256 ? NVJ / 256 : 1;     // ... per thread
+    __shared__ __attribute__((aligned(16))) T vJ[NVJ];
     __shared__ T rowacc[4][TS];
     __shared__ T dcol[4][TS];
     __shared__ T qr[256];
@@ -241,11 +257,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T *>(A + int64_t(i) * TS * lda), short(0), int(int64_t(rows_i) * lda * int64_t(sizeof(T))),
         0x00020000);
-    // Every load that does not depend on the reflector is issued first: this wave's first tile,
-    // the raw column values behind v, the ||x||^2 partials, and (block 0) the W^T x, V^T x partials.
-    // A work item has at most 8 tiles, so a wave has at most two (J0 + wave and J0 + wave + 4):
-    // both are loaded here, into two register sets.
-    u32x4_t pre[2][TS / 4];
+    // Every load that does not depend on the reflector is issued first: this wave's tiles, the raw
+    // column values behind v, the ||x||^2 partials, and (block 0) the W^T x, V^T x partials.  A work
+    // item has at most 4 SYMV_TPW tiles, so wave w has at most SYMV_TPW of them (J0 + w, and
+    // J0 + w + 4 when SYMV_TPW = 2), each loaded into a register set of its own.
+    u32x4_t pre[SYMV_TPW][TS / 4];
     auto tile_load = [&](int J, u32x4_t (&dst)[TS / 4]) {
 #pragma unroll
         for (int u = 0; u < TS / 4; ++u) {  // TS rows x 16 chunks, 64 lanes
@@ -257,12 +273,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     const int Jf = J0 + wave;
     if (Jf < J1) tile_load(Jf, pre[0]);
-    if (Jf + 4 < J1) tile_load(Jf + 4, pre[1]);
+    if (SYMV_TPW == 2 && Jf + 4 < J1) tile_load(Jf + 4, pre[SYMV_TPW - 1]);
     auto xraw = [&](int64_t x) -> T { return (x <= c + 1 || x >= n) ? T(0) : colbuf[x]; };
     const T xI = t < TS ? xraw(int64_t(i) * TS + t) : T(0);
-    T xJ[8 * TS / 256];
+    T xJ[XJ];
 #pragma unroll
-    for (int u = 0; u < 8 * TS / 256; ++u) {
+    for (int u = 0; u < XJ; ++u) {
         const int x = t + 256 * u;
         xJ[u] = x < (J1 - J0) * TS ? xraw(int64_t(J0) * TS + x) : T(0);
     }
@@ -292,7 +308,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     auto vof = [&](int64_t x, T raw) -> T { return x == c + 1 ? T(1) : raw * scale; };
     if (t < TS) vI[t] = vof(int64_t(i) * TS + t, xI);
 #pragma unroll
-    for (int u = 0; u < 8 * TS / 256; ++u) {
+    for (int u = 0; u < XJ; ++u) {
         const int x = t + 256 * u;
         if (x < (J1 - J0) * TS) vJ[x] = vof(int64_t(J0) * TS + x, xJ[u]);
     }
@@ -320,7 +336,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     T dcs = T(0);   // diagonal tile: this lane's column sum, added to the row of the same index
     bool had_diag = false;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < SYMV_TPW; ++tt) {
         const int J = Jf + 4 * tt;
         if (J >= J1) break;
         const bool diag = (J == i);
@@ -1285,11 +1301,12 @@ struct EigJob {
     void column() {
         const int64_t lda = w->lda;
         const int j = int(c - p0);
-        // tiles per symv work item: the largest of 8, 4, 2 that still gives >= 256 items (more,
-        // smaller items only add dispatch time: workgroups start at about 100 per microsecond)
+        // tiles per symv work item: the largest power of two up to 4 SYMV_TPW that still gives
+        // >= SYMV_MIN_ITEMS items (more, smaller items only add dispatch time: workgroups start at
+        // about 100 per microsecond)
         const int mt = NT - int((c + 1) / SymvTile<T>::TS);
-        int chk = 8;
-        while (chk > 1 && symv_items(mt, chk) < 256) chk >>= 1;
+        int chk = 4 * SYMV_TPW;
+        while (chk > 1 && symv_items(mt, chk) < SYMV_MIN_ITEMS) chk >>= 1;
         const int nitems = int(symv_items(mt, chk));
         // algorithmic bytes: the upper triangle of the trailing matrix, read once
         const double m1 = double(n - c - 1);
