@@ -702,7 +702,16 @@ __global__ void __launch_bounds__(256) k_trailing(T *__restrict__ A, int64_t lda
 // ---------------------------------------------------------------------------------------------
 // 2. bisection (fp64)
 // ---------------------------------------------------------------------------------------------
-// number of eigenvalues of T strictly less than x (Sturm sequence of the LDL^T of T - x I)
+// 1/q from the hardware estimate and one Newton step, r1 = r0 (2 - q r0) (the estimate's relative
+// error squared, so within a few units in the last place); a correctly rounded division is a
+// chain about three times as long, and the Sturm recurrence is one such step after another.
+__device__ __forceinline__ double recip_nr(double q) {
+    const double r0 = __builtin_amdgcn_rcp(q);
+    return fma(r0, fma(-q, r0, 1.0), r0);
+}
+
+// number of eigenvalues of T strictly less than x (Sturm sequence of the LDL^T of T - x I); the
+// pivots stay away from zero (|q| >= pivmin), so 1/q is finite
 __device__ __forceinline__ int sturm_count(const double *__restrict__ d, const double *__restrict__ e2, int64_t n,
                                            double x, double pivmin) {
     int cnt = 0;
@@ -720,13 +729,13 @@ __device__ __forceinline__ int sturm_count(const double *__restrict__ d, const d
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            q = dd[u] - x - ee[u] / q;
+            q = (dd[u] - x) - ee[u] * recip_nr(q);
             if (fabs(q) < pivmin) q = -pivmin;
             if (q < 0.0) ++cnt;
         }
     }
     for (; i < n; ++i) {
-        q = d[i] - x - e2[i - 1] / q;
+        q = (d[i] - x) - e2[i - 1] * recip_nr(q);
         if (fabs(q) < pivmin) q = -pivmin;
         if (q < 0.0) ++cnt;
     }
