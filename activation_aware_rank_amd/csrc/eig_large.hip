@@ -826,127 +826,168 @@ __device__ __forceinline__ double hash_unit(uint64_t x) {
     return double(x >> 11) * (1.0 / 9007199254740992.0) * 2.0 - 1.0;  // [-1, 1)
 }
 
+// Rows of a sweep in batches of IB, the next batch's loads in flight while the current one is
+// processed.  The loads use clamped (always valid) row indices, so they are unconditional; the
+// processing step skips rows outside the sweep.
+constexpr int IB = 8;
+template <class Buf, class Load, class Proc>
+__device__ __forceinline__ void sweep_pipelined(int64_t nbatch, const Load &load, const Proc &proc) {
+    Buf s0, s1;
+    load(int64_t(0), s0);
+    int64_t b = 0;
+    for (; b + 1 < nbatch; b += 2) {
+        load(b + 1, s1);
+        proc(b, s0);
+        load(b + 2, s0);
+        proc(b + 1, s1);
+    }
+    if (b < nbatch) proc(b, s0);
+}
+
 __global__ void __launch_bounds__(64) k_invit(const double *__restrict__ d, const double *__restrict__ e, int64_t n,
                                               const double *__restrict__ lam_asc, const double *__restrict__ bounds,
-                                              int64_t nv, double *__restrict__ Z, double *__restrict__ U0,
-                                              double *__restrict__ U1, double *__restrict__ U2, double *__restrict__ ML,
-                                              uint8_t *__restrict__ SW) {
+                                              int64_t nv, double *__restrict__ Z, double2 *__restrict__ PU,
+                                              double2 *__restrict__ PD, uint8_t *__restrict__ SW) {
     const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (j >= nv) return;
     const double lam = lam_asc[n - 1 - j];
     const double tnorm = bounds[3];
     const double tiny = DBL_EPSILON * fmax(tnorm, DBL_MIN);
-    // LU with partial pivoting of T - lam I, once: rows k of U in (U0 = 1/pivot, U1, U2), the
-    // multiplier of step k in ML and whether rows k, k+1 were swapped in SW; the start vector is
-    // eliminated on the way
+    auto at = [&](int64_t k) { return k * nv + j; };
+    // LU with partial pivoting of T - lam I, once: row k of U in PU[k] = (U1, U2) and PD[k].x = 1/U0,
+    // the multiplier of step k in PD[k].y and whether rows k, k+1 were swapped in SW[k]; the start
+    // vector is eliminated on the way.  The entries of T for IB steps are loaded first.
     double u0 = d[0] - lam, u1 = n > 1 ? e[0] : 0.0, u2 = 0.0;
     double bcur = hash_unit(uint64_t(j) + 1);
-    for (int64_t k = 0; k < n - 1; ++k) {
-        const double l = e[k], dd = d[k + 1] - lam, ee = k + 1 < n - 1 ? e[k + 1] : 0.0;
-        const double bnext = hash_unit(uint64_t(k + 1) * 0x9E3779B97F4A7C15ULL + uint64_t(j) + 1);
-        double p0, p1, p2, bp, mlt;
-        uint8_t sw;
-        if (fabs(l) > fabs(u0)) {
-            mlt = u0 / l;
-            sw = 1;
-            p0 = l; p1 = dd; p2 = ee; bp = bnext;
-            u0 = u1 - mlt * dd; u1 = u2 - mlt * ee; bcur = bcur - mlt * bnext;
-        } else {
-            if (u0 == 0.0) u0 = tiny;
-            mlt = l / u0;
-            sw = 0;
-            p0 = u0; p1 = u1; p2 = u2; bp = bcur;
-            u0 = dd - mlt * u1; u1 = ee - mlt * u2; bcur = bnext - mlt * bcur;
+    for (int64_t k0 = 0; k0 < n - 1; k0 += IB) {
+        double ev[IB + 1], dv[IB];
+#pragma unroll
+        for (int u = 0; u <= IB; ++u) ev[u] = k0 + u < n - 1 ? e[k0 + u] : 0.0;
+#pragma unroll
+        for (int u = 0; u < IB; ++u) dv[u] = k0 + u + 1 < n ? d[k0 + u + 1] : 0.0;
+#pragma unroll
+        for (int u = 0; u < IB; ++u) {
+            const int64_t k = k0 + u;
+            if (k >= n - 1) break;
+            const double l = ev[u], dd = dv[u] - lam, ee = ev[u + 1];  // ev[u + 1] = e[k + 1], 0 past the end
+            const double bnext = hash_unit(uint64_t(k + 1) * 0x9E3779B97F4A7C15ULL + uint64_t(j) + 1);
+            double p0, p1, p2, bp, mlt;
+            uint8_t sw;
+            if (fabs(l) > fabs(u0)) {
+                mlt = u0 / l;
+                sw = 1;
+                p0 = l; p1 = dd; p2 = ee; bp = bnext;
+                u0 = u1 - mlt * dd; u1 = u2 - mlt * ee; bcur = bcur - mlt * bnext;
+            } else {
+                if (u0 == 0.0) u0 = tiny;
+                mlt = l / u0;
+                sw = 0;
+                p0 = u0; p1 = u1; p2 = u2; bp = bcur;
+                u0 = dd - mlt * u1; u1 = ee - mlt * u2; bcur = bnext - mlt * bcur;
+            }
+            u2 = 0.0;
+            PU[at(k)] = double2{p1, p2};
+            PD[at(k)] = double2{1.0 / p0, mlt};
+            SW[at(k)] = sw;
+            Z[at(k)] = bp;
         }
-        u2 = 0.0;
-        U0[k * nv + j] = 1.0 / p0;
-        U1[k * nv + j] = p1;
-        U2[k * nv + j] = p2;
-        ML[k * nv + j] = mlt;
-        SW[k * nv + j] = sw;
-        Z[k * nv + j] = bp;
     }
     if (u0 == 0.0) u0 = tiny;
-    U0[(n - 1) * nv + j] = 1.0 / u0;
-    Z[(n - 1) * nv + j] = bcur;
+    PD[at(n - 1)] = double2{1.0 / u0, 0.0};
+    Z[at(n - 1)] = bcur;
     // three steps of inverse iteration; each back substitution's result is scaled by 1/max when
     // it is read by the next sweep (the elimination of the next step, or the final normalisation)
+    struct EBuf {
+        double bn[IB];
+        double2 pd[IB];
+        uint8_t sw[IB];
+    };
+    struct BBuf {
+        double z[IB];
+        double2 pu[IB], pd[IB];
+    };
     double scl = 1.0;
+    const int64_t nb = (n - 1 + IB - 1) / IB;  // batches over rows 0 .. n-2
     for (int iter = 0; iter < 3; ++iter) {
-        if (iter > 0) {  // apply the stored elimination to the new right-hand side
-            double bc = Z[j] * scl;
-            int64_t k = 0;
-            for (; k + 8 <= n - 1; k += 8) {
-                double bn[8], ml[8];
-                uint8_t sw[8];
+        if (iter > 0) {  // apply the stored elimination to the new right-hand side, rows 0 .. n-2
+            double bc = Z[at(0)] * scl;
+            sweep_pipelined<EBuf>(
+                nb,
+                [&](int64_t bt, EBuf &B) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    bn[u] = Z[(k + u + 1) * nv + j] * scl;
-                    ml[u] = ML[(k + u) * nv + j];
-                    sw[u] = SW[(k + u) * nv + j];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    if (sw[u]) {
-                        Z[(k + u) * nv + j] = bn[u];
-                        bc = bc - ml[u] * bn[u];
-                    } else {
-                        Z[(k + u) * nv + j] = bc;
-                        bc = bn[u] - ml[u] * bc;
+                    for (int u = 0; u < IB; ++u) {
+                        const int64_t k = min(bt * IB + u, n - 2);
+                        B.bn[u] = Z[at(k + 1)];
+                        B.pd[u] = PD[at(k)];
+                        B.sw[u] = SW[at(k)];
                     }
-                }
-            }
-            for (; k < n - 1; ++k) {
-                const double bn = Z[(k + 1) * nv + j] * scl, mlt = ML[k * nv + j];
-                if (SW[k * nv + j]) {
-                    Z[k * nv + j] = bn;
-                    bc = bc - mlt * bn;
-                } else {
-                    Z[k * nv + j] = bc;
-                    bc = bn - mlt * bc;
-                }
-            }
-            Z[(n - 1) * nv + j] = bc;
-        }
-        // back substitution with U; the largest entry sets the next scale
-        double y2 = 0.0, y1 = Z[(n - 1) * nv + j] * U0[(n - 1) * nv + j], ymax = fabs(y1);
-        Z[(n - 1) * nv + j] = y1;
-        int64_t k = n - 2;
-        for (; k - 7 >= 0; k -= 8) {
-            double zz[8], a0[8], a1[8], a2[8];
+                },
+                [&](int64_t bt, const EBuf &B) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t kk = k - u;
-                zz[u] = Z[kk * nv + j];
-                a0[u] = U0[kk * nv + j];
-                a1[u] = U1[kk * nv + j];
-                a2[u] = U2[kk * nv + j];
-            }
+                    for (int u = 0; u < IB; ++u) {
+                        const int64_t k = bt * IB + u;
+                        if (k >= n - 1) break;
+                        const double bn = B.bn[u] * scl, mlt = B.pd[u].y;
+                        if (B.sw[u]) {
+                            Z[at(k)] = bn;
+                            bc = bc - mlt * bn;
+                        } else {
+                            Z[at(k)] = bc;
+                            bc = bn - mlt * bc;
+                        }
+                    }
+                });
+            Z[at(n - 1)] = bc;
+        }
+        // back substitution with U, rows n-2 .. 0; the largest entry sets the next scale
+        double y2 = 0.0, y1 = Z[at(n - 1)] * PD[at(n - 1)].x, ymax = fabs(y1);
+        Z[at(n - 1)] = y1;
+        sweep_pipelined<BBuf>(
+            nb,
+            [&](int64_t bt, BBuf &B) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const double y = (zz[u] - a1[u] * y1 - a2[u] * y2) * a0[u];
-                Z[(k - u) * nv + j] = y;
-                ymax = fmax(ymax, fabs(y));
-                y2 = y1;
-                y1 = y;
-            }
-        }
-        for (; k >= 0; --k) {
-            const double y = (Z[k * nv + j] - U1[k * nv + j] * y1 - U2[k * nv + j] * y2) * U0[k * nv + j];
-            Z[k * nv + j] = y;
-            ymax = fmax(ymax, fabs(y));
-            y2 = y1;
-            y1 = y;
-        }
+                for (int u = 0; u < IB; ++u) {
+                    const int64_t k = max(n - 2 - (bt * IB + u), int64_t(0));
+                    B.z[u] = Z[at(k)];
+                    B.pu[u] = PU[at(k)];
+                    B.pd[u] = PD[at(k)];
+                }
+            },
+            [&](int64_t bt, const BBuf &B) {
+#pragma unroll
+                for (int u = 0; u < IB; ++u) {
+                    const int64_t k = n - 2 - (bt * IB + u);
+                    if (k < 0) break;
+                    const double y = (B.z[u] - B.pu[u].x * y1 - B.pu[u].y * y2) * B.pd[u].x;
+                    Z[at(k)] = y;
+                    ymax = fmax(ymax, fabs(y));
+                    y2 = y1;
+                    y1 = y;
+                }
+            });
         scl = ymax > 0.0 ? 1.0 / ymax : 1.0;
     }
-    double s2 = 0.0;
-    for (int64_t r = 0; r < n; ++r) {
-        const double z = Z[r * nv + j] * scl;
-        s2 += z * z;
+    // normalise: sum of squares (eight running sums, 32 loads at a time), then the scaled vector
+    constexpr int NQ = 32;
+    double s8[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int64_t r0 = 0; r0 < n; r0 += NQ) {
+        double z[NQ];
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) z[u] = Z[at(min(r0 + u, n - 1))] * scl;
+#pragma unroll
+        for (int u = 0; u < NQ; ++u)
+            if (r0 + u < n) s8[u % 8] += z[u] * z[u];
     }
+    const double s2 = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
     const double inv = s2 > 0.0 ? scl / sqrt(s2) : 0.0;
-    for (int64_t r = 0; r < n; ++r) Z[r * nv + j] *= inv;
+    for (int64_t r0 = 0; r0 < n; r0 += NQ) {
+        double z[NQ];
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) z[u] = Z[at(min(r0 + u, n - 1))];
+#pragma unroll
+        for (int u = 0; u < NQ; ++u)
+            if (r0 + u < n) Z[at(r0 + u)] = z[u] * inv;
+    }
 }
 
 // Re-orthogonalise clusters: vector j starts a cluster when lam_{j-1} - lam_j > ctol; the leader's
@@ -1219,7 +1260,8 @@ __global__ void k_set_info(int32_t *info, const int *bad) {
 template <class T>
 struct LargeWs {
     T *A, *Rt, *Vp, *Wp, *tau, *colbuf, *part, *qcol, *qvec, *spart, *rowpart, *colpart;
-    double *d, *e, *e2, *bounds, *lam, *Z, *U0, *U1, *U2, *ML, *Tf, *Gp, *G;
+    double *d, *e, *e2, *bounds, *lam, *Z, *Tf, *Gp, *G;
+    double2 *PU, *PD;  // inverse iteration's LU rows: (U1, U2) and (1/U0, multiplier)
     uint8_t *SW;
     int *bad;
     int64_t lda;
@@ -1253,10 +1295,8 @@ static void layout(C_ &cv, LargeWs<T> &w, int64_t n, int64_t nv, bool count_only
     w.bounds = cv.template carve<double>(4);
     w.lam = cv.template carve<double>(size_t(n));
     w.Z = cv.template carve<double>(size_t(n) * size_t(nv1));
-    w.U0 = cv.template carve<double>(size_t(n) * size_t(nv1));
-    w.U1 = cv.template carve<double>(size_t(n) * size_t(nv1));
-    w.U2 = cv.template carve<double>(size_t(n) * size_t(nv1));
-    w.ML = cv.template carve<double>(size_t(n) * size_t(nv1));
+    w.PU = cv.template carve<double2>(size_t(n) * size_t(nv1));
+    w.PD = cv.template carve<double2>(size_t(n) * size_t(nv1));
     w.SW = cv.template carve<uint8_t>(size_t(n) * size_t(nv1));
     w.Tf = cv.template carve<double>(size_t((n + NBT - 1) / NBT) * NBT * NBT);
     w.Gp = cv.template carve<double>(size_t(nch) * NBT * size_t(nv1));
@@ -1373,7 +1413,7 @@ struct EigJob {
             if (nv > 0) {
                 // 3. eigenvectors of T
                 hipLaunchKernelGGL(k_invit, dim3(cdiv(nv, 64)), dim3(64), 0, s, w->d, w->e, n, w->lam, w->bounds, nv,
-                                   w->Z, w->U0, w->U1, w->U2, w->ML, w->SW);
+                                   w->Z, w->PU, w->PD, w->SW);
                 hipLaunchKernelGGL(k_cluster_mgs, dim3(unsigned(nv)), dim3(256), 0, s, w->lam, n, nv, w->bounds, w->Z);
                 LRC_LAUNCH_CHECK("inverse iteration");
                 // all T factors of the back-transformation first, in one launch
