@@ -18,6 +18,7 @@
 #include <atomic>
 #include <cfloat>
 #include <cmath>
+#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <string>
@@ -1601,16 +1602,24 @@ static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, c
             stop.store(true);
         }
     };
+    // LRC_EIGH_HOST_THREADS=0: the calling thread enqueues all the work itself, on lane 0 (for
+    // tools that cannot follow launches from several host threads, such as counter collection,
+    // which serialises the kernels anyway)
+    const char *ht = std::getenv("LRC_EIGH_HOST_THREADS");
+    const bool threaded = !(ht && ht[0] == '0' && ht[1] == 0);
     std::vector<std::thread> th;
-    try {
-        for (int l = 1; l < lanes; ++l) th.emplace_back(lane, l);
-    } catch (...) {
-        stop.store(true);
-        for (auto &t : th) t.join();
-        return fail(LRC_ERR_HIP, "could not start the eigh lane threads");
+    if (threaded) {
+        try {
+            for (int l = 1; l < lanes; ++l) th.emplace_back(lane, l);
+        } catch (...) {
+            stop.store(true);
+            for (auto &t : th) t.join();
+            return fail(LRC_ERR_HIP, "could not start the eigh lane threads");
+        }
     }
     lane(0);
     for (auto &t : th) t.join();
+    for (int l = threaded ? lanes : 1; l < lanes; ++l) st[l] = LRC_OK;
     for (int l = 0; l < lanes; ++l) {
         LRC_HIP(hipEventRecord(L->done[l], L->st[l]));
         LRC_HIP(hipStreamWaitEvent(s, L->done[l], 0));

@@ -143,9 +143,13 @@ lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64
  *    tridiagonal eigenproblem (bisection, inverse iteration) always in fp64.
  * Batches with n > 128: up to four members are decomposed at once, each on a helper
  *    stream of the library's (default priority, created per device on first use and kept
- *    until the process ends) with a workspace of its own; the call returns at once and
- *    the caller's stream waits for every member, so results are ordered on `stream` as
- *    for any other call.  Each member's result does not depend on the batch it is in.
+ *    until the process ends) with a workspace of its own, fed by a host thread of its
+ *    own; the call returns once every launch is enqueued (without waiting for the GPU)
+ *    and the caller's stream waits for every member, so results are ordered on `stream`
+ *    as for any other call.  Each member's result does not depend on the batch it is in.
+ *    With the environment variable LRC_EIGH_HOST_THREADS=0 the calling thread enqueues
+ *    all members itself, on one helper stream (for tools that cannot follow launches
+ *    from several host threads); results are the same.
  * info: batch int32: 2 when the Jacobi sweeps did not converge, 1 for non-finite input.
  * Errors: LRC_ERR_ARG (sizes, strides, n_vec > n), LRC_ERR_DTYPE (prec), LRC_ERR_WORKSPACE.
  * ------------------------------------------------------------------------------------ */

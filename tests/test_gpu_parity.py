@@ -251,6 +251,17 @@ def test_eigh_multi_matches_single_calls(lrc, prec):
     lam_r, V_r = oracle.eigh(mats[3][0].astype(np.float64))
     check_lambda(host(out[3][0])[0], lam_r)
     assert sin_theta_max(host(out[3][1])[0], V_r, 10) <= 1e-3
+    # the calling thread enqueueing every member itself (one helper stream): the same bits
+    import os
+    os.environ["LRC_EIGH_HOST_THREADS"] = "0"
+    try:
+        out1 = lrc.lrc_eigh_multi(groups, prec=prec)
+    finally:
+        del os.environ["LRC_EIGH_HOST_THREADS"]
+    for (lam, V, info), (lam1, V1, info1) in zip(out, out1):
+        assert np.array_equal(host(info1), host(info))
+        assert np.array_equal(host(lam1), host(lam))
+        assert np.array_equal(host(V1), host(V))
 
 
 def test_eigh_nonfinite_sets_info(lrc):
