@@ -216,7 +216,8 @@ static std::vector<EighArgs> eigh_groups(const lrc_eigh_group *g, int32_t count,
     v.reserve(size_t(count));
     for (int32_t i = 0; i < count; ++i)
         v.push_back(EighArgs{g[i].C, g[i].n, g[i].ldc, g[i].batch, g[i].stride_c, prec, g[i].lambda, g[i].V,
-                             g[i].ldv, g[i].n_vec, g[i].stride_v, g[i].info});
+                             g[i].ldv, g[i].n_vec, g[i].stride_v, g[i].info, g[i].W, g[i].w_t, g[i].d_in,
+                             g[i].ldw, g[i].stride_w});
     return v;
 }
 
@@ -236,6 +237,13 @@ lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype
         lrc_status st = check_eigh(g.C, g.n, g.ldc, g.batch, g.stride_c, g.lambda, g.V, g.ldv, g.n_vec, g.stride_v,
                                    g.info);
         if (st != LRC_OK) return st;
+        if (g.W) {
+            REQUIRE(g.w_t == LRC_BF16 || g.w_t == LRC_F32 || g.w_t == LRC_F64, LRC_ERR_DTYPE,
+                    "w_t must be LRC_BF16, LRC_F32 or LRC_F64");
+            REQUIRE(g.d_in > 0 && g.ldw >= g.n, LRC_ERR_ARG, "range basis: d_in must be positive and ldw >= n");
+            REQUIRE(g.batch == 1 || g.stride_w >= g.d_in * g.ldw - (g.ldw - g.n), LRC_ERR_ARG,
+                    "stride_w overlaps range bases");
+        }
     }
     REQUIRE(prec == LRC_F32 || prec == LRC_F64, LRC_ERR_DTYPE, "prec must be LRC_F32 or LRC_F64");
     std::vector<EighArgs> v = eigh_groups(groups, count, prec);

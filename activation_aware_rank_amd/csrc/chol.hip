@@ -496,6 +496,21 @@ lrc_status to_f64_run(const void *X, lrc_dtype t, int64_t rows, int64_t cols, in
     return LRC_OK;
 }
 
+lrc_status dgemm_run(int ta, int tb, int64_t M, int64_t N, int64_t K, const double *A, int64_t lda, const double *B,
+                     int64_t ldb, double *C, int64_t ldc, int tiles, float *Cf, hipStream_t s) {
+    GemmArgs g = gemm(M, N, K, A, lda, B, ldb, C, ldc, 1.0, 0.0, tiles);
+    g.Cf = Cf;
+    if (Cf) {
+        if (ta == 0 && tb == 1) return launch_gemm<0, 1, 0, 0, 1>(g, s);
+        if (ta == 0 && tb == 0) return launch_gemm<0, 0, 0, 0, 1>(g, s);
+    } else {
+        if (ta == 0 && tb == 0) return launch_gemm<0, 0, 0, 0, 0>(g, s);
+        if (ta == 0 && tb == 1) return launch_gemm<0, 1, 0, 0, 0>(g, s);
+        if (ta == 1 && tb == 0) return launch_gemm<1, 0, 0, 0, 0>(g, s);
+    }
+    return fail(LRC_ERR_UNIMPLEMENTED, "fp64 product: operand layout not instantiated");
+}
+
 lrc_status gram_f64_run(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg, hipStream_t s) {
     GemmArgs g = gemm(m, m, n, B, ldb, B, ldb, nullptr, ldg, 1.0, 0.0, 2);
     g.Cf = G;

@@ -1336,6 +1336,7 @@ struct EigJob {
     LargeWs<T> *w = nullptr;
     hipStream_t s = nullptr;
     int stage = 0;  // 0 start, 1 tridiagonalisation, 2 eigenvalues and vectors of T, 3 back-transformation, 4 done
+    bool keep_z = false;  // leave the fp64 eigenvectors in w->Z (no sign rule, no fp32 output)
     int NT = 0, npart = 0;
     int64_t p0 = 0, p1 = 0, c = 0, c0 = 0;
 
@@ -1441,8 +1442,10 @@ struct EigJob {
             }
             LRC_LAUNCH_CHECK("back-transformation");
             if (c0 >= 0) return LRC_OK;
-            hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, w->Z, n, nv, V, ldv, w->bad);
-            LRC_LAUNCH_CHECK("k_sign_out");
+            if (!keep_z) {
+                hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, w->Z, n, nv, V, ldv, w->bad);
+                LRC_LAUNCH_CHECK("k_sign_out");
+            }
             stage = 4;
         }
         hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, s, info, w->bad);
@@ -1452,6 +1455,92 @@ struct EigJob {
     }
     bool done() const { return stage == 5; }
 };
+
+// ---------------------------------------------------------------------------------------------
+// 6. range-restricted decomposition (C = (X W)^T (X W), W d_in x n with d_in < n)
+// ---------------------------------------------------------------------------------------------
+// The range of C lies in that of W^T, so with Q (n x d_in) an orthonormal basis of it the
+// eigenpairs of C are those of B = Q^T C Q (d_in x d_in), V = Q U, plus n - d_in zero eigenvalues.
+// Q comes from the Cholesky factor of W W^T = L L^T: Q^T = L^{-1} W (fp64; its departure from
+// orthogonality is about kappa(W)^2 times the fp64 unit roundoff).
+
+// lambda (n, descending) from the d_in eigenvalues of B (descending) and n - d_in zeros: the p
+// non-negative ones, the zeros, then the negative ones; info 3 when W W^T was not positive
+// definite, 1 for non-finite input, 6 when fewer than n_vec eigenvalues of B are non-negative (the
+// vectors of the zero eigenvalues are not formed), else 0.
+__global__ void k_range_finish(const double *__restrict__ lamB, int64_t r, int64_t n, double *__restrict__ lam,
+                               const int *__restrict__ bad, const int32_t *__restrict__ chol_info, int64_t nv,
+                               int32_t *__restrict__ info) {
+    const bool nan = *bad != 0;
+    int64_t lo = 0, hi = r;  // p = first index with lamB < 0 (lamB descending)
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (lamB[mid] >= 0.0) lo = mid + 1; else hi = mid;
+    }
+    const int64_t p = lo, z = n - r;
+    for (int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; j < n; j += int64_t(gridDim.x) * blockDim.x)
+        lam[j] = nan ? double(NAN) : (j < p ? lamB[j] : (j < p + z ? 0.0 : lamB[j - z]));
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *info = *chol_info != 0 ? 3 : (nan ? 1 : (nv > p ? 6 : 0));
+}
+
+// The factor L of W W^T = L L^T has the singular values of W, so max/min of its diagonal bounds
+// kappa(W) from below; the basis Q^T = L^{-1} W loses orthogonality like kappa(W)^2 times the
+// fp64 unit roundoff.  A ratio above 1e5 (or a non-finite diagonal) marks the basis as unusable
+// (chol_info 3), as a failed Cholesky does.  One workgroup, fixed-order reduction.
+__global__ void __launch_bounds__(256) k_range_check(const double *__restrict__ L, int64_t r, int32_t *chol_info) {
+    __shared__ double smin[256], smax[256];
+    double mn = DBL_MAX, mx = 0.0;
+    for (int64_t i = threadIdx.x; i < r; i += 256) {
+        const double v = L[i * r + i];
+        mn = fmin(mn, isfinite(v) ? fabs(v) : 0.0);
+        mx = fmax(mx, isfinite(v) ? fabs(v) : DBL_MAX);
+    }
+    smin[threadIdx.x] = mn;
+    smax[threadIdx.x] = mx;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) {
+            smin[threadIdx.x] = fmin(smin[threadIdx.x], smin[threadIdx.x + o]);
+            smax[threadIdx.x] = fmax(smax[threadIdx.x], smax[threadIdx.x + o]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0 && *chol_info == 0 && !(smin[0] > 1e-5 * smax[0] && smax[0] < DBL_MAX)) *chol_info = 3;
+}
+
+struct RangeWs {
+    double *Qt, *C64, *T, *G, *lamB;
+    void *chol, *trsm;
+    float *B;
+    int32_t *iw;
+};
+
+template <class C_, class T>
+static void range_layout(C_ &cv, RangeWs &rw, LargeWs<T> &w, int64_t n, int64_t r, int64_t nv) {
+    rw.Qt = cv.template carve<double>(size_t(r) * size_t(n));
+    rw.C64 = cv.template carve<double>(size_t(n) * size_t(n));
+    rw.T = cv.template carve<double>(size_t(r) * size_t(n));  // later the n x n_vec vectors Q Z
+    rw.G = cv.template carve<double>(size_t(r) * size_t(r));
+    rw.lamB = cv.template carve<double>(size_t(r));
+    rw.chol = cv.template carve<char>(cholesky_workspace(r));
+    rw.trsm = cv.template carve<char>(trsm_workspace(0, r, n));
+    rw.B = cv.template carve<float>(size_t(r) * size_t(r));
+    rw.iw = cv.template carve<int32_t>(2);
+    layout(cv, w, r, nv, false);
+}
+
+template <class T>
+static size_t range_ws(int64_t n, int64_t r, int64_t nv) {
+    CountCarver cc;
+    RangeWs rw;
+    LargeWs<T> w;
+    range_layout(cc, rw, w, n, r, nv);
+    return cc.c.off;
+}
+
+// the range path applies when 128 < d_in < n and n_vec <= d_in
+static bool use_range(const EighArgs &a) { return a.W && a.d_in > 128 && a.d_in < a.n && a.n_vec <= a.d_in; }
 
 // Batch members are independent: up to EIG_LANES of them run at once, each on a helper stream
 // of its own with its own workspace, so the per-column launch chains of several matrices
@@ -1500,19 +1589,27 @@ struct MultiPlan {
 
 static MultiPlan multi_plan(const EighArgs *g, int count, lrc_dtype prec) {
     MultiPlan p;
+    size_t per_range = 0;
     for (int i = 0; i < count; ++i) {
         if (g[i].n <= 128) {
             p.jac = std::max(p.jac, jacobi_workspace(g[i].n, g[i].batch, prec));
         } else {
-            p.maxn = std::max(p.maxn, g[i].n);
-            p.maxnv = std::max(p.maxnv, g[i].n_vec);
             p.members += g[i].batch;
+            if (use_range(g[i])) {
+                per_range = std::max(per_range, prec == LRC_F64 ? range_ws<double>(g[i].n, g[i].d_in, g[i].n_vec)
+                                                                : range_ws<float>(g[i].n, g[i].d_in, g[i].n_vec));
+            } else {
+                p.maxn = std::max(p.maxn, g[i].n);
+                p.maxnv = std::max(p.maxnv, g[i].n_vec);
+            }
         }
     }
     p.jac = align256(p.jac);
     if (p.members > 0) {
         p.lanes = int(std::min<int64_t>(p.members, EIG_LANES));
-        p.per = prec == LRC_F64 ? large_ws<double>(p.maxn, p.maxnv) : large_ws<float>(p.maxn, p.maxnv);
+        if (p.maxn > 0)
+            p.per = prec == LRC_F64 ? large_ws<double>(p.maxn, p.maxnv) : large_ws<float>(p.maxn, p.maxnv);
+        p.per = std::max(p.per, per_range);
     }
     return p;
 }
@@ -1534,6 +1631,9 @@ struct EigMember {
     float *V;
     int64_t ldv, nv;
     int32_t *info;
+    const void *W;  // range basis (W d_in x n), or nullptr
+    lrc_dtype w_t;
+    int64_t d_in, ldw;
 };
 
 // All members with n > 128 over up to EIG_LANES helper streams, largest n first: each lane's
@@ -1564,6 +1664,57 @@ static lrc_status run_member(const EigMember &m, const MultiPlan &p, char *lws, 
     return LRC_OK;
 }
 
+// A member with a range basis: Q^T = L^{-1} W (W W^T = L L^T), B = Q^T C Q in fp64 (rounded to fp32
+// as the input of the decomposition, like C itself), B's decomposition with its fp64 vectors
+// kept, then V = Q Z with the sign rule and lambda with the n - d_in zeros.
+template <class T>
+static lrc_status run_member_range(const EigMember &m, const MultiPlan &p, char *lws, hipStream_t s, LargeWs<T> &w) {
+    const int64_t n = m.n, r = m.d_in, nv = m.nv;
+    Carver cv(lws, p.per);
+    RangeWs rw;
+    w = LargeWs<T>();
+    range_layout(cv, rw, w, n, r, nv);
+    if (!w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
+    lrc_status st = to_f64_run(m.W, m.w_t, r, n, m.ldw, 1.0, rw.Qt, n, s);
+    if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, rw.Qt, n, rw.Qt, n, rw.G, r, 1, nullptr, s);  // W W^T, lower
+    if (st == LRC_OK) st = cholesky_run(rw.G, r, r, rw.chol, cholesky_workspace(r), rw.iw, s);
+    if (st == LRC_OK) {
+        hipLaunchKernelGGL(k_range_check, dim3(1), dim3(256), 0, s, rw.G, r, rw.iw);
+        LRC_LAUNCH_CHECK("k_range_check");
+    }
+    if (st == LRC_OK) st = trsm_run(0, 0, r, n, rw.G, r, rw.Qt, n, rw.trsm, s);  // Q^T = L^{-1} W
+    if (st == LRC_OK) st = sym_to_f64_run(m.C, n, m.ldc, 1.0, rw.C64, n, s);
+    if (st == LRC_OK) st = dgemm_run(0, 0, r, n, n, rw.Qt, n, rw.C64, n, rw.T, n, 0, nullptr, s);  // Q^T C
+    if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, rw.T, n, rw.Qt, n, nullptr, r, 2, rw.B, s);  // B, upper
+    if (st != LRC_OK) return st;
+    EigJob<T> j;
+    j.C = rw.B;
+    j.ldc = r;
+    j.n = r;
+    j.lambda = rw.lamB;
+    j.V = nullptr;
+    j.ldv = nv;
+    j.nv = nv;
+    j.info = rw.iw + 1;
+    j.w = &w;
+    j.s = s;
+    j.keep_z = true;
+    while (!j.done()) {
+        st = j.advance(64);
+        if (st != LRC_OK) return st;
+    }
+    if (nv > 0) {
+        st = dgemm_run(1, 0, n, nv, r, rw.Qt, n, w.Z, nv, rw.T, nv, 0, nullptr, s);  // Q Z (n x n_vec)
+        if (st != LRC_OK) return st;
+        hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, w.bad);
+        LRC_LAUNCH_CHECK("k_sign_out");
+    }
+    hipLaunchKernelGGL(k_range_finish, dim3(cdiv(n, 256)), dim3(256), 0, s, rw.lamB, r, n, m.lambda, w.bad, rw.iw, nv,
+                       m.info);
+    LRC_LAUNCH_CHECK("k_range_finish");
+    return LRC_OK;
+}
+
 template <class T>
 static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, char *ws, hipStream_t s) {
     std::stable_sort(mem.begin(), mem.end(), [](const EigMember &x, const EigMember &y) { return x.n > y.n; });
@@ -1571,7 +1722,7 @@ static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, c
     LargeWs<T> w[EIG_LANES];
     if (lanes <= 1) {
         for (const EigMember &m : mem) {
-            const lrc_status st = run_member<T>(m, p, ws, s, w[0]);
+            const lrc_status st = m.W ? run_member_range<T>(m, p, ws, s, w[0]) : run_member<T>(m, p, ws, s, w[0]);
             if (st != LRC_OK) return st;
         }
         return LRC_OK;
@@ -1595,7 +1746,9 @@ static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, c
         while (st[l] == LRC_OK && !stop.load()) {
             const size_t i = next.fetch_add(1);
             if (i >= mem.size()) break;
-            st[l] = run_member<T>(mem[i], p, ws + p.per * size_t(l), L->st[l], w[l]);
+            char *lws = ws + p.per * size_t(l);
+            st[l] = mem[i].W ? run_member_range<T>(mem[i], p, lws, L->st[l], w[l])
+                             : run_member<T>(mem[i], p, lws, L->st[l], w[l]);
         }
         if (st[l] != LRC_OK) {
             msg[l] = lrc_last_error();
@@ -1651,9 +1804,13 @@ lrc_status eigh_multi_run(const EighArgs *g, int count, lrc_dtype prec, void *ws
     for (int i = 0; i < count; ++i) {
         const EighArgs &a = g[i];
         if (a.n <= 128) continue;
+        const bool rng = use_range(a);
+        const size_t esz = a.w_t == LRC_BF16 ? 2 : (a.w_t == LRC_F32 ? 4 : 8);
         for (int64_t b = 0; b < a.batch; ++b)
             mem.push_back(EigMember{a.C + b * a.stride_c, a.ldc, a.n, a.lambda + b * a.n,
-                                    a.V ? a.V + b * a.stride_v : nullptr, a.ldv, a.n_vec, a.info + b});
+                                    a.V ? a.V + b * a.stride_v : nullptr, a.ldv, a.n_vec, a.info + b,
+                                    rng ? static_cast<const char *>(a.W) + size_t(b * a.stride_w) * esz : nullptr,
+                                    a.w_t, a.d_in, a.ldw});
     }
     char *lw = static_cast<char *>(ws) + p.jac;
     return prec == LRC_F64 ? large_sched<double>(mem, p, lw, s) : large_sched<float>(mem, p, lw, s);

@@ -118,6 +118,10 @@ struct EighArgs {
     float *V;
     int64_t ldv, n_vec, stride_v;
     int32_t *info;
+    // optional range basis (lrc_eigh_group): C = (X W)^T (X W) with W d_in x n
+    const void *W = nullptr;
+    lrc_dtype w_t = LRC_BF16;
+    int64_t d_in = 0, ldw = 0, stride_w = 0;
 };
 size_t eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype prec);
 lrc_status eigh_run(const EighArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
@@ -176,6 +180,10 @@ lrc_status sym_to_f64_run(const float *C, int64_t n, int64_t ldc, double scale, 
                           hipStream_t s);
 lrc_status to_f64_run(const void *X, lrc_dtype t, int64_t rows, int64_t cols, int64_t ldx, double scale,
                       double *Y, int64_t ldy, hipStream_t s);
+// C = op(A) op(B) in fp64 (ta, tb: 0 plain, 1 transposed; tiles 0 all, 1 lower, 2 upper); with Cf the
+// product goes to Cf as fp32 instead
+lrc_status dgemm_run(int ta, int tb, int64_t M, int64_t N, int64_t K, const double *A, int64_t lda, const double *B,
+                     int64_t ldb, double *C, int64_t ldc, int tiles, float *Cf, hipStream_t s);
 lrc_status gram_f64_run(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg,
                         hipStream_t s);
 

@@ -186,15 +186,17 @@ def lrc_eigh_workspace(n: int, batch: int, n_vec: int, prec: int = LRC_F32) -> i
 class _EighGroup(ctypes.Structure):
     """struct lrc_eigh_group of include/lrc.h."""
     _fields_ = [("C", _vp), ("n", _i64), ("ldc", _i64), ("batch", _i64), ("stride_c", _i64), ("lambda_", _vp),
-                ("V", _vp), ("ldv", _i64), ("n_vec", _i64), ("stride_v", _i64), ("info", _vp)]
+                ("V", _vp), ("ldv", _i64), ("n_vec", _i64), ("stride_v", _i64), ("info", _vp),
+                ("W", _vp), ("w_t", _int), ("d_in", _i64), ("ldw", _i64), ("stride_w", _i64)]
 
 
 _eigh_mws = _sig("lrc_eigh_multi_workspace", _sz, ctypes.POINTER(_EighGroup), _i32, _int)
 _eigh_m = _sig("lrc_eigh_multi", _int, ctypes.POINTER(_EighGroup), _i32, _int, _vp, _sz, _vp)
 
 
-def _eigh_args(C, n_vec, lam, V, info):
-    """Marshals one lrc_eigh call: (struct, squeeze flag, lam, V, info)."""
+def _eigh_args(C, n_vec, lam, V, info, W=None):
+    """Marshals one lrc_eigh call (W: the optional range basis of lrc_eigh_multi, d_in x n or
+    batch x d_in x n): (struct, squeeze flag, lam, V, info)."""
     ldc = _rows(C, "C")
     squeeze = C.dim() == 2
     Cb = C.unsqueeze(0) if squeeze else C
@@ -208,6 +210,9 @@ def _eigh_args(C, n_vec, lam, V, info):
     stride_v = (V.stride(0) if V.dim() == 3 else 0) if V is not None else 0
     info = _info(info, batch, dev)
     g = _EighGroup(_ptr(C), n, ldc, batch, Cb.stride(0), _ptr(lam), _ptr(V), ldv, n_vec, stride_v, _ptr(info))
+    if W is not None:
+        g.W, g.w_t, g.d_in, g.ldw = _ptr(W), _dt(W), W.shape[-2], _rows(W, "W")
+        g.stride_w = W.stride(0) if W.dim() == 3 else 0
     return g, squeeze, lam, V, info
 
 
@@ -229,20 +234,29 @@ def lrc_eigh(C: torch.Tensor, n_vec: int, prec: int = LRC_F32, lam=None, V=None,
 
 
 def lrc_eigh_multi_workspace(groups, prec: int = LRC_F32) -> int:
-    """groups: sequence of (n, batch, n_vec)."""
-    arr = (_EighGroup * len(groups))(*[_EighGroup(None, n, n, b, 0, None, None, nv, nv, 0, None)
-                                      for n, b, nv in groups])
-    return _eigh_mws(arr, len(groups), prec)
+    """groups: sequence of (n, batch, n_vec) or (n, batch, n_vec, d_in) for a group with a range basis
+    of d_in rows (only its presence and d_in matter for the size)."""
+    gs = []
+    for grp in groups:
+        n, b, nv = grp[:3]
+        g = _EighGroup(None, n, n, b, 0, None, None, nv, nv, 0, None)
+        if len(grp) > 3 and grp[3]:
+            g.W, g.d_in, g.ldw = 1, grp[3], n  # any non-NULL pointer: the query reads no memory
+        gs.append(g)
+    arr = (_EighGroup * len(gs))(*gs)
+    return _eigh_mws(arr, len(gs), prec)
 
 
 def lrc_eigh_multi(groups, prec: int = LRC_F32, ws=None, stream=None):
-    """Several lrc_eigh calls in one.  groups: sequence of (C, n_vec) or (C, n_vec, lam, V, info)
-    with the meaning of lrc_eigh's arguments.  Returns a list of (lambda, V, info) per group."""
+    """Several lrc_eigh calls in one.  groups: sequence of (C, n_vec), (C, n_vec, lam, V, info) or
+    (C, n_vec, lam, V, info, W) with the meaning of lrc_eigh's arguments; W is the optional range
+    basis (d_in x n, or batch x d_in x n: C = (X W)^T (X W)).  Returns a list of (lambda, V, info)
+    per group."""
     parts = []
     for grp in groups:
         C, n_vec = grp[0], grp[1]
-        lam, V, info = (tuple(grp[2:5]) + (None, None, None))[:3]
-        parts.append(_eigh_args(C, n_vec, lam, V, info))
+        lam, V, info, W = (tuple(grp[2:6]) + (None, None, None, None))[:4]
+        parts.append(_eigh_args(C, n_vec, lam, V, info, W))
     if not parts:
         raise ValueError("lrc_eigh_multi needs at least one group")
     arr = (_EighGroup * len(parts))(*[p[0] for p in parts])

@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--curvature-prec", choices=("f32", "f64"), default="f64")
     ap.add_argument("--layer-runs", type=int, default=2,
                     help="runs of one 4096x4096 layer on its own after the timed steps (0: skip)")
+    ap.add_argument("--eig-range", choices=("on", "off"), default="on",
+                    help="on: covariances of Y = X W with d_in < d_out (gate/up) are decomposed through a basis of "
+                         "range(W^T) (their rank is at most d_in); off: the full decomposition of every covariance")
     ap.add_argument("--timing-stride", type=int, default=16,
                     help="time every s-th launch of the per-column symmetric product in the timed steps")
     a = ap.parse_args()
@@ -170,6 +173,15 @@ def main():
     geps = {g: torch.empty(len(ms), g[0] + 1, dtype=torch.float64, device=dev) for g, ms in groups.items()}
     ginfo = {g: torch.zeros(len(ms), dtype=torch.int32, device=dev) for g, ms in groups.items()}
     where = {m: (g, ms.index(m)) for g, ms in groups.items() for m in ms}
+    # groups whose covariance has rank <= d_in < d_out: their weights in one stack too (the range
+    # bases of the decomposition; the covariance calls read the same storage)
+    gW = {}
+    if a.eig_range == "on":
+        for g, ms in groups.items():
+            if sh[ms[0]][0] < g[0]:
+                gW[g] = torch.stack([W[m] for m in ms])
+                for i, m in enumerate(ms):
+                    W[m] = gW[g][i]
     C = {m: gC[where[m][0]][where[m][1]] for m in MATS}
     lam = {m: glam[where[m][0]][where[m][1]] for m in MATS}
     V = {m: gV[where[m][0]][where[m][1]] for m in MATS}
@@ -179,9 +191,10 @@ def main():
     info = torch.zeros(8, dtype=torch.int32, device=dev)
     ws_cov = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, di, True, do, 1)
                              for di, do in sh.values()), dtype=torch.uint8, device=dev)
-    ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace([(g[0], len(ms), g[1]) for g, ms in groups.items()], prec),
-                         dtype=torch.uint8, device=dev)
-    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g]) for g in groups]
+    ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace(
+        [(g[0], len(ms), g[1], sh[ms[0]][0] if g in gW else 0) for g, ms in groups.items()], prec),
+        dtype=torch.uint8, device=dev)
+    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g], gW.get(g)) for g in groups]
     gkey = "+".join("%dx%d_k%d" % (len(ms), g[0], g[1]) for g, ms in groups.items())
     kcap = {m: (di * do) // (di + do) for m, (di, do) in sh.items()}
     offs_h = [0] + list(np.cumsum([kcap[m] for m in MATS]))
@@ -297,8 +310,10 @@ def main():
     cov_flops_total = sum(cov_flops(a.tokens, di, do) for di, do in sh.values())
     cov_tflops = cov_flops_total / (cov_ms / 1000.0) / 1e12
     # one 4096x4096 layer: its covariance, its share of the block's eigendecompositions and error
-    # curves (their time split over the matrices in proportion to n^3), its factors
-    n3 = {m: float(sh[m][1]) ** 3 for m in MATS}
+    # curves (their time split over the matrices in proportion to n^3, with n = d_in for a matrix
+    # decomposed through a range basis: its GEMMs are left out, which overstates q_proj's share), its
+    # factors
+    n3 = {m: float(sh[m][0] if where[m][0] in gW else sh[m][1]) ** 3 for m in MATS}
     share = n3["q_proj"] / sum(n3.values())
     layer_s = (avg["q_proj.cov"] + (avg["eigh." + gkey] + avg["err." + gkey]) * share + avg["q_proj.fac"]) / 1000.0
     if a.breakdown:
@@ -347,7 +362,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded, generated on the GPU)",
         "config": {"workload": "LLaMA-7B-shaped block: q/k/v/o 4096x4096, gate/up 4096x11008, down 11008x4096, "
-                               "%d calibration tokens, 60%% params per matrix, eig prec %s" % (a.tokens, a.prec),
+                               "%d calibration tokens, 60%% params per matrix, eig prec %s%s"
+                               % (a.tokens, a.prec, "; gate/up (rank <= 4096) decomposed through a basis of range(W^T)"
+                                  if gW else ""),
                    "tokens": a.tokens, "d_model": a.d_model, "d_ff": a.d_ff, "ranks": ks,
                    "allocated_ranks": dict(zip(MATS, k_out.cpu().tolist()))},
         "sec_per_4096_layer": layer_alone_s,
@@ -356,7 +373,8 @@ def main():
         "sec_per_4096_layer_in_block": layer_s,
         "sec_per_4096_layer_in_block_note": "q_proj covariance + q_proj factors + %.4f of the block's "
                                             "eigendecompositions and error curves (%s, one call; the share is "
-                                            "q_proj's n^3 over the sum)" % (share, gkey),
+                                            "q_proj's n^3 over the sum, n = d_in for the matrices decomposed "
+                                            "through a range basis)" % (share, gkey),
         "cov_tokens_per_s": a.tokens / (cov_ms / 1000.0),
         "cov_ms": cov_ms, "eigh_ms": eig_ms,
         "breakdown_ms": {k: round(v, 3) for k, v in avg.items()},

@@ -170,9 +170,24 @@ lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64
  * Groups with n <= 128 run first, one Jacobi launch each, on `stream`; every member of
  *    the groups with n > 128 is then decomposed on the helper streams described under
  *    lrc_eigh, up to four at once, largest n first.  `stream` waits for all of them.
- *    Each member's result equals that of lrc_eigh on the member alone, bit for bit.
+ *    Each member's result equals that of a call on the member alone, bit for bit.
+ * Range basis (optional, per group; Swift-SVD page, section 2-ga: C = Y^T Y with Y = X W):
+ *    W != NULL states that each member's C is (X W)^T (X W) for some X, with W (d_in x n,
+ *    row-major, ldw >= n, dtype w_t: LRC_BF16, LRC_F32 or LRC_F64; member b at W +
+ *    b * stride_w elements) of full row rank.  C's rank is then at most d_in, its range
+ *    lies in that of W^T, and when 128 < d_in < n and n_vec <= d_in the member is
+ *    decomposed through B = Q^T C Q, Q (n x d_in) an orthonormal basis of range(W^T)
+ *    (Q^T = L^{-1} W with W W^T = L L^T, in fp64): lambda = the d_in eigenvalues of B and
+ *    n - d_in zeros, in descending order, V = Q U.  The part of the computed C outside
+ *    range(W^T) is rounding error, which the full decomposition would report as
+ *    eigenvalues of about 1e-7 of the largest; here they are exact zeros.  info 3: W W^T
+ *    is not positive definite, or the diagonal of L spans more than a factor 1e5 (W not
+ *    of full row rank, or so ill-conditioned that Q loses orthogonality: use the full
+ *    decomposition); 6: fewer than n_vec eigenvalues of B are non-negative.  Other d_in,
+ *    or n_vec > d_in: W is ignored.
  * ws: lrc_eigh_multi_workspace(groups, count, prec) bytes, 256-byte aligned (one region
- *    per concurrent member, each sized for the largest n and n_vec among the groups).
+ *    per concurrent member, each sized for the largest n and n_vec among the groups, or
+ *    for the largest member with a range basis if that needs more).
  * Errors: those of lrc_eigh, for the first group that fails a check; LRC_ERR_ARG for a
  *    NULL groups or count <= 0.  The workspace query returns 0 for invalid sizes.
  * ------------------------------------------------------------------------------------ */
@@ -183,6 +198,9 @@ typedef struct lrc_eigh_group {
     float *V;
     int64_t ldv, n_vec, stride_v;
     int32_t *info;
+    const void *W;      /* optional range basis, d_in x n; NULL for none */
+    lrc_dtype w_t;
+    int64_t d_in, ldw, stride_w;
 } lrc_eigh_group;
 size_t lrc_eigh_multi_workspace(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec);
 lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec, void *ws,

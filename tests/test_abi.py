@@ -114,6 +114,11 @@ def test_argument_errors_are_synchronous():
     assert lrc._eigh_m(arr, 1, 7, fake, 1 << 40, None) == 2
     need = lrc._eigh_mws(arr, 1, 1)
     assert lrc._eigh_m(arr, 1, 1, fake, need - 1, None) == 3
+    # range basis: bad dtype, ldw < n, bases of a batch overlapping
+    for w_t, ldw, stride_w, code, word in ((5, 300, 200 * 300, 2, "w_t"), (0, 299, 200 * 300, 1, "ldw"),
+                                           (0, 300, 100, 1, "stride_w")):
+        g = G(256, 300, 300, 2, 90000, 256, 256, 8, 8, 2400, 256, 256, w_t, 200, ldw, stride_w)
+        assert lrc._eigh_m((G * 1)(g), 1, 1, fake, 1 << 40, None) == code and word in lrc.lrc_last_error()
 
 
 def test_workspace_queries_are_consistent():
@@ -135,4 +140,12 @@ def test_workspace_queries_are_consistent():
     assert lrc.lrc_eigh_multi_workspace([(4096, 1, 1791), (11008, 1, 1228)], 1) == 2 * big
     assert lrc.lrc_eigh_multi_workspace([(64, 4, 8)], 2) == 0
     assert lrc.lrc_eigh_multi_workspace([(64, 4, 65)], 2) == 0
+    # a range basis of d_in rows (128 < d_in < n, n_vec <= d_in): the region also holds the basis, n x n
+    # and d_in x n fp64 products, and the decomposition of the d_in x d_in matrix; otherwise ignored
+    rng = lrc.lrc_eigh_multi_workspace([(11008, 2, 1791, 4096)], 1)
+    assert rng > 2 * 8 * 11008 * 11008 and rng != 2 * big
+    assert lrc.lrc_eigh_multi_workspace([(11008, 2, 1791, 4096), (4096, 5, 1228)], 1) == 4 * (rng // 2)
+    assert lrc.lrc_eigh_multi_workspace([(11008, 1, 1791, 12000)], 1) == big
+    assert lrc.lrc_eigh_multi_workspace([(11008, 1, 1791, 100)], 1) == big
+    assert lrc.lrc_eigh_multi_workspace([(4096, 1, 1791, 1228)], 1) == lrc.lrc_eigh_workspace(4096, 1, 1791, 1)
     assert lrc.lrc_allocate_ranks_workspace(224, 548704) > 548704 * 8

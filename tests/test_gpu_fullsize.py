@@ -7,9 +7,10 @@ any size:
   oracle (covariance, eigenvalues, retained subspace, error curve, the direct error of the GPU
   factors); all 32 heads by eigen-residual and orthogonality;
 * LLaMA-7B block at 524288 tokens (q_proj 4096 -> 4096, k = 1228; gate_proj 4096 -> 11008,
-  k = 1791), inputs drawn on the GPU as bench.py draws them: sampled covariance entries against the
-  oracle's sums over all tokens; residual and orthogonality of the retained eigenpairs; the closed
-  form eps_k = trace(C) - sum_{i<=k} v_i^T C v_i; A = W V_k on sampled rows;
+  k = 1791, by the full decomposition and through a basis of range(W^T) as bench.py runs it),
+  inputs drawn on the GPU as bench.py draws them: sampled covariance entries against the oracle's
+  sums over all tokens; residual and orthogonality of the retained eigenpairs; the closed form
+  eps_k = trace(C) - sum_{i<=k} v_i^T C v_i; A = W V_k on sampled rows;
 * 32-layer stack (224 matrices, 6,476,005,376 parameters): Fisher scores of every matrix on the GPU,
   three checked against the oracle; the greedy allocation of an 80 % budget over all 548,704
   candidate ranks, bit-exact against the oracle on identical (synthetic) spectra and scores.
@@ -87,15 +88,21 @@ def block_inputs():
     return inputs.block_gpu(524288, 4096, 11008, 20261203, torch.device("cuda"))
 
 
-@pytest.mark.parametrize("name,k", [("q_proj", 1228), ("gate_proj", 1791)])
-def test_block_matrix_full_size(lrc, block_inputs, name, k):
-    _say("block %s at 524288 tokens, k = %d (bench configuration, eig prec fp32)" % (name, k))
+@pytest.mark.parametrize("name,k,basis", [("q_proj", 1228, False), ("gate_proj", 1791, False),
+                                          ("gate_proj", 1791, True)])
+def test_block_matrix_full_size(lrc, block_inputs, name, k, basis):
+    _say("block %s at 524288 tokens, k = %d, eig prec fp32%s" % (
+        name, k, ", through a basis of range(W^T) (bench configuration)" if basis else ""))
     X, W = block_inputs["X"], block_inputs["W"][name]
     d_in, d_out = W.shape
     C = torch.zeros(d_out, d_out, dtype=torch.float32, device="cuda")
     info = lrc.lrc_cov_accumulate(X, W, C)
     assert int(host(info)[0]) == 0
-    lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=1)
+    if basis:
+        lam, V, info = lrc.lrc_eigh_multi([(C, k, None, None, None, W)], prec=1)[0]
+        assert int(host(lam == 0).sum()) >= d_out - d_in
+    else:
+        lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=1)
     assert int(host(info)[0]) == 0
     eps = lrc.lrc_error_curve(lam)
     A = torch.empty(d_in, k, dtype=torch.float32, device="cuda")

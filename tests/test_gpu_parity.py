@@ -264,6 +264,72 @@ def test_eigh_multi_matches_single_calls(lrc, prec):
         assert np.array_equal(host(V1), host(V))
 
 
+@pytest.mark.parametrize("prec", [1, 2])
+def test_eigh_range_basis_vs_oracle(lrc, prec):
+    """A covariance of Y = X W with d_in < d_out decomposed through B = Q^T C Q, Q a basis of range(W^T):
+    the oracle's full eigendecomposition (its n - d_in trailing eigenvalues are zero to rounding), the
+    closed form through the factors, and a batch with a stride between the bases equal to single
+    calls; the lower triangle of C is never read."""
+    _say("eigh with a range basis: 200 -> 520, 2048 tokens, prec %d" % prec)
+    d_in, n, k = 200, 520, 48
+    X = inputs.block_activations(d_in, 2048)
+    Ws = [inputs.weight(d_in, n, "bf16", inputs.CFG_BLOCK, 0, 30 + i) for i in range(2)]
+    Cs = [_oracle_cov32(X, "bf16", W)[0] for W in Ws]
+    Cu = np.stack([np.triu(C) + np.tril(np.full((n, n), np.nan, np.float32), -1) for C in Cs])
+    Wd = torch.stack([dev(W, "bf16") for W in Ws])
+    out = lrc.lrc_eigh_multi([(dev(Cu, "f32"), k, None, None, None, Wd)], prec=prec)
+    lam_b, V_b, info_b = (host(x) for x in out[0])
+    assert np.all(info_b == 0), info_b
+    X64 = oracle.widen(X, "bf16")
+    for m in range(2):
+        lam, V = lam_b[m], V_b[m]
+        C64 = Cs[m].astype(np.float64)
+        lam_r, V_r = oracle.eigh(C64)
+        e = check_lambda(lam, lam_r)
+        assert np.all(np.diff(lam) <= 0)
+        assert np.count_nonzero(lam == 0.0) >= n - d_in  # the complement of range(W^T)
+        s = sin_theta_max(V, V_r, k)
+        V64 = V.astype(np.float64)
+        orth = np.max(np.abs(V64.T @ V64 - np.eye(k)))
+        res = np.linalg.norm(C64 @ V64 - V64 * lam[:k], axis=0).max() / lam_r[0]
+        print("member %d: lambda err %.2e, sin theta %.2e (gap %.2e), orthogonality %.2e, residual %.2e"
+              % (m, e, s, gap(lam_r, k), orth, res))
+        assert s <= 1e-3 and orth <= 1e-5 and res <= 1e-5
+        idx = np.argmax(np.abs(V), axis=0)
+        assert np.all(V[idx, np.arange(k)] > 0)
+        # closed form: ||X W - X W V_k V_k^T||^2 = sum of the eigenvalues past k
+        W64 = oracle.widen(Ws[m], "bf16")
+        R = X64 @ (W64 - (W64 @ V64) @ V64.T)
+        eps = oracle.error_curve(lam_r)
+        assert abs(np.sum(R * R) - eps[k]) <= 1e-4 * eps[k] + 1e-6 * eps[0]
+        # the member alone: the same bits
+        l1, V1, i1 = lrc.lrc_eigh_multi([(dev(Cu[m], "f32"), k, None, None, None, Wd[m])], prec=prec)[0]
+        assert int(host(i1)[0]) == 0
+        assert np.array_equal(host(l1), lam) and np.array_equal(host(V1), V)
+
+
+def test_eigh_range_basis_fallbacks(lrc):
+    """d_in >= n, or n_vec > d_in: the basis is ignored (the full decomposition, bit for bit); a basis
+    without full row rank: info 3."""
+    X = inputs.block_activations(200, 1024)
+    W = inputs.weight(200, 180, "bf16", inputs.CFG_BLOCK, 0, 40)
+    C = _oracle_cov32(X, "bf16", W)[0]
+    l0, V0, _ = lrc.lrc_eigh(dev(C, "f32"), n_vec=20)
+    l1, V1, i1 = lrc.lrc_eigh_multi([(dev(C, "f32"), 20, None, None, None, dev(W, "bf16"))])[0]
+    assert int(host(i1)[0]) == 0
+    assert np.array_equal(host(l0), host(l1)) and np.array_equal(host(V0), host(V1))
+    W2 = inputs.weight(150, 300, "bf16", inputs.CFG_BLOCK, 0, 41)
+    X2 = inputs.block_activations(150, 1024)
+    C2 = _oracle_cov32(X2, "bf16", W2)[0]
+    l0, V0, _ = lrc.lrc_eigh(dev(C2, "f32"), n_vec=160)
+    l1, V1, i1 = lrc.lrc_eigh_multi([(dev(C2, "f32"), 160, None, None, None, dev(W2, "bf16"))])[0]
+    assert np.array_equal(host(l0), host(l1)) and np.array_equal(host(V0), host(V1))
+    W3 = W2.copy()
+    W3[7] = W3[3]  # two equal rows: W W^T singular
+    l3, V3, i3 = lrc.lrc_eigh_multi([(dev(C2, "f32"), 10, None, None, None, dev(W3, "bf16"))])[0]
+    assert int(host(i3)[0]) == 3
+
+
 def test_eigh_nonfinite_sets_info(lrc):
     C = np.eye(200, dtype=np.float32)
     C[3, 7] = np.inf
