@@ -450,7 +450,7 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
     for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
-    mfma_mainloop<BM, BM, G_THREADS, G_WGM, 2, 1, false, 1, KCHECK>(base, ld, rows, d_in, nullptr, acc, lds);
+    mfma_mainloop<BM, BM, G_THREADS, G_WGM, 2, 1, false, 1, KCHECK, 2, true>(base, ld, rows, d_in, nullptr, acc, lds);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm)
