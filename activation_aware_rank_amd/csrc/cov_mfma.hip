@@ -1,16 +1,25 @@
-// bf16 MFMA path of the covariance accumulation.
+// MFMA path of the covariance accumulation.
 //
+// Per call, before the chunks: e_i = 14 - q_i, where 2^(q_i - 1) <= max_t ||x_t|| ||W^T_i|| < 2^q_i.
+// By Cauchy-Schwarz |y_i(t)| 2^e_i < 2^14 for every token, a quarter of the fp16 range.
 // Per chunk of tokens (Swift-SVD page, section 2-ga: C is aggregated over the calibration
 // tokens, one chunk at a time):
 //   1. GEMM  Y^T[i][t] = sum_k W^T[i][k] X[t][k]        (bf16 MFMA, fp32 accumulation)
-//      epilogue: hi = bf16(y), lo = bf16(y - hi), stored in blocks of MK tokens:
-//      Y^T[i][t] at ((t / MK) * D + i) * MK + t % MK (D = d_out), so that the MK-token slice of
-//      consecutive rows that one k step of the SYRK reads is one contiguous run.
-//   2. SYRK  C[I,J] += (Yhi_I + Ylo_I)(Yhi_J + Ylo_J)^T as four bf16 MFMA products, fp32
-//      accumulation, for tiles I <= J.  All four are needed: dropping lo*lo would lower every
-//      quadratic form v^T C v by ||Ylo v||^2 (about 2e-6 of the diagonal, always one-signed),
-//      which shifts the small eigenvalues at the tail of the spectrum far more than that.
-// With W == NULL (C += X^T X) the chunk is transposed exactly and one product suffices.
+//      epilogue: s = y 2^e_i (exact), hi = fp16(s), lo = fp16(s - hi), so hi + lo carries 22 bits
+//      of y; stored in blocks of MK tokens: Y^T[i][t] at ((t / MK) * D + i) * MK + t % MK
+//      (D = d_out), so that the MK-token slice of consecutive rows that one k step of the SYRK
+//      reads is one contiguous run.
+//   2. SYRK  C[I,J] += 2^-(e_I + e_J) (hi_I hi_J^T + hi_I lo_J^T + lo_I hi_J^T), fp16 MFMA
+//      products with fp32 accumulation, for tiles I <= J.  The power-of-two scales cost no
+//      rounding.
+//   3. C_ii += 2^-2e_i sum_t lo_i(t)^2, summed on its own.  The lo lo^T terms are about 2^-24 of
+//      the hi hi^T ones.  Off the diagonal they are as often positive as negative and are left
+//      out.  On the diagonal they all have one sign (left out, every quadratic form v^T C v would
+//      lose ||Ylo v||^2), and inside the MFMA chain they would not survive either: a 16-token
+//      sum of lo^2 is below half a unit in the last place of the running fp32 chain, so round to
+//      nearest drops it every time.
+// With W == NULL (C += X^T X) the chunk is transposed exactly (bf16) and one bf16 product
+// suffices.
 //
 // Both phases are one "NT" kernel: D = A B^T with A and B row-major along the contraction
 // axis, which is exactly the layout the 32x32x16 bf16 MFMA operands want (each lane holds 8
@@ -257,6 +266,7 @@ __device__ __forceinline__ void mfma_mainloop(
 // FE 4: the MFMA chains restart every 64 tokens (two steps) and are added to acc with one
 // round-to-nearest fp32 add, as in mfma_mainloop.
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // s_waitcnt with vmcnt = n (0..63) and no wait on the other counters (gfx9 encoding)
 #define LRC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
@@ -271,8 +281,17 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
     constexpr int TM = T::TM, TN = T::TN, UA = T::UA, UB = T::UB;
     constexpr int U = UA > UB ? UA : UB;
     constexpr int NSIDE = NOPS / 2;
-    constexpr int NA = (NPROD == 4) ? 2 : 1;
+    // NPROD 1: one bf16 operand per side; 3: fp16 hi and lo per side, hi hi + hi lo + lo hi
+    constexpr int NA = (NPROD == 3) ? 2 : 1;
     static_assert(NSIDE == NA, "hi/lo operands per side");
+    static_assert(NPROD == 1 || NPROD == 3, "products");
+    using OpT = typename std::conditional<NPROD == 1, bf16x8_t, f16x8_t>::type;
+    auto mfma = [](OpT x, OpT y, f32x16_t c) {
+        if constexpr (NPROD == 1)
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(x, y, c, 0, 0, 0);
+    };
     constexpr int LPS = NSIDE * (UA + UB);  // loads per thread per step
     auto opoff = [](int o) { return o < NSIDE ? o * BM * MK : NSIDE * BM * MK + (o - NSIDE) * BN * MK; };
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -325,17 +344,16 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int c = ks * 2 + (lane >> 5);
-            bf16x8_t af[NA][TM], bfr[NA][TN];
+            OpT af[NA][TM], bfr[NA][TN];
 #pragma unroll
             for (int a = 0; a < NA; ++a) {
 #pragma unroll
                 for (int t = 0; t < TM; ++t)
-                    af[a][t] = *reinterpret_cast<const bf16x8_t *>(cur + opoff(a) +
-                                                                   swz(wm * T::WM + t * 32 + (lane & 31), c));
+                    af[a][t] = *reinterpret_cast<const OpT *>(cur + opoff(a) + swz(wm * T::WM + t * 32 + (lane & 31), c));
 #pragma unroll
                 for (int t = 0; t < TN; ++t)
-                    bfr[a][t] = *reinterpret_cast<const bf16x8_t *>(cur + opoff(NSIDE + a) +
-                                                                    swz(wn * T::WN + t * 32 + (lane & 31), c));
+                    bfr[a][t] =
+                        *reinterpret_cast<const OpT *>(cur + opoff(NSIDE + a) + swz(wn * T::WN + t * 32 + (lane & 31), c));
             }
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm)
@@ -343,12 +361,10 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
                 for (int tn = 0; tn < TN; ++tn) {
                     // a flush group's first slice starts the chain from a literal zero
                     const bool fresh = PAR == 0 && ks == 0;
-                    f32x16_t q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[0][tn],
-                                                                         fresh ? f32x16_t{} : p[tm][tn], 0, 0, 0);
-                    if (NPROD == 4) {
-                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[1][tn], q, 0, 0, 0);
-                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[0][tn], q, 0, 0, 0);
-                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[1][tn], q, 0, 0, 0);
+                    f32x16_t q = mfma(af[0][tm], bfr[0][tn], fresh ? f32x16_t{} : p[tm][tn]);
+                    if (NPROD == 3) {
+                        q = mfma(af[0][tm], bfr[1][tn], q);
+                        q = mfma(af[1][tm], bfr[0][tn], q);
                     }
                     p[tm][tn] = q;
                 }
@@ -385,30 +401,34 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
 __device__ __forceinline__ int acc_row(int lane, int r) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
-// Y^T[ib + row][t] for the 16 values of one lane, in the MK-token block layout: hi = bf16(y),
-// lo = bf16(y - hi)
+// Y^T[ib + row][t] for the 16 values of one lane, in the MK-token block layout: s = y 2^ex[i]
+// (exact), hi = fp16(s), lo = fp16(s - hi) (s - hi is exact in fp32), stored as fp16 bit patterns
 __device__ __forceinline__ void store_split_tile(const f32x16_t a, int64_t ib, int64_t t, int lane, int64_t d_out,
-                                                 bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo) {
+                                                 const int32_t *__restrict__ ex, bf16_t *__restrict__ Yhi,
+                                                 bf16_t *__restrict__ Ylo) {
     const int64_t tb = (t / MK) * d_out * MK + t % MK;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int64_t i = ib + acc_row(lane, r);
         if (i < d_out) {
-            const float y = a[r];
-            const bf16_t hi = f32_to_bf16(y);
-            Yhi[tb + i * MK] = hi;
-            Ylo[tb + i * MK] = f32_to_bf16(y - bf16_to_f32(hi));
+            const float y = ldexpf(a[r], ex[i]);
+            const _Float16 hi = _Float16(y);
+            const _Float16 lo = _Float16(y - float(hi));
+            Yhi[tb + i * MK] = __builtin_bit_cast(bf16_t, hi);
+            Ylo[tb + i * MK] = __builtin_bit_cast(bf16_t, lo);
         }
     }
 }
 
-// dst[rb + row][cc] += value for the upper triangle (row <= col) inside the hd x hd block
+// dst[rb + row][cc] += value for the upper triangle (row <= col) inside the hd x hd block; with
+// ex (exponents of the block's rows), value = a 2^-(ex[row] + ex[col]), exact up to fp32 range
 __device__ __forceinline__ void add_upper_tile(const f32x16_t a, int64_t rb, int64_t cc, int lane, int64_t hd,
-                                               float *__restrict__ dst, int64_t ldd) {
+                                               const int32_t *__restrict__ ex, float *__restrict__ dst, int64_t ldd) {
+    const int ec = (ex && cc < hd) ? ex[cc] : 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int64_t rr = rb + acc_row(lane, r);
-        if (rr < hd && cc < hd && rr <= cc) dst[rr * ldd + cc] += a[r];
+        if (rr < hd && cc < hd && rr <= cc) dst[rr * ldd + cc] += ex ? ldexpf(a[r], -(ex[rr] + ec)) : a[r];
     }
 }
 
@@ -436,7 +456,7 @@ __device__ __forceinline__ void gemm_tile_of(int64_t b, int64_t gi, int64_t gt, 
 template <int BM, bool KCHECK>
 __global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const bf16_t *__restrict__ X, int64_t ldx,
-             int64_t tc, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo) {
+             int64_t tc, const int32_t *__restrict__ ex, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo) {
     using Cfg = MfmaCfg<BM, BM, G_THREADS, G_WGM>;
     __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * BM * MK];
     int64_t ti, tt;
@@ -458,7 +478,7 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
         for (int tn = 0; tn < Cfg::TN; ++tn) {
             const int64_t ib = i0 + wm * Cfg::WM + tm * 32;
             const int64_t t = t0 + wn * Cfg::WN + tn * 32 + acc_col(lane);
-            store_split_tile(acc[tm][tn], ib, t, lane, d_out, Yhi, Ylo);
+            store_split_tile(acc[tm][tn], ib, t, lane, d_out, ex, Yhi, Ylo);
         }
 }
 
@@ -482,14 +502,17 @@ struct SyrkCfg {  // 4 waves of (BM/2) x (BN/2)
     static constexpr int THREADS = 256;
     static constexpr int WGM = 2;
 };
-template <int BM, int BN, int NPROD>
+// SPLIT: Y^T as fp16 hi/lo with the row exponents ex, three products (the diagonal's sum of lo^2
+// is added by k_lo_sq_add); else Y^T = X^T in bf16, one product.
+template <int BM, int BN, bool SPLIT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SYRK_WPE, SYRK_WPE)))
-k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64_t ldy, int64_t ktot, int64_t kchunk,
-           int64_t hd, float *__restrict__ C, int64_t ldc, float *__restrict__ P, int32_t n_blocks) {
+k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, const int32_t *__restrict__ ex,
+           int64_t ldy, int64_t ktot, int64_t kchunk, int64_t hd, float *__restrict__ C, int64_t ldc,
+           float *__restrict__ P, int32_t n_blocks) {
     constexpr int THREADS = SyrkCfg<BM, BN>::THREADS, WGM = SyrkCfg<BM, BN>::WGM;
     static_assert(THREADS == 256, "launch bounds");
     using Cfg = MfmaCfg<BM, BN, THREADS, WGM>;
-    constexpr int NOPS = (NPROD == 4) ? 4 : 2;
+    constexpr int NOPS = SPLIT ? 4 : 2;
     constexpr int STAGE = (NOPS / 2) * (BM + BN) * MK;  // elements of one LDS stage
     __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE];
     __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
@@ -521,7 +544,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
     const bf16_t *base[4];
     int64_t ld[4];
     int rows[4];
-    if (NPROD == 4) {
+    if (SPLIT) {
         base[0] = Yhi + offI; base[1] = Ylo + offI;
         base[2] = Yhi + offJ; base[3] = Ylo + offJ;
         rows[0] = rows[1] = rowsI; rows[2] = rows[3] = rowsJ;
@@ -531,7 +554,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
     }
     int64_t nrec[4];  // bytes from each operand's base to the end of its buffer
     for (int o = 0; o < 4; ++o) ld[o] = D;
-    if (NPROD == 4) {
+    if (SPLIT) {
         nrec[0] = nrec[1] = (D * ldy - offI) * 2;
         nrec[2] = nrec[3] = (D * ldy - offJ) * 2;
     } else {
@@ -544,7 +567,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
     // klen is a multiple of MK here, so no k check is needed
-    syrk_dma_mainloop<BM, BN, NOPS, NPROD>(base, D, rows, klen, nrec, acc, lds0, lds1, lds2);
+    syrk_dma_mainloop<BM, BN, NOPS, SPLIT ? 3 : 1>(base, D, rows, klen, nrec, acc, lds0, lds1, lds2);
     float *dst;
     int64_t ldd;
     if (s == 0) {
@@ -561,7 +584,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, int64
         for (int tn = 0; tn < Cfg::TN; ++tn) {
             const int64_t rb = int64_t(I) * BM + wm * Cfg::WM + tm * 32;
             const int64_t cc = int64_t(J) * BN + wn * Cfg::WN + tn * 32 + acc_col(lane);
-            add_upper_tile(acc[tm][tn], rb, cc, lane, hd, dst, ldd);
+            add_upper_tile(acc[tm][tn], rb, cc, lane, hd, SPLIT ? ex + int64_t(h) * hd : nullptr, dst, ldd);
         }
 }
 
@@ -596,6 +619,99 @@ __global__ void __launch_bounds__(256) k_chunk_transpose(const bf16_t *__restric
         const int64_t t = t0 + rr;
         if (c0 + cc < d && t < ldy) Yt[((t / MK) * d + c0 + cc) * MK + t % MK] = tile[rr][cc];
     }
+}
+
+// Sum of squares of one row of d bf16 values (16-byte aligned, d a multiple of 8), wave-wide:
+// 16-byte loads, then a butterfly, so every lane returns the same value.
+__device__ __forceinline__ float wave_row_sq(const bf16_t *__restrict__ row, int64_t d, int lane) {
+    float acc = 0.f;
+    for (int64_t k = int64_t(lane) * 8; k < d; k += 512) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(row + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float lo = __uint_as_float(v[q] << 16), hi = __uint_as_float(v[q] & 0xffff0000u);
+            acc = fmaf(lo, lo, acc);
+            acc = fmaf(hi, hi, acc);
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    return acc;
+}
+
+constexpr int XNORM_BLOCKS = 1024;
+// part[b] = max over the rows t of block b's share of ||x_t||^2 (0 for none)
+__global__ void __launch_bounds__(256) k_xnorm_partial(const bf16_t *__restrict__ X, int64_t ldx, int64_t n_tok,
+                                                       int64_t d, float *__restrict__ part) {
+    __shared__ float sh[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float m = 0.f;
+    for (int64_t t = int64_t(blockIdx.x) * 4 + wave; t < n_tok; t += int64_t(gridDim.x) * 4)
+        m = fmaxf(m, wave_row_sq(X + t * ldx, d, lane));
+    if (lane == 0) sh[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+// ex[i] = 14 - q with 2^(q-1) <= b < 2^q, b = max_t ||x_t|| ||W^T_i||: |y_i(t)| 2^ex[i] < 2^14.
+// 0 when b is zero or not finite (a NaN or infinity then reaches C as before).  One wave per row.
+__global__ void __launch_bounds__(256) k_split_exp(const float *__restrict__ part, int npart,
+                                                   const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out,
+                                                   int32_t *__restrict__ ex) {
+    const int lane = threadIdx.x & 63;
+    const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (i >= d_out) return;
+    float xm = 0.f;
+    for (int b = lane; b < npart; b += 64) xm = fmaxf(xm, part[b]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) xm = fmaxf(xm, __shfl_xor(xm, m));
+    const float w2 = wave_row_sq(Wt + i * d_in, d_in, lane);
+    const double b = sqrt(double(xm) * double(w2));
+    int e = 0;
+    if (b > 0.0 && b <= 1.7e308) {
+        int q;
+        (void)frexp(b, &q);
+        e = min(126, max(-126, 14 - q));
+    }
+    if (lane == 0) ex[i] = e;
+}
+
+constexpr int LOSQ_SEG = 16;  // token-block segments of k_lo_sq
+// part[seg][i] = sum of lo_i(t)^2 (fp16 values, fp32 sums) over the MK-token blocks
+// b = seg, seg + LOSQ_SEG, ... < nb of the chunk's Y^T lo.  A workgroup covers 64 rows, whose
+// MK-token slices are one 4 KB run per block: thread t reads 16 bytes of row t / 4.
+__global__ void __launch_bounds__(256) k_lo_sq(const bf16_t *__restrict__ Ylo, int64_t D, int64_t nb,
+                                               float *__restrict__ part) {
+    const int64_t i = int64_t(blockIdx.x) * 64 + (threadIdx.x >> 2);
+    const int qd = threadIdx.x & 3;
+    float acc = 0.f;
+    if (i < D) {
+        for (int64_t b = blockIdx.y; b < nb; b += LOSQ_SEG) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(Ylo + (b * D + i) * MK + qd * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = float(__builtin_bit_cast(_Float16, uint16_t(v[q] & 0xffffu)));
+                const float hi = float(__builtin_bit_cast(_Float16, uint16_t(v[q] >> 16)));
+                acc = fmaf(lo, lo, acc);
+                acc = fmaf(hi, hi, acc);
+            }
+        }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (i < D && qd == 0) part[int64_t(blockIdx.y) * D + i] = acc;
+}
+
+// C_jj += 2^-2ex[j] sum_seg part[seg][j] in segment order; the diagonal of head block h = j / hd
+// is at C[j * ldc + j % hd]
+__global__ void __launch_bounds__(256) k_lo_sq_add(const float *__restrict__ part, int64_t D, int64_t hd,
+                                                   const int32_t *__restrict__ ex, float *__restrict__ C, int64_t ldc) {
+    const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (j >= D) return;
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < LOSQ_SEG; ++g) s += part[int64_t(g) * D + j];
+    C[j * ldc + j % hd] += ldexpf(s, -2 * ex[j]);
 }
 
 __global__ void k_fill_f32(float *__restrict__ p, int64_t n) {
@@ -677,6 +793,11 @@ size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out,
     c.carve<bf16_t>(size_t(d_out) * size_t(p.ldy));
     if (has_w) c.carve<bf16_t>(size_t(d_out) * size_t(p.ldy));
     c.carve<float>(size_t(p.nsplit - 1) * size_t(n_blocks) * size_t(hd) * size_t(hd) + 1);
+    if (has_w) {
+        c.carve<float>(XNORM_BLOCKS);
+        c.carve<int32_t>(size_t(d_out));
+        c.carve<float>(size_t(LOSQ_SEG) * size_t(d_out));
+    }
     // the generic path's buffer, used when the call's pointers are not aligned
     c.carve<float>(size_t(d_out) * size_t(std::min<int64_t>(4096, n_tok)));
     return c.off;
@@ -692,13 +813,23 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
     bf16_t *Ylo = has_w ? cv.carve<bf16_t>(size_t(a.d_out) * size_t(p.ldy)) : nullptr;
     const size_t pn = size_t(p.nsplit - 1) * size_t(a.n_blocks) * size_t(hd) * size_t(hd);
     float *P = cv.carve<float>(pn + 1);
-    if (!P || !Yhi || (has_w && (!Wt || !Ylo))) return fail(LRC_ERR_WORKSPACE, "covariance workspace too small");
+    float *part = has_w ? cv.carve<float>(XNORM_BLOCKS) : nullptr;
+    int32_t *ex = has_w ? cv.carve<int32_t>(size_t(a.d_out)) : nullptr;
+    float *lpart = has_w ? cv.carve<float>(size_t(LOSQ_SEG) * size_t(a.d_out)) : nullptr;
+    if (!P || !Yhi || (has_w && (!Wt || !Ylo || !part || !ex || !lpart)))
+        return fail(LRC_ERR_WORKSPACE, "covariance workspace too small");
     const bf16_t *X = static_cast<const bf16_t *>(a.X);
     if (has_w) {
         dim3 g(cdiv(a.d_out, 64), cdiv(a.d_in, 64));
         hipLaunchKernelGGL(k_transpose_bf16, g, dim3(256), 0, s, static_cast<const bf16_t *>(a.W), a.ldw, a.d_in,
                            a.d_out, Wt, a.d_in);
         LRC_LAUNCH_CHECK("k_transpose_bf16");
+        // the row exponents of the fp16 split, from all tokens of the call
+        hipLaunchKernelGGL(k_xnorm_partial, dim3(XNORM_BLOCKS), dim3(256), 0, s, X, a.ldx, a.n_tok, a.d_in, part);
+        LRC_LAUNCH_CHECK("k_xnorm_partial");
+        hipLaunchKernelGGL(k_split_exp, dim3(unsigned(cdiv(a.d_out, 4))), dim3(256), 0, s, part, XNORM_BLOCKS, Wt,
+                           a.d_in, a.d_out, ex);
+        LRC_LAUNCH_CHECK("k_split_exp");
     }
     if (pn) {
         hipLaunchKernelGGL(k_fill_f32, dim3(1024), dim3(256), 0, s, P, int64_t(pn));
@@ -713,10 +844,10 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
             // d_in a multiple of the k step: no partial last step, no k check in the loads
             if (a.d_in % MK == 0)
                 LRC_TIMED_LAUNCH("k_cov_gemm_y", fl, (k_cov_gemm_y<G_BM, false>), g, dim3(G_THREADS), 0, s, Wt,
-                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo);
+                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, ex, Yhi, Ylo);
             else
                 LRC_TIMED_LAUNCH("k_cov_gemm_y", fl, (k_cov_gemm_y<G_BM, true>), g, dim3(G_THREADS), 0, s, Wt,
-                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, Yhi, Ylo);
+                                 a.d_in, a.d_out, X + t0 * a.ldx, a.ldx, tc, ex, Yhi, Ylo);
             LRC_LAUNCH_CHECK("k_cov_gemm_y");
         } else {
             dim3 g(cdiv(a.d_out, 64), cdiv(ktot, 64));
@@ -728,18 +859,26 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         // algorithmic flops of the launch: the upper triangle (incl. diagonal) of each head block
         const double fl = double(tc) * double(hd) * double(hd + 1) * double(a.n_blocks);
         if (has_w && p.wide)
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, 4>), g, dim3(256), 0, s, Yhi, Ylo, p.ldy, ktot,
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, true>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy, ktot,
                              kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         else if (has_w)
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, 4>), g, dim3(256), 0, s, Yhi, Ylo, p.ldy, ktot,
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, true>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy, ktot,
                              kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         else if (p.wide)
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, 1>), g, dim3(256), 0, s, Yhi, Ylo, p.ldy, ktot,
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, false>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy, ktot,
                              kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         else
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, 1>), g, dim3(256), 0, s, Yhi, Ylo, p.ldy, ktot,
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, false>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy, ktot,
                              kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         LRC_LAUNCH_CHECK("k_cov_syrk");
+        if (has_w) {
+            hipLaunchKernelGGL(k_lo_sq, dim3(unsigned(cdiv(a.d_out, 64)), LOSQ_SEG), dim3(256), 0, s, Ylo, a.d_out,
+                               ktot / MK, lpart);
+            LRC_LAUNCH_CHECK("k_lo_sq");
+            hipLaunchKernelGGL(k_lo_sq_add, dim3(unsigned(cdiv(a.d_out, 256))), dim3(256), 0, s, lpart, a.d_out, hd, ex,
+                               a.C, a.ldc);
+            LRC_LAUNCH_CHECK("k_lo_sq_add");
+        }
     }
     if (p.nsplit > 1) {
         hipLaunchKernelGGL(k_add_partials, dim3(2048), dim3(256), 0, s, a.C, a.ldc, P, p.nsplit, hd, a.n_blocks);

@@ -327,8 +327,9 @@ def main():
                  "launches": syrk_n, "avg_launch_ms": syrk_ms / max(syrk_n, 1),
                  "total_ms_per_step": syrk_ms / a.steps,
                  "per_launch": "algorithmic flops = tokens in the chunk x d_out (d_out + 1) (upper triangle incl. "
-                               "diagonal); the kernel executes 4 bf16 MFMA products per flop pair (hi/lo split), "
-                               "so executed MFMA utilisation is 4x frac"}
+                               "diagonal); the kernel executes 3 fp16 MFMA products per flop pair (scaled hi/lo "
+                               "split: hi hi + hi lo + lo hi; the diagonal's sum of lo^2 is a separate pass), so "
+                               "executed MFMA utilisation is 3x frac"}
     gemm_tf = gemm_fl / (gemm_ms / 1000.0) / 1e12 if gemm_ms > 0 else 0.0
     roof_gemm = {"kernel": "k_cov_gemm_y", "bound": "mfma", "achieved": gemm_tf, "peak": PEAK_BF16_TFLOPS,
                  "unit": "TFLOP/s", "frac": gemm_tf / PEAK_BF16_TFLOPS, "launches": gemm_n,

@@ -112,10 +112,15 @@ const char *lrc_last_error(void);
  *    matrix with leading dim ldc >= hd (upper triangle accumulated).
  * Accumulates: the caller zeroes C before the first chunk.  Any chunking of the tokens
  *    gives the same C up to fp32 rounding of the running sum.
- * Arithmetic: bf16 inputs use bf16 MFMA with fp32 accumulation for Y; Y is then split
- *    into bf16 hi + lo parts and C += (hi + lo)^T (hi + lo) as four bf16 products (fp32
- *    accumulation).
+ * Arithmetic: bf16 inputs use bf16 MFMA with fp32 accumulation for Y.  Output i is then
+ *    scaled by an exact power of two 2^e_i, chosen per call from max_t ||x_t|| ||W[:, i]||
+ *    so that |y 2^e_i| < 2^14, and split into fp16 hi + lo (22 bits of y).  C gains
+ *    2^-(e_i + e_j) (hi hi^T + hi lo^T + lo hi^T) from three fp16 MFMA products (fp32
+ *    accumulation), plus sum_t lo_i(t)^2 on the diagonal; the off-diagonal lo lo^T terms
+ *    (about 2^-24 of hi hi^T) are left out.  W == NULL: X^T X from one bf16 product (exact
+ *    products, fp32 sums).
  *    fp32 inputs use fp32 arithmetic throughout.
+ *    A non-finite x or W entry reaches C as before (the scale is then 1).
  * info: one int32; set to 1 when the updated C has a non-finite diagonal entry.
  * Errors: LRC_ERR_ARG for non-positive sizes, small leading dims, d_out % n_blocks != 0,
  *    NULL X or C; LRC_ERR_DTYPE for other dtypes or x_t != w_t; LRC_ERR_WORKSPACE.
