@@ -370,6 +370,19 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
                 }
         }
         if (PAR == 1) flush();
+        if constexpr (NPROD == 3 && LPS == 12 && NA * (TM + TN) == 12 && TM * TN * NPROD == 24) {
+            // 256 x 128 split tile: spread the step's 12 loads over the first slice's 24 MFMAs, with
+            // the second slice's 12 LDS reads between them, instead of issuing the loads in one
+            // burst after the barrier (7 % faster at d_out 11008, 3 % at 4096)
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads of the first slice
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load into LDS
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read of the second slice
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);  // MFMAs of the second slice
+        }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
