@@ -436,6 +436,14 @@ lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, 
     hipLaunchKernelGGL(k_trinv, dim3(nblk), dim3(256), 0, s, L, ldl, dim, Linv);
     LRC_LAUNCH_CHECK("k_trinv");
     lrc_status st = LRC_OK;
+    // Left-looking when one block of B spans at least 128 output tiles: block b first takes the
+    // products with all blocks solved before it (one GEMM with K = the solved width), then is
+    // solved in place with the inverse of its diagonal block.  Right-looking otherwise: each solved
+    // block updates every block after it (K = 64), which rewrites the unsolved part of B once per
+    // block but keeps many tiles busy when B is narrow.  For a 4096 x 11008 B the right-looking
+    // order made 64 passes over up to 360 MB each (53 ms against 4.5 ms); for 5120 x 1024 the
+    // left-looking one ran 16 tiles at a time (18.6 ms against 6.8 ms).
+    const bool left = cdiv(side ? m : n, GT) >= 128;
     for (int step = 0; step < nblk && st == LRC_OK; ++step) {
         // forward order for L^{-1} B and B L^{-T}; backward for L^{-T} B and B L^{-1}
         const bool fwd = (side == 0) == (trans == 0);
@@ -444,10 +452,17 @@ lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, 
         const double *Li = Linv + int64_t(b) * NBC * NBC;
         if (side == 0) {
             double *Bb = B + b0 * ldb;
+            if (left && !trans && b0 > 0) {  // B_b -= L[b0:b1, :b0] X[:b0]
+                st = launch_gemm<0, 0, 0, 0, 0>(gemm(nb, n, b0, L + b0 * ldl, ldl, B, ldb, Bb, ldb, -1.0, 1.0), s);
+            } else if (left && trans && b1 < m) {  // B_b -= L[b1:, b0:b1]^T X[b1:]
+                st = launch_gemm<1, 0, 0, 0, 0>(
+                    gemm(nb, n, m - b1, L + b1 * ldl + b0, ldl, B + b1 * ldb, ldb, Bb, ldb, -1.0, 1.0), s);
+            }
+            if (st != LRC_OK) break;
             // X_b = op(Linv_b) B_b in place (K = nb <= one tile of rows)
             const GemmArgs g = gemm(nb, n, nb, Li, NBC, Bb, ldb, Bb, ldb, 1.0, 0.0);
             st = trans ? launch_gemm<1, 0, 2, 0, 0>(g, s) : launch_gemm<0, 0, 1, 0, 0>(g, s);
-            if (st != LRC_OK) break;
+            if (st != LRC_OK || left) continue;
             if (!trans && b1 < m) {  // B[b1:] -= L[b1:, b0:b1] X_b
                 st = launch_gemm<0, 0, 0, 0, 0>(
                     gemm(m - b1, n, nb, L + b1 * ldl + b0, ldl, Bb, ldb, B + b1 * ldb, ldb, -1.0, 1.0), s);
@@ -456,10 +471,17 @@ lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, 
             }
         } else {
             double *Bb = B + b0;
+            if (left && !trans && b1 < n) {  // B_b -= X[:, b1:] L[b1:, b0:b1]
+                st = launch_gemm<0, 0, 0, 0, 0>(
+                    gemm(m, nb, n - b1, B + b1, ldb, L + b1 * ldl + b0, ldl, Bb, ldb, -1.0, 1.0), s);
+            } else if (left && trans && b0 > 0) {  // B_b -= X[:, :b0] L[b0:b1, :b0]^T
+                st = launch_gemm<0, 1, 0, 0, 0>(gemm(m, nb, b0, B, ldb, L + b0 * ldl, ldl, Bb, ldb, -1.0, 1.0), s);
+            }
+            if (st != LRC_OK) break;
             // X_b = B_b op(Linv_b) in place (K = nb <= one tile of columns)
             const GemmArgs g = gemm(m, nb, nb, Bb, ldb, Li, NBC, Bb, ldb, 1.0, 0.0);
             st = trans ? launch_gemm<0, 1, 0, 1, 0>(g, s) : launch_gemm<0, 0, 0, 2, 0>(g, s);
-            if (st != LRC_OK) break;
+            if (st != LRC_OK || left) continue;
             if (!trans && b0 > 0) {  // B[:, :b0] -= X_b L[b0:b1, :b0]
                 st = launch_gemm<0, 0, 0, 0, 0>(gemm(m, b0, nb, Bb, ldb, L + b0 * ldl, ldl, B, ldb, -1.0, 1.0), s);
             } else if (trans && b1 < n) {  // B[:, b1:] -= X_b L[b1:, b0:b1]^T

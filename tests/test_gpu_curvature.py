@@ -134,6 +134,23 @@ def test_trsm_parity(lrc, side, trans, scaled):
         assert err <= 1e-12, "trsm error %.3e" % err
 
 
+@pytest.mark.parametrize("side,trans", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_trsm_wide_parity(lrc, side, trans):
+    """B with at least 128 tiles of 64 across one block (8200 wide): the solve takes the
+    left-looking order (one product per block with every block solved before it)."""
+    m, n = (200, 8200) if side == 0 else (8200, 200)
+    dim = m if side == 0 else n
+    _say("trsm wide side=%d trans=%d m=%d n=%d" % (side, trans, m, n))
+    L, Lnan = _lower_with_nan_upper(dim, 70 + 2 * side + trans, False)
+    B = _gauss64(m, n, 80 + 2 * side + trans)
+    Bd = dev(B, "f64")
+    lrc.lrc_trsm(side, trans, dev(Lnan, "f64"), Bd)
+    X = host(Bd)
+    Xo = oracle.tri_solve(side, trans, L, B)
+    err = np.max(np.abs(X - Xo)) / np.max(np.abs(Xo))
+    assert err <= 1e-12, "trsm error %.3e" % err
+
+
 def test_trsm_strided_and_single_row(lrc):
     _say("trsm ldb > n, m = 1; trmm on a column slice")
     L, Lnan = _lower_with_nan_upper(1, 61, False)

@@ -78,6 +78,37 @@ def test_cov_bf16_mfma_ragged(lrc, n_tok, d_in, d_out):
     assert np.all(np.tril(C, -1) == 0)
 
 
+def _bf16_pow2(a, e):
+    """bf16 bit patterns times 2^e (e broadcast against a), exact for the normal range used here."""
+    f = (a.astype(np.uint32) << 16).view(np.float32) * np.exp2(np.asarray(e, dtype=np.float32))
+    return (np.ascontiguousarray(f, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("sx,sw", [(10, 7), (-14, -10)])
+def test_cov_split_scaled_columns(lrc, sx, sw):
+    """Per-output power-of-two scales of the fp16 hi/lo split: output magnitudes spread over 2^-9 ..
+    2^9 around 2^(sx + sw) (far outside the fp16 range at either end without the scales), two
+    outputs identically zero.  Every upper entry is checked against sqrt(C_ii C_jj), so a column
+    that lost bits to fp16 underflow or overflow fails even when it is small next to lambda_max."""
+    _say("cov split scales 2^%d x 2^%d, 6000 x 256 -> 520" % (sx, sw))
+    n_tok, d_in, d_out = 6000, 256, 520
+    X = _bf16_pow2(inputs.block_activations(d_in, n_tok), sx)
+    e = sw + (np.arange(d_out) % 7) * 3 - 9
+    W = _bf16_pow2(inputs.weight(d_in, d_out, "bf16", inputs.CFG_BLOCK, 0, 2), e[None, :])
+    W[:, [5, 17]] = 0
+    C = host(_cov_gpu(lrc, X, "bf16", W))
+    Cr = oracle.covariance(X, "bf16", W, "bf16")
+    dg = np.diag(Cr)
+    scale = np.sqrt(np.outer(dg, dg))
+    U = np.triu(np.ones((d_out, d_out), dtype=bool)) & (scale > 0)
+    rel = np.max(np.abs(C - Cr)[U] / scale[U])
+    rel_diag = np.max(np.abs(np.diag(C) - dg)[dg > 0] / dg[dg > 0])
+    print("max |dC_ij| / sqrt(C_ii C_jj) = %.3e, diagonal %.3e" % (rel, rel_diag))
+    assert rel <= 1e-5 and rel_diag <= 1e-5
+    for j in (5, 17):  # a zero output gives an exactly zero row and column
+        assert np.all(C[j, j:] == 0) and np.all(C[:j, j] == 0)
+
+
 def test_cov_identity_weight(lrc):
     _say("cov bf16 W = I, 3000 x 264")
     X = inputs.block_activations(264, 3000)
