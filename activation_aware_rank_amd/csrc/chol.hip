@@ -218,20 +218,35 @@ GemmArgs gemm(int64_t M, int64_t N, int64_t K, const double *A, int64_t lda, con
 }
 
 // Inverse of the lower-triangular 64x64 matrix in s (rows past the valid size padded with the
-// identity) into inv, column c by thread c: row i of L^{-1} e_c from rows < i.  A thread reads
-// and writes only its own column of inv, so the loop needs no barrier.
+// identity) into inv, column c by thread c: forward substitution L x = e_c with x held in registers
+// (fully unrolled, so every index is static), x_i = (delta_ic - sum_{p<i} L_ip x_p) / L_ii; the
+// rows above c come out as zero by themselves.  Each row's sum runs in two interleaved chains.  The
+// L_ip reads are the same address for every lane (LDS broadcast).  A thread writes only its own
+// column of inv, so no barrier is needed.
 __device__ __forceinline__ void lower_inverse_64(const double (*s)[NBC + 1], double (*inv)[NBC + 1]) {
     const int c = threadIdx.x;
     if (c >= NBC) return;
+    double x[NBC];
+#pragma unroll
     for (int i = 0; i < NBC; ++i) {
-        double x = (i == c) ? 1.0 : 0.0;
-        for (int p = c; p < i; ++p) x -= s[i][p] * inv[p][c];
-        inv[i][c] = (i >= c) ? x / s[i][i] : 0.0;
+        double a0 = (i == c) ? 1.0 : 0.0, a1 = 0.0;
+#pragma unroll
+        for (int p = 0; p + 1 < i; p += 2) {
+            a0 = fma(-s[i][p], x[p], a0);
+            a1 = fma(-s[i][p + 1], x[p + 1], a1);
+        }
+        if (i & 1) a0 = fma(-s[i][i - 1], x[i - 1], a0);
+        x[i] = (a0 + a1) / s[i][i];
     }
+#pragma unroll
+    for (int i = 0; i < NBC; ++i) inv[i][c] = (i >= c) ? x[i] : 0.0;
 }
 
 // Factor the diagonal block A[j0:j0+nb, j0:j0+nb] (lower triangle read) in place, zero its strict
 // upper triangle, and write the inverse of the factor (64x64, zero-padded) to Linv.
+// Left-looking (Crout) order, one wave, thread i holding row i: column c first takes
+// a_ic -= sum_{p<c} l_ip l_cp (two interleaved chains, in registers), then the pivot d = sqrt(a_cc)
+// divides it.  Two barriers per column.
 // info: 1 when a pivot is not finite, 3 when a pivot is <= 0 (first failure kept).
 __global__ __launch_bounds__(256) void k_potrf_diag(double *__restrict__ A, int64_t lda, int64_t n, int64_t j0,
                                                     double *__restrict__ Linv, int32_t *__restrict__ info) {
@@ -248,21 +263,30 @@ __global__ __launch_bounds__(256) void k_potrf_diag(double *__restrict__ A, int6
     __syncthreads();
     bool bad = false;
     for (int c = 0; c < nb; ++c) {
-        const double p = s[c][c];
-        const double d = sqrt(p);
-        if (t == 0 && !bad && !(p > 0.0 && p <= 1.7976931348623157e308)) {
+        double v = 0.0;
+        if (t >= c && t < NBC) {
+            double a0 = s[t][c], a1 = 0.0;
+            int p = 0;
+            for (; p + 1 < c; p += 2) {
+                a0 = fma(-s[t][p], s[c][p], a0);
+                a1 = fma(-s[t][p + 1], s[c][p + 1], a1);
+            }
+            if (p < c) a0 = fma(-s[t][p], s[c][p], a0);
+            v = a0 + a1;
+            if (t == c) s[c][c] = v;
+        }
+        __syncthreads();
+        const double pv = s[c][c];
+        const double d = sqrt(pv);
+        if (t == 0 && !bad && !(pv > 0.0 && pv <= 1.7976931348623157e308)) {
             bad = true;
-            if (*info == 0) *info = (p != p || p > 1.7976931348623157e308) ? LRC_INFO_NONFINITE : LRC_INFO_NOT_PD;
+            if (*info == 0) *info = (pv != pv || pv > 1.7976931348623157e308) ? LRC_INFO_NONFINITE : LRC_INFO_NOT_PD;
         }
-        if (t > c && t < NBC) s[t][c] = s[t][c] / d;
+        if (t > c && t < NBC) s[t][c] = v / d;
         __syncthreads();
-        if (t == 0) s[c][c] = d;
-        for (int e = (c + 1) * NBC + t; e < NBC * NBC; e += 256) {
-            const int i = e >> 6, j = e & 63;
-            if (j > c && j <= i) s[i][j] -= s[i][c] * s[j][c];
-        }
-        __syncthreads();
+        if (t == c) s[c][c] = d;
     }
+    __syncthreads();
     lower_inverse_64(s, inv);
     __syncthreads();
     for (int e = t; e < NBC * NBC; e += 256) {
