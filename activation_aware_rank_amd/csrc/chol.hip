@@ -39,6 +39,8 @@ struct GemmArgs {
     int64_t ldc;
     double alpha, beta;
     int tiles;   // 0 every tile; 1 tiles with ti >= tj, writing row >= col; 2 ti <= tj, row <= col
+    int split = 1;        // > 1: the k range in split parts (grid z), each writing alpha * its
+    double *P = nullptr;  // partial product to P + z * M * N (row-major M x N); C is not touched
 };
 
 // op(A)[i][k] is A[i*lda + k] (TA 0) or A[k*lda + i] (TA 1); op(B)[k][j] is B[k*ldb + j] (TB 0)
@@ -56,6 +58,11 @@ __global__ __launch_bounds__(256) void k_dgemm(GemmArgs g) {
     if (MA == 2) kb = max(kb, m0);
     if (MB == 1) ke = min(ke, n0 + GT);
     if (MB == 2) kb = max(kb, n0);
+    if (g.split > 1) {  // part z of the k range, in whole k-tiles
+        const int64_t per = ((g.K + g.split - 1) / g.split + GK - 1) / GK * GK;
+        kb = max(kb, int64_t(blockIdx.z) * per);
+        ke = min(ke, int64_t(blockIdx.z + 1) * per);
+    }
 
     __shared__ double sA[GK][GLD];
     __shared__ double sB[GK][GLD];
@@ -174,7 +181,9 @@ __global__ __launch_bounds__(256) void k_dgemm(GemmArgs g) {
                 if (g.tiles == 1 && row < col) continue;
                 if (g.tiles == 2 && row > col) continue;
                 const double v = g.alpha * acc[a][b][r];
-                if (OUTF == 1) {
+                if (g.split > 1) {
+                    g.P[(int64_t(blockIdx.z) * g.M + row) * g.N + col] = v;
+                } else if (OUTF == 1) {
                     g.Cf[row * g.ldc + col] = float(v);
                 } else {
                     double* p = g.C + row * g.ldc + col;
@@ -193,7 +202,8 @@ lrc_status launch_gemm(const GemmArgs &g, hipStream_t s) {
     double flops = 2.0 * double(g.M) * double(g.N) * double(g.K);
     if (g.tiles != 0) flops = double(g.M) * double(g.M + 1) * double(g.K);
     if (MA != 0 || MB != 0) flops = double(g.M) * double(g.N) * double(g.K + 1);
-    LRC_TIMED_LAUNCH("k_dgemm", flops, (k_dgemm<TA, TB, MA, MB, OUTF>), dim3(gx, gy), dim3(256), 0, s, g);
+    LRC_TIMED_LAUNCH("k_dgemm", flops, (k_dgemm<TA, TB, MA, MB, OUTF>), dim3(gx, gy, std::max(1, g.split)), dim3(256),
+                     0, s, g);
     LRC_LAUNCH_CHECK("k_dgemm");
     return LRC_OK;
 }
@@ -330,6 +340,18 @@ __global__ void k_zero_upper(double *__restrict__ A, int64_t lda, int64_t n) {
             A[r * lda + c] = 0.0;
 }
 
+// C[row][col] = beta C[row][col] + sum_z P[z][row][col] (z in order), for an M x N block of C
+__global__ void k_splitk_reduce(const double *__restrict__ P, int split, int64_t M, int64_t N, double beta,
+                                double *__restrict__ C, int64_t ldc) {
+    const int64_t total = M * N;
+    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total; e += int64_t(gridDim.x) * blockDim.x) {
+        double v = 0.0;
+        for (int z = 0; z < split; ++z) v += P[int64_t(z) * total + e];
+        double *c = C + (e / N) * ldc + e % N;
+        *c = beta != 0.0 ? v + beta * *c : v;
+    }
+}
+
 __global__ void k_copy2d(const double *__restrict__ X, int64_t ldx, int64_t rows, int64_t cols, double *__restrict__ Y,
                          int64_t ldy) {
     const int64_t n = rows * cols;
@@ -447,9 +469,34 @@ lrc_status trmm_run(int side, int trans, int64_t m, int64_t n, const double *L, 
     return LRC_OK;
 }
 
+constexpr int TRSM_SPLIT_MAX = 8;  // k-range parts of the left-looking products
+// the left-looking order (see trsm_run) when one block of B spans at least 128 output tiles
+bool trsm_left(int side, int64_t m, int64_t n) { return cdiv(side ? m : n, GT) >= 128; }
+
 size_t trsm_workspace(int side, int64_t m, int64_t n) {
     const int64_t dim = side ? n : m;
-    return align256(size_t(cdiv(dim, NBC)) * NBC * NBC * sizeof(double));
+    size_t bytes = align256(size_t(cdiv(dim, NBC)) * NBC * NBC * sizeof(double));
+    // partial products of the split left-looking updates: TRSM_SPLIT_MAX blocks of 64 x n (m x 64)
+    if (trsm_left(side, m, n)) bytes += align256(size_t(TRSM_SPLIT_MAX) * NBC * size_t(side ? m : n) * sizeof(double));
+    return bytes;
+}
+
+// C -= op(A) op(B) (M x N, K long) with the k range split over up to TRSM_SPLIT_MAX groups of
+// workgroups (at least 256 k per part), the parts added in order by k_splitk_reduce; P holds
+// split * M * N doubles.  Used where M x N has few tiles but K is long.
+template <int TA, int TB>
+lrc_status gemm_sub_splitk(int64_t M, int64_t N, int64_t K, const double *A, int64_t lda, const double *B,
+                           int64_t ldb, double *C, int64_t ldc, double *P, hipStream_t s) {
+    GemmArgs g = gemm(M, N, K, A, lda, B, ldb, C, ldc, -1.0, 1.0);
+    const int split = int(std::min<int64_t>(TRSM_SPLIT_MAX, std::max<int64_t>(1, K / 256)));
+    if (split == 1) return launch_gemm<TA, TB, 0, 0, 0>(g, s);
+    g.split = split;
+    g.P = P;
+    lrc_status st = launch_gemm<TA, TB, 0, 0, 0>(g, s);
+    if (st != LRC_OK) return st;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(grid1d(M * N)), dim3(256), 0, s, P, split, M, N, 1.0, C, ldc);
+    LRC_LAUNCH_CHECK("k_splitk_reduce");
+    return LRC_OK;
 }
 
 lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, int64_t ldl, double *B, int64_t ldb,
@@ -457,17 +504,19 @@ lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, 
     double *Linv = static_cast<double *>(ws);
     const int64_t dim = side ? n : m;
     const int nblk = cdiv(dim, NBC);
+    double *P = reinterpret_cast<double *>(static_cast<char *>(ws) + align256(size_t(nblk) * NBC * NBC * sizeof(double)));
     hipLaunchKernelGGL(k_trinv, dim3(nblk), dim3(256), 0, s, L, ldl, dim, Linv);
     LRC_LAUNCH_CHECK("k_trinv");
     lrc_status st = LRC_OK;
     // Left-looking when one block of B spans at least 128 output tiles: block b first takes the
-    // products with all blocks solved before it (one GEMM with K = the solved width), then is
-    // solved in place with the inverse of its diagonal block.  Right-looking otherwise: each solved
+    // products with all blocks solved before it (one GEMM with K = the solved width, its k range
+    // split over up to 8 groups of workgroups so that the few output tiles still fill the GPU), then
+    // is solved in place with the inverse of its diagonal block.  Right-looking otherwise: each solved
     // block updates every block after it (K = 64), which rewrites the unsolved part of B once per
     // block but keeps many tiles busy when B is narrow.  For a 4096 x 11008 B the right-looking
     // order made 64 passes over up to 360 MB each (53 ms against 4.5 ms); for 5120 x 1024 the
     // left-looking one ran 16 tiles at a time (18.6 ms against 6.8 ms).
-    const bool left = cdiv(side ? m : n, GT) >= 128;
+    const bool left = trsm_left(side, m, n);
     for (int step = 0; step < nblk && st == LRC_OK; ++step) {
         // forward order for L^{-1} B and B L^{-T}; backward for L^{-T} B and B L^{-1}
         const bool fwd = (side == 0) == (trans == 0);
@@ -477,10 +526,9 @@ lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, 
         if (side == 0) {
             double *Bb = B + b0 * ldb;
             if (left && !trans && b0 > 0) {  // B_b -= L[b0:b1, :b0] X[:b0]
-                st = launch_gemm<0, 0, 0, 0, 0>(gemm(nb, n, b0, L + b0 * ldl, ldl, B, ldb, Bb, ldb, -1.0, 1.0), s);
+                st = gemm_sub_splitk<0, 0>(nb, n, b0, L + b0 * ldl, ldl, B, ldb, Bb, ldb, P, s);
             } else if (left && trans && b1 < m) {  // B_b -= L[b1:, b0:b1]^T X[b1:]
-                st = launch_gemm<1, 0, 0, 0, 0>(
-                    gemm(nb, n, m - b1, L + b1 * ldl + b0, ldl, B + b1 * ldb, ldb, Bb, ldb, -1.0, 1.0), s);
+                st = gemm_sub_splitk<1, 0>(nb, n, m - b1, L + b1 * ldl + b0, ldl, B + b1 * ldb, ldb, Bb, ldb, P, s);
             }
             if (st != LRC_OK) break;
             // X_b = op(Linv_b) B_b in place (K = nb <= one tile of rows)
@@ -496,10 +544,9 @@ lrc_status trsm_run(int side, int trans, int64_t m, int64_t n, const double *L, 
         } else {
             double *Bb = B + b0;
             if (left && !trans && b1 < n) {  // B_b -= X[:, b1:] L[b1:, b0:b1]
-                st = launch_gemm<0, 0, 0, 0, 0>(
-                    gemm(m, nb, n - b1, B + b1, ldb, L + b1 * ldl + b0, ldl, Bb, ldb, -1.0, 1.0), s);
+                st = gemm_sub_splitk<0, 0>(m, nb, n - b1, B + b1, ldb, L + b1 * ldl + b0, ldl, Bb, ldb, P, s);
             } else if (left && trans && b0 > 0) {  // B_b -= X[:, :b0] L[b0:b1, :b0]^T
-                st = launch_gemm<0, 1, 0, 0, 0>(gemm(m, nb, b0, B, ldb, L + b0 * ldl, ldl, Bb, ldb, -1.0, 1.0), s);
+                st = gemm_sub_splitk<0, 1>(m, nb, b0, B, ldb, L + b0 * ldl, ldl, Bb, ldb, P, s);
             }
             if (st != LRC_OK) break;
             // X_b = B_b op(Linv_b) in place (K = nb <= one tile of columns)

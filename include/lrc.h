@@ -293,7 +293,9 @@ lrc_status lrc_allocate_ranks(int32_t n_mats, const double *alpha, const double 
  *   workspace of lrc_trmm_workspace(m, n) bytes (the product is formed out of place).
  * lrc_trsm: B <- op(L)^{-1} B (side 0) or B <- B op(L)^{-1} (side 1), same conventions, in
  *   place; workspace of lrc_trsm_workspace(side, m, n) bytes holds the inverted 64x64
- *   diagonal blocks of L.  A zero or non-finite diagonal of L gives non-finite results.
+ *   diagonal blocks of L and, when one 64-wide block of B spans at least 8192 columns
+ *   (side 0) or rows (side 1), up to 8 partial products of a block update.  A zero or
+ *   non-finite diagonal of L gives non-finite results.
  * lrc_sym_to_f64: A (n x n, both triangles) = scale * C, C fp32 with its upper triangle read
  *   (the layout lrc_cov_accumulate writes).
  * lrc_to_f64: Y (rows x cols) = scale * X, X of dtype t (LRC_BF16, LRC_F32 or LRC_F64).

@@ -137,8 +137,9 @@ def test_trsm_parity(lrc, side, trans, scaled):
 @pytest.mark.parametrize("side,trans", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_trsm_wide_parity(lrc, side, trans):
     """B with at least 128 tiles of 64 across one block (8200 wide): the solve takes the
-    left-looking order (one product per block with every block solved before it)."""
-    m, n = (200, 8200) if side == 0 else (8200, 200)
+    left-looking order (one product per block with every block solved before it, its k range split
+    in up to 4 parts here, 1088 deep at the last block)."""
+    m, n = (1100, 8200) if side == 0 else (8200, 1100)
     dim = m if side == 0 else n
     _say("trsm wide side=%d trans=%d m=%d n=%d" % (side, trans, m, n))
     L, Lnan = _lower_with_nan_upper(dim, 70 + 2 * side + trans, False)
