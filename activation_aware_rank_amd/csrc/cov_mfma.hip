@@ -43,9 +43,6 @@ constexpr int64_t MFMA_CHUNK = 32768;    // tokens per internal chunk
 #ifndef SYRK_FE
 #define SYRK_FE 4  // 16-token k slices per flush of the SYRK's MFMA chains
 #endif
-#ifndef SYRK_WPE
-#define SYRK_WPE 1  // SYRK waves per SIMD (resident blocks per CU)
-#endif
 #ifndef SYRK_DEPTH
 #define SYRK_DEPTH 2
 #endif
@@ -282,13 +279,16 @@ __device__ __forceinline__ void mfma_mainloop(
 // Rows past rows[o] read zero through an offset of 2^31, past every operand's resource.
 // FE 4: the MFMA chains restart every 64 tokens (two steps) and are added to acc with one
 // round-to-nearest fp32 add, as in mfma_mainloop.
+// NST 2: two stages and loads one step ahead, for kernels that share a CU two at a time (the other
+// workgroup's MFMAs run while one waits); each wave then also waits for its own LDS reads of the
+// stage the next loads overwrite before the barrier.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // s_waitcnt with vmcnt = n (0..63) and no wait on the other counters (gfx9 encoding)
 #define LRC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-template <int BM, int BN, int NOPS, int NPROD>
+template <int BM, int BN, int NOPS, int NPROD, int NST>
 __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, const int64_t D, const int *rows,
                                                   int64_t klen, const int64_t *nrec,
                                                   f32x16_t (&acc)[MfmaCfg<BM, BN, 256, 2>::TM][MfmaCfg<BM, BN, 256, 2>::TN],
@@ -355,9 +355,18 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
     // loads of step kt + 2 into `nxt`, then the MFMAs from `cur`; PAR: position in the flush group
     auto step = [&](int kt, const bf16_t *cur, bf16_t *nxt, auto par) {
         constexpr int PAR = decltype(par)::value;
-        LRC_WAIT_VMCNT(LPS);
-        lds_barrier();
-        issue(kt + 2, nxt);
+        if constexpr (NST == 3) {
+            LRC_WAIT_VMCNT(LPS);
+            lds_barrier();
+            issue(kt + 2, nxt);
+        } else {
+            // two stages: this wave's loads of step kt and its LDS reads of step kt - 1 (from the
+            // stage the loads of step kt + 1 overwrite) complete before the barrier
+            LRC_WAIT_VMCNT(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_barrier();
+            issue(kt + 1, nxt);
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int c = ks * 2 + (lane >> 5);
@@ -387,7 +396,7 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
                 }
         }
         if (PAR == 1) flush();
-        if constexpr (NPROD == 3 && LPS == 12 && NA * (TM + TN) == 12 && TM * TN * NPROD == 24) {
+        if constexpr (NST == 3 && NPROD == 3 && LPS == 12 && NA * (TM + TN) == 12 && TM * TN * NPROD == 24) {
             // 256 x 128 split tile: spread the step's 12 loads over the first slice's 24 MFMAs, with
             // the second slice's 12 LDS reads between them, instead of issuing the loads in one
             // burst after the barrier (7 % faster at d_out 11008, 3 % at 4096)
@@ -400,9 +409,37 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);  // MFMAs of the second slice
         }
+        if constexpr (NST == 2 && NPROD == 3 && LPS == 8 && NA * (TM + TN) == 8 && TM * TN * NPROD == 12) {
+            // 128 x 128 split tile, two stages: the same, 8 loads over 12 MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads of the first slice
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // loads into LDS
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads of the second slice
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);  // MFMAs of the second slice
+        }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    if constexpr (NST == 2) {
+        // stages 0 1 0 1 ..., flush-group positions 0 1 0 1 ...
+        issue(0, lds0);
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            step(kt, lds0, lds1, I0{});
+            step(kt + 1, lds1, lds0, I1{});
+        }
+        if (kt < nk) {
+            step(kt, lds0, lds1, I0{});
+            flush();  // the last flush group had only its first step
+        }
+        // the loads issued past the last step still write LDS: let them land before the epilogue
+        LRC_WAIT_VMCNT(0);
+        lds_barrier();
+        return;
+    }
     issue(0, lds0);
     issue(1, lds1);
     // six steps per iteration: stages 0 1 2 0 1 2, flush-group positions 0 1 0 1 0 1
@@ -534,8 +571,9 @@ struct SyrkCfg {  // 4 waves of (BM/2) x (BN/2)
 };
 // SPLIT: Y^T as fp16 hi/lo with the row exponents ex, three products (the diagonal's sum of lo^2
 // is added by k_lo_sq_add); else Y^T = X^T in bf16, one product.
-template <int BM, int BN, bool SPLIT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SYRK_WPE, SYRK_WPE)))
+// NST: LDS stages of the main loop; 2 lets two workgroups share a CU (65536 bytes of LDS each).
+template <int BM, int BN, bool SPLIT, int NST>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NST == 2 ? 2 : 1, NST == 2 ? 2 : 1)))
 k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, const int32_t *__restrict__ ex,
            int64_t ldy, int64_t ktot, int64_t kchunk, int64_t hd, float *__restrict__ C, int64_t ldc,
            float *__restrict__ P, int32_t n_blocks) {
@@ -546,7 +584,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, const
     constexpr int STAGE = (NOPS / 2) * (BM + BN) * MK;  // elements of one LDS stage
     __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE];
     __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
-    __shared__ __attribute__((aligned(16))) bf16_t lds2[STAGE];
+    __shared__ __attribute__((aligned(16))) bf16_t lds2[NST == 3 ? STAGE : 8];
     const int u = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     int I, J;
     if constexpr (BM == BN) {  // column J holds J + 1 tiles: closed form
@@ -597,7 +635,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, const
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
     // klen is a multiple of MK here, so no k check is needed
-    syrk_dma_mainloop<BM, BN, NOPS, SPLIT ? 3 : 1>(base, D, rows, klen, nrec, acc, lds0, lds1, lds2);
+    syrk_dma_mainloop<BM, BN, NOPS, SPLIT ? 3 : 1, NST>(base, D, rows, klen, nrec, acc, lds0, lds1, lds2);
     float *dst;
     int64_t ldd;
     if (s == 0) {
@@ -768,26 +806,30 @@ __global__ void k_add_partials(float *__restrict__ C, int64_t ldc, const float *
 // ---------------------------------------------------------------------------------------------
 struct MfmaPlan {
     bool wide;      // SYRK block tile 256 x 128 (4 waves of 128 x 64); else 128 x 128 (64 x 64)
+    bool pair;      // SYRK with two LDS stages, two workgroups per CU (the split path's 128 x 128)
     int64_t tcmax;  // tokens per chunk
     int64_t ldy;    // leading dim of Y^T (multiple of 256)
     int nsplit;     // token splits of the SYRK
     int64_t n_upper;  // SYRK tiles per head block
 };
 
-static MfmaPlan plan(int64_t n_tok, int64_t d_out, int32_t n_blocks) {
+static MfmaPlan plan(int64_t n_tok, int64_t d_out, int32_t n_blocks, bool has_w) {
     MfmaPlan p;
     const int64_t hd = d_out / n_blocks;
-    // the wide tile moves a quarter less LDS and L2 data per MFMA; below 256 rows it would be
-    // half empty
-    p.wide = hd >= 256;
+    // The split path (fp16 hi and lo, three products) runs 128 x 128 tiles with two LDS stages, two
+    // workgroups to a CU: 21 % faster than one 256 x 128 workgroup with three stages at d_out
+    // 4096, 1-4 % at 11008.  The one-product path keeps the wide tile, which moves a quarter less
+    // LDS and L2 data per MFMA (below 256 rows it would be half empty).
+    p.pair = has_w;
+    p.wide = !has_w && hd >= 256;
     p.tcmax = std::min<int64_t>(MFMA_CHUNK, n_tok);
     p.ldy = (p.tcmax + 255) / 256 * 256;
     p.n_upper = p.wide ? syrk_tiles<256, 128>(int(hd)) : syrk_tiles<128, 128>(int(hd));
     const int64_t tiles = p.n_upper * n_blocks;
-    // smallest split count that fills >= 90% of the last wave of 256 CUs x SYRK_WPE resident
-    // blocks, while keeping at least 8 k-steps per split
+    // smallest split count that fills >= 90% of the last wave of 256 CUs x the resident blocks
+    // per CU, while keeping at least 8 k-steps per split
     const int64_t ksteps = p.ldy / MK;
-    const int64_t slots = 256 * SYRK_WPE;
+    const int64_t slots = 256 * (p.pair ? 2 : 1);
     p.nsplit = 1;
     for (int s = 1; s <= 16; ++s) {
         if (s > 1 && ksteps / s < 8) break;
@@ -816,7 +858,7 @@ bool cov_mfma_supported(lrc_dtype x_t, const void *X, int64_t ldx, const void *W
 }
 
 size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks) {
-    const MfmaPlan p = plan(n_tok, d_out, n_blocks);
+    const MfmaPlan p = plan(n_tok, d_out, n_blocks, has_w != 0);
     const int64_t hd = d_out / n_blocks;
     Counter c;
     if (has_w) c.carve<bf16_t>(size_t(d_out) * size_t(d_in));
@@ -834,7 +876,7 @@ size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out,
 }
 
 lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
-    const MfmaPlan p = plan(a.n_tok, a.d_out, a.n_blocks);
+    const MfmaPlan p = plan(a.n_tok, a.d_out, a.n_blocks, a.W != nullptr);
     const int64_t hd = a.d_out / a.n_blocks;
     const bool has_w = a.W != nullptr;
     Carver cv(ws, ws_bytes);
@@ -888,18 +930,15 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         dim3 g(unsigned(p.n_upper), unsigned(a.n_blocks), unsigned(p.nsplit));
         // algorithmic flops of the launch: the upper triangle (incl. diagonal) of each head block
         const double fl = double(tc) * double(hd) * double(hd + 1) * double(a.n_blocks);
-        if (has_w && p.wide)
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, true>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy, ktot,
-                             kchunk, hd, a.C, a.ldc, P, a.n_blocks);
-        else if (has_w)
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, true>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy, ktot,
-                             kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+        if (p.pair)
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, true, 2>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy,
+                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         else if (p.wide)
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, false>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy, ktot,
-                             kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, false, 3>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy,
+                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         else
-            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, false>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy, ktot,
-                             kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+            LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, false, 3>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy,
+                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
         LRC_LAUNCH_CHECK("k_cov_syrk");
         if (has_w) {
             hipLaunchKernelGGL(k_lo_sq, dim3(unsigned(cdiv(a.d_out, 64)), LOSQ_SEG), dim3(256), 0, s, Ylo, a.d_out,
