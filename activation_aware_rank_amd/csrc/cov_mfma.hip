@@ -576,7 +576,7 @@ template <int BM, int BN, bool SPLIT, int NST>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NST == 2 ? 2 : 1, NST == 2 ? 2 : 1)))
 k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, const int32_t *__restrict__ ex,
            int64_t ldy, int64_t ktot, int64_t kchunk, int64_t hd, float *__restrict__ C, int64_t ldc,
-           float *__restrict__ P, int32_t n_blocks) {
+           float *__restrict__ P, int32_t n_blocks, int32_t xcd_order) {
     constexpr int THREADS = SyrkCfg<BM, BN>::THREADS, WGM = SyrkCfg<BM, BN>::WGM;
     static_assert(THREADS == 256, "launch bounds");
     using Cfg = MfmaCfg<BM, BN, THREADS, WGM>;
@@ -585,9 +585,51 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, const
     __shared__ __attribute__((aligned(16))) bf16_t lds0[STAGE];
     __shared__ __attribute__((aligned(16))) bf16_t lds1[STAGE];
     __shared__ __attribute__((aligned(16))) bf16_t lds2[NST == 3 ? STAGE : 8];
-    const int u = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    int u = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     int I, J;
-    if constexpr (BM == BN) {  // column J holds J + 1 tiles: closed form
+    if (BM == BN && xcd_order) {
+        // Workgroups go to the 8 XCDs in turn (linear id mod 8), each with an L2 of its own: XCD x
+        // takes a contiguous share of the (tile, head block, split) order, and tiles are ordered in
+        // super-tiles of 8 x 8, so the ~64 workgroups an XCD runs at once share 16 panels of Y^T
+        // (d_out 11008: 12.55 -> 11.96 ms per chunk; at 4096, 528 tiles in 7 token splits, 4 %
+        // slower, so the host asks for it only with many tiles per split).
+        const int64_t G = int64_t(gridDim.x) * gridDim.y * gridDim.z;
+        const int64_t g = blockIdx.x + int64_t(gridDim.x) * (blockIdx.y + int64_t(gridDim.y) * blockIdx.z);
+        const int64_t x = g % 8, slot = g / 8, per = G / 8, extra = G % 8;
+        const int64_t L = x * per + (x < extra ? x : extra) + slot;
+        u = int(L % gridDim.x);
+        h = int((L / gridDim.x) % gridDim.y);
+        s = int(L / (int64_t(gridDim.x) * gridDim.y));
+        // tile u: super-tile column block jb (columns 8 jb ..), super-tile row block ib, then column
+        // by column inside the super-tile; column j holds min(nI, j + 1) tiles
+        const int nI = int((hd + BM - 1) / BM), nJ = nI;
+        constexpr int SI = 8, SJ = 8;
+        int rem = u, jb = 0;
+        for (;; ++jb) {
+            int cnt = 0;
+            for (int j = jb * SJ; j < min(nJ, jb * SJ + SJ); ++j) cnt += min(nI, j + 1);
+            if (rem < cnt || jb * SJ + SJ >= nJ) break;
+            rem -= cnt;
+        }
+        int ib = 0;
+        for (;; ++ib) {
+            int cnt = 0;
+            for (int j = jb * SJ; j < min(nJ, jb * SJ + SJ); ++j) cnt += max(0, min(min(nI, j + 1), ib * SI + SI) - ib * SI);
+            if (rem < cnt || ib * SI + SI >= nI) break;
+            rem -= cnt;
+        }
+        J = jb * SJ;
+        I = ib * SI;
+        for (int j = jb * SJ; j < min(nJ, jb * SJ + SJ); ++j) {
+            const int nj = max(0, min(min(nI, j + 1), ib * SI + SI) - ib * SI);
+            if (rem < nj) {
+                J = j;
+                I = ib * SI + rem;
+                break;
+            }
+            rem -= nj;
+        }
+    } else if constexpr (BM == BN) {  // column J holds J + 1 tiles: closed form
         J = int((sqrtf(8.f * float(u) + 1.f) - 1.f) * 0.5f);
         while (J * (J + 1) / 2 > u) --J;
         while ((J + 1) * (J + 2) / 2 <= u) ++J;
@@ -930,15 +972,17 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         dim3 g(unsigned(p.n_upper), unsigned(a.n_blocks), unsigned(p.nsplit));
         // algorithmic flops of the launch: the upper triangle (incl. diagonal) of each head block
         const double fl = double(tc) * double(hd) * double(hd + 1) * double(a.n_blocks);
+        // the per-XCD order with at least 2048 tiles per token split (d_out 11008: 3741; 4096: 528)
+        const int32_t xo = p.pair && p.n_upper * a.n_blocks >= 2048 ? 1 : 0;
         if (p.pair)
             LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, true, 2>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy,
-                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks, xo);
         else if (p.wide)
             LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<256, 128, false, 3>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy,
-                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks, 0);
         else
             LRC_TIMED_LAUNCH("k_cov_syrk", fl, (k_cov_syrk<128, 128, false, 3>), g, dim3(256), 0, s, Yhi, Ylo, ex, p.ldy,
-                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks);
+                             ktot, kchunk, hd, a.C, a.ldc, P, a.n_blocks, 0);
         LRC_LAUNCH_CHECK("k_cov_syrk");
         if (has_w) {
             hipLaunchKernelGGL(k_lo_sq, dim3(unsigned(cdiv(a.d_out, 64)), LOSQ_SEG), dim3(256), 0, s, Ylo, a.d_out,

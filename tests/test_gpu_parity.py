@@ -109,6 +109,23 @@ def test_cov_split_scaled_columns(lrc, sx, sw):
         assert np.all(C[j, j:] == 0) and np.all(C[:j, j] == 0)
 
 
+def test_cov_many_tiles_xcd_order(lrc):
+    """d_out 8320: 65 block rows of 128, 2145 upper tiles per token split, enough for the per-XCD
+    super-tile order (a ragged last super-tile row and column: 65 = 8 x 8 + 1)."""
+    _say("cov bf16 300 x 136 -> 8320")
+    X = inputs.block_activations(136, 300)
+    W = inputs.weight(136, 8320, "bf16", inputs.CFG_BLOCK, 0, 3)
+    C = host(_cov_gpu(lrc, X, "bf16", W))
+    Cr = oracle.covariance(X, "bf16", W, "bf16")
+    dg = np.diag(Cr)
+    scale = np.sqrt(np.outer(dg, dg))
+    U = np.triu(np.ones(Cr.shape, dtype=bool))
+    rel = np.max(np.abs(C - Cr)[U] / scale[U])
+    print("max |dC_ij| / sqrt(C_ii C_jj) = %.3e" % rel)
+    assert rel <= 1e-5
+    assert np.all(np.tril(C, -1) == 0)
+
+
 def test_cov_identity_weight(lrc):
     _say("cov bf16 W = I, 3000 x 264")
     X = inputs.block_activations(264, 3000)
