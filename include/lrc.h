@@ -146,7 +146,7 @@ lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64
  *    n <= 128: one-sided Jacobi, one matrix per workgroup held in LDS, in prec.
  *    n > 128: Householder tridiagonalisation and back-transformation in prec; the
  *    tridiagonal eigenproblem (bisection, inverse iteration) always in fp64.
- * Batches with n > 128: up to four members are decomposed at once, each on a helper
+ * Batches with n > 128: up to eight members are decomposed at once, each on a helper
  *    stream of the library's (default priority, created per device on first use and kept
  *    until the process ends) with a workspace of its own, fed by a host thread of its
  *    own; the call returns once every launch is enqueued (without waiting for the GPU)
@@ -174,7 +174,7 @@ lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64
  *    groups use the working precision prec.  Groups must not overlap in lambda, V, info.
  * Groups with n <= 128 run first, one Jacobi launch each, on `stream`; every member of
  *    the groups with n > 128 is then decomposed on the helper streams described under
- *    lrc_eigh, up to four at once, largest n first.  `stream` waits for all of them.
+ *    lrc_eigh, up to eight at once, largest n first.  `stream` waits for all of them.
  *    Each member's result equals that of a call on the member alone, bit for bit.
  * Range basis (optional, per group; Swift-SVD page, section 2-ga: C = Y^T Y with Y = X W):
  *    W != NULL states that each member's C is (X W)^T (X W) for some X, with W (d_in x n,

@@ -128,14 +128,15 @@ def test_workspace_queries_are_consistent():
     assert 0 < a < b
     assert lrc.lrc_eigh_workspace(4096, 1, 1228, 1) > lrc.lrc_eigh_workspace(4096, 1, 0, 1)
     assert lrc.lrc_eigh_workspace(128, 32, 32, 2) == 0  # Jacobi keeps everything in LDS
-    # batched members run up to four at a time, each with a region of its own
+    # batched members run up to eight at a time, each with a region of its own
     one = lrc.lrc_eigh_workspace(4096, 1, 1228, 1)
     assert lrc.lrc_eigh_workspace(4096, 3, 1228, 1) == 3 * one
-    assert lrc.lrc_eigh_workspace(4096, 9, 1228, 1) == 4 * one
+    assert lrc.lrc_eigh_workspace(4096, 9, 1228, 1) == 8 * one
     # several groups: as many regions as concurrent members, each sized for the largest group
     assert lrc.lrc_eigh_multi_workspace([(4096, 3, 1228)], 1) == 3 * one
     big = lrc.lrc_eigh_workspace(11008, 1, 1791, 1)
-    assert lrc.lrc_eigh_multi_workspace([(4096, 5, 1228), (11008, 2, 1791), (128, 32, 32)], 1) == 4 * big
+    assert lrc.lrc_eigh_multi_workspace([(4096, 5, 1228), (11008, 2, 1791), (128, 32, 32)], 1) == 7 * big
+    assert lrc.lrc_eigh_multi_workspace([(4096, 8, 1228), (11008, 2, 1791)], 1) == 8 * big
     # the largest n and the largest n_vec may come from different groups
     assert lrc.lrc_eigh_multi_workspace([(4096, 1, 1791), (11008, 1, 1228)], 1) == 2 * big
     assert lrc.lrc_eigh_multi_workspace([(64, 4, 8)], 2) == 0
@@ -144,7 +145,7 @@ def test_workspace_queries_are_consistent():
     # and d_in x n fp64 products, and the decomposition of the d_in x d_in matrix; otherwise ignored
     rng = lrc.lrc_eigh_multi_workspace([(11008, 2, 1791, 4096)], 1)
     assert rng > 2 * 8 * 11008 * 11008 and rng != 2 * big
-    assert lrc.lrc_eigh_multi_workspace([(11008, 2, 1791, 4096), (4096, 5, 1228)], 1) == 4 * (rng // 2)
+    assert lrc.lrc_eigh_multi_workspace([(11008, 2, 1791, 4096), (4096, 5, 1228)], 1) == 7 * (rng // 2)
     assert lrc.lrc_eigh_multi_workspace([(11008, 1, 1791, 12000)], 1) == big
     assert lrc.lrc_eigh_multi_workspace([(11008, 1, 1791, 100)], 1) == big
     assert lrc.lrc_eigh_multi_workspace([(4096, 1, 1791, 1228)], 1) == lrc.lrc_eigh_workspace(4096, 1, 1791, 1)
