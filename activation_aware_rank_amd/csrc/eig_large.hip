@@ -1554,12 +1554,36 @@ static bool use_range(const EighArgs &a) { return a.W && a.d_in > 128 && a.d_in 
 // took 297 ms against 358 ms four at a time (six at a time: 356 ms).
 constexpr int EIG_LANES = 8;
 
+// Calls may run at once from several host threads (for instance one per group of matrices whose
+// covariances are ready): each call takes its lanes from a rotating base, so calls that together
+// have at most EIG_LANES members use different streams, and its own events from a pool.
 struct EigLanes {
     hipStream_t st[EIG_LANES];
-    hipEvent_t start, done[EIG_LANES];
-    std::mutex busy;  // held while one call enqueues, so the shared events are not re-recorded under it
+    std::atomic<unsigned> base{0};  // first lane of the next call
+    std::mutex pool_mu;
+    std::vector<hipEvent_t> pool;  // events not in use by a call (never destroyed)
     bool ok = false;
 };
+
+static lrc_status take_events(EigLanes *L, int n, hipEvent_t *out) {
+    std::lock_guard<std::mutex> lk(L->pool_mu);
+    for (int i = 0; i < n; ++i) {
+        if (L->pool.empty()) {
+            hipEvent_t e;
+            LRC_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+            L->pool.push_back(e);
+        }
+        out[i] = L->pool.back();
+        L->pool.pop_back();
+    }
+    return LRC_OK;
+}
+
+// events go back once the waits on them are enqueued: a later record does not affect them
+static void give_events(EigLanes *L, int n, const hipEvent_t *ev) {
+    std::lock_guard<std::mutex> lk(L->pool_mu);
+    for (int i = 0; i < n; ++i) L->pool.push_back(ev[i]);
+}
 
 static lrc_status eig_lanes(EigLanes **out) {
     static std::mutex mu;
@@ -1569,11 +1593,7 @@ static lrc_status eig_lanes(EigLanes **out) {
     std::lock_guard<std::mutex> lk(mu);
     EigLanes &L = lanes[devid];
     if (!L.ok) {
-        for (int i = 0; i < EIG_LANES; ++i) {
-            LRC_HIP(hipStreamCreateWithFlags(&L.st[i], hipStreamNonBlocking));
-            LRC_HIP(hipEventCreateWithFlags(&L.done[i], hipEventDisableTiming));
-        }
-        LRC_HIP(hipEventCreateWithFlags(&L.start, hipEventDisableTiming));
+        for (int i = 0; i < EIG_LANES; ++i) LRC_HIP(hipStreamCreateWithFlags(&L.st[i], hipStreamNonBlocking));
         L.ok = true;
     }
     *out = &L;
@@ -1732,11 +1752,24 @@ static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, c
     EigLanes *L = nullptr;
     lrc_status st0 = eig_lanes(&L);
     if (st0 != LRC_OK) return st0;
-    std::lock_guard<std::mutex> hold(L->busy);
     int dev = 0;
     LRC_HIP(hipGetDevice(&dev));
-    LRC_HIP(hipEventRecord(L->start, s));
-    for (int l = 0; l < lanes; ++l) LRC_HIP(hipStreamWaitEvent(L->st[l], L->start, 0));
+    hipEvent_t ev[EIG_LANES + 1];  // ev[0]: start on s; ev[1 + l]: lane l done
+    st0 = take_events(L, lanes + 1, ev);
+    if (st0 != LRC_OK) return st0;
+    const unsigned base = L->base.fetch_add(unsigned(lanes));
+    hipStream_t ls[EIG_LANES];
+    for (int l = 0; l < lanes; ++l) ls[l] = L->st[(base + unsigned(l)) % EIG_LANES];
+    auto enqueue_start = [&]() -> lrc_status {
+        LRC_HIP(hipEventRecord(ev[0], s));
+        for (int l = 0; l < lanes; ++l) LRC_HIP(hipStreamWaitEvent(ls[l], ev[0], 0));
+        return LRC_OK;
+    };
+    st0 = enqueue_start();
+    if (st0 != LRC_OK) {
+        give_events(L, lanes + 1, ev);
+        return st0;
+    }
     std::atomic<size_t> next{0};
     std::atomic<bool> stop{false};
     lrc_status st[EIG_LANES];
@@ -1749,8 +1782,8 @@ static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, c
             const size_t i = next.fetch_add(1);
             if (i >= mem.size()) break;
             char *lws = ws + p.per * size_t(l);
-            st[l] = mem[i].W ? run_member_range<T>(mem[i], p, lws, L->st[l], w[l])
-                             : run_member<T>(mem[i], p, lws, L->st[l], w[l]);
+            st[l] = mem[i].W ? run_member_range<T>(mem[i], p, lws, ls[l], w[l])
+                             : run_member<T>(mem[i], p, lws, ls[l], w[l]);
         }
         if (st[l] != LRC_OK) {
             msg[l] = lrc_last_error();
@@ -1769,16 +1802,23 @@ static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, c
         } catch (...) {
             stop.store(true);
             for (auto &t : th) t.join();
+            give_events(L, lanes + 1, ev);
             return fail(LRC_ERR_HIP, "could not start the eigh lane threads");
         }
     }
     lane(0);
     for (auto &t : th) t.join();
     for (int l = threaded ? lanes : 1; l < lanes; ++l) st[l] = LRC_OK;
-    for (int l = 0; l < lanes; ++l) {
-        LRC_HIP(hipEventRecord(L->done[l], L->st[l]));
-        LRC_HIP(hipStreamWaitEvent(s, L->done[l], 0));
-    }
+    auto enqueue_done = [&]() -> lrc_status {
+        for (int l = 0; l < lanes; ++l) {
+            LRC_HIP(hipEventRecord(ev[1 + l], ls[l]));
+            LRC_HIP(hipStreamWaitEvent(s, ev[1 + l], 0));
+        }
+        return LRC_OK;
+    };
+    const lrc_status sd = enqueue_done();
+    give_events(L, lanes + 1, ev);
+    if (sd != LRC_OK) return sd;
     for (int l = 0; l < lanes; ++l)
         if (st[l] != LRC_OK) return fail(st[l], msg[l]);
     return LRC_OK;

@@ -19,6 +19,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -135,6 +136,12 @@ def main():
     ap.add_argument("--curvature-prec", choices=("f32", "f64"), default="f64")
     ap.add_argument("--layer-runs", type=int, default=2,
                     help="runs of one 4096x4096 layer on its own after the timed steps (0: skip)")
+    ap.add_argument("--overlap", choices=("on", "off"), default="on",
+                    help="decompose each group of matrices (grouped by output width and rank) as soon as its "
+                         "covariances are done, on a side stream from a host thread of its own, while the "
+                         "remaining covariances run")
+    ap.add_argument("--overlap-order", choices=("large-first", "most-first"), default="large-first",
+                    help="group order: largest n first, or the group with the most matrices first")
     ap.add_argument("--eig-range", choices=("on", "off"), default="on",
                     help="on: covariances of Y = X W with d_in < d_out (gate/up) are decomposed through a basis of "
                          "range(W^T) (their rank is at most d_in); off: the full decomposition of every covariance")
@@ -196,6 +203,14 @@ def main():
         dtype=torch.uint8, device=dev)
     eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g], gW.get(g)) for g in groups]
     gkey = "+".join("%dx%d_k%d" % (len(ms), g[0], g[1]) for g, ms in groups.items())
+    # overlap: covariances group by group, largest n first; each group's eigendecompositions and
+    # error curves on a side stream of its own (default priority) with a workspace of its own
+    g_order = sorted(groups, key=lambda g: -g[0] if a.overlap_order == "large-first" else len(groups[g]) * -1)
+    side = {g: torch.cuda.Stream(device=dev) for g in groups}
+    ws_eig_g = {g: torch.empty(lrc.lrc_eigh_multi_workspace(
+        [(g[0], len(groups[g]), g[1], sh[groups[g][0]][0] if g in gW else 0)], prec), dtype=torch.uint8, device=dev)
+        for g in groups} if a.overlap == "on" else {}
+    gname = {g: "%dx%d_k%d" % (len(groups[g]), g[0], g[1]) for g in groups}
     kcap = {m: (di * do) // (di + do) for m, (di, do) in sh.items()}
     offs_h = [0] + list(np.cumsum([kcap[m] for m in MATS]))
     offs = torch.tensor(offs_h, dtype=torch.int64, device=dev)
@@ -216,23 +231,49 @@ def main():
         e.record(st)
         return e
 
-    def step(times):
-        for i, m in enumerate(MATS):
-            xin = Xd if m == "down_proj" else X
-            C[m].zero_()
-            e0 = ev(stream)
-            lrc.lrc_cov_accumulate(xin, W[m], C[m], info=info[i:i + 1], ws=ws_cov)
-            e1 = ev(stream)
-            times.append((m + ".cov", e0, e1))
-        # every eigendecomposition of the block in one call: the library runs up to four at once
+    def cov(m, times):
+        i = MATS.index(m)
+        xin = Xd if m == "down_proj" else X
+        C[m].zero_()
         e0 = ev(stream)
-        lrc.lrc_eigh_multi(eig_groups, prec=prec, ws=ws_eig)
+        lrc.lrc_cov_accumulate(xin, W[m], C[m], info=info[i:i + 1], ws=ws_cov)
         e1 = ev(stream)
-        for g in groups:
-            lrc.lrc_error_curve(glam[g], eps=geps[g])
-        e2 = ev(stream)
-        times.append(("eigh." + gkey, e0, e1))
-        times.append(("err." + gkey, e1, e2))
+        times.append((m + ".cov", e0, e1))
+
+    def eig_group(g, ready, times):
+        # runs on a host thread of its own: the library call returns once its launches are
+        # enqueued, which takes about as long as they run
+        sg = side[g]
+        sg.wait_event(ready)
+        e0 = ev(sg)
+        lrc.lrc_eigh_multi([eig_groups[list(groups).index(g)]], prec=prec, ws=ws_eig_g[g], stream=sg)
+        lrc.lrc_error_curve(glam[g], eps=geps[g], stream=sg)
+        e1 = ev(sg)
+        times.append(("eigh." + gname[g], e0, e1))
+
+    def step(times):
+        if a.overlap == "on":
+            threads = []
+            for g in g_order:
+                for m in groups[g]:
+                    cov(m, times)
+                t = threading.Thread(target=eig_group, args=(g, ev(stream), times))
+                t.start()
+                threads.append(t)
+            for t in threads:
+                t.join()
+            for g in groups:
+                stream.wait_stream(side[g])
+        else:
+            for m in MATS:
+                cov(m, times)
+            # every eigendecomposition of the block in one call: the library runs up to eight at once
+            e0 = ev(stream)
+            lrc.lrc_eigh_multi(eig_groups, prec=prec, ws=ws_eig)
+            for g in groups:
+                lrc.lrc_error_curve(glam[g], eps=geps[g])
+            e1 = ev(stream)
+            times.append(("eigh." + gkey, e0, e1))
         for m in MATS:
             e0 = ev(stream)
             lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m])
@@ -315,7 +356,7 @@ def main():
     # factors
     n3 = {m: float(sh[m][0] if where[m][0] in gW else sh[m][1]) ** 3 for m in MATS}
     share = n3["q_proj"] / sum(n3.values())
-    layer_s = (avg["q_proj.cov"] + (avg["eigh." + gkey] + avg["err." + gkey]) * share + avg["q_proj.fac"]) / 1000.0
+    layer_s = (avg["q_proj.cov"] + eig_ms * share + avg["q_proj.fac"]) / 1000.0
     if a.breakdown:
         for k in sorted(avg):
             print("%-20s %10.3f ms" % (k, avg[k]), file=sys.stderr)
@@ -348,12 +389,16 @@ def main():
         r["sampled"] = "every launch in the timed steps (start/stop events recorded by the dispatch)"
     roof_symv["sampled"] = ("every %d-th launch in the timed steps (start/stop events recorded by the dispatch)"
                             % a.timing_stride)
-    roof_symv["overlap"] = ("launches on up to four helper streams overlap (several eigendecompositions at once): "
-                            "a launch's event-timed duration includes time its workgroups wait for CUs held by the "
-                            "other streams' kernels, and summed durations exceed the eigendecomposition stage's "
-                            "wall time")
-    # the roofline entry is the covariance SYRK: the kernel with the largest time among those that
-    # run alone (the covariance stage is serial), so its event-timed duration is its execution time
+    roof_symv["overlap"] = ("launches on up to eight helper streams overlap (several eigendecompositions at once, "
+                            "and with --overlap on the covariance kernels of later groups): a launch's event-timed "
+                            "duration includes time its workgroups wait for CUs held by the other streams' kernels, "
+                            "and summed durations exceed the eigendecomposition stage's wall time")
+    if a.overlap == "on":
+        for r in (roof_syrk, roof_gemm):
+            r["overlap"] = ("the eigendecompositions of earlier groups run on side streams during later groups' "
+                            "covariances: a launch's event-timed duration includes time its workgroups wait for "
+                            "CUs held by those kernels (--overlap off times the covariance alone)")
+    # the roofline entry is the covariance SYRK: the kernel with the largest time
     roof = roof_syrk
     out = {
         "metric": "calibration tokens/s into Y^T Y; sec per 4096x4096 layer compressed (eig incl.)",
@@ -378,6 +423,11 @@ def main():
                                             "through a range basis)" % (share, gkey),
         "cov_tokens_per_s": a.tokens / (cov_ms / 1000.0),
         "cov_ms": cov_ms, "eigh_ms": eig_ms,
+        "overlap": a.overlap,
+        "overlap_note": (("covariances group by group (%s), each group's eigendecompositions and error curves "
+                          "on a side stream as soon as its covariances are done: cov_ms and eigh_ms are summed "
+                          "call times that overlap in the step" % ", ".join(gname[g] for g in g_order))
+                         if a.overlap == "on" else "covariances, then one call for every eigendecomposition"),
         "breakdown_ms": {k: round(v, 3) for k, v in avg.items()},
         "roofline": roof,
         "rooflines": {"k_cov_syrk": roof_syrk, "k_trd_symv": roof_symv, "k_cov_gemm_y": roof_gemm},

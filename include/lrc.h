@@ -152,6 +152,9 @@ lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64
  *    own; the call returns once every launch is enqueued (without waiting for the GPU)
  *    and the caller's stream waits for every member, so results are ordered on `stream`
  *    as for any other call.  Each member's result does not depend on the batch it is in.
+ *    Calls may run at once from several host threads (each with its own workspace and
+ *    stream): each call takes its helper streams from a rotating base, so calls that
+ *    together hold at most eight members do not queue behind one another.
  *    With the environment variable LRC_EIGH_HOST_THREADS=0 the calling thread enqueues
  *    all members itself, on one helper stream (for tools that cannot follow launches
  *    from several host threads); results are the same.
