@@ -312,6 +312,53 @@ def test_eigh_multi_matches_single_calls(lrc, prec):
         assert np.array_equal(host(V1), host(V))
 
 
+def test_eigh_multi_concurrent_calls(lrc):
+    """Three lrc_eigh_multi calls at once from three host threads, each on its own stream with its own
+    workspace (the calls take different helper streams: 3 + 2 + 1 members fit the eight): every member
+    must equal the same matrix decomposed alone, bit for bit."""
+    import threading
+    _say("eigh multi: three concurrent calls (3 x 300, 2 x 260, 1 x 513)")
+    X = inputs.block_activations(320, 4096)
+    spec = [(300, 3, 40), (260, 2, 24), (513, 1, 10)]
+    mats, Cd = [], []
+    for gi, (n, b, nv) in enumerate(spec):
+        Cs = [oracle.covariance(X, "bf16", inputs.weight(320, n, "bf16", inputs.CFG_BLOCK, 0, 60 + 4 * gi + m),
+                                "bf16").astype(np.float32) for m in range(b)]
+        mats.append(Cs)
+        Cd.append(dev(np.stack(Cs), "f32"))
+    streams = [torch.cuda.Stream() for _ in spec]
+    wss = [torch.empty(lrc.lrc_eigh_multi_workspace([(n, b, nv)], 1), dtype=torch.uint8, device="cuda")
+           for n, b, nv in spec]
+    # outputs allocated (and info zeroed) here, before the threads, so no call orders against another stream
+    outs = [(torch.empty(b, n, dtype=torch.float64, device="cuda"), torch.empty(b, n, nv, dtype=torch.float32,
+             device="cuda"), torch.zeros(b, dtype=torch.int32, device="cuda")) for n, b, nv in spec]
+    torch.cuda.synchronize()
+    out, errs = [None] * len(spec), []
+
+    def run(i):
+        try:
+            n, b, nv = spec[i]
+            lrc.lrc_eigh_multi([(Cd[i], nv) + outs[i]], prec=1, ws=wss[i], stream=streams[i])
+            out[i] = outs[i]
+        except Exception as e:  # reported after the join
+            errs.append(e)
+
+    th = [threading.Thread(target=run, args=(i,)) for i in range(len(spec))]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errs, errs
+    torch.cuda.synchronize()
+    for (n, b, nv), Cs, (lam, V, info) in zip(spec, mats, out):
+        lam, V, info = host(lam), host(V), host(info)
+        assert np.all(info == 0)
+        for m in range(b):
+            l1, V1, i1 = lrc.lrc_eigh(dev(Cs[m], "f32"), n_vec=nv, prec=1)
+            assert np.array_equal(lam[m], host(l1)), (n, m)
+            assert np.array_equal(V[m], host(V1)), (n, m)
+
+
 @pytest.mark.parametrize("prec", [1, 2])
 def test_eigh_range_basis_vs_oracle(lrc, prec):
     """A covariance of Y = X W with d_in < d_out decomposed through B = Q^T C Q, Q a basis of range(W^T):
