@@ -170,7 +170,7 @@ def main():
     # outputs and workspaces allocated once, outside the timed region.  The matrices are grouped
     # by output width and rank (q/k/v/o: 4096 and 1228, down: 4096 and 1791, gate/up: 11008 and
     # 1791); each group's covariances sit in one stack, and all groups go through one call that
-    # decomposes up to four matrices at once.
+    # decomposes up to eight matrices at once.
     groups = {}
     for m in MATS:
         groups.setdefault((sh[m][1], ks[m]), []).append(m)
