@@ -380,6 +380,46 @@ lrc_status lrc_to_f64(const void *X, lrc_dtype t, int64_t rows, int64_t cols, in
     return to_f64_run(X, t, rows, cols, ldx, scale, Y, ldy, static_cast<hipStream_t>(stream));
 }
 
+// C = W^T H W from the input covariance H = X^T X (SAES-SVD page, section 1 of the method (CEALC):
+// the closed form works from the layer's input covariance H); the same C as the covariance of
+// Y = X W by associativity.  fp64 workspace: H widened to both triangles, W widened, T = H W.
+static size_t cov_from_input_layout(int64_t d_in, int64_t d_out, size_t *offs) {
+    const size_t sz[3] = {size_t(d_in) * size_t(d_in), size_t(d_in) * size_t(d_out), size_t(d_in) * size_t(d_out)};
+    size_t off = 0;
+    for (int i = 0; i < 3; ++i) {
+        if (offs) offs[i] = off;
+        off += (sz[i] * sizeof(double) + 255) / 256 * 256;
+    }
+    return off;
+}
+
+size_t lrc_cov_from_input_workspace(int64_t d_in, int64_t d_out) {
+    return (d_in > 0 && d_out > 0) ? cov_from_input_layout(d_in, d_out, nullptr) : 0;
+}
+
+lrc_status lrc_cov_from_input(const float *H, int64_t d_in, int64_t ldh, const void *W, lrc_dtype w_t, int64_t d_out,
+                              int64_t ldw, float *C, int64_t ldc, void *ws, size_t ws_bytes, void *stream) {
+    REQUIRE(H && W && C, LRC_ERR_ARG, "H, W and C must be non-NULL");
+    REQUIRE(w_t == LRC_BF16 || w_t == LRC_F32 || w_t == LRC_F64, LRC_ERR_DTYPE, "W must be bf16, fp32 or fp64");
+    REQUIRE(d_in > 0 && d_out > 0 && ldh >= d_in && ldw >= d_out && ldc >= d_out, LRC_ERR_ARG,
+            "bad sizes or leading dims");
+    size_t offs[3];
+    const size_t need = cov_from_input_layout(d_in, d_out, offs);
+    REQUIRE(ws && ws_bytes >= need && reinterpret_cast<uintptr_t>(ws) % 256 == 0, LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_cov_from_input_workspace() or not 256-byte aligned");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+    double *H64 = reinterpret_cast<double *>(base + offs[0]);
+    double *W64 = reinterpret_cast<double *>(base + offs[1]);
+    double *T = reinterpret_cast<double *>(base + offs[2]);
+    lrc_status st = sym_to_f64_run(H, d_in, ldh, 1.0, H64, d_in, s);
+    if (st == LRC_OK) st = to_f64_run(W, w_t, d_in, d_out, ldw, 1.0, W64, d_out, s);
+    // T = H W (d_in x d_out), then C[upper] = W^T T rounded once to fp32
+    if (st == LRC_OK) st = dgemm_run(0, 0, d_in, d_out, d_in, H64, d_in, W64, d_out, T, d_out, 0, nullptr, s);
+    if (st == LRC_OK) st = dgemm_run(1, 0, d_out, d_out, d_in, W64, d_out, T, d_out, nullptr, ldc, 2, C, s);
+    return st;
+}
+
 lrc_status lrc_gram_f64(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg, void *stream) {
     REQUIRE(B && G, LRC_ERR_ARG, "B and G must be non-NULL");
     REQUIRE(m > 0 && n > 0 && ldb >= n && ldg >= m, LRC_ERR_ARG, "bad sizes or leading dims");

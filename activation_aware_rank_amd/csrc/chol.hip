@@ -596,6 +596,7 @@ lrc_status dgemm_run(int ta, int tb, int64_t M, int64_t N, int64_t K, const doub
     if (Cf) {
         if (ta == 0 && tb == 1) return launch_gemm<0, 1, 0, 0, 1>(g, s);
         if (ta == 0 && tb == 0) return launch_gemm<0, 0, 0, 0, 1>(g, s);
+        if (ta == 1 && tb == 0) return launch_gemm<1, 0, 0, 0, 1>(g, s);
     } else {
         if (ta == 0 && tb == 0) return launch_gemm<0, 0, 0, 0, 0>(g, s);
         if (ta == 0 && tb == 1) return launch_gemm<0, 1, 0, 0, 0>(g, s);

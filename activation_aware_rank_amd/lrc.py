@@ -61,6 +61,8 @@ _trsm = _sig("lrc_trsm", _int, _i32, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp
 _sym64 = _sig("lrc_sym_to_f64", _int, _vp, _i64, _i64, ctypes.c_double, _vp, _i64, _vp)
 _to64 = _sig("lrc_to_f64", _int, _vp, _int, _i64, _i64, _i64, ctypes.c_double, _vp, _i64, _vp)
 _gram64 = _sig("lrc_gram_f64", _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp)
+_cfi_ws = _sig("lrc_cov_from_input_workspace", _sz, _i64, _i64)
+_cfi = _sig("lrc_cov_from_input", _int, _vp, _i64, _i64, _vp, _int, _i64, _i64, _vp, _i64, _vp, _sz, _vp)
 _tim_en = _sig("lrc_timing_enable", _int, _int)
 _tim_st = _sig("lrc_timing_set_stride", _int, ctypes.c_char_p, _int)
 _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
@@ -72,6 +74,7 @@ EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_a
             "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_allocate_ranks_workspace",
             "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm_workspace", "lrc_trmm",
             "lrc_trsm_workspace", "lrc_trsm", "lrc_sym_to_f64", "lrc_to_f64", "lrc_gram_f64",
+            "lrc_cov_from_input_workspace", "lrc_cov_from_input",
             "lrc_timing_enable", "lrc_timing_set_stride", "lrc_timing_read")
 
 
@@ -454,3 +457,28 @@ def lrc_gram_f64(B: torch.Tensor, G=None, stream=None):
         raise ValueError("G must be float32")
     _check(_gram64(_ptr(B), m, n, ldb, _ptr(G), _rows(G, "G"), _stream(stream)))
     return G
+
+
+def lrc_cov_from_input_workspace(d_in: int, d_out: int) -> int:
+    return _cfi_ws(d_in, d_out)
+
+
+def lrc_cov_from_input(H: torch.Tensor, W: torch.Tensor, C=None, ws=None, stream=None) -> torch.Tensor:
+    """Upper triangle of C = W^T H W (fp32), from the input covariance H = X^T X (fp32 d_in x d_in, upper
+    triangle read, as lrc_cov_accumulate writes it with W = None) and W (d_in x d_out): the covariance
+    of Y = X W, formed in fp64."""
+    ldh = _rows(H, "H")
+    if H.dtype != torch.float32:
+        raise ValueError("H must be float32")
+    d_in = H.shape[0]
+    ldw = _rows(W, "W")
+    if W.shape[0] != d_in:
+        raise ValueError("W must have d_in rows")
+    d_out = W.shape[1]
+    if C is None:
+        C = torch.zeros(d_out, d_out, dtype=torch.float32, device=H.device)
+    if C.dtype != torch.float32:
+        raise ValueError("C must be float32")
+    w, wn = _workspace(_cfi_ws(d_in, d_out), H.device, ws)
+    _check(_cfi(_ptr(H), d_in, ldh, _ptr(W), _dt(W), d_out, ldw, _ptr(C), _rows(C, "C"), _ptr(w), wn, _stream(stream)))
+    return C

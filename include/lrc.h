@@ -322,6 +322,30 @@ lrc_status lrc_to_f64(const void *X, lrc_dtype t, int64_t rows, int64_t cols, in
 lrc_status lrc_gram_f64(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg,
                         void *stream);
 
+/* ------------------------------------------------------------------------------------
+ * Covariance from the input covariance (SAES-SVD page "SAES-SVD", section 1 of the method
+ * (CEALC): the closed form works from a layer's input covariance H).  For Y = X W,
+ * Y^T Y = W^T (X^T X) W, so one H = X^T X (lrc_cov_accumulate with W == NULL) serves every
+ * matrix that reads the same X.
+ *
+ *   C[upper] = W^T H W
+ *
+ * H: d_in x d_in fp32, leading dim ldh >= d_in, upper triangle incl. diagonal read (the layout
+ *    lrc_cov_accumulate writes).
+ * W: d_in x d_out, leading dim ldw >= d_out, dtype w_t (LRC_BF16, LRC_F32 or LRC_F64).
+ * C: d_out x d_out fp32, ldc >= d_out: the upper triangle incl. diagonal is overwritten (not
+ *    accumulated), the strict lower triangle is never written.
+ * Arithmetic: H and W widened exactly to fp64, T = H W and W^T T on fp64 MFMA with fp64 sums,
+ *    rounded once to fp32.
+ * ws: lrc_cov_from_input_workspace(d_in, d_out) bytes, 256-byte aligned (fp64 copies of H and
+ *    W and the product T: 8 (d_in^2 + 2 d_in d_out) bytes); caller-owned, used on `stream`.
+ * Errors: LRC_ERR_ARG (NULL pointers, sizes, leading dims), LRC_ERR_DTYPE, LRC_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_cov_from_input_workspace(int64_t d_in, int64_t d_out);
+lrc_status lrc_cov_from_input(const float *H, int64_t d_in, int64_t ldh, const void *W, lrc_dtype w_t,
+                              int64_t d_out, int64_t ldw, float *C, int64_t ldc, void *ws, size_t ws_bytes,
+                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,15 @@ def test_argument_errors_are_synchronous():
     # identity W with d_out != d_in
     rc = lrc._cov(fake, 0, 10, 8, 8, None, 0, 16, 0, 1, fake, 16, None, 0, fake, None)
     assert rc == 1
+    # covariance from the input covariance: NULL H, W dtype, ldh < d_in, workspace too small
+    need = lrc.lrc_cov_from_input_workspace(8, 12)
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert need == up(8 * 8 * 8) + 2 * up(8 * 12 * 8)  # fp64 H, W and H W
+    assert lrc._cfi(None, 8, 8, fake, 0, 12, 12, fake, 12, fake, need, None) == 1
+    assert lrc._cfi(fake, 8, 8, fake, 7, 12, 12, fake, 12, fake, need, None) == 2
+    assert lrc._cfi(fake, 8, 7, fake, 0, 12, 12, fake, 12, fake, need, None) == 1
+    rc = lrc._cfi(fake, 8, 8, fake, 0, 12, 12, fake, 12, fake, need - 1, None)
+    assert rc == 3 and "workspace" in lrc.lrc_last_error()
     # workspace too small
     need = lrc.lrc_cov_accumulate_workspace(0, 1000, 64, True, 64, 1)
     assert need > 0

@@ -126,6 +126,32 @@ def test_cov_many_tiles_xcd_order(lrc):
     assert np.all(np.tril(C, -1) == 0)
 
 
+@pytest.mark.parametrize("d_out", [640, 384])
+def test_cov_from_input_vs_oracle(lrc, d_out):
+    """C = W^T H W from the GPU's input covariance H = X^T X (one bf16 product, fp32 sums) against the
+    oracle's direct covariance of Y = X W: every upper entry relative to sqrt(C_ii C_jj), then the
+    eigenvalues and the error curve of the factored C to the pipeline's tolerances."""
+    _say("cov from input covariance, 5000 x 512 -> %d" % d_out)
+    X = inputs.block_activations(512, 5000)
+    W = inputs.weight(512, d_out, "bf16", inputs.CFG_BLOCK, 0, 4)
+    H = _cov_gpu(lrc, X, "bf16", None)
+    C = lrc.lrc_cov_from_input(H, dev(W, "bf16"))
+    Cr = oracle.covariance(X, "bf16", W, "bf16")
+    Ch = host(C).astype(np.float64)
+    dg = np.sqrt(np.outer(np.diag(Cr), np.diag(Cr)))
+    U = np.triu(np.ones(Cr.shape, dtype=bool))
+    rel = np.max(np.abs(Ch - Cr)[U] / dg[U])
+    print("max |dC_ij| / sqrt(C_ii C_jj) = %.3e" % rel)
+    assert rel <= 1e-5
+    assert np.all(np.tril(Ch, -1) == 0)
+    lam, V, info = lrc.lrc_eigh(C, n_vec=64, prec=2)
+    assert int(info.item()) == 0
+    eps = host(lrc.lrc_error_curve(lam[None]))[0]
+    lam_r, V_r = oracle.eigh(Cr)
+    check_lambda(host(lam), lam_r)
+    check_eps(eps, oracle.error_curve(lam_r))
+
+
 def test_cov_identity_weight(lrc):
     _say("cov bf16 W = I, 3000 x 264")
     X = inputs.block_activations(264, 3000)

@@ -58,6 +58,19 @@ def test_cov_closed_form_diagonal():
     assert np.array_equal(C, np.diag(s * s))
 
 
+def test_cov_from_input_covariance_identity():
+    """(X W)^T (X W) = W^T (X^T X) W: the oracle's direct covariance against the product of its
+    input covariance (W = I) with W on both sides, on bf16 inputs of block shape."""
+    X = inputs.block_activations(96, 700)
+    for d_out in (64, 160):
+        W = inputs.weight(96, d_out, "bf16", inputs.CFG_BLOCK, 0, 5)
+        C = oracle.covariance(X, "bf16", W, "bf16")
+        H = oracle.covariance(X, "bf16")
+        W64 = oracle.widen(W, "bf16")
+        C2 = W64.T @ H @ W64
+        assert np.allclose(C, C2, rtol=1e-11, atol=1e-11 * np.max(np.abs(C)))
+
+
 def test_cov_bruteforce_tiny():
     r = np.random.default_rng(1)
     X = r.standard_normal((5, 3))
