@@ -142,6 +142,8 @@ def main():
                          "remaining covariances run")
     ap.add_argument("--overlap-order", choices=("large-first", "most-first"), default="large-first",
                     help="group order: largest n first, or the group with the most matrices first")
+    ap.add_argument("--factored-steps", type=int, default=2,
+                    help="timed steps of the variant that forms the covariances from X^T X (0: skip)")
     ap.add_argument("--eig-range", choices=("on", "off"), default="on",
                     help="on: covariances of Y = X W with d_in < d_out (gate/up) are decomposed through a basis of "
                          "range(W^T) (their rank is at most d_in); off: the full decomposition of every covariance")
@@ -251,6 +253,24 @@ def main():
         e1 = ev(sg)
         times.append(("eigh." + gname[g], e0, e1))
 
+    def tail(times):
+        for m in MATS:
+            e0 = ev(stream)
+            lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m])
+            e1 = ev(stream)
+            times.append((m + ".fac", e0, e1))
+        e5 = ev(stream)
+        lrc.lrc_fisher_scores([G[m] for m in MATS], [W[m] for m in MATS], alpha=alpha, ws=ws_fsh)
+        e6 = ev(stream)
+        for i, m in enumerate(MATS):  # gather lambda_m[:K_m] and eps_{m,0} (device copies)
+            lam_packed[offs_h[i]:offs_h[i] + kcap[m]].copy_(lam[m][:kcap[m]])
+            eps0[i:i + 1].copy_(eps[m][0:1])
+        e7 = ev(stream)
+        lrc.lrc_allocate_ranks(alpha, lam_packed, offs, eps0, cost, budget, k_out=k_out, ws=ws_alc)
+        e8 = ev(stream)
+        times.append(("fisher", e5, e6))
+        times.append(("alloc", e7, e8))
+
     def step(times):
         if a.overlap == "on":
             threads = []
@@ -274,22 +294,60 @@ def main():
                 lrc.lrc_error_curve(glam[g], eps=geps[g])
             e1 = ev(stream)
             times.append(("eigh." + gkey, e0, e1))
-        for m in MATS:
+        tail(times)
+
+    def factored_leg():
+        """The same step with the covariances formed from the input covariances (H = X^T X for the six
+        matrices that read X, H_d = X_d^T X_d for down, then C_m = W_m^T H W_m in fp64), the stages in
+        series; timed like the main step."""
+        H = torch.empty(a.d_model, a.d_model, dtype=torch.float32, device=dev)
+        Hd = torch.empty(a.d_ff, a.d_ff, dtype=torch.float32, device=dev)
+        ws_h = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, d, False, d, 1)
+                               for d in (a.d_model, a.d_ff)), dtype=torch.uint8, device=dev)
+        ws_f = torch.empty(max(lrc.lrc_cov_from_input_workspace(di, do) for di, do in sh.values()),
+                           dtype=torch.uint8, device=dev)
+
+        def fstep(times):
             e0 = ev(stream)
-            lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m])
+            H.zero_()
+            lrc.lrc_cov_accumulate(X, None, H, info=info[0:1], ws=ws_h)
+            Hd.zero_()
+            lrc.lrc_cov_accumulate(Xd, None, Hd, info=info[1:2], ws=ws_h)
             e1 = ev(stream)
-            times.append((m + ".fac", e0, e1))
-        e5 = ev(stream)
-        lrc.lrc_fisher_scores([G[m] for m in MATS], [W[m] for m in MATS], alpha=alpha, ws=ws_fsh)
-        e6 = ev(stream)
-        for i, m in enumerate(MATS):  # gather lambda_m[:K_m] and eps_{m,0} (device copies)
-            lam_packed[offs_h[i]:offs_h[i] + kcap[m]].copy_(lam[m][:kcap[m]])
-            eps0[i:i + 1].copy_(eps[m][0:1])
-        e7 = ev(stream)
-        lrc.lrc_allocate_ranks(alpha, lam_packed, offs, eps0, cost, budget, k_out=k_out, ws=ws_alc)
-        e8 = ev(stream)
-        times.append(("fisher", e5, e6))
-        times.append(("alloc", e7, e8))
+            for m in MATS:
+                lrc.lrc_cov_from_input(Hd if m == "down_proj" else H, W[m], C=C[m], ws=ws_f)
+            e2 = ev(stream)
+            lrc.lrc_eigh_multi(eig_groups, prec=prec, ws=ws_eig)
+            for g in groups:
+                lrc.lrc_error_curve(glam[g], eps=geps[g])
+            e3 = ev(stream)
+            times += [("input_cov", e0, e1), ("cov_from_input", e1, e2), ("eigh", e2, e3)]
+            tail(times)
+
+        for _ in range(a.warmup):
+            fstep([])
+        torch.cuda.synchronize()
+        recs_f = []
+        t0f = time.perf_counter()
+        for _ in range(a.factored_steps):
+            r = []
+            fstep(r)
+            recs_f.append(r)
+        torch.cuda.synchronize()
+        wall_f = time.perf_counter() - t0f
+        assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
+        per_f = {}
+        for r in recs_f:
+            for key, x0, x1 in r:
+                per_f.setdefault(key, []).append(x0.elapsed_time(x1))
+        avg_f = {k: round(float(np.mean(v)), 3) for k, v in per_f.items() if k in ("input_cov", "cov_from_input", "eigh")}
+        ms_f = wall_f * 1000.0 / a.factored_steps
+        return {"metric": "calibration tokens/s into Y^T Y", "value": a.tokens / (ms_f / 1000.0), "unit": "tokens/s",
+                "ms_per_step": ms_f, "steps": a.factored_steps, "breakdown_ms": avg_f,
+                "cov_tokens_per_s": a.tokens / ((avg_f["input_cov"] + avg_f["cov_from_input"]) / 1000.0),
+                "note": "same block, inputs, eigendecompositions, factors, Fisher scores and allocation as the main "
+                        "step; the covariances by C_m = W_m^T (X^T X) W_m (one bf16 SYRK of X and one of X_d, then "
+                        "two fp64 products per matrix) instead of the fused GEMM + split SYRK; stages in series"}
 
     # a plain copy of known size, outside the timed region: the reference that scales HBM byte
     # counters (FETCH_SIZE / WRITE_SIZE) of a profiled run into bytes
@@ -438,6 +496,8 @@ def main():
         "roofline": roof,
         "rooflines": {"k_cov_syrk": roof_syrk, "k_trd_symv": roof_symv, "k_cov_gemm_y": roof_gemm},
     }
+    if a.factored_steps > 0:
+        out["factored"] = factored_leg()
     if a.curvature_tokens > 0:
         del X, Xd, W, G, C, V, A, B, gC, gV, glam, geps, lam, eps, ws_cov, ws_eig
         torch.cuda.empty_cache()
