@@ -325,6 +325,14 @@ lrc_status lrc_allocate_ranks(int32_t n_mats, const double *alpha, const double 
     return alloc_run(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+lrc_status lrc_allocate_proportional(int32_t n_mats, const double *alpha, int32_t n_budgets, const int64_t *budgets,
+                                     int64_t *r_out, int32_t *info, void *stream) {
+    REQUIRE(alpha && budgets && r_out && info, LRC_ERR_ARG, "null argument");
+    REQUIRE(n_mats > 0 && n_mats <= PROP_MAX, LRC_ERR_ARG, "n_mats must be in 1 .. 1024");
+    REQUIRE(n_budgets > 0, LRC_ERR_ARG, "n_budgets must be positive");
+    return alloc_prop_run(n_mats, alpha, n_budgets, budgets, r_out, info, static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------------------------------------
 size_t lrc_cholesky_workspace(int64_t n) { return n > 0 ? cholesky_workspace(n) : 0; }
 

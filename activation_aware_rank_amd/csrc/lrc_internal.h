@@ -182,6 +182,9 @@ lrc_status to_f64_run(const void *X, lrc_dtype t, int64_t rows, int64_t cols, in
                       double *Y, int64_t ldy, hipStream_t s);
 // C = op(A) op(B) in fp64 (ta, tb: 0 plain, 1 transposed; tiles 0 all, 1 lower, 2 upper); with Cf the
 // product goes to Cf as fp32 instead
+constexpr int PROP_MAX = 1024;  // matrices per proportional allocation
+lrc_status alloc_prop_run(int32_t n, const double *alpha, int32_t nb, const int64_t *budgets, int64_t *r_out,
+                          int32_t *info, hipStream_t s);
 lrc_status dgemm_run(int ta, int tb, int64_t M, int64_t N, int64_t K, const double *A, int64_t lda, const double *B,
                      int64_t ldb, double *C, int64_t ldc, int tiles, float *Cf, hipStream_t s);
 lrc_status gram_f64_run(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg,

@@ -362,6 +362,83 @@ size_t alloc_workspace(int32_t n_mats, int64_t n_items) {
     return c.off;
 }
 
+// Proportional ranks (FLRC page, method 1: r_m = round(alpha_m / S * R); method 2: the same rule for
+// each budget R(t) of a non-increasing schedule), one workgroup per budget, one thread per matrix.
+// Rounding half away from zero, then the sum brought to R by largest remainders: the d matrices
+// first in (q_m - r_m descending, m ascending) order gain one when the sum is short by d; when it is
+// over by d, the d matrices with r_m > 0 first in (q_m - r_m ascending, m ascending) order lose one
+// (one unit per matrix suffices: every rounding moved q_m by at most one half).  q_m = (alpha_m R) / S
+// in fp64 with S summed in index order by one thread, so the decisions match a sequential
+// evaluation bit for bit.
+__global__ void __launch_bounds__(PROP_MAX) k_alloc_prop(int32_t n, const double *__restrict__ alpha, int32_t nb,
+                                                         const int64_t *__restrict__ budgets, int64_t *__restrict__ r_out,
+                                                         int32_t *__restrict__ info) {
+    __shared__ double S_sh;
+    __shared__ int bad_sh;
+    __shared__ double rem[PROP_MAX];
+    __shared__ long long rr[PROP_MAX];
+    __shared__ long long sum_sh;
+    const int m = threadIdx.x, t = blockIdx.x;
+    if (m == 0) {
+        double S = 0.0;
+        int bad = 0;
+        for (int i = 0; i < n; ++i) {
+            const double v = alpha[i];
+            if (!(v >= 0.0)) bad = 1;
+            S = S + v;
+        }
+        if (!(S > 0.0 && S <= 1.7976931348623157e308)) bad = 1;
+        for (int i = 0; i < nb; ++i)
+            if (budgets[i] < 0) bad = 1;
+        S_sh = S;
+        bad_sh = bad;
+    }
+    __syncthreads();
+    if (bad_sh) {
+        if (m < n) r_out[int64_t(t) * n + m] = 0;
+        if (t == 0 && m == 0) *info = 5;
+        return;
+    }
+    const int64_t R = budgets[t];
+    double q = 0.0;
+    long long r = 0;
+    if (m < n) {
+        q = (alpha[m] * double(R)) / S_sh;
+        r = (long long)floor(q + 0.5);
+        rem[m] = q - double(r);
+        rr[m] = r;
+    }
+    __syncthreads();
+    if (m == 0) {
+        long long sm = 0;
+        for (int i = 0; i < n; ++i) sm += rr[i];
+        sum_sh = sm;
+    }
+    __syncthreads();
+    const long long d = (long long)R - sum_sh;
+    if (m < n) {
+        if (d > 0) {
+            long long rank = 0;
+            for (int i = 0; i < n; ++i) rank += (rem[i] > rem[m] || (rem[i] == rem[m] && i < m)) ? 1 : 0;
+            if (rank < d) r += 1;
+        } else if (d < 0 && rr[m] > 0) {
+            long long rank = 0;
+            for (int i = 0; i < n; ++i)
+                rank += (rr[i] > 0 && (rem[i] < rem[m] || (rem[i] == rem[m] && i < m))) ? 1 : 0;
+            if (rank < -d) r -= 1;
+        }
+        r_out[int64_t(t) * n + m] = r;
+    }
+    if (t == 0 && m == 0) *info = 0;
+}
+
+lrc_status alloc_prop_run(int32_t n, const double *alpha, int32_t nb, const int64_t *budgets, int64_t *r_out,
+                          int32_t *info, hipStream_t s) {
+    hipLaunchKernelGGL(k_alloc_prop, dim3(unsigned(nb)), dim3(PROP_MAX), 0, s, n, alpha, nb, budgets, r_out, info);
+    LRC_LAUNCH_CHECK("k_alloc_prop");
+    return LRC_OK;
+}
+
 lrc_status alloc_run(const AllocArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
     Carver cv(ws, ws_bytes);
     double *wm = cv.carve<double>(size_t(a.n_mats));

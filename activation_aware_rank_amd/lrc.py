@@ -62,6 +62,7 @@ _sym64 = _sig("lrc_sym_to_f64", _int, _vp, _i64, _i64, ctypes.c_double, _vp, _i6
 _to64 = _sig("lrc_to_f64", _int, _vp, _int, _i64, _i64, _i64, ctypes.c_double, _vp, _i64, _vp)
 _gram64 = _sig("lrc_gram_f64", _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp)
 _cfi_ws = _sig("lrc_cov_from_input_workspace", _sz, _i64, _i64)
+_aprop = _sig("lrc_allocate_proportional", _int, _i32, _vp, _i32, _vp, _vp, _vp, _vp)
 _cfi = _sig("lrc_cov_from_input", _int, _vp, _i64, _i64, _vp, _int, _i64, _i64, _vp, _i64, _vp, _sz, _vp)
 _tim_en = _sig("lrc_timing_enable", _int, _int)
 _tim_st = _sig("lrc_timing_set_stride", _int, ctypes.c_char_p, _int)
@@ -74,7 +75,7 @@ EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_a
             "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_allocate_ranks_workspace",
             "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm_workspace", "lrc_trmm",
             "lrc_trsm_workspace", "lrc_trsm", "lrc_sym_to_f64", "lrc_to_f64", "lrc_gram_f64",
-            "lrc_cov_from_input_workspace", "lrc_cov_from_input",
+            "lrc_cov_from_input_workspace", "lrc_cov_from_input", "lrc_allocate_proportional",
             "lrc_timing_enable", "lrc_timing_set_stride", "lrc_timing_read")
 
 
@@ -482,3 +483,21 @@ def lrc_cov_from_input(H: torch.Tensor, W: torch.Tensor, C=None, ws=None, stream
     w, wn = _workspace(_cfi_ws(d_in, d_out), H.device, ws)
     _check(_cfi(_ptr(H), d_in, ldh, _ptr(W), _dt(W), d_out, ldw, _ptr(C), _rows(C, "C"), _ptr(w), wn, _stream(stream)))
     return C
+
+
+def lrc_allocate_proportional(alpha: torch.Tensor, budgets: torch.Tensor, r_out=None, info=None, stream=None):
+    """Ranks r[t][m] = round(alpha_m / S * budgets[t]), the rows brought to sum to budgets[t] by largest
+    remainders (see include/lrc.h).  alpha fp64 (n_mats,), budgets int64 (n_budgets,) on the GPU.
+    Returns (r int64 (n_budgets, n_mats), info int32 (1,))."""
+    _dev(alpha, "alpha")
+    _dev(budgets, "budgets")
+    if alpha.dtype != torch.float64 or not alpha.is_contiguous():
+        raise ValueError("alpha must be a contiguous float64 vector")
+    if budgets.dtype != torch.int64 or not budgets.is_contiguous():
+        raise ValueError("budgets must be a contiguous int64 vector")
+    n, nb = alpha.numel(), budgets.numel()
+    if r_out is None:
+        r_out = torch.empty(nb, n, dtype=torch.int64, device=alpha.device)
+    info = _info(info, 1, alpha.device)
+    _check(_aprop(n, _ptr(alpha), nb, _ptr(budgets), _ptr(r_out), _ptr(info), _stream(stream)))
+    return r_out, info

@@ -281,6 +281,26 @@ lrc_status lrc_allocate_ranks(int32_t n_mats, const double *alpha, const double 
                               int32_t *k_out, void *ws, size_t ws_bytes, int32_t *info, void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * Proportional rank allocation (FLRC page, method 1: each projection's rank in proportion to
+ * its Fisher importance, r_m = round(alpha_m / S * R) with S = sum of alpha; method 2: the same
+ * rule for each budget R(t) of a non-increasing per-token schedule).
+ *
+ * alpha: n_mats fp64 (1 <= n_mats <= 1024), e.g. lrc_fisher_scores' output.
+ * budgets: n_budgets int64 total rank budgets R (one row of output each).
+ * r_out: n_budgets x n_mats int64 ranks, row t for budgets[t].
+ * Rounding (the page leaves it open): half away from zero, then the row is brought to sum to
+ *    exactly R by largest remainders (short by d: the d matrices with the largest alpha_m R / S
+ *    - r_m gain one, ties to the smaller m; over by d: the d matrices with r_m > 0 and the
+ *    smallest remainders lose one, ties to the smaller m).  q_m = (alpha_m R) / S in fp64 with S
+ *    summed in index order, so the result is bit-exact against a sequential evaluation.
+ * info: one int32: 0, or 5 when an alpha is negative or NaN, S is not positive and finite, or a
+ *    budget is negative (every rank is then 0).
+ * Errors: LRC_ERR_ARG (NULL pointers, n_mats outside 1 .. 1024, n_budgets <= 0).
+ * ------------------------------------------------------------------------------------ */
+lrc_status lrc_allocate_proportional(int32_t n_mats, const double *alpha, int32_t n_budgets,
+                                     const int64_t *budgets, int64_t *r_out, int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Curvature-weighted variant (LASER page, method 1: the loss increase of a perturbation dW
  * is approximated by 1/2 vec(dW)^T (G (x) X) vec(dW) with X, G the activation and gradient
  * covariances; W is moved to W~ = S_x W S_g with Cholesky factors S_x, S_g, truncated there

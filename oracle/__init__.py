@@ -255,6 +255,43 @@ def allocation_priorities(alpha, lams, eps0, cost, k_min):
     return np.concatenate(p_all), np.concatenate(m_all), np.concatenate(k_all)
 
 
+def allocate_proportional(alpha, budgets) -> tuple[np.ndarray, int]:
+    """Ranks in proportion to the Fisher importance, for one or several rank budgets.
+
+    FLRC page, method 1: r_m = round(alpha_m / S * R) with S the sum of the alpha_m and R the total
+    rank budget; method 2 evaluates the same rule for a non-increasing budget R(t) per decoding
+    step.  Readings (the page fixes neither): round half away from zero, then the sum is brought to
+    exactly R by largest remainders -- while it is short, the matrix with the largest q_m - r_m
+    (ties: smaller m) gains one; while it is over, the matrix with r_m > 0 and the smallest
+    q_m - r_m (ties: smaller m) loses one -- with q_m = (alpha_m * R) / S in fp64 and S summed in
+    index order.  Returns (r, info): r has one row per budget; info 5 when an alpha is negative or
+    NaN or S is not positive and finite, or a budget is negative (r is then all zero).
+    """
+    a = np.asarray(alpha, dtype=np.float64)
+    B = [int(b) for b in budgets]
+    r = np.zeros((len(B), len(a)), dtype=np.int64)
+    S = 0.0
+    for v in a:  # index order
+        S = S + float(v)
+    if np.any(~(a >= 0)) or not (0 < S < np.inf) or any(b < 0 for b in B):
+        return r, 5
+    for t, R in enumerate(B):
+        q = [(float(a[m]) * float(R)) / S for m in range(len(a))]
+        rt = [int(np.floor(x + 0.5)) for x in q]  # half away from zero (q >= 0)
+        d = R - sum(rt)
+        while d > 0:
+            m = max(range(len(a)), key=lambda i: (q[i] - rt[i], -i))
+            rt[m] += 1
+            d -= 1
+        while d < 0:
+            cand = [i for i in range(len(a)) if rt[i] > 0]
+            m = min(cand, key=lambda i: (q[i] - rt[i], i))
+            rt[m] -= 1
+            d += 1
+        r[t] = rt
+    return r, 0
+
+
 def allocate_ranks(alpha, lams, eps0, cost, budget: int, k_min=None) -> tuple[np.ndarray, int]:
     """Greedy global rank allocation under a parameter budget.
 

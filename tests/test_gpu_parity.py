@@ -694,3 +694,21 @@ def test_pipeline_per_head_scaled(lrc):
     d = inputs.per_head(n_tok=8192, d_model=512, head_dim=128)
     out = _pipeline(lrc, d["X"], "bf16", d["W"], 32, n_blocks=4)
     _check_pipeline(d["X"], "bf16", d["W"], 32, *out[:5], n_blocks=4, C_gpu=out[5])
+
+
+def test_allocate_proportional_bitexact(lrc):
+    """FLRC proportional ranks (and a non-increasing budget schedule) bit-exact against the oracle:
+    224 lognormal importances with repeated values (ties), 7 importances, and bad scores (info 5)."""
+    _say("allocate proportional: 224 and 7 matrices, 6 budgets")
+    rng = np.random.default_rng(11)
+    a224 = rng.lognormal(0.0, 2.0, size=224)
+    a224[10:20] = a224[5]  # ties in the remainders
+    budgets = np.array([500000, 400000, 123457, 2241, 7, 0], dtype=np.int64)
+    for a in (a224, np.array([3.0, 1.0, 4.0, 1.0, 5.0, 9.0, 2.0])):
+        r, info = lrc.lrc_allocate_proportional(dev(a.astype(np.float64), "f64"), dev(budgets, "i64"))
+        r_o, info_o = oracle.allocate_proportional(a, budgets.tolist())
+        assert int(host(info)[0]) == info_o == 0
+        assert np.array_equal(host(r), r_o)
+        assert np.array_equal(host(r).sum(axis=1), budgets)
+    r, info = lrc.lrc_allocate_proportional(dev(np.array([1.0, -2.0, 3.0]), "f64"), dev(budgets, "i64"))
+    assert int(host(info)[0]) == 5 and np.all(host(r) == 0)

@@ -517,3 +517,39 @@ def test_tri_solve_against_dense_solve(side, trans):
     # and the product undoes the solve
     assert np.allclose(oracle.tri_product(side, trans, Lt, X), B, atol=1e-12)
 
+
+
+def test_allocate_proportional_worked_examples():
+    """FLRC page, method 1: r = round(alpha / S * R), with the sum brought to R by largest remainders
+    (hand-worked: 10 x [1, 2, 3] / 6 = [1.67, 3.33, 5] -> [2, 3, 5]; 10 x [1, 1, 1] / 3 = 3.33 each ->
+    [3, 3, 3] + 1 to the first of the tied remainders; 3 x [1, 1] / 2 = 1.5 each rounds up to [2, 2],
+    one too many, taken from the first of the tied remainders)."""
+    r, info = oracle.allocate_proportional([1.0, 2.0, 3.0], [10, 0, 6])
+    assert info == 0 and r.tolist() == [[2, 3, 5], [0, 0, 0], [1, 2, 3]]
+    r, _ = oracle.allocate_proportional([1.0, 1.0, 1.0], [10])
+    assert r.tolist() == [[4, 3, 3]]
+    r, _ = oracle.allocate_proportional([1.0, 1.0], [3])
+    assert r.tolist() == [[1, 2]]
+    # a zero importance gets no rank; bad scores set info 5
+    r, _ = oracle.allocate_proportional([0.0, 5.0], [7])
+    assert r.tolist() == [[0, 7]]
+    for bad in ([-1.0, 2.0], [float("nan"), 1.0], [0.0, 0.0]):
+        assert oracle.allocate_proportional(bad, [4])[1] == 5
+
+
+def test_allocate_proportional_invariants():
+    """Sum exactly R; each r_m within one of alpha_m R / S; a larger alpha never gets a smaller rank;
+    the progressive schedule's ranks do not increase as the budget falls (budgets 4000 ... 0)."""
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        a = rng.lognormal(0.0, 2.0, size=int(rng.integers(1, 40)))
+        budgets = sorted(rng.integers(0, 5000, size=6).tolist(), reverse=True)
+        r, info = oracle.allocate_proportional(a, budgets)
+        assert info == 0
+        S = float(np.sum(a))
+        for t, R in enumerate(budgets):
+            assert int(r[t].sum()) == R
+            assert np.all(np.abs(r[t] - a * R / S) < 1.0 + 1e-9)
+            order = np.argsort(a, kind="stable")
+            assert np.all(np.diff(r[t][order]) >= 0) or len(set(a.tolist())) < len(a)
+        assert np.all(np.diff(r, axis=0) <= 0 + 1)  # within one step of monotone per matrix
