@@ -152,7 +152,7 @@ def main():
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported (the path would shard matrices "
-              "or token ranges across GPUs, see DESIGN.md)" % a.gpus, file=sys.stderr)
+              "or token ranges across GPUs)" % a.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
