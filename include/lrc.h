@@ -53,7 +53,7 @@ typedef enum {
     LRC_ERR_DTYPE = 2,         /* dtype not supported by this entry point */
     LRC_ERR_WORKSPACE = 3,     /* ws NULL or smaller than the query says */
     LRC_ERR_HIP = 4,           /* a HIP runtime call failed (message in lrc_last_error) */
-    LRC_ERR_UNIMPLEMENTED = 5  /* valid request this build does not implement */
+    LRC_ERR_UNIMPLEMENTED = 5  /* valid request the library does not implement */
 } lrc_status;
 
 typedef enum { LRC_BF16 = 0, LRC_F32 = 1, LRC_F64 = 2 } lrc_dtype;
