@@ -143,7 +143,8 @@ lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64
  *    j is the unit eigenvector of lambda[j], j < n_vec, with its entry of largest
  *    magnitude positive (first index on ties).  V may be NULL when n_vec == 0.
  * prec: working precision, LRC_F32 or LRC_F64.
- *    n <= 128: one-sided Jacobi, one matrix per workgroup held in LDS, in prec.
+ *    n <= 128: one-sided Jacobi, one matrix per workgroup held in LDS, always in fp64
+ *    (prec has no effect there).
  *    n > 128: Householder tridiagonalisation and back-transformation in prec; the
  *    tridiagonal eigenproblem (bisection, inverse iteration) always in fp64.
  * Batches with n > 128: up to eight members are decomposed at once, each on a helper

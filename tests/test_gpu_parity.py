@@ -2,8 +2,8 @@
 at sizes the oracle finishes in seconds that still span several tiles and have ragged tails.
 
 Tolerances (the contract): eigenvalues within 1e-5 lambda_max; eps_k within 1e-4 relative where
-eps_k >= 1e-4 eps_0 and within 2^-23 eps_0 (one fp32 unit of the trace) below that; largest principal angle of the retained
-subspace below 1e-3 rad; allocation bit-exact on identical inputs; error curve bit-exact on
+eps_k >= 1e-4 eps_0 and below that within 2^-23 eps_0 (fp32 eigensolver) or 2^-24 eps_0 (fp64 eigensolver
+and the n <= 128 Jacobi path); largest principal angle of the retained subspace below 1e-3 rad; allocation bit-exact on identical inputs; error curve bit-exact on
 identical eigenvalues (same summation order).  Diagnostics: covariance entries within 1e-5
 lambda_max, Fisher scores within 1e-12 relative, factors within 1e-6 relative (Frobenius).
 """
@@ -149,7 +149,7 @@ def test_cov_from_input_vs_oracle(lrc, d_out):
     eps = host(lrc.lrc_error_curve(lam[None]))[0]
     lam_r, V_r = oracle.eigh(Cr)
     check_lambda(host(lam), lam_r)
-    check_eps(eps, oracle.error_curve(lam_r))
+    check_eps(eps, oracle.error_curve(lam_r), prec=2)
 
 
 def test_cov_identity_weight(lrc):
@@ -263,10 +263,10 @@ def test_eigh_jacobi_vs_oracle(lrc, n, batch, prec):
     for b in range(batch):
         assert info[b] == 0
         lam_r, V_r = oracle.eigh(C32[b].astype(np.float64))
-        check_lambda(lam[b], lam_r)
+        el = check_lambda(lam[b], lam_r)
         s = sin_theta_max(V[b], V_r, k)
-        lim = 1e-3 if prec == 2 else 1e-2
-        assert s <= lim, (b, s, gap(lam_r, k))
+        print("matrix %d: lambda err %.2e lambda_max, sin theta(k=%d) %.2e, gap %.2e" % (b, el, k, s, gap(lam_r, k)))
+        assert s <= 1e-3, (b, s, gap(lam_r, k))
 
 
 @pytest.mark.parametrize("prec", [1, 2])
@@ -626,8 +626,8 @@ def _pipeline(lrc, X, xdt, W, k, n_blocks=1, prec=1):
     if n_blocks == 1:
         lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=prec)
         lam, V = lam[None], V[None]
-    else:
-        lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=2)
+    else:  # n <= 128: the batched Jacobi path, in fp64 whatever prec says
+        lam, V, info = lrc.lrc_eigh(C, n_vec=k, prec=prec)
     assert np.all(host(info) == 0)
     eps = lrc.lrc_error_curve(lam)
     A = torch.empty(n_blocks, W.shape[0], k, dtype=torch.float32, device="cuda")
@@ -638,7 +638,7 @@ def _pipeline(lrc, X, xdt, W, k, n_blocks=1, prec=1):
     return host(lam), host(V), host(eps), host(A), host(B), (Ch[None] if n_blocks == 1 else Ch)
 
 
-def _check_pipeline(X, xdt, W, k, lam, V, eps, A, B, n_blocks=1, C_gpu=None):
+def _check_pipeline(X, xdt, W, k, lam, V, eps, A, B, n_blocks=1, C_gpu=None, prec=1):
     C = oracle.covariance(X, xdt, W, xdt, n_blocks=n_blocks)
     C = C[None] if n_blocks == 1 else C
     W64 = oracle.widen(W, xdt)
@@ -666,7 +666,7 @@ def _check_pipeline(X, xdt, W, k, lam, V, eps, A, B, n_blocks=1, C_gpu=None):
               % (h, el, np.max(np.abs(eps[h][big] - eps_r[big]) / eps_r[big]),
                  np.max(np.abs(eps[h][~big] - eps_r[~big])) / eps_r[0] if (~big).any() else 0.0, s, gap(lam_r, k),
                  direct / eps_r[k] - 1))
-        check_eps(eps[h], eps_r)
+        check_eps(eps[h], eps_r, prec=prec)
         assert s <= 1e-3
         assert abs(direct - eps_r[k]) <= 1e-4 * eps_r[k] + 1e-6 * eps_r[0]
 
@@ -676,7 +676,7 @@ def test_pipeline_single_layer(lrc, prec):
     _say("pipeline single layer 2048 x 256 -> 256, k = 64, prec %d" % prec)
     d = inputs.single_layer()
     out = _pipeline(lrc, d["X"], "f32", d["W"], 64, prec=prec)
-    _check_pipeline(d["X"], "f32", d["W"], 64, *out[:5], C_gpu=out[5])
+    _check_pipeline(d["X"], "f32", d["W"], 64, *out[:5], C_gpu=out[5], prec=prec)
 
 
 @pytest.mark.parametrize("prec", [1, 2])
@@ -686,14 +686,14 @@ def test_pipeline_block_scaled(lrc, prec):
     W = inputs.weight(512, 640, "bf16", inputs.CFG_BLOCK, 0, 0)
     k = inputs.rank_at_ratio(512, 640, 0.6)
     out = _pipeline(lrc, X, "bf16", W, k, prec=prec)
-    _check_pipeline(X, "bf16", W, k, *out[:5], C_gpu=out[5])
+    _check_pipeline(X, "bf16", W, k, *out[:5], C_gpu=out[5], prec=prec)
 
 
 def test_pipeline_per_head_scaled(lrc):
     _say("pipeline per-head 8192 x 512, 4 heads of 128, k = 32")
     d = inputs.per_head(n_tok=8192, d_model=512, head_dim=128)
-    out = _pipeline(lrc, d["X"], "bf16", d["W"], 32, n_blocks=4)
-    _check_pipeline(d["X"], "bf16", d["W"], 32, *out[:5], n_blocks=4, C_gpu=out[5])
+    out = _pipeline(lrc, d["X"], "bf16", d["W"], 32, n_blocks=4)  # default prec: the Jacobi path is fp64
+    _check_pipeline(d["X"], "bf16", d["W"], 32, *out[:5], n_blocks=4, C_gpu=out[5], prec=2)
 
 
 def test_allocate_proportional_bitexact(lrc):
