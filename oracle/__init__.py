@@ -12,7 +12,8 @@ O1 ``covariance``     C = sum_t y_t^T y_t for Y = X W (Swift-SVD page, section 2
                       per-head diagonal blocks (WSVD page, methodology 1, per-head SVD).
 O2 ``eigh``           one symmetric eigendecomposition C = V diag(lam) V^T (Swift-SVD page,
                       section 2-ga: V and Sigma^2 of Y from one eig of Y^T Y), solved by the
-                      cyclic two-sided Jacobi method in ``lrco.c``.
+                      cyclic two-sided Jacobi method in ``lrco.c``; ``eigh_large`` runs the
+                      same sweeps from a nearly diagonalising start basis (orders ~4096).
 O3 ``truncate``       W_k = (W V_k) V_k^T with factors A = W V_k, B = V_k^T (Swift-SVD page,
                       section 2-ga, the closed-form optimum W*_k).
 O4 ``error_curve``    eps_k = sum_{i>k} lam_i, k = 0..n (the closed-form minimal error eps*_k
@@ -20,7 +21,10 @@ O4 ``error_curve``    eps_k = sum_{i>k} lam_i, k = 0..n (the closed-form minimal
 O5 ``direct_error``   ||X W - X W_k||_F^2, straight from its definition.
 O6 ``fisher``         alpha = sum_i (G[i] W[i])^2 (FLRC page, method 1, importance alpha_{l,p}).
 O7 ``allocate_ranks`` greedy global allocation by importance per parameter (LASER page,
-                      method 2, "global optimisation"), with per-matrix Fisher weights.
+                      method 2, "global optimisation"), with per-matrix Fisher weights;
+                      ``allocate_proportional`` (FLRC page, methods 1-2), ``swift_scores`` /
+                      ``swift_allocate`` (Swift-SVD page, section 2-na), ``component_fisher`` /
+                      ``allocate_components`` (LASER page, method 2, per-component score).
 O8 ``kfac_*``         LASER page, method 1: covariances of activations and gradients,
                       Cholesky factors, whitened W~ = L_x^T W L_g, its SVD from the eig of
                       W~ W~^T, factors mapped back; ``cholesky``, ``tri_product`` and
@@ -40,6 +44,7 @@ forms, invariants, brute force on tiny inputs or LAPACK, none of which share its
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -174,6 +179,49 @@ def eigh(C: np.ndarray, max_sweeps: int = 60) -> tuple[np.ndarray, np.ndarray]:
     if rc != 0:
         raise OracleError("Jacobi did not converge in %d sweeps" % max_sweeps)
     return lam, V
+
+
+def eigh_from_basis(C: np.ndarray, Q: np.ndarray, max_sweeps: int = 60) -> tuple[np.ndarray, np.ndarray]:
+    """Eigenpairs of C by the same cyclic Jacobi, started from an orthogonal basis Q.
+
+    The sweeps run on B = Q^T C Q (formed in fp64) and stop under the same relative threshold
+    as ``eigh``; then C = (Q V_B) diag(lam) (Q V_B)^T.  Q only changes how many sweeps are
+    needed: whatever basis it is, the result is certified by the sweeps, which leave every
+    off-diagonal entry of the rotated B below 2^-52 of its diagonal scale.  Q must be
+    orthogonal to fp64 rounding.  Descending order and signs as in ``eigh``.
+    """
+    C = np.ascontiguousarray(C, dtype=np.float64)
+    Q = np.ascontiguousarray(Q, dtype=np.float64)  # strided views would leave the BLAS path
+    n = C.shape[0]
+    if C.shape != (n, n) or Q.shape != (n, n):
+        raise ValueError("square matrices of one order expected")
+    Cs = (C + C.T) * 0.5
+    B = Q.T @ Cs @ Q
+    B = np.ascontiguousarray((B + B.T) * 0.5)
+    lam = np.empty(n)
+    VB = np.empty((n, n))
+    sweeps = ctypes.c_int(0)
+    rc = _load().lrco_jacobi_eigh(n, _dp(B), _dp(lam), _dp(VB), max_sweeps, ctypes.byref(sweeps))
+    if rc != 0:
+        raise OracleError("Jacobi did not converge in %d sweeps" % max_sweeps)
+    V = Q @ VB
+    # the sign rule of eigh, applied after the change of basis
+    idx = np.argmax(np.abs(V), axis=0)
+    V *= np.where(V[idx, np.arange(n)] < 0, -1.0, 1.0)[None, :]
+    return lam, V
+
+
+def eigh_large(C: np.ndarray, max_sweeps: int = 60) -> tuple[np.ndarray, np.ndarray]:
+    """``eigh`` for orders in the thousands, where sweeps from the identity take minutes on a host.
+
+    The cyclic Jacobi starts from the eigenvectors that LAPACK's symmetric eigensolver
+    (numpy.linalg.eigh, a test-only library step) gives for C, so that one sweep does the
+    remaining rotations and the next one confirms convergence (``eigh_from_basis``).  The answer
+    rests on the Jacobi sweeps' stopping rule, not on the library's accuracy.
+    """
+    C = np.asarray(C, dtype=np.float64)
+    _, Q = np.linalg.eigh((C + C.T) * 0.5)
+    return eigh_from_basis(C, Q[:, ::-1], max_sweeps)
 
 
 def eigh_upper(C_upper: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
@@ -333,6 +381,139 @@ def allocate_ranks(alpha, lams, eps0, cost, budget: int, k_min=None) -> tuple[np
         rem -= c
         kout[m[idx]] += 1
     return kout, 0
+
+
+def swift_scores(beta, eps_kbar, alpha: float) -> np.ndarray:
+    """Allocation scores of the Swift-SVD page, section 2-na (strategy, step 1).
+
+    s_i = beta_i^alpha * log(e + eps_{kbar,i})^(1 - alpha): beta_i the importance of matrix i and
+    eps_{kbar,i} its closed-form error at the uniform rank kbar_i.  Readings: beta is the Fisher
+    importance of the FLRC page (the only importance this path computes; any non-negative
+    importance can be passed), eps is the absolute closed-form error eps*_k (negative rounding
+    residue counts as 0).  log(e + eps) >= 1, so s_i > 0 whenever beta_i > 0.  fp64 with the host
+    C library's pow and log.
+    """
+    b = np.asarray(beta, dtype=np.float64)
+    e = np.asarray(eps_kbar, dtype=np.float64)
+    out = np.empty(b.shape[0])
+    for i in range(b.shape[0]):
+        L = math.log(math.e + max(float(e[i]), 0.0))
+        out[i] = math.pow(float(b[i]), alpha) * math.pow(L, 1.0 - alpha)
+    return out
+
+
+def swift_allocate(scores, kbar, cost, k_cap, delta: float, budget: int) -> tuple[np.ndarray, int]:
+    """Ranks from Swift-SVD scores under a parameter budget (Swift-SVD page, section 2-na, steps 1-2).
+
+    Step 2 guarantees every matrix the minimum rank floor(kbar_i * delta) (the retained ratio delta of
+    the uniform rank kbar_i).  Reading of step 1 (the page gives the score, not the rule that turns it
+    into ranks): the parameters left after the minima, E = budget - sum kmin_i cost_i, go to the
+    matrices in proportion to their scores, rank = floor(share / cost_i), no rank above k_cap_i; a
+    matrix that reaches k_cap_i keeps it and the rest is split again among the others (water
+    filling).  Each split takes S = sum of the scores of the matrices still open (index order) and
+    R = the parameters not yet committed, and gives matrix i floor(((s_i * R) / S) / cost_i) more
+    ranks (fp64, one operation at a time).  Should rounding ever overshoot the budget, the open
+    matrix of highest index with an extra rank gives one back, until the total fits.
+    Returns (k, info): info 4 when the minima exceed the budget (k = minima), 5 for a negative or
+    NaN score, a kbar outside [0, k_cap], a cost <= 0 or delta outside [0, 1] (k = zeros).
+    """
+    s = [float(x) for x in scores]
+    kbar = [int(x) for x in kbar]
+    cost = [int(x) for x in cost]
+    k_cap = [int(x) for x in k_cap]
+    M = len(s)
+    if (not (0.0 <= delta <= 1.0) or any(not (x >= 0.0) for x in s) or any(c <= 0 for c in cost)
+            or any(kbar[i] < 0 or kbar[i] > k_cap[i] for i in range(M))):
+        return np.zeros(M, dtype=np.int64), 5
+    kmin = [int(math.floor(float(kbar[i]) * delta)) for i in range(M)]
+    mand = sum(kmin[i] * cost[i] for i in range(M))
+    if mand > budget:
+        return np.array(kmin, dtype=np.int64), 4
+    E = int(budget) - mand
+    x = [0] * M
+    open_ = [i for i in range(M) if kmin[i] < k_cap[i]]
+    committed = 0
+    while open_:
+        S = 0.0
+        for i in open_:
+            S = S + s[i]
+        if not S > 0.0:
+            break
+        R = float(E - committed)
+        q = {i: int(math.floor(((s[i] * R) / S) / float(cost[i]))) for i in open_}
+        capped = [i for i in open_ if kmin[i] + q[i] >= k_cap[i]]
+        if not capped:
+            for i in open_:
+                x[i] = q[i]
+            break
+        for i in capped:
+            x[i] = k_cap[i] - kmin[i]
+            committed += x[i] * cost[i]
+        open_ = [i for i in open_ if i not in capped]
+    total = sum((kmin[i] + x[i]) * cost[i] for i in range(M))
+    while total > budget:
+        i = max(j for j in open_ if x[j] > 0)
+        x[i] -= 1
+        total -= cost[i]
+    return np.array([kmin[i] + x[i] for i in range(M)], dtype=np.int64), 0
+
+
+def component_fisher(W64: np.ndarray, G64: np.ndarray, V: np.ndarray, k: int) -> np.ndarray:
+    """Empirical-Fisher importance of each retained component (LASER page, method 2).
+
+    Removing component i of the truncation changes W by dW_i = W v_i v_i^T.  Reading (the page
+    describes the score, it does not print it): with the calibration gradient G of the same shape
+    as W, the empirical-Fisher quadratic loss of that change is <G, dW_i>^2 = (v_i^T W^T G v_i)^2,
+    which grows with the component's magnitude W v_i and its alignment with the gradient.  Computed
+    as the diagonal of V_k^T (W^T G) V_k in fp64.
+    """
+    Vk = np.asarray(V, dtype=np.float64)[:, :k]
+    M = W64.T @ G64
+    d = np.einsum("ri,ri->i", Vk, M @ Vk)
+    return d * d
+
+
+def allocate_components(scores, cost, budget: int, k_min=None) -> tuple[np.ndarray, list, int]:
+    """Greedy selection of single components by importance per parameter (LASER page, method 2).
+
+    Candidates are the components i = k_min_m+1 .. K_m of every matrix m (K_m = len(scores[m]));
+    the first k_min_m components of m (largest eigenvalues) are kept and charged first.  Priority
+    p = s_{m,i} / cost_m (one IEEE fp64 division); candidates are taken in (p desc, m asc, i asc)
+    order while they fit and the first that does not ends the scan.  The taken components of a
+    matrix need not be its leading ones: the result is k_m and, per matrix, the mask of kept
+    components.  Returns (k, masks, info): info 4 when the minima exceed the budget, 5 for a
+    negative or NaN score, a cost <= 0 or a k_min outside [0, K_m].
+    """
+    M = len(scores)
+    sc = [np.asarray(x, dtype=np.float64) for x in scores]
+    k_min = [0] * M if k_min is None else [int(v) for v in k_min]
+    cost = [int(c) for c in cost]
+    masks = [np.zeros(len(x), dtype=bool) for x in sc]
+    if (any(np.any(~(x >= 0.0)) for x in sc) or any(c <= 0 for c in cost)
+            or any(k_min[m] < 0 or k_min[m] > len(sc[m]) for m in range(M))):
+        return np.array(k_min, dtype=np.int64), masks, 5
+    for m in range(M):
+        masks[m][:k_min[m]] = True
+    rem = int(budget) - sum(k_min[m] * cost[m] for m in range(M))
+    if rem < 0:
+        return np.array(k_min, dtype=np.int64), masks, 4
+    p, mm, ii = [], [], []
+    for m in range(M):
+        idx = np.arange(k_min[m], len(sc[m]))
+        p.append(sc[m][idx] / np.float64(cost[m]))
+        mm.append(np.full(idx.shape, m, dtype=np.int64))
+        ii.append(idx.astype(np.int64))
+    p, mm, ii = np.concatenate(p), np.concatenate(mm), np.concatenate(ii)
+    order = np.lexsort((ii, mm, -p))
+    k = list(k_min)
+    for j in order:
+        c = cost[mm[j]]
+        if c > rem:
+            break
+        rem -= c
+        k[mm[j]] += 1
+        masks[mm[j]][ii[j]] = True
+    return np.array(k, dtype=np.int64), masks, 0
 
 
 # ----------------------------------------------------------------------------------------------

@@ -214,6 +214,55 @@ def test_eig_nonconvergence_is_reported():
         oracle.eigh(C, max_sweeps=1)
 
 
+def test_eig_from_identity_basis_is_plain_jacobi():
+    C, _ = _spd(57, 10)
+    l1, V1 = oracle.eigh_from_basis(C, np.eye(57))
+    l2, V2 = oracle.eigh(C)
+    assert np.array_equal(l1, l2) and np.array_equal(V1, V2)
+
+
+@pytest.mark.parametrize("start", ["random", "permutation", "lapack"])
+def test_eig_from_basis_any_start_matches_lapack(start):
+    """The start basis only changes the number of sweeps: any orthogonal start gives the
+    eigenpairs of C (LAPACK on C as the independent check), with the same order and sign rule."""
+    n = 150
+    r = np.random.default_rng(12)
+    Z = r.standard_normal((3 * n, n)) * np.exp(r.standard_normal(n))
+    C = Z.T @ Z
+    if start == "random":
+        Q, _ = np.linalg.qr(r.standard_normal((n, n)))
+        lam, V = oracle.eigh_from_basis(C, Q)
+    elif start == "permutation":
+        lam, V = oracle.eigh_from_basis(C, np.eye(n)[:, r.permutation(n)])
+    else:
+        lam, V = oracle.eigh_large(C)
+    ref_l, ref_V = np.linalg.eigh(C)
+    ref_l, ref_V = ref_l[::-1], ref_V[:, ::-1]
+    assert np.max(np.abs(lam - ref_l)) <= 1e-12 * ref_l[0]
+    assert np.all(np.diff(lam) <= 0)
+    assert np.max(np.abs(V.T @ V - np.eye(n))) < 1e-13
+    assert np.linalg.norm(C @ V - V * lam) <= 1e-13 * np.linalg.norm(C)
+    sep = np.minimum(np.r_[np.inf, -np.diff(ref_l)], np.r_[-np.diff(ref_l), np.inf]) > 1e-6 * ref_l[0]
+    assert np.max(np.abs(np.abs(np.sum(V * ref_V, 0)) - 1)[sep]) < 1e-8
+    idx = np.argmax(np.abs(V), axis=0)
+    assert np.all(V[idx, np.arange(n)] > 0)
+
+
+def test_eig_large_agrees_with_plain_sweeps():
+    """At an order where both finish quickly, the started sweeps and the plain sweeps from the
+    identity agree on a block-shaped covariance (lognormal channel scales)."""
+    X = inputs.block_activations(96, 2048)
+    W = inputs.weight(96, 400, "bf16", inputs.CFG_BLOCK, 0, 9)
+    C = oracle.covariance(X, "bf16", W, "bf16")
+    l1, V1 = oracle.eigh_large(C)
+    l2, V2 = oracle.eigh(C)
+    assert np.max(np.abs(l1 - l2)) <= 1e-12 * l2[0]
+    k = 60
+    R = V1[:, :k] - V2[:, :k] @ (V2[:, :k].T @ V1[:, :k])
+    assert np.linalg.norm(R, 2) <= 1e-9
+    assert np.all(np.abs(l1[96:]) <= 1e-12 * l1[0])  # rank 96
+
+
 def test_eig_upper_triangle_reader():
     C, _ = _spd(12, 9)
     U = np.triu(C) + np.tril(np.full((12, 12), 1e9), -1)  # garbage below the diagonal
@@ -553,3 +602,187 @@ def test_allocate_proportional_invariants():
             order = np.argsort(a, kind="stable")
             assert np.all(np.diff(r[t][order]) >= 0) or len(set(a.tolist())) < len(a)
         assert np.all(np.diff(r, axis=0) <= 0 + 1)  # within one step of monotone per matrix
+
+
+# ---------------------------------------------------------------------------------------------
+# Swift-SVD allocation candidates (Swift-SVD page, section 2-na, strategy steps 1-2)
+# ---------------------------------------------------------------------------------------------
+
+def test_swift_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "swift_alloc_worked_example.json")))
+    for case in ex["cases"]:
+        k, info = oracle.swift_allocate(case["scores"], ex["kbar"], ex["cost"], ex["k_cap"], case["delta"],
+                                        case["budget"])
+        assert info == case["info"], case
+        assert list(k) == case["k"], case
+
+
+def test_swift_scores_special_cases():
+    beta = np.array([0.0, 0.5, 2.0, 7.25])
+    e = np.e
+    eps = np.array([0.0, e ** 3 - e, e ** 2 - e, 1e6])
+    assert np.array_equal(oracle.swift_scores(beta, eps, 1.0), beta)  # importance only
+    L = np.log(e + eps)
+    assert np.allclose(oracle.swift_scores(beta, eps, 0.0), L, rtol=1e-15)  # error only
+    assert oracle.swift_scores([3.0], [0.0], 0.4)[0] == 3.0 ** 0.4  # log(e + 0) = 1
+    s = oracle.swift_scores(beta[1:3], eps[1:3], 0.3)
+    assert np.allclose(s, beta[1:3] ** 0.3 * np.array([3.0, 2.0]) ** 0.7, rtol=1e-14)
+    assert np.all(oracle.swift_scores(beta, -np.ones(4), 0.5) == beta ** 0.5)  # negative residue counts as 0
+
+
+def _swift_exact(scores, kbar, cost, k_cap, delta_num, delta_den, budget):
+    """Water filling in exact rational arithmetic (scores are integers here)."""
+    from fractions import Fraction
+    M = len(scores)
+    kmin = [(kbar[i] * delta_num) // delta_den for i in range(M)]
+    E = budget - sum(kmin[i] * cost[i] for i in range(M))
+    x = [0] * M
+    open_ = [i for i in range(M) if kmin[i] < k_cap[i]]
+    committed = 0
+    while open_:
+        S = sum(scores[i] for i in open_)
+        if S == 0:
+            break
+        R = E - committed
+        q = {i: int(Fraction(scores[i] * R, S * cost[i])) for i in open_}
+        capped = [i for i in open_ if kmin[i] + q[i] >= k_cap[i]]
+        if not capped:
+            for i in open_:
+                x[i] = q[i]
+            break
+        for i in capped:
+            x[i] = k_cap[i] - kmin[i]
+            committed += x[i] * cost[i]
+        open_ = [i for i in open_ if i not in capped]
+    return [kmin[i] + x[i] for i in range(M)]
+
+
+def test_swift_allocate_matches_exact_water_filling():
+    r = np.random.default_rng(21)
+    for trial in range(200):
+        M = int(r.integers(1, 9))
+        scores = [int(v) for v in r.integers(0, 30, M)]
+        cost = [int(v) for v in r.integers(1, 12, M)]
+        k_cap = [int(v) for v in r.integers(1, 60, M)]
+        kbar = [int(r.integers(0, c + 1)) for c in k_cap]
+        delta = [0.0, 0.25, 0.5, 0.75, 1.0][int(r.integers(0, 5))]
+        total = sum(k_cap[i] * cost[i] for i in range(M))
+        budget = int(r.integers(0, total + 10))
+        k, info = oracle.swift_allocate([float(v) for v in scores], kbar, cost, k_cap, delta, budget)
+        kmin = [int(np.floor(kbar[i] * delta)) for i in range(M)]
+        if sum(kmin[i] * cost[i] for i in range(M)) > budget:
+            assert info == 4 and list(k) == kmin
+            continue
+        assert info == 0
+        assert list(k) == _swift_exact(scores, kbar, cost, k_cap, int(delta * 4), 4, budget), trial
+
+
+def test_swift_allocate_invariants():
+    r = np.random.default_rng(22)
+    for trial in range(100):
+        M = int(r.integers(1, 40))
+        scores = r.lognormal(0.0, 1.5, M) * (r.random(M) > 0.1)
+        cost = r.integers(100, 5000, M)
+        k_cap = r.integers(10, 500, M)
+        kbar = (k_cap * r.uniform(0.3, 1.0, M)).astype(np.int64)
+        delta = float(r.uniform(0.0, 1.0))
+        budget = int(np.sum(kbar * cost))
+        k, info = oracle.swift_allocate(scores, kbar, cost, k_cap, delta, budget)
+        assert info == 0
+        kmin = np.floor(kbar * delta).astype(np.int64)
+        used = int(np.sum(k * cost))
+        assert np.all(k >= kmin) and np.all(k <= k_cap) and used <= budget
+        # no slack beyond the floors: each open matrix with a positive score loses < one rank's cost
+        open_ = (k < k_cap) & (scores > 0)
+        assert budget - used < max(1, int(np.sum(cost[open_]))) or not open_.any()
+        # a larger score never lowers that matrix's rank
+        j = int(r.integers(0, M))
+        s2 = scores.copy()
+        s2[j] *= 3.0
+        k2, _ = oracle.swift_allocate(s2, kbar, cost, k_cap, delta, budget)
+        assert k2[j] >= k[j]
+
+
+def test_swift_allocate_bad_inputs():
+    assert oracle.swift_allocate([1.0, np.nan], [1, 1], [2, 2], [3, 3], 0.5, 10)[1] == 5
+    assert oracle.swift_allocate([1.0, -1.0], [1, 1], [2, 2], [3, 3], 0.5, 10)[1] == 5
+    assert oracle.swift_allocate([1.0, 1.0], [1, 4], [2, 2], [3, 3], 0.5, 10)[1] == 5  # kbar > k_cap
+    assert oracle.swift_allocate([1.0, 1.0], [1, 1], [2, 0], [3, 3], 0.5, 10)[1] == 5
+    assert oracle.swift_allocate([1.0, 1.0], [1, 1], [2, 2], [3, 3], 1.5, 10)[1] == 5
+
+
+# ---------------------------------------------------------------------------------------------
+# LASER per-component empirical-Fisher score and its greedy (LASER page, method 2)
+# ---------------------------------------------------------------------------------------------
+
+def test_component_fisher_is_loss_of_removing_the_component():
+    """<G, dW_i>^2 with dW_i = W v_i v_i^T built explicitly (the change that dropping component i
+    makes), on a small matrix; plus G = c W, where the score is c^2 ||W v_i||^4."""
+    r = np.random.default_rng(23)
+    W = r.standard_normal((9, 7))
+    G = r.standard_normal((9, 7)) * 1e-3
+    V, _ = np.linalg.qr(r.standard_normal((7, 7)))
+    s = oracle.component_fisher(W, G, V, 5)
+    ref = [float(np.sum(G * (W @ np.outer(V[:, i], V[:, i])))) ** 2 for i in range(5)]
+    assert np.allclose(s, ref, rtol=1e-12)
+    s2 = oracle.component_fisher(W, -2.5 * W, V, 7)
+    assert np.allclose(s2, 6.25 * np.linalg.norm(W @ V, axis=0) ** 4, rtol=1e-12)
+    s3 = oracle.component_fisher(W, G, np.eye(7), 7)  # the standard basis: column inner products
+    assert np.allclose(s3, np.sum(W * G, axis=0) ** 2, rtol=1e-12)
+
+
+def test_component_alloc_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "component_alloc_worked_example.json")))
+    for case in ex["cases"]:
+        k, masks, info = oracle.allocate_components(ex["scores"], ex["cost"], case["budget"], case["k_min"])
+        assert info == case["info"], case
+        assert list(k) == case["k"], case
+        assert [list(m.astype(int)) for m in masks] == case["masks"], case
+
+
+def _component_greedy_by_definition(scores, cost, budget, k_min):
+    """Repeatedly take the best remaining component (highest s / cost as exact rationals of the fp64
+    values; ties: lower matrix, lower component) while it fits; stop at the first that does not."""
+    from fractions import Fraction
+    M = len(scores)
+    rem = budget - sum(k_min[m] * cost[m] for m in range(M))
+    masks = [[i < k_min[m] for i in range(len(scores[m]))] for m in range(M)]
+    if rem < 0:
+        return None
+    cand = [(Fraction(float(np.float64(scores[m][i]) / np.float64(cost[m]))), m, i)
+            for m in range(M) for i in range(k_min[m], len(scores[m]))]
+    while cand:
+        best = max(cand, key=lambda t: (t[0], -t[1], -t[2]))
+        if cost[best[1]] > rem:
+            break
+        rem -= cost[best[1]]
+        masks[best[1]][best[2]] = True
+        cand.remove(best)
+    return masks
+
+
+def test_component_alloc_equals_greedy_definition_random():
+    r = np.random.default_rng(24)
+    for trial in range(60):
+        M = int(r.integers(1, 5))
+        scores = [np.round(r.lognormal(0, 1, int(r.integers(1, 7))), 1) for _ in range(M)]
+        if trial % 3 == 0:  # ties
+            scores = [np.floor(x) for x in scores]
+        cost = [int(v) for v in r.integers(1, 6, M)]
+        k_min = [int(r.integers(0, len(x) + 1)) if r.random() < 0.3 else 0 for x in scores]
+        budget = int(r.integers(0, 40))
+        k, masks, info = oracle.allocate_components(scores, cost, budget, k_min)
+        ref = _component_greedy_by_definition(scores, cost, budget, k_min)
+        if ref is None:
+            assert info == 4
+            continue
+        assert info == 0
+        assert [list(m) for m in masks] == ref, trial
+        assert list(k) == [int(np.sum(m)) for m in ref]
+        assert sum(k[m] * cost[m] for m in range(M)) <= budget
+
+
+def test_component_alloc_bad_scores():
+    assert oracle.allocate_components([[1.0, np.nan]], [2], 10)[2] == 5
+    assert oracle.allocate_components([[1.0, -0.5]], [2], 10)[2] == 5
+    assert oracle.allocate_components([[1.0]], [0], 10)[2] == 5
