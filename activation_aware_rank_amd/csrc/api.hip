@@ -333,6 +333,63 @@ lrc_status lrc_allocate_proportional(int32_t n_mats, const double *alpha, int32_
     return alloc_prop_run(n_mats, alpha, n_budgets, budgets, r_out, info, static_cast<hipStream_t>(stream));
 }
 
+lrc_status lrc_allocate_swift(int32_t n_mats, const double *beta, const double *eps_kbar, const int64_t *kbar,
+                              const int64_t *cost, const int64_t *k_cap, double delta, int32_t n_alpha,
+                              const double *alpha_grid, int64_t budget_params, double *scores, int32_t *k_out,
+                              int32_t *info, void *stream) {
+    REQUIRE(beta && eps_kbar && kbar && cost && k_cap && alpha_grid && scores && k_out && info, LRC_ERR_ARG,
+            "null argument");
+    REQUIRE(n_mats > 0 && n_mats <= 1024, LRC_ERR_ARG, "n_mats must be in 1 .. 1024");
+    REQUIRE(n_alpha > 0 && n_alpha <= 65535, LRC_ERR_ARG, "n_alpha must be in 1 .. 65535");
+    REQUIRE(budget_params >= 0, LRC_ERR_ARG, "negative budget");
+    return alloc_swift_run(n_mats, beta, eps_kbar, kbar, cost, k_cap, delta, n_alpha, alpha_grid, budget_params,
+                           scores, k_out, info, static_cast<hipStream_t>(stream));
+}
+
+size_t lrc_component_fisher_workspace(int64_t d_in, int64_t k, int64_t batch) {
+    return (d_in > 0 && k > 0 && batch > 0) ? comp_fisher_workspace(d_in, k, batch) : 0;
+}
+
+lrc_status lrc_component_fisher(const void *W, const void *G, lrc_dtype t, int64_t d_in, int64_t d_out, int64_t ldw,
+                                int64_t ldg, const float *V, int64_t ldv, int64_t k, int64_t batch, int64_t stride_w,
+                                int64_t stride_g, int64_t stride_v, double *score, int64_t stride_s, void *ws,
+                                size_t ws_bytes, void *stream) {
+    REQUIRE(W && G && V && score, LRC_ERR_ARG, "null argument");
+    REQUIRE(t == LRC_BF16 || t == LRC_F32, LRC_ERR_DTYPE, "W and G must be bf16 or fp32");
+    REQUIRE(d_in > 0 && d_out > 0 && k > 0 && k <= d_out && batch > 0, LRC_ERR_ARG, "bad sizes");
+    REQUIRE(ldw >= d_out && ldg >= d_out && ldv >= k, LRC_ERR_ARG, "bad leading dims");
+    REQUIRE(batch == 1 || (stride_w >= 0 && stride_g >= 0 && stride_v >= 0 && stride_s >= k), LRC_ERR_ARG,
+            "bad batch strides");
+    const size_t need = comp_fisher_workspace(d_in, k, batch);
+    REQUIRE(ws && ws_bytes >= need && aligned(ws, 256), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_component_fisher_workspace() or not 256-byte aligned");
+    CompFisherArgs a{W, G, t, d_in, d_out, ldw, ldg, V, ldv, k, batch, stride_w, stride_g, stride_v, score,
+                     batch == 1 ? k : stride_s};
+    return comp_fisher_run(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t lrc_allocate_components_workspace(int32_t n_mats, int64_t n_items) {
+    if (n_mats <= 0 || n_items < 0) return 0;
+    return alloc_workspace(n_mats, n_items);
+}
+
+lrc_status lrc_allocate_components(int32_t n_mats, const double *score_packed, const int64_t *offsets,
+                                   int64_t n_items, const int64_t *cost, const int32_t *k_min, int64_t budget_params,
+                                   int32_t *k_out, uint8_t *selected, void *ws, size_t ws_bytes, int32_t *info,
+                                   void *stream) {
+    REQUIRE(n_mats > 0 && offsets && cost && k_out && info, LRC_ERR_ARG, "null argument or n_mats <= 0");
+    REQUIRE(n_items >= 0 && (n_items == 0 || score_packed), LRC_ERR_ARG, "bad n_items or score_packed");
+    REQUIRE(n_items < (int64_t(1) << 31), LRC_ERR_ARG, "n_items too large");
+    REQUIRE(budget_params >= 0, LRC_ERR_ARG, "negative budget");
+    size_t need = alloc_workspace(n_mats, n_items);
+    REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned(ws, 256))), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_allocate_components_workspace() or not 256-byte aligned");
+    AllocArgs a{n_mats, nullptr, score_packed, offsets, n_items, nullptr, cost, k_min, budget_params, k_out, info};
+    a.per_component = 1;
+    a.selected = selected;
+    return alloc_run(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------------------------------------
 size_t lrc_cholesky_workspace(int64_t n) { return n > 0 ? cholesky_workspace(n) : 0; }
 

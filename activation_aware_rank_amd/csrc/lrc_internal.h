@@ -163,6 +163,8 @@ struct AllocArgs {
     int64_t budget;
     int32_t *k_out;
     int32_t *info;
+    int per_component = 0;       // 1: lambda_packed holds per-component scores, p = s / cost
+    uint8_t *selected = nullptr;  // optional mask of kept components, one byte per item
 };
 size_t alloc_workspace(int32_t n_mats, int64_t n_items);
 lrc_status alloc_run(const AllocArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
@@ -182,6 +184,23 @@ lrc_status to_f64_run(const void *X, lrc_dtype t, int64_t rows, int64_t cols, in
                       double *Y, int64_t ldy, hipStream_t s);
 // C = op(A) op(B) in fp64 (ta, tb: 0 plain, 1 transposed; tiles 0 all, 1 lower, 2 upper); with Cf the
 // product goes to Cf as fp32 instead
+// Swift-SVD allocation candidates (one per alpha of a grid)
+lrc_status alloc_swift_run(int32_t n, const double *beta, const double *eps_kbar, const int64_t *kbar,
+                           const int64_t *cost, const int64_t *k_cap, double delta, int32_t n_alpha,
+                           const double *alpha_grid, int64_t budget, double *scores, int32_t *k_out, int32_t *info,
+                           hipStream_t s);
+// per-component empirical-Fisher scores s_i = ((W v_i) . (G v_i))^2
+struct CompFisherArgs {
+    const void *W, *G;
+    lrc_dtype t;
+    int64_t d_in, d_out, ldw, ldg;
+    const float *V;
+    int64_t ldv, k, batch, stride_w, stride_g, stride_v;
+    double *score;
+    int64_t stride_s;
+};
+size_t comp_fisher_workspace(int64_t d_in, int64_t k, int64_t batch);
+lrc_status comp_fisher_run(const CompFisherArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
 constexpr int PROP_MAX = 1024;  // matrices per proportional allocation
 lrc_status alloc_prop_run(int32_t n, const double *alpha, int32_t nb, const int64_t *budgets, int64_t *r_out,
                           int32_t *info, hipStream_t s);

@@ -4,7 +4,8 @@
 //    eigenvalues beyond k).
 //  * Fisher importance: FLRC page, method 1 (alpha_{l,p} = sum_i (G[i] W[i])^2).
 //  * greedy allocation: LASER page, method 2 (take components of highest importance per
-//    parameter until the budget is reached), Swift-SVD page, section 2-na (minimum rank).
+//    parameter until the budget is reached), Swift-SVD page, section 2-na (minimum rank); the
+//    same scan over per-component empirical-Fisher scores (LASER page, method 2).
 #include <cmath>
 #include <algorithm>
 #include <cstring>
@@ -223,6 +224,33 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t *sh) {
     return r;  // valid in every thread
 }
 
+// Marks the kept items of each matrix (one thread per matrix, its items in k order): the first
+// k_min always; with how == 1 every candidate; with how == 2 the candidates with p > t* and the first
+// take[m] of those with p == t*.
+__device__ void alloc_mark(int32_t n_mats, const int64_t *offsets, const int32_t *k_min, const double *p, int how,
+                           double tstar, const int32_t *take, uint8_t *selected) {
+    for (int m = threadIdx.x; m < n_mats; m += blockDim.x) {
+        const int64_t j0 = offsets[m], j1 = offsets[m + 1];
+        const int32_t km = k_min ? k_min[m] : 0;
+        int32_t ties = how == 2 ? __hip_atomic_load(&take[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        for (int64_t j = j0; j < j1; ++j) {
+            bool keep = j - j0 < km;
+            if (!keep && how == 1) keep = true;
+            if (!keep && how == 2) {
+                const double pj = p[j];
+                if (pj > tstar) keep = true;
+                else if (pj == tstar && ties > 0) { keep = true; --ties; }
+            }
+            selected[j] = keep ? 1 : 0;
+        }
+    }
+}
+
+// MODE 0: p = w_m max(lambda, 0) with w_m = alpha_m / (eps0_m cost_m) (Fisher-weighted eigenvalues).
+// MODE 1: p = s / cost_m with s = lam[j] a per-component score (alpha and eps0 unused); a negative or
+//         NaN score is a bad score.
+// selected (optional): one byte per item, 1 for the kept components.
+template <int MODE>
 __global__ void __launch_bounds__(ALC_THREADS) k_allocate(int32_t n_mats, const double *__restrict__ alpha,
                                                           const double *__restrict__ lam, const int64_t *__restrict__ offsets,
                                                           int64_t n_items, const double *__restrict__ eps0,
@@ -230,7 +258,7 @@ __global__ void __launch_bounds__(ALC_THREADS) k_allocate(int32_t n_mats, const 
                                                           int64_t budget, int32_t *__restrict__ k_out, int32_t *__restrict__ info,
                                                           double *__restrict__ wm, double *__restrict__ p,
                                                           int32_t *__restrict__ item_m, int32_t *__restrict__ cnt_above,
-                                                          int32_t *__restrict__ cnt_tie) {
+                                                          int32_t *__restrict__ cnt_tie, uint8_t *__restrict__ selected) {
     __shared__ int64_t sh[ALC_THREADS / 64];
     __shared__ int bad;
     const int tid = threadIdx.x;
@@ -239,15 +267,19 @@ __global__ void __launch_bounds__(ALC_THREADS) k_allocate(int32_t n_mats, const 
     // 1. weights, validity, mandatory ranks
     int64_t mand = 0;
     for (int m = tid; m < n_mats; m += ALC_THREADS) {
-        const double a = alpha[m], e0 = eps0[m];
         const int64_t c = cost[m];
         double w = 0.0;
-        if (!(a >= 0.0) || !(e0 >= 0.0) || c <= 0) {
+        if (MODE == 0) {
+            const double a = alpha[m], e0 = eps0[m];
+            if (!(a >= 0.0) || !(e0 >= 0.0) || c <= 0) {
+                atomicOr(&bad, 1);
+            } else if (e0 != 0.0) {
+                const double t = e0 * double(c);
+                w = a / t;
+                if (!isfinite(w)) atomicOr(&bad, 1);
+            }
+        } else if (c <= 0) {
             atomicOr(&bad, 1);
-        } else if (e0 != 0.0) {
-            const double t = e0 * double(c);
-            w = a / t;
-            if (!isfinite(w)) atomicOr(&bad, 1);
         }
         wm[m] = w;
         const int32_t km = k_min ? k_min[m] : 0;
@@ -270,19 +302,20 @@ __global__ void __launch_bounds__(ALC_THREADS) k_allocate(int32_t n_mats, const 
         const int64_t k = j - offsets[m] + 1;
         const int32_t km = k_min ? k_min[m] : 0;
         const double l = lam[j];
-        if (isnan(l)) atomicOr(&bad, 1);
         item_m[j] = m;
-        p[j] = (k > km) ? wm[m] * (l > 0.0 ? l : 0.0) : -1.0;
+        if (MODE == 0) {
+            if (isnan(l)) atomicOr(&bad, 1);
+            p[j] = (k > km) ? wm[m] * (l > 0.0 ? l : 0.0) : -1.0;
+        } else {
+            if (!(l >= 0.0)) atomicOr(&bad, 1);
+            p[j] = (k > km) ? l / double(cost[m]) : -1.0;
+        }
     }
     __syncthreads();
-    if (bad) {
+    if (bad || mand > budget) {
         for (int m = tid; m < n_mats; m += ALC_THREADS) k_out[m] = k_min ? k_min[m] : 0;
-        if (tid == 0) *info = LRC_INFO_BAD_SCORE;
-        return;
-    }
-    if (mand > budget) {
-        for (int m = tid; m < n_mats; m += ALC_THREADS) k_out[m] = k_min ? k_min[m] : 0;
-        if (tid == 0) *info = LRC_INFO_BUDGET;
+        if (selected) alloc_mark(n_mats, offsets, k_min, p, 0, 0.0, cnt_tie, selected);
+        if (tid == 0) *info = bad ? LRC_INFO_BAD_SCORE : LRC_INFO_BUDGET;
         return;
     }
     const int64_t rem = budget - mand;
@@ -294,6 +327,7 @@ __global__ void __launch_bounds__(ALC_THREADS) k_allocate(int32_t n_mats, const 
     if (tot <= rem) {
         for (int m = tid; m < n_mats; m += ALC_THREADS)
             k_out[m] = int32_t(offsets[m + 1] - offsets[m]);
+        if (selected) alloc_mark(n_mats, offsets, k_min, p, 1, 0.0, cnt_tie, selected);
         if (tid == 0) *info = LRC_INFO_OK;
         return;
     }
@@ -349,6 +383,7 @@ __global__ void __launch_bounds__(ALC_THREADS) k_allocate(int32_t n_mats, const 
         k_out[m] = (k_min ? k_min[m] : 0) +
                    __hip_atomic_load(&cnt_above[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
                    __hip_atomic_load(&cnt_tie[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (selected) alloc_mark(n_mats, offsets, k_min, p, 2, tstar, cnt_tie, selected);
     if (tid == 0) *info = LRC_INFO_OK;
 }
 
@@ -447,8 +482,14 @@ lrc_status alloc_run(const AllocArgs &a, void *ws, size_t ws_bytes, hipStream_t 
     int32_t *ca = cv.carve<int32_t>(size_t(a.n_mats));
     int32_t *ct = cv.carve<int32_t>(size_t(a.n_mats));
     if (!ct) return fail(LRC_ERR_WORKSPACE, "allocation workspace too small");
-    hipLaunchKernelGGL(k_allocate, dim3(1), dim3(ALC_THREADS), 0, s, a.n_mats, a.alpha, a.lambda_packed, a.offsets,
-                       a.n_items, a.eps0, a.cost, a.k_min, a.budget, a.k_out, a.info, wm, p, im, ca, ct);
+    if (a.per_component)
+        hipLaunchKernelGGL(k_allocate<1>, dim3(1), dim3(ALC_THREADS), 0, s, a.n_mats, a.alpha, a.lambda_packed,
+                           a.offsets, a.n_items, a.eps0, a.cost, a.k_min, a.budget, a.k_out, a.info, wm, p, im, ca, ct,
+                           a.selected);
+    else
+        hipLaunchKernelGGL(k_allocate<0>, dim3(1), dim3(ALC_THREADS), 0, s, a.n_mats, a.alpha, a.lambda_packed,
+                           a.offsets, a.n_items, a.eps0, a.cost, a.k_min, a.budget, a.k_out, a.info, wm, p, im, ca, ct,
+                           a.selected);
     LRC_LAUNCH_CHECK("k_allocate");
     return LRC_OK;
 }

@@ -64,6 +64,13 @@ _gram64 = _sig("lrc_gram_f64", _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp)
 _cfi_ws = _sig("lrc_cov_from_input_workspace", _sz, _i64, _i64)
 _aprop = _sig("lrc_allocate_proportional", _int, _i32, _vp, _i32, _vp, _vp, _vp, _vp)
 _cfi = _sig("lrc_cov_from_input", _int, _vp, _i64, _i64, _vp, _int, _i64, _i64, _vp, _i64, _vp, _sz, _vp)
+_aswift = _sig("lrc_allocate_swift", _int, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_double, _i32, _vp, _i64, _vp, _vp,
+               _vp, _vp)
+_cfsh_ws = _sig("lrc_component_fisher_workspace", _sz, _i64, _i64, _i64)
+_cfsh = _sig("lrc_component_fisher", _int, _vp, _vp, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+             _i64, _vp, _i64, _vp, _sz, _vp)
+_acomp_ws = _sig("lrc_allocate_components_workspace", _sz, _i32, _i64)
+_acomp = _sig("lrc_allocate_components", _int, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp, _vp)
 _tim_en = _sig("lrc_timing_enable", _int, _int)
 _tim_st = _sig("lrc_timing_set_stride", _int, ctypes.c_char_p, _int)
 _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
@@ -72,10 +79,13 @@ _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c
 EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_accumulate_workspace",
             "lrc_cov_accumulate", "lrc_eigh_workspace", "lrc_eigh", "lrc_eigh_multi_workspace", "lrc_eigh_multi",
             "lrc_error_curve", "lrc_factorize",
-            "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_allocate_ranks_workspace",
+            "lrc_fisher_scores_workspace", "lrc_fisher_scores",
+            "lrc_allocate_ranks_workspace",
             "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm_workspace", "lrc_trmm",
             "lrc_trsm_workspace", "lrc_trsm", "lrc_sym_to_f64", "lrc_to_f64", "lrc_gram_f64",
             "lrc_cov_from_input_workspace", "lrc_cov_from_input", "lrc_allocate_proportional",
+            "lrc_allocate_swift", "lrc_component_fisher_workspace", "lrc_component_fisher",
+            "lrc_allocate_components_workspace", "lrc_allocate_components",
             "lrc_timing_enable", "lrc_timing_set_stride", "lrc_timing_read")
 
 
@@ -501,3 +511,83 @@ def lrc_allocate_proportional(alpha: torch.Tensor, budgets: torch.Tensor, r_out=
     info = _info(info, 1, alpha.device)
     _check(_aprop(n, _ptr(alpha), nb, _ptr(budgets), _ptr(r_out), _ptr(info), _stream(stream)))
     return r_out, info
+
+
+def _vec(t: torch.Tensor, name: str, dtype):
+    _dev(t, name)
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s GPU tensor" % (name, dtype))
+
+
+def lrc_allocate_swift(beta, eps_kbar, kbar, cost, k_cap, delta: float, alpha_grid, budget: int, scores=None,
+                       k_out=None, info=None, stream=None):
+    """Swift-SVD candidate allocations, one per alpha of the grid (see include/lrc.h).  beta, eps_kbar,
+    alpha_grid fp64; kbar, cost, k_cap int64; all GPU vectors.  Returns (scores fp64 (n_alpha, n),
+    k int32 (n_alpha, n), info int32 (n_alpha,))."""
+    for t, nm in ((beta, "beta"), (eps_kbar, "eps_kbar"), (alpha_grid, "alpha_grid")):
+        _vec(t, nm, torch.float64)
+    for t, nm in ((kbar, "kbar"), (cost, "cost"), (k_cap, "k_cap")):
+        _vec(t, nm, torch.int64)
+    n, na = beta.numel(), alpha_grid.numel()
+    if not (eps_kbar.numel() == kbar.numel() == cost.numel() == k_cap.numel() == n):
+        raise ValueError("per-matrix vectors must have the same length")
+    dev = beta.device
+    if scores is None:
+        scores = torch.empty(na, n, dtype=torch.float64, device=dev)
+    if k_out is None:
+        k_out = torch.empty(na, n, dtype=torch.int32, device=dev)
+    info = _info(info, na, dev)
+    _check(_aswift(n, _ptr(beta), _ptr(eps_kbar), _ptr(kbar), _ptr(cost), _ptr(k_cap), float(delta), na,
+                   _ptr(alpha_grid), int(budget), _ptr(scores), _ptr(k_out), _ptr(info), _stream(stream)))
+    return scores, k_out, info
+
+
+def lrc_component_fisher_workspace(d_in: int, k: int, batch: int = 1) -> int:
+    return _cfsh_ws(d_in, k, batch)
+
+
+def lrc_component_fisher(W: torch.Tensor, G: torch.Tensor, V: torch.Tensor, k: int, score=None, d_in=None, d_out=None,
+                         batch: int = 1, stride_w: int = 0, stride_g: int = 0, stride_v: int = 0, stride_s: int = 0,
+                         ws=None, stream=None) -> torch.Tensor:
+    """score[b][i] = ((W v_i) . (G v_i))^2 for the first k columns of V (fp64); batched by element strides."""
+    ldw, ldg, ldv = _rows(W, "W"), _rows(G, "G"), _rows(V, "V")
+    if W.dtype != G.dtype:
+        raise TypeError("W and G must have the same dtype")
+    if V.dtype != torch.float32:
+        raise TypeError("V must be float32")
+    d_in = W.shape[-2] if d_in is None else d_in
+    d_out = W.shape[-1] if d_out is None else d_out
+    if score is None:
+        score = torch.empty(batch, k, dtype=torch.float64, device=W.device)
+        stride_s = k
+    w, wn = _workspace(_cfsh_ws(d_in, k, batch), W.device, ws)
+    _check(_cfsh(_ptr(W), _ptr(G), _dt(W), d_in, d_out, ldw, ldg, _ptr(V), ldv, k, batch, stride_w, stride_g,
+                 stride_v, _ptr(score), stride_s, _ptr(w), wn, _stream(stream)))
+    return score
+
+
+def lrc_allocate_components_workspace(n_mats: int, n_items: int) -> int:
+    return _acomp_ws(n_mats, n_items)
+
+
+def lrc_allocate_components(score_packed, offsets, cost, budget: int, k_min=None, k_out=None, selected=None,
+                            info=None, ws=None, stream=None):
+    """Greedy selection of single components by score per parameter (see include/lrc.h).  Returns
+    (k int32 per matrix, selected uint8 per component, info int32 (1,))."""
+    _vec(score_packed, "score_packed", torch.float64)
+    _vec(offsets, "offsets", torch.int64)
+    _vec(cost, "cost", torch.int64)
+    if k_min is not None:
+        _vec(k_min, "k_min", torch.int32)
+    n = cost.numel()
+    n_items = score_packed.numel()
+    dev = cost.device
+    w, wn = _workspace(_acomp_ws(n, n_items), dev, ws)
+    if k_out is None:
+        k_out = torch.empty(n, dtype=torch.int32, device=dev)
+    if selected is None:
+        selected = torch.empty(max(n_items, 1), dtype=torch.uint8, device=dev)
+    info = _info(info, 1, dev)
+    _check(_acomp(n, _ptr(score_packed), _ptr(offsets), n_items, _ptr(cost), _ptr(k_min), int(budget), _ptr(k_out),
+                  _ptr(selected), _ptr(w), wn, _ptr(info), _stream(stream)))
+    return k_out, selected[:n_items], info

@@ -302,6 +302,88 @@ lrc_status lrc_allocate_proportional(int32_t n_mats, const double *alpha, int32_
                                      const int64_t *budgets, int64_t *r_out, int32_t *info, void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * Swift-SVD allocation candidates (Swift-SVD page, section 2-na, dynamic rank allocation: step 1
+ * scores each matrix by s_i = beta_i^alpha * log(e + eps_{kbar,i})^(1 - alpha), combining its
+ * importance beta_i with its closed-form error at the uniform rank; step 2 keeps a minimum rank
+ * kbar * delta per matrix; step 3 compares candidates over a grid of alpha -- that selection, by
+ * validation loss, is the caller's).
+ *
+ * beta: n_mats fp64 importances (e.g. lrc_fisher_scores' alpha).  eps_kbar: n_mats fp64, matrix
+ *    i's error eps_i[kbar_i] from lrc_error_curve (a negative rounding residue counts as 0).
+ * kbar: n_mats int64 uniform ranks, 0 <= kbar_i <= k_cap_i; cost: n_mats int64 parameters per
+ *    rank (d_in + d_out, > 0); k_cap: n_mats int64 largest ranks.  delta in [0, 1].
+ * alpha_grid: n_alpha fp64 values in [0, 1] (device), one candidate allocation each.
+ * scores: n_alpha x n_mats fp64 (row a for alpha_grid[a]); k_out: n_alpha x n_mats int32 ranks.
+ * Ranks (a reading, the page does not print the rule): k_i = floor(kbar_i delta) + extra_i, where
+ *    the parameters left after the minima, E = budget - sum floor(kbar_i delta) cost_i, are split
+ *    in proportion to the scores: with S the index-order sum of the scores of the matrices still
+ *    open and R the parameters not yet committed, extra_i = floor(((s_i R) / S) / cost_i) (fp64,
+ *    one operation at a time); a matrix whose rank would reach k_cap_i is set to k_cap_i and
+ *    closed, and the split is redone among the others until none reaches its cap.  If rounding
+ *    ever made the total exceed the budget, the open matrices of highest index give ranks back.
+ *    pow and log are the device's fp64 functions; the ranks are bit-exact against a sequential
+ *    evaluation given the same scores.
+ * info: n_alpha int32: 0; 4 when the minima exceed the budget (k = minima); 5 when a score is
+ *    negative, NaN or infinite, a kbar lies outside [0, k_cap], a cost is <= 0, or alpha or delta
+ *    lies outside [0, 1] (k = 0).
+ * Errors: LRC_ERR_ARG (NULL pointers, n_mats outside 1 .. 1024, n_alpha outside 1 .. 65535,
+ *    negative budget).
+ * ------------------------------------------------------------------------------------ */
+lrc_status lrc_allocate_swift(int32_t n_mats, const double *beta, const double *eps_kbar, const int64_t *kbar,
+                              const int64_t *cost, const int64_t *k_cap, double delta, int32_t n_alpha,
+                              const double *alpha_grid, int64_t budget_params, double *scores, int32_t *k_out,
+                              int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Per-component empirical-Fisher importance (LASER page, method 2: each singular component is
+ * scored by its contribution to the empirical-Fisher quadratic loss, from the component's
+ * magnitude and its alignment with the calibration gradient).
+ *
+ *   score[b][i] = ((W v_i) . (G v_i))^2 = <G, W v_i v_i^T>^2,  i < k,
+ *
+ * the squared first-order loss change of removing component i (W v_i v_i^T) of the truncation
+ * W_k = (W V_k) V_k^T (a reading: the page does not print the score).
+ * W, G: d_in x d_out of dtype t (LRC_BF16 or LRC_F32; G the calibration gradient of W), leading
+ *    dims ldw, ldg >= d_out.  V: d_out x (>= k) fp32 (lrc_eigh's V), leading dim ldv >= k.
+ * Batched: matrix b uses W + b stride_w, G + b stride_g, V + b stride_v, score + b stride_s.
+ * score: fp64.  Arithmetic: W V_k and G V_k in fp64 (inputs widened exactly, fp64 MFMA), the dot
+ *    products in fp64 with a fixed-order reduction.
+ * ws: lrc_component_fisher_workspace(d_in, k, batch) bytes, 256-byte aligned (fp64 partial dot
+ *    products per 64-row tile).
+ * Errors: LRC_ERR_ARG, LRC_ERR_DTYPE, LRC_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_component_fisher_workspace(int64_t d_in, int64_t k, int64_t batch);
+lrc_status lrc_component_fisher(const void *W, const void *G, lrc_dtype t, int64_t d_in, int64_t d_out, int64_t ldw,
+                                int64_t ldg, const float *V, int64_t ldv, int64_t k, int64_t batch, int64_t stride_w,
+                                int64_t stride_g, int64_t stride_v, double *score, int64_t stride_s, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Greedy selection of single components (LASER page, method 2: the components of highest
+ * importance score per parameter cost are taken until the parameter budget is reached).
+ *
+ * score_packed: fp64 per-component scores, matrix m's K_m = offsets[m+1] - offsets[m] scores at
+ *    offsets[m] in component order (e.g. lrc_component_fisher's output).  cost: n_mats int64 (> 0)
+ *    parameters per component (d_in + d_out).  k_min: n_mats int32 or NULL: the first k_min[m]
+ *    components of m are kept and charged first.
+ * Candidates are the other components, priority p = score / cost_m (one IEEE fp64 division),
+ *    ordered by p descending, then m ascending, then component ascending, taken while they fit in
+ *    the budget; the first that does not fit ends the scan.  The kept components of a matrix need
+ *    not be its leading ones.
+ * k_out: n_mats int32 numbers of kept components; selected: n_items bytes (device) or NULL, 1 for
+ *    a kept component.
+ * info: one int32: 4 mandatory components exceed the budget (k = k_min), 5 a score negative or
+ *    NaN, a cost <= 0 or a k_min outside [0, K_m].
+ * ws: lrc_allocate_components_workspace(n_mats, n_items) bytes, 256-byte aligned.
+ * Bit-exact: the result depends only on the fp64 priorities, computed as stated.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_allocate_components_workspace(int32_t n_mats, int64_t n_items);
+lrc_status lrc_allocate_components(int32_t n_mats, const double *score_packed, const int64_t *offsets,
+                                   int64_t n_items, const int64_t *cost, const int32_t *k_min, int64_t budget_params,
+                                   int32_t *k_out, uint8_t *selected, void *ws, size_t ws_bytes, int32_t *info,
+                                   void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Curvature-weighted variant (LASER page, method 1: the loss increase of a perturbation dW
  * is approximated by 1/2 vec(dW)^T (G (x) X) vec(dW) with X, G the activation and gradient
  * covariances; W is moved to W~ = S_x W S_g with Cholesky factors S_x, S_g, truncated there

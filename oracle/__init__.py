@@ -397,7 +397,8 @@ def swift_scores(beta, eps_kbar, alpha: float) -> np.ndarray:
     e = np.asarray(eps_kbar, dtype=np.float64)
     out = np.empty(b.shape[0])
     for i in range(b.shape[0]):
-        L = math.log(math.e + max(float(e[i]), 0.0))
+        x = float(e[i])
+        L = math.log(math.e + (x if (math.isnan(x) or x > 0.0) else 0.0))  # NaN stays NaN
         out[i] = math.pow(float(b[i]), alpha) * math.pow(L, 1.0 - alpha)
     return out
 
@@ -414,15 +415,15 @@ def swift_allocate(scores, kbar, cost, k_cap, delta: float, budget: int) -> tupl
     R = the parameters not yet committed, and gives matrix i floor(((s_i * R) / S) / cost_i) more
     ranks (fp64, one operation at a time).  Should rounding ever overshoot the budget, the open
     matrix of highest index with an extra rank gives one back, until the total fits.
-    Returns (k, info): info 4 when the minima exceed the budget (k = minima), 5 for a negative or
-    NaN score, a kbar outside [0, k_cap], a cost <= 0 or delta outside [0, 1] (k = zeros).
+    Returns (k, info): info 4 when the minima exceed the budget (k = minima), 5 for a negative,
+    NaN or infinite score, a kbar outside [0, k_cap], a cost <= 0 or delta outside [0, 1] (k = zeros).
     """
     s = [float(x) for x in scores]
     kbar = [int(x) for x in kbar]
     cost = [int(x) for x in cost]
     k_cap = [int(x) for x in k_cap]
     M = len(s)
-    if (not (0.0 <= delta <= 1.0) or any(not (x >= 0.0) for x in s) or any(c <= 0 for c in cost)
+    if (not (0.0 <= delta <= 1.0) or any(not (0.0 <= x < math.inf) for x in s) or any(c <= 0 for c in cost)
             or any(kbar[i] < 0 or kbar[i] > k_cap[i] for i in range(M))):
         return np.zeros(M, dtype=np.int64), 5
     kmin = [int(math.floor(float(kbar[i]) * delta)) for i in range(M)]

@@ -159,3 +159,26 @@ def test_workspace_queries_are_consistent():
     assert lrc.lrc_eigh_multi_workspace([(11008, 1, 1791, 100)], 1) == big
     assert lrc.lrc_eigh_multi_workspace([(4096, 1, 1791, 1228)], 1) == lrc.lrc_eigh_workspace(4096, 1, 1791, 1)
     assert lrc.lrc_allocate_ranks_workspace(224, 548704) > 548704 * 8
+
+
+def test_allocation_scores_argument_errors():
+    from activation_aware_rank_amd import lrc
+    fake = ctypes.c_void_p(256)
+    # Swift-SVD candidates: NULL pointer, n_mats out of range, n_alpha 0, negative budget
+    assert lrc._aswift(3, None, fake, fake, fake, fake, 0.5, 2, fake, 10, fake, fake, fake, None) == 1
+    assert lrc._aswift(1025, fake, fake, fake, fake, fake, 0.5, 2, fake, 10, fake, fake, fake, None) == 1
+    assert lrc._aswift(3, fake, fake, fake, fake, fake, 0.5, 0, fake, 10, fake, fake, fake, None) == 1
+    assert lrc._aswift(3, fake, fake, fake, fake, fake, 0.5, 2, fake, -1, fake, fake, fake, None) == 1
+    # component scores: dtype, k > d_out, ldv < k, workspace
+    ws = lrc.lrc_component_fisher_workspace(100, 20, 1)
+    assert ws >= 2 * 20 * 8
+    assert lrc._cfsh(fake, fake, 2, 100, 50, 50, 50, fake, 20, 20, 1, 0, 0, 0, fake, 20, fake, ws, None) == 2
+    assert lrc._cfsh(fake, fake, 0, 100, 50, 50, 50, fake, 60, 60, 1, 0, 0, 0, fake, 60, fake, 1 << 30, None) == 1
+    assert lrc._cfsh(fake, fake, 0, 100, 50, 50, 50, fake, 10, 20, 1, 0, 0, 0, fake, 20, fake, ws, None) == 1
+    assert lrc._cfsh(fake, fake, 0, 100, 50, 50, 50, fake, 20, 20, 1, 0, 0, 0, fake, 20, fake, ws - 1, None) == 3
+    # component greedy: NULL offsets, negative budget, small workspace
+    need = lrc.lrc_allocate_components_workspace(4, 100)
+    assert need == lrc.lrc_allocate_ranks_workspace(4, 100)
+    assert lrc._acomp(4, fake, None, 100, fake, None, 10, fake, None, fake, need, fake, None) == 1
+    assert lrc._acomp(4, fake, fake, 100, fake, None, -1, fake, None, fake, need, fake, None) == 1
+    assert lrc._acomp(4, fake, fake, 100, fake, None, 10, fake, None, fake, need - 1, fake, None) == 3

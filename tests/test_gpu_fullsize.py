@@ -233,3 +233,51 @@ def test_stack_allocation_full_size_bitexact(lrc):
     used = int(np.sum(k_gpu.astype(np.int64) * cost))
     print("allocated %d of %d parameters; ranks %d .. %d" % (used, budget, k_gpu.min(), k_gpu.max()))
     assert used <= budget
+
+
+def test_component_fisher_full_size(lrc):
+    """Per-component scores of a gate_proj-shaped matrix (4096 x 11008) for all K = 2985 candidate
+    components, in one launch; 64 sampled components against the oracle's definition
+    ((W v_i) . (G v_i))^2 one by one.  The score's formula holds for any V: a Gaussian one stands in
+    for the eigenvectors here."""
+    _say("component scores at full size: 4096 x 11008, k = 2985")
+    d_in, d_out = 4096, 11008
+    K = (d_in * d_out) // (d_in + d_out)
+    W = inputs.weight(d_in, d_out, "bf16", inputs.CFG_STACK, 0, 4)
+    G = inputs.gradient(d_in, d_out, 1e-4, inputs.CFG_STACK, 0, 4)
+    V = (np.random.default_rng(41).standard_normal((d_out, K)) / np.sqrt(d_out)).astype(np.float32)
+    s = host(lrc.lrc_component_fisher(dev(W, "bf16"), dev(G, "bf16"), dev(V, "f32"), K))[0]
+    W64, G64 = oracle.widen(W, "bf16"), oracle.widen(G, "bf16")
+    idx = np.random.default_rng(42).choice(K, 64, replace=False)
+    idx[0] = K - 1
+    Vs = V[:, idx].astype(np.float64)
+    ref = oracle.component_fisher(W64, G64, Vs, len(idx))
+    scale = (np.linalg.norm(W64 @ Vs, axis=0) * np.linalg.norm(G64 @ Vs, axis=0)) ** 2
+    err = np.max(np.abs(s[idx] - ref) / scale)
+    print("sampled component scores: max |ds| / (||W v|| ||G v||)^2 = %.2e" % err)
+    assert err <= 1e-13
+    assert np.all(np.isfinite(s)) and np.all(s >= 0)
+
+
+def test_stack_component_allocation_full_size_bitexact(lrc):
+    """The component greedy over the 224-matrix stack: 548,704 candidates whose scores do not fall
+    with the component index (a decaying spectrum times a lognormal alignment factor), 80 % budget;
+    ranks and kept components bit-exact against the oracle on the same scores."""
+    _say("component greedy over 224 matrices, 548704 candidates, 80 % budget")
+    st = inputs.stack_spectra()
+    r = np.random.default_rng(43)
+    scores = [lam * r.lognormal(0.0, 1.0, lam.shape[0]) * a for lam, a in zip(st["lams"], st["alpha"])]
+    cost = st["cost"]
+    budget = int(np.floor(0.8 * 6476005376))
+    k_ref, masks_ref, info_ref = oracle.allocate_components(scores, cost, budget)
+    offs = np.concatenate([[0], np.cumsum([len(x) for x in scores])]).astype(np.int64)
+    k, sel, info = lrc.lrc_allocate_components(dev(np.concatenate(scores), "f64"), dev(offs, "i64"),
+                                               dev(cost, "i64"), budget)
+    assert int(host(info)[0]) == info_ref == 0
+    assert np.array_equal(host(k), k_ref)
+    sel = host(sel).astype(bool)
+    assert np.array_equal(sel, np.concatenate(masks_ref))
+    used = int(np.sum(host(k).astype(np.int64) * cost))
+    non_prefix = sum(int(not np.all(m[:int(np.sum(m))])) for m in masks_ref)
+    print("allocated %d of %d parameters; %d of 224 matrices keep a non-leading set" % (used, budget, non_prefix))
+    assert used <= budget
