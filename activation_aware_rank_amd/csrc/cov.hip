@@ -13,8 +13,9 @@
 //
 // Paths:
 //   * generic: any dtype/alignment, fp32 arithmetic, LDS-tiled FMA (used for fp32 inputs).
-//   * mfma (cov_mfma.hip): bf16 inputs with 16-byte aligned rows; bf16 MFMA for Y, Y split into
-//     bf16 hi + lo and C += hi^T hi + hi^T lo + lo^T hi with bf16 MFMA, fp32 accumulation.
+//   * mfma (cov_mfma.hip): bf16 inputs with 16-byte aligned rows; bf16 MFMA for Y, each output
+//     scaled by a power of two and split into fp16 hi + lo, C += 2^-(e_i + e_j) (hi^T hi + hi^T lo +
+//     lo^T hi) with fp16 MFMA and fp32 accumulation, plus the diagonal's sum of lo^2 on its own.
 #include "lrc_internal.h"
 #include "cov_mfma.h"
 

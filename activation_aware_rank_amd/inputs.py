@@ -282,3 +282,60 @@ def stack_spectra(n_layers: int = 32, d_model: int = 4096, d_ff: int = 11008, cf
             cost.append(di + do)
     return {"lams": lams, "eps0": np.array(eps0), "alpha": np.array(alpha), "cost": np.array(cost, dtype=np.int64)}
 
+
+
+def per_head_gpu(n_tok: int, d_model: int, seed: int, device, n_outliers: int = 8, outlier_scale: float = 50.0,
+                 df: int = 3) -> dict:
+    """The per_head recipe drawn on the GPU by torch's seeded generator: X Student-t(df) entries (a
+    normal over the root of a chi-square(df) / df, the chi-square as a sum of df squared normals)
+    with n_outliers columns scaled by outlier_scale, W ~ N(0, 0.02^2), both bf16.  Other numbers than
+    the host draw; used at full size for timing."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    cols = torch.randperm(d_model, generator=g, device=device)[:n_outliers]
+    scale = torch.ones(d_model, device=device)
+    scale[cols] = outlier_scale
+    X = torch.empty(n_tok, d_model, dtype=torch.bfloat16, device=device)
+    for r0 in range(0, n_tok, 8192):
+        r1 = min(n_tok, r0 + 8192)
+        z = torch.randn(r1 - r0, d_model, generator=g, device=device)
+        chi = torch.zeros_like(z)
+        for _ in range(df):
+            chi += torch.randn(r1 - r0, d_model, generator=g, device=device) ** 2
+        X[r0:r1] = (z / torch.sqrt(chi / df) * scale).to(torch.bfloat16)
+    W = (torch.randn(d_model, d_model, generator=g, device=device) * 0.02).to(torch.bfloat16)
+    return {"X": X, "W": W}
+
+
+def stack_layer_gpu(g, n_tok: int, d_model: int, d_ff: int, device, X=None, Xd=None) -> tuple:
+    """The calibration inputs of one stack layer (the block recipe) drawn on the GPU from the torch
+    generator g, into X (n_tok x d_model) and Xd (n_tok x d_ff) when given: N(0,1) times per-channel
+    exp(N(0,1)) scales, bf16."""
+    import torch
+
+    def act(width, out):
+        scale = torch.exp(torch.randn(width, generator=g, device=device, dtype=torch.float32))
+        if out is None:
+            out = torch.empty(n_tok, width, dtype=torch.bfloat16, device=device)
+        for r0 in range(0, n_tok, 16384):
+            r1 = min(n_tok, r0 + 16384)
+            out[r0:r1] = (torch.randn(r1 - r0, width, generator=g, device=device) * scale).to(torch.bfloat16)
+        return out
+
+    return act(d_model, X), act(d_ff, Xd)
+
+
+def stack_weights_gpu(g, n_layers: int, d_model: int, d_ff: int, device) -> tuple:
+    """Weights N(0, 0.02^2) and gradients N(0, 1e-4^2) of every matrix of an n_layers stack (block
+    shapes), bf16, drawn on the GPU from the torch generator g: lists of dicts per layer."""
+    import torch
+    Ws, Gs = [], []
+    for _ in range(n_layers):
+        W, G = {}, {}
+        for m, (di, do) in block_shapes(d_model, d_ff).items():
+            W[m] = (torch.randn(di, do, generator=g, device=device) * 0.02).to(torch.bfloat16)
+            G[m] = (torch.randn(di, do, generator=g, device=device) * 1e-4).to(torch.bfloat16)
+        Ws.append(W)
+        Gs.append(G)
+    return Ws, Gs

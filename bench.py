@@ -57,25 +57,86 @@ def measured_traffic(kernel):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(d_model, d_ff, sample_tok):
-    """The fp64 oracle's covariance throughput on a bounded token sample of the same block."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(d_model, d_ff, sample_tok, layer_tokens, heads_sample):
+    """The fp64 oracle timed on the host's cores, on bounded samples of the workloads.
+
+    value: the oracle's direct covariance (Y = X W, C = Y^T Y) of all 7 block matrices over
+    sample_tok tokens, as tokens/s (the headline's unit).  Beside it: the oracle's seconds per
+    4096 x 4096 layer at layer_tokens tokens (covariance, cyclic Jacobi eigendecomposition, factors,
+    error curve), and one-core times of the single fp32 layer (whole) and of the per-head case (a
+    heads_sample-token slice of its 32768 tokens, all 32 heads)."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from activation_aware_rank_amd import inputs
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     X = inputs.block_activations(d_model, sample_tok)
     Xd = inputs.block_activations(d_ff, sample_tok, feeds_down=True)
     Ws = {m: inputs.block_weight(m, d_model, d_ff) for m in MATS}
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     t0 = time.perf_counter()
     for m in MATS:
         oracle.covariance(Xd if m == "down_proj" else X, "bf16", Ws[m], "bf16")
     dt = time.perf_counter() - t0
-    return {"value": sample_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "fp64 direct covariance (Y = XW, C = Y^T Y) of all 7 block matrices over %d tokens "
-                      "(%.1f s); eigendecomposition, error curve and factors excluded, so this is an upper "
-                      "bound on the oracle's whole-step throughput" % (sample_tok, dt),
-            "seconds": dt}
+    out = {"value": sample_tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu_model": _cpu_model(),
+           "sample": "fp64 direct covariance (Y = XW, C = Y^T Y) of all 7 block matrices over %d tokens "
+                     "(%.1f s); eigendecomposition, error curve and factors excluded, so this is an upper "
+                     "bound on the oracle's whole-step throughput" % (sample_tok, dt),
+           "seconds": dt}
+    del X, Xd
+    if layer_tokens > 0:
+        # one 4096 x 4096 layer at its calibration size: O1 + O2 + O3 + O4
+        k = int(np.floor(0.6 * d_model * d_model / (2 * d_model)))
+        Xl = inputs.block_activations(d_model, layer_tokens, layer=1)
+        Wl = inputs.weight(d_model, d_model, "bf16", inputs.CFG_STACK, 1, 0)
+        t0 = time.perf_counter()
+        C = oracle.covariance(Xl, "bf16", Wl, "bf16")
+        t1 = time.perf_counter()
+        lam, V = oracle.eigh_large(C)
+        t2 = time.perf_counter()
+        oracle.truncate(oracle.widen(Wl, "bf16"), V, k)
+        oracle.error_curve(lam)
+        t3 = time.perf_counter()
+        out["sec_per_4096_layer"] = t3 - t0
+        out["sec_per_4096_layer_note"] = (
+            "%d tokens, k = %d, %d threads: covariance %.1f s, eigendecomposition %.1f s (LAPACK start "
+            "basis, then the cyclic Jacobi sweeps), factors and error curve %.1f s"
+            % (layer_tokens, k, threads, t1 - t0, t2 - t1, t3 - t2))
+        del Xl, C, V
+    with threadpool_limits(limits=1):
+        d = inputs.single_layer()
+        t0 = time.perf_counter()
+        C = oracle.covariance(d["X"], "f32", d["W"], "f32")
+        lam, V = oracle.eigh(C)
+        oracle.truncate(oracle.widen(d["W"], "f32"), V, 64)
+        oracle.error_curve(lam)
+        t1 = time.perf_counter()
+        out["one_core_single_layer_s"] = t1 - t0
+        if heads_sample > 0:
+            dh = inputs.per_head(n_tok=heads_sample)
+            t0 = time.perf_counter()
+            Ch = oracle.covariance(dh["X"], "bf16", dh["W"], "bf16", n_blocks=32)
+            for h in range(32):
+                lam_h, V_h = oracle.eigh(Ch[h])
+                oracle.error_curve(lam_h)
+            t1 = time.perf_counter()
+            out["one_core_per_head_tokens_per_s"] = heads_sample / (t1 - t0)
+        out["one_core_note"] = ("one thread: the single fp32 layer whole (2048 tokens, 256 -> 256: covariance, "
+                                "Jacobi, factors at k = 64, error curve); the per-head keys over a %d-token slice "
+                                "(covariances of all 32 heads of 128, Jacobi and error curve of each), as tokens/s"
+                                % heads_sample)
+    return out
 
 
 PEAK_F64_TFLOPS = 78.6  # MI355X dense fp64 (MFMA and vector)
@@ -117,6 +178,229 @@ def curvature_leg(torch, lrc, n_tok, seed, prec, dev, d_in=5120, d_out=13824, k=
     }
 
 
+def _events(torch):
+    def ev(st=None):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(st)
+        return e
+    return ev
+
+
+def single_layer_leg(torch, lrc, dev, runs=5):
+    """The single fp32 linear layer (2048 tokens, 256 -> 256, k = 64): covariance (fp32 path), fp32
+    eigendecomposition, error curve, factors; mean of `runs` after one warm-up."""
+    from activation_aware_rank_amd import inputs
+    ev = _events(torch)
+    d = inputs.single_layer()
+    X = torch.from_numpy(d["X"]).to(dev)
+    W = torch.from_numpy(d["W"]).to(dev)
+    k = 64
+    C = torch.empty(256, 256, dtype=torch.float32, device=dev)
+    A = torch.empty(256, k, dtype=torch.float32, device=dev)
+    B = torch.empty(k, 256, dtype=torch.float32, device=dev)
+    info = torch.zeros(2, dtype=torch.int32, device=dev)
+    ws_cov = torch.empty(lrc.lrc_cov_accumulate_workspace(lrc.LRC_F32, 2048, 256, True, 256, 1) + 256,
+                         dtype=torch.uint8, device=dev)
+
+    def run():
+        C.zero_()
+        lrc.lrc_cov_accumulate(X, W, C, info=info[0:1], ws=ws_cov)
+        lam, V, _ = lrc.lrc_eigh(C, k, prec=lrc.LRC_F32, info=info[1:2])
+        lrc.lrc_error_curve(lam[None])
+        lrc.lrc_factorize(W, V, k, A, B)
+
+    run()
+    torch.cuda.synchronize()
+    e0 = ev()
+    for _ in range(runs):
+        run()
+    e1 = ev()
+    torch.cuda.synchronize()
+    assert int(info.sum().item()) == 0
+    s = e0.elapsed_time(e1) / 1000.0 / runs
+    return {"workload": "single fp32 linear layer: 2048 tokens, W 256x256, k = 64, eig prec f32",
+            "seconds_per_layer": s, "tokens_per_s": 2048 / s}
+
+
+def per_head_leg(torch, lrc, n_tok, seed, dev, d_model=4096, hd=128, k=32, runs=3):
+    """Per-head keys (WSVD page, methodology 1): X n_tok x 4096 bf16 Student-t(3) with 8 outlier
+    channels x50, W_K 4096 x 4096 bf16, 32 heads of 128: the diagonal-block covariances, 32 batched
+    Jacobi eigendecompositions, error curves and factors at k = 32; mean of `runs` after a warm-up."""
+    from activation_aware_rank_amd import inputs
+    ev = _events(torch)
+    d = inputs.per_head_gpu(n_tok, d_model, seed + 11, dev)
+    X, W = d["X"], d["W"]
+    nh = d_model // hd
+    C = torch.empty(nh, hd, hd, dtype=torch.float32, device=dev)
+    lam = torch.empty(nh, hd, dtype=torch.float64, device=dev)
+    V = torch.empty(nh, hd, k, dtype=torch.float32, device=dev)
+    eps = torch.empty(nh, hd + 1, dtype=torch.float64, device=dev)
+    A = torch.empty(nh, d_model, k, dtype=torch.float32, device=dev)
+    B = torch.empty(nh, k, hd, dtype=torch.float32, device=dev)
+    info = torch.zeros(nh + 1, dtype=torch.int32, device=dev)
+    ws_cov = torch.empty(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, n_tok, d_model, True, d_model, nh),
+                         dtype=torch.uint8, device=dev)
+
+    def run(marks):
+        C.zero_()
+        marks.append(ev())
+        lrc.lrc_cov_accumulate(X, W, C, n_blocks=nh, info=info[0:1], ws=ws_cov)
+        marks.append(ev())
+        lrc.lrc_eigh(C, k, lam=lam, V=V, info=info[1:])
+        lrc.lrc_error_curve(lam, eps=eps)
+        marks.append(ev())
+        lrc.lrc_factorize(W, V, k, A, B, d_in=d_model, d_out=hd, batch=nh, stride_w=hd, stride_v=hd * k,
+                          stride_a=d_model * k, stride_b=k * hd)
+        marks.append(ev())
+
+    run([])
+    torch.cuda.synchronize()
+    recs = []
+    for _ in range(runs):
+        m = []
+        run(m)
+        recs.append(m)
+    torch.cuda.synchronize()
+    assert int(info.sum().item()) == 0, "per-head info flags: %s" % info.tolist()
+    cov = sum(m[0].elapsed_time(m[1]) for m in recs) / runs
+    eig = sum(m[1].elapsed_time(m[2]) for m in recs) / runs
+    fac = sum(m[2].elapsed_time(m[3]) for m in recs) / runs
+    tot = (cov + eig + fac) / 1000.0
+    fl = n_tok * (2 * d_model * d_model + nh * hd * (hd + 1))
+    return {"workload": "per-head keys: %d tokens x 4096 (Student-t(3), 8 outlier channels x50), W_K 4096x4096, "
+                        "32 heads of 128, k = 32" % n_tok,
+            "tokens_per_s": n_tok / tot, "cov_tokens_per_s": n_tok / (cov / 1000.0),
+            "cov_tflops_algorithmic": fl / (cov / 1000.0) / 1e12,
+            "stage_ms": {"covariance": round(cov, 3), "eigh_and_error_curve": round(eig, 3), "factors": round(fac, 3)}}
+
+
+def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=11008, rho=0.8):
+    """The 32-layer stack end to end (FLRC page, method 1; LASER page, method 2): for every layer its
+    own n_tok calibration tokens, the 7 covariances, one call decomposing all 7 (gate/up through a basis
+    of range(W^T)) with k_cap = floor(d_in d_out / (d_in + d_out)) vectors each, the error curves; then
+    the Fisher scores of all 224 matrices, the greedy allocation of rho of the parameters from the real
+    eigenvalues, and the factors of every matrix at its allocated rank.  One timed pass (inputs drawn
+    before the clock starts, except each layer's calibration tokens, which are drawn into the same
+    buffers before that layer's covariances and timed apart)."""
+    import numpy as np
+
+    from activation_aware_rank_amd import inputs
+    ev = _events(torch)
+    sh = shapes(d_model, d_ff)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 7)
+    Ws, Gs = inputs.stack_weights_gpu(g, n_layers, d_model, d_ff, dev)
+    X = torch.empty(n_tok, d_model, dtype=torch.bfloat16, device=dev)
+    Xd = torch.empty(n_tok, d_ff, dtype=torch.bfloat16, device=dev)
+    kcap = {m: (di * do) // (di + do) for m, (di, do) in sh.items()}
+    groups = {}
+    for m in MATS:
+        groups.setdefault((sh[m][1], kcap[m]), []).append(m)
+    gC = {gk: torch.empty(len(ms), gk[0], gk[0], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
+    where = {m: (gk, ms.index(m)) for gk, ms in groups.items() for m in ms}
+    V = [{m: torch.empty(sh[m][1], kcap[m], dtype=torch.float32, device=dev) for m in MATS} for _ in range(n_layers)]
+    lam = [{m: torch.empty(sh[m][1], dtype=torch.float64, device=dev) for m in MATS} for _ in range(n_layers)]
+    eps = [{m: torch.empty(sh[m][1] + 1, dtype=torch.float64, device=dev) for m in MATS} for _ in range(n_layers)]
+    ginfo_g = {gk: torch.zeros(len(ms), dtype=torch.int32, device=dev) for gk, ms in groups.items()}
+    cinfo = torch.zeros(1, dtype=torch.int32, device=dev)
+    bad = torch.zeros(1, dtype=torch.int64, device=dev)
+    # each group decomposes from stacked buffers (the range bases of gate/up included) and its
+    # eigenvalues and vectors are copied out to the per-matrix buffers
+    gV = {gk: torch.empty(len(ms), gk[0], gk[1], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
+    glam = {gk: torch.empty(len(ms), gk[0], dtype=torch.float64, device=dev) for gk, ms in groups.items()}
+    ws_cov = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, n_tok, di, True, do, 1)
+                             for di, do in sh.values()), dtype=torch.uint8, device=dev)
+    ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace(
+        [(gk[0], len(ms), gk[1], sh[ms[0]][0] if sh[ms[0]][0] < gk[0] else 0) for gk, ms in groups.items()], prec),
+        dtype=torch.uint8, device=dev)
+    gW = {gk: torch.empty(len(ms), sh[ms[0]][0], gk[0], dtype=torch.bfloat16, device=dev)
+          for gk, ms in groups.items() if sh[ms[0]][0] < gk[0]}
+    offs_h = [0] + list(np.cumsum([kcap[m] for _ in range(n_layers) for m in MATS]))
+    offs = torch.tensor(offs_h, dtype=torch.int64, device=dev)
+    lam_packed = torch.empty(int(offs_h[-1]), dtype=torch.float64, device=dev)
+    eps0 = torch.empty(n_layers * 7, dtype=torch.float64, device=dev)
+    cost = torch.tensor([sum(sh[m]) for _ in range(n_layers) for m in MATS], dtype=torch.int64, device=dev)
+    budget = int(np.floor(rho * n_layers * sum(di * do for di, do in sh.values())))
+    alpha = torch.empty(n_layers * 7, dtype=torch.float64, device=dev)
+    k_out = torch.empty(n_layers * 7, dtype=torch.int32, device=dev)
+    ws_alc = torch.empty(lrc.lrc_allocate_ranks_workspace(n_layers * 7, lam_packed.numel()), dtype=torch.uint8,
+                         device=dev)
+    Gl = [Gs[l][m] for l in range(n_layers) for m in MATS]
+    Wl = [Ws[l][m] for l in range(n_layers) for m in MATS]
+    ws_fsh = torch.empty(lrc.lrc_fisher_scores_workspace([w.numel() for w in Wl]), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t_gen = 0.0
+    marks = {"cov": 0.0, "eig": 0.0}
+    t0 = time.perf_counter()
+    for layer in range(n_layers):
+        a0 = ev()
+        inputs.stack_layer_gpu(g, n_tok, d_model, d_ff, dev, X, Xd)
+        a1 = ev()
+        for i, m in enumerate(MATS):
+            gk, j = where[m]
+            C = gC[gk][j]
+            C.zero_()
+            lrc.lrc_cov_accumulate(Xd if m == "down_proj" else X, Ws[layer][m], C, info=cinfo, ws=ws_cov)
+            bad += cinfo
+        a2 = ev()
+        for gk, ms in groups.items():
+            if gk in gW:
+                for j, m in enumerate(ms):
+                    gW[gk][j].copy_(Ws[layer][m])
+        lrc.lrc_eigh_multi([(gC[gk], gk[1], glam[gk], gV[gk], ginfo_g[gk], gW.get(gk)) for gk in groups], prec=prec,
+                           ws=ws_eig)
+        for gk, ms in groups.items():
+            bad += ginfo_g[gk].abs().sum()
+            for j, m in enumerate(ms):
+                lam[layer][m].copy_(glam[gk][j])
+                V[layer][m].copy_(gV[gk][j])
+        for i, m in enumerate(MATS):
+            lrc.lrc_error_curve(lam[layer][m][None], eps=eps[layer][m][None])
+            q = layer * 7 + i
+            lam_packed[offs_h[q]:offs_h[q] + kcap[m]].copy_(lam[layer][m][:kcap[m]])
+            eps0[q:q + 1].copy_(eps[layer][m][0:1])
+        a3 = ev()
+        a3.synchronize()
+        t_gen += a0.elapsed_time(a1) / 1000.0
+        marks["cov"] += a1.elapsed_time(a2)
+        marks["eig"] += a2.elapsed_time(a3)
+    b0 = ev()
+    lrc.lrc_fisher_scores(Gl, Wl, alpha=alpha, ws=ws_fsh)
+    lrc.lrc_allocate_ranks(alpha, lam_packed, offs, eps0, cost, budget, k_out=k_out, ws=ws_alc)
+    b1 = ev()
+    kk = k_out.cpu().tolist()
+    fac_ms = 0.0
+    for layer in range(n_layers):
+        for i, m in enumerate(MATS):
+            km = kk[layer * 7 + i]
+            if km <= 0:
+                continue
+            di, do = sh[m]
+            A = torch.empty(di, km, dtype=torch.float32, device=dev)
+            B = torch.empty(km, do, dtype=torch.float32, device=dev)
+            f0 = ev()
+            lrc.lrc_factorize(Ws[layer][m], V[layer][m], km, A, B)
+            f1 = ev()
+            f1.synchronize()
+            fac_ms += f0.elapsed_time(f1)
+            del A, B
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0 - t_gen
+    assert int(bad.item()) == 0, "stack: device info flags set"
+    used = sum(kk[q] * sum(sh[MATS[q % 7]]) for q in range(len(kk)))
+    return {"workload": "%d-layer LLaMA-7B-shaped stack (%d matrices, %d parameters), %d calibration tokens per "
+                        "layer, eig prec %s, k_cap vectors per matrix, greedy allocation of %.0f%% of the parameters"
+                        % (n_layers, n_layers * 7, n_layers * sum(di * do for di, do in sh.values()), n_tok,
+                           "f32" if prec == lrc.LRC_F32 else "f64", rho * 100),
+            "seconds": wall, "seconds_per_layer": wall / n_layers,
+            "tokens_per_s": n_layers * n_tok / wall,
+            "stage_s": {"covariances": marks["cov"] / 1000.0, "eigh_and_error_curves": marks["eig"] / 1000.0,
+                        "fisher_and_allocation": b0.elapsed_time(b1) / 1000.0, "factors": fac_ms / 1000.0},
+            "input_generation_s_excluded": t_gen,
+            "allocated_parameters": used, "budget": budget,
+            "rank_range": [min(kk), max(kk)]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +433,16 @@ def main():
                          "range(W^T) (their rank is at most d_in); off: the full decomposition of every covariance")
     ap.add_argument("--timing-stride", type=int, default=16,
                     help="time every s-th launch of the per-column symmetric product in the timed steps")
+    ap.add_argument("--layer-tokens", type=int, default=65536,
+                    help="also time one 4096x4096 layer over this many tokens (a stack layer's calibration size; 0: skip)")
+    ap.add_argument("--heads-tokens", type=int, default=32768, help="tokens of the per-head keys leg (0: skip)")
+    ap.add_argument("--single", choices=("on", "off"), default="on", help="the single fp32 layer leg")
+    ap.add_argument("--stack-layers", type=int, default=32, help="layers of the stack leg (0: skip)")
+    ap.add_argument("--stack-tokens", type=int, default=65536, help="calibration tokens per layer of the stack leg")
+    ap.add_argument("--cpu-layer-tokens", type=int, default=65536,
+                    help="tokens of the oracle's 4096x4096 layer in the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-heads-sample", type=int, default=4096,
+                    help="token slice of the per-head keys for the oracle's one-core time (0: skip)")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported (the path would shard matrices "
@@ -379,10 +673,10 @@ def main():
 
     # one 4096x4096 layer on its own, after the timed steps: covariance, eigendecomposition (alone,
     # not batched), error curve, factors; mean of --layer-runs runs
-    def one_layer(m="q_proj"):
+    def one_layer(m="q_proj", n_tok=None):
         C[m].zero_()
         e0 = ev(stream)
-        lrc.lrc_cov_accumulate(X, W[m], C[m], info=info[0:1], ws=ws_cov)
+        lrc.lrc_cov_accumulate(X if n_tok is None else X[:n_tok], W[m], C[m], info=info[0:1], ws=ws_cov)
         lrc.lrc_eigh(C[m], ks[m], prec=prec, lam=lam[m][None], V=V[m][None], info=info[7:8], ws=ws_eig)
         lrc.lrc_error_curve(lam[m][None], eps=eps[m][None])
         lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m])
@@ -392,6 +686,12 @@ def main():
     layer_runs = [one_layer() for _ in range(a.layer_runs)]
     torch.cuda.synchronize()
     layer_alone_s = float(np.mean([x.elapsed_time(y) for x, y in layer_runs])) / 1000.0 if layer_runs else None
+    layer_s_short = None
+    if a.layer_tokens > 0 and a.layer_runs > 0:
+        one_layer(n_tok=a.layer_tokens)  # warm-up at this size
+        short_runs = [one_layer(n_tok=a.layer_tokens) for _ in range(a.layer_runs)]
+        torch.cuda.synchronize()
+        layer_s_short = float(np.mean([x.elapsed_time(y) for x, y in short_runs])) / 1000.0
     assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
 
     # per-call times from the events (ms), averaged over steps
@@ -478,6 +778,7 @@ def main():
         "sec_per_4096_layer": layer_alone_s,
         "sec_per_4096_layer_note": "q_proj compressed on its own (covariance over all tokens, eigendecomposition, "
                                    "error curve, factors), after the timed steps",
+        "sec_per_4096_layer_at_%d_tokens" % a.layer_tokens: layer_s_short,
         "sec_per_4096_layer_in_block": layer_s,
         "sec_per_4096_layer_in_block_note": "q_proj covariance + q_proj factors + %.4f of the step's wall time "
                                             "outside the covariance, factor, Fisher and allocation calls (the "
@@ -498,13 +799,20 @@ def main():
     }
     if a.factored_steps > 0:
         out["factored"] = factored_leg()
+    if a.single == "on":
+        out["single_layer"] = single_layer_leg(torch, lrc, dev)
+    if a.heads_tokens > 0:
+        out["per_head"] = per_head_leg(torch, lrc, a.heads_tokens, a.seed, dev)
     if a.curvature_tokens > 0:
         del X, Xd, W, G, C, V, A, B, gC, gV, glam, geps, lam, eps, ws_cov, ws_eig
         torch.cuda.empty_cache()
         out["curvature_layer"] = curvature_leg(torch, lrc, a.curvature_tokens, a.seed,
                                                lrc.LRC_F32 if a.curvature_prec == "f32" else lrc.LRC_F64, dev)
+    if a.stack_layers > 0:
+        torch.cuda.empty_cache()
+        out["stack"] = stack_leg(torch, lrc, a.stack_layers, a.stack_tokens, a.seed, prec, dev, a.d_model, a.d_ff)
     if a.cpu_sample > 0:
-        out["cpu_baseline"] = cpu_baseline(a.d_model, a.d_ff, a.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(a.d_model, a.d_ff, a.cpu_sample, a.cpu_layer_tokens, a.cpu_heads_sample)
     print(json.dumps(out))
 
 
