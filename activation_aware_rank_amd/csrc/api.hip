@@ -303,6 +303,17 @@ lrc_status lrc_fisher_scores(int32_t n_mats, const void *const *G, const void *c
     return fisher_run(n_mats, G, W, numel, t, alpha, ws, ws_bytes, info, static_cast<hipStream_t>(stream));
 }
 
+lrc_status lrc_fisher_scores_noalloc(int32_t n_mats, const void *const *G, const void *const *W,
+                                     const int64_t *numel, lrc_dtype t, double *alpha, int32_t *info, void *stream) {
+    REQUIRE(n_mats > 0 && G && W && numel && alpha && info, LRC_ERR_ARG, "null argument or n_mats <= 0");
+    REQUIRE(t == LRC_BF16 || t == LRC_F32, LRC_ERR_DTYPE, "t must be LRC_BF16 or LRC_F32");
+    for (int i = 0; i < n_mats; ++i) {
+        REQUIRE(numel[i] >= 0, LRC_ERR_ARG, "negative numel");
+        REQUIRE(numel[i] == 0 || (G[i] && W[i]), LRC_ERR_ARG, "null G[m] or W[m]");
+    }
+    return fisher_run_noalloc(n_mats, G, W, numel, t, alpha, info, static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------------------------------------
 size_t lrc_allocate_ranks_workspace(int32_t n_mats, int64_t n_items) {
     if (n_mats <= 0 || n_items < 0) return 0;

@@ -151,6 +151,10 @@ lrc_status factorize_run(const FactorizeArgs &a, hipStream_t s);
 size_t fisher_workspace(int32_t n_mats, const int64_t *numel);
 lrc_status fisher_run(int32_t n_mats, const void *const *G, const void *const *W, const int64_t *numel,
                       lrc_dtype t, double *alpha, void *ws, size_t ws_bytes, int32_t *info, hipStream_t s);
+// the same with the partials in the library's file-scope device array (no workspace, no allocation)
+lrc_status fisher_run_noalloc(int32_t n_mats, const void *const *G, const void *const *W, const int64_t *numel,
+                              lrc_dtype t, double *alpha, int32_t *info, hipStream_t s);
+int64_t fisher_scratch_partials();
 
 struct AllocArgs {
     int32_t n_mats;

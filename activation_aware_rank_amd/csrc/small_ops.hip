@@ -9,6 +9,7 @@
 #include <cmath>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "lrc_internal.h"
 
@@ -199,6 +200,50 @@ lrc_status fisher_run(int32_t n_mats, const void *const *G, const void *const *W
         base += nb;
     }
     return LRC_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fisher scores without a caller workspace: the partials go to a file-scope device array of fixed
+// size (one copy per GPU, held until the process ends).  Host code never passes the array's name
+// to a kernel -- on the host that name is only a stand-in -- but the device address that
+// hipGetSymbolAddress returns for it, looked up once per device with that device current.  Every
+// partial is written before it is read in the same call, so the array needs no clearing; calls that
+// overlap on one GPU share it and race.
+// ---------------------------------------------------------------------------------------------
+constexpr int64_t FSH_SCRATCH_PARTIALS = int64_t(1) << 19;  // 4 MiB: up to 2^34 elements in one call
+static __device__ __align__(256) double scratch[FSH_SCRATCH_PARTIALS];
+
+constexpr int SCR_MAX_DEVICES = 64;
+static std::mutex g_scr_mu;
+static double *g_scr_ptr[SCR_MAX_DEVICES] = {};
+
+static lrc_status scratch_ptr(double **out) {
+    int dev = -1;
+    LRC_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= SCR_MAX_DEVICES) return fail(LRC_ERR_ARG, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    if (!g_scr_ptr[dev]) {
+        void *p = nullptr;
+        LRC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return fail(LRC_ERR_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+        g_scr_ptr[dev] = static_cast<double *>(p);
+    }
+    *out = g_scr_ptr[dev];
+    return LRC_OK;
+}
+
+int64_t fisher_scratch_partials() { return FSH_SCRATCH_PARTIALS; }
+
+lrc_status fisher_run_noalloc(int32_t n_mats, const void *const *G, const void *const *W, const int64_t *numel,
+                              lrc_dtype t, double *alpha, int32_t *info, hipStream_t s) {
+    int64_t nb_total = 0;
+    for (int i = 0; i < n_mats; ++i) nb_total += fisher_blocks(numel[i]);
+    if (nb_total > FSH_SCRATCH_PARTIALS)
+        return fail(LRC_ERR_ARG, "input larger than the scratch maximum (2^34 elements per call)");
+    double *ptr = nullptr;
+    const lrc_status st = scratch_ptr(&ptr);
+    if (st != LRC_OK) return st;
+    return fisher_run(n_mats, G, W, numel, t, alpha, ptr, size_t(FSH_SCRATCH_PARTIALS) * sizeof(double), info, s);
 }
 
 // ---------------------------------------------------------------------------------------------

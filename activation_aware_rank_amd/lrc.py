@@ -50,6 +50,7 @@ _fac = _sig("lrc_factorize", _int, _vp, _int, _i32, _i64, _i64, _i64, _vp, _i64,
             _i64, _vp, _i64, _i64, _vp)
 _fsh_ws = _sig("lrc_fisher_scores_workspace", _sz, _i32, _vp)
 _fsh = _sig("lrc_fisher_scores", _int, _i32, _vp, _vp, _vp, _int, _vp, _vp, _sz, _vp, _vp)
+_fsh_na = _sig("lrc_fisher_scores_noalloc", _int, _i32, _vp, _vp, _vp, _int, _vp, _vp, _vp)
 _alc_ws = _sig("lrc_allocate_ranks_workspace", _sz, _i32, _i64)
 _alc = _sig("lrc_allocate_ranks", _int, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp, _vp)
 _chol_ws = _sig("lrc_cholesky_workspace", _sz, _i64)
@@ -79,7 +80,7 @@ _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c
 EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_accumulate_workspace",
             "lrc_cov_accumulate", "lrc_eigh_workspace", "lrc_eigh", "lrc_eigh_multi_workspace", "lrc_eigh_multi",
             "lrc_error_curve", "lrc_factorize",
-            "lrc_fisher_scores_workspace", "lrc_fisher_scores",
+            "lrc_fisher_scores_workspace", "lrc_fisher_scores", "lrc_fisher_scores_noalloc",
             "lrc_allocate_ranks_workspace",
             "lrc_allocate_ranks", "lrc_cholesky_workspace", "lrc_cholesky", "lrc_trmm_workspace", "lrc_trmm",
             "lrc_trsm_workspace", "lrc_trsm", "lrc_sym_to_f64", "lrc_to_f64", "lrc_gram_f64",
@@ -329,6 +330,26 @@ def lrc_fisher_scores(Gs, Ws, alpha=None, info=None, ws=None, stream=None):
         alpha = torch.empty(n, dtype=torch.float64, device=dev)
     info = _info(info, n, dev)
     _check(_fsh(n, gp, wp, ne, _dt(Gs[0]), _ptr(alpha), _ptr(w), wn, _ptr(info), _stream(stream)))
+    return alpha, info
+
+
+def lrc_fisher_scores_noalloc(Gs, Ws, alpha, info, stream=None):
+    """lrc_fisher_scores with the partials in the library's own device scratch array: no workspace
+    and no allocation in the call (alpha fp64 and info int32 must be given)."""
+    n = len(Gs)
+    if n != len(Ws) or n == 0:
+        raise ValueError("G and W lists must have the same non-zero length")
+    for g, w in zip(Gs, Ws):
+        _dev(g, "G")
+        _dev(w, "W")
+        if g.numel() != w.numel() or not g.is_contiguous() or not w.is_contiguous() or g.dtype != w.dtype:
+            raise ValueError("G[m] and W[m] must be contiguous, same size and dtype")
+    if alpha.dtype != torch.float64 or alpha.numel() < n or info.dtype != torch.int32 or info.numel() < n:
+        raise ValueError("alpha (fp64) and info (int32) must hold n_mats entries")
+    gp = (ctypes.c_void_p * n)(*[g.data_ptr() for g in Gs])
+    wp = (ctypes.c_void_p * n)(*[w.data_ptr() for w in Ws])
+    ne = (ctypes.c_int64 * n)(*[g.numel() for g in Gs])
+    _check(_fsh_na(n, gp, wp, ne, _dt(Gs[0]), _ptr(alpha), _ptr(info), _stream(stream)))
     return alpha, info
 
 

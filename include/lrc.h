@@ -256,6 +256,22 @@ lrc_status lrc_fisher_scores(int32_t n_mats, const void *const *G /* host */, co
                              size_t ws_bytes, int32_t *info, void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * lrc_fisher_scores without workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, result and info as lrc_fisher_scores minus ws / ws_bytes.  The per-block partial
+ * sums go to a scratch array that the library holds in device memory, 4 MiB (2^19 fp64
+ * partials) per GPU, allocated when the library is loaded and kept until the process ends.  No
+ * hipMalloc, hipFree or other allocating call is made.  Limit: the total number of 32768-element
+ * blocks over all matrices (sum of ceil(numel[m] / 32768)) must not exceed 2^19, about 1.7e10
+ * elements in one call; larger inputs return LRC_ERR_ARG and nothing is launched.  Every call on
+ * one GPU shares that GPU's scratch array: calls that overlap on one GPU (several streams or host
+ * threads at once) race and must be serialised by the caller.
+ * ------------------------------------------------------------------------------------ */
+lrc_status lrc_fisher_scores_noalloc(int32_t n_mats, const void *const *G /* host */,
+                                     const void *const *W /* host */, const int64_t *numel /* host */,
+                                     lrc_dtype t, double *alpha, int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Greedy global rank allocation under a parameter budget (LASER page, method 2: take the
  * singular components of highest importance per parameter cost until the budget is
  * reached; FLRC page, method 1: Fisher importance per projection; Swift-SVD page, section
