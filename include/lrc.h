@@ -310,6 +310,8 @@ lrc_status lrc_allocate_ranks(int32_t n_mats, const double *alpha, const double 
  *    - r_m gain one, ties to the smaller m; over by d: the d matrices with r_m > 0 and the
  *    smallest remainders lose one, ties to the smaller m).  q_m = (alpha_m R) / S in fp64 with S
  *    summed in index order, so the result is bit-exact against a sequential evaluation.
+ *    Along a falling schedule R(t) a matrix's rank can rise by one from one budget to the next
+ *    (largest-remainder rounding is subject to the Alabama paradox), never by more.
  * info: one int32: 0, or 5 when an alpha is negative or NaN, S is not positive and finite, or a
  *    budget is negative (every rank is then 0).
  * Errors: LRC_ERR_ARG (NULL pointers, n_mats outside 1 .. 1024, n_budgets <= 0).

@@ -588,7 +588,9 @@ def test_allocate_proportional_worked_examples():
 
 def test_allocate_proportional_invariants():
     """Sum exactly R; each r_m within one of alpha_m R / S; a larger alpha never gets a smaller rank;
-    the progressive schedule's ranks do not increase as the budget falls (budgets 4000 ... 0)."""
+    along the progressive schedule (budgets falling from ~5000 to 0) each rank stays within one step
+    of monotone: largest-remainder rounding is subject to the Alabama paradox, so a matrix's rank can
+    rise by one when R(t) falls, never by more."""
     rng = np.random.default_rng(7)
     for trial in range(20):
         a = rng.lognormal(0.0, 2.0, size=int(rng.integers(1, 40)))
