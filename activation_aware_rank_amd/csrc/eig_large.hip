@@ -20,6 +20,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <thread>
@@ -57,8 +58,17 @@ __global__ void k_fill_full(const float *__restrict__ C, int64_t ldc, int64_t n,
     }
 }
 
+// Several matrices of one order decomposed in lockstep: the tridiagonalisation kernels take the
+// pointers of the first matrix's workspace region and the byte stride zs between regions (every
+// region has the same layout), and workgroup z works on matrix z.  zs = 0 with one z: one matrix.
+template <class P>
+__device__ __forceinline__ P zoff(P p, int64_t zs) {
+    return reinterpret_cast<P>(reinterpret_cast<uintptr_t>(p) + uintptr_t(int64_t(blockIdx.z) * zs));
+}
+
 template <class T>
-__global__ void k_fill_zero(T *__restrict__ p, int64_t n) {
+__global__ void k_fill_zero(T *__restrict__ p, int64_t n, int64_t zs) {
+    p = zoff(p, zs);
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
         p[i] = T(0);
 }
@@ -167,8 +177,12 @@ __device__ __forceinline__ void rs_step(T (&p)[N], int lane) {
 template <class T>
 __global__ void __launch_bounds__(256) k_trd_col0(const T *__restrict__ A, int64_t lda, int64_t n, int64_t c,
                                                   T *__restrict__ colbuf, T *__restrict__ part,
-                                                  double *__restrict__ d) {
+                                                  double *__restrict__ d, int64_t zs) {
     __shared__ T sh[4];
+    A = zoff(A, zs);
+    colbuf = zoff(colbuf, zs);
+    part = zoff(part, zs);
+    d = zoff(d, zs);
     const int64_t r = c + int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     T ss = T(0);
     if (r < n) {
@@ -226,10 +240,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SYMV_W
                                                   T *__restrict__ Rt, T *__restrict__ rowpart,
                                                   T *__restrict__ colpart, const T *__restrict__ qcol,
                                                   T *__restrict__ qvec, T *__restrict__ spart, T *__restrict__ tau,
-                                                  double *__restrict__ e, int NT, int CHK) {
+                                                  double *__restrict__ e, int NT, int CHK, int64_t zs) {
     LRC_ARGS_AT_ENTRY("s"(A), "s"(lda), "s"(n), "s"(c), "s"(j), "s"(colbuf), "s"(part), "s"(npart), "s"(Vp), "s"(Wp),
                       "s"(Rt), "s"(rowpart), "s"(colpart), "s"(qcol), "s"(qvec), "s"(spart), "s"(tau), "s"(e),
-                      "s"(NT), "s"(CHK));
+                      "s"(NT), "s"(CHK), "s"(zs));
+    A = zoff(A, zs);
+    colbuf = zoff(colbuf, zs);
+    part = zoff(part, zs);
+    Vp = zoff(Vp, zs);
+    Wp = zoff(Wp, zs);
+    Rt = zoff(Rt, zs);
+    rowpart = zoff(rowpart, zs);
+    colpart = zoff(colpart, zs);
+    qcol = zoff(qcol, zs);
+    qvec = zoff(qvec, zs);
+    spart = zoff(spart, zs);
+    tau = zoff(tau, zs);
+    e = zoff(e, zs);
     constexpr int TS = SymvTile<T>::TS, EPC = SymvTile<T>::EPC, H = SymvTile<T>::H;
     static_assert(16 * EPC == TS, "tile geometry");
     typedef T vec_t __attribute__((ext_vector_type(EPC)));
@@ -444,7 +471,7 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
             T *__restrict__ Wp, const T *__restrict__ rowpart, const T *__restrict__ colpart,
             const T *__restrict__ qvec, const T *__restrict__ spart, int nsp, int NT, int CHK,
             const T *__restrict__ tau, T *__restrict__ colbuf, T *__restrict__ part, T *__restrict__ qcol,
-            double *__restrict__ d) {
+            double *__restrict__ d, int64_t zs) {
     constexpr int QW = NB / 4;  // panel columns per wave
     __shared__ T sh[8];
     __shared__ T qs[2 * NB];
@@ -453,7 +480,19 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
     __shared__ T v1s[NB], w1s[NB];
     LRC_ARGS_AT_ENTRY("s"(A), "s"(lda), "s"(n), "s"(c), "s"(j), "s"(next), "s"(Vp), "s"(Wp), "s"(rowpart),
                       "s"(colpart), "s"(qvec), "s"(spart), "s"(nsp), "s"(NT), "s"(CHK), "s"(tau), "s"(colbuf),
-                      "s"(part), "s"(qcol), "s"(d));
+                      "s"(part), "s"(qcol), "s"(d), "s"(zs));
+    A = zoff(A, zs);
+    Vp = zoff(Vp, zs);
+    Wp = zoff(Wp, zs);
+    rowpart = zoff(rowpart, zs);
+    colpart = zoff(colpart, zs);
+    qvec = zoff(qvec, zs);
+    spart = zoff(spart, zs);
+    tau = zoff(tau, zs);
+    colbuf = zoff(colbuf, zs);
+    part = zoff(part, zs);
+    qcol = zoff(qcol, zs);
+    d = zoff(d, zs);
     const int T0 = int((c + 1) / SymvTile<T>::TS);
     const int t = threadIdx.x;
     const int rl = t & 63, sub = t >> 6;
@@ -640,8 +679,11 @@ struct TrailMfma<double> {
 
 template <class T>
 __global__ void __launch_bounds__(256) k_trailing(T *__restrict__ A, int64_t lda, int64_t n, int64_t p, int jn,
-                                                  const T *__restrict__ Vp, const T *__restrict__ Wp) {
+                                                  const T *__restrict__ Vp, const T *__restrict__ Wp, int64_t zs) {
     using M = TrailMfma<T>;
+    A = zoff(A, zs);
+    Vp = zoff(Vp, zs);
+    Wp = zoff(Wp, zs);
     constexpr int LD = 64 + 4;
     __shared__ T ar[2 * NB][LD], bs[2 * NB][LD];
     const int u = blockIdx.x;
@@ -1337,16 +1379,31 @@ struct EigJob {
     hipStream_t s = nullptr;
     int stage = 0;  // 0 start, 1 tridiagonalisation, 2 eigenvalues and vectors of T, 3 back-transformation, 4 done
     bool keep_z = false;  // leave the fp64 eigenvectors in w->Z (no sign rule, no fp32 output)
+    // lockstep: the tridiagonalisation of nbatch matrices of order n whose workspace regions start
+    // zs bytes apart (w is the first one's); such a job stops after stage 1
+    unsigned nbatch = 1;
+    int64_t zs = 0;
     int NT = 0, npart = 0;
     int64_t p0 = 0, p1 = 0, c = 0, c0 = 0;
 
     void start_panel() {
         p1 = std::min<int64_t>(p0 + NB, n - 1);
-        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w->Vp, int64_t(n) * NB);
-        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256), dim3(256), 0, s, w->Wp, int64_t(n) * NB);
+        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256, 1, nbatch), dim3(256), 0, s, w->Vp, int64_t(n) * NB, zs);
+        hipLaunchKernelGGL(k_fill_zero<T>, dim3(256, 1, nbatch), dim3(256), 0, s, w->Wp, int64_t(n) * NB, zs);
         npart = cdiv(n - p0, 256);
-        hipLaunchKernelGGL(k_trd_col0<T>, dim3(npart), dim3(256), 0, s, w->A, w->lda, n, p0, w->colbuf, w->part, w->d);
+        hipLaunchKernelGGL(k_trd_col0<T>, dim3(npart, 1, nbatch), dim3(256), 0, s, w->A, w->lda, n, p0, w->colbuf,
+                           w->part, w->d, zs);
         c = p0;
+    }
+
+    // stage 0 up to the tridiagonalisation: the info flag cleared, C copied into A (both
+    // triangles' storage, padding zero)
+    lrc_status prepare() {
+        hipLaunchKernelGGL(k_fill_zero<int>, dim3(1), dim3(64), 0, s, w->bad, int64_t(1), int64_t(0));
+        hipLaunchKernelGGL(k_fill_full<T>, dim3(2048), dim3(256), 0, s, C, ldc, n, w->A, w->lda, w->bad);
+        LRC_LAUNCH_CHECK("k_fill_full");
+        NT = int(symv_tiles<T>(n));
+        return LRC_OK;
     }
 
     void column() {
@@ -1361,26 +1418,24 @@ struct EigJob {
         const int nitems = int(symv_items(mt, chk));
         // algorithmic bytes: the upper triangle of the trailing matrix, read once
         const double m1 = double(n - c - 1);
-        LRC_TIMED_LAUNCH("k_trd_symv", m1 * (m1 + 1.0) * 0.5 * double(sizeof(T)), k_trd_symv<T>, dim3(nitems),
-                         dim3(256), 0, s, w->A, lda, n, c, j, w->colbuf, w->part, npart, w->Vp, w->Wp, w->Rt,
-                         w->rowpart, w->colpart, w->qcol, w->qvec, w->spart, w->tau, w->e, NT, chk);
+        LRC_TIMED_LAUNCH("k_trd_symv", m1 * (m1 + 1.0) * 0.5 * double(sizeof(T)) * double(nbatch), k_trd_symv<T>,
+                         dim3(nitems, 1, nbatch), dim3(256), 0, s, w->A, lda, n, c, j, w->colbuf, w->part, npart, w->Vp,
+                         w->Wp, w->Rt, w->rowpart, w->colpart, w->qcol, w->qvec, w->spart, w->tau, w->e, NT, chk, zs);
         // the next column is handled here unless a trailing update comes first (the last column
         // n-1 has no reflector, only d[n-1])
         const int next = (c + 1 < p1 || p1 == n - 1) ? 1 : 0;
         const int nw = cdiv(n - c - 1, 64);
-        hipLaunchKernelGGL(k_trd_w1col<T>, dim3(nw), dim3(256), 0, s, w->A, lda, n, c, j, next, w->Vp, w->Wp,
-                           w->rowpart, w->colpart, w->qvec, w->spart, nitems, NT, chk, w->tau, w->colbuf, w->part,
-                           w->qcol, w->d);
+        hipLaunchKernelGGL(k_trd_w1col<T>, dim3(nw, 1, nbatch), dim3(256), 0, s, w->A, lda, n, c, j, next, w->Vp,
+                           w->Wp, w->rowpart, w->colpart, w->qvec, w->spart, nitems, NT, chk, w->tau, w->colbuf,
+                           w->part, w->qcol, w->d, zs);
         npart = nw;
     }
 
     // Enqueues about `cols` columns' worth of launches; returns LRC_OK or a launch error.
     lrc_status advance(int cols) {
         if (stage == 0) {
-            hipLaunchKernelGGL(k_fill_zero<int>, dim3(1), dim3(64), 0, s, w->bad, int64_t(1));
-            hipLaunchKernelGGL(k_fill_full<T>, dim3(2048), dim3(256), 0, s, C, ldc, n, w->A, w->lda, w->bad);
-            LRC_LAUNCH_CHECK("k_fill_full");
-            NT = int(symv_tiles<T>(n));
+            const lrc_status st = prepare();
+            if (st != LRC_OK) return st;
             p0 = 0;
             start_panel();
             stage = 1;
@@ -1393,8 +1448,8 @@ struct EigJob {
                 LRC_LAUNCH_CHECK("tridiagonal panel");
                 if (p1 < n - 1) {
                     const int64_t nt = cdiv(n - p1, 64);  // tile rows of the trailing matrix
-                    hipLaunchKernelGGL(k_trailing<T>, dim3(unsigned(nt * (nt + 1) / 2)), dim3(256), 0, s, w->A, w->lda,
-                                       n, p1, int(p1 - p0), w->Vp, w->Wp);
+                    hipLaunchKernelGGL(k_trailing<T>, dim3(unsigned(nt * (nt + 1) / 2), 1, nbatch), dim3(256), 0, s,
+                                       w->A, w->lda, n, p1, int(p1 - p0), w->Vp, w->Wp, zs);
                     LRC_LAUNCH_CHECK("k_trailing");
                 }
                 p0 += NB;
@@ -1516,8 +1571,11 @@ struct RangeWs {
     int32_t *iw;
 };
 
+// The decomposition's own arrays come first, at the offsets a member without a basis of order r has,
+// so that members of both kinds can be tridiagonalised in lockstep.
 template <class C_, class T>
 static void range_layout(C_ &cv, RangeWs &rw, LargeWs<T> &w, int64_t n, int64_t r, int64_t nv) {
+    layout(cv, w, r, nv, false);
     rw.Qt = cv.template carve<double>(size_t(r) * size_t(n));
     rw.C64 = cv.template carve<double>(size_t(n) * size_t(n));
     rw.T = cv.template carve<double>(size_t(r) * size_t(n));  // later the n x n_vec vectors Q Z
@@ -1527,7 +1585,6 @@ static void range_layout(C_ &cv, RangeWs &rw, LargeWs<T> &w, int64_t n, int64_t 
     rw.trsm = cv.template carve<char>(trsm_workspace(0, r, n));
     rw.B = cv.template carve<float>(size_t(r) * size_t(r));
     rw.iw = cv.template carve<int32_t>(2);
-    layout(cv, w, r, nv, false);
 }
 
 template <class T>
@@ -1658,45 +1715,44 @@ struct EigMember {
     int64_t d_in, ldw;
 };
 
-// All members with n > 128 over up to EIG_LANES helper streams, largest n first: each lane's
-// thread takes the next member once its own is enqueued (its stream runs in order, so the lane's
-// workspace is free by then).  Which lane runs a member does not change its results: the
-// computation depends only on the member, and every lane's workspace has the same layout.
+// One member's decomposition: its layout on a workspace region and its job; for a member with a
+// range basis also the basis Q and B = Q^T C Q (the job decomposes B) and, once the job is done,
+// V = Q Z and the eigenvalues with the n - d_in zeros.
 template <class T>
-static lrc_status run_member(const EigMember &m, const MultiPlan &p, char *lws, hipStream_t s, LargeWs<T> &w) {
-    Carver cv(lws, p.per);
-    w = LargeWs<T>();
-    layout(cv, w, m.n, m.nv, false);
-    if (!w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
+struct MemberRun {
+    EigMember m{};
+    LargeWs<T> w;
+    RangeWs rw{};
     EigJob<T> j;
-    j.C = m.C;
-    j.ldc = m.ldc;
-    j.n = m.n;
-    j.lambda = m.lambda;
-    j.V = m.V;
-    j.ldv = m.ldv;
-    j.nv = m.nv;
-    j.info = m.info;
-    j.w = &w;
-    j.s = s;
-    while (!j.done()) {
-        const lrc_status st = j.advance(64);
-        if (st != LRC_OK) return st;
-    }
-    return LRC_OK;
-}
+};
 
-// A member with a range basis: Q^T = L^{-1} W (W W^T = L L^T), B = Q^T C Q in fp64 (rounded to fp32
-// as the input of the decomposition, like C itself), B's decomposition with its fp64 vectors
-// kept, then V = Q Z with the sign rule and lambda with the n - d_in zeros.
+// Lays out the region and sets up the job; a range member's basis and B are enqueued on s.
 template <class T>
-static lrc_status run_member_range(const EigMember &m, const MultiPlan &p, char *lws, hipStream_t s, LargeWs<T> &w) {
-    const int64_t n = m.n, r = m.d_in, nv = m.nv;
+static lrc_status member_begin(MemberRun<T> &R, const MultiPlan &p, char *lws, hipStream_t s) {
+    const EigMember &m = R.m;
     Carver cv(lws, p.per);
-    RangeWs rw;
-    w = LargeWs<T>();
-    range_layout(cv, rw, w, n, r, nv);
-    if (!w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
+    R.w = LargeWs<T>();
+    EigJob<T> &j = R.j;
+    j = EigJob<T>();
+    j.w = &R.w;
+    j.s = s;
+    if (!m.W) {
+        layout(cv, R.w, m.n, m.nv, false);
+        if (!R.w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
+        j.C = m.C;
+        j.ldc = m.ldc;
+        j.n = m.n;
+        j.lambda = m.lambda;
+        j.V = m.V;
+        j.ldv = m.ldv;
+        j.nv = m.nv;
+        j.info = m.info;
+        return LRC_OK;
+    }
+    const int64_t n = m.n, r = m.d_in, nv = m.nv;
+    RangeWs &rw = R.rw;
+    range_layout(cv, rw, R.w, n, r, nv);
+    if (!R.w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
     lrc_status st = to_f64_run(m.W, m.w_t, r, n, m.ldw, 1.0, rw.Qt, n, s);
     if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, rw.Qt, n, rw.Qt, n, rw.G, r, 1, nullptr, s);  // W W^T, lower
     if (st == LRC_OK) st = cholesky_run(rw.G, r, r, rw.chol, cholesky_workspace(r), rw.iw, s);
@@ -1709,7 +1765,6 @@ static lrc_status run_member_range(const EigMember &m, const MultiPlan &p, char 
     if (st == LRC_OK) st = dgemm_run(0, 0, r, n, n, rw.Qt, n, rw.C64, n, rw.T, n, 0, nullptr, s);  // Q^T C
     if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, rw.T, n, rw.Qt, n, nullptr, r, 2, rw.B, s);  // B, upper
     if (st != LRC_OK) return st;
-    EigJob<T> j;
     j.C = rw.B;
     j.ldc = r;
     j.n = r;
@@ -1718,37 +1773,132 @@ static lrc_status run_member_range(const EigMember &m, const MultiPlan &p, char 
     j.ldv = nv;
     j.nv = nv;
     j.info = rw.iw + 1;
-    j.w = &w;
-    j.s = s;
     j.keep_z = true;
-    while (!j.done()) {
-        st = j.advance(64);
-        if (st != LRC_OK) return st;
-    }
+    return LRC_OK;
+}
+
+// After the job: a range member's V = Q Z (sign rule) and lambda with the zeros, on s.
+template <class T>
+static lrc_status member_end(MemberRun<T> &R, hipStream_t s) {
+    const EigMember &m = R.m;
+    if (!m.W) return LRC_OK;
+    const int64_t n = m.n, r = m.d_in, nv = m.nv;
+    RangeWs &rw = R.rw;
     if (nv > 0) {
-        st = dgemm_run(1, 0, n, nv, r, rw.Qt, n, w.Z, nv, rw.T, nv, 0, nullptr, s);  // Q Z (n x n_vec)
+        const lrc_status st = dgemm_run(1, 0, n, nv, r, rw.Qt, n, R.w.Z, nv, rw.T, nv, 0, nullptr, s);  // Q Z
         if (st != LRC_OK) return st;
-        hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, w.bad);
+        hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, R.w.bad);
         LRC_LAUNCH_CHECK("k_sign_out");
     }
-    hipLaunchKernelGGL(k_range_finish, dim3(cdiv(n, 256)), dim3(256), 0, s, rw.lamB, r, n, m.lambda, w.bad, rw.iw, nv,
+    hipLaunchKernelGGL(k_range_finish, dim3(cdiv(n, 256)), dim3(256), 0, s, rw.lamB, r, n, m.lambda, R.w.bad, rw.iw, nv,
                        m.info);
     LRC_LAUNCH_CHECK("k_range_finish");
     return LRC_OK;
+}
+
+// All members with n > 128 over up to EIG_LANES helper streams, largest n first: each lane's
+// thread takes the next member once its own is enqueued (its stream runs in order, so the lane's
+// workspace is free by then).  Which lane runs a member does not change its results: the
+// computation depends only on the member, and every lane's workspace has the same layout.
+template <class T>
+static lrc_status run_member(const EigMember &m, const MultiPlan &p, char *lws, hipStream_t s, MemberRun<T> &R) {
+    R.m = m;
+    lrc_status st = member_begin(R, p, lws, s);
+    while (st == LRC_OK && !R.j.done()) st = R.j.advance(64);
+    if (st == LRC_OK) st = member_end(R, s);
+    return st;
+}
+
+// Members whose matrices have one order (n, or d_in with a range basis) and fit a workspace region
+// each are tridiagonalised in lockstep: every launch of the column chain works on all of them (one
+// z slice per matrix), so a chain of two small launches per column serves the whole group instead
+// of each matrix paying its own launch and latency cost on a stream of its own.  The rest of each
+// decomposition (eigenvalues and vectors of T, back-transformation, a range member's V = Q Z) then
+// runs on a helper stream per member.  Every member's arithmetic is the same as alone, so its
+// results are bit-identical to a call on it alone.  LRC_EIGH_LOCKSTEP=0 turns this off (each
+// member on a lane of its own throughout, as for members of different orders).
+static int64_t trd_order(const EigMember &m) { return m.W ? m.d_in : m.n; }
+
+static bool lockstep_ok(const std::vector<EigMember> &mem, int lanes) {
+    if (mem.size() < 2 || mem.size() > size_t(lanes)) return false;
+    const char *e = std::getenv("LRC_EIGH_LOCKSTEP");
+    if (e && e[0] == '0' && e[1] == 0) return false;
+    for (const EigMember &m : mem)
+        if (trd_order(m) != trd_order(mem[0])) return false;
+    return true;
+}
+
+template <class T>
+static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p, char *ws, hipStream_t s,
+                                 MemberRun<T> *R) {
+    const int nb = int(mem.size());
+    // 1. each member's setup (a range member's basis and B) and its matrix copied into A, on s
+    for (int i = 0; i < nb; ++i) {
+        R[i].m = mem[i];
+        lrc_status st = member_begin(R[i], p, ws + p.per * size_t(i), s);
+        if (st == LRC_OK) st = R[i].j.prepare();
+        if (st != LRC_OK) return st;
+    }
+    // 2. the tridiagonalisations in lockstep, on s (regions p.per bytes apart, identical layouts up to
+    // the arrays that depend on n_vec, which the tridiagonalisation does not touch)
+    EigJob<T> bj = R[0].j;
+    bj.nbatch = unsigned(nb);
+    bj.zs = int64_t(p.per);
+    bj.p0 = 0;
+    bj.start_panel();
+    bj.stage = 1;
+    while (bj.stage == 1) {
+        const lrc_status st = bj.advance(64);
+        if (st != LRC_OK) return st;
+    }
+    // 3. the rest of each decomposition on a helper stream of its own
+    EigLanes *L = nullptr;
+    lrc_status st0 = eig_lanes(&L);
+    if (st0 != LRC_OK) return st0;
+    hipEvent_t ev[EIG_LANES + 1];
+    st0 = take_events(L, nb + 1, ev);
+    if (st0 != LRC_OK) return st0;
+    const unsigned base = L->base.fetch_add(unsigned(nb));
+    hipStream_t ls[EIG_LANES];
+    for (int i = 0; i < nb; ++i) ls[i] = L->st[(base + unsigned(i)) % EIG_LANES];
+    auto fan = [&]() -> lrc_status {
+        LRC_HIP(hipEventRecord(ev[0], s));
+        for (int i = 0; i < nb; ++i) LRC_HIP(hipStreamWaitEvent(ls[i], ev[0], 0));
+        for (int i = 0; i < nb; ++i) {
+            EigJob<T> &j = R[i].j;
+            j.s = ls[i];
+            j.stage = 2;
+            while (!j.done()) {
+                const lrc_status st = j.advance(64);
+                if (st != LRC_OK) return st;
+            }
+            const lrc_status st = member_end(R[i], ls[i]);
+            if (st != LRC_OK) return st;
+        }
+        for (int i = 0; i < nb; ++i) {
+            LRC_HIP(hipEventRecord(ev[1 + i], ls[i]));
+            LRC_HIP(hipStreamWaitEvent(s, ev[1 + i], 0));
+        }
+        return LRC_OK;
+    };
+    const lrc_status st = fan();
+    give_events(L, nb + 1, ev);
+    return st;
 }
 
 template <class T>
 static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, char *ws, hipStream_t s) {
     std::stable_sort(mem.begin(), mem.end(), [](const EigMember &x, const EigMember &y) { return x.n > y.n; });
     const int lanes = p.lanes;
-    LargeWs<T> w[EIG_LANES];
+    std::unique_ptr<MemberRun<T>[]> R(new MemberRun<T>[EIG_LANES]);
     if (lanes <= 1) {
         for (const EigMember &m : mem) {
-            const lrc_status st = m.W ? run_member_range<T>(m, p, ws, s, w[0]) : run_member<T>(m, p, ws, s, w[0]);
+            const lrc_status st = run_member<T>(m, p, ws, s, R[0]);
             if (st != LRC_OK) return st;
         }
         return LRC_OK;
     }
+    if (lockstep_ok(mem, lanes)) return large_lockstep<T>(mem, p, ws, s, R.get());
     EigLanes *L = nullptr;
     lrc_status st0 = eig_lanes(&L);
     if (st0 != LRC_OK) return st0;
@@ -1782,8 +1932,7 @@ static lrc_status large_sched(std::vector<EigMember> &mem, const MultiPlan &p, c
             const size_t i = next.fetch_add(1);
             if (i >= mem.size()) break;
             char *lws = ws + p.per * size_t(l);
-            st[l] = mem[i].W ? run_member_range<T>(mem[i], p, lws, ls[l], w[l])
-                             : run_member<T>(mem[i], p, lws, ls[l], w[l]);
+            st[l] = run_member<T>(mem[i], p, lws, ls[l], R[l]);
         }
         if (st[l] != LRC_OK) {
             msg[l] = lrc_last_error();
