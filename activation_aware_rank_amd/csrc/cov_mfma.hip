@@ -23,9 +23,12 @@
 //
 // Both phases are one "NT" kernel: D = A B^T with A and B row-major along the contraction
 // axis, which is exactly the layout the 32x32x16 bf16 MFMA operands want (each lane holds 8
-// contiguous k-values of one row).  4 waves (2 x 2) per block; block tile 256 x 256 for the
-// GEMM and 128 x 128 for the SYRK; k step 32, double-buffered LDS with an XOR swizzle of the
-// 16-byte chunks (no padding, no bank conflicts on 16-byte reads), one barrier per k step.
+// contiguous k-values of one row).  The GEMM's block tile is 256 x 256 on 8 waves (2 x 4) of
+// 128 x 64, two waves to a SIMD (10 % faster than 4 waves of 128 x 128 at d_in 4096: a wave's
+// accumulators and operands fit its registers without spills, and one wave's MFMAs run while the
+// other waits); the SYRK's is 128 x 128 on 4 waves; k step 32, double-buffered LDS with an XOR
+// swizzle of the 16-byte chunks (no padding, no bank conflicts on 16-byte reads), one barrier
+// per k step.
 //
 // Load balance of the SYRK: the upper triangle may have fewer tiles than the GPU has CUs, so
 // the token range of a chunk is split S ways; split s > 0 accumulates into its own fp32
@@ -235,6 +238,24 @@ __device__ __forceinline__ void mfma_mainloop(
         }
         if (FLUSH && (FE == 2 || (FE == 4 && PAR == 1))) flush();
         if (NOBRANCH || kt + 1 < nk) sstore(cur ^ 1, sset);
+        if constexpr (NOBRANCH && NPROD == 1 && TM == 4 && TN == 2 && NOPS == 2 && UA == 2 && UB == 2) {
+            // 256 x 256 GEMM tile on 8 waves of 128 x 64: the step's 4 global loads spread over the first
+            // slice's 8 MFMAs with 4 of the second slice's 6 LDS reads between them, then the 4 LDS
+            // stores of the next step over the second slice's MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads of the first slice
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read of the second slice
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the second slice's other LDS reads
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS store
+            }
+        }
         if constexpr (NOBRANCH && NPROD == 1 && TM == 4 && TN == 4 && NOPS == 2 && UA == 4 && UB == 4) {
             // 256 x 256 GEMM tile: spread the 8 global loads over the first slice's 16 MFMAs, with
             // the second slice's 8 LDS reads between them, and the 8 LDS stores of the next step
@@ -505,7 +526,7 @@ __device__ __forceinline__ void add_upper_tile(const f32x16_t a, int64_t rb, int
 }
 
 // Phase 1: Y^T tile (rows = output features i, cols = tokens t), split into hi/lo.
-constexpr int G_BM = 256, G_THREADS = 256, G_WGM = 2;
+constexpr int G_BM = 256, G_THREADS = 512, G_WGM = 2;
 constexpr int G_GT = 8;  // token tiles per group of the launch order
 
 // Tile (i, t) of block b in a 1-D launch of gi x gt tiles.  Workgroups go to the 8 XCDs in turn
@@ -526,7 +547,7 @@ __device__ __forceinline__ void gemm_tile_of(int64_t b, int64_t gi, int64_t gt, 
     t = t0 + r % gte;
 }
 template <int BM, bool KCHECK>
-__global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const bf16_t *__restrict__ X, int64_t ldx,
              int64_t tc, const int32_t *__restrict__ ex, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo) {
     using Cfg = MfmaCfg<BM, BM, G_THREADS, G_WGM>;

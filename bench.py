@@ -424,8 +424,10 @@ def main():
                     help="decompose each group of matrices (grouped by output width and rank) as soon as its "
                          "covariances are done, on a side stream from a host thread of its own, while the "
                          "remaining covariances run")
-    ap.add_argument("--overlap-order", choices=("large-first", "most-first"), default="large-first",
-                    help="group order: largest n first, or the group with the most matrices first")
+    ap.add_argument("--overlap-order", choices=("small-first", "large-first", "most-first"), default="large-first",
+                    help="small-first: the groups of one output width decomposed in one call (the library "
+                         "tridiagonalises matrices of one order in lockstep), narrow widths first; large-first / "
+                         "most-first: one group at a time, largest n or most matrices first")
     ap.add_argument("--factored-steps", type=int, default=2,
                     help="timed steps of the variant that forms the covariances from X^T X (0: skip)")
     ap.add_argument("--eig-range", choices=("on", "off"), default="on",
@@ -501,12 +503,19 @@ def main():
     gkey = "+".join("%dx%d_k%d" % (len(ms), g[0], g[1]) for g, ms in groups.items())
     # overlap: covariances group by group, largest n first; each group's eigendecompositions and
     # error curves on a side stream of its own (default priority) with a workspace of its own
-    g_order = sorted(groups, key=lambda g: -g[0] if a.overlap_order == "large-first" else len(groups[g]) * -1)
-    side = {g: torch.cuda.Stream(device=dev) for g in groups}
-    ws_eig_g = {g: torch.empty(lrc.lrc_eigh_multi_workspace(
-        [(g[0], len(groups[g]), g[1], sh[groups[g][0]][0] if g in gW else 0)], prec), dtype=torch.uint8, device=dev)
-        for g in groups} if a.overlap == "on" else {}
+    # phases: the covariances of a phase's groups, then (on a side stream) one call decomposing them all
+    if a.overlap_order == "small-first":  # groups of one output width together, narrow widths first
+        widths = sorted({g[0] for g in groups})
+        phases = [[g for g in groups if g[0] == wd] for wd in widths]
+    else:
+        g_order = sorted(groups, key=lambda g: -g[0] if a.overlap_order == "large-first" else len(groups[g]) * -1)
+        phases = [[g] for g in g_order]
+    side = [torch.cuda.Stream(device=dev) for _ in phases]
+    ws_eig_g = [torch.empty(lrc.lrc_eigh_multi_workspace(
+        [(g[0], len(groups[g]), g[1], sh[groups[g][0]][0] if g in gW else 0) for g in ph], prec), dtype=torch.uint8,
+        device=dev) for ph in phases] if a.overlap == "on" else []
     gname = {g: "%dx%d_k%d" % (len(groups[g]), g[0], g[1]) for g in groups}
+    pname = ["+".join(gname[g] for g in ph) for ph in phases]
     kcap = {m: (di * do) // (di + do) for m, (di, do) in sh.items()}
     offs_h = [0] + list(np.cumsum([kcap[m] for m in MATS]))
     offs = torch.tensor(offs_h, dtype=torch.int64, device=dev)
@@ -536,16 +545,18 @@ def main():
         e1 = ev(stream)
         times.append((m + ".cov", e0, e1))
 
-    def eig_group(g, ready, times):
+    def eig_group(pi, ready, times):
         # runs on a host thread of its own: the library call returns once its launches are
         # enqueued, which takes about as long as they run
-        sg = side[g]
+        sg = side[pi]
         sg.wait_event(ready)
         e0 = ev(sg)
-        lrc.lrc_eigh_multi([eig_groups[list(groups).index(g)]], prec=prec, ws=ws_eig_g[g], stream=sg)
-        lrc.lrc_error_curve(glam[g], eps=geps[g], stream=sg)
+        lrc.lrc_eigh_multi([eig_groups[list(groups).index(g)] for g in phases[pi]], prec=prec, ws=ws_eig_g[pi],
+                           stream=sg)
+        for g in phases[pi]:
+            lrc.lrc_error_curve(glam[g], eps=geps[g], stream=sg)
         e1 = ev(sg)
-        times.append(("eigh." + gname[g], e0, e1))
+        times.append(("eigh." + pname[pi], e0, e1))
 
     def tail(times):
         for m in MATS:
@@ -568,16 +579,17 @@ def main():
     def step(times):
         if a.overlap == "on":
             threads = []
-            for g in g_order:
-                for m in groups[g]:
-                    cov(m, times)
-                t = threading.Thread(target=eig_group, args=(g, ev(stream), times))
+            for pi, ph in enumerate(phases):
+                for g in ph:
+                    for m in groups[g]:
+                        cov(m, times)
+                t = threading.Thread(target=eig_group, args=(pi, ev(stream), times))
                 t.start()
                 threads.append(t)
             for t in threads:
                 t.join()
-            for g in groups:
-                stream.wait_stream(side[g])
+            for sd in side:
+                stream.wait_stream(sd)
         else:
             for m in MATS:
                 cov(m, times)
@@ -791,7 +803,7 @@ def main():
         "overlap": a.overlap,
         "overlap_note": (("covariances group by group (%s), each group's eigendecompositions and error curves "
                           "on a side stream as soon as its covariances are done: cov_ms and eigh_ms are summed "
-                          "call times that overlap in the step" % ", ".join(gname[g] for g in g_order))
+                          "call times that overlap in the step" % ", ".join(pname))
                          if a.overlap == "on" else "covariances, then one call for every eigendecomposition"),
         "breakdown_ms": {k: round(v, 3) for k, v in avg.items()},
         "roofline": roof,
