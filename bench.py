@@ -42,19 +42,42 @@ def cov_flops(n_tok, d_in, d_out):
     return n_tok * (2 * d_in * d_out + d_out * (d_out + 1))
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter record, if the kernel's source is
-    unchanged since the counters were taken (else None)."""
+def _profile_record(name, source_key="source"):
+    """A committed rocprofv3 counter record under profiles/, if the kernel source it names is unchanged
+    since the counters were taken (else None)."""
     import hashlib
-    rec_path = os.path.join(ROOT, "profiles", "%s_traffic.json" % kernel)
     try:
-        rec = json.load(open(rec_path))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        rec = json.load(open(os.path.join(ROOT, "profiles", name)))
+        src = open(os.path.join(ROOT, rec[source_key]), "rb").read()
     except (OSError, ValueError, KeyError):
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def measured_traffic(kernel, algorithmic_bytes_per_launch=None):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE record. With the algorithmic bytes
+    per launch of this run given, the record's ratio of measured to algorithmic bytes scales them (for
+    a kernel whose launches carry a different amount of work here than in the counted run)."""
+    rec = _profile_record("%s_traffic.json" % kernel)
+    if rec is None:
+        return None
+    if algorithmic_bytes_per_launch is not None:
+        return rec["traffic_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"] * algorithmic_bytes_per_launch
+    return rec["traffic_bytes_per_launch"]
+
+
+def mfma_counters(kernel):
+    """Executed MFMA rate, shader clock and busy fraction from the committed counter record."""
+    rec = _profile_record("k_cov_mfma_counters.json")
+    if rec is None or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return {"executed_tflops": k["executed_mfma_tflops"], "shader_clock_ghz": k["shader_clock_ghz"],
+            "mfma_busy": k["mfma_busy_fraction"], "counted_launch_ms": k["mean_launch_ms"],
+            "source": "profiles/k_cov_mfma_counters.json (rocprofv3 MFMA and GRBM counters, one step with "
+                      "--overlap off)"}
 
 
 def _cpu_model():
@@ -743,17 +766,22 @@ def main():
                  "total_ms_per_step": syrk_ms / a.steps,
                  "per_launch": "algorithmic flops = tokens in the chunk x d_out (d_out + 1) (upper triangle incl. "
                                "diagonal); the kernel executes 3 fp16 MFMA products per flop pair (scaled hi/lo "
-                               "split: hi hi + hi lo + lo hi; the diagonal's sum of lo^2 is a separate pass), so "
-                               "executed MFMA utilisation is 3x frac"}
+                               "split: hi hi + hi lo + lo hi; the diagonal's sum of lo^2 is a separate pass)",
+                 "mfma_counters": mfma_counters("k_cov_syrk")}
     gemm_tf = gemm_fl / (gemm_ms / 1000.0) / 1e12 if gemm_ms > 0 else 0.0
     roof_gemm = {"kernel": "k_cov_gemm_y", "bound": "mfma", "achieved": gemm_tf, "peak": PEAK_BF16_TFLOPS,
                  "unit": "TFLOP/s", "frac": gemm_tf / PEAK_BF16_TFLOPS, "launches": gemm_n,
                  "avg_launch_ms": gemm_ms / max(gemm_n, 1),
                  "total_ms_per_step": gemm_ms / a.steps,
-                 "per_launch": "algorithmic flops = 2 x tokens in the chunk x d_in x d_out"}
+                 "per_launch": "algorithmic flops = 2 x tokens in the chunk x d_in x d_out",
+                 "mfma_counters": mfma_counters("k_cov_gemm_y")}
     symv_gbs = symv_by / (symv_ms / 1000.0) / 1e9 if symv_ms > 0 else 0.0
     roof_symv = {"kernel": "k_trd_symv", "bound": "hbm", "achieved": symv_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                 "frac": symv_gbs / PEAK_HBM_GBS, "traffic": measured_traffic("k_trd_symv"), "launches": symv_n,
+                 "frac": symv_gbs / PEAK_HBM_GBS,
+                 "traffic": measured_traffic("k_trd_symv", symv_by / max(symv_n, 1)) if symv_n else None,
+                 "traffic_note": "measured HBM bytes per algorithmic byte of the counted run (seven decompositions "
+                                 "per launch, profiles/k_trd_symv_traffic.json) x this run's algorithmic bytes per "
+                                 "launch", "launches": symv_n,
                  "avg_launch_ms": symv_ms / max(symv_n, 1),
                  "total_ms_per_step": symv_ms * a.timing_stride / a.steps,
                  "avg_bytes_per_launch": symv_by / max(symv_n, 1),

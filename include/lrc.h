@@ -179,6 +179,10 @@ lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64
  * Groups with n <= 128 run first, one Jacobi launch each, on `stream`; every member of
  *    the groups with n > 128 is then decomposed on the helper streams described under
  *    lrc_eigh, up to eight at once, largest n first.  `stream` waits for all of them.
+ *    When there are 2 to 8 such members and all have one tridiagonal order (n, or d_in
+ *    for a member decomposed through its range basis), their tridiagonalisations run in
+ *    lockstep on `stream`, one launch per column for all of them, before the rest of each
+ *    decomposition moves to the helper streams (environment LRC_EIGH_LOCKSTEP=0: off).
  *    Each member's result equals that of a call on the member alone, bit for bit.
  * Range basis (optional, per group; Swift-SVD page, section 2-ga: C = Y^T Y with Y = X W):
  *    W != NULL states that each member's C is (X W)^T (X W) for some X, with W (d_in x n,
