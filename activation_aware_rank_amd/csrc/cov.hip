@@ -12,7 +12,7 @@
 // contraction (token) axis.
 //
 // Paths:
-//   * generic: any dtype/alignment, fp32 arithmetic, LDS-tiled FMA (used for fp32 inputs).
+//   * fp32: any dtype/alignment, fp32 arithmetic on the 32x32x2 fp32 MFMA (used for fp32 inputs).
 //   * mfma (cov_mfma.hip): bf16 inputs with 16-byte aligned rows; bf16 MFMA for Y, each output
 //     scaled by a power of two and split into fp16 hi + lo, C += 2^-(e_i + e_j) (hi^T hi + hi^T lo +
 //     lo^T hi) with fp16 MFMA and fp32 accumulation, plus the diagonal's sum of lo^2 on its own.
@@ -21,9 +21,7 @@
 
 namespace lrc {
 
-constexpr int GT = 64;   // generic tile
-constexpr int GK = 16;   // generic k step
-constexpr int64_t GEN_CHUNK = 4096;  // tokens per generic chunk
+constexpr int64_t GEN_CHUNK = 4096;  // tokens per chunk of the fp32 path
 
 template <class XT>
 __device__ __forceinline__ float ld_as_f32(const XT *p, int64_t i);
@@ -32,99 +30,155 @@ __device__ __forceinline__ float ld_as_f32<bf16_t>(const bf16_t *p, int64_t i) {
 template <>
 __device__ __forceinline__ float ld_as_f32<float>(const float *p, int64_t i) { return p[i]; }
 
-// Y^T[i][t] = sum_k X[t0+t][k] W[k][i]  (W == nullptr: Y^T[i][t] = X[t0+t][i])
+// fp32 MFMA path (fp32 inputs, and bf16 inputs the bf16 MFMA path cannot take): 128 x 128 block
+// tiles on 4 waves of 64 x 64, each 2 x 2 tiles of the 32x32x2 fp32 MFMA (one product per lane and
+// k slice, fp32 accumulation, so the same arithmetic as an fp32 FMA chain), k steps of FK staged
+// k-major in two LDS buffers; the next step's values are loaded into registers while the current
+// step's MFMAs run.
+constexpr int FT = 128;      // block tile
+constexpr int FK = 16;       // k step
+constexpr int FLD = FT + 1;  // padded LDS row
+constexpr int FPT = FT * FK / 256;  // values per thread and operand per step
+
+// Element (k, m) of an operand tile: KC operands are contiguous along k (X and Y^T rows: 16 threads
+// read 16 consecutive k of one row), the others along m (W rows).  Values past `rows` or `klen` are 0.
+template <class ET, bool KC>
+struct F32Operand {
+    const ET *p;
+    int64_t ld;
+    int rows;
+    __device__ __forceinline__ void load(int64_t k0, int64_t klen, float (&r)[FPT]) const {
+#pragma unroll
+        for (int u = 0; u < FPT; ++u) {
+            const int idx = int(threadIdx.x) + 256 * u;
+            const int k = KC ? idx % FK : idx / FT, m = KC ? idx / FK : idx % FT;
+            const int64_t kk = k0 + k;
+            r[u] = (m < rows && kk < klen) ? ld_as_f32(p, KC ? int64_t(m) * ld + kk : kk * ld + m) : 0.f;
+        }
+    }
+    __device__ __forceinline__ void store(const float (&r)[FPT], float (*s)[FLD]) const {
+#pragma unroll
+        for (int u = 0; u < FPT; ++u) {
+            const int idx = int(threadIdx.x) + 256 * u;
+            const int k = KC ? idx % FK : idx / FT, m = KC ? idx / FK : idx % FT;
+            s[k][m] = r[u];
+        }
+    }
+};
+
+// acc[x][y] = sum over k < klen of A(k, m) B(k, n) for the wave's 64 x 64 tile
+template <class OA, class OB>
+__device__ __forceinline__ void f32_mainloop(const OA &A, const OB &B, int64_t klen, f32x16_t (&acc)[2][2]) {
+    __shared__ float sa[2][FK][FLD], sb[2][FK][FLD];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f32x16_t{};
+    const int64_t nk = (klen + FK - 1) / FK;
+    if (nk <= 0) return;
+    float ra[FPT], rb[FPT];
+    A.load(0, klen, ra);
+    B.load(0, klen, rb);
+    A.store(ra, sa[0]);
+    B.store(rb, sb[0]);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = int(kt & 1);
+        if (kt + 1 < nk) {
+            A.load((kt + 1) * FK, klen, ra);
+            B.load((kt + 1) * FK, klen, rb);
+        }
+#pragma unroll
+        for (int kk = 0; kk < FK; kk += 2) {
+            const int k = kk + (lane >> 5);
+            const float a0 = sa[cur][k][wm + (lane & 31)], a1 = sa[cur][k][wm + 32 + (lane & 31)];
+            const float b0 = sb[cur][k][wn + (lane & 31)], b1 = sb[cur][k][wn + 32 + (lane & 31)];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        }
+        if (kt + 1 < nk) {  // the other buffer was last read before the previous barrier
+            A.store(ra, sa[cur ^ 1]);
+            B.store(rb, sb[cur ^ 1]);
+        }
+        __syncthreads();
+    }
+}
+
+// row and column of accumulator element r of lane `lane` in the wave's tile (x, y)
+__device__ __forceinline__ int f32_row(int x, int r, int lane) { return x * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
+__device__ __forceinline__ int f32_col(int y, int lane) { return y * 32 + (lane & 31); }
+
+// Y^T[i][t] = sum_k X[t0+t][k] W[k][i] for the chunk's tokens; block (i tile, t tile)
 template <class XT>
-__global__ void __launch_bounds__(256) k_gemm_y_generic(const XT *__restrict__ X, int64_t ldx, const XT *__restrict__ W,
-                                                        int64_t ldw, int64_t d_in, int64_t d_out, int64_t t0, int64_t tc,
-                                                        float *__restrict__ Yt, int64_t ldy) {
-    __shared__ float As[GK][GT + 1];  // W tile: k x i
-    __shared__ float Bs[GK][GT + 1];  // X tile: k x t
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    const int64_t i0 = int64_t(blockIdx.x) * GT, tt0 = int64_t(blockIdx.y) * GT;
-    if (!W) {
-        for (int e = threadIdx.x; e < GT * GT; e += 256) {
-            const int ii = e / GT, tt = e % GT;
-            const int64_t i = i0 + ii, t = tt0 + tt;
-            if (i < d_out && t < tc) Yt[i * ldy + t] = ld_as_f32(X, (t0 + t) * ldx + i);
-        }
-        return;
-    }
-    float acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < d_in; k0 += GK) {
-        for (int e = threadIdx.x; e < GK * GT; e += 256) {
-            const int kk = e / GT, c = e % GT;
-            const int64_t k = k0 + kk;
-            As[kk][c] = (k < d_in && i0 + c < d_out) ? ld_as_f32(W, k * ldw + i0 + c) : 0.f;
-            const int tt = e / GK, kk2 = e % GK;
-            const int64_t k2 = k0 + kk2;
-            Bs[kk2][tt] = (k2 < d_in && tt0 + tt < tc) ? ld_as_f32(X, (t0 + tt0 + tt) * ldx + k2) : 0.f;
-        }
-        __syncthreads();
+__global__ void __launch_bounds__(256) k_gemm_y_f32(const XT *__restrict__ X, int64_t ldx, const XT *__restrict__ W,
+                                                    int64_t ldw, int64_t d_in, int64_t d_out, int64_t t0, int64_t tc,
+                                                    float *__restrict__ Yt, int64_t ldy) {
+    const int64_t i0 = int64_t(blockIdx.x) * FT, tt0 = int64_t(blockIdx.y) * FT;
+    const F32Operand<XT, false> A{W + i0, ldw, int(std::min<int64_t>(FT, d_out - i0))};
+    const F32Operand<XT, true> B{X + (t0 + tt0) * ldx, ldx, int(std::min<int64_t>(FT, tc - tt0))};
+    f32x16_t acc[2][2];
+    f32_mainloop(A, B, d_in, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
 #pragma unroll
-        for (int kk = 0; kk < GK; ++kk) {
-            float a[4], b[4];
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a[q] = As[kk][ty * 4 + q];
-                b[q] = Bs[kk][tx * 4 + q];
+        for (int y = 0; y < 2; ++y) {
+            const int64_t t = tt0 + wn + f32_col(y, lane);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t i = i0 + wm + f32_row(x, r, lane);
+                if (i < d_out && t < tc) Yt[i * ldy + t] = acc[x][y][r];
             }
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[p][q] = fmaf(a[p], b[q], acc[p][q]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t i = i0 + ty * 4 + p, t = tt0 + tx * 4 + q;
-            if (i < d_out && t < tc) Yt[i * ldy + t] = acc[p][q];
         }
 }
 
-// C_h[r][c] += sum_t Y^T[h hd + r][t] Y^T[h hd + c][t] for r <= c (upper, incl. diagonal)
-__global__ void __launch_bounds__(256) k_syrk_generic(const float *__restrict__ Yt, int64_t ldy, int64_t tc,
-                                                      float *__restrict__ C, int64_t ldc, int64_t hd) {
+// Y^T[i][t] = X[t0+t][i] (no W: the covariance of X itself)
+template <class XT>
+__global__ void __launch_bounds__(256) k_copy_xt(const XT *__restrict__ X, int64_t ldx, int64_t d_out, int64_t t0,
+                                                 int64_t tc, float *__restrict__ Yt, int64_t ldy) {
+    __shared__ float tile[64][65];
+    const int64_t i0 = int64_t(blockIdx.x) * 64, tt0 = int64_t(blockIdx.y) * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {  // read along i (X rows), write along t
+        const int tt = e / 64, ii = e % 64;
+        tile[tt][ii] = (i0 + ii < d_out && tt0 + tt < tc) ? ld_as_f32(X, (t0 + tt0 + tt) * ldx + i0 + ii) : 0.f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int ii = e / 64, tt = e % 64;
+        if (i0 + ii < d_out && tt0 + tt < tc) Yt[(i0 + ii) * ldy + tt0 + tt] = tile[tt][ii];
+    }
+}
+
+// C_h[r][c] += sum_t Y^T[h hd + r][t] Y^T[h hd + c][t] for r <= c (upper, incl. diagonal); block
+// (I, J, h) with I <= J
+__global__ void __launch_bounds__(256) k_syrk_f32(const float *__restrict__ Yt, int64_t ldy, int64_t tc,
+                                                  float *__restrict__ C, int64_t ldc, int64_t hd) {
     const int I = blockIdx.x, J = blockIdx.y, h = blockIdx.z;
     if (I > J) return;
-    __shared__ float As[GK][GT + 1];
-    __shared__ float Bs[GK][GT + 1];
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    const int64_t r0 = int64_t(I) * GT, c0 = int64_t(J) * GT;
+    const int64_t r0 = int64_t(I) * FT, c0 = int64_t(J) * FT;
     const float *Yh = Yt + int64_t(h) * hd * ldy;
-    float acc[4][4] = {};
-    for (int64_t t0 = 0; t0 < tc; t0 += GK) {
-        for (int e = threadIdx.x; e < GK * GT; e += 256) {
-            const int rr = e / GK, kk = e % GK;
-            const int64_t t = t0 + kk;
-            As[kk][rr] = (t < tc && r0 + rr < hd) ? Yh[(r0 + rr) * ldy + t] : 0.f;
-            Bs[kk][rr] = (t < tc && c0 + rr < hd) ? Yh[(c0 + rr) * ldy + t] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < GK; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a[q] = As[kk][ty * 4 + q];
-                b[q] = Bs[kk][tx * 4 + q];
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[p][q] = fmaf(a[p], b[q], acc[p][q]);
-        }
-        __syncthreads();
-    }
+    const F32Operand<float, true> A{Yh + r0 * ldy, ldy, int(std::min<int64_t>(FT, hd - r0))};
+    const F32Operand<float, true> B{Yh + c0 * ldy, ldy, int(std::min<int64_t>(FT, hd - c0))};
+    f32x16_t acc[2][2];
+    f32_mainloop(A, B, tc, acc);
     float *Ch = C + int64_t(h) * hd * ldc;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t r = r0 + ty * 4 + p, c = c0 + tx * 4 + q;
-            if (r < hd && c < hd && r <= c) Ch[r * ldc + c] += acc[p][q];
+        for (int y = 0; y < 2; ++y) {
+            const int64_t c = c0 + wn + f32_col(y, lane);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t rr = r0 + wm + f32_row(x, r, lane);
+                if (rr < hd && c < hd && rr <= c) Ch[rr * ldc + c] += acc[x][y][r];
+            }
         }
 }
 
@@ -168,17 +222,28 @@ lrc_status cov_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
         const int64_t ldy = tcmax;
         for (int64_t t0 = 0; t0 < a.n_tok; t0 += tcmax) {
             const int64_t tc = std::min(tcmax, a.n_tok - t0);
-            dim3 g1(cdiv(a.d_out, GT), cdiv(tc, GT));
-            if (a.x_t == LRC_BF16)
-                hipLaunchKernelGGL(k_gemm_y_generic<bf16_t>, g1, dim3(256), 0, s, static_cast<const bf16_t *>(a.X), a.ldx,
-                                   static_cast<const bf16_t *>(a.W), a.ldw, a.d_in, a.d_out, t0, tc, Yt, ldy);
-            else
-                hipLaunchKernelGGL(k_gemm_y_generic<float>, g1, dim3(256), 0, s, static_cast<const float *>(a.X), a.ldx,
-                                   static_cast<const float *>(a.W), a.ldw, a.d_in, a.d_out, t0, tc, Yt, ldy);
-            LRC_LAUNCH_CHECK("k_gemm_y_generic");
-            dim3 g2(cdiv(hd, GT), cdiv(hd, GT), a.n_blocks);
-            hipLaunchKernelGGL(k_syrk_generic, g2, dim3(256), 0, s, Yt, ldy, tc, a.C, a.ldc, hd);
-            LRC_LAUNCH_CHECK("k_syrk_generic");
+            if (!a.W) {
+                dim3 g0(cdiv(a.d_out, 64), cdiv(tc, 64));
+                if (a.x_t == LRC_BF16)
+                    hipLaunchKernelGGL(k_copy_xt<bf16_t>, g0, dim3(256), 0, s, static_cast<const bf16_t *>(a.X), a.ldx,
+                                       a.d_out, t0, tc, Yt, ldy);
+                else
+                    hipLaunchKernelGGL(k_copy_xt<float>, g0, dim3(256), 0, s, static_cast<const float *>(a.X), a.ldx,
+                                       a.d_out, t0, tc, Yt, ldy);
+                LRC_LAUNCH_CHECK("k_copy_xt");
+            } else {
+                dim3 g1(cdiv(a.d_out, FT), cdiv(tc, FT));
+                if (a.x_t == LRC_BF16)
+                    hipLaunchKernelGGL(k_gemm_y_f32<bf16_t>, g1, dim3(256), 0, s, static_cast<const bf16_t *>(a.X),
+                                       a.ldx, static_cast<const bf16_t *>(a.W), a.ldw, a.d_in, a.d_out, t0, tc, Yt, ldy);
+                else
+                    hipLaunchKernelGGL(k_gemm_y_f32<float>, g1, dim3(256), 0, s, static_cast<const float *>(a.X), a.ldx,
+                                       static_cast<const float *>(a.W), a.ldw, a.d_in, a.d_out, t0, tc, Yt, ldy);
+                LRC_LAUNCH_CHECK("k_gemm_y_f32");
+            }
+            dim3 g2(cdiv(hd, FT), cdiv(hd, FT), a.n_blocks);
+            hipLaunchKernelGGL(k_syrk_f32, g2, dim3(256), 0, s, Yt, ldy, tc, a.C, a.ldc, hd);
+            LRC_LAUNCH_CHECK("k_syrk_f32");
         }
     }
     hipLaunchKernelGGL(k_cov_check, dim3(1), dim3(256), 0, s, a.C, a.ldc, hd, a.n_blocks, a.info);
