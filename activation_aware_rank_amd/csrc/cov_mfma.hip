@@ -28,7 +28,11 @@
 // accumulators and operands fit its registers without spills, and one wave's MFMAs run while the
 // other waits); the SYRK's is 128 x 128 on 4 waves; k step 32, double-buffered LDS with an XOR
 // swizzle of the 16-byte chunks (no padding, no bank conflicts on 16-byte reads), one barrier
-// per k step.
+// per k step, placed between the step's two k slices: the LDS reads of the next step's first
+// slice go out right after it and land while the current step's second slice is multiplied,
+// instead of stalling the next step's first MFMAs (GEMM 3-4 %, SYRK up to 4 % faster).  A
+// scheduling barrier at each step boundary keeps the compiler from moving a step's MFMAs past
+// the next step's wait for its loads (SYRK 3-4 % faster).
 //
 // Load balance of the SYRK: the upper triangle may have fewer tiles than the GPU has CUs, so
 // the token range of a chunk is split S ways; split s > 0 accumulates into its own fp32
@@ -48,12 +52,6 @@ constexpr int64_t MFMA_CHUNK = 32768;    // tokens per internal chunk
 // 5 % faster), MFMA_CHUNK above (at 11008 the larger chunk was 3 % slower).  2 MFMA_CHUNK x 8193
 // rows of Y^T stay below the 2^31-byte reach of a buffer resource.
 static int64_t chunk_tokens(int64_t d_out) { return d_out <= 8192 ? 2 * MFMA_CHUNK : MFMA_CHUNK; }
-#ifndef SYRK_FE
-#define SYRK_FE 4  // 16-token k slices per flush of the SYRK's MFMA chains
-#endif
-#ifndef SYRK_DEPTH
-#define SYRK_DEPTH 2
-#endif
 
 // 16-byte chunk c of row r: XOR with bits 1..3 of r so that 16 consecutive rows reading one chunk
 // column hit 16 distinct 16-byte bank groups (and 8 consecutive rows 8 distinct groups)
@@ -72,85 +70,46 @@ struct MfmaCfg {
     static_assert(UA * THREADS == BM * (MK / 8) && UB * THREADS == BN * (MK / 8), "operand tile / threads");
 };
 
-// acc[tm][tn] += sum over k in [0, klen) of A[row][k] B[col][k]; ops: {A(,Alo), B(,Blo)}.
-// NPROD 4 forms (Ahi + Alo)(Bhi + Blo)^T, NPROD 1 forms A B^T.
-// FLUSH: the MFMA chain of each 16-wide k slice starts from zero and its result is added to acc
-// with a round-to-nearest fp32 add, so a running sum over many tokens carries the error of one
-// fp32 addition per 16 tokens instead of a long chain of MFMA accumulations.  Otherwise the
-// MFMAs accumulate into acc directly (used where the contraction is short or the rounding
-// errors are not one-signed).
-// DEPTH: k steps of global loads in flight (1: the next step; 2: the next two, in two register
-// sets used alternately -- the k loop is unrolled by two so that every index is static).
-// TILED: the operands are in the MK-token block layout of Y^T (ld = rows per token block, D):
-// row r of step kt is at (kt * D + r) * MK; operand o's buffer resource covers nrec[o] < 2^31
-// bytes from its base.  Rows past rows[o] (those of the next head block) read zero: their byte
-// offsets start at 2^31, past every resource, so the mask costs no wait on the loaded data.  In
-// the row-major layout a k step reads 64 bytes of each of 16 rows per wave instruction; in the
-// block layout it reads 1 KB in one run, which halves the cache lines the loads touch.
-// NOBRANCH: the loads of step kt + DEPTH and the LDS store of step kt + 1 are issued in every
-// step, also past the last one (those loads read zeros or unused values and those stores go to
-// the buffer no wave reads any more).  With no branch around them the compiler counts the loads
-// in flight exactly and waits only for the older register set before storing it; behind a
-// branch it also waits for the loads just issued, which leaves one step of latency hiding.
-// Operands 0 .. NOPS/2-1 are A operands (BM rows), the rest B operands (BN rows); LDS holds two
-// buffers of NOPS/2 * (BM + BN) rows of MK elements.
-template <int BM, int BN, int THREADS, int WGM, int NOPS, int NPROD, bool FLUSH, int FE = 1, bool KCHECK = true,
-          int DEPTH = 1, bool NOBRANCH = false, bool TILED = false>
-__device__ __forceinline__ void mfma_mainloop(
-    const bf16_t *const *base, const int64_t *ld, const int *rows, int64_t klen, const int64_t *nrec,
-    f32x16_t (&acc)[MfmaCfg<BM, BN, THREADS, WGM>::TM][MfmaCfg<BM, BN, THREADS, WGM>::TN], bf16_t *lds) {
-    using T = MfmaCfg<BM, BN, THREADS, WGM>;
-    constexpr int TM = T::TM, TN = T::TN, UA = T::UA, UB = T::UB;
-    constexpr int U = UA > UB ? UA : UB;
-    constexpr int NSIDE = NOPS / 2;
-    static_assert(NSIDE * 2 == NOPS, "as many A as B operands");
-    // element offset of operand o inside one LDS buffer, and the buffer size
-    auto opoff = [](int o) { return o < NSIDE ? o * BM * MK : NSIDE * BM * MK + (o - NSIDE) * BN * MK; };
-    constexpr int BUFSZ = NSIDE * (BM + BN) * MK;
+// GEMM main loop (one bf16 product, operands A = W^T rows and B = X rows, both contiguous along k)
+// with the LDS reads of each step's first k slice issued before the previous step ends.  Global
+// loads run two steps ahead through two register sets; per step kt:
+//   loads of step kt+2; LDS reads of slice 2 of kt; MFMAs of slice 1 (its fragments were read at
+//   the end of step kt-1); LDS stores of step kt+1 into the other buffer; every wave's LDS reads
+//   and stores done, barrier; LDS reads of slice 1 of kt+1; MFMAs of slice 2 of kt.
+// so the reads after the barrier are in flight while slice 2's MFMAs run instead of stalling the
+// first MFMAs of the next step.  A buffer is stored only after the barrier that follows the last
+// reads of it (slice 2 of its previous step, waited for before that barrier).
+template <int BM, int THREADS, int WGM, bool KCHECK>
+__device__ __forceinline__ void gemm_mainloop(const bf16_t *const *base, const int64_t *ld, const int *rows,
+                                              int64_t klen,
+                                              f32x16_t (&acc)[MfmaCfg<BM, BM, THREADS, WGM>::TM][MfmaCfg<BM, BM, THREADS, WGM>::TN],
+                                              bf16_t *lds) {
+    using T = MfmaCfg<BM, BM, THREADS, WGM>;
+    constexpr int TM = T::TM, TN = T::TN, U = T::UA;
+    static_assert(T::UA == T::UB, "square block tile");
+    constexpr int BUFSZ = 2 * BM * MK;  // one buffer: A then B, BM rows of MK elements each
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / T::WGN, wn = wave % T::WGN;
     const int nk = int((klen + MK - 1) / MK);
-    u32x4_t regs[DEPTH][NOPS][U];
-    // One buffer resource per operand, ending at element klen - 1 of its last row: a load past
-    // that returns zero without a branch (and never touches memory after the operand).  Offsets
-    // are 32-bit byte offsets from the operand's first row (the host keeps rows * ld * 2 below
-    // 2^31).
-    __amdgpu_buffer_rsrc_t rs[NOPS];
+    if (nk <= 0) return;
+    __amdgpu_buffer_rsrc_t rs[2];
 #pragma unroll
-    for (int o = 0; o < NOPS; ++o)
+    for (int o = 0; o < 2; ++o)
         rs[o] = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<bf16_t *>(base[o]), short(0),
-            int(TILED ? nrec[o] : rows[o] > 0 ? ((int64_t(rows[o]) - 1) * ld[o] + klen) * 2 : int64_t(0)), 0x00020000);
-
-    // TILED: per operand and chunk, the byte offset of its row at step 0 (2^31 for masked rows)
-    uint32_t roff[NOPS][U];
-    if constexpr (TILED) {
-#pragma unroll
-        for (int o = 0; o < NOPS; ++o)
-#pragma unroll
-            for (int u = 0; u < (o < NSIDE ? UA : UB); ++u) {
-                const int q = tid + THREADS * u;
-                const int r = q >> 2, c = q & 3;
-                roff[o][u] = r < rows[o] ? uint32_t((r * MK + c * 8) * 2) : 0x80000000u;
-            }
-    }
+            int(rows[o] > 0 ? ((int64_t(rows[o]) - 1) * ld[o] + klen) * 2 : int64_t(0)), 0x00020000);
+    u32x4_t regs[2][2][U];
     auto gload = [&](int kt, auto set) {
         constexpr int S = decltype(set)::value;
         const int k0 = kt * MK;
 #pragma unroll
-        for (int o = 0; o < NOPS; ++o)
+        for (int o = 0; o < 2; ++o)
 #pragma unroll
-            for (int u = 0; u < (o < NSIDE ? UA : UB); ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int q = tid + THREADS * u;
                 const int r = q >> 2, c = q & 3;
                 const int k = k0 + c * 8;
-                u32x4_t v;
-                if constexpr (TILED) {
-                    const uint32_t off = roff[o][u] + uint32_t(kt) * uint32_t(ld[o] * MK * 2);
-                    v = __builtin_amdgcn_raw_buffer_load_b128(rs[o], int(off), 0, 0);
-                } else {
-                    v = __builtin_amdgcn_raw_buffer_load_b128(rs[o], (r * int(ld[o]) + k) * 2, 0, 0);
-                }
+                u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs[o], (r * int(ld[o]) + k) * 2, 0, 0);
                 if (KCHECK && k >= klen) v = u32x4_t{0u, 0u, 0u, 0u};
                 regs[S][o][u] = v;
             }
@@ -158,139 +117,80 @@ __device__ __forceinline__ void mfma_mainloop(
     auto sstore = [&](int buf, auto set) {
         constexpr int S = decltype(set)::value;
 #pragma unroll
-        for (int o = 0; o < NOPS; ++o)
+        for (int o = 0; o < 2; ++o)
 #pragma unroll
-            for (int u = 0; u < (o < NSIDE ? UA : UB); ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int q = tid + THREADS * u;
                 const int r = q >> 2, c = q & 3;
-                *reinterpret_cast<u32x4_t *>(lds + buf * BUFSZ + opoff(o) + swz(r, c)) = regs[S][o][u];
+                *reinterpret_cast<u32x4_t *>(lds + buf * BUFSZ + o * BM * MK + swz(r, c)) = regs[S][o][u];
             }
     };
-
-    if (nk <= 0) return;
-    // FLUSH: p holds the MFMA chain of the last FE 16-wide k slices (FE = 1, 2 or 4)
-    f32x16_t p[TM][TN];
+    bf16x8_t f1a[TM], f1b[TN], f2a[TM], f2b[TN];  // fragments of slices 1 and 2
+    auto fread = [&](int buf, int ks, bf16x8_t (&fa)[TM], bf16x8_t (&fb)[TN]) {
+        const bf16_t *sb = lds + buf * BUFSZ;
+        const int c = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+        for (int t = 0; t < TM; ++t)
+            fa[t] = *reinterpret_cast<const bf16x8_t *>(sb + swz(wm * T::WM + t * 32 + (lane & 31), c));
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) p[tm][tn] = f32x16_t{};
-    auto flush = [&]() {
+        for (int t = 0; t < TN; ++t)
+            fb[t] = *reinterpret_cast<const bf16x8_t *>(sb + BM * MK + swz(wn * T::WN + t * 32 + (lane & 31), c));
+    };
+    auto mfmas = [&](const bf16x8_t (&fa)[TM], const bf16x8_t (&fb)[TN]) {
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[tm][tn][r] = __fadd_rn(acc[tm][tn][r], p[tm][tn][r]);
-            }
+            for (int tn = 0; tn < TN; ++tn)
+                acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     gload(0, I0{});
     sstore(0, I0{});
-    if constexpr (DEPTH == 2) {
-        if (NOBRANCH || nk > 1) gload(1, I1{});
-    }
-    __syncthreads();
-    constexpr int NA = (NPROD == 4) ? 2 : 1;
-    // one k step from LDS buffer cur; loads of step kt + DEPTH go to register set lset, and step
-    // kt + 1 is stored from register set sset
-    // par: the step's position in the unrolled pair (static); with FE 4 a flush group is the pair
-    auto step = [&](int kt, int cur, auto lset, auto sset, auto par) {
-        constexpr int PAR = decltype(par)::value;
-        if (NOBRANCH || kt + DEPTH < nk) gload(kt + DEPTH, lset);
-        // keep the loads at the top of the step, ahead of this step's MFMAs
-        if constexpr (NOBRANCH) __builtin_amdgcn_sched_barrier(0);
-        const bf16_t *sb = lds + cur * BUFSZ;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int c = ks * 2 + (lane >> 5);
-            bf16x8_t af[NA][TM], bfr[NA][TN];
-#pragma unroll
-            for (int a = 0; a < NA; ++a) {
-#pragma unroll
-                for (int t = 0; t < TM; ++t)
-                    af[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + opoff(a) +
-                                                                   swz(wm * T::WM + t * 32 + (lane & 31), c));
-#pragma unroll
-                for (int t = 0; t < TN; ++t)
-                    bfr[a][t] = *reinterpret_cast<const bf16x8_t *>(sb + opoff(NSIDE + a) +
-                                                                    swz(wn * T::WN + t * 32 + (lane & 31), c));
-            }
-#pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    // a flush group's first slice starts the chain from a literal zero
-                    const bool fresh = FLUSH && (FE == 1 || (FE == 2 && ks == 0) || (FE == 4 && PAR == 0 && ks == 0));
-                    f32x16_t q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        af[0][tm], bfr[0][tn], fresh ? f32x16_t{} : (FLUSH ? p[tm][tn] : acc[tm][tn]), 0, 0, 0);
-                    if (NPROD == 4) {
-                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][tm], bfr[1][tn], q, 0, 0, 0);
-                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[0][tn], q, 0, 0, 0);
-                        q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][tm], bfr[1][tn], q, 0, 0, 0);
-                    }
-                    if (FLUSH)
-                        p[tm][tn] = q;
-                    else
-                        acc[tm][tn] = q;
-                }
-            if (FLUSH && FE == 1) flush();
-        }
-        if (FLUSH && (FE == 2 || (FE == 4 && PAR == 1))) flush();
-        if (NOBRANCH || kt + 1 < nk) sstore(cur ^ 1, sset);
-        if constexpr (NOBRANCH && NPROD == 1 && TM == 4 && TN == 2 && NOPS == 2 && UA == 2 && UB == 2) {
-            // 256 x 256 GEMM tile on 8 waves of 128 x 64: the step's 4 global loads spread over the first
-            // slice's 8 MFMAs with 4 of the second slice's 6 LDS reads between them, then the 4 LDS
-            // stores of the next step over the second slice's MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads of the first slice
+    gload(1, I1{});
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    fread(0, 0, f1a, f1b);
+    // step kt: data in buffer kt & 1; its slice-1 fragments already in f1; the loads of step kt+1
+    // are in register set (kt+1) & 1 and those of kt+2 go to set kt & 1 (stored at step kt-1).
+    // Every load, store and read is issued in every step (past the end the loads return zero and
+    // the stores and reads touch buffers no later step uses), so the compiler counts the loads in
+    // flight exactly.
+    auto step = [&](int kt, auto lset, auto sset) {
+        const int cur = kt & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        gload(kt + 2, lset);
+        fread(cur, 1, f2a, f2b);
+        mfmas(f1a, f1b);
+        sstore(cur ^ 1, sset);
+        // 256 x 256 tile on 8 waves of 128 x 64: the 4 global loads and the 6 slice-2 reads among
+        // the first 4 MFMAs, the 4 LDS stores among the last 4
+        if constexpr (TM == 4 && TN == 2 && U == 2) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);  // global loads
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads of slice 2
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read of the second slice
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the second slice's other LDS reads
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS store
             }
         }
-        if constexpr (NOBRANCH && NPROD == 1 && TM == 4 && TN == 4 && NOPS == 2 && UA == 4 && UB == 4) {
-            // 256 x 256 GEMM tile: spread the 8 global loads over the first slice's 16 MFMAs, with
-            // the second slice's 8 LDS reads between them, and the 8 LDS stores of the next step
-            // over the second slice's MFMAs (9 % faster than the compiler's own order)
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads of the first slice
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read of the second slice
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS store
-            }
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        fread(cur ^ 1, 0, f1a, f1b);
+        mfmas(f2a, f2b);
+        if constexpr (TM == 4 && TN == 2) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads of the next slice 1
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMAs of slice 2
         }
-        __syncthreads();
     };
-    static_assert(FE != 4 || DEPTH == 2, "a 64-token flush group needs the unrolled pair");
-    if constexpr (DEPTH == 1) {
-        for (int kt = 0; kt < nk; ++kt) step(kt, kt & 1, I0{}, I0{}, I0{});
-    } else {
-        // pairs of steps, then a lone last step when nk is odd (outside the loop, so that no path
-        // through the loop body skips a step and the compiler's count of loads in flight stays exact)
-        int kt = 0;
-        for (; kt + 1 < nk; kt += 2) {
-            step(kt, 0, I0{}, I1{}, I0{});
-            step(kt + 1, 1, I1{}, I0{}, I1{});
-        }
-        if (kt < nk) {
-            step(kt, 0, I0{}, I1{}, I0{});
-            if (FLUSH && FE == 4) flush();  // the last group had only its first step
-        }
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        step(kt, I0{}, I1{});
+        step(kt + 1, I1{}, I0{});
     }
+    if (kt < nk) step(kt, I0{}, I1{});
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // SYRK main loop with the operands loaded straight into LDS (16-byte buffer loads with an LDS
@@ -303,24 +203,25 @@ __device__ __forceinline__ void mfma_mainloop(
 // A wave's 16-byte load of row r lands at lds + r * 64 + 16 * (lane & 3) (linear in the lane), so
 // the XOR swizzle of swz() is applied to the global side: that lane loads chunk (lane & 3) ^ f(r).
 // Rows past rows[o] read zero through an offset of 2^31, past every operand's resource.
-// FE 4: the MFMA chains restart every 64 tokens (two steps) and are added to acc with one
-// round-to-nearest fp32 add, as in mfma_mainloop.
+// The MFMA chains restart from zero every 64 tokens (two steps) and their sums are added to acc
+// with one round-to-nearest fp32 add, so a running sum over many tokens carries the error of one
+// fp32 addition per 64 tokens instead of a long chain of MFMA accumulations.
 // NST 2: two stages and loads one step ahead, for kernels that share a CU two at a time (the other
-// workgroup's MFMAs run while one waits); each wave then also waits for its own LDS reads of the
-// stage the next loads overwrite before the barrier.
+// workgroup's MFMAs run while one waits), with each step's first LDS reads issued before the
+// previous step ends (step2 below).
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // s_waitcnt with vmcnt = n (0..63) and no wait on the other counters (gfx9 encoding)
 #define LRC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-template <int BM, int BN, int NOPS, int NPROD, int NST>
+template <int BM, int BN, int NOPS, int NPROD, int NST, int THREADS, int WGM>
 __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, const int64_t D, const int *rows,
                                                   int64_t klen, const int64_t *nrec,
-                                                  f32x16_t (&acc)[MfmaCfg<BM, BN, 256, 2>::TM][MfmaCfg<BM, BN, 256, 2>::TN],
+                                                  f32x16_t (&acc)[MfmaCfg<BM, BN, THREADS, WGM>::TM][MfmaCfg<BM, BN, THREADS, WGM>::TN],
                                                   bf16_t *lds0, bf16_t *lds1, bf16_t *lds2) {
-    using T = MfmaCfg<BM, BN, 256, 2>;
-    constexpr int THREADS = 256;
+    using T = MfmaCfg<BM, BN, THREADS, WGM>;
+    constexpr int RPU = 16 * (THREADS / 64);  // rows of an operand covered by one load per thread
     constexpr int TM = T::TM, TN = T::TN, UA = T::UA, UB = T::UB;
     constexpr int U = UA > UB ? UA : UB;
     constexpr int NSIDE = NOPS / 2;
@@ -348,7 +249,7 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
         rs[o] = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base[o]), short(0), int(nrec[o]), 0x00020000);
 #pragma unroll
         for (int u = 0; u < (o < NSIDE ? UA : UB); ++u) {
-            const int r = 16 * wave + (lane >> 2) + 64 * u;  // row of this lane's 16 bytes
+            const int r = 16 * wave + (lane >> 2) + RPU * u;  // row of this lane's 16 bytes
             const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
             roff[o][u] = r < rows[o] ? uint32_t((r * MK + c * 8) * 2) : 0x80000000u;
         }
@@ -361,7 +262,7 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
 #pragma unroll
             for (int u = 0; u < (o < NSIDE ? UA : UB); ++u)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs[o], (lds_void_t *)(st + opoff(o) + (16 * wave + 64 * u) * MK), 16,
+                    rs[o], (lds_void_t *)(st + opoff(o) + (16 * wave + RPU * u) * MK), 16,
                     int(roff[o][u] + uint32_t(kt) * kstride), 0, 0, 0);
     };
     f32x16_t p[TM][TN];
@@ -381,18 +282,12 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
     // loads of step kt + 2 into `nxt`, then the MFMAs from `cur`; PAR: position in the flush group
     auto step = [&](int kt, const bf16_t *cur, bf16_t *nxt, auto par) {
         constexpr int PAR = decltype(par)::value;
-        if constexpr (NST == 3) {
-            LRC_WAIT_VMCNT(LPS);
-            lds_barrier();
-            issue(kt + 2, nxt);
-        } else {
-            // two stages: this wave's loads of step kt and its LDS reads of step kt - 1 (from the
-            // stage the loads of step kt + 1 overwrite) complete before the barrier
-            LRC_WAIT_VMCNT(0);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            lds_barrier();
-            issue(kt + 1, nxt);
-        }
+        // nothing moves across a step boundary: the wait below is for loads issued a step earlier,
+        // and MFMAs of the previous step scheduled after it would wait for them too
+        __builtin_amdgcn_sched_barrier(0);
+        LRC_WAIT_VMCNT(LPS);
+        lds_barrier();
+        issue(kt + 2, nxt);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int c = ks * 2 + (lane >> 5);
@@ -435,30 +330,85 @@ __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, con
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);  // MFMAs of the second slice
         }
-        if constexpr (NST == 2 && NPROD == 3 && LPS == 8 && NA * (TM + TN) == 8 && TM * TN * NPROD == 12) {
-            // 128 x 128 split tile, two stages: the same, 8 loads over 12 MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads of the first slice
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // loads into LDS
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads of the second slice
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);  // MFMAs of the second slice
-        }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    // Two stages, with the LDS reads of each step's first slice issued before the previous step
+    // ends.  Step kt (its slice-1 fragments read at the end of step kt-1): slice-2 reads of kt and
+    // slice-1 MFMAs; this wave's loads of step kt+1 and its LDS reads done, barrier; loads of step
+    // kt+2 into the stage of kt (read completely before the barrier); slice-1 reads of kt+1; slice-2
+    // MFMAs of kt.  The loads of a step have one step of MFMAs to land, and the reads after the
+    // barrier are in flight while the slice-2 MFMAs run instead of stalling the next step's first.
+    OpT f1a[NA][TM], f1b[NA][TN], f2a[NA][TM], f2b[NA][TN];
+    auto fread = [&](const bf16_t *st, int ks, OpT (&fa)[NA][TM], OpT (&fb)[NA][TN]) {
+        const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+                fa[a][t] = *reinterpret_cast<const OpT *>(st + opoff(a) + swz(wm * T::WM + t * 32 + (lane & 31), c));
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+                fb[a][t] = *reinterpret_cast<const OpT *>(st + opoff(NSIDE + a) + swz(wn * T::WN + t * 32 + (lane & 31), c));
+        }
+    };
+    auto mfmas = [&](const OpT (&fa)[NA][TM], const OpT (&fb)[NA][TN], bool fresh) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                f32x16_t q = mfma(fa[0][tm], fb[0][tn], fresh ? f32x16_t{} : p[tm][tn]);
+                if (NPROD == 3) {
+                    q = mfma(fa[0][tm], fb[1][tn], q);
+                    q = mfma(fa[1][tm], fb[0][tn], q);
+                }
+                p[tm][tn] = q;
+            }
+    };
+    auto step2 = [&](int kt, bf16_t *cur, const bf16_t *nxt, auto par) {
+        constexpr int PAR = decltype(par)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        fread(cur, 1, f2a, f2b);
+        mfmas(f1a, f1b, PAR == 0);  // a flush group's first slice starts its chains from zero
+        if constexpr (NPROD == 3 && NA * (TM + TN) == 8 && TM * TN == 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads of slice 2
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        LRC_WAIT_VMCNT(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + 2, cur);
+        fread(nxt, 0, f1a, f1b);
+        mfmas(f2a, f2b, false);
+        if constexpr (NPROD == 3 && NA * (TM + TN) == 8 && TM * TN == 4 && LPS == 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // loads into LDS
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads of the next slice 1
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
+            }
+        }
+        if (PAR == 1) flush();
+    };
     if constexpr (NST == 2) {
         // stages 0 1 0 1 ..., flush-group positions 0 1 0 1 ...
         issue(0, lds0);
+        LRC_WAIT_VMCNT(0);
+        lds_barrier();
+        issue(1, lds1);
+        fread(lds0, 0, f1a, f1b);
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
-            step(kt, lds0, lds1, I0{});
-            step(kt + 1, lds1, lds0, I1{});
+            step2(kt, lds0, lds1, I0{});
+            step2(kt + 1, lds1, lds0, I1{});
         }
         if (kt < nk) {
-            step(kt, lds0, lds1, I0{});
+            step2(kt, lds0, lds1, I0{});
             flush();  // the last flush group had only its first step
         }
         // the loads issued past the last step still write LDS: let them land before the epilogue
@@ -563,7 +513,7 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
     for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
-    mfma_mainloop<BM, BM, G_THREADS, G_WGM, 2, 1, false, 1, KCHECK, 2, true>(base, ld, rows, d_in, nullptr, acc, lds);
+    gemm_mainloop<BM, G_THREADS, G_WGM, KCHECK>(base, ld, rows, d_in, acc, lds);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm)
@@ -590,21 +540,21 @@ __host__ __device__ __forceinline__ int syrk_tiles(int hd) {
     for (int J = 0; J < nJ; ++J) n += syrk_col_tiles<BM, BN>(J, nI);
     return n;
 }
-template <int BM, int BN>
-struct SyrkCfg {  // 4 waves of (BM/2) x (BN/2)
-    static constexpr int THREADS = 256;
-    static constexpr int WGM = 2;
+template <int BM, int BN, int THREADS>
+struct SyrkCfg {  // 4 waves of (BM/2) x (BN/2), or 8 waves of (BM/4) x (BN/2)
+    static constexpr int WGM = THREADS == 512 ? 4 : 2;
 };
 // SPLIT: Y^T as fp16 hi/lo with the row exponents ex, three products (the diagonal's sum of lo^2
 // is added by k_lo_sq_add); else Y^T = X^T in bf16, one product.
 // NST: LDS stages of the main loop; 2 lets two workgroups share a CU (65536 bytes of LDS each).
-template <int BM, int BN, bool SPLIT, int NST>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NST == 2 ? 2 : 1, NST == 2 ? 2 : 1)))
+template <int BM, int BN, bool SPLIT, int NST, int THREADS = 256>
+__global__ void __launch_bounds__(THREADS)
+__attribute__((amdgpu_waves_per_eu(NST == 2 || THREADS == 512 ? 2 : 1, NST == 2 || THREADS == 512 ? 2 : 1)))
 k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, const int32_t *__restrict__ ex,
            int64_t ldy, int64_t ktot, int64_t kchunk, int64_t hd, float *__restrict__ C, int64_t ldc,
            float *__restrict__ P, int32_t n_blocks, int32_t xcd_order) {
-    constexpr int THREADS = SyrkCfg<BM, BN>::THREADS, WGM = SyrkCfg<BM, BN>::WGM;
-    static_assert(THREADS == 256, "launch bounds");
+    constexpr int WGM = SyrkCfg<BM, BN, THREADS>::WGM;
+    static_assert(THREADS == 256 || THREADS == 512, "launch bounds");
     using Cfg = MfmaCfg<BM, BN, THREADS, WGM>;
     constexpr int NOPS = SPLIT ? 4 : 2;
     constexpr int STAGE = (NOPS / 2) * (BM + BN) * MK;  // elements of one LDS stage
@@ -703,7 +653,7 @@ k_cov_syrk(const bf16_t *__restrict__ Yhi, const bf16_t *__restrict__ Ylo, const
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
     // klen is a multiple of MK here, so no k check is needed
-    syrk_dma_mainloop<BM, BN, NOPS, SPLIT ? 3 : 1, NST>(base, D, rows, klen, nrec, acc, lds0, lds1, lds2);
+    syrk_dma_mainloop<BM, BN, NOPS, SPLIT ? 3 : 1, NST, THREADS, WGM>(base, D, rows, klen, nrec, acc, lds0, lds1, lds2);
     float *dst;
     int64_t ldd;
     if (s == 0) {
