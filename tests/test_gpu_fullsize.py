@@ -9,6 +9,8 @@ hold at any size:
 * one 4096 x 4096 matrix of a stack layer at its 65536 calibration tokens (k = 1228): everything
   against the oracle in full -- its fp64 covariance and cyclic Jacobi eigendecomposition give the
   eigenvalues, the error curve, the retained subspace and the direct error;
+* the gate shape at a quarter of its size (1024 -> 2752, 16384 tokens) through the basis of
+  range(W^T), as bench.py decomposes gate and up: the same comparisons with the oracle in full;
 * LLaMA-7B block at 524288 tokens (q_proj 4096 -> 4096, k = 1228; gate_proj 4096 -> 11008,
   k = 1791, by the full decomposition and through a basis of range(W^T) as bench.py runs it),
   inputs drawn on the GPU as bench.py draws them: sampled covariance entries against the oracle's
@@ -113,6 +115,48 @@ def test_q_proj_65536_tokens_vs_oracle(lrc):
     lrc.lrc_factorize(Wd, V, k, A, B)
     lam_h, V_h, eps_h, A_h, B_h = host(lam), host(V), host(eps)[0], host(A), host(B)
     del Xd, Wd, C, V, A, B
+    Cr = oracle.covariance(X, "bf16", W, "bf16")
+    lam_r, V_r = oracle.eigh_large(Cr)
+    eps_r = oracle.error_curve(lam_r)
+    el = check_lambda(lam_h, lam_r)
+    e_big, e_small = check_eps(eps_h, eps_r, prec=1)
+    s = sin_theta_max(V_h, V_r, k)
+    W64 = oracle.widen(W, "bf16")
+    direct = oracle.direct_error(X, "bf16", W64, A_h.astype(np.float64) @ B_h.astype(np.float64))
+    print("lambda err %.2e lambda_max, eps rel %.2e, tail %.2e eps_0, sin theta(k=%d) %.2e, "
+          "gap (lam_k - lam_k+1)/lam_1 %.2e, direct/eps_k - 1 = %.2e"
+          % (el, e_big, e_small, k, s, gap(lam_r, k), direct / eps_r[k] - 1))
+    assert s <= 1e-3
+    assert abs(direct - eps_r[k]) <= 1e-4 * eps_r[k] + 1e-6 * eps_r[0]
+
+
+@pytest.mark.timeout(900)
+def test_range_basis_gate_shape_vs_oracle(lrc):
+    """The gate/up shape at a quarter of its size through the basis of range(W^T), as bench.py
+    decomposes gate and up (1024 -> 2752, 16384 tokens of the block recipe, k = 447 for 60 % of the
+    parameters, fp32 eig, host-drawn inputs shared by both sides), against the oracle in full: its
+    fp64 covariance of the 2752 outputs and cyclic Jacobi of that 2752 x 2752 matrix give the
+    eigenvalues (the trailing 1728 are zero to rounding), the error curve, the retained subspace and
+    the direct error of the GPU factors."""
+    n_tok, d_in, d_out = 16384, 1024, 2752
+    k = int(0.6 * d_in * d_out / (d_in + d_out))
+    _say("gate shape / 4 through the range basis: %d x %d -> %d, k = %d, full oracle comparison"
+         % (n_tok, d_in, d_out, k))
+    X = inputs.block_activations(d_in, n_tok, layer=2)
+    W = inputs.weight(d_in, d_out, "bf16", inputs.CFG_BLOCK, 2, 4)
+    Xd, Wd = dev(X, "bf16"), dev(W, "bf16")
+    C = torch.zeros(d_out, d_out, dtype=torch.float32, device="cuda")
+    info = lrc.lrc_cov_accumulate(Xd, Wd, C)
+    assert int(host(info)[0]) == 0
+    lam, V, info = lrc.lrc_eigh_multi([(C, k, None, None, None, Wd)], prec=1)[0]
+    assert int(host(info)[0]) == 0
+    eps = lrc.lrc_error_curve(lam[None])
+    A = torch.empty(d_in, k, dtype=torch.float32, device="cuda")
+    B = torch.empty(k, d_out, dtype=torch.float32, device="cuda")
+    lrc.lrc_factorize(Wd, V, k, A, B)
+    lam_h, V_h, eps_h, A_h, B_h = host(lam), host(V), host(eps)[0], host(A), host(B)
+    del Xd, Wd, C, V, A, B
+    assert np.count_nonzero(lam_h == 0.0) >= d_out - d_in  # exact zeros outside range(W^T)
     Cr = oracle.covariance(X, "bf16", W, "bf16")
     lam_r, V_r = oracle.eigh_large(Cr)
     eps_r = oracle.error_curve(lam_r)
