@@ -3,9 +3,10 @@
 //
 // Stages, all on the GPU:
 //  1. Householder tridiagonalisation Q^T C Q = T, blocked (panel of NB columns, then a rank-2NB
-//     update of the trailing matrix), working precision T_ (fp32 or fp64).  The matrix is kept
-//     in full (both triangles) so the symmetric matrix-vector product of each column is a plain
-//     row-wise product with coalesced rows; three launches per column.
+//     update of the trailing matrix), working precision T_ (fp32 or fp64).  Only the upper
+//     triangle is kept current; the symmetric product of each column reads every upper tile once
+//     and forms both its row and its column contribution.  Two launches per column (the product,
+//     then the column's W and the next column), one for all members of a lockstep group.
 //  2. All n eigenvalues of T by multisection on Sturm counts, fp64, 16 lanes per eigenvalue.
 //  3. Eigenvectors of T for the n_vec largest eigenvalues by inverse iteration, fp64, one thread
 //     per vector (LU with partial pivoting of T - lambda I once, then three solves); vectors of
@@ -146,7 +147,7 @@ struct StridedSum {
     }
 };
 
-// Each column of a panel takes three launches; each global reduction is done by the next launch,
+// Each column of a panel takes two launches; each global reduction is done by the next launch,
 // redundantly in every block that needs it and always in the same fixed order, so all blocks see
 // bit-identical values (no atomics, no device-wide fences):
 //   k_trd_symv : reflector of column c (reduces the ||x||^2 partials; block 0 also reduces the
