@@ -297,7 +297,7 @@ def per_head_leg(torch, lrc, n_tok, seed, dev, d_model=4096, hd=128, k=32, runs=
             "stage_ms": {"covariance": round(cov, 3), "eigh_and_error_curve": round(eig, 3), "factors": round(fac, 3)}}
 
 
-def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=11008, rho=0.8):
+def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=11008, rho=0.8, sets=3):
     """The 32-layer stack end to end (FLRC page, method 1; LASER page, method 2): for every layer its
     own n_tok calibration tokens, the 7 covariances, one call decomposing all 7 (gate/up through a basis
     of range(W^T)) with k_cap = floor(d_in d_out / (d_in + d_out)) vectors each, the error curves; then
@@ -319,25 +319,33 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
     groups = {}
     for m in MATS:
         groups.setdefault((sh[m][1], kcap[m]), []).append(m)
-    gC = {gk: torch.empty(len(ms), gk[0], gk[0], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
     where = {m: (gk, ms.index(m)) for gk, ms in groups.items() for m in ms}
     V = [{m: torch.empty(sh[m][1], kcap[m], dtype=torch.float32, device=dev) for m in MATS} for _ in range(n_layers)]
     lam = [{m: torch.empty(sh[m][1], dtype=torch.float64, device=dev) for m in MATS} for _ in range(n_layers)]
     eps = [{m: torch.empty(sh[m][1] + 1, dtype=torch.float64, device=dev) for m in MATS} for _ in range(n_layers)]
-    ginfo_g = {gk: torch.zeros(len(ms), dtype=torch.int32, device=dev) for gk, ms in groups.items()}
+    # `sets` sets of the per-layer buffers: layer l's decompositions (on side stream l % sets, from a
+    # host thread of their own) overlap the next layers' covariances on the main stream; a set is
+    # reused `sets` layers later, after its decompositions and copies are done
+    NS = max(1, sets)
+    gC = [{gk: torch.empty(len(ms), gk[0], gk[0], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
+          for _ in range(NS)]
+    ginfo_g = [{gk: torch.zeros(len(ms), dtype=torch.int32, device=dev) for gk, ms in groups.items()} for _ in range(NS)]
     cinfo = torch.zeros(1, dtype=torch.int32, device=dev)
-    bad = torch.zeros(1, dtype=torch.int64, device=dev)
+    bad = [torch.zeros(1, dtype=torch.int64, device=dev) for _ in range(NS + 1)]  # per set, and the covariances'
     # each group decomposes from stacked buffers (the range bases of gate/up included) and its
     # eigenvalues and vectors are copied out to the per-matrix buffers
-    gV = {gk: torch.empty(len(ms), gk[0], gk[1], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
-    glam = {gk: torch.empty(len(ms), gk[0], dtype=torch.float64, device=dev) for gk, ms in groups.items()}
+    gV = [{gk: torch.empty(len(ms), gk[0], gk[1], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
+          for _ in range(NS)]
+    glam = [{gk: torch.empty(len(ms), gk[0], dtype=torch.float64, device=dev) for gk, ms in groups.items()}
+            for _ in range(NS)]
     ws_cov = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, n_tok, di, True, do, 1)
                              for di, do in sh.values()), dtype=torch.uint8, device=dev)
-    ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace(
+    ws_eig = [torch.empty(lrc.lrc_eigh_multi_workspace(
         [(gk[0], len(ms), gk[1], sh[ms[0]][0] if sh[ms[0]][0] < gk[0] else 0) for gk, ms in groups.items()], prec),
-        dtype=torch.uint8, device=dev)
-    gW = {gk: torch.empty(len(ms), sh[ms[0]][0], gk[0], dtype=torch.bfloat16, device=dev)
-          for gk, ms in groups.items() if sh[ms[0]][0] < gk[0]}
+        dtype=torch.uint8, device=dev) for _ in range(NS)]
+    gW = [{gk: torch.empty(len(ms), sh[ms[0]][0], gk[0], dtype=torch.bfloat16, device=dev)
+           for gk, ms in groups.items() if sh[ms[0]][0] < gk[0]} for _ in range(NS)]
+    side = [torch.cuda.Stream(device=dev) for _ in range(NS)]
     offs_h = [0] + list(np.cumsum([kcap[m] for _ in range(n_layers) for m in MATS]))
     offs = torch.tensor(offs_h, dtype=torch.int64, device=dev)
     lam_packed = torch.empty(int(offs_h[-1]), dtype=torch.float64, device=dev)
@@ -351,65 +359,86 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
     Gl = [Gs[l][m] for l in range(n_layers) for m in MATS]
     Wl = [Ws[l][m] for l in range(n_layers) for m in MATS]
     ws_fsh = torch.empty(lrc.lrc_fisher_scores_workspace([w.numel() for w in Wl]), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    t_gen = 0.0
-    marks = {"cov": 0.0, "eig": 0.0}
+    gen_ev, cov_ev, eig_ev = [], [], []
+
+    def decompose(layer, si, ready):
+        # runs on a host thread of its own: the library call returns once its launches are enqueued
+        sd = side[si]
+        with torch.cuda.stream(sd):
+            sd.wait_event(ready)
+            e0 = ev(sd)
+            lrc.lrc_eigh_multi([(gC[si][gk], gk[1], glam[si][gk], gV[si][gk], ginfo_g[si][gk], gW[si].get(gk))
+                                for gk in groups], prec=prec, ws=ws_eig[si], stream=sd)
+            for gk, ms in groups.items():
+                bad[si] += ginfo_g[si][gk].abs().sum()
+                for j, m in enumerate(ms):
+                    lam[layer][m].copy_(glam[si][gk][j])
+                    V[layer][m].copy_(gV[si][gk][j])
+            for i, m in enumerate(MATS):
+                lrc.lrc_error_curve(lam[layer][m][None], eps=eps[layer][m][None], stream=sd)
+                q = layer * 7 + i
+                lam_packed[offs_h[q]:offs_h[q] + kcap[m]].copy_(lam[layer][m][:kcap[m]])
+                eps0[q:q + 1].copy_(eps[layer][m][0:1])
+            eig_ev.append((e0, ev(sd)))
+
+    threads = [None] * NS
+    done = [None] * NS
     t0 = time.perf_counter()
     for layer in range(n_layers):
-        a0 = ev()
+        si = layer % NS
+        if threads[si] is not None:  # this set's previous decompositions enqueued; the GPU waits for them
+            threads[si].join()
+            stream.wait_stream(side[si])
+        a0 = ev(stream)
         inputs.stack_layer_gpu(g, n_tok, d_model, d_ff, dev, X, Xd)
-        a1 = ev()
+        a1 = ev(stream)
         for i, m in enumerate(MATS):
             gk, j = where[m]
-            C = gC[gk][j]
+            C = gC[si][gk][j]
             C.zero_()
             lrc.lrc_cov_accumulate(Xd if m == "down_proj" else X, Ws[layer][m], C, info=cinfo, ws=ws_cov)
-            bad += cinfo
-        a2 = ev()
+            bad[NS] += cinfo
         for gk, ms in groups.items():
-            if gk in gW:
+            if gk in gW[si]:
                 for j, m in enumerate(ms):
-                    gW[gk][j].copy_(Ws[layer][m])
-        lrc.lrc_eigh_multi([(gC[gk], gk[1], glam[gk], gV[gk], ginfo_g[gk], gW.get(gk)) for gk in groups], prec=prec,
-                           ws=ws_eig)
-        for gk, ms in groups.items():
-            bad += ginfo_g[gk].abs().sum()
-            for j, m in enumerate(ms):
-                lam[layer][m].copy_(glam[gk][j])
-                V[layer][m].copy_(gV[gk][j])
-        for i, m in enumerate(MATS):
-            lrc.lrc_error_curve(lam[layer][m][None], eps=eps[layer][m][None])
-            q = layer * 7 + i
-            lam_packed[offs_h[q]:offs_h[q] + kcap[m]].copy_(lam[layer][m][:kcap[m]])
-            eps0[q:q + 1].copy_(eps[layer][m][0:1])
-        a3 = ev()
-        a3.synchronize()
-        t_gen += a0.elapsed_time(a1) / 1000.0
-        marks["cov"] += a1.elapsed_time(a2)
-        marks["eig"] += a2.elapsed_time(a3)
+                    gW[si][gk][j].copy_(Ws[layer][m])
+        a2 = ev(stream)
+        gen_ev.append((a0, a1))
+        cov_ev.append((a1, a2))
+        threads[si] = threading.Thread(target=decompose, args=(layer, si, a2))
+        threads[si].start()
+    for t in threads:
+        if t is not None:
+            t.join()
+    for sd in side:
+        stream.wait_stream(sd)
     b0 = ev()
     lrc.lrc_fisher_scores(Gl, Wl, alpha=alpha, ws=ws_fsh)
     lrc.lrc_allocate_ranks(alpha, lam_packed, offs, eps0, cost, budget, k_out=k_out, ws=ws_alc)
     b1 = ev()
     kk = k_out.cpu().tolist()
-    fac_ms = 0.0
+    # the factors at the allocated ranks, into buffers of the largest rank (no allocation per matrix)
+    kmax = max(kk)
+    A_buf = torch.empty(max(di for di, do in sh.values()) * kmax, dtype=torch.float32, device=dev)
+    B_buf = torch.empty(max(do for di, do in sh.values()) * kmax, dtype=torch.float32, device=dev)
+    fac_ev = []
     for layer in range(n_layers):
         for i, m in enumerate(MATS):
             km = kk[layer * 7 + i]
             if km <= 0:
                 continue
             di, do = sh[m]
-            A = torch.empty(di, km, dtype=torch.float32, device=dev)
-            B = torch.empty(km, do, dtype=torch.float32, device=dev)
-            f0 = ev()
-            lrc.lrc_factorize(Ws[layer][m], V[layer][m], km, A, B)
-            f1 = ev()
-            f1.synchronize()
-            fac_ms += f0.elapsed_time(f1)
-            del A, B
+            f0 = ev(stream)
+            lrc.lrc_factorize(Ws[layer][m], V[layer][m], km, A_buf[:di * km].view(di, km), B_buf[:km * do].view(km, do))
+            fac_ev.append((f0, ev(stream)))
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0 - t_gen
-    assert int(bad.item()) == 0, "stack: device info flags set"
+    wall = time.perf_counter() - t0
+    t_gen = sum(x.elapsed_time(y) for x, y in gen_ev) / 1000.0
+    fac_ms = sum(x.elapsed_time(y) for x, y in fac_ev)
+    marks = {"cov": sum(x.elapsed_time(y) for x, y in cov_ev), "eig": sum(x.elapsed_time(y) for x, y in eig_ev)}
+    assert int(sum(b.item() for b in bad)) == 0, "stack: device info flags set"
     used = sum(kk[q] * sum(sh[MATS[q % 7]]) for q in range(len(kk)))
     return {"workload": "%d-layer LLaMA-7B-shaped stack (%d matrices, %d parameters), %d calibration tokens per "
                         "layer, eig prec %s, k_cap vectors per matrix, greedy allocation of %.0f%% of the parameters"
@@ -419,7 +448,10 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
             "tokens_per_s": n_layers * n_tok / wall,
             "stage_s": {"covariances": marks["cov"] / 1000.0, "eigh_and_error_curves": marks["eig"] / 1000.0,
                         "fisher_and_allocation": b0.elapsed_time(b1) / 1000.0, "factors": fac_ms / 1000.0},
-            "input_generation_s_excluded": t_gen,
+            "stage_note": "layer l's decompositions and error curves run on a side stream during layer l+1's "
+                          "input generation and covariances, so the stage times overlap and add up to more than "
+                          "the wall time",
+            "input_generation_s_included": t_gen,
             "allocated_parameters": used, "budget": budget,
             "rank_range": [min(kk), max(kk)]}
 
@@ -464,6 +496,8 @@ def main():
     ap.add_argument("--single", choices=("on", "off"), default="on", help="the single fp32 layer leg")
     ap.add_argument("--stack-layers", type=int, default=32, help="layers of the stack leg (0: skip)")
     ap.add_argument("--stack-tokens", type=int, default=65536, help="calibration tokens per layer of the stack leg")
+    ap.add_argument("--stack-sets", type=int, default=3,
+                    help="buffer sets of the stack leg: layers whose decompositions may run at once")
     ap.add_argument("--cpu-layer-tokens", type=int, default=65536,
                     help="tokens of the oracle's 4096x4096 layer in the CPU baseline (0: skip)")
     ap.add_argument("--cpu-heads-sample", type=int, default=4096,
@@ -580,9 +614,17 @@ def main():
             lrc.lrc_error_curve(glam[g], eps=geps[g], stream=sg)
         e1 = ev(sg)
         times.append(("eigh." + pname[pi], e0, e1))
+        # the group's factors at the fixed ranks right after its eigenvectors, on the same stream
+        # (they do not depend on the allocation), so that only the last group's stay in the tail
+        for g in phases[pi]:
+            for m in groups[g]:
+                f0 = ev(sg)
+                lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m], stream=sg)
+                f1 = ev(sg)
+                times.append((m + ".fac", f0, f1))
 
-    def tail(times):
-        for m in MATS:
+    def tail(times, factors=True):
+        for m in MATS if factors else ():
             e0 = ev(stream)
             lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m])
             e1 = ev(stream)
@@ -613,6 +655,8 @@ def main():
                 t.join()
             for sd in side:
                 stream.wait_stream(sd)
+            tail(times, factors=False)
+            return
         else:
             for m in MATS:
                 cov(m, times)
@@ -751,9 +795,12 @@ def main():
     share = n3["q_proj"] / sum(n3.values())
     # the step's wall time outside the covariance, factor, Fisher and allocation calls: the part of
     # the eigendecompositions not hidden behind the covariances (all of them with --overlap off)
-    fac_ms = sum(avg[m + ".fac"] for m in MATS)
+    # with --overlap on the factors run on the side streams after each group's eigendecompositions,
+    # so the wall time outside the covariance, Fisher and allocation calls holds the unhidden part of
+    # the decompositions, error curves and factors; with --overlap off the factor calls are in series
+    fac_ms = sum(avg[m + ".fac"] for m in MATS) if a.overlap == "off" else 0.0
     eig_wall_ms = max(0.0, step_ms - cov_ms - fac_ms - avg["fisher"] - avg["alloc"])
-    layer_s = (avg["q_proj.cov"] + eig_wall_ms * share + avg["q_proj.fac"]) / 1000.0
+    layer_s = (avg["q_proj.cov"] + eig_wall_ms * share + (avg["q_proj.fac"] if a.overlap == "off" else 0.0)) / 1000.0
     if a.breakdown:
         for k in sorted(avg):
             print("%-20s %10.3f ms" % (k, avg[k]), file=sys.stderr)
@@ -820,12 +867,13 @@ def main():
                                    "error curve, factors), after the timed steps",
         "sec_per_4096_layer_at_%d_tokens" % a.layer_tokens: layer_s_short,
         "sec_per_4096_layer_in_block": layer_s,
-        "sec_per_4096_layer_in_block_note": "q_proj covariance + q_proj factors + %.4f of the step's wall time "
-                                            "outside the covariance, factor, Fisher and allocation calls (the "
-                                            "eigendecompositions and error curves of %s not hidden behind the "
-                                            "covariances: %.1f ms; the share is q_proj's n^3 over the sum, n = d_in "
-                                            "for the matrices decomposed through a range basis)"
-                                            % (share, gkey, eig_wall_ms),
+        "sec_per_4096_layer_in_block_note": "an attribution estimate, not a measurement: q_proj covariance + %.4f "
+                                            "of the step's wall time outside the covariance, Fisher and allocation "
+                                            "calls (the eigendecompositions, error curves and factors of %s not "
+                                            "hidden behind the covariances: %.1f ms; with --overlap off the factor "
+                                            "calls are left out of that time and q_proj's is added; the share is "
+                                            "q_proj's n^3 over the sum, n = d_in for the matrices decomposed "
+                                            "through a range basis)" % (share, gkey, eig_wall_ms),
         "cov_tokens_per_s": a.tokens / (cov_ms / 1000.0),
         "cov_ms": cov_ms, "eigh_ms": eig_ms,
         "overlap": a.overlap,
@@ -850,7 +898,8 @@ def main():
                                                lrc.LRC_F32 if a.curvature_prec == "f32" else lrc.LRC_F64, dev)
     if a.stack_layers > 0:
         torch.cuda.empty_cache()
-        out["stack"] = stack_leg(torch, lrc, a.stack_layers, a.stack_tokens, a.seed, prec, dev, a.d_model, a.d_ff)
+        out["stack"] = stack_leg(torch, lrc, a.stack_layers, a.stack_tokens, a.seed, prec, dev, a.d_model, a.d_ff,
+                                 sets=a.stack_sets)
     if a.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(a.d_model, a.d_ff, a.cpu_sample, a.cpu_layer_tokens, a.cpu_heads_sample)
     print(json.dumps(out))
