@@ -479,6 +479,8 @@ def main():
                     help="decompose each group of matrices (grouped by output width and rank) as soon as its "
                          "covariances are done, on a side stream from a host thread of its own, while the "
                          "remaining covariances run")
+    ap.add_argument("--overlap-chunk", type=int, default=0,
+                    help="with --overlap on: split groups into parts of this many matrices (0: whole groups)")
     ap.add_argument("--overlap-order", choices=("small-first", "large-first", "most-first"), default="large-first",
                     help="small-first: the groups of one output width decomposed in one call (the library "
                          "tridiagonalises matrices of one order in lockstep), narrow widths first; large-first / "
@@ -561,18 +563,22 @@ def main():
     # overlap: covariances group by group, largest n first; each group's eigendecompositions and
     # error curves on a side stream of its own (default priority) with a workspace of its own
     # phases: the covariances of a phase's groups, then (on a side stream) one call decomposing them all
+    # a phase is a list of parts (g, lo, hi): members lo .. hi-1 of group g; --overlap-chunk splits
+    # larger groups into parts of that many members, each a phase of its own
+    def parts_of(g):
+        n, c = len(groups[g]), a.overlap_chunk if a.overlap_chunk > 0 else len(groups[g])
+        return [(g, lo, min(lo + c, n)) for lo in range(0, n, c)]
     if a.overlap_order == "small-first":  # groups of one output width together, narrow widths first
         widths = sorted({g[0] for g in groups})
-        phases = [[g for g in groups if g[0] == wd] for wd in widths]
+        phases = [[pt for g in groups if g[0] == wd for pt in parts_of(g)] for wd in widths]
     else:
         g_order = sorted(groups, key=lambda g: -g[0] if a.overlap_order == "large-first" else len(groups[g]) * -1)
-        phases = [[g] for g in g_order]
+        phases = [[pt] for g in g_order for pt in parts_of(g)]
     side = [torch.cuda.Stream(device=dev) for _ in phases]
     ws_eig_g = [torch.empty(lrc.lrc_eigh_multi_workspace(
-        [(g[0], len(groups[g]), g[1], sh[groups[g][0]][0] if g in gW else 0) for g in ph], prec), dtype=torch.uint8,
+        [(g[0], hi - lo, g[1], sh[groups[g][0]][0] if g in gW else 0) for g, lo, hi in ph], prec), dtype=torch.uint8,
         device=dev) for ph in phases] if a.overlap == "on" else []
-    gname = {g: "%dx%d_k%d" % (len(groups[g]), g[0], g[1]) for g in groups}
-    pname = ["+".join(gname[g] for g in ph) for ph in phases]
+    pname = ["+".join("%dx%d_k%d" % (hi - lo, g[0], g[1]) for g, lo, hi in ph) for ph in phases]
     kcap = {m: (di * do) // (di + do) for m, (di, do) in sh.items()}
     offs_h = [0] + list(np.cumsum([kcap[m] for m in MATS]))
     offs = torch.tensor(offs_h, dtype=torch.int64, device=dev)
@@ -608,16 +614,17 @@ def main():
         sg = side[pi]
         sg.wait_event(ready)
         e0 = ev(sg)
-        lrc.lrc_eigh_multi([eig_groups[list(groups).index(g)] for g in phases[pi]], prec=prec, ws=ws_eig_g[pi],
-                           stream=sg)
-        for g in phases[pi]:
-            lrc.lrc_error_curve(glam[g], eps=geps[g], stream=sg)
+        lrc.lrc_eigh_multi([(gC[g][lo:hi], g[1], glam[g][lo:hi], gV[g][lo:hi], ginfo[g][lo:hi],
+                             gW[g][lo:hi] if g in gW else None) for g, lo, hi in phases[pi]], prec=prec,
+                           ws=ws_eig_g[pi], stream=sg)
+        for g, lo, hi in phases[pi]:
+            lrc.lrc_error_curve(glam[g][lo:hi], eps=geps[g][lo:hi], stream=sg)
         e1 = ev(sg)
         times.append(("eigh." + pname[pi], e0, e1))
         # the group's factors at the fixed ranks right after its eigenvectors, on the same stream
         # (they do not depend on the allocation), so that only the last group's stay in the tail
-        for g in phases[pi]:
-            for m in groups[g]:
+        for g, lo, hi in phases[pi]:
+            for m in groups[g][lo:hi]:
                 f0 = ev(sg)
                 lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m], stream=sg)
                 f1 = ev(sg)
@@ -645,8 +652,8 @@ def main():
         if a.overlap == "on":
             threads = []
             for pi, ph in enumerate(phases):
-                for g in ph:
-                    for m in groups[g]:
+                for g, lo, hi in ph:
+                    for m in groups[g][lo:hi]:
                         cov(m, times)
                 t = threading.Thread(target=eig_group, args=(pi, ev(stream), times))
                 t.start()
