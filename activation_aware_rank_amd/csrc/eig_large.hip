@@ -787,7 +787,11 @@ __device__ __forceinline__ int sturm_count(const double *__restrict__ d, const d
 }
 
 __global__ void k_tri_prep(const double *__restrict__ d, const double *__restrict__ e, int64_t n, double *__restrict__ e2,
-                           double *__restrict__ bounds) {
+                           double *__restrict__ bounds, int64_t zs) {
+    d = zoff(d, zs);
+    e = zoff(e, zs);
+    e2 = zoff(e2, zs);
+    bounds = zoff(bounds, zs);
     // one block: e2, Gershgorin bounds, pivmin, norm
     __shared__ double smin[256], smax[256], se2[256];
     double lo = DBL_MAX, hi = -DBL_MAX, mx = 0.0;
@@ -824,7 +828,12 @@ __global__ void k_tri_prep(const double *__restrict__ d, const double *__restric
 // sixteenth that holds eigenvalue i (about 14 passes to full fp64 accuracy).
 constexpr int MSEC = 16;
 __global__ void __launch_bounds__(256) k_bisect(const double *__restrict__ d, const double *__restrict__ e2, int64_t n,
-                                                const double *__restrict__ bounds, double *__restrict__ lam_asc) {
+                                                const double *__restrict__ bounds, double *__restrict__ lam_asc,
+                                                int64_t zs) {
+    d = zoff(d, zs);
+    e2 = zoff(e2, zs);
+    bounds = zoff(bounds, zs);
+    lam_asc = zoff(lam_asc, zs);
     const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t i = gid / MSEC;
     const int sub = int(gid % MSEC);
@@ -891,7 +900,15 @@ __device__ __forceinline__ void sweep_pipelined(int64_t nbatch, const Load &load
 __global__ void __launch_bounds__(64) k_invit(const double *__restrict__ d, const double *__restrict__ e, int64_t n,
                                               const double *__restrict__ lam_asc, const double *__restrict__ bounds,
                                               int64_t nv, double *__restrict__ Z, double2 *__restrict__ PU,
-                                              double2 *__restrict__ PD, uint8_t *__restrict__ SW) {
+                                              double2 *__restrict__ PD, uint8_t *__restrict__ SW, int64_t zs) {
+    d = zoff(d, zs);
+    e = zoff(e, zs);
+    lam_asc = zoff(lam_asc, zs);
+    bounds = zoff(bounds, zs);
+    Z = zoff(Z, zs);
+    PU = zoff(PU, zs);
+    PD = zoff(PD, zs);
+    SW = zoff(SW, zs);
     const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (j >= nv) return;
     const double lam = lam_asc[n - 1 - j];
@@ -1037,7 +1054,11 @@ __global__ void __launch_bounds__(64) k_invit(const double *__restrict__ d, cons
 // Re-orthogonalise clusters: vector j starts a cluster when lam_{j-1} - lam_j > ctol; the leader's
 // block runs modified Gram-Schmidt over its cluster members in order.
 __global__ void __launch_bounds__(256) k_cluster_mgs(const double *__restrict__ lam_asc, int64_t n, int64_t nv,
-                                                     const double *__restrict__ bounds, double *__restrict__ Z) {
+                                                     const double *__restrict__ bounds, double *__restrict__ Z,
+                                                     int64_t zs) {
+    lam_asc = zoff(lam_asc, zs);
+    bounds = zoff(bounds, zs);
+    Z = zoff(Z, zs);
     __shared__ double sh[4];
     const int64_t j0 = blockIdx.x;
     const double ctol = 1e-10 * bounds[3];
@@ -1072,7 +1093,10 @@ __global__ void __launch_bounds__(256) k_cluster_mgs(const double *__restrict__ 
 // tau_i.  V_b is rows c0 .. c0+nb-1 of Rt, nonzero from column c0+1 on.
 template <class T>
 __global__ void __launch_bounds__(256) k_bt_tall(const T *__restrict__ Rt, int64_t ldr, int64_t n, int64_t nrefl,
-                                                 const T *__restrict__ tau, double *__restrict__ Tall) {
+                                                 const T *__restrict__ tau, double *__restrict__ Tall, int64_t zs) {
+    Rt = zoff(Rt, zs);
+    tau = zoff(tau, zs);
+    Tall = zoff(Tall, zs);
     __shared__ double vs[NBT][65];
     __shared__ double S[NBT][NBT + 1], Tm[NBT][NBT + 1];
     const int64_t c0 = int64_t(blockIdx.x) * NBT;
@@ -1177,7 +1201,10 @@ __device__ __forceinline__ int bt_col(int y) { return (((threadIdx.x >> 6) & 1) 
 template <class T>
 __global__ void __launch_bounds__(256) k_bt_g(const T *__restrict__ Rt, int64_t ldr, int64_t n, int64_t c0, int nb,
                                               const double *__restrict__ Z, int64_t nv, double *__restrict__ Gp,
-                                              int rch) {
+                                              int rch, int64_t zs) {
+    Rt = zoff(Rt, zs);
+    Z = zoff(Z, zs);
+    Gp = zoff(Gp, zs);
     __shared__ double As[BK][BLD], Bs[BK][BLD];
     const int64_t j0 = int64_t(blockIdx.x) * 64;
     const int64_t r0 = c0 + 1 + int64_t(blockIdx.y) * rch, r1 = min(r0 + rch, n);
@@ -1207,7 +1234,10 @@ __global__ void __launch_bounds__(256) k_bt_g(const T *__restrict__ Rt, int64_t 
 // Blocks of 16 columns.
 constexpr int GR_COLS = 16;
 __global__ void __launch_bounds__(256) k_bt_greduce(const double *__restrict__ Gp, int nchunk, int64_t nv,
-                                                    const double *__restrict__ Tf, double *__restrict__ G) {
+                                                    const double *__restrict__ Tf, double *__restrict__ G, int64_t zs) {
+    Gp = zoff(Gp, zs);
+    Tf = zoff(Tf, zs);
+    G = zoff(G, zs);
     __shared__ double Tm[NBT][NBT + 1];
     __shared__ double g[NBT][GR_COLS + 1];
     const int t = threadIdx.x, cl = t % GR_COLS, qg = t / GR_COLS;
@@ -1234,7 +1264,11 @@ __global__ void __launch_bounds__(256) k_bt_greduce(const double *__restrict__ G
 // the block's nb reflectors on MFMA; grid (column tiles, row tiles from row c0 + 1)
 template <class T>
 __global__ void __launch_bounds__(256) k_bt_update(const T *__restrict__ Rt, int64_t ldr, int64_t n, int64_t c0, int nb,
-                                                   const double *__restrict__ G, double *__restrict__ Z, int64_t nv) {
+                                                   const double *__restrict__ G, double *__restrict__ Z, int64_t nv,
+                                                   int64_t zs) {
+    Rt = zoff(Rt, zs);
+    G = zoff(G, zs);
+    Z = zoff(Z, zs);
     __shared__ double As[BK][BLD], Bs[BK][BLD];
     const int64_t j0 = int64_t(blockIdx.x) * 64, i0 = c0 + 1 + int64_t(blockIdx.y) * 64;
     const T *V = Rt + c0 * ldr + i0;
@@ -1464,19 +1498,22 @@ struct EigJob {
         }
         if (stage == 2) {
             // 2. eigenvalues
-            hipLaunchKernelGGL(k_tri_prep, dim3(1), dim3(256), 0, s, w->d, w->e, n, w->e2, w->bounds);
-            hipLaunchKernelGGL(k_bisect, dim3(cdiv(n * MSEC, 256)), dim3(256), 0, s, w->d, w->e2, n, w->bounds, w->lam);
-            hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(n, 256)), dim3(256), 0, s, w->lam, n, lambda, w->bad);
+            hipLaunchKernelGGL(k_tri_prep, dim3(1, 1, nbatch), dim3(256), 0, s, w->d, w->e, n, w->e2, w->bounds, zs);
+            hipLaunchKernelGGL(k_bisect, dim3(cdiv(n * MSEC, 256), 1, nbatch), dim3(256), 0, s, w->d, w->e2, n,
+                               w->bounds, w->lam, zs);
+            if (nbatch == 1)  // a batch's per-matrix outputs are written by its caller
+                hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(n, 256)), dim3(256), 0, s, w->lam, n, lambda, w->bad);
             LRC_LAUNCH_CHECK("bisection");
             if (nv > 0) {
                 // 3. eigenvectors of T
-                hipLaunchKernelGGL(k_invit, dim3(cdiv(nv, 64)), dim3(64), 0, s, w->d, w->e, n, w->lam, w->bounds, nv,
-                                   w->Z, w->PU, w->PD, w->SW);
-                hipLaunchKernelGGL(k_cluster_mgs, dim3(unsigned(nv)), dim3(256), 0, s, w->lam, n, nv, w->bounds, w->Z);
+                hipLaunchKernelGGL(k_invit, dim3(cdiv(nv, 64), 1, nbatch), dim3(64), 0, s, w->d, w->e, n, w->lam,
+                                   w->bounds, nv, w->Z, w->PU, w->PD, w->SW, zs);
+                hipLaunchKernelGGL(k_cluster_mgs, dim3(unsigned(nv), 1, nbatch), dim3(256), 0, s, w->lam, n, nv,
+                                   w->bounds, w->Z, zs);
                 LRC_LAUNCH_CHECK("inverse iteration");
                 // all T factors of the back-transformation first, in one launch
-                hipLaunchKernelGGL(k_bt_tall<T>, dim3(cdiv(n - 1, NBT)), dim3(256), 0, s, w->Rt, n, n, n - 1, w->tau,
-                                   w->Tf);
+                hipLaunchKernelGGL(k_bt_tall<T>, dim3(cdiv(n - 1, NBT), 1, nbatch), dim3(256), 0, s, w->Rt, n, n, n - 1,
+                                   w->tau, w->Tf, zs);
                 c0 = ((n - 2) / NBT) * NBT;
                 stage = 3;
                 return LRC_OK;
@@ -1489,23 +1526,25 @@ struct EigJob {
                 const int nb = int(std::min<int64_t>(NBT, nrefl - c0));
                 const int64_t mrows = n - c0 - 1;  // rows the block's reflectors touch
                 const int nch = cdiv(mrows, RCH);
-                hipLaunchKernelGGL(k_bt_g<T>, dim3(cdiv(nv, 64), nch), dim3(256), 0, s, w->Rt, n, n, c0, nb, w->Z, nv,
-                                   w->Gp, RCH);
-                hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, GR_COLS)), dim3(256), 0, s, w->Gp, nch, nv,
-                                   w->Tf + (c0 / NBT) * NBT * NBT, w->G);
-                hipLaunchKernelGGL(k_bt_update<T>, dim3(cdiv(nv, 64), cdiv(mrows, 64)), dim3(256), 0, s, w->Rt, n, n,
-                                   c0, nb, w->G, w->Z, nv);
+                hipLaunchKernelGGL(k_bt_g<T>, dim3(cdiv(nv, 64), nch, nbatch), dim3(256), 0, s, w->Rt, n, n, c0, nb,
+                                   w->Z, nv, w->Gp, RCH, zs);
+                hipLaunchKernelGGL(k_bt_greduce, dim3(cdiv(nv, GR_COLS), 1, nbatch), dim3(256), 0, s, w->Gp, nch, nv,
+                                   w->Tf + (c0 / NBT) * NBT * NBT, w->G, zs);
+                hipLaunchKernelGGL(k_bt_update<T>, dim3(cdiv(nv, 64), cdiv(mrows, 64), nbatch), dim3(256), 0, s,
+                                   w->Rt, n, n, c0, nb, w->G, w->Z, nv, zs);
             }
             LRC_LAUNCH_CHECK("back-transformation");
             if (c0 >= 0) return LRC_OK;
-            if (!keep_z) {
+            if (!keep_z && nbatch == 1) {
                 hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, w->Z, n, nv, V, ldv, w->bad);
                 LRC_LAUNCH_CHECK("k_sign_out");
             }
             stage = 4;
         }
-        hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, s, info, w->bad);
-        LRC_LAUNCH_CHECK("k_set_info");
+        if (nbatch == 1) {
+            hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, s, info, w->bad);
+            LRC_LAUNCH_CHECK("k_set_info");
+        }
         stage = 5;
         return LRC_OK;
     }
@@ -1813,11 +1852,13 @@ static lrc_status run_member(const EigMember &m, const MultiPlan &p, char *lws, 
 // Members whose matrices have one order (n, or d_in with a range basis) and fit a workspace region
 // each are tridiagonalised in lockstep: every launch of the column chain works on all of them (one
 // z slice per matrix), so a chain of two small launches per column serves the whole group instead
-// of each matrix paying its own launch and latency cost on a stream of its own.  The rest of each
-// decomposition (eigenvalues and vectors of T, back-transformation, a range member's V = Q Z) then
-// runs on a helper stream per member.  Every member's arithmetic is the same as alone, so its
-// results are bit-identical to a call on it alone.  LRC_EIGH_LOCKSTEP=0 turns this off (each
-// member on a lane of its own throughout, as for members of different orders).
+// of each matrix paying its own launch and latency cost on a stream of its own.  When the members
+// also share n_vec, the eigenvalues, the vectors of T and the back-transformation are batched the
+// same way (one launch per step for all members); otherwise the rest of each decomposition runs on
+// a helper stream per member.  A range member's V = Q Z follows on the call's stream.  Every
+// member's arithmetic is the same as alone, so its results are bit-identical to a call on it alone.
+// LRC_EIGH_LOCKSTEP=0 turns this off (each member on a lane of its own throughout, as for members
+// of different orders).
 static int64_t trd_order(const EigMember &m) { return m.W ? m.d_in : m.n; }
 
 static bool lockstep_ok(const std::vector<EigMember> &mem, int lanes) {
@@ -1852,7 +1893,30 @@ static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p
         const lrc_status st = bj.advance(64);
         if (st != LRC_OK) return st;
     }
-    // 3. the rest of each decomposition on a helper stream of its own
+    bool same_nv = true;
+    for (int i = 1; i < nb; ++i) same_nv = same_nv && R[i].j.nv == R[0].j.nv;
+    if (same_nv) {
+        // 3. with one n_vec the regions agree up to their last array, so the eigenvalues, the vectors
+        // of T and the back-transformation run batched as well (workgroup z on member z), on s;
+        // then each member's outputs and a range member's V = Q Z and lambda with the zeros
+        while (!bj.done()) {
+            const lrc_status st = bj.advance(64);
+            if (st != LRC_OK) return st;
+        }
+        for (int i = 0; i < nb; ++i) {
+            const EigJob<T> &j = R[i].j;
+            LargeWs<T> &w = R[i].w;
+            hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(j.n, 256)), dim3(256), 0, s, w.lam, j.n, j.lambda, w.bad);
+            if (j.nv > 0 && !j.keep_z)
+                hipLaunchKernelGGL(k_sign_out, dim3(unsigned(j.nv)), dim3(256), 0, s, w.Z, j.n, j.nv, j.V, j.ldv, w.bad);
+            hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, s, j.info, w.bad);
+            LRC_LAUNCH_CHECK("lockstep outputs");
+            const lrc_status st = member_end(R[i], s);
+            if (st != LRC_OK) return st;
+        }
+        return LRC_OK;
+    }
+    // 3. otherwise the rest of each decomposition on a helper stream of its own
     EigLanes *L = nullptr;
     lrc_status st0 = eig_lanes(&L);
     if (st0 != LRC_OK) return st0;

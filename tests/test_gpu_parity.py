@@ -429,22 +429,25 @@ def test_eigh_range_basis_vs_oracle(lrc, prec):
         assert np.array_equal(host(l1), lam) and np.array_equal(host(V1), V)
 
 
-@pytest.mark.parametrize("prec", [1, 2])
-def test_eigh_lockstep_mixed_members(lrc, prec):
+@pytest.mark.parametrize("prec,same_nv", [(1, False), (2, False), (1, True), (2, True)])
+def test_eigh_lockstep_mixed_members(lrc, prec, same_nv):
     """Members of one tridiagonal order in one call are tridiagonalised in lockstep (one launch per
     column for all of them): two full decompositions of order 300 (one with a NaN entry), one of order
-    520 through a 300-row range basis, and a third full one in a group of its own.  Every member must
-    equal the same call with lockstep off and the member decomposed alone, bit for bit; the NaN member
-    reports info 1 without touching the others."""
-    _say("eigh lockstep: 2 x 300 (one NaN) + 520 via a 300-row basis + 1 x 300, prec %d" % prec)
+    520 through a 300-row range basis, and a third full one in a group of its own.  With one n_vec for
+    all, the eigenvalues, vectors of T and back-transformation are batched too; with different n_vec
+    they run per member.  Every member must equal the same call with lockstep off and the member
+    decomposed alone, bit for bit; the NaN member reports info 1 without touching the others."""
+    _say("eigh lockstep: 2 x 300 (one NaN) + 520 via a 300-row basis + 1 x 300, prec %d, same n_vec %s"
+         % (prec, same_nv))
+    nvs = (24, 24, 24) if same_nv else (24, 40, 16)
     X = inputs.block_activations(300, 1024)
     Cf = [oracle.covariance(X, "bf16", inputs.weight(300, 300, "bf16", inputs.CFG_BLOCK, 0, 70 + m),
                             "bf16").astype(np.float32) for m in range(3)]
     Cf[1][2, 9] = np.nan
     Wr = inputs.weight(300, 520, "bf16", inputs.CFG_BLOCK, 0, 74)
     Cr = _oracle_cov32(X, "bf16", Wr)[0]
-    groups = [(dev(np.stack(Cf[:2]), "f32"), 24), (dev(Cr, "f32"), 40, None, None, None, dev(Wr, "bf16")),
-              (dev(Cf[2], "f32"), 16)]
+    groups = [(dev(np.stack(Cf[:2]), "f32"), nvs[0]), (dev(Cr, "f32"), nvs[1], None, None, None, dev(Wr, "bf16")),
+              (dev(Cf[2], "f32"), nvs[2])]
     out = lrc.lrc_eigh_multi(groups, prec=prec)
     os.environ["LRC_EIGH_LOCKSTEP"] = "0"
     try:
@@ -457,16 +460,16 @@ def test_eigh_lockstep_mixed_members(lrc, prec):
         assert np.array_equal(host(V), host(V0), equal_nan=True)
     assert list(host(out[0][2])) == [0, 1] and int(host(out[1][2])[0]) == 0 and int(host(out[2][2])[0]) == 0
     # a 2-D C gives lambda (n,), V (n, n_vec), info (1,)
-    singles = [((dev(Cf[0], "f32"), 24), out[0][0][0], out[0][1][0]),
-               ((dev(Cr, "f32"), 40, None, None, None, dev(Wr, "bf16")), out[1][0], out[1][1]),
-               ((dev(Cf[2], "f32"), 16), out[2][0], out[2][1])]
+    singles = [((dev(Cf[0], "f32"), nvs[0]), out[0][0][0], out[0][1][0]),
+               ((dev(Cr, "f32"), nvs[1], None, None, None, dev(Wr, "bf16")), out[1][0], out[1][1]),
+               ((dev(Cf[2], "f32"), nvs[2]), out[2][0], out[2][1])]
     for grp, lam, V in singles:
         l1, V1, i1 = lrc.lrc_eigh_multi([grp], prec=prec)[0]
         assert int(host(i1)[0]) == 0
         assert np.array_equal(host(l1), host(lam)) and np.array_equal(host(V1), host(V))
     lam_r, V_r = oracle.eigh(Cr.astype(np.float64))
     check_lambda(host(out[1][0]), lam_r)
-    assert sin_theta_max(host(out[1][1]), V_r, 40) <= 1e-3
+    assert sin_theta_max(host(out[1][1]), V_r, nvs[1]) <= 1e-3
 
 
 def test_eigh_range_basis_fallbacks(lrc):
