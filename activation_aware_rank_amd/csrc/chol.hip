@@ -24,7 +24,6 @@ namespace {
 
 constexpr int GT = 64;        // output tile edge of k_dgemm (rows and cols)
 constexpr int GK = 16;        // k-tile of k_dgemm
-constexpr int GLD = GT + 16;  // padded LDS row (doubles): k rows 1 apart land in other banks
 constexpr int NBC = 64;       // block size of the Cholesky and of the triangular solves
 constexpr int GRID_Y_MAX = 65535;
 
@@ -47,16 +46,22 @@ struct GemmArgs {
 // or B[j*ldb + k] (TB 1).  Masks: MA 1 keeps op(A)[i][k] only for k <= i, MA 2 only for k >= i;
 // MB 1 keeps op(B)[k][j] only for k <= j, MB 2 only for k >= j.  Masked entries are never read.
 // OUTF 0: C = alpha acc + beta C (C not read when beta == 0); OUTF 1: Cf = (float)(alpha acc).
-template <int TA, int TB, int MA, int MB, int OUTF>
-__global__ __launch_bounds__(256) void k_dgemm(GemmArgs g) {
+// BT: output tile edge, 64 (4 waves of 32 x 32) or 128 (4 waves of 64 x 64, for large products:
+// half the operand traffic per flop).  Each wave holds (BT / 32) x (BT / 32) tiles of the 16x16x4
+// fp64 MFMA.
+template <int TA, int TB, int MA, int MB, int OUTF, int BT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BT == 128 ? 2 : 1))) void k_dgemm(GemmArgs g) {
+    constexpr int NF = BT / 32;        // MFMA tiles per wave and dimension
+    constexpr int NU = BT / 64;        // 64-row passes of the operand loads
+    constexpr int LD = BT + 16;        // padded LDS row (doubles): k rows 1 apart land in other banks
     const int ti = blockIdx.y, tj = blockIdx.x;
     if (g.tiles == 1 && ti < tj) return;
     if (g.tiles == 2 && ti > tj) return;
-    const int64_t m0 = int64_t(ti) * GT, n0 = int64_t(tj) * GT;
+    const int64_t m0 = int64_t(ti) * BT, n0 = int64_t(tj) * BT;
     int64_t kb = 0, ke = g.K;
-    if (MA == 1) ke = min(ke, m0 + GT);
+    if (MA == 1) ke = min(ke, m0 + BT);
     if (MA == 2) kb = max(kb, m0);
-    if (MB == 1) ke = min(ke, n0 + GT);
+    if (MB == 1) ke = min(ke, n0 + BT);
     if (MB == 2) kb = max(kb, n0);
     if (g.split > 1) {  // part z of the k range, in whole k-tiles
         const int64_t per = ((g.K + g.split - 1) / g.split + GK - 1) / GK * GK;
@@ -64,87 +69,93 @@ __global__ __launch_bounds__(256) void k_dgemm(GemmArgs g) {
         ke = min(ke, int64_t(blockIdx.z + 1) * per);
     }
 
-    __shared__ double sA[GK][GLD];
-    __shared__ double sB[GK][GLD];
+    __shared__ double sA[GK][LD];
+    __shared__ double sB[GK][LD];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+    const int wr = (w >> 1) * (BT / 2), wc = (w & 1) * (BT / 2);
 
-    // each thread stages 4 entries of each operand per k-tile
-    double ra[4], rb[4];
+    // each thread stages 4 NU entries of each operand per k-tile
+    double ra[4 * NU], rb[4 * NU];
     auto gload = [&](int64_t k0) {
-        if (TA == 0) {
-            const int i = t >> 2, kq = (t & 3) * 4;
-            const int64_t row = m0 + i;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t k = k0 + kq + u;
-                bool ok = row < g.M && k < ke;
-                if (MA == 1) ok = ok && k <= row;
-                if (MA == 2) ok = ok && k >= row;
-                ra[u] = ok ? g.A[row * g.lda + k] : 0.0;
+        for (int q = 0; q < NU; ++q) {
+            if (TA == 0) {
+                const int i = (t >> 2) + 64 * q, kq = (t & 3) * 4;
+                const int64_t row = m0 + i;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t k = k0 + kq + u;
+                    bool ok = row < g.M && k < ke;
+                    if (MA == 1) ok = ok && k <= row;
+                    if (MA == 2) ok = ok && k >= row;
+                    ra[4 * q + u] = ok ? g.A[row * g.lda + k] : 0.0;
+                }
+            } else {
+                const int kk = t >> 4, iq = (t & 15) * 4 + 64 * q;
+                const int64_t k = k0 + kk;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t row = m0 + iq + u;
+                    bool ok = row < g.M && k < ke;
+                    if (MA == 1) ok = ok && k <= row;
+                    if (MA == 2) ok = ok && k >= row;
+                    ra[4 * q + u] = ok ? g.A[k * g.lda + row] : 0.0;
+                }
             }
-        } else {
-            const int kk = t >> 4, iq = (t & 15) * 4;
-            const int64_t k = k0 + kk;
+            if (TB == 0) {
+                const int kk = t >> 4, jq = (t & 15) * 4 + 64 * q;
+                const int64_t k = k0 + kk;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t row = m0 + iq + u;
-                bool ok = row < g.M && k < ke;
-                if (MA == 1) ok = ok && k <= row;
-                if (MA == 2) ok = ok && k >= row;
-                ra[u] = ok ? g.A[k * g.lda + row] : 0.0;
-            }
-        }
-        if (TB == 0) {
-            const int kk = t >> 4, jq = (t & 15) * 4;
-            const int64_t k = k0 + kk;
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t col = n0 + jq + u;
+                    bool ok = col < g.N && k < ke;
+                    if (MB == 1) ok = ok && k <= col;
+                    if (MB == 2) ok = ok && k >= col;
+                    rb[4 * q + u] = ok ? g.B[k * g.ldb + col] : 0.0;
+                }
+            } else {
+                const int j = (t >> 2) + 64 * q, kq = (t & 3) * 4;
+                const int64_t col = n0 + j;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t col = n0 + jq + u;
-                bool ok = col < g.N && k < ke;
-                if (MB == 1) ok = ok && k <= col;
-                if (MB == 2) ok = ok && k >= col;
-                rb[u] = ok ? g.B[k * g.ldb + col] : 0.0;
-            }
-        } else {
-            const int j = t >> 2, kq = (t & 3) * 4;
-            const int64_t col = n0 + j;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t k = k0 + kq + u;
-                bool ok = col < g.N && k < ke;
-                if (MB == 1) ok = ok && k <= col;
-                if (MB == 2) ok = ok && k >= col;
-                rb[u] = ok ? g.B[col * g.ldb + k] : 0.0;
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t k = k0 + kq + u;
+                    bool ok = col < g.N && k < ke;
+                    if (MB == 1) ok = ok && k <= col;
+                    if (MB == 2) ok = ok && k >= col;
+                    rb[4 * q + u] = ok ? g.B[col * g.ldb + k] : 0.0;
+                }
             }
         }
     };
     auto sstore = [&]() {
-        if (TA == 0) {
-            const int i = t >> 2, kq = (t & 3) * 4;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) sA[kq + u][i] = ra[u];
-        } else {
-            const int kk = t >> 4, iq = (t & 15) * 4;
+        for (int q = 0; q < NU; ++q) {
+            if (TA == 0) {
+                const int i = (t >> 2) + 64 * q, kq = (t & 3) * 4;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) sA[kk][iq + u] = ra[u];
-        }
-        if (TB == 0) {
-            const int kk = t >> 4, jq = (t & 15) * 4;
+                for (int u = 0; u < 4; ++u) sA[kq + u][i] = ra[4 * q + u];
+            } else {
+                const int kk = t >> 4, iq = (t & 15) * 4 + 64 * q;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) sB[kk][jq + u] = rb[u];
-        } else {
-            const int j = t >> 2, kq = (t & 3) * 4;
+                for (int u = 0; u < 4; ++u) sA[kk][iq + u] = ra[4 * q + u];
+            }
+            if (TB == 0) {
+                const int kk = t >> 4, jq = (t & 15) * 4 + 64 * q;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) sB[kq + u][j] = rb[u];
+                for (int u = 0; u < 4; ++u) sB[kk][jq + u] = rb[4 * q + u];
+            } else {
+                const int j = (t >> 2) + 64 * q, kq = (t & 3) * 4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sB[kq + u][j] = rb[4 * q + u];
+            }
         }
     };
 
-    f64x4_t acc[2][2];
+    f64x4_t acc[NF][NF];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NF; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+        for (int b = 0; b < NF; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 
     if (kb < ke) {
         gload(kb);
@@ -155,14 +166,17 @@ __global__ __launch_bounds__(256) void k_dgemm(GemmArgs g) {
 #pragma unroll
             for (int ks = 0; ks < GK / 4; ++ks) {
                 const int kk = ks * 4 + (lane >> 4);
-                const double a0 = sA[kk][wr + (lane & 15)];
-                const double a1 = sA[kk][wr + 16 + (lane & 15)];
-                const double b0 = sB[kk][wc + (lane & 15)];
-                const double b1 = sB[kk][wc + 16 + (lane & 15)];
-                acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+                double av[NF], bv[NF];
+#pragma unroll
+                for (int x = 0; x < NF; ++x) {
+                    av[x] = sA[kk][wr + x * 16 + (lane & 15)];
+                    bv[x] = sB[kk][wc + x * 16 + (lane & 15)];
+                }
+#pragma unroll
+                for (int x = 0; x < NF; ++x)
+#pragma unroll
+                    for (int y = 0; y < NF; ++y)
+                        acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
             }
             __syncthreads();
         }
@@ -170,9 +184,9 @@ __global__ __launch_bounds__(256) void k_dgemm(GemmArgs g) {
 
     // 16x16 f64 MFMA result: accumulator r of a lane holds row 4 r + lane/16, column lane%16
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NF; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NF; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = m0 + wr + a * 16 + r * 4 + (lane >> 4);
@@ -195,15 +209,25 @@ __global__ __launch_bounds__(256) void k_dgemm(GemmArgs g) {
 template <int TA, int TB, int MA, int MB, int OUTF>
 lrc_status launch_gemm(const GemmArgs &g, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return LRC_OK;
-    const int gy = cdiv(g.M, GT), gx = cdiv(g.N, GT);
+    // 128 x 128 tiles for long contractions that still give every CU two workgroups (a triangular
+    // output launches about half its tiles), else 64 x 64: with k = 64 (the Cholesky's and the
+    // solves' block updates) the larger tiles were slower (two Cholesky factorisations of 5120^2:
+    // 72 -> 91 ms), with k in the thousands faster (whitening products 33 -> 27 ms, Gram 9.7 -> 7.8)
+    const int64_t t128 = cdiv(g.M, 128) * cdiv(g.N, 128) * std::max(1, g.split) / (g.tiles ? 2 : 1);
+    const int BT = (t128 >= 512 && g.K / std::max(1, g.split) >= 512) ? 128 : GT;
+    const int gy = cdiv(g.M, BT), gx = cdiv(g.N, BT);
     if (gy > GRID_Y_MAX) return fail(LRC_ERR_ARG, "matrix too tall for the fp64 product kernel");
     // algorithmic flops: a triangular output (square M = N) counts its triangle incl. the diagonal,
     // a triangular operand of order K its nonzero half
     double flops = 2.0 * double(g.M) * double(g.N) * double(g.K);
     if (g.tiles != 0) flops = double(g.M) * double(g.M + 1) * double(g.K);
     if (MA != 0 || MB != 0) flops = double(g.M) * double(g.N) * double(g.K + 1);
-    LRC_TIMED_LAUNCH("k_dgemm", flops, (k_dgemm<TA, TB, MA, MB, OUTF>), dim3(gx, gy, std::max(1, g.split)), dim3(256),
-                     0, s, g);
+    if (BT == 128)
+        LRC_TIMED_LAUNCH("k_dgemm", flops, (k_dgemm<TA, TB, MA, MB, OUTF, 128>), dim3(gx, gy, std::max(1, g.split)),
+                         dim3(256), 0, s, g);
+    else
+        LRC_TIMED_LAUNCH("k_dgemm", flops, (k_dgemm<TA, TB, MA, MB, OUTF, GT>), dim3(gx, gy, std::max(1, g.split)),
+                         dim3(256), 0, s, g);
     LRC_LAUNCH_CHECK("k_dgemm");
     return LRC_OK;
 }
