@@ -25,6 +25,7 @@ namespace {
 constexpr int GT = 64;        // output tile edge of k_dgemm (rows and cols)
 constexpr int GK = 16;        // k-tile of k_dgemm
 constexpr int NBC = 64;       // block size of the Cholesky and of the triangular solves
+constexpr int CH_PANEL = 256;  // Cholesky panel: columns between two updates of the trailing matrix
 constexpr int GRID_Y_MAX = 65535;
 
 struct GemmArgs {
@@ -217,10 +218,10 @@ lrc_status launch_gemm(const GemmArgs &g, hipStream_t s) {
     const int BT = (t128 >= 512 && g.K / std::max(1, g.split) >= 512) ? 128 : GT;
     const int gy = cdiv(g.M, BT), gx = cdiv(g.N, BT);
     if (gy > GRID_Y_MAX) return fail(LRC_ERR_ARG, "matrix too tall for the fp64 product kernel");
-    // algorithmic flops: a triangular output (square M = N) counts its triangle incl. the diagonal,
-    // a triangular operand of order K its nonzero half
+    // algorithmic flops: a triangular output (origin on the diagonal, M >= N) counts its entries on
+    // one side of the diagonal incl. the diagonal, a triangular operand of order K its nonzero half
     double flops = 2.0 * double(g.M) * double(g.N) * double(g.K);
-    if (g.tiles != 0) flops = double(g.M) * double(g.M + 1) * double(g.K);
+    if (g.tiles != 0) flops -= double(g.N) * double(g.N - 1) * double(g.K);
     if (MA != 0 || MB != 0) flops = double(g.M) * double(g.N) * double(g.K + 1);
     if (BT == 128)
         LRC_TIMED_LAUNCH("k_dgemm", flops, (k_dgemm<TA, TB, MA, MB, OUTF, 128>), dim3(gx, gy, std::max(1, g.split)),
@@ -451,19 +452,37 @@ lrc_status cholesky_run(double *A, int64_t n, int64_t lda, void *ws, size_t, int
     double *Linv = static_cast<double *>(ws);
     hipLaunchKernelGGL(k_info_zero, dim3(1), dim3(64), 0, s, info);
     LRC_LAUNCH_CHECK("k_info_zero");
-    for (int64_t j0 = 0; j0 < n; j0 += NBC) {
-        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, s, A, lda, n, j0, Linv, info);
-        LRC_LAUNCH_CHECK("k_potrf_diag");
-        const int64_t j1 = j0 + NBC;
-        if (j1 >= n) break;
-        double *A21 = A + j1 * lda + j0;
-        // L21 = A21 L11^{-T}, in place: one output column tile, so each workgroup reads its rows
-        // of A21 completely before it writes them
-        lrc_status st = launch_gemm<0, 1, 0, 1, 0>(gemm(n - j1, NBC, NBC, A21, lda, Linv, NBC, A21, lda, 1.0, 0.0), s);
-        if (st != LRC_OK) return st;
-        // A22 -= L21 L21^T on the lower triangle
-        st = launch_gemm<0, 1, 0, 0, 0>(
-            gemm(n - j1, n - j1, NBC, A21, lda, A21, lda, A + j1 * lda + j1, lda, -1.0, 1.0, 1), s);
+    // Two levels of blocking: panels of CH_PANEL columns, each factored in blocks of NBC (the
+    // diagonal block, then L21 for every row below it, then the update of the panel's remaining
+    // columns), and one update of the trailing matrix per panel with a contraction of CH_PANEL:
+    // long enough for the MFMA products to run efficiently, where an update after every 64
+    // columns is a short launch (k = 64) over the whole trailing matrix.
+    for (int64_t p0 = 0; p0 < n; p0 += CH_PANEL) {
+        const int64_t p1 = std::min(n, p0 + CH_PANEL);
+        for (int64_t j0 = p0; j0 < p1; j0 += NBC) {
+            hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, s, A, lda, n, j0, Linv, info);
+            LRC_LAUNCH_CHECK("k_potrf_diag");
+            const int64_t j1 = j0 + NBC;
+            if (j1 >= n) break;
+            double *A21 = A + j1 * lda + j0;
+            // L21 = A21 L11^{-T}, in place: one output column tile, so each workgroup reads its rows
+            // of A21 completely before it writes them
+            lrc_status st =
+                launch_gemm<0, 1, 0, 1, 0>(gemm(n - j1, NBC, NBC, A21, lda, Linv, NBC, A21, lda, 1.0, 0.0), s);
+            if (st != LRC_OK) return st;
+            // the panel's remaining columns j1 .. p1-1, every row below: A -= L21 L21[panel]^T, on
+            // and below the diagonal
+            if (j1 < p1) {
+                st = launch_gemm<0, 1, 0, 0, 0>(
+                    gemm(n - j1, p1 - j1, NBC, A21, lda, A21, lda, A + j1 * lda + j1, lda, -1.0, 1.0, 1), s);
+                if (st != LRC_OK) return st;
+            }
+        }
+        if (p1 >= n) break;
+        // the trailing matrix: A22 -= L[p1:, p0:p1] L[p1:, p0:p1]^T on the lower triangle
+        double *L21 = A + p1 * lda + p0;
+        const lrc_status st = launch_gemm<0, 1, 0, 0, 0>(
+            gemm(n - p1, n - p1, p1 - p0, L21, lda, L21, lda, A + p1 * lda + p1, lda, -1.0, 1.0, 1), s);
         if (st != LRC_OK) return st;
     }
     if (n > 1) {
