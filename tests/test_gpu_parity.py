@@ -269,6 +269,41 @@ def test_eigh_jacobi_vs_oracle(lrc, n, batch, prec):
         assert s <= 1e-3, (b, s, gap(lam_r, k))
 
 
+def test_eigh_jacobi_degenerate(lrc):
+    """The n <= 128 path on degenerate inputs: a rank-deficient per-head covariance (40 tokens,
+    n = 128: 88 eigenvalues at rounding level), a permuted diagonal with repeated eigenvalues
+    (n = 96), the zero matrix and the orders 1 and 2."""
+    _say("eigh jacobi degenerate inputs")
+    d = inputs.per_head(n_tok=40, d_model=128, head_dim=128)
+    C = oracle.covariance(d["X"], "bf16", d["W"], "bf16").astype(np.float32)
+    lam, V, info = lrc.lrc_eigh(dev(C, "f32"), n_vec=128, prec=2)
+    lam, V = host(lam), host(V).astype(np.float64)
+    assert int(host(info)[0]) == 0
+    lam_r, V_r = oracle.eigh(C.astype(np.float64))
+    assert np.max(np.abs(lam - lam_r)) <= 1e-5 * lam_r[0]
+    assert np.all(np.abs(lam[40:]) <= 1e-5 * lam_r[0])
+    assert sin_theta_max(V, V_r, 32) <= 1e-3
+    assert np.max(np.abs(V.T @ V - np.eye(128))) <= 1e-5
+    dvals = np.array([3.0] * 30 + [1.5] * 50 + [0.25] * 16, dtype=np.float32)
+    perm = np.random.default_rng(4).permutation(96)
+    lam, V, info = lrc.lrc_eigh(dev(np.diag(dvals[perm]), "f32"), n_vec=96, prec=2)
+    lam, V = host(lam), host(V).astype(np.float64)
+    assert int(host(info)[0]) == 0
+    assert np.allclose(lam, np.sort(dvals)[::-1], rtol=0, atol=1e-12)
+    assert np.max(np.abs(V.T @ V - np.eye(96))) <= 1e-12
+    P = V[:, :30] @ V[:, :30].T
+    assert np.allclose(P, np.diag((dvals[perm] == 3).astype(float)), atol=1e-12)
+    lam, V, info = lrc.lrc_eigh(torch.zeros(128, 128, dtype=torch.float32, device="cuda"), n_vec=128, prec=2)
+    assert int(host(info)[0]) == 0 and np.all(host(lam) == 0)
+    assert np.array_equal(host(V), np.eye(128, dtype=np.float32))
+    for Cs in (np.array([[2.5]]), np.array([[2.0, 1.0], [1.0, 2.0]])):
+        lam, V, info = lrc.lrc_eigh(dev(Cs.astype(np.float32), "f32"), n_vec=len(Cs), prec=2)
+        lam_r, V_r = oracle.eigh(Cs)
+        assert int(host(info)[0]) == 0
+        assert np.allclose(host(lam), lam_r, rtol=1e-14, atol=0)
+        assert np.allclose(np.abs(host(V)), np.abs(V_r), atol=1e-7)
+
+
 @pytest.mark.parametrize("prec", [1, 2])
 def test_eigh_large_batch_matches_single_calls(lrc, prec):
     """Members of a batch (n > 128) run concurrently on helper streams, several at a time, each
