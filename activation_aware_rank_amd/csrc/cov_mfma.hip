@@ -26,8 +26,11 @@
 // contiguous k-values of one row).  The GEMM's block tile is 256 x 256 on 8 waves (2 x 4) of
 // 128 x 64, two waves to a SIMD (10 % faster than 4 waves of 128 x 128 at d_in 4096: a wave's
 // accumulators and operands fit its registers without spills, and one wave's MFMAs run while the
-// other waits); the SYRK's is 128 x 128 on 4 waves; k step 32, double-buffered LDS with an XOR
-// swizzle of the 16-byte chunks (no padding, no bank conflicts on 16-byte reads), one barrier
+// other waits; with the operands loaded straight into LDS the 4-wave tile is still 5-10 % slower);
+// the SYRK's is 128 x 128 on 4 waves; k step 32, LDS stages with an XOR swizzle of the 16-byte
+// chunks (no padding, no bank conflicts on 16-byte reads), both operands loaded by 16-byte buffer
+// loads with an LDS destination (GEMM: three stages, 4-5 % faster than staging the loads through
+// registers, which remains for a contraction length that is not a multiple of 32), one barrier
 // per k step, placed between the step's two k slices: the LDS reads of the next step's first
 // slice go out right after it and land while the current step's second slice is multiplied,
 // instead of stalling the next step's first MFMAs (GEMM 3-4 %, SYRK up to 4 % faster).  A
@@ -214,6 +217,115 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // s_waitcnt with vmcnt = n (0..63) and no wait on the other counters (gfx9 encoding)
 #define LRC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// GEMM main loop with the operands loaded straight into LDS (k a multiple of the k step).  Three LDS
+// stages; per step kt: loads of step kt+2 into the stage step kt-1 read; LDS reads of slice 2 of
+// kt; MFMAs of slice 1 (its fragments read at the end of step kt-1); this wave's loads of step kt+1
+// and its LDS reads done, barrier; LDS reads of slice 1 of kt+1; MFMAs of slice 2 of kt.  A lane's
+// 16-byte load of row r lands at st + r * MK + 8 (lane & 3) (linear in the lane), so the swizzle of
+// swz() is applied on the global side; rows past rows[o] read zero through an offset of 2^31.
+template <int BM, int THREADS, int WGM>
+__device__ __forceinline__ void gemm_dma_mainloop(const bf16_t *const *base, const int64_t *ld, const int *rows,
+                                                  int64_t klen,
+                                                  f32x16_t (&acc)[MfmaCfg<BM, BM, THREADS, WGM>::TM][MfmaCfg<BM, BM, THREADS, WGM>::TN],
+                                                  bf16_t *lds0, bf16_t *lds1, bf16_t *lds2) {
+    using T = MfmaCfg<BM, BM, THREADS, WGM>;
+    constexpr int TM = T::TM, TN = T::TN, U = T::UA;
+    static_assert(T::UA == T::UB, "square block tile");
+    constexpr int RPU = 16 * (THREADS / 64);  // rows covered by one load per thread
+    constexpr int LPS = 2 * U;                // loads per thread per step
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / T::WGN, wn = wave % T::WGN;
+    const int nk = int(klen / MK);
+    if (nk <= 0) return;
+    __amdgpu_buffer_rsrc_t rs[2];
+    uint32_t roff[2][U];
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+        rs[o] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t *>(base[o]), short(0),
+            int(rows[o] > 0 ? ((int64_t(rows[o]) - 1) * ld[o] + klen) * 2 : int64_t(0)), 0x00020000);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = 16 * wave + (lane >> 2) + RPU * u;
+            const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+            roff[o][u] = r < rows[o] ? uint32_t((int64_t(r) * ld[o] + c * 8) * 2) : 0x80000000u;
+        }
+    }
+    auto issue = [&](int kt, bf16_t *st) {
+#pragma unroll
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[o], (lds_void_t *)(st + o * BM * MK + (16 * wave + RPU * u) * MK),
+                                                         16, int(roff[o][u] + uint32_t(kt) * uint32_t(MK * 2)), 0, 0, 0);
+    };
+    bf16x8_t f1a[TM], f1b[TN], f2a[TM], f2b[TN];
+    auto fread = [&](const bf16_t *st, int ks, bf16x8_t (&fa)[TM], bf16x8_t (&fb)[TN]) {
+        const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            fa[t] = *reinterpret_cast<const bf16x8_t *>(st + swz(wm * T::WM + t * 32 + (lane & 31), c));
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            fb[t] = *reinterpret_cast<const bf16x8_t *>(st + BM * MK + swz(wn * T::WN + t * 32 + (lane & 31), c));
+    };
+    auto mfmas = [&](const bf16x8_t (&fa)[TM], const bf16x8_t (&fb)[TN]) {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+                acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
+    };
+    auto step = [&](int kt, const bf16_t *cur, const bf16_t *nxt, bf16_t *fre) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kt + 2, fre);
+        fread(cur, 1, f2a, f2b);
+        mfmas(f1a, f1b);
+        if constexpr (TM == 4 && TN == 2 && LPS == 4) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load into LDS
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads of slice 2
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            }
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        LRC_WAIT_VMCNT(LPS);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        fread(nxt, 0, f1a, f1b);
+        mfmas(f2a, f2b);
+        if constexpr (TM == 4 && TN == 2) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads of the next slice 1
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+    };
+    issue(0, lds0);
+    issue(1, lds1);
+    LRC_WAIT_VMCNT(LPS);
+    lds_barrier();
+    fread(lds0, 0, f1a, f1b);
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 3) {
+        step(kt, lds0, lds1, lds2);
+        step(kt + 1, lds1, lds2, lds0);
+        step(kt + 2, lds2, lds0, lds1);
+    }
+    if (kt < nk) step(kt, lds0, lds1, lds2);
+    if (kt + 1 < nk) step(kt + 1, lds1, lds2, lds0);
+    // the loads issued past the last step still write LDS: let them land before the epilogue
+    __builtin_amdgcn_sched_barrier(0);
+    LRC_WAIT_VMCNT(0);
+    lds_barrier();
+}
 
 template <int BM, int BN, int NOPS, int NPROD, int NST, int THREADS, int WGM>
 __device__ __forceinline__ void syrk_dma_mainloop(const bf16_t *const *base, const int64_t D, const int *rows,
@@ -501,7 +613,7 @@ __global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(
 k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const bf16_t *__restrict__ X, int64_t ldx,
              int64_t tc, const int32_t *__restrict__ ex, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo) {
     using Cfg = MfmaCfg<BM, BM, G_THREADS, G_WGM>;
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * BM * MK];
+    __shared__ __attribute__((aligned(16))) bf16_t lds[(KCHECK ? 2 : 3) * 2 * BM * MK];
     int64_t ti, tt;
     gemm_tile_of(blockIdx.x, (d_out + BM - 1) / BM, (tc + BM - 1) / BM, ti, tt);
     const int64_t i0 = ti * BM, t0 = tt * BM;
@@ -513,7 +625,10 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
     for (int a = 0; a < Cfg::TM; ++a)
 #pragma unroll
         for (int b = 0; b < Cfg::TN; ++b) acc[a][b] = f32x16_t{};
-    gemm_mainloop<BM, G_THREADS, G_WGM, KCHECK>(base, ld, rows, d_in, acc, lds);
+    if constexpr (KCHECK)
+        gemm_mainloop<BM, G_THREADS, G_WGM, KCHECK>(base, ld, rows, d_in, acc, lds);
+    else
+        gemm_dma_mainloop<BM, G_THREADS, G_WGM>(base, ld, rows, d_in, acc, lds, lds + 2 * BM * MK, lds + 4 * BM * MK);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm)
