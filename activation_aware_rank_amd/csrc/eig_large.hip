@@ -6,7 +6,9 @@
 //     update of the trailing matrix), working precision T_ (fp32 or fp64).  Only the upper
 //     triangle is kept current; the symmetric product of each column reads every upper tile once
 //     and forms both its row and its column contribution.  Two launches per column (the product,
-//     then the column's W and the next column), one for all members of a lockstep group.
+//     then the column's W and the next column), one for all members of a lockstep group.  Once the
+//     trailing block fits in LDS (order <= 256 in fp32, <= 192 in fp64; from the start for such
+//     orders), one workgroup reduces the rest of it (k_trd_small).
 //  2. All n eigenvalues of T by multisection on Sturm counts, fp64, 16 lanes per eigenvalue.
 //  3. Eigenvectors of T for the n_vec largest eigenvalues by inverse iteration, fp64, one thread
 //     per vector (LU with partial pivoting of T - lambda I once, then three solves); vectors of
@@ -618,6 +620,107 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
         const int idx = v < QW ? QW * sub + v : NB + QW * sub + (v - QW);
         qcol[int64_t(blockIdx.x) * 2 * NB + idx] = qsum;
     }
+}
+
+// The last m = n - p0 columns of the tridiagonalisation by one workgroup (the whole matrix when
+// p0 = 0), with the trailing block's upper triangle packed in LDS: row i of the block holds A(i, j),
+// j >= i, at rb(i) + j, rb(i) = i (2m - i - 1) / 2.  Same reflectors as the column chain above
+// (H_c = I - tau v v^T, v[c+1] = 1), unblocked: per column c = p0 + k, with L = m - k - 1 and x the
+// block's row k right of the diagonal,
+//   beta, tau, v from x (every wave forms ||x[1:]||^2 itself, the same sum in the same order, and
+//     every thread takes v[j] = x[j] / (alpha - beta) from LDS where it needs it: no barrier);
+//   p = tau A_t v over the trailing L x L block, four lanes per row; barrier;
+//   w = p - (tau/2)(p^T v) v (p^T v formed by every wave), A_t -= v w^T + w v^T; barrier.
+// Two barriers per column instead of two launches: a 256-column block in LDS takes the time that a
+// few columns of the launch chain take.
+template <class T>
+struct TrdSmall {
+    static constexpr int NMAX = sizeof(T) == 4 ? 256 : 192;  // packed triangle + p within 160 KiB
+    static size_t smem(int m) { return (size_t(m) * size_t(m + 1) / 2 + size_t(m)) * sizeof(T); }
+};
+constexpr int TRS_THREADS = 1024;
+
+template <class T>
+__global__ void __launch_bounds__(TRS_THREADS) k_trd_small(const T *__restrict__ A, int64_t lda, int64_t n, int64_t p0,
+                                                         T *__restrict__ Rt, T *__restrict__ tau,
+                                                         double *__restrict__ d, double *__restrict__ e, int64_t zs) {
+    A = zoff(A, zs);
+    Rt = zoff(Rt, zs);
+    tau = zoff(tau, zs);
+    d = zoff(d, zs);
+    e = zoff(e, zs);
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int m = int(n - p0);
+    T *P = reinterpret_cast<T *>(smem);
+    T *pp = P + m * (m + 1) / 2;
+    constexpr int NW = TRS_THREADS / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto rb = [m](int i) { return i * (2 * m - i - 1) / 2; };
+    for (int i = wave; i < m; i += NW) {
+        const T *src = A + (p0 + i) * lda + p0;
+        T *dst = P + rb(i);
+        for (int j = i + lane; j < m; j += 64) dst[j] = src[j];
+    }
+    __syncthreads();
+    for (int k = 0; k < m - 1; ++k) {
+        const int64_t c = p0 + k;
+        const int L = m - k - 1;
+        const T *x = P + rb(k) + k + 1;  // x[j] = A(k, k + 1 + j), j < L
+        T s2 = T(0);
+        for (int j = 1 + lane; j < L; j += 64) s2 += x[j] * x[j];
+        for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o);
+        const T alpha = x[0];
+        T beta, tv, scale;
+        if (s2 == T(0)) {
+            tv = T(0);
+            beta = alpha;
+            scale = T(0);
+        } else {
+            const T nrm = sqrt(alpha * alpha + s2);
+            beta = alpha >= T(0) ? -nrm : nrm;
+            tv = (beta - alpha) / beta;
+            scale = T(1) / (alpha - beta);
+        }
+        auto v = [&](int j) -> T { return j == 0 ? T(1) : x[j] * scale; };
+        if (tid == 0) {
+            d[c] = double(P[rb(k) + k]);
+            e[c] = double(beta);
+            tau[c] = tv;
+        }
+        for (int64_t r = tid; r < n; r += TRS_THREADS) Rt[c * n + r] = r <= c ? T(0) : v(int(r - c - 1));
+        {
+            // p[i] = tau sum_j A_t(i, j) v[j]: lane q of a row's four takes j = q, q + 4, ...; the
+            // entries left of the diagonal are read down column k + 1 + i
+            const int i = tid >> 2, q = tid & 3;
+            T acc = T(0);
+            if (i < L) {
+                const int gi = k + 1 + i;
+                int j = q;
+                for (; j < i; j += 4) acc += P[rb(k + 1 + j) + gi] * v(j);
+                const T *row = P + rb(gi) + k + 1;
+                for (; j < L; j += 4) acc += row[j] * v(j);
+            }
+            acc += __shfl_xor(acc, 1);
+            acc += __shfl_xor(acc, 2);
+            if (q == 0 && i < L) pp[i] = tv * acc;
+        }
+        __syncthreads();
+        T pv = T(0);
+        for (int j = lane; j < L; j += 64) pv += pp[j] * v(j);
+        for (int o = 32; o > 0; o >>= 1) pv += __shfl_xor(pv, o);
+        const T K = T(0.5) * tv * pv;
+        for (int i = wave; i < L; i += NW) {
+            const int gi = k + 1 + i;
+            const T vi = v(i), wi = pp[i] - K * vi;
+            T *row = P + rb(gi) + k + 1;
+            for (int j = i + lane; j < L; j += 64) {
+                const T vj = v(j);
+                row[j] -= vi * (pp[j] - K * vj) + wi * vj;
+            }
+        }
+        __syncthreads();
+    }
+    if (tid == 0) d[n - 1] = double(P[rb(m - 1) + m - 1]);
 }
 
 // Rank-2 jn update of the trailing matrix, A[r][s] -= sum_q V[r][q] W[s][q] + W[r][q] V[s][q] for
@@ -1421,6 +1524,26 @@ struct EigJob {
     int NT = 0, npart = 0;
     int64_t p0 = 0, p1 = 0, c = 0, c0 = 0;
 
+    // the last columns by one workgroup in LDS (p0 = 0: the whole matrix), then on to stage 2
+    lrc_status small_tail() {
+        const size_t sm = TrdSmall<T>::smem(int(n - p0));
+        LRC_HIP(hipFuncSetAttribute(reinterpret_cast<const void *>(k_trd_small<T>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(sm)));
+        hipLaunchKernelGGL(k_trd_small<T>, dim3(1, 1, nbatch), dim3(TRS_THREADS), sm, s, w->A, w->lda, n, p0, w->Rt,
+                           w->tau, w->d, w->e, zs);
+        LRC_LAUNCH_CHECK("k_trd_small");
+        stage = 2;
+        return LRC_OK;
+    }
+    // stage 1 from column 0 (or the whole tridiagonalisation in LDS for a small order)
+    lrc_status begin_tridiagonal() {
+        p0 = 0;
+        if (n <= TrdSmall<T>::NMAX) return small_tail();
+        start_panel();
+        stage = 1;
+        return LRC_OK;
+    }
+
     void start_panel() {
         p1 = std::min<int64_t>(p0 + NB, n - 1);
         hipLaunchKernelGGL(k_fill_zero<T>, dim3(256, 1, nbatch), dim3(256), 0, s, w->Vp, int64_t(n) * NB, zs);
@@ -1471,10 +1594,7 @@ struct EigJob {
         if (stage == 0) {
             const lrc_status st = prepare();
             if (st != LRC_OK) return st;
-            p0 = 0;
-            start_panel();
-            stage = 1;
-            return LRC_OK;
+            return begin_tridiagonal();
         }
         if (stage == 1) {  // 1. tridiagonalisation, panels over reflector columns 0 .. n-2
             for (int q = 0; q < cols; ++q) {
@@ -1492,6 +1612,7 @@ struct EigJob {
                     stage = 2;
                     return LRC_OK;
                 }
+                if (n - p0 <= TrdSmall<T>::NMAX) return small_tail();
                 start_panel();
             }
             return LRC_OK;
@@ -1886,9 +2007,10 @@ static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p
     EigJob<T> bj = R[0].j;
     bj.nbatch = unsigned(nb);
     bj.zs = int64_t(p.per);
-    bj.p0 = 0;
-    bj.start_panel();
-    bj.stage = 1;
+    {
+        const lrc_status st = bj.begin_tridiagonal();
+        if (st != LRC_OK) return st;
+    }
     while (bj.stage == 1) {
         const lrc_status st = bj.advance(64);
         if (st != LRC_OK) return st;

@@ -215,13 +215,21 @@ def _oracle_cov32(X, xdt, W, n_blocks=1):
 
 
 @pytest.mark.parametrize("prec", [1, 2])
-@pytest.mark.parametrize("case", ["single256", "block300", "gate_like"])
+@pytest.mark.parametrize("case", ["single256", "block300", "gate_like", "order129", "order193"])
 def test_eigh_large_vs_oracle(lrc, case, prec):
+    """Orders above 128: 256 (fp32: the whole tridiagonalisation by one workgroup in LDS), 300 and 430
+    (the column chain, then the last block in LDS), 129 (the smallest order of this path) and 193 (fp64:
+    one column panel before the block)."""
     _say("eigh large %s prec %d" % (case, prec))
     if case == "single256":
         d = inputs.single_layer()
         C32, C64 = _oracle_cov32(d["X"], "f32", d["W"])
         k = 64
+    elif case in ("order129", "order193"):
+        n = 129 if case == "order129" else 193
+        d = inputs.single_layer(n_tok=1024, d_in=n, d_out=n)
+        C32, C64 = _oracle_cov32(d["X"], "f32", d["W"])
+        k = n // 4
     elif case == "block300":
         X = inputs.block_activations(320, 4096)
         W = inputs.weight(320, 300, "bf16", inputs.CFG_BLOCK, 0, 3)
