@@ -7,7 +7,7 @@
 //     triangle is kept current; the symmetric product of each column reads every upper tile once
 //     and forms both its row and its column contribution.  Two launches per column (the product,
 //     then the column's W and the next column), one for all members of a lockstep group.  Once the
-//     trailing block fits in LDS (order <= 256 in fp32, <= 192 in fp64; from the start for such
+//     trailing block fits in LDS (order <= 256 in fp32, <= 176 in fp64; from the start for such
 //     orders), one workgroup reduces the rest of it (k_trd_small).
 //  2. All n eigenvalues of T by multisection on Sturm counts, fp64, 16 lanes per eigenvalue.
 //  3. Eigenvectors of T for the n_vec largest eigenvalues by inverse iteration, fp64, one thread
@@ -625,25 +625,68 @@ k_trd_w1col(T *__restrict__ A, int64_t lda, int64_t n, int64_t c, int j, int nex
 // The last m = n - p0 columns of the tridiagonalisation by one workgroup (the whole matrix when
 // p0 = 0), with the trailing block's upper triangle packed in LDS: row i of the block holds A(i, j),
 // j >= i, at rb(i) + j, rb(i) = i (2m - i - 1) / 2.  Same reflectors as the column chain above
-// (H_c = I - tau v v^T, v[c+1] = 1), unblocked: per column c = p0 + k, with L = m - k - 1 and x the
-// block's row k right of the diagonal,
-//   beta, tau, v from x (every wave forms ||x[1:]||^2 itself, the same sum in the same order, and
-//     every thread takes v[j] = x[j] / (alpha - beta) from LDS where it needs it: no barrier);
-//   p = tau A_t v over the trailing L x L block, four lanes per row; barrier;
-//   w = p - (tau/2)(p^T v) v (p^T v formed by every wave), A_t -= v w^T + w v^T; barrier.
-// Two barriers per column instead of two launches: a 256-column block in LDS takes the time that a
-// few columns of the launch chain take.
+// (H_c = I - tau v v^T, v[c+1] = 1), unblocked.  Per column c = p0 + k, with L = m - k - 1, the
+// trailing indices a, b < L and x the block's row k right of the diagonal:
+//   beta, tau, v from x: every wave forms ||x[1:]||^2 itself (the same sum in the same order) and
+//     every lane takes v[a] = x[a] / (alpha - beta) from LDS where it needs it, so no barrier;
+//   wave w loads its rows b = w, w + 16, ... (entries a >= b, lane l holding a = l + 64 u) into
+//     registers, all at once; from them, p = tau A_t v as row parts sum_{a>=b} A(b, a) v[a] (summed
+//     over each 16-lane row by DPP, four sums per row to LDS) and column parts sum_{b<a} A(b, a) v[b]
+//     (accumulated per lane over the wave's rows, one vector per wave to LDS); barrier; the parts
+//     added in a fixed order, four lanes per entry; barrier;
+//   w = p - (tau/2)(p^T v) v (p^T v formed by every wave), A_t -= v w^T + w v^T from the rows still in
+//     registers; barrier.
+// Each stored entry is read once per column, a wave's accesses to the triangle are to consecutive
+// entries, and its loads are all in flight together.  Three barriers per column instead of two
+// launches.
 template <class T>
 struct TrdSmall {
-    static constexpr int NMAX = sizeof(T) == 4 ? 256 : 192;  // packed triangle + p within 160 KiB
-    static size_t smem(int m) { return (size_t(m) * size_t(m + 1) / 2 + size_t(m)) * sizeof(T); }
+    static constexpr int NMAX = sizeof(T) == 4 ? 256 : 176;  // triangle + partial sums within 160 KiB
+    static constexpr int RPW = (NMAX + 15) / 16;             // rows per wave
+    static constexpr int CH = (NMAX + 63) / 64;              // 64-entry chunks of a row
+    static size_t smem(int m) { return (size_t(m) * size_t(m + 1) / 2 + 21 * size_t(m)) * sizeof(T); }
 };
 constexpr int TRS_THREADS = 1024;
+
+template <int CTRL>
+__device__ __forceinline__ float trs_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double trs_dpp(double v) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ float trs_lane(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+__device__ __forceinline__ double trs_lane(double v, int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l), __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+// sums over the four lanes of a quad and over each row of 16 lanes, the same value in each lane
+// (every step adds a lane pair both ways)
+template <class T>
+__device__ __forceinline__ T trs_quad_sum(T v) {
+    v += trs_dpp<0xB1>(v);        // quad_perm [1, 0, 3, 2]
+    return v + trs_dpp<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+}
+template <class T>
+__device__ __forceinline__ T trs_row16_sum(T v) {
+    v = trs_quad_sum(v);
+    v += trs_dpp<0x141>(v);        // row_half_mirror
+    return v + trs_dpp<0x140>(v);  // row_mirror
+}
+// sum over the 64 lanes, the same value in each: the four row sums added in a fixed order
+template <class T>
+__device__ __forceinline__ T trs_wave_sum(T v) {
+    v = trs_row16_sum(v);
+    return (trs_lane(v, 0) + trs_lane(v, 16)) + (trs_lane(v, 32) + trs_lane(v, 48));
+}
 
 template <class T>
 __global__ void __launch_bounds__(TRS_THREADS) k_trd_small(const T *__restrict__ A, int64_t lda, int64_t n, int64_t p0,
                                                          T *__restrict__ Rt, T *__restrict__ tau,
                                                          double *__restrict__ d, double *__restrict__ e, int64_t zs) {
+    using S = TrdSmall<T>;
     A = zoff(A, zs);
     Rt = zoff(Rt, zs);
     tau = zoff(tau, zs);
@@ -651,9 +694,11 @@ __global__ void __launch_bounds__(TRS_THREADS) k_trd_small(const T *__restrict__
     e = zoff(e, zs);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int m = int(n - p0);
-    T *P = reinterpret_cast<T *>(smem);
-    T *pp = P + m * (m + 1) / 2;
     constexpr int NW = TRS_THREADS / 64;
+    T *P = reinterpret_cast<T *>(smem);
+    T *cpw = P + m * (m + 1) / 2;  // column parts, one vector of m per wave
+    T *rp4 = cpw + NW * m;         // row parts, four per entry
+    T *pp = rp4 + 4 * m;           // p
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     auto rb = [m](int i) { return i * (2 * m - i - 1) / 2; };
     for (int i = wave; i < m; i += NW) {
@@ -664,11 +709,11 @@ __global__ void __launch_bounds__(TRS_THREADS) k_trd_small(const T *__restrict__
     __syncthreads();
     for (int k = 0; k < m - 1; ++k) {
         const int64_t c = p0 + k;
-        const int L = m - k - 1;
-        const T *x = P + rb(k) + k + 1;  // x[j] = A(k, k + 1 + j), j < L
+        const int L = m - k - 1, k1 = k + 1;
+        const T *x = P + rb(k) + k1;  // x[a] = A(k, k + 1 + a), a < L
         T s2 = T(0);
-        for (int j = 1 + lane; j < L; j += 64) s2 += x[j] * x[j];
-        for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o);
+        for (int a = 1 + lane; a < L; a += 64) s2 += x[a] * x[a];
+        s2 = trs_wave_sum(s2);
         const T alpha = x[0];
         T beta, tv, scale;
         if (s2 == T(0)) {
@@ -681,41 +726,80 @@ __global__ void __launch_bounds__(TRS_THREADS) k_trd_small(const T *__restrict__
             tv = (beta - alpha) / beta;
             scale = T(1) / (alpha - beta);
         }
-        auto v = [&](int j) -> T { return j == 0 ? T(1) : x[j] * scale; };
+        auto v = [&](int a) -> T { return a == 0 ? T(1) : x[a] * scale; };
         if (tid == 0) {
             d[c] = double(P[rb(k) + k]);
             e[c] = double(beta);
             tau[c] = tv;
         }
         for (int64_t r = tid; r < n; r += TRS_THREADS) Rt[c * n + r] = r <= c ? T(0) : v(int(r - c - 1));
-        {
-            // p[i] = tau sum_j A_t(i, j) v[j]: lane q of a row's four takes j = q, q + 4, ...; the
-            // entries left of the diagonal are read down column k + 1 + i
-            const int i = tid >> 2, q = tid & 3;
-            T acc = T(0);
-            if (i < L) {
-                const int gi = k + 1 + i;
-                int j = q;
-                for (; j < i; j += 4) acc += P[rb(k + 1 + j) + gi] * v(j);
-                const T *row = P + rb(gi) + k + 1;
-                for (; j < L; j += 4) acc += row[j] * v(j);
+        T vj[S::CH];  // v of this lane's entries a = lane + 64 u
+#pragma unroll
+        for (int u = 0; u < S::CH; ++u) vj[u] = lane + 64 * u < L ? v(lane + 64 * u) : T(0);
+        // this wave's rows, entries a >= b of row b, all loaded before any is used
+        T el[S::RPW][S::CH];
+#pragma unroll
+        for (int t = 0; t < S::RPW; ++t) {
+            const int b = wave + NW * t;
+            const T *row = P + rb(k1 + (b < L ? b : 0)) + k1;
+#pragma unroll
+            for (int u = 0; u < S::CH; ++u) {
+                const int a = lane + 64 * u;
+                el[t][u] = (b < L && a >= b && a < L) ? row[a] : T(0);
             }
-            acc += __shfl_xor(acc, 1);
-            acc += __shfl_xor(acc, 2);
-            if (q == 0 && i < L) pp[i] = tv * acc;
+        }
+        T cacc[S::CH];
+#pragma unroll
+        for (int u = 0; u < S::CH; ++u) cacc[u] = T(0);
+#pragma unroll
+        for (int t = 0; t < S::RPW; ++t) {
+            const int b = wave + NW * t;
+            if (b >= L) break;  // wave-uniform
+            T rs = T(0);
+#pragma unroll
+            for (int u = 0; u < S::CH; ++u) rs += el[t][u] * vj[u];
+            rs = trs_row16_sum(rs);
+            if ((lane & 15) == 0) rp4[b * 4 + (lane >> 4)] = rs;
+            const T vb = v(b);
+#pragma unroll
+            for (int u = 0; u < S::CH; ++u)
+                if (lane + 64 * u > b) cacc[u] += el[t][u] * vb;
+        }
+#pragma unroll
+        for (int u = 0; u < S::CH; ++u)
+            if (lane + 64 * u < m) cpw[wave * m + lane + 64 * u] = cacc[u];
+        __syncthreads();
+        {  // p[a] = tau (row part + column parts of the 16 waves), lane g of a's four adding four waves
+            const int a = tid >> 2, g = tid & 3;
+            T sp = T(0);
+            if (a < L) {
+                sp = rp4[a * 4 + g];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) sp += cpw[(4 * g + w) * m + a];
+            }
+            sp = trs_quad_sum(sp);
+            if (g == 0 && a < L) pp[a] = tv * sp;
         }
         __syncthreads();
         T pv = T(0);
-        for (int j = lane; j < L; j += 64) pv += pp[j] * v(j);
-        for (int o = 32; o > 0; o >>= 1) pv += __shfl_xor(pv, o);
+#pragma unroll
+        for (int u = 0; u < S::CH; ++u)
+            if (lane + 64 * u < L) pv += pp[lane + 64 * u] * vj[u];
+        pv = trs_wave_sum(pv);
         const T K = T(0.5) * tv * pv;
-        for (int i = wave; i < L; i += NW) {
-            const int gi = k + 1 + i;
-            const T vi = v(i), wi = pp[i] - K * vi;
-            T *row = P + rb(gi) + k + 1;
-            for (int j = i + lane; j < L; j += 64) {
-                const T vj = v(j);
-                row[j] -= vi * (pp[j] - K * vj) + wi * vj;
+        T wj[S::CH];
+#pragma unroll
+        for (int u = 0; u < S::CH; ++u) wj[u] = lane + 64 * u < L ? pp[lane + 64 * u] - K * vj[u] : T(0);
+#pragma unroll
+        for (int t = 0; t < S::RPW; ++t) {
+            const int b = wave + NW * t;
+            if (b >= L) break;
+            const T vb = v(b), wb = pp[b] - K * vb;
+            T *row = P + rb(k1 + b) + k1;
+#pragma unroll
+            for (int u = 0; u < S::CH; ++u) {
+                const int a = lane + 64 * u;
+                if (a >= b && a < L) row[a] = el[t][u] - (vb * wj[u] + wb * vj[u]);
             }
         }
         __syncthreads();
