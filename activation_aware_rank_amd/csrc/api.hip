@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "lrc_internal.h"
+#include "cov_mfma.h"
 
 namespace lrc {
 
@@ -178,19 +179,67 @@ lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64
 }
 
 // ---------------------------------------------------------------------------------------------
+size_t lrc_range_factor_workspace(int64_t d_in, int64_t n) {
+    if (d_in <= 0 || n <= 0) return 0;
+    Counter c;
+    c.carve<double>(size_t(d_in) * size_t(n));
+    c.carve<char>(cholesky_workspace(d_in));
+    return c.off;
+}
+
+lrc_status lrc_range_factor(const void *W, lrc_dtype w_t, int64_t d_in, int64_t n, int64_t ldw, double *L,
+                            int64_t ldl, void *ws, size_t ws_bytes, int32_t *info, void *stream) {
+    REQUIRE(W && L && info, LRC_ERR_ARG, "W, L and info must be non-NULL");
+    REQUIRE(d_in > 0 && n >= d_in, LRC_ERR_ARG, "need 0 < d_in <= n");
+    REQUIRE(ldw >= n && ldl >= d_in, LRC_ERR_ARG, "ldw < n or ldl < d_in");
+    REQUIRE(w_t == LRC_BF16 || w_t == LRC_F32 || w_t == LRC_F64, LRC_ERR_DTYPE, "w_t must be LRC_BF16, LRC_F32 or LRC_F64");
+    const size_t need = lrc_range_factor_workspace(d_in, n);
+    REQUIRE(ws_bytes >= need && ws && aligned(ws, 256), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_range_factor_workspace() or not 256-byte aligned");
+    Carver cv(ws, ws_bytes);
+    double *Wf = cv.carve<double>(size_t(d_in) * size_t(n));
+    void *chol = cv.carve<char>(cholesky_workspace(d_in));
+    return range_factor_enqueue(W, w_t, d_in, n, ldw, Wf, L, ldl, chol, info, static_cast<hipStream_t>(stream));
+}
+
+size_t lrc_cov_accumulate_range_workspace(int64_t n_tok, int64_t d_in) {
+    if (n_tok <= 0 || d_in <= 0) return 0;
+    return cov_range_workspace(n_tok, d_in);
+}
+
+lrc_status lrc_cov_accumulate_range(const void *X, lrc_dtype x_t, int64_t n_tok, int64_t d_in, int64_t ldx,
+                                    const double *L, int64_t ldl, float *B, int64_t ldb, void *ws, size_t ws_bytes,
+                                    int32_t *info, void *stream) {
+    REQUIRE(X && L && B && info, LRC_ERR_ARG, "X, L, B and info must be non-NULL");
+    REQUIRE(n_tok > 0 && d_in > 0, LRC_ERR_ARG, "n_tok and d_in must be positive");
+    REQUIRE(x_t == LRC_BF16, LRC_ERR_DTYPE, "x_t must be LRC_BF16");
+    REQUIRE(d_in % 32 == 0, LRC_ERR_ARG, "d_in must be a multiple of 32");
+    REQUIRE(ldx >= d_in && ldl >= d_in && ldb >= d_in, LRC_ERR_ARG, "ldx, ldl or ldb < d_in");
+    REQUIRE(cov_mfma_supported(x_t, X, ldx, nullptr, 0, d_in, d_in, 1), LRC_ERR_ARG,
+            "X must be 16-byte aligned with ldx a multiple of 8 (and below 2^21)");
+    const size_t need = cov_range_workspace(n_tok, d_in);
+    REQUIRE(ws_bytes >= need && ws && aligned(ws, 256), LRC_ERR_WORKSPACE,
+            "workspace smaller than lrc_cov_accumulate_range_workspace() or not 256-byte aligned");
+    CovArgs a{X, x_t, n_tok, d_in, ldx, nullptr, d_in, 0, 1, B, ldb, info, L, ldl};
+    return cov_run(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------------
 size_t lrc_eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype prec) {
     if (n <= 0 || batch <= 0 || n_vec < 0 || n_vec > n) return 0;
     return eigh_workspace(n, batch, n_vec, prec);
 }
 
+// nc: the order of the stored matrices (n, or d_in for a projected group)
 static lrc_status check_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64_t stride_c,
                              const double *lambda, const float *V, int64_t ldv, int64_t n_vec, int64_t stride_v,
-                             const int32_t *info) {
+                             const int32_t *info, int64_t nc = -1) {
+    if (nc < 0) nc = n;
     REQUIRE(C && lambda && info, LRC_ERR_ARG, "C, lambda and info must be non-NULL");
     REQUIRE(n > 0 && batch > 0, LRC_ERR_ARG, "n and batch must be positive");
     REQUIRE(n <= (int64_t(1) << 20), LRC_ERR_ARG, "n too large");
-    REQUIRE(ldc >= n, LRC_ERR_ARG, "ldc < n");
-    REQUIRE(batch == 1 || stride_c >= n * ldc - (ldc - n), LRC_ERR_ARG, "stride_c overlaps matrices");
+    REQUIRE(ldc >= nc, LRC_ERR_ARG, "ldc < n (d_in for a projected group)");
+    REQUIRE(batch == 1 || stride_c >= nc * ldc - (ldc - nc), LRC_ERR_ARG, "stride_c overlaps matrices");
     REQUIRE(n_vec >= 0 && n_vec <= n, LRC_ERR_ARG, "n_vec must be in [0, n]");
     REQUIRE(n_vec == 0 || (V && ldv >= n_vec), LRC_ERR_ARG, "V NULL or ldv < n_vec");
     REQUIRE(n_vec == 0 || batch == 1 || stride_v >= n * ldv - (ldv - n_vec), LRC_ERR_ARG,
@@ -217,7 +266,7 @@ static std::vector<EighArgs> eigh_groups(const lrc_eigh_group *g, int32_t count,
     for (int32_t i = 0; i < count; ++i)
         v.push_back(EighArgs{g[i].C, g[i].n, g[i].ldc, g[i].batch, g[i].stride_c, prec, g[i].lambda, g[i].V,
                              g[i].ldv, g[i].n_vec, g[i].stride_v, g[i].info, g[i].W, g[i].w_t, g[i].d_in,
-                             g[i].ldw, g[i].stride_w});
+                             g[i].ldw, g[i].stride_w, g[i].projected});
     return v;
 }
 
@@ -234,8 +283,12 @@ lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype
     REQUIRE(groups && count > 0, LRC_ERR_ARG, "groups must be non-NULL and count positive");
     for (int32_t i = 0; i < count; ++i) {
         const lrc_eigh_group &g = groups[i];
+        REQUIRE(g.projected == 0 || g.projected == 1, LRC_ERR_ARG, "projected must be 0 or 1");
+        if (g.projected)
+            REQUIRE(g.W && g.d_in > 128 && g.d_in < g.n && g.n_vec <= g.d_in, LRC_ERR_ARG,
+                    "a projected group needs its range basis W with 128 < d_in < n and n_vec <= d_in");
         lrc_status st = check_eigh(g.C, g.n, g.ldc, g.batch, g.stride_c, g.lambda, g.V, g.ldv, g.n_vec, g.stride_v,
-                                   g.info);
+                                   g.info, g.projected ? g.d_in : g.n);
         if (st != LRC_OK) return st;
         if (g.W) {
             REQUIRE(g.w_t == LRC_BF16 || g.w_t == LRC_F32 || g.w_t == LRC_F64, LRC_ERR_DTYPE,

@@ -211,7 +211,7 @@ size_t cov_workspace(lrc_dtype x_t, int64_t n_tok, int64_t d_in, int has_w, int6
 
 lrc_status cov_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
     const int64_t hd = a.d_out / a.n_blocks;
-    if (use_mfma(a)) {
+    if (a.L || use_mfma(a)) {  // the range-projected product has only the MFMA path
         lrc_status st = cov_mfma_run(a, ws, ws_bytes, s);
         if (st != LRC_OK) return st;
     } else {

@@ -224,11 +224,16 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // and its LDS reads done, barrier; LDS reads of slice 1 of kt+1; MFMAs of slice 2 of kt.  A lane's
 // 16-byte load of row r lands at st + r * MK + 8 (lane & 3) (linear in the lane), so the swizzle of
 // swz() is applied on the global side; rows past rows[o] read zero through an offset of 2^31.
-template <int BM, int THREADS, int WGM>
+//
+// NP > 1 (the range-projected product): the A rows hold NP pieces of klen values each, side by
+// side (A row length NP klen), all multiplied by the same B row, and only k steps kt0 .. klen/MK - 1
+// of each piece are taken (A is zero left of them): step j of the loop is step kt0 + j % span of
+// piece j / span, span = klen/MK - kt0.
+template <int BM, int THREADS, int WGM, int NP = 1>
 __device__ __forceinline__ void gemm_dma_mainloop(const bf16_t *const *base, const int64_t *ld, const int *rows,
                                                   int64_t klen,
                                                   f32x16_t (&acc)[MfmaCfg<BM, BM, THREADS, WGM>::TM][MfmaCfg<BM, BM, THREADS, WGM>::TN],
-                                                  bf16_t *lds0, bf16_t *lds1, bf16_t *lds2) {
+                                                  bf16_t *lds0, bf16_t *lds1, bf16_t *lds2, int kt0 = 0) {
     using T = MfmaCfg<BM, BM, THREADS, WGM>;
     constexpr int TM = T::TM, TN = T::TN, U = T::UA;
     static_assert(T::UA == T::UB, "square block tile");
@@ -236,15 +241,18 @@ __device__ __forceinline__ void gemm_dma_mainloop(const bf16_t *const *base, con
     constexpr int LPS = 2 * U;                // loads per thread per step
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / T::WGN, wn = wave % T::WGN;
-    const int nk = int(klen / MK);
+    const int nkx = int(klen / MK);
+    const int span = NP == 1 ? nkx : nkx - kt0;
+    const int nk = NP * span;
     if (nk <= 0) return;
     __amdgpu_buffer_rsrc_t rs[2];
     uint32_t roff[2][U];
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
+        const int64_t kl = o == 0 ? NP * klen : klen;  // row length of the operand
         rs[o] = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<bf16_t *>(base[o]), short(0),
-            int(rows[o] > 0 ? ((int64_t(rows[o]) - 1) * ld[o] + klen) * 2 : int64_t(0)), 0x00020000);
+            int(rows[o] > 0 ? ((int64_t(rows[o]) - 1) * ld[o] + kl) * 2 : int64_t(0)), 0x00020000);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = 16 * wave + (lane >> 2) + RPU * u;
@@ -253,12 +261,20 @@ __device__ __forceinline__ void gemm_dma_mainloop(const bf16_t *const *base, con
         }
     }
     auto issue = [&](int kt, bf16_t *st) {
+        int ks[2] = {kt, kt};  // k step of A and of B
+        if constexpr (NP > 1) {
+            // steps past the last one (loaded, never read) stay inside the operands' resources
+            static_assert(NP <= 3, "at most three pieces");
+            const int p = int(kt >= span) + int(NP > 2 && kt >= 2 * span);
+            ks[1] = kt0 + kt - p * span;
+            ks[0] = p * nkx + ks[1];
+        }
 #pragma unroll
         for (int o = 0; o < 2; ++o)
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[o], (lds_void_t *)(st + o * BM * MK + (16 * wave + RPU * u) * MK),
-                                                         16, int(roff[o][u] + uint32_t(kt) * uint32_t(MK * 2)), 0, 0, 0);
+                                                         16, int(roff[o][u] + uint32_t(ks[o]) * uint32_t(MK * 2)), 0, 0, 0);
     };
     bf16x8_t f1a[TM], f1b[TN], f2a[TM], f2b[TN];
     auto fread = [&](const bf16_t *st, int ks, bf16x8_t (&fa)[TM], bf16x8_t (&fb)[TN]) {
@@ -608,17 +624,21 @@ __device__ __forceinline__ void gemm_tile_of(int64_t b, int64_t gi, int64_t gt, 
     i = r / gte;
     t = t0 + r % gte;
 }
-template <int BM, bool KCHECK>
+// NP == 3: the range-projected product Y~ = X L.  Wt then holds A = L^T (d_out = d_in rows) as
+// three bf16 pieces side by side (row length 3 d_in, see k_range_pieces); A is upper triangular,
+// so block row i0 takes only the k steps from i0 / MK on, in each piece.
+template <int BM, bool KCHECK, int NP = 1>
 __global__ void __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const bf16_t *__restrict__ X, int64_t ldx,
              int64_t tc, const int32_t *__restrict__ ex, bf16_t *__restrict__ Yhi, bf16_t *__restrict__ Ylo) {
+    static_assert(NP == 1 || !KCHECK, "pieces need a contraction length that is a multiple of the k step");
     using Cfg = MfmaCfg<BM, BM, G_THREADS, G_WGM>;
     __shared__ __attribute__((aligned(16))) bf16_t lds[(KCHECK ? 2 : 3) * 2 * BM * MK];
     int64_t ti, tt;
     gemm_tile_of(blockIdx.x, (d_out + BM - 1) / BM, (tc + BM - 1) / BM, ti, tt);
     const int64_t i0 = ti * BM, t0 = tt * BM;
-    const bf16_t *base[2] = {Wt + i0 * d_in, X + t0 * ldx};
-    const int64_t ld[2] = {d_in, ldx};
+    const bf16_t *base[2] = {Wt + i0 * d_in * NP, X + t0 * ldx};
+    const int64_t ld[2] = {d_in * NP, ldx};
     const int rows[2] = {int(std::min<int64_t>(BM, d_out - i0)), int(std::max<int64_t>(0, std::min<int64_t>(BM, tc - t0)))};
     f32x16_t acc[Cfg::TM][Cfg::TN];
 #pragma unroll
@@ -628,7 +648,8 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
     if constexpr (KCHECK)
         gemm_mainloop<BM, G_THREADS, G_WGM, KCHECK>(base, ld, rows, d_in, acc, lds);
     else
-        gemm_dma_mainloop<BM, G_THREADS, G_WGM>(base, ld, rows, d_in, acc, lds, lds + 2 * BM * MK, lds + 4 * BM * MK);
+        gemm_dma_mainloop<BM, G_THREADS, G_WGM, NP>(base, ld, rows, d_in, acc, lds, lds + 2 * BM * MK, lds + 4 * BM * MK,
+                                                    NP > 1 ? int(i0 / MK) : 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 #pragma unroll
     for (int tm = 0; tm < Cfg::TM; ++tm)
@@ -915,6 +936,38 @@ __global__ void __launch_bounds__(256) k_lo_sq_add(const float *__restrict__ par
     C[j * ldc + j % hd] += ldexpf(s, -2 * ex[j]);
 }
 
+// A = L^T in three bf16 pieces from the lower triangle of L (d x d fp64, ldl): row i of A is
+// [hi | mid | lo] of column i of L, A[i][p d + k] = piece p of L[k][i] for k >= i and 0 for k < i
+// (the strict upper triangle of L is not read).  hi = bf16(v), mid = bf16(v - hi), lo =
+// bf16(v - hi - mid), each difference exact in fp64, so hi + mid + lo equals v to about 2^-26 |v|.
+// 64 x 64 tiles of L transposed through LDS.
+__global__ void __launch_bounds__(256) k_range_pieces(const double *__restrict__ L, int64_t ldl, int64_t d,
+                                                      bf16_t *__restrict__ A) {
+    __shared__ double tile[64][65];
+    const int64_t k0 = int64_t(blockIdx.y) * 64, i0 = int64_t(blockIdx.x) * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int kk = e / 64, ii = e % 64;
+        const int64_t k = k0 + kk, i = i0 + ii;
+        tile[kk][ii] = (k < d && i < d && k >= i) ? L[k * ldl + i] : 0.0;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int ii = e / 64, kk = e % 64;
+        const int64_t k = k0 + kk, i = i0 + ii;
+        if (k >= d || i >= d) continue;
+        const double v = tile[kk][ii];
+        const bf16_t hi = f32_to_bf16(float(v));
+        const double r1 = v - double(bf16_to_f32(hi));
+        const bf16_t mid = f32_to_bf16(float(r1));
+        const double r2 = r1 - double(bf16_to_f32(mid));
+        const bf16_t lo = f32_to_bf16(float(r2));
+        bf16_t *row = A + i * 3 * d;
+        row[k] = hi;
+        row[d + k] = mid;
+        row[2 * d + k] = lo;
+    }
+}
+
 __global__ void k_fill_f32(float *__restrict__ p, int64_t n) {
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
         p[i] = 0.f;
@@ -990,11 +1043,12 @@ bool cov_mfma_supported(lrc_dtype x_t, const void *X, int64_t ldx, const void *W
            (d_out + 1) * (MFMA_CHUNK + 4 * MK) * 2 < (int64_t(1) << 31);
 }
 
-size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks) {
+// np: 1, or 3 for the range-projected product (A = L^T in three pieces)
+static size_t mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks, int np) {
     const MfmaPlan p = plan(n_tok, d_out, n_blocks, has_w != 0);
     const int64_t hd = d_out / n_blocks;
     Counter c;
-    if (has_w) c.carve<bf16_t>(size_t(d_out) * size_t(d_in));
+    if (has_w) c.carve<bf16_t>(size_t(np) * size_t(d_out) * size_t(d_in));
     c.carve<bf16_t>(size_t(d_out) * size_t(p.ldy));
     if (has_w) c.carve<bf16_t>(size_t(d_out) * size_t(p.ldy));
     c.carve<float>(size_t(p.nsplit - 1) * size_t(n_blocks) * size_t(hd) * size_t(hd) + 1);
@@ -1004,16 +1058,24 @@ size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out,
         c.carve<float>(size_t(LOSQ_SEG) * size_t(d_out));
     }
     // the generic path's buffer, used when the call's pointers are not aligned
-    c.carve<float>(size_t(d_out) * size_t(std::min<int64_t>(4096, n_tok)));
+    if (np == 1) c.carve<float>(size_t(d_out) * size_t(std::min<int64_t>(4096, n_tok)));
     return c.off;
 }
 
+size_t cov_mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks) {
+    return mfma_workspace(n_tok, d_in, has_w, d_out, n_blocks, 1);
+}
+
+size_t cov_range_workspace(int64_t n_tok, int64_t d) { return mfma_workspace(n_tok, d, 1, d, 1, 3); }
+
 lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
-    const MfmaPlan p = plan(a.n_tok, a.d_out, a.n_blocks, a.W != nullptr);
+    const bool rng = a.L != nullptr;  // range-projected: A = L^T in three pieces
+    const bool has_w = a.W != nullptr || rng;
+    const int np = rng ? 3 : 1;
+    const MfmaPlan p = plan(a.n_tok, a.d_out, a.n_blocks, has_w);
     const int64_t hd = a.d_out / a.n_blocks;
-    const bool has_w = a.W != nullptr;
     Carver cv(ws, ws_bytes);
-    bf16_t *Wt = has_w ? cv.carve<bf16_t>(size_t(a.d_out) * size_t(a.d_in)) : nullptr;
+    bf16_t *Wt = has_w ? cv.carve<bf16_t>(size_t(np) * size_t(a.d_out) * size_t(a.d_in)) : nullptr;
     bf16_t *Yhi = cv.carve<bf16_t>(size_t(a.d_out) * size_t(p.ldy));
     bf16_t *Ylo = has_w ? cv.carve<bf16_t>(size_t(a.d_out) * size_t(p.ldy)) : nullptr;
     const size_t pn = size_t(p.nsplit - 1) * size_t(a.n_blocks) * size_t(hd) * size_t(hd);
@@ -1024,16 +1086,23 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
     if (!P || !Yhi || (has_w && (!Wt || !Ylo || !part || !ex || !lpart)))
         return fail(LRC_ERR_WORKSPACE, "covariance workspace too small");
     const bf16_t *X = static_cast<const bf16_t *>(a.X);
-    if (has_w) {
+    if (rng) {
+        dim3 g(cdiv(a.d_in, 64), cdiv(a.d_in, 64));
+        hipLaunchKernelGGL(k_range_pieces, g, dim3(256), 0, s, a.L, a.ldl, a.d_in, Wt);
+        LRC_LAUNCH_CHECK("k_range_pieces");
+    } else if (has_w) {
         dim3 g(cdiv(a.d_out, 64), cdiv(a.d_in, 64));
         hipLaunchKernelGGL(k_transpose_bf16, g, dim3(256), 0, s, static_cast<const bf16_t *>(a.W), a.ldw, a.d_in,
                            a.d_out, Wt, a.d_in);
         LRC_LAUNCH_CHECK("k_transpose_bf16");
-        // the row exponents of the fp16 split, from all tokens of the call
+    }
+    if (has_w) {
+        // the row exponents of the fp16 split, from all tokens of the call (with pieces the row norm
+        // of hi, mid and lo together, within 2^-8 of that of L's column)
         hipLaunchKernelGGL(k_xnorm_partial, dim3(XNORM_BLOCKS), dim3(256), 0, s, X, a.ldx, a.n_tok, a.d_in, part);
         LRC_LAUNCH_CHECK("k_xnorm_partial");
         hipLaunchKernelGGL(k_split_exp, dim3(unsigned(cdiv(a.d_out, 4))), dim3(256), 0, s, part, XNORM_BLOCKS, Wt,
-                           a.d_in, a.d_out, ex);
+                           np * a.d_in, a.d_out, ex);
         LRC_LAUNCH_CHECK("k_split_exp");
     }
     if (pn) {
@@ -1043,7 +1112,14 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
     for (int64_t t0 = 0; t0 < a.n_tok; t0 += p.tcmax) {
         const int64_t tc = std::min(p.tcmax, a.n_tok - t0);
         const int64_t ktot = (tc + MK - 1) / MK * MK;
-        if (has_w) {
+        if (rng) {
+            dim3 g(unsigned(cdiv(a.d_out, G_BM)) * unsigned(cdiv(tc, G_BM)));
+            // algorithmic flops of the triangular product X L: d (d + 1) per token
+            const double fl = double(tc) * double(a.d_in) * double(a.d_in + 1);
+            LRC_TIMED_LAUNCH("k_cov_gemm_l", fl, (k_cov_gemm_y<G_BM, false, 3>), g, dim3(G_THREADS), 0, s, Wt, a.d_in,
+                             a.d_out, X + t0 * a.ldx, a.ldx, tc, ex, Yhi, Ylo);
+            LRC_LAUNCH_CHECK("k_cov_gemm_l");
+        } else if (has_w) {
             dim3 g(unsigned(cdiv(a.d_out, G_BM)) * unsigned(cdiv(tc, G_BM)));
             const double fl = 2.0 * double(tc) * double(a.d_in) * double(a.d_out);
             // d_in a multiple of the k step: no partial last step, no k check in the loads

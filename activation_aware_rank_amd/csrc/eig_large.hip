@@ -1788,11 +1788,12 @@ __global__ void k_range_finish(const double *__restrict__ lamB, int64_t r, int64
 // kappa(W) from below; the basis Q^T = L^{-1} W loses orthogonality like kappa(W)^2 times the
 // fp64 unit roundoff.  A ratio above 1e5 (or a non-finite diagonal) marks the basis as unusable
 // (chol_info 3), as a failed Cholesky does.  One workgroup, fixed-order reduction.
-__global__ void __launch_bounds__(256) k_range_check(const double *__restrict__ L, int64_t r, int32_t *chol_info) {
+__global__ void __launch_bounds__(256) k_range_check(const double *__restrict__ L, int64_t r, int64_t ldl,
+                                                     int32_t *chol_info) {
     __shared__ double smin[256], smax[256];
     double mn = DBL_MAX, mx = 0.0;
     for (int64_t i = threadIdx.x; i < r; i += 256) {
-        const double v = L[i * r + i];
+        const double v = L[i * ldl + i];
         mn = fmin(mn, isfinite(v) ? fabs(v) : 0.0);
         mx = fmax(mx, isfinite(v) ? fabs(v) : DBL_MAX);
     }
@@ -1817,32 +1818,50 @@ struct RangeWs {
 };
 
 // The decomposition's own arrays come first, at the offsets a member without a basis of order r has,
-// so that members of both kinds can be tridiagonalised in lockstep.
+// so that members of both kinds can be tridiagonalised in lockstep.  A projected member (its matrix
+// is B = Q^T C Q already) needs neither the fp64 copy of C nor B.
 template <class C_, class T>
-static void range_layout(C_ &cv, RangeWs &rw, LargeWs<T> &w, int64_t n, int64_t r, int64_t nv) {
+static void range_layout(C_ &cv, RangeWs &rw, LargeWs<T> &w, int64_t n, int64_t r, int64_t nv, bool proj) {
     layout(cv, w, r, nv, false);
     rw.Qt = cv.template carve<double>(size_t(r) * size_t(n));
-    rw.C64 = cv.template carve<double>(size_t(n) * size_t(n));
+    rw.C64 = proj ? nullptr : cv.template carve<double>(size_t(n) * size_t(n));
     rw.T = cv.template carve<double>(size_t(r) * size_t(n));  // later the n x n_vec vectors Q Z
     rw.G = cv.template carve<double>(size_t(r) * size_t(r));
     rw.lamB = cv.template carve<double>(size_t(r));
     rw.chol = cv.template carve<char>(cholesky_workspace(r));
     rw.trsm = cv.template carve<char>(trsm_workspace(0, r, n));
-    rw.B = cv.template carve<float>(size_t(r) * size_t(r));
+    rw.B = proj ? nullptr : cv.template carve<float>(size_t(r) * size_t(r));
     rw.iw = cv.template carve<int32_t>(2);
 }
 
 template <class T>
-static size_t range_ws(int64_t n, int64_t r, int64_t nv) {
+static size_t range_ws(int64_t n, int64_t r, int64_t nv, bool proj) {
     CountCarver cc;
     RangeWs rw;
     LargeWs<T> w;
-    range_layout(cc, rw, w, n, r, nv);
+    range_layout(cc, rw, w, n, r, nv, proj);
     return cc.c.off;
 }
 
 // the range path applies when 128 < d_in < n and n_vec <= d_in
 static bool use_range(const EighArgs &a) { return a.W && a.d_in > 128 && a.d_in < a.n && a.n_vec <= a.d_in; }
+
+// The factor L of W W^T = L L^T (W: r x n of dtype w_t, ldw): Wf = W in fp64 (r x n, leading dim n),
+// the lower triangle of W W^T into L (ldl), its Cholesky factorisation in place, and the check of
+// L's diagonal; info 3 when W W^T is not positive definite or the diagonal spans more than 1e5.
+// Used by the range path of the eigendecomposition and by lrc_range_factor, with the same kernels,
+// so both give the same L bit for bit.
+lrc_status range_factor_enqueue(const void *W, lrc_dtype w_t, int64_t r, int64_t n, int64_t ldw, double *Wf,
+                                double *L, int64_t ldl, void *chol_ws, int32_t *info, hipStream_t s) {
+    lrc_status st = to_f64_run(W, w_t, r, n, ldw, 1.0, Wf, n, s);
+    if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, Wf, n, Wf, n, L, ldl, 1, nullptr, s);  // W W^T, lower
+    if (st == LRC_OK) st = cholesky_run(L, r, ldl, chol_ws, cholesky_workspace(r), info, s);
+    if (st == LRC_OK) {
+        hipLaunchKernelGGL(k_range_check, dim3(1), dim3(256), 0, s, L, r, ldl, info);
+        LRC_LAUNCH_CHECK("k_range_check");
+    }
+    return st;
+}
 
 // Batch members are independent: up to EIG_LANES of them run at once, each on a helper stream
 // of its own with its own workspace, so the per-column launch chains of several matrices
@@ -1920,8 +1939,9 @@ static MultiPlan multi_plan(const EighArgs *g, int count, lrc_dtype prec) {
         } else {
             p.members += g[i].batch;
             if (use_range(g[i])) {
-                per_range = std::max(per_range, prec == LRC_F64 ? range_ws<double>(g[i].n, g[i].d_in, g[i].n_vec)
-                                                                : range_ws<float>(g[i].n, g[i].d_in, g[i].n_vec));
+                const bool pj = g[i].projected != 0;
+                per_range = std::max(per_range, prec == LRC_F64 ? range_ws<double>(g[i].n, g[i].d_in, g[i].n_vec, pj)
+                                                                : range_ws<float>(g[i].n, g[i].d_in, g[i].n_vec, pj));
             } else {
                 p.maxn = std::max(p.maxn, g[i].n);
                 p.maxnv = std::max(p.maxnv, g[i].n_vec);
@@ -1958,6 +1978,7 @@ struct EigMember {
     const void *W;  // range basis (W d_in x n), or nullptr
     lrc_dtype w_t;
     int64_t d_in, ldw;
+    bool proj;  // C holds B = Q^T C Q (d_in x d_in, ldc) instead of C
 };
 
 // One member's decomposition: its layout on a workspace region and its job; for a member with a
@@ -1996,22 +2017,18 @@ static lrc_status member_begin(MemberRun<T> &R, const MultiPlan &p, char *lws, h
     }
     const int64_t n = m.n, r = m.d_in, nv = m.nv;
     RangeWs &rw = R.rw;
-    range_layout(cv, rw, R.w, n, r, nv);
+    range_layout(cv, rw, R.w, n, r, nv, m.proj);
     if (!R.w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
-    lrc_status st = to_f64_run(m.W, m.w_t, r, n, m.ldw, 1.0, rw.Qt, n, s);
-    if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, rw.Qt, n, rw.Qt, n, rw.G, r, 1, nullptr, s);  // W W^T, lower
-    if (st == LRC_OK) st = cholesky_run(rw.G, r, r, rw.chol, cholesky_workspace(r), rw.iw, s);
-    if (st == LRC_OK) {
-        hipLaunchKernelGGL(k_range_check, dim3(1), dim3(256), 0, s, rw.G, r, rw.iw);
-        LRC_LAUNCH_CHECK("k_range_check");
-    }
+    lrc_status st = range_factor_enqueue(m.W, m.w_t, r, n, m.ldw, rw.Qt, rw.G, r, rw.chol, rw.iw, s);
     if (st == LRC_OK) st = trsm_run(0, 0, r, n, rw.G, r, rw.Qt, n, rw.trsm, s);  // Q^T = L^{-1} W
-    if (st == LRC_OK) st = sym_to_f64_run(m.C, n, m.ldc, 1.0, rw.C64, n, s);
-    if (st == LRC_OK) st = dgemm_run(0, 0, r, n, n, rw.Qt, n, rw.C64, n, rw.T, n, 0, nullptr, s);  // Q^T C
-    if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, rw.T, n, rw.Qt, n, nullptr, r, 2, rw.B, s);  // B, upper
+    if (!m.proj) {
+        if (st == LRC_OK) st = sym_to_f64_run(m.C, n, m.ldc, 1.0, rw.C64, n, s);
+        if (st == LRC_OK) st = dgemm_run(0, 0, r, n, n, rw.Qt, n, rw.C64, n, rw.T, n, 0, nullptr, s);  // Q^T C
+        if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, rw.T, n, rw.Qt, n, nullptr, r, 2, rw.B, s);  // B, upper
+    }
     if (st != LRC_OK) return st;
-    j.C = rw.B;
-    j.ldc = r;
+    j.C = m.proj ? m.C : rw.B;
+    j.ldc = m.proj ? m.ldc : r;
     j.n = r;
     j.lambda = rw.lamB;
     j.V = nullptr;
@@ -2272,7 +2289,7 @@ lrc_status eigh_multi_run(const EighArgs *g, int count, lrc_dtype prec, void *ws
             mem.push_back(EigMember{a.C + b * a.stride_c, a.ldc, a.n, a.lambda + b * a.n,
                                     a.V ? a.V + b * a.stride_v : nullptr, a.ldv, a.n_vec, a.info + b,
                                     rng ? static_cast<const char *>(a.W) + size_t(b * a.stride_w) * esz : nullptr,
-                                    a.w_t, a.d_in, a.ldw});
+                                    a.w_t, a.d_in, a.ldw, rng && a.projected != 0});
     }
     char *lw = static_cast<char *>(ws) + p.jac;
     return prec == LRC_F64 ? large_sched<double>(mem, p, lw, s) : large_sched<float>(mem, p, lw, s);

@@ -106,7 +106,12 @@ struct CovArgs {
     float *C;
     int64_t ldc;
     int32_t *info;
+    // range-projected covariance (lrc_cov_accumulate_range): W is NULL and C += (X L)^T (X L) with
+    // L (d_in x d_in, fp64, lower triangle read, leading dim ldl); d_out == d_in
+    const double *L = nullptr;
+    int64_t ldl = 0;
 };
+size_t cov_range_workspace(int64_t n_tok, int64_t d);
 size_t cov_workspace(lrc_dtype x_t, int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks);
 lrc_status cov_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
 
@@ -122,7 +127,11 @@ struct EighArgs {
     const void *W = nullptr;
     lrc_dtype w_t = LRC_BF16;
     int64_t d_in = 0, ldw = 0, stride_w = 0;
+    // C holds B = Q^T C Q (d_in x d_in), the covariance of lrc_cov_accumulate_range
+    int32_t projected = 0;
 };
+lrc_status range_factor_enqueue(const void *W, lrc_dtype w_t, int64_t r, int64_t n, int64_t ldw, double *Wf,
+                                double *L, int64_t ldl, void *chol_ws, int32_t *info, hipStream_t s);
 size_t eigh_workspace(int64_t n, int64_t batch, int64_t n_vec, lrc_dtype prec);
 lrc_status eigh_run(const EighArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
 // several groups in one call (prec overrides each group's own)

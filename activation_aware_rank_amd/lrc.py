@@ -72,6 +72,10 @@ _cfsh = _sig("lrc_component_fisher", _int, _vp, _vp, _int, _i64, _i64, _i64, _i6
              _i64, _vp, _i64, _vp, _sz, _vp)
 _acomp_ws = _sig("lrc_allocate_components_workspace", _sz, _i32, _i64)
 _acomp = _sig("lrc_allocate_components", _int, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp, _vp)
+_rfac_ws = _sig("lrc_range_factor_workspace", _sz, _i64, _i64)
+_rfac = _sig("lrc_range_factor", _int, _vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _sz, _vp, _vp)
+_covr_ws = _sig("lrc_cov_accumulate_range_workspace", _sz, _i64, _i64)
+_covr = _sig("lrc_cov_accumulate_range", _int, _vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp, _vp)
 _tim_en = _sig("lrc_timing_enable", _int, _int)
 _tim_st = _sig("lrc_timing_set_stride", _int, ctypes.c_char_p, _int)
 _tim_rd = _sig("lrc_timing_read", _int, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
@@ -87,7 +91,8 @@ EXPORTED = ("lrc_abi_version", "lrc_status_string", "lrc_last_error", "lrc_cov_a
             "lrc_cov_from_input_workspace", "lrc_cov_from_input", "lrc_allocate_proportional",
             "lrc_allocate_swift", "lrc_component_fisher_workspace", "lrc_component_fisher",
             "lrc_allocate_components_workspace", "lrc_allocate_components",
-            "lrc_timing_enable", "lrc_timing_set_stride", "lrc_timing_read")
+            "lrc_range_factor_workspace", "lrc_range_factor", "lrc_cov_accumulate_range_workspace",
+            "lrc_cov_accumulate_range", "lrc_timing_enable", "lrc_timing_set_stride", "lrc_timing_read")
 
 
 class LrcError(RuntimeError):
@@ -202,20 +207,26 @@ class _EighGroup(ctypes.Structure):
     """struct lrc_eigh_group of include/lrc.h."""
     _fields_ = [("C", _vp), ("n", _i64), ("ldc", _i64), ("batch", _i64), ("stride_c", _i64), ("lambda_", _vp),
                 ("V", _vp), ("ldv", _i64), ("n_vec", _i64), ("stride_v", _i64), ("info", _vp),
-                ("W", _vp), ("w_t", _int), ("d_in", _i64), ("ldw", _i64), ("stride_w", _i64)]
+                ("W", _vp), ("w_t", _int), ("d_in", _i64), ("ldw", _i64), ("stride_w", _i64),
+                ("projected", _i32)]
 
 
 _eigh_mws = _sig("lrc_eigh_multi_workspace", _sz, ctypes.POINTER(_EighGroup), _i32, _int)
 _eigh_m = _sig("lrc_eigh_multi", _int, ctypes.POINTER(_EighGroup), _i32, _int, _vp, _sz, _vp)
 
 
-def _eigh_args(C, n_vec, lam, V, info, W=None):
+def _eigh_args(C, n_vec, lam, V, info, W=None, projected=False):
     """Marshals one lrc_eigh call (W: the optional range basis of lrc_eigh_multi, d_in x n or
-    batch x d_in x n): (struct, squeeze flag, lam, V, info)."""
+    batch x d_in x n; projected: C is B = Q^T C Q, d_in x d_in): (struct, squeeze flag, lam, V,
+    info)."""
     ldc = _rows(C, "C")
     squeeze = C.dim() == 2
     Cb = C.unsqueeze(0) if squeeze else C
     batch, n = Cb.shape[0], Cb.shape[1]
+    if projected:
+        if W is None:
+            raise ValueError("a projected group needs its range basis W")
+        n = W.shape[-1]
     dev = C.device
     if lam is None:
         lam = torch.empty(batch, n, dtype=torch.float64, device=dev)
@@ -228,6 +239,7 @@ def _eigh_args(C, n_vec, lam, V, info, W=None):
     if W is not None:
         g.W, g.w_t, g.d_in, g.ldw = _ptr(W), _dt(W), W.shape[-2], _rows(W, "W")
         g.stride_w = W.stride(0) if W.dim() == 3 else 0
+        g.projected = int(bool(projected))
     return g, squeeze, lam, V, info
 
 
@@ -249,29 +261,31 @@ def lrc_eigh(C: torch.Tensor, n_vec: int, prec: int = LRC_F32, lam=None, V=None,
 
 
 def lrc_eigh_multi_workspace(groups, prec: int = LRC_F32) -> int:
-    """groups: sequence of (n, batch, n_vec) or (n, batch, n_vec, d_in) for a group with a range basis
-    of d_in rows (only its presence and d_in matter for the size)."""
+    """groups: sequence of (n, batch, n_vec), (n, batch, n_vec, d_in) for a group with a range basis
+    of d_in rows (only its presence and d_in matter for the size) or (n, batch, n_vec, d_in, projected)."""
     gs = []
     for grp in groups:
         n, b, nv = grp[:3]
         g = _EighGroup(None, n, n, b, 0, None, None, nv, nv, 0, None)
         if len(grp) > 3 and grp[3]:
             g.W, g.d_in, g.ldw = 1, grp[3], n  # any non-NULL pointer: the query reads no memory
+            g.projected = int(bool(grp[4])) if len(grp) > 4 else 0
         gs.append(g)
     arr = (_EighGroup * len(gs))(*gs)
     return _eigh_mws(arr, len(gs), prec)
 
 
 def lrc_eigh_multi(groups, prec: int = LRC_F32, ws=None, stream=None):
-    """Several lrc_eigh calls in one.  groups: sequence of (C, n_vec), (C, n_vec, lam, V, info) or
-    (C, n_vec, lam, V, info, W) with the meaning of lrc_eigh's arguments; W is the optional range
-    basis (d_in x n, or batch x d_in x n: C = (X W)^T (X W)).  Returns a list of (lambda, V, info)
-    per group."""
+    """Several lrc_eigh calls in one.  groups: sequence of (C, n_vec), (C, n_vec, lam, V, info),
+    (C, n_vec, lam, V, info, W) or (C, n_vec, lam, V, info, W, projected) with the meaning of
+    lrc_eigh's arguments; W is the optional range basis (d_in x n, or batch x d_in x n: C = (X W)^T
+    (X W)); projected: C is B = Q^T C Q (d_in x d_in) from lrc_cov_accumulate_range.  Returns a list
+    of (lambda, V, info) per group."""
     parts = []
     for grp in groups:
         C, n_vec = grp[0], grp[1]
-        lam, V, info, W = (tuple(grp[2:6]) + (None, None, None, None))[:4]
-        parts.append(_eigh_args(C, n_vec, lam, V, info, W))
+        lam, V, info, W, pj = (tuple(grp[2:7]) + (None, None, None, None, False))[:5]
+        parts.append(_eigh_args(C, n_vec, lam, V, info, W, bool(pj)))
     if not parts:
         raise ValueError("lrc_eigh_multi needs at least one group")
     arr = (_EighGroup * len(parts))(*[p[0] for p in parts])
@@ -279,6 +293,45 @@ def lrc_eigh_multi(groups, prec: int = LRC_F32, ws=None, stream=None):
     w, wn = _workspace(nbytes, groups[0][0].device, ws)
     _check(_eigh_m(arr, len(parts), prec, _ptr(w), wn, _stream(stream)))
     return [_eigh_out(*p[1:]) for p in parts]
+
+
+def lrc_range_factor_workspace(d_in: int, n: int) -> int:
+    return _rfac_ws(d_in, n)
+
+
+def lrc_range_factor(W: torch.Tensor, L=None, info=None, ws=None, stream=None):
+    """L (d_in, d_in) fp64 with W W^T = L L^T (lower triangle written) for W (d_in, n), n >= d_in.
+    Returns (L, info)."""
+    ldw = _rows(W, "W")
+    d_in, n = W.shape
+    if L is None:
+        L = torch.zeros(d_in, d_in, dtype=torch.float64, device=W.device)
+    ldl = _f64_matrix(L, "L")
+    w, wn = _workspace(_rfac_ws(d_in, n), W.device, ws)
+    info = _info(info, 1, W.device)
+    _check(_rfac(_ptr(W), _dt(W), d_in, n, ldw, _ptr(L), ldl, _ptr(w), wn, _ptr(info), _stream(stream)))
+    return L, info
+
+
+def lrc_cov_accumulate_range_workspace(n_tok: int, d_in: int) -> int:
+    return _covr_ws(n_tok, d_in)
+
+
+def lrc_cov_accumulate_range(X: torch.Tensor, L: torch.Tensor, B: torch.Tensor, info=None, ws=None,
+                             stream=None) -> torch.Tensor:
+    """B[upper] += (X L)^T (X L): X (n_tok, d_in) bf16, L (d_in, d_in) fp64 from lrc_range_factor,
+    B (d_in, d_in) fp32.  Returns the int32 info tensor."""
+    ldx = _rows(X, "X")
+    n_tok, d_in = X.shape
+    ldl = _f64_matrix(L, "L")
+    ldb = _rows(B, "B")
+    if B.dtype != torch.float32:
+        raise TypeError("B must be float32")
+    w, wn = _workspace(_covr_ws(n_tok, d_in), X.device, ws)
+    info = _info(info, 1, X.device)
+    _check(_covr(_ptr(X), _dt(X), n_tok, d_in, ldx, _ptr(L), ldl, _ptr(B), ldb, _ptr(w), wn, _ptr(info),
+                 _stream(stream)))
+    return info
 
 
 def lrc_error_curve(lam: torch.Tensor, eps=None, stream=None) -> torch.Tensor:

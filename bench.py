@@ -297,10 +297,12 @@ def per_head_leg(torch, lrc, n_tok, seed, dev, d_model=4096, hd=128, k=32, runs=
             "stage_ms": {"covariance": round(cov, 3), "eigh_and_error_curve": round(eig, 3), "factors": round(fac, 3)}}
 
 
-def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=11008, rho=0.8, sets=3):
+def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=11008, rho=0.8, sets=3,
+              cov_range=True):
     """The 32-layer stack end to end (FLRC page, method 1; LASER page, method 2): for every layer its
-    own n_tok calibration tokens, the 7 covariances, one call decomposing all 7 (gate/up through a basis
-    of range(W^T)) with k_cap = floor(d_in d_out / (d_in + d_out)) vectors each, the error curves; then
+    own n_tok calibration tokens, the 7 covariances (cov_range: gate/up's in the coordinates of
+    range(W^T), B = (X L)^T (X L) with W W^T = L L^T), one call decomposing all 7 (gate/up through a
+    basis of range(W^T)) with k_cap = floor(d_in d_out / (d_in + d_out)) vectors each, the error curves; then
     the Fisher scores of all 224 matrices, the greedy allocation of rho of the parameters from the real
     eigenvalues, and the factors of every matrix at its allocated rank.  One timed pass (inputs drawn
     before the clock starts, except each layer's calibration tokens, which are drawn into the same
@@ -327,8 +329,11 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
     # host thread of their own) overlap the next layers' covariances on the main stream; a set is
     # reused `sets` layers later, after its decompositions and copies are done
     NS = max(1, sets)
-    gC = [{gk: torch.empty(len(ms), gk[0], gk[0], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
+    proj = {gk: cov_range and sh[ms[0]][0] < gk[0] for gk, ms in groups.items()}  # B = (X L)^T (X L)
+    gd = {gk: sh[ms[0]][0] if proj[gk] else gk[0] for gk, ms in groups.items()}  # order of the stored matrices
+    gC = [{gk: torch.empty(len(ms), gd[gk], gd[gk], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
           for _ in range(NS)]
+    Lf = {m: torch.zeros(sh[m][0], sh[m][0], dtype=torch.float64, device=dev) for m in MATS if proj[where[m][0]]}
     ginfo_g = [{gk: torch.zeros(len(ms), dtype=torch.int32, device=dev) for gk, ms in groups.items()} for _ in range(NS)]
     cinfo = torch.zeros(1, dtype=torch.int32, device=dev)
     bad = [torch.zeros(1, dtype=torch.int64, device=dev) for _ in range(NS + 1)]  # per set, and the covariances'
@@ -338,11 +343,14 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
           for _ in range(NS)]
     glam = [{gk: torch.empty(len(ms), gk[0], dtype=torch.float64, device=dev) for gk, ms in groups.items()}
             for _ in range(NS)]
-    ws_cov = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, n_tok, di, True, do, 1)
-                             for di, do in sh.values()), dtype=torch.uint8, device=dev)
+    ws_cov = torch.empty(max([lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, n_tok, di, True, do, 1)
+                              for di, do in sh.values()] +
+                             [lrc.lrc_cov_accumulate_range_workspace(n_tok, sh[m][0]) for m in Lf]),
+                         dtype=torch.uint8, device=dev)
+    ws_rf = torch.empty(max([lrc.lrc_range_factor_workspace(*sh[m]) for m in Lf] + [1]), dtype=torch.uint8, device=dev)
     ws_eig = [torch.empty(lrc.lrc_eigh_multi_workspace(
-        [(gk[0], len(ms), gk[1], sh[ms[0]][0] if sh[ms[0]][0] < gk[0] else 0) for gk, ms in groups.items()], prec),
-        dtype=torch.uint8, device=dev) for _ in range(NS)]
+        [(gk[0], len(ms), gk[1], sh[ms[0]][0] if sh[ms[0]][0] < gk[0] else 0, proj[gk]) for gk, ms in groups.items()],
+        prec), dtype=torch.uint8, device=dev) for _ in range(NS)]
     gW = [{gk: torch.empty(len(ms), sh[ms[0]][0], gk[0], dtype=torch.bfloat16, device=dev)
            for gk, ms in groups.items() if sh[ms[0]][0] < gk[0]} for _ in range(NS)]
     side = [torch.cuda.Stream(device=dev) for _ in range(NS)]
@@ -369,8 +377,8 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
         with torch.cuda.stream(sd):
             sd.wait_event(ready)
             e0 = ev(sd)
-            lrc.lrc_eigh_multi([(gC[si][gk], gk[1], glam[si][gk], gV[si][gk], ginfo_g[si][gk], gW[si].get(gk))
-                                for gk in groups], prec=prec, ws=ws_eig[si], stream=sd)
+            lrc.lrc_eigh_multi([(gC[si][gk], gk[1], glam[si][gk], gV[si][gk], ginfo_g[si][gk], gW[si].get(gk),
+                                 proj[gk]) for gk in groups], prec=prec, ws=ws_eig[si], stream=sd)
             for gk, ms in groups.items():
                 bad[si] += ginfo_g[si][gk].abs().sum()
                 for j, m in enumerate(ms):
@@ -398,7 +406,12 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
             gk, j = where[m]
             C = gC[si][gk][j]
             C.zero_()
-            lrc.lrc_cov_accumulate(Xd if m == "down_proj" else X, Ws[layer][m], C, info=cinfo, ws=ws_cov)
+            if m in Lf:
+                lrc.lrc_range_factor(Ws[layer][m], L=Lf[m], info=cinfo, ws=ws_rf)
+                bad[NS] += cinfo
+                lrc.lrc_cov_accumulate_range(X, Lf[m], C, info=cinfo, ws=ws_cov)
+            else:
+                lrc.lrc_cov_accumulate(Xd if m == "down_proj" else X, Ws[layer][m], C, info=cinfo, ws=ws_cov)
             bad[NS] += cinfo
         for gk, ms in groups.items():
             if gk in gW[si]:
@@ -441,9 +454,10 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
     assert int(sum(b.item() for b in bad)) == 0, "stack: device info flags set"
     used = sum(kk[q] * sum(sh[MATS[q % 7]]) for q in range(len(kk)))
     return {"workload": "%d-layer LLaMA-7B-shaped stack (%d matrices, %d parameters), %d calibration tokens per "
-                        "layer, eig prec %s, k_cap vectors per matrix, greedy allocation of %.0f%% of the parameters"
+                        "layer, eig prec %s, k_cap vectors per matrix, greedy allocation of %.0f%% of the parameters%s"
                         % (n_layers, n_layers * 7, n_layers * sum(di * do for di, do in sh.values()), n_tok,
-                           "f32" if prec == lrc.LRC_F32 else "f64", rho * 100),
+                           "f32" if prec == lrc.LRC_F32 else "f64", rho * 100,
+                           "; gate/up covariances in the coordinates of range(W^T)" if Lf else ""),
             "seconds": wall, "seconds_per_layer": wall / n_layers,
             "tokens_per_s": n_layers * n_tok / wall,
             "stage_s": {"covariances": marks["cov"] / 1000.0, "eigh_and_error_curves": marks["eig"] / 1000.0,
@@ -490,6 +504,10 @@ def main():
     ap.add_argument("--eig-range", choices=("on", "off"), default="on",
                     help="on: covariances of Y = X W with d_in < d_out (gate/up) are decomposed through a basis of "
                          "range(W^T) (their rank is at most d_in); off: the full decomposition of every covariance")
+    ap.add_argument("--cov-range", choices=("on", "off"), default="on",
+                    help="with --eig-range on: those covariances are accumulated in the coordinates of the basis, "
+                         "B = (X L)^T (X L) with W W^T = L L^T (d_in x d_in), and decomposed from B; off: the full "
+                         "d_out x d_out covariance is accumulated and projected by the decomposition")
     ap.add_argument("--timing-stride", type=int, default=16,
                     help="time every s-th launch of the per-column symmetric product in the timed steps")
     ap.add_argument("--layer-tokens", type=int, default=65536,
@@ -531,14 +549,8 @@ def main():
     groups = {}
     for m in MATS:
         groups.setdefault((sh[m][1], ks[m]), []).append(m)
-    gC = {g: torch.empty(len(ms), g[0], g[0], dtype=torch.float32, device=dev) for g, ms in groups.items()}
-    glam = {g: torch.empty(len(ms), g[0], dtype=torch.float64, device=dev) for g, ms in groups.items()}
-    gV = {g: torch.empty(len(ms), g[0], g[1], dtype=torch.float32, device=dev) for g, ms in groups.items()}
-    geps = {g: torch.empty(len(ms), g[0] + 1, dtype=torch.float64, device=dev) for g, ms in groups.items()}
-    ginfo = {g: torch.zeros(len(ms), dtype=torch.int32, device=dev) for g, ms in groups.items()}
-    where = {m: (g, ms.index(m)) for g, ms in groups.items() for m in ms}
-    # groups whose covariance has rank <= d_in < d_out: their weights in one stack too (the range
-    # bases of the decomposition; the covariance calls read the same storage)
+    # groups whose covariance has rank <= d_in < d_out: their weights in one stack (the range bases of
+    # the decomposition; the covariance calls read the same storage)
     gW = {}
     if a.eig_range == "on":
         for g, ms in groups.items():
@@ -546,6 +558,19 @@ def main():
                 gW[g] = torch.stack([W[m] for m in ms])
                 for i, m in enumerate(ms):
                     W[m] = gW[g][i]
+    # --cov-range on: those groups' covariances in the basis's coordinates, B = (X L)^T (X L), d_in x d_in,
+    # from the factor L of W W^T (one per matrix, formed in the step)
+    gP = set(gW) if a.cov_range == "on" else set()
+    gd = {g: (sh[ms[0]][0] if g in gP else g[0]) for g, ms in groups.items()}  # order of the stored matrices
+    gC = {g: torch.empty(len(ms), gd[g], gd[g], dtype=torch.float32, device=dev) for g, ms in groups.items()}
+    gL = {g: torch.zeros(len(groups[g]), gd[g], gd[g], dtype=torch.float64, device=dev) for g in gP}
+    glam = {g: torch.empty(len(ms), g[0], dtype=torch.float64, device=dev) for g, ms in groups.items()}
+    gV = {g: torch.empty(len(ms), g[0], g[1], dtype=torch.float32, device=dev) for g, ms in groups.items()}
+    geps = {g: torch.empty(len(ms), g[0] + 1, dtype=torch.float64, device=dev) for g, ms in groups.items()}
+    ginfo = {g: torch.zeros(len(ms), dtype=torch.int32, device=dev) for g, ms in groups.items()}
+    where = {m: (g, ms.index(m)) for g, ms in groups.items() for m in ms}
+    Lf = {m: gL[where[m][0]][where[m][1]] for m in MATS if where[m][0] in gP}
+    rinfo = torch.zeros(len(MATS), dtype=torch.int32, device=dev)
     C = {m: gC[where[m][0]][where[m][1]] for m in MATS}
     lam = {m: glam[where[m][0]][where[m][1]] for m in MATS}
     V = {m: gV[where[m][0]][where[m][1]] for m in MATS}
@@ -553,12 +578,16 @@ def main():
     A = {m: torch.empty(di, ks[m], dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
     B = {m: torch.empty(ks[m], do, dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
     info = torch.zeros(8, dtype=torch.int32, device=dev)
-    ws_cov = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, di, True, do, 1)
-                             for di, do in sh.values()), dtype=torch.uint8, device=dev)
+    ws_cov = torch.empty(max([lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, di, True, do, 1)
+                              for di, do in sh.values()] +
+                             [lrc.lrc_cov_accumulate_range_workspace(a.tokens, gd[g]) for g in gP]),
+                         dtype=torch.uint8, device=dev)
+    ws_rf = torch.empty(max([lrc.lrc_range_factor_workspace(gd[g], g[0]) for g in gP] + [1]), dtype=torch.uint8,
+                        device=dev)
     ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace(
-        [(g[0], len(ms), g[1], sh[ms[0]][0] if g in gW else 0) for g, ms in groups.items()], prec),
+        [(g[0], len(ms), g[1], sh[ms[0]][0] if g in gW else 0, g in gP) for g, ms in groups.items()], prec),
         dtype=torch.uint8, device=dev)
-    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g], gW.get(g)) for g in groups]
+    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g], gW.get(g), g in gP) for g in groups]
     gkey = "+".join("%dx%d_k%d" % (len(ms), g[0], g[1]) for g, ms in groups.items())
     # overlap: covariances group by group, largest n first; each group's eigendecompositions and
     # error curves on a side stream of its own (default priority) with a workspace of its own
@@ -576,8 +605,8 @@ def main():
         phases = [[pt] for g in g_order for pt in parts_of(g)]
     side = [torch.cuda.Stream(device=dev) for _ in phases]
     ws_eig_g = [torch.empty(lrc.lrc_eigh_multi_workspace(
-        [(g[0], hi - lo, g[1], sh[groups[g][0]][0] if g in gW else 0) for g, lo, hi in ph], prec), dtype=torch.uint8,
-        device=dev) for ph in phases] if a.overlap == "on" else []
+        [(g[0], hi - lo, g[1], sh[groups[g][0]][0] if g in gW else 0, g in gP) for g, lo, hi in ph], prec),
+        dtype=torch.uint8, device=dev) for ph in phases] if a.overlap == "on" else []
     pname = ["+".join("%dx%d_k%d" % (hi - lo, g[0], g[1]) for g, lo, hi in ph) for ph in phases]
     kcap = {m: (di * do) // (di + do) for m, (di, do) in sh.items()}
     offs_h = [0] + list(np.cumsum([kcap[m] for m in MATS]))
@@ -604,7 +633,11 @@ def main():
         xin = Xd if m == "down_proj" else X
         C[m].zero_()
         e0 = ev(stream)
-        lrc.lrc_cov_accumulate(xin, W[m], C[m], info=info[i:i + 1], ws=ws_cov)
+        if m in Lf:  # B = (X L)^T (X L) in the coordinates of range(W^T), L from W W^T = L L^T
+            lrc.lrc_range_factor(W[m], L=Lf[m], info=rinfo[i:i + 1], ws=ws_rf)
+            lrc.lrc_cov_accumulate_range(xin, Lf[m], C[m], info=info[i:i + 1], ws=ws_cov)
+        else:
+            lrc.lrc_cov_accumulate(xin, W[m], C[m], info=info[i:i + 1], ws=ws_cov)
         e1 = ev(stream)
         times.append((m + ".cov", e0, e1))
 
@@ -615,7 +648,7 @@ def main():
         sg.wait_event(ready)
         e0 = ev(sg)
         lrc.lrc_eigh_multi([(gC[g][lo:hi], g[1], glam[g][lo:hi], gV[g][lo:hi], ginfo[g][lo:hi],
-                             gW[g][lo:hi] if g in gW else None) for g, lo, hi in phases[pi]], prec=prec,
+                             gW[g][lo:hi] if g in gW else None, g in gP) for g, lo, hi in phases[pi]], prec=prec,
                            ws=ws_eig_g[pi], stream=sg)
         for g, lo, hi in phases[pi]:
             lrc.lrc_error_curve(glam[g][lo:hi], eps=geps[g][lo:hi], stream=sg)
@@ -684,7 +717,7 @@ def main():
         Hd = torch.empty(a.d_ff, a.d_ff, dtype=torch.float32, device=dev)
         ws_h = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, d, False, d, 1)
                                for d in (a.d_model, a.d_ff)), dtype=torch.uint8, device=dev)
-        ws_f = torch.empty(max(lrc.lrc_cov_from_input_workspace(di, do) for di, do in sh.values()),
+        ws_f = torch.empty(max(lrc.lrc_cov_from_input_workspace(di, gd[where[m][0]]) for m, (di, do) in sh.items()),
                            dtype=torch.uint8, device=dev)
 
         def fstep(times):
@@ -695,7 +728,9 @@ def main():
             lrc.lrc_cov_accumulate(Xd, None, Hd, info=info[1:2], ws=ws_h)
             e1 = ev(stream)
             for m in MATS:
-                lrc.lrc_cov_from_input(Hd if m == "down_proj" else H, W[m], C=C[m], ws=ws_f)
+                if m in Lf:  # B = L^T H L for the matrices decomposed from the basis's coordinates
+                    lrc.lrc_range_factor(W[m], L=Lf[m], info=rinfo[MATS.index(m):MATS.index(m) + 1], ws=ws_rf)
+                lrc.lrc_cov_from_input(Hd if m == "down_proj" else H, Lf.get(m, W[m]), C=C[m], ws=ws_f)
             e2 = ev(stream)
             lrc.lrc_eigh_multi(eig_groups, prec=prec, ws=ws_eig)
             for g in groups:
@@ -727,7 +762,8 @@ def main():
                 "cov_tokens_per_s": a.tokens / ((avg_f["input_cov"] + avg_f["cov_from_input"]) / 1000.0),
                 "note": "same block, inputs, eigendecompositions, factors, Fisher scores and allocation as the main "
                         "step; the covariances by C_m = W_m^T (X^T X) W_m (one bf16 SYRK of X and one of X_d, then "
-                        "two fp64 products per matrix) instead of the fused GEMM + split SYRK; stages in series"}
+                        "two fp64 products per matrix; %s) instead of the fused GEMM + split SYRK; stages in series"
+                        % ("for gate/up B = L^T (X^T X) L, W W^T = L L^T" if gP else "all in full")}
 
     # a plain copy of known size, outside the timed region: the reference that scales HBM byte
     # counters (FETCH_SIZE / WRITE_SIZE) of a profiled run into bytes
@@ -752,8 +788,10 @@ def main():
     lrc.lrc_timing_enable(False)
     syrk_n, syrk_ms, syrk_fl = lrc.lrc_timing_read("k_cov_syrk", reset=False)
     gemm_n, gemm_ms, gemm_fl = lrc.lrc_timing_read("k_cov_gemm_y", reset=False)
+    geml_n, geml_ms, geml_fl = lrc.lrc_timing_read("k_cov_gemm_l", reset=False)
     symv_n, symv_ms, symv_by = lrc.lrc_timing_read("k_trd_symv", reset=True)
     assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
+    assert int(rinfo.sum().item()) == 0, "range factor info flags set: %s" % rinfo.tolist()
     for g, gi in ginfo.items():
         assert int(gi.sum().item()) == 0, "eigh info flags set (n = %d): %s" % (g[0], gi.tolist())
 
@@ -829,6 +867,13 @@ def main():
                  "total_ms_per_step": gemm_ms / a.steps,
                  "per_launch": "algorithmic flops = 2 x tokens in the chunk x d_in x d_out",
                  "mfma_counters": mfma_counters("k_cov_gemm_y")}
+    geml_tf = geml_fl / (geml_ms / 1000.0) / 1e12 if geml_ms > 0 else 0.0
+    roof_geml = {"kernel": "k_cov_gemm_l", "bound": "mfma", "achieved": geml_tf, "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": geml_tf / PEAK_BF16_TFLOPS, "launches": geml_n,
+                 "avg_launch_ms": geml_ms / max(geml_n, 1), "total_ms_per_step": geml_ms / a.steps,
+                 "per_launch": "algorithmic flops = tokens in the chunk x d_in (d_in + 1) (X L, L lower triangular); "
+                               "the kernel executes 3 bf16 MFMA products (hi, mid and lo pieces of L) over the "
+                               "nonzero block columns of each block row"}
     symv_gbs = symv_by / (symv_ms / 1000.0) / 1e9 if symv_ms > 0 else 0.0
     roof_symv = {"kernel": "k_trd_symv", "bound": "hbm", "achieved": symv_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": symv_gbs / PEAK_HBM_GBS,
@@ -841,7 +886,7 @@ def main():
                  "avg_bytes_per_launch": symv_by / max(symv_n, 1),
                  "per_launch": "algorithmic bytes = upper triangle of the trailing matrix read once, "
                                "(n-c-1)(n-c)/2 x 4 bytes for column c (one launch per column)"}
-    for r in (roof_syrk, roof_gemm):
+    for r in (roof_syrk, roof_gemm, roof_geml):
         r["sampled"] = "every launch in the timed steps (start/stop events recorded by the dispatch)"
     roof_symv["sampled"] = ("every %d-th launch in the timed steps (start/stop events recorded by the dispatch)"
                             % a.timing_stride)
@@ -850,7 +895,7 @@ def main():
                             "duration includes time its workgroups wait for CUs held by the other streams' kernels, "
                             "and summed durations exceed the eigendecomposition stage's wall time")
     if a.overlap == "on":
-        for r in (roof_syrk, roof_gemm):
+        for r in (roof_syrk, roof_gemm, roof_geml):
             r["overlap"] = ("the eigendecompositions of earlier groups run on side streams during later groups' "
                             "covariances: a launch's event-timed duration includes time its workgroups wait for "
                             "CUs held by those kernels (--overlap off times the covariance alone)")
@@ -865,7 +910,9 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded, generated on the GPU)",
         "config": {"workload": "LLaMA-7B-shaped block: q/k/v/o 4096x4096, gate/up 4096x11008, down 11008x4096, "
                                "%d calibration tokens, 60%% params per matrix, eig prec %s%s"
-                               % (a.tokens, a.prec, "; gate/up (rank <= 4096) decomposed through a basis of range(W^T)"
+                               % (a.tokens, a.prec, ("; gate/up (rank <= 4096) decomposed through a basis of range(W^T)"
+                                  + ("; their covariances accumulated in its coordinates, B = (X L)^T (X L) with "
+                                     "W W^T = L L^T (the factor formed in the step)" if gP else ""))
                                   if gW else ""),
                    "tokens": a.tokens, "d_model": a.d_model, "d_ff": a.d_ff, "ranks": ks,
                    "allocated_ranks": dict(zip(MATS, k_out.cpu().tolist()))},
@@ -890,7 +937,8 @@ def main():
                          if a.overlap == "on" else "covariances, then one call for every eigendecomposition"),
         "breakdown_ms": {k: round(v, 3) for k, v in avg.items()},
         "roofline": roof,
-        "rooflines": {"k_cov_syrk": roof_syrk, "k_trd_symv": roof_symv, "k_cov_gemm_y": roof_gemm},
+        "rooflines": {"k_cov_syrk": roof_syrk, "k_trd_symv": roof_symv, "k_cov_gemm_y": roof_gemm,
+                      **({"k_cov_gemm_l": roof_geml} if geml_n else {})},
     }
     if a.factored_steps > 0:
         out["factored"] = factored_leg()
@@ -906,7 +954,7 @@ def main():
     if a.stack_layers > 0:
         torch.cuda.empty_cache()
         out["stack"] = stack_leg(torch, lrc, a.stack_layers, a.stack_tokens, a.seed, prec, dev, a.d_model, a.d_ff,
-                                 sets=a.stack_sets)
+                                 sets=a.stack_sets, cov_range=a.cov_range == "on" and a.eig_range == "on")
     if a.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(a.d_model, a.d_ff, a.cpu_sample, a.cpu_layer_tokens, a.cpu_heads_sample)
     print(json.dumps(out))

@@ -133,6 +133,38 @@ lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64
                               void *stream);
 
 /* ------------------------------------------------------------------------------------
+ * Range-projected covariance (Swift-SVD page, section 2-ga: only Y^T Y's eigenpairs enter
+ * the closed form; for a layer that widens, d_in < d_out, C = Y^T Y has rank at most d_in).
+ *
+ * lrc_range_factor: L (d_in x d_in, fp64, lower triangle written, the strict upper triangle
+ *    left as it is) with W W^T = L L^T, W: d_in x n (ldw >= n, n >= d_in) of dtype LRC_BF16,
+ *    LRC_F32 or LRC_F64, widened exactly to fp64; W W^T and its Cholesky factorisation in
+ *    fp64 (the kernels of lrc_cholesky).  info (one int32): 0; 3 when W W^T is not
+ *    positive definite or L's diagonal spans more than a factor 1e5 (W not of full row rank
+ *    or too ill-conditioned for Q = W^T L^{-T} to be orthonormal in fp64).
+ * lrc_cov_accumulate_range: B[upper] += (X L)^T (X L) over the n_tok rows of X (bf16,
+ *    n_tok x d_in, ldx >= d_in, 16-byte aligned, ldx a multiple of 8); B d_in x d_in fp32
+ *    (ldb >= d_in), the caller zeroes it before the first chunk.  With Q = W^T L^{-T}, an
+ *    orthonormal basis of range(W^T), X L = X W Q, so B = Q^T C Q for C = (X W)^T (X W):
+ *    C's covariance of Y = X W in the coordinates of the basis, C = Q B Q^T, and the
+ *    eigenpairs of C are those of B (V = Q U) plus n - d_in zeros.  lrc_eigh_multi takes B
+ *    with projected = 1.  Arithmetic: L^T is rounded to three bf16 pieces (hi, mid, lo, their
+ *    sum within about 2^-26 of L), X L is their three bf16 MFMA products with one fp32
+ *    accumulator (block rows of the triangular L^T start at their diagonal), then the
+ *    scaled fp16 hi/lo split and the three-product SYRK of lrc_cov_accumulate.
+ * info: one int32; 1 when the updated B has a non-finite diagonal entry.
+ * Errors: LRC_ERR_ARG for sizes (d_in a multiple of 32), leading dims, NULL pointers or an
+ *    unaligned X; LRC_ERR_DTYPE for x_t other than LRC_BF16; LRC_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------------------ */
+size_t lrc_range_factor_workspace(int64_t d_in, int64_t n);
+lrc_status lrc_range_factor(const void *W, lrc_dtype w_t, int64_t d_in, int64_t n, int64_t ldw, double *L,
+                            int64_t ldl, void *ws, size_t ws_bytes, int32_t *info, void *stream);
+size_t lrc_cov_accumulate_range_workspace(int64_t n_tok, int64_t d_in);
+lrc_status lrc_cov_accumulate_range(const void *X, lrc_dtype x_t, int64_t n_tok, int64_t d_in, int64_t ldx,
+                                    const double *L, int64_t ldl, float *B, int64_t ldb, void *ws,
+                                    size_t ws_bytes, int32_t *info, void *stream);
+
+/* ------------------------------------------------------------------------------------
  * Symmetric eigendecomposition (Swift-SVD page, section 2-ga: one eigendecomposition of
  * Y^T Y gives V and Sigma^2 of Y).
  *
@@ -198,6 +230,11 @@ lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64
  *    of full row rank, or so ill-conditioned that Q loses orthogonality: use the full
  *    decomposition); 6: fewer than n_vec eigenvalues of B are non-negative.  Other d_in,
  *    or n_vec > d_in: W is ignored.
+ * projected = 1 (needs W with 128 < d_in < n and n_vec <= d_in, else LRC_ERR_ARG): C points
+ *    at B itself, d_in x d_in fp32 (upper triangle read, ldc >= d_in, stride_c between
+ *    members), as lrc_cov_accumulate_range forms it from the L of lrc_range_factor; the
+ *    library forms Q from W with the same kernels (the same L bit for bit) and proceeds as
+ *    above from B.  lambda (n values) and V (n x n_vec) keep their meaning.  0: C is n x n.
  * ws: lrc_eigh_multi_workspace(groups, count, prec) bytes, 256-byte aligned (one region
  *    per concurrent member, each sized for the largest n and n_vec among the groups, or
  *    for the largest member with a range basis if that needs more).
@@ -214,6 +251,7 @@ typedef struct lrc_eigh_group {
     const void *W;      /* optional range basis, d_in x n; NULL for none */
     lrc_dtype w_t;
     int64_t d_in, ldw, stride_w;
+    int32_t projected;  /* 1: C holds B = Q^T C Q (d_in x d_in) from lrc_cov_accumulate_range */
 } lrc_eigh_group;
 size_t lrc_eigh_multi_workspace(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec);
 lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec, void *ws,

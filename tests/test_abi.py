@@ -68,6 +68,26 @@ def test_argument_errors_are_synchronous():
     # identity W with d_out != d_in
     rc = lrc._cov(fake, 0, 10, 8, 8, None, 0, 16, 0, 1, fake, 16, None, 0, fake, None)
     assert rc == 1
+    # range-projected covariance: d_in not a multiple of 32, NULL L, fp32 X, small ldb
+    rc = lrc._covr(fake, 0, 10, 48, 48, fake, 48, fake, 48, fake, 1 << 20, fake, None)
+    assert rc == 1 and "multiple of 32" in lrc.lrc_last_error()
+    rc = lrc._covr(fake, 0, 10, 64, 64, None, 64, fake, 64, fake, 1 << 20, fake, None)
+    assert rc == 1
+    rc = lrc._covr(fake, 1, 10, 64, 64, fake, 64, fake, 64, fake, 1 << 20, fake, None)
+    assert rc == 2
+    rc = lrc._covr(fake, 0, 10, 64, 64, fake, 64, fake, 32, fake, 1 << 20, fake, None)
+    assert rc == 1
+    # range factor: n < d_in
+    rc = lrc._rfac(fake, 0, 64, 32, 32, fake, 64, fake, 1 << 20, fake, None)
+    assert rc == 1
+    # a projected eigendecomposition group without its basis, or with n_vec > d_in
+    g = lrc._EighGroup(fake, 400, 200, 1, 0, fake, fake, 8, 8, 0, fake)
+    g.projected = 1
+    arr = (lrc._EighGroup * 1)(g)
+    assert lrc._eigh_m(arr, 1, 1, fake, 1 << 30, None) == 1
+    g.W, g.w_t, g.d_in, g.ldw, g.n_vec, g.ldv = fake, 0, 200, 400, 201, 201
+    arr = (lrc._EighGroup * 1)(g)
+    assert lrc._eigh_m(arr, 1, 1, fake, 1 << 30, None) == 1
     # covariance from the input covariance: NULL H, W dtype, ldh < d_in, workspace too small
     need = lrc.lrc_cov_from_input_workspace(8, 12)
     up = lambda b: (b + 255) // 256 * 256  # noqa: E731

@@ -10,9 +10,11 @@ hold at any size:
   against the oracle in full -- its fp64 covariance and cyclic Jacobi eigendecomposition give the
   eigenvalues, the error curve, the retained subspace and the direct error;
 * the gate shape at a quarter of its size (1024 -> 2752, 16384 tokens) through the basis of
-  range(W^T), as bench.py decomposes gate and up: the same comparisons with the oracle in full;
+  range(W^T), with the full covariance and with the covariance in the basis's coordinates (as
+  bench.py runs gate and up): the same comparisons with the oracle in full;
 * LLaMA-7B block at 524288 tokens (q_proj 4096 -> 4096, k = 1228; gate_proj 4096 -> 11008,
-  k = 1791, by the full decomposition and through a basis of range(W^T) as bench.py runs it),
+  k = 1791, by the full decomposition, through a basis of range(W^T), and with the covariance
+  accumulated in that basis's coordinates as bench.py runs it),
   inputs drawn on the GPU as bench.py draws them: sampled covariance entries against the oracle's
   sums over all tokens; residual and orthogonality of the retained eigenpairs; the closed form
   eps_k = trace(C) - sum_{i<=k} v_i^T C v_i; A = W V_k on sampled rows;
@@ -130,25 +132,49 @@ def test_q_proj_65536_tokens_vs_oracle(lrc):
     assert abs(direct - eps_r[k]) <= 1e-4 * eps_r[k] + 1e-6 * eps_r[0]
 
 
+_GATE_QUARTER = {}
+
+
+def _gate_quarter_oracle():
+    """Inputs of the quarter-size gate case and the oracle's eigendecomposition of their covariance
+    (computed once for both routes)."""
+    if not _GATE_QUARTER:
+        n_tok, d_in, d_out = 16384, 1024, 2752
+        X = inputs.block_activations(d_in, n_tok, layer=2)
+        W = inputs.weight(d_in, d_out, "bf16", inputs.CFG_BLOCK, 2, 4)
+        Cr = oracle.covariance(X, "bf16", W, "bf16")
+        lam_r, V_r = oracle.eigh_large(Cr)
+        _GATE_QUARTER.update(X=X, W=W, lam_r=lam_r, V_r=V_r)
+    return _GATE_QUARTER
+
+
 @pytest.mark.timeout(900)
-def test_range_basis_gate_shape_vs_oracle(lrc):
+@pytest.mark.parametrize("projected", [False, True])
+def test_range_basis_gate_shape_vs_oracle(lrc, projected):
     """The gate/up shape at a quarter of its size through the basis of range(W^T), as bench.py
     decomposes gate and up (1024 -> 2752, 16384 tokens of the block recipe, k = 447 for 60 % of the
     parameters, fp32 eig, host-drawn inputs shared by both sides), against the oracle in full: its
     fp64 covariance of the 2752 outputs and cyclic Jacobi of that 2752 x 2752 matrix give the
     eigenvalues (the trailing 1728 are zero to rounding), the error curve, the retained subspace and
-    the direct error of the GPU factors."""
+    the direct error of the GPU factors.  projected: the covariance accumulated in the basis's
+    coordinates (lrc_range_factor, lrc_cov_accumulate_range), as bench.py runs gate and up."""
     n_tok, d_in, d_out = 16384, 1024, 2752
     k = int(0.6 * d_in * d_out / (d_in + d_out))
-    _say("gate shape / 4 through the range basis: %d x %d -> %d, k = %d, full oracle comparison"
-         % (n_tok, d_in, d_out, k))
-    X = inputs.block_activations(d_in, n_tok, layer=2)
-    W = inputs.weight(d_in, d_out, "bf16", inputs.CFG_BLOCK, 2, 4)
+    _say("gate shape / 4 through the range basis%s: %d x %d -> %d, k = %d, full oracle comparison"
+         % (", covariance in its coordinates" if projected else "", n_tok, d_in, d_out, k))
+    ref = _gate_quarter_oracle()
+    X, W = ref["X"], ref["W"]
     Xd, Wd = dev(X, "bf16"), dev(W, "bf16")
-    C = torch.zeros(d_out, d_out, dtype=torch.float32, device="cuda")
-    info = lrc.lrc_cov_accumulate(Xd, Wd, C)
+    if projected:
+        L, info = lrc.lrc_range_factor(Wd)
+        assert int(host(info)[0]) == 0
+        C = torch.zeros(d_in, d_in, dtype=torch.float32, device="cuda")
+        info = lrc.lrc_cov_accumulate_range(Xd, L, C)
+    else:
+        C = torch.zeros(d_out, d_out, dtype=torch.float32, device="cuda")
+        info = lrc.lrc_cov_accumulate(Xd, Wd, C)
     assert int(host(info)[0]) == 0
-    lam, V, info = lrc.lrc_eigh_multi([(C, k, None, None, None, Wd)], prec=1)[0]
+    lam, V, info = lrc.lrc_eigh_multi([(C, k, None, None, None, Wd, projected)], prec=1)[0]
     assert int(host(info)[0]) == 0
     eps = lrc.lrc_error_curve(lam[None])
     A = torch.empty(d_in, k, dtype=torch.float32, device="cuda")
@@ -157,8 +183,7 @@ def test_range_basis_gate_shape_vs_oracle(lrc):
     lam_h, V_h, eps_h, A_h, B_h = host(lam), host(V), host(eps)[0], host(A), host(B)
     del Xd, Wd, C, V, A, B
     assert np.count_nonzero(lam_h == 0.0) >= d_out - d_in  # exact zeros outside range(W^T)
-    Cr = oracle.covariance(X, "bf16", W, "bf16")
-    lam_r, V_r = oracle.eigh_large(Cr)
+    lam_r, V_r = ref["lam_r"], ref["V_r"]
     eps_r = oracle.error_curve(lam_r)
     el = check_lambda(lam_h, lam_r)
     e_big, e_small = check_eps(eps_h, eps_r, prec=1)
@@ -175,6 +200,62 @@ def test_range_basis_gate_shape_vs_oracle(lrc):
 @pytest.fixture(scope="module")
 def block_inputs():
     return inputs.block_gpu(524288, 4096, 11008, 20261203, torch.device("cuda"))
+
+
+def test_gate_projected_full_size(lrc, block_inputs):
+    """gate_proj at 524288 tokens as bench.py runs it: L from lrc_range_factor, B = (X L)^T (X L) by
+    lrc_cov_accumulate_range, B decomposed with projected = 1 (k = 1791, fp32 eig).  L against
+    numpy's Cholesky of W W^T (fp64); sampled entries of B against the oracle's fp64 sums over all
+    tokens with the weight L; the retained eigenpairs of C = W^T H W (H = X^T X summed in fp64 on the
+    GPU by torch) by residual, orthogonality and the closed form eps_k = trace(C) - sum v_i^T C v_i;
+    the n - d_in trailing eigenvalues exactly zero."""
+    _say("block gate_proj at 524288 tokens, k = 1791, covariance in the coordinates of range(W^T)")
+    k = 1791
+    X, W = block_inputs["X"], block_inputs["W"]["gate_proj"]
+    d_in, d_out = W.shape
+    L, info = lrc.lrc_range_factor(W)
+    assert int(host(info)[0]) == 0
+    B = torch.zeros(d_in, d_in, dtype=torch.float32, device="cuda")
+    info = lrc.lrc_cov_accumulate_range(X, L, B)
+    assert int(host(info)[0]) == 0
+    lam, V, info = lrc.lrc_eigh_multi([(B, k, None, None, None, W, True)], prec=1)[0]
+    assert int(host(info)[0]) == 0
+    eps_h = host(lrc.lrc_error_curve(lam))
+    lam_h = host(lam)
+    assert np.count_nonzero(lam_h == 0.0) >= d_out - d_in and np.all(np.diff(lam_h) <= 0)
+    f64 = torch.float64
+    W64 = W.to(f64)
+    L_np = np.linalg.cholesky(host(W64 @ W64.T))
+    L_h = np.tril(host(L))
+    errL = np.max(np.abs(L_h - L_np)) / np.max(np.abs(L_np))
+    H = torch.zeros(d_in, d_in, dtype=f64, device="cuda")
+    for t0 in range(0, X.shape[0], 65536):
+        Xc = X[t0:t0 + 65536].to(f64)
+        H += Xc.T @ Xc
+    del Xc
+    Vk = V.to(f64)
+    CV = W64.T @ (H @ (W64 @ Vk))
+    lam_d = lam.to(f64)
+    res = float(torch.linalg.vector_norm(CV - Vk * lam_d[:k], dim=0).max() / lam_d[0])
+    orth = float((Vk.T @ Vk - torch.eye(k, dtype=f64, device="cuda")).abs().max())
+    tr = float((H * (W64 @ W64.T)).sum())
+    kept = float((Vk * CV).sum())
+    cf = abs((tr - kept) - eps_h[k]) / eps_h[k]
+    r = np.random.default_rng(19)
+    ii = np.concatenate([r.integers(0, d_in, 12), np.arange(4)])
+    jj = np.concatenate([r.integers(0, d_in, 12), np.arange(4)])
+    ii, jj = np.minimum(ii, jj), np.maximum(ii, jj)
+    Xh = host(X.view(torch.int16)).view(np.uint16)
+    refB = oracle.covariance_entries(Xh, "bf16", L_np, "f64", ii, jj)
+    Bh = host(B)
+    dB = np.sqrt(np.diag(Bh).astype(np.float64)[ii] * np.diag(Bh).astype(np.float64)[jj])
+    errB = np.max(np.abs(Bh[ii, jj] - refB) / dB)
+    print("gate_proj projected: L err %.2e, sampled B entries %.2e of sqrt(B_ii B_jj), residual %.2e, "
+          "orthogonality %.2e, closed form %.2e, eps_0 vs trace %.2e"
+          % (errL, errB, res, orth, cf, abs(eps_h[0] - tr) / tr))
+    assert errL <= 1e-12 and errB <= 1e-5
+    assert res <= 1e-5 and orth <= 1e-5
+    assert cf <= 1e-4 and abs(eps_h[0] - tr) <= 1e-6 * tr
 
 
 @pytest.mark.parametrize("name,k,basis", [("q_proj", 1228, False), ("gate_proj", 1791, False),

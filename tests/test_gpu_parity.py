@@ -515,6 +515,68 @@ def test_eigh_lockstep_mixed_members(lrc, prec, same_nv):
     assert sin_theta_max(host(out[1][1]), V_r, nvs[1]) <= 1e-3
 
 
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("d_in,n,n_tok", [(320, 640, 3000), (256, 416, 1000)])
+def test_cov_range_projected_vs_oracle(lrc, prec, d_in, n, n_tok):
+    """The widening layer's covariance through its range basis without forming C: L from
+    lrc_range_factor (W W^T = L L^T), B = (X L)^T (X L) from lrc_cov_accumulate_range in two calls (a
+    ragged split of the tokens), B's eigendecomposition with projected = 1.  Against the oracle's
+    direct covariance C = (X W)^T (X W) of the same bytes and its cyclic-Jacobi eigendecomposition:
+    all n eigenvalues (the n - d_in past d_in are zero), eps_k, the retained subspace at k and the
+    sign rule.  Diagnostics: L against numpy's Cholesky of W W^T, B against (X L)^T (X L) in fp64.
+    320 spans two 256-row block tiles of the product (the second starting at its diagonal) and three
+    128-wide SYRK tiles, ragged."""
+    _say("cov range-projected %d x %d -> %d, prec %d" % (n_tok, d_in, n, prec))
+    k = 64
+    X = inputs.block_activations(d_in, n_tok)
+    W = inputs.weight(d_in, n, "bf16", inputs.CFG_BLOCK, 0, 90)
+    Xd, Wd = dev(X, "bf16"), dev(W, "bf16")
+    L, info = lrc.lrc_range_factor(Wd)
+    assert int(host(info)[0]) == 0
+    B = torch.zeros(d_in, d_in, dtype=torch.float32, device="cuda")
+    t1 = n_tok // 3 + 5
+    for a, b in ((0, t1), (t1, n_tok)):
+        i2 = lrc.lrc_cov_accumulate_range(Xd[a:b], L, B)
+        assert int(host(i2)[0]) == 0
+    X64, W64 = oracle.widen(X, "bf16"), oracle.widen(W, "bf16")
+    L_np = np.linalg.cholesky(W64 @ W64.T)
+    L_h = np.tril(host(L))
+    errL = np.max(np.abs(L_h - L_np)) / np.max(np.abs(L_np))
+    Y = X64 @ L_np
+    B_ref = Y.T @ Y
+    B_h = host(B).astype(np.float64)
+    dg = np.sqrt(np.outer(np.diag(B_ref), np.diag(B_ref)))
+    U = np.triu(np.ones((d_in, d_in), dtype=bool))
+    errB = np.max(np.abs(B_h - B_ref)[U] / dg[U])
+    assert np.all(np.tril(B_h, -1) == 0)
+    out = lrc.lrc_eigh_multi([(B, k, None, None, None, Wd, True)], prec=prec)
+    lam, V, info3 = (host(x) for x in out[0])
+    assert int(info3[0]) == 0
+    eps = host(lrc.lrc_error_curve(torch.from_numpy(lam).cuda()))
+    C = oracle.covariance(X, "bf16", W, "bf16")
+    lam_r, V_r = oracle.eigh(C)
+    e = check_lambda(lam, lam_r)
+    assert np.all(np.diff(lam) <= 0) and np.count_nonzero(lam == 0.0) >= n - d_in
+    eb, es = check_eps(eps, oracle.error_curve(lam_r), prec=prec)
+    s = sin_theta_max(V, V_r, k)
+    V64 = V.astype(np.float64)
+    orth = np.max(np.abs(V64.T @ V64 - np.eye(k)))
+    print("L err %.2e, B err %.2e (of sqrt(B_ii B_jj)), lambda err %.2e, eps err %.2e / tail %.2e, "
+          "sin theta %.2e (gap %.2e), orthogonality %.2e" % (errL, errB, e, eb, es, s, gap(lam_r, k), orth))
+    assert errL <= 1e-12 and errB <= 1e-5
+    assert s <= 1e-3 and orth <= 1e-5
+    idx = np.argmax(np.abs(V), axis=0)
+    assert np.all(V[idx, np.arange(k)] > 0)
+
+
+def test_cov_range_rank_deficient_basis(lrc):
+    """A weight whose rows are not independent: lrc_range_factor reports info 3."""
+    W = inputs.weight(160, 400, "bf16", inputs.CFG_BLOCK, 0, 91)
+    W[9] = W[4]
+    L, info = lrc.lrc_range_factor(dev(W, "bf16"))
+    assert int(host(info)[0]) == 3
+
+
 def test_eigh_range_basis_fallbacks(lrc):
     """d_in >= n, or n_vec > d_in: the basis is ignored (the full decomposition, bit for bit); a basis
     without full row rank: info 3."""
