@@ -266,7 +266,7 @@ static std::vector<EighArgs> eigh_groups(const lrc_eigh_group *g, int32_t count,
     for (int32_t i = 0; i < count; ++i)
         v.push_back(EighArgs{g[i].C, g[i].n, g[i].ldc, g[i].batch, g[i].stride_c, prec, g[i].lambda, g[i].V,
                              g[i].ldv, g[i].n_vec, g[i].stride_v, g[i].info, g[i].W, g[i].w_t, g[i].d_in,
-                             g[i].ldw, g[i].stride_w, g[i].projected});
+                             g[i].ldw, g[i].stride_w, g[i].projected, g[i].L, g[i].ldl, g[i].stride_l});
     return v;
 }
 
@@ -287,6 +287,9 @@ lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype
         if (g.projected)
             REQUIRE(g.W && g.d_in > 128 && g.d_in < g.n && g.n_vec <= g.d_in, LRC_ERR_ARG,
                     "a projected group needs its range basis W with 128 < d_in < n and n_vec <= d_in");
+        if (g.L)
+            REQUIRE(g.W && g.ldl >= g.d_in && (g.batch == 1 || g.stride_l >= g.d_in * g.ldl - (g.ldl - g.d_in)),
+                    LRC_ERR_ARG, "L needs the range basis W, ldl >= d_in and stride_l between members");
         lrc_status st = check_eigh(g.C, g.n, g.ldc, g.batch, g.stride_c, g.lambda, g.V, g.ldv, g.n_vec, g.stride_v,
                                    g.info, g.projected ? g.d_in : g.n);
         if (st != LRC_OK) return st;

@@ -1519,6 +1519,10 @@ __global__ void k_set_info(int32_t *info, const int *bad) {
     if (threadIdx.x == 0) *info = *bad ? LRC_INFO_NONFINITE : LRC_INFO_OK;
 }
 
+__global__ void k_zero_i32(int32_t *p) {
+    if (threadIdx.x == 0) *p = 0;
+}
+
 // ---------------------------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------------------------
@@ -1979,6 +1983,8 @@ struct EigMember {
     lrc_dtype w_t;
     int64_t d_in, ldw;
     bool proj;  // C holds B = Q^T C Q (d_in x d_in, ldc) instead of C
+    const double *L;  // the factor of W W^T given by the caller (lower, ldl), or nullptr
+    int64_t ldl;
 };
 
 // One member's decomposition: its layout on a workspace region and its job; for a member with a
@@ -1990,6 +1996,8 @@ struct MemberRun {
     LargeWs<T> w;
     RangeWs rw{};
     EigJob<T> j;
+    const double *L = nullptr;  // the factor of W W^T in use (the caller's or rw.G)
+    int64_t ldl = 0;
 };
 
 // Lays out the region and sets up the job; a range member's basis and B are enqueued on s.
@@ -2019,9 +2027,22 @@ static lrc_status member_begin(MemberRun<T> &R, const MultiPlan &p, char *lws, h
     RangeWs &rw = R.rw;
     range_layout(cv, rw, R.w, n, r, nv, m.proj);
     if (!R.w.bad) return fail(LRC_ERR_WORKSPACE, "eigh workspace too small");
-    lrc_status st = range_factor_enqueue(m.W, m.w_t, r, n, m.ldw, rw.Qt, rw.G, r, rw.chol, rw.iw, s);
-    if (st == LRC_OK) st = trsm_run(0, 0, r, n, rw.G, r, rw.Qt, n, rw.trsm, s);  // Q^T = L^{-1} W
+    // rw.Qt first holds W in fp64; a projected member keeps it so (V = W^T (L^{-T} Z) at the end,
+    // a triangular solve on the d_in x n_vec block instead of on the d_in x n basis)
+    lrc_status st = LRC_OK;
+    if (m.L) {  // the caller's factor (from lrc_range_factor, the same kernels)
+        R.L = m.L;
+        R.ldl = m.ldl;
+        st = to_f64_run(m.W, m.w_t, r, n, m.ldw, 1.0, rw.Qt, n, s);
+        hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(64), 0, s, rw.iw);
+        LRC_LAUNCH_CHECK("k_zero_i32");
+    } else {
+        R.L = rw.G;
+        R.ldl = r;
+        st = range_factor_enqueue(m.W, m.w_t, r, n, m.ldw, rw.Qt, rw.G, r, rw.chol, rw.iw, s);
+    }
     if (!m.proj) {
+        if (st == LRC_OK) st = trsm_run(0, 0, r, n, R.L, R.ldl, rw.Qt, n, rw.trsm, s);  // Q^T = L^{-1} W
         if (st == LRC_OK) st = sym_to_f64_run(m.C, n, m.ldc, 1.0, rw.C64, n, s);
         if (st == LRC_OK) st = dgemm_run(0, 0, r, n, n, rw.Qt, n, rw.C64, n, rw.T, n, 0, nullptr, s);  // Q^T C
         if (st == LRC_OK) st = dgemm_run(0, 1, r, r, n, rw.T, n, rw.Qt, n, nullptr, r, 2, rw.B, s);  // B, upper
@@ -2047,7 +2068,13 @@ static lrc_status member_end(MemberRun<T> &R, hipStream_t s) {
     const int64_t n = m.n, r = m.d_in, nv = m.nv;
     RangeWs &rw = R.rw;
     if (nv > 0) {
-        const lrc_status st = dgemm_run(1, 0, n, nv, r, rw.Qt, n, R.w.Z, nv, rw.T, nv, 0, nullptr, s);  // Q Z
+        lrc_status st = LRC_OK;
+        if (m.proj) {  // Q Z = W^T L^{-T} Z: Z <- L^{-T} Z, then W^T Z
+            st = trsm_run(0, 1, r, nv, R.L, R.ldl, R.w.Z, nv, rw.trsm, s);
+            if (st == LRC_OK) st = dgemm_run(1, 0, n, nv, r, rw.Qt, n, R.w.Z, nv, rw.T, nv, 0, nullptr, s);
+        } else {
+            st = dgemm_run(1, 0, n, nv, r, rw.Qt, n, R.w.Z, nv, rw.T, nv, 0, nullptr, s);  // Q Z
+        }
         if (st != LRC_OK) return st;
         hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, R.w.bad);
         LRC_LAUNCH_CHECK("k_sign_out");
@@ -2289,7 +2316,8 @@ lrc_status eigh_multi_run(const EighArgs *g, int count, lrc_dtype prec, void *ws
             mem.push_back(EigMember{a.C + b * a.stride_c, a.ldc, a.n, a.lambda + b * a.n,
                                     a.V ? a.V + b * a.stride_v : nullptr, a.ldv, a.n_vec, a.info + b,
                                     rng ? static_cast<const char *>(a.W) + size_t(b * a.stride_w) * esz : nullptr,
-                                    a.w_t, a.d_in, a.ldw, rng && a.projected != 0});
+                                    a.w_t, a.d_in, a.ldw, rng && a.projected != 0,
+                                    rng && a.L ? a.L + b * a.stride_l : nullptr, a.ldl});
     }
     char *lw = static_cast<char *>(ws) + p.jac;
     return prec == LRC_F64 ? large_sched<double>(mem, p, lw, s) : large_sched<float>(mem, p, lw, s);

@@ -129,6 +129,9 @@ struct EighArgs {
     int64_t d_in = 0, ldw = 0, stride_w = 0;
     // C holds B = Q^T C Q (d_in x d_in), the covariance of lrc_cov_accumulate_range
     int32_t projected = 0;
+    // optional factor of W W^T from lrc_range_factor (lower, d_in x d_in, member b at L + b stride_l)
+    const double *L = nullptr;
+    int64_t ldl = 0, stride_l = 0;
 };
 lrc_status range_factor_enqueue(const void *W, lrc_dtype w_t, int64_t r, int64_t n, int64_t ldw, double *Wf,
                                 double *L, int64_t ldl, void *chol_ws, int32_t *info, hipStream_t s);

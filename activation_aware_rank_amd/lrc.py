@@ -208,14 +208,14 @@ class _EighGroup(ctypes.Structure):
     _fields_ = [("C", _vp), ("n", _i64), ("ldc", _i64), ("batch", _i64), ("stride_c", _i64), ("lambda_", _vp),
                 ("V", _vp), ("ldv", _i64), ("n_vec", _i64), ("stride_v", _i64), ("info", _vp),
                 ("W", _vp), ("w_t", _int), ("d_in", _i64), ("ldw", _i64), ("stride_w", _i64),
-                ("projected", _i32)]
+                ("projected", _i32), ("L", _vp), ("ldl", _i64), ("stride_l", _i64)]
 
 
 _eigh_mws = _sig("lrc_eigh_multi_workspace", _sz, ctypes.POINTER(_EighGroup), _i32, _int)
 _eigh_m = _sig("lrc_eigh_multi", _int, ctypes.POINTER(_EighGroup), _i32, _int, _vp, _sz, _vp)
 
 
-def _eigh_args(C, n_vec, lam, V, info, W=None, projected=False):
+def _eigh_args(C, n_vec, lam, V, info, W=None, projected=False, L=None):
     """Marshals one lrc_eigh call (W: the optional range basis of lrc_eigh_multi, d_in x n or
     batch x d_in x n; projected: C is B = Q^T C Q, d_in x d_in): (struct, squeeze flag, lam, V,
     info)."""
@@ -240,6 +240,9 @@ def _eigh_args(C, n_vec, lam, V, info, W=None, projected=False):
         g.W, g.w_t, g.d_in, g.ldw = _ptr(W), _dt(W), W.shape[-2], _rows(W, "W")
         g.stride_w = W.stride(0) if W.dim() == 3 else 0
         g.projected = int(bool(projected))
+        if L is not None:
+            g.L, g.ldl = _ptr(L), _f64_matrix(L, "L")
+            g.stride_l = L.stride(0) if L.dim() == 3 else 0
     return g, squeeze, lam, V, info
 
 
@@ -277,15 +280,16 @@ def lrc_eigh_multi_workspace(groups, prec: int = LRC_F32) -> int:
 
 def lrc_eigh_multi(groups, prec: int = LRC_F32, ws=None, stream=None):
     """Several lrc_eigh calls in one.  groups: sequence of (C, n_vec), (C, n_vec, lam, V, info),
-    (C, n_vec, lam, V, info, W) or (C, n_vec, lam, V, info, W, projected) with the meaning of
-    lrc_eigh's arguments; W is the optional range basis (d_in x n, or batch x d_in x n: C = (X W)^T
-    (X W)); projected: C is B = Q^T C Q (d_in x d_in) from lrc_cov_accumulate_range.  Returns a list
-    of (lambda, V, info) per group."""
+    (C, n_vec, lam, V, info, W), (C, n_vec, lam, V, info, W, projected) or (..., projected, L) with
+    the meaning of lrc_eigh's arguments; W is the optional range basis (d_in x n, or batch x d_in x
+    n: C = (X W)^T (X W)); projected: C is B = Q^T C Q (d_in x d_in) from lrc_cov_accumulate_range;
+    L: the factor of W W^T from lrc_range_factor (d_in x d_in, or batch x d_in x d_in).  Returns a
+    list of (lambda, V, info) per group."""
     parts = []
     for grp in groups:
         C, n_vec = grp[0], grp[1]
-        lam, V, info, W, pj = (tuple(grp[2:7]) + (None, None, None, None, False))[:5]
-        parts.append(_eigh_args(C, n_vec, lam, V, info, W, bool(pj)))
+        lam, V, info, W, pj, L = (tuple(grp[2:8]) + (None, None, None, None, False, None))[:6]
+        parts.append(_eigh_args(C, n_vec, lam, V, info, W, bool(pj), L))
     if not parts:
         raise ValueError("lrc_eigh_multi needs at least one group")
     arr = (_EighGroup * len(parts))(*[p[0] for p in parts])

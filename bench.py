@@ -333,7 +333,10 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
     gd = {gk: sh[ms[0]][0] if proj[gk] else gk[0] for gk, ms in groups.items()}  # order of the stored matrices
     gC = [{gk: torch.empty(len(ms), gd[gk], gd[gk], dtype=torch.float32, device=dev) for gk, ms in groups.items()}
           for _ in range(NS)]
-    Lf = {m: torch.zeros(sh[m][0], sh[m][0], dtype=torch.float64, device=dev) for m in MATS if proj[where[m][0]]}
+    # the factors of W W^T, per buffer set (a set's decompositions read them on their side stream)
+    gL = [{gk: torch.zeros(len(ms), sh[ms[0]][0], sh[ms[0]][0], dtype=torch.float64, device=dev)
+           for gk, ms in groups.items() if proj[gk]} for _ in range(NS)]
+    Lf = [{m: gL[si][where[m][0]][where[m][1]] for m in MATS if proj[where[m][0]]} for si in range(NS)]
     ginfo_g = [{gk: torch.zeros(len(ms), dtype=torch.int32, device=dev) for gk, ms in groups.items()} for _ in range(NS)]
     cinfo = torch.zeros(1, dtype=torch.int32, device=dev)
     bad = [torch.zeros(1, dtype=torch.int64, device=dev) for _ in range(NS + 1)]  # per set, and the covariances'
@@ -345,9 +348,10 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
             for _ in range(NS)]
     ws_cov = torch.empty(max([lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, n_tok, di, True, do, 1)
                               for di, do in sh.values()] +
-                             [lrc.lrc_cov_accumulate_range_workspace(n_tok, sh[m][0]) for m in Lf]),
+                             [lrc.lrc_cov_accumulate_range_workspace(n_tok, sh[m][0]) for m in Lf[0]]),
                          dtype=torch.uint8, device=dev)
-    ws_rf = torch.empty(max([lrc.lrc_range_factor_workspace(*sh[m]) for m in Lf] + [1]), dtype=torch.uint8, device=dev)
+    ws_rf = torch.empty(max([lrc.lrc_range_factor_workspace(*sh[m]) for m in Lf[0]] + [1]), dtype=torch.uint8,
+                        device=dev)
     ws_eig = [torch.empty(lrc.lrc_eigh_multi_workspace(
         [(gk[0], len(ms), gk[1], sh[ms[0]][0] if sh[ms[0]][0] < gk[0] else 0, proj[gk]) for gk, ms in groups.items()],
         prec), dtype=torch.uint8, device=dev) for _ in range(NS)]
@@ -378,7 +382,7 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
             sd.wait_event(ready)
             e0 = ev(sd)
             lrc.lrc_eigh_multi([(gC[si][gk], gk[1], glam[si][gk], gV[si][gk], ginfo_g[si][gk], gW[si].get(gk),
-                                 proj[gk]) for gk in groups], prec=prec, ws=ws_eig[si], stream=sd)
+                                 proj[gk], gL[si].get(gk)) for gk in groups], prec=prec, ws=ws_eig[si], stream=sd)
             for gk, ms in groups.items():
                 bad[si] += ginfo_g[si][gk].abs().sum()
                 for j, m in enumerate(ms):
@@ -406,10 +410,10 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
             gk, j = where[m]
             C = gC[si][gk][j]
             C.zero_()
-            if m in Lf:
-                lrc.lrc_range_factor(Ws[layer][m], L=Lf[m], info=cinfo, ws=ws_rf)
+            if m in Lf[si]:
+                lrc.lrc_range_factor(Ws[layer][m], L=Lf[si][m], info=cinfo, ws=ws_rf)
                 bad[NS] += cinfo
-                lrc.lrc_cov_accumulate_range(X, Lf[m], C, info=cinfo, ws=ws_cov)
+                lrc.lrc_cov_accumulate_range(X, Lf[si][m], C, info=cinfo, ws=ws_cov)
             else:
                 lrc.lrc_cov_accumulate(Xd if m == "down_proj" else X, Ws[layer][m], C, info=cinfo, ws=ws_cov)
             bad[NS] += cinfo
@@ -457,7 +461,7 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
                         "layer, eig prec %s, k_cap vectors per matrix, greedy allocation of %.0f%% of the parameters%s"
                         % (n_layers, n_layers * 7, n_layers * sum(di * do for di, do in sh.values()), n_tok,
                            "f32" if prec == lrc.LRC_F32 else "f64", rho * 100,
-                           "; gate/up covariances in the coordinates of range(W^T)" if Lf else ""),
+                           "; gate/up covariances in the coordinates of range(W^T)" if Lf[0] else ""),
             "seconds": wall, "seconds_per_layer": wall / n_layers,
             "tokens_per_s": n_layers * n_tok / wall,
             "stage_s": {"covariances": marks["cov"] / 1000.0, "eigh_and_error_curves": marks["eig"] / 1000.0,
@@ -495,10 +499,13 @@ def main():
                          "remaining covariances run")
     ap.add_argument("--overlap-chunk", type=int, default=0,
                     help="with --overlap on: split groups into parts of this many matrices (0: whole groups)")
-    ap.add_argument("--overlap-order", choices=("small-first", "large-first", "most-first"), default="large-first",
+    ap.add_argument("--overlap-order", choices=("small-first", "large-first", "most-first", "rank-small", "rank-large"),
+                    default="rank-small",
                     help="small-first: the groups of one output width decomposed in one call (the library "
                          "tridiagonalises matrices of one order in lockstep), narrow widths first; large-first / "
-                         "most-first: one group at a time, largest n or most matrices first")
+                         "most-first: one group at a time, largest n or most matrices first; rank-small / "
+                         "rank-large: the groups of one tridiagonal order (d_in for a projected covariance) and "
+                         "rank in one call (lockstep and batched throughout), smaller or larger rank first")
     ap.add_argument("--factored-steps", type=int, default=2,
                     help="timed steps of the variant that forms the covariances from X^T X (0: skip)")
     ap.add_argument("--eig-range", choices=("on", "off"), default="on",
@@ -582,12 +589,12 @@ def main():
                               for di, do in sh.values()] +
                              [lrc.lrc_cov_accumulate_range_workspace(a.tokens, gd[g]) for g in gP]),
                          dtype=torch.uint8, device=dev)
-    ws_rf = torch.empty(max([lrc.lrc_range_factor_workspace(gd[g], g[0]) for g in gP] + [1]), dtype=torch.uint8,
-                        device=dev)
+    ws_rf = {m: torch.empty(lrc.lrc_range_factor_workspace(*sh[m]), dtype=torch.uint8, device=dev)
+             for m in MATS if where[m][0] in gP}
     ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace(
         [(g[0], len(ms), g[1], sh[ms[0]][0] if g in gW else 0, g in gP) for g, ms in groups.items()], prec),
         dtype=torch.uint8, device=dev)
-    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g], gW.get(g), g in gP) for g in groups]
+    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g], gW.get(g), g in gP, gL.get(g)) for g in groups]
     gkey = "+".join("%dx%d_k%d" % (len(ms), g[0], g[1]) for g, ms in groups.items())
     # overlap: covariances group by group, largest n first; each group's eigendecompositions and
     # error curves on a side stream of its own (default priority) with a workspace of its own
@@ -600,6 +607,10 @@ def main():
     if a.overlap_order == "small-first":  # groups of one output width together, narrow widths first
         widths = sorted({g[0] for g in groups})
         phases = [[pt for g in groups if g[0] == wd for pt in parts_of(g)] for wd in widths]
+    elif a.overlap_order in ("rank-small", "rank-large"):  # groups of one tridiagonal order and rank together
+        keys = sorted({(gd[g], g[1]) for g in groups}, key=lambda x: (x[1], x[0]),
+                      reverse=a.overlap_order == "rank-large")
+        phases = [[pt for g in groups if (gd[g], g[1]) == kk for pt in parts_of(g)] for kk in keys]
     else:
         g_order = sorted(groups, key=lambda g: -g[0] if a.overlap_order == "large-first" else len(groups[g]) * -1)
         phases = [[pt] for g in g_order for pt in parts_of(g)]
@@ -628,13 +639,28 @@ def main():
         e.record(st)
         return e
 
+    fstream = torch.cuda.Stream(device=dev)  # the range factors, off the covariance stream
+    fready = {}
+
+    def factors(times):
+        # L of every matrix with a projected covariance, on a side stream from the step's start; the
+        # covariance stream waits for each only where it needs it (it also serves the decomposition)
+        fstream.wait_stream(stream)
+        for m in MATS:
+            if m in Lf:
+                i = MATS.index(m)
+                e0 = ev(fstream)
+                lrc.lrc_range_factor(W[m], L=Lf[m], info=rinfo[i:i + 1], ws=ws_rf[m], stream=fstream)
+                fready[m] = ev(fstream)
+                times.append((m + ".factor", e0, fready[m]))
+
     def cov(m, times):
         i = MATS.index(m)
         xin = Xd if m == "down_proj" else X
         C[m].zero_()
         e0 = ev(stream)
         if m in Lf:  # B = (X L)^T (X L) in the coordinates of range(W^T), L from W W^T = L L^T
-            lrc.lrc_range_factor(W[m], L=Lf[m], info=rinfo[i:i + 1], ws=ws_rf)
+            stream.wait_event(fready[m])
             lrc.lrc_cov_accumulate_range(xin, Lf[m], C[m], info=info[i:i + 1], ws=ws_cov)
         else:
             lrc.lrc_cov_accumulate(xin, W[m], C[m], info=info[i:i + 1], ws=ws_cov)
@@ -648,8 +674,8 @@ def main():
         sg.wait_event(ready)
         e0 = ev(sg)
         lrc.lrc_eigh_multi([(gC[g][lo:hi], g[1], glam[g][lo:hi], gV[g][lo:hi], ginfo[g][lo:hi],
-                             gW[g][lo:hi] if g in gW else None, g in gP) for g, lo, hi in phases[pi]], prec=prec,
-                           ws=ws_eig_g[pi], stream=sg)
+                             gW[g][lo:hi] if g in gW else None, g in gP, gL[g][lo:hi] if g in gP else None)
+                            for g, lo, hi in phases[pi]], prec=prec, ws=ws_eig_g[pi], stream=sg)
         for g, lo, hi in phases[pi]:
             lrc.lrc_error_curve(glam[g][lo:hi], eps=geps[g][lo:hi], stream=sg)
         e1 = ev(sg)
@@ -682,6 +708,7 @@ def main():
         times.append(("alloc", e7, e8))
 
     def step(times):
+        factors(times)
         if a.overlap == "on":
             threads = []
             for pi, ph in enumerate(phases):
@@ -729,7 +756,7 @@ def main():
             e1 = ev(stream)
             for m in MATS:
                 if m in Lf:  # B = L^T H L for the matrices decomposed from the basis's coordinates
-                    lrc.lrc_range_factor(W[m], L=Lf[m], info=rinfo[MATS.index(m):MATS.index(m) + 1], ws=ws_rf)
+                    lrc.lrc_range_factor(W[m], L=Lf[m], info=rinfo[MATS.index(m):MATS.index(m) + 1], ws=ws_rf[m])
                 lrc.lrc_cov_from_input(Hd if m == "down_proj" else H, Lf.get(m, W[m]), C=C[m], ws=ws_f)
             e2 = ev(stream)
             lrc.lrc_eigh_multi(eig_groups, prec=prec, ws=ws_eig)
@@ -899,8 +926,13 @@ def main():
             r["overlap"] = ("the eigendecompositions of earlier groups run on side streams during later groups' "
                             "covariances: a launch's event-timed duration includes time its workgroups wait for "
                             "CUs held by those kernels (--overlap off times the covariance alone)")
-    # the roofline entry is the covariance SYRK: the kernel with the largest time
-    roof = roof_syrk
+    # the roofline entry is the kernel with the largest summed launch time in the timed steps (events
+    # recorded by the dispatches; for k_trd_symv every timing_stride-th launch, scaled up)
+    cands = [roof_syrk, roof_symv, roof_gemm] + ([roof_geml] if geml_n else [])
+    roof = dict(max(cands, key=lambda r: r["total_ms_per_step"]))
+    roof["dominant_by"] = ("largest summed launch time per step among %s (%s ms)"
+                           % (", ".join(r["kernel"] for r in cands),
+                              ", ".join("%.1f" % r["total_ms_per_step"] for r in cands)))
     out = {
         "metric": "calibration tokens/s into Y^T Y; sec per 4096x4096 layer compressed (eig incl.)",
         "value": a.tokens / (step_ms / 1000.0),

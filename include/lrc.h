@@ -235,6 +235,10 @@ lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64
  *    members), as lrc_cov_accumulate_range forms it from the L of lrc_range_factor; the
  *    library forms Q from W with the same kernels (the same L bit for bit) and proceeds as
  *    above from B.  lambda (n values) and V (n x n_vec) keep their meaning.  0: C is n x n.
+ * L (optional, with W): the lower factor of W W^T = L L^T that lrc_range_factor gave (info 0),
+ *    d_in x d_in fp64, ldl >= d_in, member b at L + b * stride_l; the library then uses it
+ *    instead of forming its own (the same values when it came from lrc_range_factor on the
+ *    same W).  For a projected member V = W^T (L^{-T} U), the same Q U.  NULL: formed here.
  * ws: lrc_eigh_multi_workspace(groups, count, prec) bytes, 256-byte aligned (one region
  *    per concurrent member, each sized for the largest n and n_vec among the groups, or
  *    for the largest member with a range basis if that needs more).
@@ -252,6 +256,8 @@ typedef struct lrc_eigh_group {
     lrc_dtype w_t;
     int64_t d_in, ldw, stride_w;
     int32_t projected;  /* 1: C holds B = Q^T C Q (d_in x d_in) from lrc_cov_accumulate_range */
+    const double *L;    /* optional factor of W W^T from lrc_range_factor (info 0); NULL: formed here */
+    int64_t ldl, stride_l;
 } lrc_eigh_group;
 size_t lrc_eigh_multi_workspace(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec);
 lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec, void *ws,

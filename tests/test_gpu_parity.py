@@ -552,6 +552,11 @@ def test_cov_range_projected_vs_oracle(lrc, prec, d_in, n, n_tok):
     out = lrc.lrc_eigh_multi([(B, k, None, None, None, Wd, True)], prec=prec)
     lam, V, info3 = (host(x) for x in out[0])
     assert int(info3[0]) == 0
+    # the caller's factor in place of the library's own: the same values, so the same bits; and the
+    # full covariance route with that factor equals the route without it
+    outL = lrc.lrc_eigh_multi([(B, k, None, None, None, Wd, True, L)], prec=prec)
+    assert int(host(outL[0][2])[0]) == 0
+    assert np.array_equal(host(outL[0][0]), lam) and np.array_equal(host(outL[0][1]), V)
     eps = host(lrc.lrc_error_curve(torch.from_numpy(lam).cuda()))
     C = oracle.covariance(X, "bf16", W, "bf16")
     lam_r, V_r = oracle.eigh(C)
