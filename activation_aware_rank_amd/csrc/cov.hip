@@ -16,6 +16,8 @@
 //   * mfma (cov_mfma.hip): bf16 inputs with 16-byte aligned rows; bf16 MFMA for Y, each output
 //     scaled by a power of two and split into fp16 hi + lo, C += 2^-(e_i + e_j) (hi^T hi + hi^T lo +
 //     lo^T hi) with fp16 MFMA and fp32 accumulation, plus the diagonal's sum of lo^2 on its own.
+//   * range-projected (cov_mfma.hip, lrc_cov_accumulate_range): C += (X L)^T (X L) for the factor L of
+//     W W^T, L^T as three bf16 pieces in the same GEMM, then the same split SYRK.
 #include "lrc_internal.h"
 #include "cov_mfma.h"
 
