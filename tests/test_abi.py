@@ -88,6 +88,14 @@ def test_argument_errors_are_synchronous():
     g.W, g.w_t, g.d_in, g.ldw, g.n_vec, g.ldv = fake, 0, 200, 400, 201, 201
     arr = (lrc._EighGroup * 1)(g)
     assert lrc._eigh_m(arr, 1, 1, fake, 1 << 30, None) == 1
+    # a caller's factor with ldl < d_in, or without the basis
+    g.n_vec, g.ldv, g.L, g.ldl = 8, 8, fake, 100
+    arr = (lrc._EighGroup * 1)(g)
+    assert lrc._eigh_m(arr, 1, 1, fake, 1 << 30, None) == 1 and "ldl" in lrc.lrc_last_error()
+    g2 = lrc._EighGroup(fake, 400, 400, 1, 0, fake, fake, 8, 8, 0, fake)
+    g2.L, g2.ldl = fake, 400
+    arr = (lrc._EighGroup * 1)(g2)
+    assert lrc._eigh_m(arr, 1, 1, fake, 1 << 30, None) == 1
     # covariance from the input covariance: NULL H, W dtype, ldh < d_in, workspace too small
     need = lrc.lrc_cov_from_input_workspace(8, 12)
     up = lambda b: (b + 255) // 256 * 256  # noqa: E731

@@ -574,6 +574,39 @@ def test_cov_range_projected_vs_oracle(lrc, prec, d_in, n, n_tok):
     assert np.all(V[idx, np.arange(k)] > 0)
 
 
+def test_cov_range_batched_members_and_dtypes(lrc):
+    """Two projected members stacked in one group (B, W and L with strides) equal the members decomposed
+    one by one, bit for bit; lrc_range_factor gives the same L from the bf16 weight and from its exact
+    fp32 and fp64 widenings."""
+    _say("projected members in one group: 2 x (2048 x 256 -> 448)")
+    d_in, n, k = 256, 448, 40
+    X = inputs.block_activations(d_in, 2048)
+    Ws = [inputs.weight(d_in, n, "bf16", inputs.CFG_BLOCK, 0, 92 + i) for i in range(2)]
+    Wd = torch.stack([dev(W, "bf16") for W in Ws])
+    Xd = dev(X, "bf16")
+    Ls, Bs = [], []
+    for i in range(2):
+        L, info = lrc.lrc_range_factor(Wd[i])
+        assert int(host(info)[0]) == 0
+        B = torch.zeros(d_in, d_in, dtype=torch.float32, device="cuda")
+        assert int(host(lrc.lrc_cov_accumulate_range(Xd, L, B))[0]) == 0
+        Ls.append(L)
+        Bs.append(B)
+        W64 = oracle.widen(Ws[i], "bf16")
+        for w in (torch.from_numpy(W64.astype(np.float32)).cuda(), torch.from_numpy(W64).cuda()):
+            L2, info2 = lrc.lrc_range_factor(w)
+            assert int(host(info2)[0]) == 0
+            assert torch.equal(torch.tril(L2), torch.tril(L))
+    Bst, Lst = torch.stack(Bs), torch.stack(Ls)
+    for prec in (1, 2):
+        lam, V, info = lrc.lrc_eigh_multi([(Bst, k, None, None, None, Wd, True, Lst)], prec=prec)[0]
+        assert np.all(host(info) == 0)
+        for i in range(2):
+            l1, V1, i1 = lrc.lrc_eigh_multi([(Bs[i], k, None, None, None, Wd[i], True, Ls[i])], prec=prec)[0]
+            assert int(host(i1)[0]) == 0
+            assert torch.equal(l1, lam[i]) and torch.equal(V1, V[i])
+
+
 def test_cov_range_rank_deficient_basis(lrc):
     """A weight whose rows are not independent: lrc_range_factor reports info 3."""
     W = inputs.weight(160, 400, "bf16", inputs.CFG_BLOCK, 0, 91)
