@@ -515,6 +515,9 @@ def main():
                     help="with --eig-range on: those covariances are accumulated in the coordinates of the basis, "
                          "B = (X L)^T (X L) with W W^T = L L^T (d_in x d_in), and decomposed from B; off: the full "
                          "d_out x d_out covariance is accumulated and projected by the decomposition")
+    ap.add_argument("--full-steps", type=int, default=2,
+                    help="timed steps of the variant that forms every covariance in full (gate/up 11008 x 11008, "
+                         "then projected by the decomposition), stages in series (0: skip; only with --cov-range on)")
     ap.add_argument("--timing-stride", type=int, default=16,
                     help="time every s-th launch of the per-column symmetric product in the timed steps")
     ap.add_argument("--layer-tokens", type=int, default=65536,
@@ -792,6 +795,62 @@ def main():
                         "two fp64 products per matrix; %s) instead of the fused GEMM + split SYRK; stages in series"
                         % ("for gate/up B = L^T (X^T X) L, W W^T = L L^T" if gP else "all in full")}
 
+    def full_leg():
+        """The same step with every covariance formed in full (gate/up as 11008 x 11008 C, decomposed
+        through their range basis), the stages in series; timed like the main step."""
+        Cfull = {g: torch.empty(len(groups[g]), g[0], g[0], dtype=torch.float32, device=dev) for g in gP}
+        ws_covf = torch.empty(max(lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, di, True, do, 1)
+                                  for di, do in sh.values()), dtype=torch.uint8, device=dev)
+        ws_eigf = torch.empty(lrc.lrc_eigh_multi_workspace(
+            [(g[0], len(ms), g[1], sh[ms[0]][0] if g in gW else 0) for g, ms in groups.items()], prec),
+            dtype=torch.uint8, device=dev)
+        groups_f = [((Cfull[g] if g in gP else gC[g]), g[1], glam[g], gV[g], ginfo[g], gW.get(g)) for g in groups]
+
+        def fstep(times):
+            e0 = ev(stream)
+            for m in MATS:
+                i = MATS.index(m)
+                g, j = where[m]
+                Cm = Cfull[g][j] if g in gP else C[m]
+                Cm.zero_()
+                lrc.lrc_cov_accumulate(Xd if m == "down_proj" else X, W[m], Cm, info=info[i:i + 1], ws=ws_covf)
+            e1 = ev(stream)
+            lrc.lrc_eigh_multi(groups_f, prec=prec, ws=ws_eigf)
+            for g in groups:
+                lrc.lrc_error_curve(glam[g], eps=geps[g])
+            e2 = ev(stream)
+            times += [("cov", e0, e1), ("eigh", e1, e2)]
+            tail(times)
+
+        for _ in range(a.warmup):
+            fstep([])
+        torch.cuda.synchronize()
+        recs_f = []
+        t0f = time.perf_counter()
+        for _ in range(a.full_steps):
+            r = []
+            fstep(r)
+            recs_f.append(r)
+        torch.cuda.synchronize()
+        wall_f = time.perf_counter() - t0f
+        assert int(info.sum().item()) == 0, "device info flags set: %s" % info.tolist()
+        per_f = {}
+        for r in recs_f:
+            for key, x0, x1 in r:
+                per_f.setdefault(key, []).append(x0.elapsed_time(x1))
+        avg_f = {k: round(float(np.mean(v)), 3) for k, v in per_f.items() if k in ("cov", "eigh")}
+        ms_f = wall_f * 1000.0 / a.full_steps
+        kf = k_out.cpu().tolist()
+        del Cfull, ws_covf, ws_eigf
+        return {"metric": "calibration tokens/s into Y^T Y", "value": a.tokens / (ms_f / 1000.0), "unit": "tokens/s",
+                "ms_per_step": ms_f, "steps": a.full_steps, "breakdown_ms": avg_f,
+                "cov_tokens_per_s": a.tokens / (avg_f["cov"] / 1000.0),
+                "allocated_ranks": dict(zip(MATS, kf)),
+                "note": "same block, inputs, factors, Fisher scores and allocation as the main step, with every "
+                        "covariance C = (X W)^T (X W) formed in full (gate/up 11008 x 11008 by the fused GEMM + "
+                        "split SYRK, decomposed through their range basis, which projects C itself); stages in "
+                        "series"}
+
     # a plain copy of known size, outside the timed region: the reference that scales HBM byte
     # counters (FETCH_SIZE / WRITE_SIZE) of a profiled run into bytes
     calib_src = torch.empty(a.calib_copy_mb << 20, dtype=torch.uint8, device=dev)
@@ -974,6 +1033,8 @@ def main():
     }
     if a.factored_steps > 0:
         out["factored"] = factored_leg()
+    if a.full_steps > 0 and gP:
+        out["full_covariance"] = full_leg()
     if a.single == "on":
         out["single_layer"] = single_layer_leg(torch, lrc, dev)
     if a.heads_tokens > 0:
