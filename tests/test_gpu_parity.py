@@ -607,6 +607,30 @@ def test_cov_range_batched_members_and_dtypes(lrc):
             assert torch.equal(l1, lam[i]) and torch.equal(V1, V[i])
 
 
+@pytest.mark.parametrize("n_tok", [1, 37])
+def test_cov_range_tiny_and_nonfinite(lrc, n_tok):
+    """d_in = 160 (one partly filled 256-row block of the product, two 128-wide SYRK tiles) and 1 or 37
+    tokens: B against (X L)^T (X L) in fp64; a NaN in X sets info 1."""
+    d_in, n = 160, 300
+    X = inputs.block_activations(d_in, 64)[:n_tok].copy()
+    W = inputs.weight(d_in, n, "bf16", inputs.CFG_BLOCK, 0, 93)
+    Wd = dev(W, "bf16")
+    L, info = lrc.lrc_range_factor(Wd)
+    assert int(host(info)[0]) == 0
+    B = torch.zeros(d_in, d_in, dtype=torch.float32, device="cuda")
+    assert int(host(lrc.lrc_cov_accumulate_range(dev(X, "bf16"), L, B))[0]) == 0
+    Y = oracle.widen(X, "bf16") @ np.tril(host(L))
+    B_ref = Y.T @ Y
+    dg = np.sqrt(np.outer(np.diag(B_ref), np.diag(B_ref)))
+    U = np.triu(np.ones((d_in, d_in), dtype=bool))
+    err = np.max(np.abs(host(B).astype(np.float64) - B_ref)[U] / dg[U])
+    assert err <= 1e-5, err
+    Xn = X.copy()
+    Xn[0, 5] = 0x7FC0  # bf16 NaN
+    B2 = torch.zeros(d_in, d_in, dtype=torch.float32, device="cuda")
+    assert int(host(lrc.lrc_cov_accumulate_range(dev(Xn, "bf16"), L, B2))[0]) == 1
+
+
 def test_cov_range_rank_deficient_basis(lrc):
     """A weight whose rows are not independent: lrc_range_factor reports info 3."""
     W = inputs.weight(160, 400, "bf16", inputs.CFG_BLOCK, 0, 91)
