@@ -2101,10 +2101,10 @@ static lrc_status run_member(const EigMember &m, const MultiPlan &p, char *lws, 
 // Members whose matrices have one order (n, or d_in with a range basis) and fit a workspace region
 // each are tridiagonalised in lockstep: every launch of the column chain works on all of them (one
 // z slice per matrix), so a chain of two small launches per column serves the whole group instead
-// of each matrix paying its own launch and latency cost on a stream of its own.  When the members
-// also share n_vec, the eigenvalues, the vectors of T and the back-transformation are batched the
-// same way (one launch per step for all members); otherwise the rest of each decomposition runs on
-// a helper stream per member.  A range member's V = Q Z follows on the call's stream.  Every
+// of each matrix paying its own launch and latency cost on a stream of its own.  The eigenvalues, the
+// vectors of T and the back-transformation are batched the same way for the members that share n_vec
+// (one launch per step for all of them): on the call's stream when all do, else one class of equal
+// n_vec per helper stream.  A range member's V = Q Z follows on the call's stream.  Every
 // member's arithmetic is the same as alone, so its results are bit-identical to a call on it alone.
 // LRC_EIGH_LOCKSTEP=0 turns this off (each member on a lane of its own throughout, as for members
 // of different orders).
@@ -2123,6 +2123,9 @@ template <class T>
 static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p, char *ws, hipStream_t s,
                                  MemberRun<T> *R) {
     const int nb = int(mem.size());
+    // members of one n_vec next to each other (regions in this order), so that each such class can
+    // run the stages after the tridiagonalisation batched; a member's results do not depend on its place
+    std::stable_sort(mem.begin(), mem.end(), [](const EigMember &x, const EigMember &y) { return x.nv > y.nv; });
     // 1. each member's setup (a range member's basis and B) and its matrix copied into A, on s
     for (int i = 0; i < nb; ++i) {
         R[i].m = mem[i];
@@ -2166,38 +2169,64 @@ static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p
         }
         return LRC_OK;
     }
-    // 3. otherwise the rest of each decomposition on a helper stream of its own
+    // 3. otherwise the members fall into classes of consecutive members with one n_vec (the order is
+    // the callers', stable under the sort by n); each class runs the stages after the tridiagonal-
+    // isation batched, as above, on a helper stream of its own (a class of one as a single job)
+    std::vector<std::pair<int, int>> cls;  // [first, last + 1)
+    for (int i = 0; i < nb;) {
+        int k = i + 1;
+        while (k < nb && R[k].j.nv == R[i].j.nv) ++k;
+        cls.push_back({i, k});
+        i = k;
+    }
+    const int ncl = int(cls.size());
     EigLanes *L = nullptr;
     lrc_status st0 = eig_lanes(&L);
     if (st0 != LRC_OK) return st0;
     hipEvent_t ev[EIG_LANES + 1];
-    st0 = take_events(L, nb + 1, ev);
+    st0 = take_events(L, ncl + 1, ev);
     if (st0 != LRC_OK) return st0;
-    const unsigned base = L->base.fetch_add(unsigned(nb));
+    const unsigned base = L->base.fetch_add(unsigned(ncl));
     hipStream_t ls[EIG_LANES];
-    for (int i = 0; i < nb; ++i) ls[i] = L->st[(base + unsigned(i)) % EIG_LANES];
+    for (int q = 0; q < ncl; ++q) ls[q] = L->st[(base + unsigned(q)) % EIG_LANES];
     auto fan = [&]() -> lrc_status {
         LRC_HIP(hipEventRecord(ev[0], s));
-        for (int i = 0; i < nb; ++i) LRC_HIP(hipStreamWaitEvent(ls[i], ev[0], 0));
-        for (int i = 0; i < nb; ++i) {
-            EigJob<T> &j = R[i].j;
-            j.s = ls[i];
-            j.stage = 2;
-            while (!j.done()) {
-                const lrc_status st = j.advance(64);
+        for (int q = 0; q < ncl; ++q) LRC_HIP(hipStreamWaitEvent(ls[q], ev[0], 0));
+        for (int q = 0; q < ncl; ++q) {
+            const int i0 = cls[q].first, i1 = cls[q].second;
+            EigJob<T> cj = R[i0].j;  // member i0's region; the class's regions follow p.per apart
+            cj.s = ls[q];
+            cj.stage = 2;
+            cj.nbatch = unsigned(i1 - i0);
+            cj.zs = int64_t(p.per);
+            while (!cj.done()) {
+                const lrc_status st = cj.advance(64);
                 if (st != LRC_OK) return st;
             }
-            const lrc_status st = member_end(R[i], ls[i]);
-            if (st != LRC_OK) return st;
+            for (int i = i0; i < i1; ++i) {
+                if (i1 - i0 > 1) {  // a batch's per-matrix outputs
+                    const EigJob<T> &j = R[i].j;
+                    LargeWs<T> &w = R[i].w;
+                    hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(j.n, 256)), dim3(256), 0, ls[q], w.lam, j.n, j.lambda,
+                                       w.bad);
+                    if (j.nv > 0 && !j.keep_z)
+                        hipLaunchKernelGGL(k_sign_out, dim3(unsigned(j.nv)), dim3(256), 0, ls[q], w.Z, j.n, j.nv, j.V,
+                                           j.ldv, w.bad);
+                    hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, ls[q], j.info, w.bad);
+                    LRC_LAUNCH_CHECK("lockstep class outputs");
+                }
+                const lrc_status st = member_end(R[i], ls[q]);
+                if (st != LRC_OK) return st;
+            }
         }
-        for (int i = 0; i < nb; ++i) {
-            LRC_HIP(hipEventRecord(ev[1 + i], ls[i]));
-            LRC_HIP(hipStreamWaitEvent(s, ev[1 + i], 0));
+        for (int q = 0; q < ncl; ++q) {
+            LRC_HIP(hipEventRecord(ev[1 + q], ls[q]));
+            LRC_HIP(hipStreamWaitEvent(s, ev[1 + q], 0));
         }
         return LRC_OK;
     };
     const lrc_status st = fan();
-    give_events(L, nb + 1, ev);
+    give_events(L, ncl + 1, ev);
     return st;
 }
 
