@@ -350,14 +350,16 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
                               for di, do in sh.values()] +
                              [lrc.lrc_cov_accumulate_range_workspace(n_tok, sh[m][0]) for m in Lf[0]]),
                          dtype=torch.uint8, device=dev)
-    ws_rf = torch.empty(max([lrc.lrc_range_factor_workspace(*sh[m]) for m in Lf[0]] + [1]), dtype=torch.uint8,
-                        device=dev)
     ws_eig = [torch.empty(lrc.lrc_eigh_multi_workspace(
         [(gk[0], len(ms), gk[1], sh[ms[0]][0] if sh[ms[0]][0] < gk[0] else 0, proj[gk]) for gk, ms in groups.items()],
         prec), dtype=torch.uint8, device=dev) for _ in range(NS)]
     gW = [{gk: torch.empty(len(ms), sh[ms[0]][0], gk[0], dtype=torch.bfloat16, device=dev)
            for gk, ms in groups.items() if sh[ms[0]][0] < gk[0]} for _ in range(NS)]
     side = [torch.cuda.Stream(device=dev) for _ in range(NS)]
+    # the range factors of a layer on streams of their own, beside that layer's first covariances
+    fst = {m: torch.cuda.Stream(device=dev) for m in Lf[0]}
+    ws_rfm = {m: torch.empty(lrc.lrc_range_factor_workspace(*sh[m]), dtype=torch.uint8, device=dev) for m in Lf[0]}
+    finfo = {m: torch.zeros(1, dtype=torch.int32, device=dev) for m in Lf[0]}
     offs_h = [0] + list(np.cumsum([kcap[m] for _ in range(n_layers) for m in MATS]))
     offs = torch.tensor(offs_h, dtype=torch.int64, device=dev)
     lam_packed = torch.empty(int(offs_h[-1]), dtype=torch.float64, device=dev)
@@ -404,6 +406,11 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
             threads[si].join()
             stream.wait_stream(side[si])
         a0 = ev(stream)
+        fev = {}
+        for m in Lf[si]:  # after this set's previous decompositions (the stream waited for them above)
+            fst[m].wait_stream(stream)
+            lrc.lrc_range_factor(Ws[layer][m], L=Lf[si][m], info=finfo[m], ws=ws_rfm[m], stream=fst[m])
+            fev[m] = ev(fst[m])
         inputs.stack_layer_gpu(g, n_tok, d_model, d_ff, dev, X, Xd)
         a1 = ev(stream)
         for i, m in enumerate(MATS):
@@ -411,8 +418,8 @@ def stack_leg(torch, lrc, n_layers, n_tok, seed, prec, dev, d_model=4096, d_ff=1
             C = gC[si][gk][j]
             C.zero_()
             if m in Lf[si]:
-                lrc.lrc_range_factor(Ws[layer][m], L=Lf[si][m], info=cinfo, ws=ws_rf)
-                bad[NS] += cinfo
+                stream.wait_event(fev[m])
+                bad[NS] += finfo[m]
                 lrc.lrc_cov_accumulate_range(X, Lf[si][m], C, info=cinfo, ws=ws_cov)
             else:
                 lrc.lrc_cov_accumulate(Xd if m == "down_proj" else X, Ws[layer][m], C, info=cinfo, ws=ws_cov)
