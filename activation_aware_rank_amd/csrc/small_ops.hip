@@ -18,8 +18,11 @@
 namespace lrc {
 
 // ---------------------------------------------------------------------------------------------
-// error curve: one thread per matrix, summed from the smallest eigenvalue (fixed order)
+// error curve: one thread per matrix, summed from the smallest eigenvalue (fixed order).  The
+// values come in blocks of ECB, the next block's loads issued before the current block's adds, so the
+// chain of dependent adds does not wait for memory at every step.
 // ---------------------------------------------------------------------------------------------
+constexpr int ECB = 32;
 __global__ void k_error_curve(const double *__restrict__ lam, int64_t n, int64_t batch, double *__restrict__ eps) {
     int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (b >= batch) return;
@@ -27,9 +30,23 @@ __global__ void k_error_curve(const double *__restrict__ lam, int64_t n, int64_t
     double *e = eps + b * (n + 1);
     double acc = 0.0;
     e[n] = 0.0;
-    for (int64_t k = n - 1; k >= 0; --k) {
-        acc = acc + l[k];
-        e[k] = acc;
+    // block q holds l[k] for k = n - 1 - q ECB - i, i = 0 .. ECB - 1 (those >= 0)
+    double cur[ECB], nxt[ECB];
+#pragma unroll
+    for (int i = 0; i < ECB; ++i) cur[i] = n - 1 - i >= 0 ? l[n - 1 - i] : 0.0;
+    for (int64_t k0 = n - 1; k0 >= 0; k0 -= ECB) {
+        const int64_t k1 = k0 - ECB;  // first index of the next block
+#pragma unroll
+        for (int i = 0; i < ECB; ++i) nxt[i] = k1 - i >= 0 ? l[k1 - i] : 0.0;
+#pragma unroll
+        for (int i = 0; i < ECB; ++i) {
+            if (k0 - i >= 0) {
+                acc = acc + cur[i];
+                e[k0 - i] = acc;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < ECB; ++i) cur[i] = nxt[i];
     }
 }
 
