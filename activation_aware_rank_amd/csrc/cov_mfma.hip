@@ -42,6 +42,7 @@
 // buffer and the buffers are added to C in split order at the end of the call (fixed order,
 // deterministic).
 #include <cmath>
+#include <cstdlib>
 #include <type_traits>
 
 #include "cov_mfma.h"
@@ -661,6 +662,142 @@ k_cov_gemm_y(const bf16_t *__restrict__ Wt, int64_t d_in, int64_t d_out, const b
         }
 }
 
+// Per-head covariance in one kernel (WSVD page, methodology 1: the covariance of each head's slice of
+// the output): workgroup (h, s) takes head h's 128 outputs over token range s.  Per 128-token tile the
+// GEMM main loop above forms Y_h^T (128 outputs x 128 tokens) = W_h^T X_tile^T; the epilogue scales y
+// by 2^e_i and splits it into fp16 hi and lo straight into LDS (over the GEMM's stages, free by then);
+// C_h's upper 64 x 64 blocks then take hi hi^T + hi lo^T + lo hi^T from LDS (three of the four waves;
+// each 64-token MFMA chain starts from zero and is added to the running block with a round-to-nearest
+// fp32 add, as in k_cov_syrk), and every output's sum of lo^2 is formed from LDS too, so Y never goes
+// to memory.  The range's C_h (scaled back by 2^-(e_i + e_j)) and sums of lo^2 (by 2^-2e_i) go to
+// P[s][h] and PD[s][h]; k_head_reduce adds them into C in range order.  Workgroup b = h S + s runs on
+// XCD b mod 8, so with S a multiple of 8 every head of one token range runs on one XCD and its L2 holds
+// the range's rows of X for all of them.
+constexpr int HF = 128;  // head width, and tokens per tile
+constexpr int HF_THREADS = 512;
+constexpr int HF_WGM = 4;  // 8 waves, 4 x 2, of 32 x 64
+// element (i, t) of a 128 x 128 fp16 tile, row i contiguous along t, 16-byte chunks XOR-swizzled by i so
+// that the 16 rows a quarter-wave reads at one chunk column land in 16 different bank groups
+__device__ __forceinline__ int hf_sw(int i, int t) { return i * HF + (((t >> 3) ^ (i & 15)) << 3) + (t & 7); }
+
+__global__ void __launch_bounds__(HF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_cov_head_fused(const bf16_t *__restrict__ Wt, int64_t d_in, const bf16_t *__restrict__ X, int64_t ldx,
+                 int64_t n_tok, int64_t tpr, int S, const int32_t *__restrict__ ex, float *__restrict__ P,
+                 float *__restrict__ PD) {
+    using Cfg = MfmaCfg<HF, HF, HF_THREADS, HF_WGM>;
+    static_assert(Cfg::TM == 1 && Cfg::TN == 2 && Cfg::WM == 32 && Cfg::WN == 64, "wave tile");
+    // three GEMM stages (2 x 128 x 32 bf16 each) or the Y tile (hi and lo, 2 x 128 x 128 fp16)
+    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * HF * HF];
+    const int H = int(gridDim.x) / S;
+    const int h = int(blockIdx.x) / S, s = int(blockIdx.x) % S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
+    const int64_t tbeg = int64_t(s) * tpr, tend = std::min<int64_t>(n_tok, tbeg + tpr);
+    const int32_t *exh = ex + int64_t(h) * HF;
+    bf16_t *yhi = lds, *ylo = lds + HF * HF;
+    // this wave's block of C_h: rows 32 wm .. + 31, columns 64 wn .. + 63; the six blocks that meet the
+    // upper triangle are formed (waves (2, 0) and (3, 0) lie below it)
+    const bool cwave = wm <= 2 * wn + 1;
+    f32x16_t cacc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) cacc[b] = f32x16_t{};
+    float sq = 0.f;  // sum of lo^2 of output tid / 4 over tokens (tid & 3) 32 .. + 31 of each tile
+    for (int64_t t0 = tbeg; t0 < tend; t0 += HF) {
+        f32x16_t acc[1][2] = {{f32x16_t{}, f32x16_t{}}};
+        const bf16_t *base[2] = {Wt + int64_t(h) * HF * d_in, X + t0 * ldx};
+        const int64_t ld[2] = {d_in, ldx};
+        const int rows[2] = {HF, int(std::min<int64_t>(HF, tend - t0))};
+        // ends with its loads landed and a barrier: the stages are free afterwards
+        gemm_dma_mainloop<HF, HF_THREADS, HF_WGM>(base, ld, rows, d_in, acc, lds, lds + 2 * HF * MK,
+                                                  lds + 4 * HF * MK);
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = wm * 32 + acc_row(lane, r);
+                const int t = wn * 64 + tn * 32 + acc_col(lane);
+                const float y = ldexpf(acc[0][tn][r], exh[i]);
+                const _Float16 hi = _Float16(y);
+                const _Float16 lo = _Float16(y - float(hi));
+                yhi[hf_sw(i, t)] = __builtin_bit_cast(bf16_t, hi);
+                ylo[hf_sw(i, t)] = __builtin_bit_cast(bf16_t, lo);
+            }
+        __syncthreads();
+        {
+            const int i = tid >> 2, tb = (tid & 3) * 32;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const f16x8_t v = *reinterpret_cast<const f16x8_t *>(ylo + hf_sw(i, tb + c * 8));
+#pragma unroll
+                for (int u = 0; u < 8; ++u) sq = fmaf(float(v[u]), float(v[u]), sq);
+            }
+        }
+        if (cwave) {
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {  // two 64-token chains
+                f32x16_t p[2];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {  // 16 tokens per slice
+                    const int tok = ch * 64 + ks * 16 + (lane >> 5) * 8;
+                    const int ia = wm * 32 + (lane & 31);
+                    const f16x8_t ah = *reinterpret_cast<const f16x8_t *>(yhi + hf_sw(ia, tok));
+                    const f16x8_t al = *reinterpret_cast<const f16x8_t *>(ylo + hf_sw(ia, tok));
+                    f16x8_t bh[2], bl[2];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int ib = wn * 64 + q * 32 + (lane & 31);
+                        bh[q] = *reinterpret_cast<const f16x8_t *>(yhi + hf_sw(ib, tok));
+                        bl[q] = *reinterpret_cast<const f16x8_t *>(ylo + hf_sw(ib, tok));
+                    }
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn) {
+                        f32x16_t q = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[tn], ks == 0 ? f32x16_t{} : p[tn],
+                                                                            0, 0, 0);
+                        q = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[tn], q, 0, 0, 0);
+                        q = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[tn], q, 0, 0, 0);
+                        p[tn] = q;
+                    }
+                }
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) cacc[tn][r] = __fadd_rn(cacc[tn][r], p[tn][r]);
+            }
+        }
+        __syncthreads();  // the next tile's loads overwrite the Y tile
+    }
+    float *dst = P + (int64_t(s) * H + h) * HF * HF;
+    if (cwave) {
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = wm * 32 + acc_row(lane, r);
+                const int j = wn * 64 + tn * 32 + acc_col(lane);
+                if (i <= j) dst[i * HF + j] = ldexpf(cacc[tn][r], -(exh[i] + exh[j]));
+            }
+    }
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    if ((tid & 3) == 0) PD[(int64_t(s) * H + h) * HF + (tid >> 2)] = ldexpf(sq, -2 * exh[tid >> 2]);
+}
+
+// C_h[i][j] (i <= j) += sum_s P[s][h][i][j] (+ sum_s PD[s][h][i] on the diagonal), s in order; head h's
+// block at C + h * HF * ldc
+__global__ void __launch_bounds__(256) k_head_reduce(float *__restrict__ C, int64_t ldc, const float *__restrict__ P,
+                                                     const float *__restrict__ PD, int S, int H) {
+    const int64_t per = int64_t(HF) * HF, total = per * H;
+    for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total; e += int64_t(gridDim.x) * blockDim.x) {
+        const int h = int(e / per), i = int((e % per) / HF), j = int(e % HF);
+        if (i > j) continue;
+        float acc = C[int64_t(h) * HF * ldc + int64_t(i) * ldc + j];
+        for (int s = 0; s < S; ++s) acc += P[(int64_t(s) * H + h) * per + int64_t(i) * HF + j];
+        if (i == j)
+            for (int s = 0; s < S; ++s) acc += PD[(int64_t(s) * H + h) * HF + i];
+        C[int64_t(h) * HF * ldc + int64_t(i) * ldc + j] = acc;
+    }
+}
+
 // Phase 2: block tiles of each head block that meet its upper triangle, split s of the token
 // range.  A tile is BM rows (block row I) by BN columns (block column J); it meets the upper
 // triangle when its last column is at or right of its first row.  Tiles are numbered column
@@ -1043,6 +1180,20 @@ bool cov_mfma_supported(lrc_dtype x_t, const void *X, int64_t ldx, const void *W
            (d_out + 1) * (MFMA_CHUNK + 4 * MK) * 2 < (int64_t(1) << 31);
 }
 
+// The fused per-head kernel, taken with the environment variable LRC_HEAD_FUSED=1 for head blocks of
+// width HF with a weight and d_in a multiple of the k step.  It is not the default: on the per-head keys
+// (32768 tokens, 32 heads of 128) it took 2.21 ms against 1.42 ms for the GEMM and the SYRK through
+// memory, whose 256 x 256 GEMM tiles give each wave twice the MFMAs per barrier, while Y's round trip
+// through HBM costs about 0.1 ms there.
+static bool head_fused(int has_w, int64_t d_in, int64_t d_out, int32_t n_blocks, int np) {
+    const char *e = std::getenv("LRC_HEAD_FUSED");
+    if (!(e && e[0] == '1' && e[1] == 0)) return false;
+    return has_w && np == 1 && n_blocks > 1 && d_out / n_blocks == HF && d_in % MK == 0;
+}
+// token ranges of the fused per-head kernel: about 256 workgroups in all (one per CU), at most one per
+// 128-token tile
+static int head_ranges_max(int32_t n_blocks) { return std::max(1, (256 + n_blocks - 1) / n_blocks); }
+
 // np: 1, or 3 for the range-projected product (A = L^T in three pieces)
 static size_t mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_out, int32_t n_blocks, int np) {
     const MfmaPlan p = plan(n_tok, d_out, n_blocks, has_w != 0);
@@ -1056,6 +1207,11 @@ static size_t mfma_workspace(int64_t n_tok, int64_t d_in, int has_w, int64_t d_o
         c.carve<float>(XNORM_BLOCKS);
         c.carve<int32_t>(size_t(d_out));
         c.carve<float>(size_t(LOSQ_SEG) * size_t(d_out));
+    }
+    if (head_fused(has_w, d_in, d_out, n_blocks, np)) {
+        const size_t hs = size_t(n_blocks) * size_t(head_ranges_max(n_blocks));
+        c.carve<float>(hs * HF * HF);
+        c.carve<float>(hs * HF);
     }
     // the generic path's buffer, used when the call's pointers are not aligned
     if (np == 1) c.carve<float>(size_t(d_out) * size_t(std::min<int64_t>(4096, n_tok)));
@@ -1083,7 +1239,11 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
     float *part = has_w ? cv.carve<float>(XNORM_BLOCKS) : nullptr;
     int32_t *ex = has_w ? cv.carve<int32_t>(size_t(a.d_out)) : nullptr;
     float *lpart = has_w ? cv.carve<float>(size_t(LOSQ_SEG) * size_t(a.d_out)) : nullptr;
-    if (!P || !Yhi || (has_w && (!Wt || !Ylo || !part || !ex || !lpart)))
+    const bool hf = head_fused(has_w, a.d_in, a.d_out, a.n_blocks, np);
+    const size_t hs = size_t(a.n_blocks) * size_t(head_ranges_max(a.n_blocks));
+    float *HP = hf ? cv.carve<float>(hs * HF * HF) : nullptr;
+    float *HPD = hf ? cv.carve<float>(hs * HF) : nullptr;
+    if (!P || !Yhi || (has_w && (!Wt || !Ylo || !part || !ex || !lpart)) || (hf && (!HP || !HPD)))
         return fail(LRC_ERR_WORKSPACE, "covariance workspace too small");
     const bf16_t *X = static_cast<const bf16_t *>(a.X);
     if (rng) {
@@ -1104,6 +1264,19 @@ lrc_status cov_mfma_run(const CovArgs &a, void *ws, size_t ws_bytes, hipStream_t
         hipLaunchKernelGGL(k_split_exp, dim3(unsigned(cdiv(a.d_out, 4))), dim3(256), 0, s, part, XNORM_BLOCKS, Wt,
                            np * a.d_in, a.d_out, ex);
         LRC_LAUNCH_CHECK("k_split_exp");
+    }
+    if (hf) {  // per-head blocks of 128: GEMM, split and SYRK in one kernel, then the range sums
+        const int H = a.n_blocks;
+        const int64_t tiles = (a.n_tok + HF - 1) / HF;
+        const int S = int(std::min<int64_t>(tiles, head_ranges_max(H)));
+        const int64_t tpr = (tiles + S - 1) / S * HF;
+        const double fl = double(a.n_tok) * (2.0 * double(a.d_in) * double(a.d_out) + double(H) * HF * (HF + 1));
+        LRC_TIMED_LAUNCH("k_cov_head_fused", fl, k_cov_head_fused, dim3(unsigned(H * S)), dim3(HF_THREADS), 0, s, Wt,
+                         a.d_in, X, a.ldx, a.n_tok, tpr, S, ex, HP, HPD);
+        LRC_LAUNCH_CHECK("k_cov_head_fused");
+        hipLaunchKernelGGL(k_head_reduce, dim3(1024), dim3(256), 0, s, a.C, a.ldc, HP, HPD, S, H);
+        LRC_LAUNCH_CHECK("k_head_reduce");
+        return LRC_OK;
     }
     if (pn) {
         hipLaunchKernelGGL(k_fill_f32, dim3(1024), dim3(256), 0, s, P, int64_t(pn));

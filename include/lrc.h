@@ -121,6 +121,9 @@ const char *lrc_last_error(void);
  *    products, fp32 sums).
  *    fp32 inputs use fp32 arithmetic throughout.
  *    A non-finite x or W entry reaches C as before (the scale is then 1).
+ *    Per-head blocks of 128 with the environment variable LRC_HEAD_FUSED=1: the same arithmetic
+ *    with each head's Y tile kept in LDS (one kernel), the token ranges' partial sums added in
+ *    order; results agree with the default path to fp32 rounding (not bit for bit).
  * info: one int32; set to 1 when the updated C has a non-finite diagonal entry.
  * Errors: LRC_ERR_ARG for non-positive sizes, small leading dims, d_out % n_blocks != 0,
  *    NULL X or C; LRC_ERR_DTYPE for other dtypes or x_t != w_t; LRC_ERR_WORKSPACE.

@@ -54,6 +54,34 @@ def _upper_err(C_hat, C_ref):
     return np.max(np.abs(np.where(U, C_hat - C_ref, 0.0)))
 
 
+@pytest.mark.parametrize("n_tok,d_in,heads", [(1000, 256, 8), (300, 512, 3), (5000, 4096, 2)])
+def test_cov_per_head_fused_vs_oracle(lrc, n_tok, d_in, heads):
+    """Heads of 128 with LRC_HEAD_FUSED=1 take the fused kernel (GEMM, fp16 split and SYRK of each head's
+    128-token tiles in LDS, partial sums per token range added in range order): every head block against
+    the oracle's per-head covariance (1e-5 of sqrt(C_ii C_jj)), and the default two-kernel path through
+    memory to the same bar; ragged token counts, the fused path over two accumulating calls."""
+    _say("cov per-head fused %d x %d, %d heads of 128" % (n_tok, d_in, heads))
+    X = inputs.per_head(n_tok=n_tok, d_model=d_in, head_dim=128)["X"]
+    W = inputs.weight(d_in, heads * 128, "bf16", inputs.CFG_HEADS, 0, 7)
+    os.environ["LRC_HEAD_FUSED"] = "1"
+    try:
+        C = _cov_gpu(lrc, X[:n_tok // 3], "bf16", W, n_blocks=heads)
+        _cov_gpu(lrc, X[n_tok // 3:], "bf16", W, n_blocks=heads, C=C)
+    finally:
+        del os.environ["LRC_HEAD_FUSED"]
+    C = host(C).astype(np.float64)
+    C2 = host(_cov_gpu(lrc, X, "bf16", W, n_blocks=heads)).astype(np.float64)
+    Cr = oracle.covariance(X, "bf16", W, "bf16", n_blocks=heads)
+    U = np.triu(np.ones((128, 128), dtype=bool))
+    for hh in range(heads):
+        dg = np.sqrt(np.outer(np.diag(Cr[hh]), np.diag(Cr[hh])))
+        e1 = np.max(np.abs(C[hh] - Cr[hh])[U] / dg[U])
+        e2 = np.max(np.abs(C2[hh] - Cr[hh])[U] / dg[U])
+        print("head %d: fused %.2e, through memory %.2e of sqrt(C_ii C_jj)" % (hh, e1, e2))
+        assert e1 <= 1e-5 and e2 <= 1e-5
+        assert np.all(np.tril(C[hh], -1) == 0)
+
+
 def test_cov_single_layer_fp32(lrc):
     _say("cov fp32 2048x256 -> 256 (full single-layer size)")
     d = inputs.single_layer()
