@@ -266,7 +266,8 @@ static std::vector<EighArgs> eigh_groups(const lrc_eigh_group *g, int32_t count,
     for (int32_t i = 0; i < count; ++i)
         v.push_back(EighArgs{g[i].C, g[i].n, g[i].ldc, g[i].batch, g[i].stride_c, prec, g[i].lambda, g[i].V,
                              g[i].ldv, g[i].n_vec, g[i].stride_v, g[i].info, g[i].W, g[i].w_t, g[i].d_in,
-                             g[i].ldw, g[i].stride_w, g[i].projected, g[i].L, g[i].ldl, g[i].stride_l});
+                             g[i].ldw, g[i].stride_w, g[i].projected, g[i].L, g[i].ldl, g[i].stride_l, g[i].A,
+                             g[i].lda, g[i].stride_a});
     return v;
 }
 
@@ -290,6 +291,10 @@ lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype
         if (g.L)
             REQUIRE(g.W && g.ldl >= g.d_in && (g.batch == 1 || g.stride_l >= g.d_in * g.ldl - (g.ldl - g.d_in)),
                     LRC_ERR_ARG, "L needs the range basis W, ldl >= d_in and stride_l between members");
+        if (g.A)
+            REQUIRE(g.projected && g.n_vec > 0 && g.lda >= g.n_vec &&
+                        (g.batch == 1 || g.stride_a >= g.d_in * g.lda - (g.lda - g.n_vec)),
+                    LRC_ERR_ARG, "A needs a projected group, n_vec > 0, lda >= n_vec and stride_a between members");
         lrc_status st = check_eigh(g.C, g.n, g.ldc, g.batch, g.stride_c, g.lambda, g.V, g.ldv, g.n_vec, g.stride_v,
                                    g.info, g.projected ? g.d_in : g.n);
         if (st != LRC_OK) return st;
@@ -321,15 +326,15 @@ lrc_status lrc_factorize(const void *W, lrc_dtype w_t, int32_t trans_w, int64_t 
                          const float *V, int64_t ldv, int64_t k, int64_t batch, int64_t stride_w,
                          int64_t stride_v, float *A, int64_t lda, int64_t stride_a, float *B, int64_t ldb,
                          int64_t stride_b, void *stream) {
-    REQUIRE(W && V && A, LRC_ERR_ARG, "W, V and A must be non-NULL");
+    REQUIRE(W && V && (A || B), LRC_ERR_ARG, "W and V must be non-NULL, and A or B");
     REQUIRE(trans_w == 0 || trans_w == 1, LRC_ERR_ARG, "trans_w must be 0 or 1");
     REQUIRE(d_in > 0 && d_out > 0 && k > 0 && batch > 0, LRC_ERR_ARG, "sizes must be positive");
     REQUIRE(ldw >= d_out, LRC_ERR_ARG, "ldw < d_out");
-    REQUIRE(ldv >= k && lda >= k, LRC_ERR_ARG, "ldv or lda < k");
+    REQUIRE(ldv >= k && (!A || lda >= k), LRC_ERR_ARG, "ldv or lda < k");
     const int64_t vrows = trans_w ? d_in : d_out;
     REQUIRE(k <= vrows, LRC_ERR_ARG, "k larger than the rows of V");
     REQUIRE(!B || ldb >= vrows, LRC_ERR_ARG, "ldb < rows of V");
-    REQUIRE(batch == 1 || (stride_w >= 0 && stride_v >= 0 && stride_a > 0 && (!B || stride_b > 0)),
+    REQUIRE(batch == 1 || (stride_w >= 0 && stride_v >= 0 && (!A || stride_a > 0) && (!B || stride_b > 0)),
             LRC_ERR_ARG, "bad batch strides");
     REQUIRE(w_t == LRC_BF16 || w_t == LRC_F32 || w_t == LRC_F64, LRC_ERR_DTYPE, "w_t must be bf16, f32 or f64");
     FactorizeArgs a{W, w_t, trans_w, d_in, d_out, ldw, V, ldv, k, batch, stride_w, stride_v,

@@ -648,6 +648,11 @@ lrc_status dgemm_run(int ta, int tb, int64_t M, int64_t N, int64_t K, const doub
     return fail(LRC_ERR_UNIMPLEMENTED, "fp64 product: operand layout not instantiated");
 }
 
+lrc_status lower_product_run(int64_t m, int64_t n, const double *L, int64_t ldl, const double *B, int64_t ldb,
+                             double *C, int64_t ldc, hipStream_t s) {
+    return launch_gemm<0, 0, 1, 0, 0>(gemm(m, n, m, L, ldl, B, ldb, C, ldc, 1.0, 0.0), s);
+}
+
 lrc_status gram_f64_run(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg, hipStream_t s) {
     GemmArgs g = gemm(m, m, n, B, ldb, B, ldb, nullptr, ldg, 1.0, 0.0, 2);
     g.Cf = G;

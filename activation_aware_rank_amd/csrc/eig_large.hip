@@ -1515,6 +1515,42 @@ __global__ void __launch_bounds__(256) k_sign_out(const double *__restrict__ Z, 
         V[r * ldv + j] = isbad ? NAN : float(sgn * Z[r * nv + j]);
 }
 
+// k_sign_out for a projected member that also returns the factor A = W V = L U: V's column j (from Z,
+// n x nv) takes the sign rule, and column j of A (from Z2 = L U, n2 x nv) the same sign
+__global__ void __launch_bounds__(256) k_sign_out_pair(const double *__restrict__ Z, int64_t n, int64_t nv,
+                                                       float *__restrict__ V, int64_t ldv, const double *__restrict__ Z2,
+                                                       int64_t n2, float *__restrict__ A, int64_t lda, const int *bad) {
+    __shared__ double sb[256];
+    __shared__ int si[256];
+    const int64_t j = blockIdx.x;
+    double best = -1.0;
+    int64_t bi = n;
+    for (int64_t r = threadIdx.x; r < n; r += blockDim.x) {
+        const double a = fabs(Z[r * nv + j]);
+        if (a > best) { best = a; bi = r; }
+    }
+    sb[threadIdx.x] = best;
+    si[threadIdx.x] = int(bi);
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) {
+            const double ob = sb[threadIdx.x + o];
+            const int oi = si[threadIdx.x + o];
+            if (ob > sb[threadIdx.x] || (ob == sb[threadIdx.x] && oi < si[threadIdx.x])) {
+                sb[threadIdx.x] = ob;
+                si[threadIdx.x] = oi;
+            }
+        }
+        __syncthreads();
+    }
+    const double sgn = (si[0] < n && Z[int64_t(si[0]) * nv + j] < 0.0) ? -1.0 : 1.0;
+    const bool isbad = *bad != 0;
+    for (int64_t r = threadIdx.x; r < n; r += blockDim.x)
+        V[r * ldv + j] = isbad ? NAN : float(sgn * Z[r * nv + j]);
+    for (int64_t r = threadIdx.x; r < n2; r += blockDim.x)
+        A[r * lda + j] = isbad ? NAN : float(sgn * Z2[r * nv + j]);
+}
+
 __global__ void k_set_info(int32_t *info, const int *bad) {
     if (threadIdx.x == 0) *info = *bad ? LRC_INFO_NONFINITE : LRC_INFO_OK;
 }
@@ -1815,7 +1851,7 @@ __global__ void __launch_bounds__(256) k_range_check(const double *__restrict__ 
 }
 
 struct RangeWs {
-    double *Qt, *C64, *T, *G, *lamB;
+    double *Qt, *C64, *T, *G, *lamB, *A64;
     void *chol, *trsm;
     float *B;
     int32_t *iw;
@@ -1836,6 +1872,7 @@ static void range_layout(C_ &cv, RangeWs &rw, LargeWs<T> &w, int64_t n, int64_t 
     rw.trsm = cv.template carve<char>(trsm_workspace(0, r, n));
     rw.B = proj ? nullptr : cv.template carve<float>(size_t(r) * size_t(r));
     rw.iw = cv.template carve<int32_t>(2);
+    rw.A64 = proj ? cv.template carve<double>(size_t(r) * size_t(nv)) : nullptr;  // L U, for the factor A
 }
 
 template <class T>
@@ -1985,6 +2022,8 @@ struct EigMember {
     bool proj;  // C holds B = Q^T C Q (d_in x d_in, ldc) instead of C
     const double *L;  // the factor of W W^T given by the caller (lower, ldl), or nullptr
     int64_t ldl;
+    float *A;  // a projected member's factor W V = L U (d_in x nv, lda), or nullptr
+    int64_t lda;
 };
 
 // One member's decomposition: its layout on a workspace region and its job; for a member with a
@@ -2069,14 +2108,19 @@ static lrc_status member_end(MemberRun<T> &R, hipStream_t s) {
     RangeWs &rw = R.rw;
     if (nv > 0) {
         lrc_status st = LRC_OK;
-        if (m.proj) {  // Q Z = W^T L^{-T} Z: Z <- L^{-T} Z, then W^T Z
-            st = trsm_run(0, 1, r, nv, R.L, R.ldl, R.w.Z, nv, rw.trsm, s);
+        if (m.proj) {  // Q Z = W^T L^{-T} Z: Z <- L^{-T} Z, then W^T Z (first L Z for the factor A)
+            if (m.A) st = lower_product_run(r, nv, R.L, R.ldl, R.w.Z, nv, rw.A64, nv, s);
+            if (st == LRC_OK) st = trsm_run(0, 1, r, nv, R.L, R.ldl, R.w.Z, nv, rw.trsm, s);
             if (st == LRC_OK) st = dgemm_run(1, 0, n, nv, r, rw.Qt, n, R.w.Z, nv, rw.T, nv, 0, nullptr, s);
         } else {
             st = dgemm_run(1, 0, n, nv, r, rw.Qt, n, R.w.Z, nv, rw.T, nv, 0, nullptr, s);  // Q Z
         }
         if (st != LRC_OK) return st;
-        hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, R.w.bad);
+        if (m.proj && m.A)
+            hipLaunchKernelGGL(k_sign_out_pair, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, rw.A64, r,
+                               m.A, m.lda, R.w.bad);
+        else
+            hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, R.w.bad);
         LRC_LAUNCH_CHECK("k_sign_out");
     }
     hipLaunchKernelGGL(k_range_finish, dim3(cdiv(n, 256)), dim3(256), 0, s, rw.lamB, r, n, m.lambda, R.w.bad, rw.iw, nv,
@@ -2346,7 +2390,8 @@ lrc_status eigh_multi_run(const EighArgs *g, int count, lrc_dtype prec, void *ws
                                     a.V ? a.V + b * a.stride_v : nullptr, a.ldv, a.n_vec, a.info + b,
                                     rng ? static_cast<const char *>(a.W) + size_t(b * a.stride_w) * esz : nullptr,
                                     a.w_t, a.d_in, a.ldw, rng && a.projected != 0,
-                                    rng && a.L ? a.L + b * a.stride_l : nullptr, a.ldl});
+                                    rng && a.L ? a.L + b * a.stride_l : nullptr, a.ldl,
+                                    rng && a.projected && a.A ? a.A + b * a.stride_a : nullptr, a.lda});
     }
     char *lw = static_cast<char *>(ws) + p.jac;
     return prec == LRC_F64 ? large_sched<double>(mem, p, lw, s) : large_sched<float>(mem, p, lw, s);

@@ -136,12 +136,14 @@ static void launch_gemm(const FactorizeArgs &a, hipStream_t s) {
 
 lrc_status factorize_run(const FactorizeArgs &a, hipStream_t s) {
     if (a.batch > 65535) return fail(LRC_ERR_ARG, "batch too large");
-    switch (a.w_t) {
-        case LRC_BF16: launch_gemm<bf16_t>(a, s); break;
-        case LRC_F32: launch_gemm<float>(a, s); break;
-        case LRC_F64: launch_gemm<double>(a, s); break;
+    if (a.A) {
+        switch (a.w_t) {
+            case LRC_BF16: launch_gemm<bf16_t>(a, s); break;
+            case LRC_F32: launch_gemm<float>(a, s); break;
+            case LRC_F64: launch_gemm<double>(a, s); break;
+        }
+        LRC_LAUNCH_CHECK("k_factor_gemm");
     }
-    LRC_LAUNCH_CHECK("k_factor_gemm");
     if (a.B) {
         const int64_t rows = a.trans_w ? a.d_in : a.d_out;
         dim3 g(cdiv(a.k, 64), cdiv(rows, 64), unsigned(a.batch));

@@ -132,6 +132,9 @@ struct EighArgs {
     // optional factor of W W^T from lrc_range_factor (lower, d_in x d_in, member b at L + b stride_l)
     const double *L = nullptr;
     int64_t ldl = 0, stride_l = 0;
+    // optional, projected members: A = W V[:, :n_vec] (d_in x n_vec fp32) formed as L U
+    float *A = nullptr;
+    int64_t lda = 0, stride_a = 0;
 };
 lrc_status range_factor_enqueue(const void *W, lrc_dtype w_t, int64_t r, int64_t n, int64_t ldw, double *Wf,
                                 double *L, int64_t ldl, void *chol_ws, int32_t *info, hipStream_t s);
@@ -224,5 +227,8 @@ lrc_status dgemm_run(int ta, int tb, int64_t M, int64_t N, int64_t K, const doub
                      int64_t ldb, double *C, int64_t ldc, int tiles, float *Cf, hipStream_t s);
 lrc_status gram_f64_run(const double *B, int64_t m, int64_t n, int64_t ldb, float *G, int64_t ldg,
                         hipStream_t s);
+// C (m x n) = L B with L lower triangular (m x m, its strict upper triangle not read), fp64
+lrc_status lower_product_run(int64_t m, int64_t n, const double *L, int64_t ldl, const double *B, int64_t ldb,
+                             double *C, int64_t ldc, hipStream_t s);
 
 }  // namespace lrc

@@ -208,14 +208,15 @@ class _EighGroup(ctypes.Structure):
     _fields_ = [("C", _vp), ("n", _i64), ("ldc", _i64), ("batch", _i64), ("stride_c", _i64), ("lambda_", _vp),
                 ("V", _vp), ("ldv", _i64), ("n_vec", _i64), ("stride_v", _i64), ("info", _vp),
                 ("W", _vp), ("w_t", _int), ("d_in", _i64), ("ldw", _i64), ("stride_w", _i64),
-                ("projected", _i32), ("L", _vp), ("ldl", _i64), ("stride_l", _i64)]
+                ("projected", _i32), ("L", _vp), ("ldl", _i64), ("stride_l", _i64),
+                ("A", _vp), ("lda", _i64), ("stride_a", _i64)]
 
 
 _eigh_mws = _sig("lrc_eigh_multi_workspace", _sz, ctypes.POINTER(_EighGroup), _i32, _int)
 _eigh_m = _sig("lrc_eigh_multi", _int, ctypes.POINTER(_EighGroup), _i32, _int, _vp, _sz, _vp)
 
 
-def _eigh_args(C, n_vec, lam, V, info, W=None, projected=False, L=None):
+def _eigh_args(C, n_vec, lam, V, info, W=None, projected=False, L=None, A=None):
     """Marshals one lrc_eigh call (W: the optional range basis of lrc_eigh_multi, d_in x n or
     batch x d_in x n; projected: C is B = Q^T C Q, d_in x d_in): (struct, squeeze flag, lam, V,
     info)."""
@@ -243,6 +244,11 @@ def _eigh_args(C, n_vec, lam, V, info, W=None, projected=False, L=None):
         if L is not None:
             g.L, g.ldl = _ptr(L), _f64_matrix(L, "L")
             g.stride_l = L.stride(0) if L.dim() == 3 else 0
+        if A is not None:
+            if A.dtype != torch.float32:
+                raise TypeError("A must be float32")
+            g.A, g.lda = _ptr(A), _rows(A, "A")
+            g.stride_a = A.stride(0) if A.dim() == 3 else 0
     return g, squeeze, lam, V, info
 
 
@@ -283,13 +289,14 @@ def lrc_eigh_multi(groups, prec: int = LRC_F32, ws=None, stream=None):
     (C, n_vec, lam, V, info, W), (C, n_vec, lam, V, info, W, projected) or (..., projected, L) with
     the meaning of lrc_eigh's arguments; W is the optional range basis (d_in x n, or batch x d_in x
     n: C = (X W)^T (X W)); projected: C is B = Q^T C Q (d_in x d_in) from lrc_cov_accumulate_range;
-    L: the factor of W W^T from lrc_range_factor (d_in x d_in, or batch x d_in x d_in).  Returns a
+    L: the factor of W W^T from lrc_range_factor (d_in x d_in, or batch x d_in x d_in); an optional
+    ninth element A (d_in x n_vec fp32, or batched) of a projected group receives W V = L U.  Returns a
     list of (lambda, V, info) per group."""
     parts = []
     for grp in groups:
         C, n_vec = grp[0], grp[1]
-        lam, V, info, W, pj, L = (tuple(grp[2:8]) + (None, None, None, None, False, None))[:6]
-        parts.append(_eigh_args(C, n_vec, lam, V, info, W, bool(pj), L))
+        lam, V, info, W, pj, L, A = (tuple(grp[2:9]) + (None, None, None, None, False, None, None))[:7]
+        parts.append(_eigh_args(C, n_vec, lam, V, info, W, bool(pj), L, A))
     if not parts:
         raise ValueError("lrc_eigh_multi needs at least one group")
     arr = (_EighGroup * len(parts))(*[p[0] for p in parts])
@@ -351,16 +358,18 @@ def lrc_error_curve(lam: torch.Tensor, eps=None, stream=None) -> torch.Tensor:
     return eps
 
 
-def lrc_factorize(W: torch.Tensor, V: torch.Tensor, k: int, A: torch.Tensor, B: torch.Tensor | None = None,
+def lrc_factorize(W: torch.Tensor, V: torch.Tensor, k: int, A: torch.Tensor | None, B: torch.Tensor | None = None,
                   trans_w: int = 0, d_in: int | None = None, d_out: int | None = None, batch: int = 1,
                   stride_w: int = 0, stride_v: int = 0, stride_a: int = 0, stride_b: int = 0, stream=None):
-    """A = W V[:, :k] (trans_w 0) or W^T V[:, :k] (trans_w 1); B = V[:, :k]^T when given.
-    Batched matrices are addressed by element strides (a per-head W_h is a column slice)."""
-    ldw, ldv, lda = _rows(W, "W"), _rows(V, "V"), _rows(A, "A")
+    """A = W V[:, :k] (trans_w 0) or W^T V[:, :k] (trans_w 1) when A is given; B = V[:, :k]^T when
+    given.  Batched matrices are addressed by element strides (a per-head W_h is a column slice)."""
+    ldw, ldv = _rows(W, "W"), _rows(V, "V")
+    lda = _rows(A, "A") if A is not None else 0
     ldb = _rows(B, "B") if B is not None else 0
     d_in = W.shape[-2] if d_in is None else d_in
     d_out = W.shape[-1] if d_out is None else d_out
-    if V.dtype != torch.float32 or A.dtype != torch.float32 or (B is not None and B.dtype != torch.float32):
+    if V.dtype != torch.float32 or (A is not None and A.dtype != torch.float32) or \
+            (B is not None and B.dtype != torch.float32):
         raise TypeError("V, A and B must be float32")
     _check(_fac(_ptr(W), _dt(W), trans_w, d_in, d_out, ldw, _ptr(V), ldv, k, batch, stride_w, stride_v, _ptr(A), lda,
                 stride_a, _ptr(B), ldb, stride_b, _stream(stream)))

@@ -593,6 +593,11 @@ def main():
     V = {m: gV[where[m][0]][where[m][1]] for m in MATS}
     eps = {m: geps[where[m][0]][where[m][1]] for m in MATS}
     A = {m: torch.empty(di, ks[m], dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
+    # a projected group's factors A = W V = L U come out of its decomposition (stacked per group)
+    gA = {g: torch.empty(len(groups[g]), sh[groups[g][0]][0], g[1], dtype=torch.float32, device=dev) for g in gP}
+    for g in gP:
+        for i, m in enumerate(groups[g]):
+            A[m] = gA[g][i]
     B = {m: torch.empty(ks[m], do, dtype=torch.float32, device=dev) for m, (di, do) in sh.items()}
     info = torch.zeros(8, dtype=torch.int32, device=dev)
     ws_cov = torch.empty(max([lrc.lrc_cov_accumulate_workspace(lrc.LRC_BF16, a.tokens, di, True, do, 1)
@@ -604,7 +609,7 @@ def main():
     ws_eig = torch.empty(lrc.lrc_eigh_multi_workspace(
         [(g[0], len(ms), g[1], sh[ms[0]][0] if g in gW else 0, g in gP) for g, ms in groups.items()], prec),
         dtype=torch.uint8, device=dev)
-    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g], gW.get(g), g in gP, gL.get(g)) for g in groups]
+    eig_groups = [(gC[g], g[1], glam[g], gV[g], ginfo[g], gW.get(g), g in gP, gL.get(g), gA.get(g)) for g in groups]
     gkey = "+".join("%dx%d_k%d" % (len(ms), g[0], g[1]) for g, ms in groups.items())
     # overlap: covariances group by group, largest n first; each group's eigendecompositions and
     # error curves on a side stream of its own (default priority) with a workspace of its own
@@ -684,7 +689,8 @@ def main():
         sg.wait_event(ready)
         e0 = ev(sg)
         lrc.lrc_eigh_multi([(gC[g][lo:hi], g[1], glam[g][lo:hi], gV[g][lo:hi], ginfo[g][lo:hi],
-                             gW[g][lo:hi] if g in gW else None, g in gP, gL[g][lo:hi] if g in gP else None)
+                             gW[g][lo:hi] if g in gW else None, g in gP, gL[g][lo:hi] if g in gP else None,
+                             gA[g][lo:hi] if g in gP else None)
                             for g, lo, hi in phases[pi]], prec=prec, ws=ws_eig_g[pi], stream=sg)
         for g, lo, hi in phases[pi]:
             lrc.lrc_error_curve(glam[g][lo:hi], eps=geps[g][lo:hi], stream=sg)
@@ -695,14 +701,15 @@ def main():
         for g, lo, hi in phases[pi]:
             for m in groups[g][lo:hi]:
                 f0 = ev(sg)
-                lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m], stream=sg)
+                lrc.lrc_factorize(W[m], V[m], ks[m], None if m in Lf else A[m], B[m], stream=sg)
                 f1 = ev(sg)
                 times.append((m + ".fac", f0, f1))
 
-    def tail(times, factors=True):
+    def tail(times, factors=True, a_from_eig=True):
+        # a_from_eig: the projected groups' decompositions formed A (only B is formed here for them)
         for m in MATS if factors else ():
             e0 = ev(stream)
-            lrc.lrc_factorize(W[m], V[m], ks[m], A[m], B[m])
+            lrc.lrc_factorize(W[m], V[m], ks[m], None if (a_from_eig and m in Lf) else A[m], B[m])
             e1 = ev(stream)
             times.append((m + ".fac", e0, e1))
         e5 = ev(stream)
@@ -827,7 +834,7 @@ def main():
                 lrc.lrc_error_curve(glam[g], eps=geps[g])
             e2 = ev(stream)
             times += [("cov", e0, e1), ("eigh", e1, e2)]
-            tail(times)
+            tail(times, a_from_eig=False)
 
         for _ in range(a.warmup):
             fstep([])

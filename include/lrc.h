@@ -139,8 +139,8 @@ lrc_status lrc_cov_accumulate(const void *X, lrc_dtype x_t, int64_t n_tok, int64
  * Range-projected covariance (Swift-SVD page, section 2-ga: only Y^T Y's eigenpairs enter
  * the closed form; for a layer that widens, d_in < d_out, C = Y^T Y has rank at most d_in).
  *
- * lrc_range_factor: L (d_in x d_in, fp64, lower triangle written, the strict upper triangle
- *    left as it is) with W W^T = L L^T, W: d_in x n (ldw >= n, n >= d_in) of dtype LRC_BF16,
+ * lrc_range_factor: L (d_in x d_in, fp64, lower; its strict upper triangle set to 0) with
+ *    W W^T = L L^T, W: d_in x n (ldw >= n, n >= d_in) of dtype LRC_BF16,
  *    LRC_F32 or LRC_F64, widened exactly to fp64; W W^T and its Cholesky factorisation in
  *    fp64 (the kernels of lrc_cholesky).  info (one int32): 0; 3 when W W^T is not
  *    positive definite or L's diagonal spans more than a factor 1e5 (W not of full row rank
@@ -242,6 +242,10 @@ lrc_status lrc_eigh(const float *C, int64_t n, int64_t ldc, int64_t batch, int64
  *    d_in x d_in fp64, ldl >= d_in, member b at L + b * stride_l; the library then uses it
  *    instead of forming its own (the same values when it came from lrc_range_factor on the
  *    same W).  For a projected member V = W^T (L^{-T} U), the same Q U.  NULL: formed here.
+ * A (optional, projected groups only): also the factor A = W V[:, :n_vec] of lrc_factorize
+ *    (d_in x n_vec fp32, lda >= n_vec, member b at A + b * stride_a), formed as L U with U's
+ *    columns signed as V's (W V = W W^T L^{-T} U = L U exactly), in fp64, rounded once; the
+ *    caller then needs lrc_factorize only for B.  NULL: not formed.
  * ws: lrc_eigh_multi_workspace(groups, count, prec) bytes, 256-byte aligned (one region
  *    per concurrent member, each sized for the largest n and n_vec among the groups, or
  *    for the largest member with a range basis if that needs more).
@@ -261,6 +265,8 @@ typedef struct lrc_eigh_group {
     int32_t projected;  /* 1: C holds B = Q^T C Q (d_in x d_in) from lrc_cov_accumulate_range */
     const double *L;    /* optional factor of W W^T from lrc_range_factor (info 0); NULL: formed here */
     int64_t ldl, stride_l;
+    float *A;           /* optional, projected groups: the factor W V[:, :n_vec], d_in x n_vec */
+    int64_t lda, stride_a;
 } lrc_eigh_group;
 size_t lrc_eigh_multi_workspace(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec);
 lrc_status lrc_eigh_multi(const lrc_eigh_group *groups, int32_t count, lrc_dtype prec, void *ws,
@@ -280,7 +286,8 @@ lrc_status lrc_error_curve(const double *lambda, int64_t n, int64_t batch, doubl
  *
  * trans_w == 0:  A = W V[:, :k]   (A: d_in x k),  W d_in x d_out, V d_out x (>= k).
  * trans_w == 1:  A = W^T V[:, :k] (A: d_out x k), W d_in x d_out, V d_in x (>= k).
- * B = V[:, :k]^T (k x rows(V)) when B != NULL.
+ * B = V[:, :k]^T (k x rows(V)) when B != NULL.  A may be NULL when B is not (only B is formed:
+ *    a projected decomposition of lrc_eigh_multi can return A itself).
  * W: dtype w_t (LRC_BF16, LRC_F32 or LRC_F64), leading dim ldw >= d_out; V fp32 with
  *    leading dim ldv >= k; A fp32 (lda >= k); B fp32 (ldb >= rows of V).
  * Batched: matrix b uses W + b*stride_w, V + b*stride_v, A + b*stride_a, B + b*stride_b

@@ -218,7 +218,8 @@ def test_gate_projected_full_size(lrc, block_inputs):
     B = torch.zeros(d_in, d_in, dtype=torch.float32, device="cuda")
     info = lrc.lrc_cov_accumulate_range(X, L, B)
     assert int(host(info)[0]) == 0
-    lam, V, info = lrc.lrc_eigh_multi([(B, k, None, None, None, W, True)], prec=1)[0]
+    Af = torch.empty(d_in, k, dtype=torch.float32, device="cuda")
+    lam, V, info = lrc.lrc_eigh_multi([(B, k, None, None, None, W, True, L, Af)], prec=1)[0]
     assert int(host(info)[0]) == 0
     eps_h = host(lrc.lrc_error_curve(lam))
     lam_h = host(lam)
@@ -250,9 +251,13 @@ def test_gate_projected_full_size(lrc, block_inputs):
     Bh = host(B)
     dB = np.sqrt(np.diag(Bh).astype(np.float64)[ii] * np.diag(Bh).astype(np.float64)[jj])
     errB = np.max(np.abs(Bh[ii, jj] - refB) / dB)
+    rows = torch.randint(0, d_in, (64,), generator=torch.Generator().manual_seed(5)).cuda()
+    Ar = W64[rows] @ Vk
+    fa = float((Af[rows].to(f64) - Ar).abs().max() / Ar.abs().max())
     print("gate_proj projected: L err %.2e, sampled B entries %.2e of sqrt(B_ii B_jj), residual %.2e, "
-          "orthogonality %.2e, closed form %.2e, eps_0 vs trace %.2e"
-          % (errL, errB, res, orth, cf, abs(eps_h[0] - tr) / tr))
+          "orthogonality %.2e, closed form %.2e, eps_0 vs trace %.2e, factor A = L U vs W V %.2e"
+          % (errL, errB, res, orth, cf, abs(eps_h[0] - tr) / tr, fa))
+    assert fa <= 1e-6
     assert errL <= 1e-12 and errB <= 1e-5
     assert res <= 1e-5 and orth <= 1e-5
     assert cf <= 1e-4 and abs(eps_h[0] - tr) <= 1e-6 * tr

@@ -627,12 +627,28 @@ def test_cov_range_batched_members_and_dtypes(lrc):
             assert torch.equal(torch.tril(L2), torch.tril(L))
     Bst, Lst = torch.stack(Bs), torch.stack(Ls)
     for prec in (1, 2):
-        lam, V, info = lrc.lrc_eigh_multi([(Bst, k, None, None, None, Wd, True, Lst)], prec=prec)[0]
+        Ast = torch.empty(2, d_in, k, dtype=torch.float32, device="cuda")
+        lam, V, info = lrc.lrc_eigh_multi([(Bst, k, None, None, None, Wd, True, Lst, Ast)], prec=prec)[0]
         assert np.all(host(info) == 0)
         for i in range(2):
-            l1, V1, i1 = lrc.lrc_eigh_multi([(Bs[i], k, None, None, None, Wd[i], True, Ls[i])], prec=prec)[0]
+            A1 = torch.empty(d_in, k, dtype=torch.float32, device="cuda")
+            l1, V1, i1 = lrc.lrc_eigh_multi([(Bs[i], k, None, None, None, Wd[i], True, Ls[i], A1)], prec=prec)[0]
             assert int(host(i1)[0]) == 0
-            assert torch.equal(l1, lam[i]) and torch.equal(V1, V[i])
+            assert torch.equal(l1, lam[i]) and torch.equal(V1, V[i]) and torch.equal(A1, Ast[i])
+            # the factor A = W V = L U against the fp64 product of W and the returned V, and against
+            # lrc_factorize's own A; B alone from lrc_factorize (A = NULL)
+            W64 = oracle.widen(Ws[i], "bf16")
+            Ar = W64 @ host(V[i]).astype(np.float64)
+            Ah = host(Ast[i]).astype(np.float64)
+            err = np.linalg.norm(Ah - Ar) / np.linalg.norm(Ar)
+            A2 = torch.empty(d_in, k, dtype=torch.float32, device="cuda")
+            lrc.lrc_factorize(Wd[i], V[i], k, A2, None)
+            Bt2 = torch.empty(k, n, dtype=torch.float32, device="cuda")
+            lrc.lrc_factorize(Wd[i], V[i], k, None, Bt2)
+            err2 = np.linalg.norm(Ah - host(A2).astype(np.float64)) / np.linalg.norm(Ar)
+            print("member %d prec %d: A from the decomposition vs W V %.2e, vs lrc_factorize %.2e" % (i, prec, err, err2))
+            assert err <= 1e-6 and err2 <= 1e-6
+            assert torch.equal(Bt2, V[i].T.contiguous())
 
 
 @pytest.mark.parametrize("n_tok", [1, 37])
