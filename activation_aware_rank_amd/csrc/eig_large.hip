@@ -2148,8 +2148,9 @@ static lrc_status run_member(const EigMember &m, const MultiPlan &p, char *lws, 
 // of each matrix paying its own launch and latency cost on a stream of its own.  The eigenvalues, the
 // vectors of T and the back-transformation are batched the same way for the members that share n_vec
 // (one launch per step for all of them): on the call's stream when all do, else one class of equal
-// n_vec per helper stream.  A range member's V = Q Z follows on the call's stream.  Every
-// member's arithmetic is the same as alone, so its results are bit-identical to a call on it alone.
+// n_vec per helper stream.  A range member's V = Q Z follows (two or more range members each on a
+// helper stream, concurrently).  Every member's arithmetic is the same as alone, so its results are
+// bit-identical to a call on it alone.
 // LRC_EIGH_LOCKSTEP=0 turns this off (each member on a lane of its own throughout, as for members
 // of different orders).
 static int64_t trd_order(const EigMember &m) { return m.W ? m.d_in : m.n; }
@@ -2200,6 +2201,7 @@ static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p
             const lrc_status st = bj.advance(64);
             if (st != LRC_OK) return st;
         }
+        std::vector<int> rg;  // members with a range basis: V = Q Z and lambda with the zeros to follow
         for (int i = 0; i < nb; ++i) {
             const EigJob<T> &j = R[i].j;
             LargeWs<T> &w = R[i].w;
@@ -2208,10 +2210,41 @@ static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p
                 hipLaunchKernelGGL(k_sign_out, dim3(unsigned(j.nv)), dim3(256), 0, s, w.Z, j.n, j.nv, j.V, j.ldv, w.bad);
             hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, s, j.info, w.bad);
             LRC_LAUNCH_CHECK("lockstep outputs");
-            const lrc_status st = member_end(R[i], s);
-            if (st != LRC_OK) return st;
+            if (R[i].m.W) rg.push_back(i);
         }
-        return LRC_OK;
+        if (rg.size() < 2) {
+            for (int i : rg) {
+                const lrc_status st = member_end(R[i], s);
+                if (st != LRC_OK) return st;
+            }
+            return LRC_OK;
+        }
+        // two or more range members: each one's V = Q Z (a triangular solve of many small launches for
+        // a projected member, then an fp64 product) on a helper stream of its own, so that the solves
+        // overlap; the call's stream waits for all of them
+        const int nr = int(rg.size());
+        EigLanes *L = nullptr;
+        lrc_status st0 = eig_lanes(&L);
+        if (st0 != LRC_OK) return st0;
+        hipEvent_t ev[EIG_LANES + 1];
+        st0 = take_events(L, nr + 1, ev);
+        if (st0 != LRC_OK) return st0;
+        const unsigned base = L->base.fetch_add(unsigned(nr));
+        auto fan = [&]() -> lrc_status {
+            LRC_HIP(hipEventRecord(ev[0], s));
+            for (int q = 0; q < nr; ++q) {
+                hipStream_t lq = L->st[(base + unsigned(q)) % EIG_LANES];
+                LRC_HIP(hipStreamWaitEvent(lq, ev[0], 0));
+                const lrc_status st = member_end(R[rg[q]], lq);
+                if (st != LRC_OK) return st;
+                LRC_HIP(hipEventRecord(ev[1 + q], lq));
+                LRC_HIP(hipStreamWaitEvent(s, ev[1 + q], 0));
+            }
+            return LRC_OK;
+        };
+        const lrc_status st = fan();
+        give_events(L, nr + 1, ev);
+        return st;
     }
     // 3. otherwise the members fall into classes of consecutive members with one n_vec (the order is
     // the callers', stable under the sort by n); each class runs the stages after the tridiagonal-
