@@ -765,6 +765,39 @@ def test_factorize_matches_fp64_product(lrc, wdt):
     assert np.linalg.norm(host(A2) - ref2) <= 1e-6 * np.linalg.norm(ref2)
 
 
+@pytest.mark.parametrize("trans,vcols", [(0, 2850), (1, 2850), (0, 2852), (1, 2852)])
+def test_factorize_large_tiles(lrc, trans, vcols):
+    """Products with at least 512 output tiles of 128 x 128 take the kernel's large-tile instance:
+    2900 x 2850 outputs over a contraction of 2860 (ragged in every dimension), against the fp64
+    product; a batch of two equals the members computed one by one, bit for bit.  V with 2852
+    columns (rows 4-element aligned) takes the vector loads, with 2850 the element loads."""
+    _say("factorize 128-wide tiles, trans_w %d, V with %d columns" % (trans, vcols))
+    rows, red, k = 2900, 2860, 2850
+    W = inputs.weight(rows, red, "bf16", inputs.CFG_BLOCK, 0, 7) if trans == 0 else \
+        inputs.weight(red, rows, "bf16", inputs.CFG_BLOCK, 0, 7)
+    V = np.random.default_rng(4).standard_normal((red, vcols)).astype(np.float32)
+    A = torch.empty(rows, k, dtype=torch.float32, device="cuda")
+    Wd, Vd = dev(W, "bf16"), dev(V, "f32")
+    lrc.lrc_factorize(Wd, Vd, k, A, None, trans_w=trans)
+    W64 = oracle.widen(W, "bf16")
+    ref = (W64 if trans == 0 else W64.T) @ V[:, :k].astype(np.float64)
+    Ah = host(A).astype(np.float64)
+    err = np.linalg.norm(Ah - ref) / np.linalg.norm(ref)
+    print("relative Frobenius error %.2e" % err)
+    assert err <= 1e-6
+    # the fp64 product rounded once to fp32 (half an fp32 ulp), up to the order of the fp64 sums
+    # (entries with heavy cancellation, below 1e-6 of the largest, left to the norm check)
+    big = np.abs(ref) >= 1e-6 * np.abs(ref).max()
+    assert np.max(np.abs(Ah - ref)[big] / np.abs(ref)[big]) <= 2.0 ** -23
+    Wb, Vb = torch.stack([Wd, Wd.flip(0)]), torch.stack([Vd, Vd.flip(1)])
+    Ab = torch.empty(2, rows, k, dtype=torch.float32, device="cuda")
+    lrc.lrc_factorize(Wb, Vb, k, Ab, None, trans_w=trans, d_in=Wd.shape[0], d_out=Wd.shape[1], batch=2,
+                      stride_w=Wd.numel(), stride_v=Vd.numel(), stride_a=rows * k)
+    A1 = torch.empty(rows, k, dtype=torch.float32, device="cuda")
+    lrc.lrc_factorize(Wb[1], Vb[1], k, A1, None, trans_w=trans)
+    assert torch.equal(Ab[0], A) and torch.equal(Ab[1], A1)
+
+
 def test_factorize_per_head_batch(lrc):
     _say("factorize per-head batch")
     W = inputs.weight(512, 512, "bf16", inputs.CFG_HEADS, 0, 0)
