@@ -765,21 +765,26 @@ def test_factorize_matches_fp64_product(lrc, wdt):
     assert np.linalg.norm(host(A2) - ref2) <= 1e-6 * np.linalg.norm(ref2)
 
 
-@pytest.mark.parametrize("trans,vcols", [(0, 2850), (1, 2850), (0, 2852), (1, 2852)])
-def test_factorize_large_tiles(lrc, trans, vcols):
+@pytest.mark.parametrize("trans,vcols,wdt", [(0, 2850, "bf16"), (1, 2850, "bf16"), (0, 2852, "bf16"),
+                                             (1, 2852, "bf16"), (0, 2852, "f32"), (1, 2852, "f64")])
+def test_factorize_large_tiles(lrc, trans, vcols, wdt):
     """Products with at least 512 output tiles of 128 x 128 take the kernel's large-tile instance:
     2900 x 2850 outputs over a contraction of 2860 (ragged in every dimension), against the fp64
     product; a batch of two equals the members computed one by one, bit for bit.  V with 2852
-    columns (rows 4-element aligned) takes the vector loads, with 2850 the element loads."""
-    _say("factorize 128-wide tiles, trans_w %d, V with %d columns" % (trans, vcols))
+    columns (rows 4-element aligned) takes the vector loads, with 2850 the element loads; W in bf16,
+    fp32 and fp64 (the fp64 weight holds fp32 values, widened exactly)."""
+    _say("factorize 128-wide tiles, trans_w %d, V with %d columns, W %s" % (trans, vcols, wdt))
     rows, red, k = 2900, 2860, 2850
-    W = inputs.weight(rows, red, "bf16", inputs.CFG_BLOCK, 0, 7) if trans == 0 else \
-        inputs.weight(red, rows, "bf16", inputs.CFG_BLOCK, 0, 7)
+    gen = "bf16" if wdt == "bf16" else "f32"
+    W = inputs.weight(rows, red, gen, inputs.CFG_BLOCK, 0, 7) if trans == 0 else \
+        inputs.weight(red, rows, gen, inputs.CFG_BLOCK, 0, 7)
+    if wdt == "f64":
+        W = W.astype(np.float64)
     V = np.random.default_rng(4).standard_normal((red, vcols)).astype(np.float32)
     A = torch.empty(rows, k, dtype=torch.float32, device="cuda")
-    Wd, Vd = dev(W, "bf16"), dev(V, "f32")
+    Wd, Vd = dev(W, wdt), dev(V, "f32")
     lrc.lrc_factorize(Wd, Vd, k, A, None, trans_w=trans)
-    W64 = oracle.widen(W, "bf16")
+    W64 = oracle.widen(W, wdt)
     ref = (W64 if trans == 0 else W64.T) @ V[:, :k].astype(np.float64)
     Ah = host(A).astype(np.float64)
     err = np.linalg.norm(Ah - ref) / np.linalg.norm(ref)
