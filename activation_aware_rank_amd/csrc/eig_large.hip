@@ -1484,71 +1484,62 @@ __global__ void __launch_bounds__(256) k_bt_update(const T *__restrict__ Rt, int
 // ---------------------------------------------------------------------------------------------
 // 5. signs and output
 // ---------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_sign_out(const double *__restrict__ Z, int64_t n, int64_t nv,
-                                                  float *__restrict__ V, int64_t ldv, const int *bad) {
-    __shared__ double sb[256];
-    __shared__ int si[256];
-    const int64_t j = blockIdx.x;
+// Sign rule and fp32 output: column j of V (from Z, n x nv fp64) is scaled by the sign of its entry
+// of largest magnitude (the first such row on ties; NaN entries never win), and with Z2 != NULL
+// column j of A (from Z2, n2 x nv) takes the same sign.  A workgroup takes 16 columns, its 64 row
+// groups stride down them, so every row's 16 values come in one 128-byte run; the per-group
+// maxima are combined in a fixed tree with the same tie rule.  NaN everywhere when *bad is set.
+constexpr int SG_COLS = 16, SG_ROWS = 64;
+__global__ void __launch_bounds__(SG_COLS * SG_ROWS) k_sign_cols(const double *__restrict__ Z, int64_t n, int64_t nv,
+                                                               float *__restrict__ V, int64_t ldv,
+                                                               const double *__restrict__ Z2, int64_t n2,
+                                                               float *__restrict__ A, int64_t lda, const int *bad) {
+    __shared__ double sb[SG_ROWS][SG_COLS];
+    __shared__ int si[SG_ROWS][SG_COLS];
+    __shared__ double sg[SG_COLS];
+    const int t = threadIdx.x, jc = t % SG_COLS, rg = t / SG_COLS;
+    const int64_t j = int64_t(blockIdx.x) * SG_COLS + jc;
+    const bool live = j < nv;
     double best = -1.0;
     int64_t bi = n;
-    for (int64_t r = threadIdx.x; r < n; r += blockDim.x) {
-        const double a = fabs(Z[r * nv + j]);
-        if (a > best) { best = a; bi = r; }
+    if (live) {
+#pragma unroll 8
+        for (int64_t r = rg; r < n; r += SG_ROWS) {
+            const double a = fabs(Z[r * nv + j]);
+            if (a > best) {
+                best = a;
+                bi = r;
+            }
+        }
     }
-    sb[threadIdx.x] = best;
-    si[threadIdx.x] = int(bi);
+    sb[rg][jc] = best;
+    si[rg][jc] = int(bi);
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (threadIdx.x < o) {
-            const double ob = sb[threadIdx.x + o];
-            const int oi = si[threadIdx.x + o];
-            if (ob > sb[threadIdx.x] || (ob == sb[threadIdx.x] && oi < si[threadIdx.x])) {
-                sb[threadIdx.x] = ob;
-                si[threadIdx.x] = oi;
+    for (int o = SG_ROWS / 2; o > 0; o >>= 1) {
+        if (rg < o) {
+            const double ob = sb[rg + o][jc];
+            const int oi = si[rg + o][jc];
+            if (ob > sb[rg][jc] || (ob == sb[rg][jc] && oi < si[rg][jc])) {
+                sb[rg][jc] = ob;
+                si[rg][jc] = oi;
             }
         }
         __syncthreads();
     }
-    const double sgn = (si[0] < n && Z[int64_t(si[0]) * nv + j] < 0.0) ? -1.0 : 1.0;
+    if (rg == 0) sg[jc] = (live && si[0][jc] < n && Z[int64_t(si[0][jc]) * nv + j] < 0.0) ? -1.0 : 1.0;
+    __syncthreads();
+    if (!live) return;
+    const double sgn = sg[jc];
     const bool isbad = *bad != 0;
-    for (int64_t r = threadIdx.x; r < n; r += blockDim.x)
-        V[r * ldv + j] = isbad ? NAN : float(sgn * Z[r * nv + j]);
+    for (int64_t r = rg; r < n; r += SG_ROWS) V[r * ldv + j] = isbad ? NAN : float(sgn * Z[r * nv + j]);
+    if (Z2)
+        for (int64_t r = rg; r < n2; r += SG_ROWS) A[r * lda + j] = isbad ? NAN : float(sgn * Z2[r * nv + j]);
 }
 
-// k_sign_out for a projected member that also returns the factor A = W V = L U: V's column j (from Z,
-// n x nv) takes the sign rule, and column j of A (from Z2 = L U, n2 x nv) the same sign
-__global__ void __launch_bounds__(256) k_sign_out_pair(const double *__restrict__ Z, int64_t n, int64_t nv,
-                                                       float *__restrict__ V, int64_t ldv, const double *__restrict__ Z2,
-                                                       int64_t n2, float *__restrict__ A, int64_t lda, const int *bad) {
-    __shared__ double sb[256];
-    __shared__ int si[256];
-    const int64_t j = blockIdx.x;
-    double best = -1.0;
-    int64_t bi = n;
-    for (int64_t r = threadIdx.x; r < n; r += blockDim.x) {
-        const double a = fabs(Z[r * nv + j]);
-        if (a > best) { best = a; bi = r; }
-    }
-    sb[threadIdx.x] = best;
-    si[threadIdx.x] = int(bi);
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (threadIdx.x < o) {
-            const double ob = sb[threadIdx.x + o];
-            const int oi = si[threadIdx.x + o];
-            if (ob > sb[threadIdx.x] || (ob == sb[threadIdx.x] && oi < si[threadIdx.x])) {
-                sb[threadIdx.x] = ob;
-                si[threadIdx.x] = oi;
-            }
-        }
-        __syncthreads();
-    }
-    const double sgn = (si[0] < n && Z[int64_t(si[0]) * nv + j] < 0.0) ? -1.0 : 1.0;
-    const bool isbad = *bad != 0;
-    for (int64_t r = threadIdx.x; r < n; r += blockDim.x)
-        V[r * ldv + j] = isbad ? NAN : float(sgn * Z[r * nv + j]);
-    for (int64_t r = threadIdx.x; r < n2; r += blockDim.x)
-        A[r * lda + j] = isbad ? NAN : float(sgn * Z2[r * nv + j]);
+static void sign_out(const double *Z, int64_t n, int64_t nv, float *V, int64_t ldv, const int *bad, hipStream_t s,
+                     const double *Z2 = nullptr, int64_t n2 = 0, float *A = nullptr, int64_t lda = 0) {
+    hipLaunchKernelGGL(k_sign_cols, dim3(unsigned(cdiv(nv, SG_COLS))), dim3(SG_COLS * SG_ROWS), 0, s, Z, n, nv, V, ldv,
+                       Z2, n2, A, lda, bad);
 }
 
 __global__ void k_set_info(int32_t *info, const int *bad) {
@@ -1781,8 +1772,8 @@ struct EigJob {
             LRC_LAUNCH_CHECK("back-transformation");
             if (c0 >= 0) return LRC_OK;
             if (!keep_z && nbatch == 1) {
-                hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, w->Z, n, nv, V, ldv, w->bad);
-                LRC_LAUNCH_CHECK("k_sign_out");
+                sign_out(w->Z, n, nv, V, ldv, w->bad, s);
+                LRC_LAUNCH_CHECK("k_sign_cols");
             }
             stage = 4;
         }
@@ -2117,11 +2108,10 @@ static lrc_status member_end(MemberRun<T> &R, hipStream_t s) {
         }
         if (st != LRC_OK) return st;
         if (m.proj && m.A)
-            hipLaunchKernelGGL(k_sign_out_pair, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, rw.A64, r,
-                               m.A, m.lda, R.w.bad);
+            sign_out(rw.T, n, nv, m.V, m.ldv, R.w.bad, s, rw.A64, r, m.A, m.lda);
         else
-            hipLaunchKernelGGL(k_sign_out, dim3(unsigned(nv)), dim3(256), 0, s, rw.T, n, nv, m.V, m.ldv, R.w.bad);
-        LRC_LAUNCH_CHECK("k_sign_out");
+            sign_out(rw.T, n, nv, m.V, m.ldv, R.w.bad, s);
+        LRC_LAUNCH_CHECK("k_sign_cols");
     }
     hipLaunchKernelGGL(k_range_finish, dim3(cdiv(n, 256)), dim3(256), 0, s, rw.lamB, r, n, m.lambda, R.w.bad, rw.iw, nv,
                        m.info);
@@ -2207,7 +2197,7 @@ static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p
             LargeWs<T> &w = R[i].w;
             hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(j.n, 256)), dim3(256), 0, s, w.lam, j.n, j.lambda, w.bad);
             if (j.nv > 0 && !j.keep_z)
-                hipLaunchKernelGGL(k_sign_out, dim3(unsigned(j.nv)), dim3(256), 0, s, w.Z, j.n, j.nv, j.V, j.ldv, w.bad);
+                sign_out(w.Z, j.n, j.nv, j.V, j.ldv, w.bad, s);
             hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, s, j.info, w.bad);
             LRC_LAUNCH_CHECK("lockstep outputs");
             if (R[i].m.W) rg.push_back(i);
@@ -2287,8 +2277,7 @@ static lrc_status large_lockstep(std::vector<EigMember> &mem, const MultiPlan &p
                     hipLaunchKernelGGL(k_lambda_desc, dim3(cdiv(j.n, 256)), dim3(256), 0, ls[q], w.lam, j.n, j.lambda,
                                        w.bad);
                     if (j.nv > 0 && !j.keep_z)
-                        hipLaunchKernelGGL(k_sign_out, dim3(unsigned(j.nv)), dim3(256), 0, ls[q], w.Z, j.n, j.nv, j.V,
-                                           j.ldv, w.bad);
+                        sign_out(w.Z, j.n, j.nv, j.V, j.ldv, w.bad, ls[q]);
                     hipLaunchKernelGGL(k_set_info, dim3(1), dim3(64), 0, ls[q], j.info, w.bad);
                     LRC_LAUNCH_CHECK("lockstep class outputs");
                 }
