@@ -582,7 +582,10 @@ def main():
     gC = {g: torch.empty(len(ms), gd[g], gd[g], dtype=torch.float32, device=dev) for g, ms in groups.items()}
     gL = {g: torch.zeros(len(groups[g]), gd[g], gd[g], dtype=torch.float64, device=dev) for g in gP}
     glam = {g: torch.empty(len(ms), g[0], dtype=torch.float64, device=dev) for g, ms in groups.items()}
-    gV = {g: torch.empty(len(ms), g[0], g[1], dtype=torch.float32, device=dev) for g, ms in groups.items()}
+    # V's rows padded to a multiple of four values (16 bytes), so that the factor products can load
+    # four consecutive values of V at a time; the decompositions write the first n_vec of each row
+    gV = {g: torch.empty(len(ms), g[0], (g[1] + 3) // 4 * 4, dtype=torch.float32, device=dev)[:, :, :g[1]]
+          for g, ms in groups.items()}
     geps = {g: torch.empty(len(ms), g[0] + 1, dtype=torch.float64, device=dev) for g, ms in groups.items()}
     ginfo = {g: torch.zeros(len(ms), dtype=torch.int32, device=dev) for g, ms in groups.items()}
     where = {m: (g, ms.index(m)) for g, ms in groups.items() for m in ms}
