@@ -233,6 +233,11 @@ def _eigh_args(C, n_vec, lam, V, info, W=None, projected=False, L=None, A=None):
         lam = torch.empty(batch, n, dtype=torch.float64, device=dev)
     if V is None and n_vec > 0:
         V = torch.empty(batch, n, n_vec, dtype=torch.float32, device=dev)
+    if squeeze:  # a caller's lam (n,) and V (n, n_vec) for a single matrix, as batches of one (views)
+        if lam.dim() == 1:
+            lam = lam.unsqueeze(0)
+        if V is not None and V.dim() == 2:
+            V = V.unsqueeze(0)
     ldv = _rows(V, "V") if V is not None else max(n_vec, 1)
     stride_v = (V.stride(0) if V.dim() == 3 else 0) if V is not None else 0
     info = _info(info, batch, dev)

@@ -500,6 +500,28 @@ def test_eigh_range_basis_vs_oracle(lrc, prec):
         assert np.array_equal(host(l1), lam) and np.array_equal(host(V1), V)
 
 
+def test_eigh_padded_vector_rows(lrc):
+    """V with a leading dimension larger than n_vec (rows padded to 16 bytes, as bench.py allocates it):
+    a lockstep pair of order 300 and a member through a 300-row range basis of order 520, n_vec = 37,
+    equal the contiguous outputs bit for bit, and the padding columns are left as they were."""
+    _say("eigh with padded V rows: 2 x 300 and 520 via a 300-row basis, n_vec 37 in rows of 40")
+    X = inputs.block_activations(300, 1024)
+    Cf = np.stack([oracle.covariance(X, "bf16", inputs.weight(300, 300, "bf16", inputs.CFG_BLOCK, 0, 80 + m),
+                                     "bf16").astype(np.float32) for m in range(2)])
+    Wr = inputs.weight(300, 520, "bf16", inputs.CFG_BLOCK, 0, 82)
+    Cr = _oracle_cov32(X, "bf16", Wr)[0]
+    nv = 37
+    ref = lrc.lrc_eigh_multi([(dev(Cf, "f32"), nv), (dev(Cr, "f32"), nv, None, None, None, dev(Wr, "bf16"))], prec=1)
+    Vp1 = torch.full((2, 300, 40), float("nan"), dtype=torch.float32, device="cuda")
+    Vp2 = torch.full((520, 40), float("nan"), dtype=torch.float32, device="cuda")
+    out = lrc.lrc_eigh_multi([(dev(Cf, "f32"), nv, None, Vp1[:, :, :nv], None),
+                              (dev(Cr, "f32"), nv, None, Vp2[:, :nv], None, dev(Wr, "bf16"))], prec=1)
+    for (l0, V0, i0), (l1, V1, i1) in zip(ref, out):
+        assert np.all(host(i1) == 0)
+        assert torch.equal(l0, l1) and torch.equal(V0, V1)
+    assert bool(torch.isnan(Vp1[:, :, nv:]).all()) and bool(torch.isnan(Vp2[:, nv:]).all())
+
+
 @pytest.mark.parametrize("prec,same_nv", [(1, False), (2, False), (1, True), (2, True)])
 def test_eigh_lockstep_mixed_members(lrc, prec, same_nv):
     """Members of one tridiagonal order in one call are tridiagonalised in lockstep (one launch per
